@@ -1,0 +1,178 @@
+"""fp64 CPU oracle for the forward selective scans -- TEST INFRASTRUCTURE.
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+may import this module.  The product path (the HIP library and its binding)
+never does, and this module imports nothing from the product package.
+
+The arithmetic lives in ``ssm_oracle.c`` (plain C, double precision, the
+sequential recurrence exactly as defined on the pages); this file only builds
+and loads it and marshals numpy arrays.  Inputs are float32 (bf16 inputs are
+passed as their exactly-widened float32 values); outputs are float64.
+
+Parity status of each function (what pins it is listed in the tests):
+  s6_fwd    pinned: exact-fraction hand cases, A->0 cumulative-sum limit,
+            closed-form brute force, carry composition, linearity.
+  ssd_fwd   pinned: brute-force semiseparable matrix, chunked algebra,
+            reduction to S6, group replication, hand case.
+  cssd_fwd  pinned: reduction to the real SSD at zero phase, L=1 closed form,
+            brute-force complex semiseparable matrix, conjugate-C identity.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# flag values of the library interface (restated by value)
+BBAR_ZOH, BBAR_DT, BBAR_ONE = 0x0, 0x1, 0x2
+CPLX_STABLE, CPLX_DOC, CPLX_CODE, CPLX_CONJ_C = 0x0, 0x4, 0x8, 0x10
+
+
+def build() -> str:
+    """Compile the oracle with gcc (IEEE double, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+           "-o", _LIB, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    common = [P] * 8
+    lib.oracle_s6_fwd.argtypes = common + [I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
+    lib.oracle_ssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
+    lib.oracle_cssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
+    for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd):
+        f.restype = None
+    lib.oracle_softplus.argtypes = [ctypes.c_double]
+    lib.oracle_softplus.restype = ctypes.c_double
+    lib.oracle_phi1.argtypes = [ctypes.c_double]
+    lib.oracle_phi1.restype = ctypes.c_double
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f32(a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def softplus(x: float) -> float:
+    return _load().oracle_softplus(float(x))
+
+
+def phi1(z: float) -> float:
+    return _load().oracle_phi1(float(z))
+
+
+def _units(units, n0, n1):
+    if units is None:
+        bb, ii = np.meshgrid(np.arange(n0), np.arange(n1), indexing="ij")
+        return np.ascontiguousarray(np.stack([bb.ravel(), ii.ravel()], 1).astype(np.int64)), True
+    u = np.ascontiguousarray(np.asarray(units, dtype=np.int64).reshape(-1, 2))
+    if u.size and (u[:, 0].min() < 0 or u[:, 0].max() >= n0 or u[:, 1].min() < 0 or u[:, 1].max() >= n1):
+        raise ValueError("unit index out of range")
+    return u, False
+
+
+def s6_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, flags=BBAR_ZOH, units=None, nthreads=None):
+    """Sequential S6 recurrence in fp64.
+
+    u, dt: (batch, L, d_inner); dt_bias, D: (d_inner,) or None (zero);
+    A_log: (d_inner, N); B, C: (batch, L, N); h0: (batch, d_inner, N) or None.
+    ``units``: optional (b, d) pairs; then y is (n_units, L) and h_final
+    (n_units, N).  Without units: y (batch, L, d_inner), h_final (batch, d_inner, N).
+    """
+    u, dt, dt_bias, A_log, B, C, D, h0 = map(_f32, (u, dt, dt_bias, A_log, B, C, D, h0))
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    uu, full = _units(units, batch, Dm)
+    nu = uu.shape[0]
+    y = np.empty((nu, L), np.float64)
+    hf = np.empty((nu, N), np.float64)
+    _load().oracle_s6_fwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                          _ptr(h0), batch, L, Dm, N, flags, _ptr(uu), nu, _ptr(y), _ptr(hf),
+                          nthreads or default_threads())
+    if full:
+        return (y.reshape(batch, Dm, L).transpose(0, 2, 1).copy(), hf.reshape(batch, Dm, N))
+    return y, hf
+
+
+def ssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_DT, units=None,
+            nthreads=None):
+    """Sequential SSD (scalar A per head) recurrence in fp64.
+
+    x: (batch, L, H, P); dt: (batch, L, H); dt_bias, A_log, D: (H,);
+    B, C: (batch, L, G, N); h0: (batch, H, P, N) or None.
+    Without units: y (batch, L, H, P), h_final (batch, H, P, N); with (b, h)
+    units: y (n_units, L, P), h_final (n_units, P, N).
+    """
+    x, dt, dt_bias, A_log, B, C, D, h0 = map(_f32, (x, dt, dt_bias, A_log, B, C, D, h0))
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert G == ngroups
+    uu, full = _units(units, batch, H)
+    nu = uu.shape[0]
+    y = np.empty((nu, L, P), np.float64)
+    hf = np.empty((nu, P, N), np.float64)
+    _load().oracle_ssd_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                           _ptr(h0), batch, L, H, P, N, G, flags, _ptr(uu), nu, _ptr(y), _ptr(hf),
+                           nthreads or default_threads())
+    if full:
+        return (y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(), hf.reshape(batch, H, P, N))
+    return y, hf
+
+
+def cssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_ZOH | CPLX_STABLE,
+             units=None, nthreads=None):
+    """Sequential complex-state SSD recurrence in fp64.
+
+    x: (batch, L, H, P); dt: (batch, L, H); A_log: (H, 2) = [log|A|, arg A];
+    B, C: (batch, L, G, Nc, 2) interleaved (re, im); h0: (batch, H, P, Nc, 2).
+    Returns y (batch, L, H, P) and h_final (batch, H, P, Nc, 2), or per-unit
+    (n_units, L, P) / (n_units, P, Nc, 2) when (b, h) units are given.
+    """
+    x, dt, dt_bias, A_log, B, C, D, h0 = map(_f32, (x, dt, dt_bias, A_log, B, C, D, h0))
+    batch, L, H, P = x.shape
+    G, Nc = B.shape[2], B.shape[3]
+    assert G == ngroups and B.shape[4] == 2
+    uu, full = _units(units, batch, H)
+    nu = uu.shape[0]
+    y = np.empty((nu, L, P), np.float64)
+    hf = np.empty((nu, P, Nc, 2), np.float64)
+    _load().oracle_cssd_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                            _ptr(h0), batch, L, H, P, Nc, G, flags, _ptr(uu), nu, _ptr(y), _ptr(hf),
+                            nthreads or default_threads())
+    if full:
+        return (y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(),
+                hf.reshape(batch, H, P, Nc, 2))
+    return y, hf

@@ -1,0 +1,345 @@
+/*
+ * ssm_oracle.c -- plain, slow, fp64 CPU oracle for the forward selective
+ * state-space scans.  TEST INFRASTRUCTURE ONLY: it is loaded by the tests,
+ * by the package smoke check and by the CPU-baseline leg of the benchmark,
+ * never by the product path.  It shares no source, header, table or helper
+ * with the HIP library.
+ *
+ * Every function runs the sequential recurrence exactly as the pages define
+ * it, one independent unit at a time, in double precision:
+ *
+ *   S6 (per batch b, channel d, state n) -- builderforce-memory-engine
+ *   2026.6.18, dist/kernels/selective_scan.js, header comment and the
+ *   helpers softplus / discretise_A / discretise_B:
+ *       delta_t = softplus(dt[b,t,d] + dt_bias[d])
+ *       A       = -exp(A_log[d,n])
+ *       Abar    = exp(delta_t * A)
+ *       beta    = (Abar - 1)/A            (zero-order hold; = delta*phi1(delta*A))
+ *       h_t     = Abar*h_{t-1} + beta*B[b,t,n]*u[b,t,d]
+ *       y[b,t,d]= sum_n C[b,t,n]*h_t[n] + D[d]*u[b,t,d]
+ *
+ *   SSD (per batch b, head h, channel p, state n) -- same package,
+ *   dist/kernels/ssd.js, header comment and ssd_chunk_forward, read with
+ *   A = -exp(A_log[h]) and an input scale sigma_t (delta_t by default):
+ *       a_t     = delta_t * A_h
+ *       S_t     = exp(a_t)*S_{t-1} + sigma_t * x[b,t,h,p] * B[b,t,g,n]
+ *       y[b,t,h,p] = sum_n C[b,t,g,n]*S_t[p,n] + D[h]*x[b,t,h,p]
+ *     with group g = floor(h*G/H).
+ *
+ *   Complex SSD -- same package, src/kernels/complex_ssd.ts, header comment
+ *   and complex_ssd_forward: complex state per (p, n_c), complex decay
+ *   Abar = exp(delta*lambda_h), exponential-trapezoid input scale
+ *   beta = (Abar - 1)/lambda_h, output Re(C.h) + D x.
+ *
+ * The chunked decomposition the GPU uses is NOT here: the oracle is the
+ * definition, and the tests check the chunked algebra against it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <pthread.h>
+
+/* flag values of the library interface, restated here by value */
+#define OR_BBAR_MASK   0x3
+#define OR_BBAR_ZOH    0x0
+#define OR_BBAR_DT     0x1
+#define OR_BBAR_ONE    0x2
+#define OR_CPLX_MASK   0xC
+#define OR_CPLX_STABLE 0x0
+#define OR_CPLX_DOC    0x4
+#define OR_CPLX_CODE   0x8
+#define OR_CPLX_CONJ_C 0x10
+
+/* softplus(x) = log(1 + e^x), evaluated without overflow.  The pages write
+ * it as log(1 + exp(x)) (selective_scan.js and ssd.js, fn softplus); this
+ * is the same function. */
+static double sp(double x)
+{
+    return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+}
+
+/* phi1(z) = (e^z - 1)/z, phi1(0) = 1: the zero-order-hold factor, so that
+ * (exp(delta*A) - 1)/A = delta * phi1(delta*A) also at A = 0. */
+static double phi1(double z)
+{
+    return z == 0.0 ? 1.0 : expm1(z) / z;
+}
+
+/* ---------------------------------------------------------------- S6 --- */
+
+typedef struct {
+    const float *u, *dt, *dt_bias, *A_log, *B, *C, *D, *h0;
+    int64_t batch, L, Dm, N;
+    uint32_t flags;
+    const int64_t *units;   /* pairs (b, d) */
+    int64_t n_units;
+    double *y_out;          /* [n_units][L] */
+    double *hf_out;         /* [n_units][N] or NULL */
+} s6_job;
+
+static void s6_unit(const s6_job *j, int64_t k)
+{
+    const int64_t b = j->units[2 * k], d = j->units[2 * k + 1];
+    const int64_t L = j->L, Dm = j->Dm, N = j->N;
+    const int mode = (int)(j->flags & OR_BBAR_MASK);
+    double *A = (double *)malloc(sizeof(double) * (size_t)N);
+    double *h = (double *)malloc(sizeof(double) * (size_t)N);
+    for (int64_t n = 0; n < N; ++n) {
+        A[n] = -exp((double)j->A_log[d * N + n]);
+        h[n] = j->h0 ? (double)j->h0[(b * Dm + d) * N + n] : 0.0;
+    }
+    const double bias = j->dt_bias ? (double)j->dt_bias[d] : 0.0;
+    const double Dd = j->D ? (double)j->D[d] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t e = (b * L + t) * Dm + d;
+        const double delta = sp((double)j->dt[e] + bias);
+        const double uu = (double)j->u[e];
+        const float *Bt = j->B + (b * L + t) * N;
+        const float *Ct = j->C + (b * L + t) * N;
+        double yv = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double z = delta * A[n];
+            double beta;
+            if (mode == OR_BBAR_ZOH) beta = delta * phi1(z);
+            else if (mode == OR_BBAR_DT) beta = delta;
+            else beta = 1.0;
+            h[n] = exp(z) * h[n] + beta * (double)Bt[n] * uu;
+            yv += (double)Ct[n] * h[n];
+        }
+        j->y_out[k * L + t] = yv + Dd * uu;
+    }
+    if (j->hf_out)
+        for (int64_t n = 0; n < N; ++n) j->hf_out[k * N + n] = h[n];
+    free(A);
+    free(h);
+}
+
+/* ---------------------------------------------------------------- SSD --- */
+
+typedef struct {
+    const float *x, *dt, *dt_bias, *A_log, *B, *C, *D, *h0;
+    int64_t batch, L, H, P, N, G;
+    uint32_t flags;
+    const int64_t *units;   /* pairs (b, h) */
+    int64_t n_units;
+    double *y_out;          /* [n_units][L][P] */
+    double *hf_out;         /* [n_units][P][N] or NULL */
+} ssd_job;
+
+static void ssd_unit(const ssd_job *j, int64_t k)
+{
+    const int64_t b = j->units[2 * k], hh = j->units[2 * k + 1];
+    const int64_t L = j->L, H = j->H, P = j->P, N = j->N, G = j->G;
+    const int64_t g = hh * G / H;
+    const int mode = (int)(j->flags & OR_BBAR_MASK);
+    const double A = -exp((double)j->A_log[hh]);
+    const double bias = j->dt_bias ? (double)j->dt_bias[hh] : 0.0;
+    const double Dh = j->D ? (double)j->D[hh] : 0.0;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(P * N));
+    for (int64_t i = 0; i < P * N; ++i)
+        S[i] = j->h0 ? (double)j->h0[(b * H + hh) * P * N + i] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta = sp((double)j->dt[(b * L + t) * H + hh] + bias);
+        const double a = delta * A;
+        double sigma;
+        if (mode == OR_BBAR_DT) sigma = delta;
+        else if (mode == OR_BBAR_ZOH) sigma = delta * phi1(a);
+        else sigma = 1.0;
+        const double dec = exp(a);
+        const float *xt = j->x + ((b * L + t) * H + hh) * P;
+        const float *Bt = j->B + ((b * L + t) * G + g) * N;
+        const float *Ct = j->C + ((b * L + t) * G + g) * N;
+        double *yt = j->y_out + (k * L + t) * P;
+        for (int64_t p = 0; p < P; ++p) {
+            const double xv = (double)xt[p];
+            double *Sp = S + p * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                Sp[n] = dec * Sp[n] + sigma * xv * (double)Bt[n];
+                acc += (double)Ct[n] * Sp[n];
+            }
+            yt[p] = acc + Dh * xv;
+        }
+    }
+    if (j->hf_out) memcpy(j->hf_out + k * P * N, S, sizeof(double) * (size_t)(P * N));
+    free(S);
+}
+
+/* ------------------------------------------------------- complex SSD --- */
+
+typedef struct { double re, im; } cplx;
+
+static cplx cmul(cplx a, cplx b) { cplx r = {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; return r; }
+static cplx cdivc(cplx a, cplx b)
+{
+    const double den = b.re * b.re + b.im * b.im;
+    cplx r = {(a.re * b.re + a.im * b.im) / den, (a.im * b.re - a.re * b.im) / den};
+    return r;
+}
+static cplx cexp_(cplx w) { const double m = exp(w.re); cplx r = {m * cos(w.im), m * sin(w.im)}; return r; }
+/* e^w - 1 without cancellation: Re = expm1(x)cos(y) - 2 sin^2(y/2), Im = e^x sin(y) */
+static cplx cexpm1_(cplx w)
+{
+    const double s = sin(0.5 * w.im);
+    cplx r = {expm1(w.re) * cos(w.im) - 2.0 * s * s, exp(w.re) * sin(w.im)};
+    return r;
+}
+/* complex phi1(w) = (e^w - 1)/w, phi1(0) = 1 */
+static cplx cphi1(cplx w)
+{
+    if (w.re == 0.0 && w.im == 0.0) { cplx one = {1.0, 0.0}; return one; }
+    return cdivc(cexpm1_(w), w);
+}
+
+typedef struct {
+    const float *x, *dt, *dt_bias, *A_log, *B, *C, *D, *h0;
+    int64_t batch, L, H, P, Nc, G;
+    uint32_t flags;
+    const int64_t *units;
+    int64_t n_units;
+    double *y_out;          /* [n_units][L][P] */
+    double *hf_out;         /* [n_units][P][Nc][2] or NULL */
+} cssd_job;
+
+static void cssd_unit(const cssd_job *j, int64_t k)
+{
+    const int64_t b = j->units[2 * k], hh = j->units[2 * k + 1];
+    const int64_t L = j->L, H = j->H, P = j->P, Nc = j->Nc, G = j->G;
+    const int64_t g = hh * G / H;
+    const int bmode = (int)(j->flags & OR_BBAR_MASK);
+    const int amode = (int)(j->flags & OR_CPLX_MASK);
+    const int conj_c = (j->flags & OR_CPLX_CONJ_C) != 0;
+    const double ell = (double)j->A_log[2 * hh], phi = (double)j->A_log[2 * hh + 1];
+    const double bias = j->dt_bias ? (double)j->dt_bias[hh] : 0.0;
+    const double Dh = j->D ? (double)j->D[hh] : 0.0;
+    cplx lam;
+    if (amode == OR_CPLX_DOC) { lam.re = exp(ell) * cos(phi); lam.im = exp(ell) * sin(phi); }
+    else { lam.re = -exp(ell); lam.im = phi; }      /* stable reading */
+    cplx *S = (cplx *)malloc(sizeof(cplx) * (size_t)(P * Nc));
+    for (int64_t i = 0; i < P * Nc; ++i) {
+        if (j->h0) {
+            S[i].re = (double)j->h0[((b * H + hh) * P * Nc + i) * 2];
+            S[i].im = (double)j->h0[((b * H + hh) * P * Nc + i) * 2 + 1];
+        } else { S[i].re = 0.0; S[i].im = 0.0; }
+    }
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta = sp((double)j->dt[(b * L + t) * H + hh] + bias);
+        cplx abar, beta;
+        if (amode == OR_CPLX_CODE) {
+            /* the page kernel taken literally: Abar = exp(delta*log|A| + i*delta*arg A),
+             * beta = (Abar - 1) * exp(-log|A| - i*arg A) */
+            cplx w = {delta * ell, delta * phi};
+            cplx inv = {-ell, -phi};
+            abar = cexp_(w);
+            beta = cmul(cexpm1_(w), cexp_(inv));
+        } else {
+            cplx w = {delta * lam.re, delta * lam.im};
+            abar = cexp_(w);
+            if (bmode == OR_BBAR_ZOH) { cplx f = cphi1(w); beta.re = delta * f.re; beta.im = delta * f.im; }
+            else if (bmode == OR_BBAR_DT) { beta.re = delta; beta.im = 0.0; }
+            else { beta.re = 1.0; beta.im = 0.0; }
+        }
+        const float *xt = j->x + ((b * L + t) * H + hh) * P;
+        const float *Bt = j->B + ((b * L + t) * G + g) * Nc * 2;
+        const float *Ct = j->C + ((b * L + t) * G + g) * Nc * 2;
+        double *yt = j->y_out + (k * L + t) * P;
+        for (int64_t p = 0; p < P; ++p) {
+            const double xv = (double)xt[p];
+            cplx *Sp = S + p * Nc;
+            double acc = 0.0;
+            for (int64_t n = 0; n < Nc; ++n) {
+                cplx Bn = {(double)Bt[2 * n], (double)Bt[2 * n + 1]};
+                cplx inp = cmul(beta, Bn);
+                cplx hn = cmul(abar, Sp[n]);
+                hn.re += inp.re * xv;
+                hn.im += inp.im * xv;
+                Sp[n] = hn;
+                const double cr = (double)Ct[2 * n], ci = (double)Ct[2 * n + 1];
+                acc += conj_c ? (cr * hn.re + ci * hn.im) : (cr * hn.re - ci * hn.im);
+            }
+            yt[p] = acc + Dh * xv;
+        }
+    }
+    if (j->hf_out)
+        for (int64_t i = 0; i < P * Nc; ++i) {
+            j->hf_out[(k * P * Nc + i) * 2] = S[i].re;
+            j->hf_out[(k * P * Nc + i) * 2 + 1] = S[i].im;
+        }
+    free(S);
+}
+
+/* ------------------------------------------------------------ threads --- */
+
+typedef struct {
+    int kind;               /* 0 S6, 1 SSD, 2 complex */
+    const void *job;
+    int64_t n_units;
+    int tid, nthreads;
+} worker_arg;
+
+static void *worker(void *p)
+{
+    const worker_arg *w = (const worker_arg *)p;
+    for (int64_t k = w->tid; k < w->n_units; k += w->nthreads) {
+        if (w->kind == 0) s6_unit((const s6_job *)w->job, k);
+        else if (w->kind == 1) ssd_unit((const ssd_job *)w->job, k);
+        else cssd_unit((const cssd_job *)w->job, k);
+    }
+    return NULL;
+}
+
+static void run_units(int kind, const void *job, int64_t n_units, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > n_units) nthreads = (int)(n_units > 0 ? n_units : 1);
+    pthread_t th[256];
+    worker_arg args[256];
+    for (int i = 0; i < nthreads; ++i) {
+        args[i].kind = kind; args[i].job = job; args[i].n_units = n_units;
+        args[i].tid = i; args[i].nthreads = nthreads;
+    }
+    if (nthreads == 1) { worker(&args[0]); return; }
+    for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, worker, &args[i]);
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+}
+
+/* ------------------------------------------------------------ exports --- */
+
+void oracle_s6_fwd(const float *u, const float *dt, const float *dt_bias, const float *A_log,
+                   const float *B, const float *C, const float *D, const float *h0,
+                   int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, uint32_t flags,
+                   const int64_t *units, int64_t n_units, double *y_out, double *hf_out,
+                   int nthreads)
+{
+    s6_job j = {u, dt, dt_bias, A_log, B, C, D, h0, batch, L, d_inner, d_state, flags,
+                units, n_units, y_out, hf_out};
+    run_units(0, &j, n_units, nthreads);
+}
+
+void oracle_ssd_fwd(const float *x, const float *dt, const float *dt_bias, const float *A_log,
+                    const float *B, const float *C, const float *D, const float *h0,
+                    int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                    int64_t ngroups, uint32_t flags, const int64_t *units, int64_t n_units,
+                    double *y_out, double *hf_out, int nthreads)
+{
+    ssd_job j = {x, dt, dt_bias, A_log, B, C, D, h0, batch, L, nheads, headdim, d_state, ngroups,
+                 flags, units, n_units, y_out, hf_out};
+    run_units(1, &j, n_units, nthreads);
+}
+
+void oracle_cssd_fwd(const float *x, const float *dt, const float *dt_bias, const float *A_log,
+                     const float *B, const float *C, const float *D, const float *h0,
+                     int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t n_complex,
+                     int64_t ngroups, uint32_t flags, const int64_t *units, int64_t n_units,
+                     double *y_out, double *hf_out, int nthreads)
+{
+    cssd_job j = {x, dt, dt_bias, A_log, B, C, D, h0, batch, L, nheads, headdim, n_complex, ngroups,
+                  flags, units, n_units, y_out, hf_out};
+    run_units(2, &j, n_units, nthreads);
+}
+
+/* elementary functions, exported so the tests can pin them on their own */
+double oracle_softplus(double x) { return sp(x); }
+double oracle_phi1(double z) { return phi1(z); }
