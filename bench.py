@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the forward selective-scan hot path on one MI355X.
+
+A step is one call of the scan entry point over one batch of synthetic input
+already resident in HBM (for S6: softplus, discretisation, recurrence, state
+reduction and skip term, all inside one kernel).  The headline workload is the
+S6 scan at a Mamba-1 layer shape (batch 8, L 2048, d_inner 1536, N 16, fp32);
+the SSD and complex-SSD workloads are measured the same way and reported under
+"secondary".  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (no sparsity), TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, non-packed fp32
+N_ROTATE = 3                     # input copies rotated between steps (> Infinity Cache)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def s6_model(d):
+    """Algorithmic bytes and operations of one S6 call."""
+    B, L, D, N = d["batch"], d["L"], d["d_inner"], d["d_state"]
+    elems = B * L * D
+    isz = 4
+    bytes_ = elems * (isz + 4 + 4) + 2 * B * L * N * isz + D * N * 4 + 2 * D * 4 + B * D * N * 4
+    ops = elems * N * 10           # per (b,t,d,n): 9 flops + 1 exp
+    return elems, bytes_, ops
+
+
+def ssd_model(d):
+    B, L, H, P, N, G, Q = (d["batch"], d["L"], d["nheads"], d["headdim"], d["d_state"], d["ngroups"],
+                           d["chunk_len"])
+    elems = B * L * H * P
+    nc = -(-L // Q)
+    bytes_ = elems * 2 + 2 * B * L * G * N * 2 + B * L * H * 4 + elems * 4 + B * H * P * N * 4
+    # dense-square MFMA flops: C.B^T once per (b, chunk, group); (G o L) X, chunk states and
+    # state->output per (b, chunk, head)
+    flops = 2 * B * nc * (G * Q * Q * N + H * (Q * Q * P + 2 * Q * P * N))
+    return elems, bytes_, flops
+
+
+def cssd_model(d):
+    B, L, H, P, Nc, G, Q = (d["batch"], d["L"], d["nheads"], d["headdim"], d["n_complex"],
+                            d["ngroups"], d["chunk_len"])
+    elems = B * L * H * P
+    bytes_ = elems * 4 * 2 + 2 * B * L * G * Nc * 8 + B * L * H * 4 + B * H * P * Nc * 8
+    nc = -(-L // Q)
+    flops = 2 * B * nc * H * (4 * Q * Q * Nc + Q * Q * P + 2 * 4 * Q * P * Nc)
+    return elems, bytes_, flops
+
+
+def make_runner(name, dev):
+    """Returns (step_fn(i), dims, kernel names) with N_ROTATE resident input copies."""
+    import torch
+    import selective_state_space_s6_amd as lib
+    import synth
+    w = dict(synth.WORKLOADS[name])
+    kind = w["kind"]
+    copies = []
+    for r in range(N_ROTATE):
+        inp = synth.workload_inputs(name, seed=(r,))
+        copies.append(inp.torch(dev))
+        dims = inp.dims
+    if kind == "s6":
+        t0 = copies[0]
+        y = torch.empty_like(t0["u"], dtype=torch.float32)
+        hf = torch.empty((dims["batch"], dims["d_inner"], dims["d_state"]), dtype=torch.float32, device=dev)
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            lib.ssm_s6_scan_fwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                None, y=y, h_final=hf)
+        return step, dims, w, ["s6_scan_kernel"]
+    if kind == "ssd":
+        t0 = copies[0]
+        y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
+        hf = torch.empty((dims["batch"], dims["nheads"], dims["headdim"], dims["d_state"]),
+                         dtype=torch.float32, device=dev)
+        ws = torch.empty(lib.ssd_chunk_scan_fwd_workspace_size(
+            dims["batch"], dims["L"], dims["nheads"], dims["headdim"], dims["d_state"],
+            dims["ngroups"], w["chunk_len"]), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            lib.ssd_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                   None, chunk_len=w["chunk_len"], y=y, h_final=hf, workspace=ws)
+        return step, dims, w, ["ssd_chunk_state_kernel", "ssd_state_pass_kernel", "ssd_chunk_scan_kernel"]
+    t0 = copies[0]
+    y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
+    hf = torch.empty((dims["batch"], dims["nheads"], dims["headdim"], dims["n_complex"], 2),
+                     dtype=torch.float32, device=dev)
+    ws = torch.empty(lib.ssd_cplx_chunk_scan_fwd_workspace_size(
+        dims["batch"], dims["L"], dims["nheads"], dims["headdim"], dims["n_complex"],
+        dims["ngroups"], w["chunk_len"]), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        t = copies[i % N_ROTATE]
+        lib.ssd_cplx_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                    None, chunk_len=w["chunk_len"], y=y, h_final=hf, workspace=ws)
+    return step, dims, w, ["cssd_chunk_state_kernel", "cssd_state_pass_kernel", "cssd_chunk_scan_kernel"]
+
+
+def time_steps(step, steps, warmup):
+    """Warmup, then time exactly `steps` steps between two device synchronisations.
+    Per-step HIP events on the launch stream give the per-launch durations."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record()
+        step(warmup + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in evs]   # ms
+    return wall, per
+
+
+def cpu_baseline_s6(name):
+    """The fp64 oracle, untuned, on the host cores: the whole workload."""
+    import numpy as np
+    import oracle
+    import synth
+    inp = synth.workload_inputs(name, seed=(0,))
+    d = inp.dims
+    nthr = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.s6_fwd(**inp.arrays, nthreads=nthr)
+    sec = time.perf_counter() - t0
+    elems = d["batch"] * d["L"] * d["d_inner"]
+    return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
+            "sample": f"whole {name} workload ({elems} elements, fp64, {sec:.2f} s wall on {nthr} threads)"}
+
+
+def cpu_baseline_units(name, n_units):
+    """The fp64 oracle on a bounded sample of (b, h) units of an SSD-type workload."""
+    import numpy as np
+    import oracle
+    import synth
+    inp = synth.workload_inputs(name, seed=(0,))
+    d = inp.dims
+    w = synth.WORKLOADS[name]
+    nthr = oracle.default_threads()
+    n_units = min(n_units, d["batch"] * d["nheads"])
+    units = np.stack([np.arange(n_units) % d["batch"], np.arange(n_units) // d["batch"]], 1)
+    fn = oracle.ssd_fwd if w["kind"] == "ssd" else oracle.cssd_fwd
+    t0 = time.perf_counter()
+    fn(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
+    sec = time.perf_counter() - t0
+    elems = n_units * d["L"] * d["headdim"]
+    return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{n_units} of {d['batch'] * d['nheads']} (b, head) units of {name} "
+                      f"({elems} elements, {sec:.2f} s wall)"}
+
+
+def measure(name, dev, steps, warmup):
+    step, dims, w, kernels = make_runner(name, dev)
+    wall, per = time_steps(step, steps, warmup)
+    ms = wall * 1e3 / steps
+    kind = w["kind"]
+    dims = dict(dims, chunk_len=w.get("chunk_len"))
+    if kind == "s6":
+        elems, bytes_, ops = s6_model(dims)
+    elif kind == "ssd":
+        elems, bytes_, ops = ssd_model(dims)
+    else:
+        elems, bytes_, ops = cssd_model(dims)
+    ev_ms = sorted(per)[len(per) // 2]
+    return dict(name=name, kind=kind, dims=dims, dtype=w["dtype"], ms=ms, event_ms_median=ev_ms,
+                event_ms=per, elems=elems, bytes=bytes_, ops=ops, kernels=kernels)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="s6_mamba1")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); the scan "
+              "shards over batch and heads with no communication, and no multi-GPU path exists here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    import synth
+
+    log(f"[bench] headline {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    m = measure(args.workload, dev, args.steps, args.warmup)
+    kind = m["kind"]
+    ev_s = m["event_ms_median"] * 1e-3
+    gbs = m["bytes"] / ev_s / 1e9
+    if kind == "s6":
+        roof = {"bound": "alu", "achieved": round(m["ops"] / ev_s / 1e12, 3),
+                "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(m["ops"] / ev_s / 1e12 / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "s6_scan_kernel", "kernel_ms": round(m["event_ms_median"], 5),
+                "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "+".join(m["kernels"]), "kernel_ms": round(m["event_ms_median"], 5)}
+    value = m["elems"] / (m["ms"] * 1e-3)
+    out = {
+        "metric": "scan elements/s (batch*L*d_inner)",
+        "value": round(value, 1),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if m["dtype"] == "f32" else "bf16-in/f32-acc",
+        "data": "synthetic",
+        "config": {"workload": args.workload, **{k: v for k, v in m["dims"].items() if v is not None}},
+        "roofline": roof,
+    }
+    if not args.no_secondary and args.workload == "s6_mamba1":
+        sec = []
+        for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5)):
+            log(f"[bench] secondary {name}")
+            s = measure(name, dev, steps, 2)
+            es = s["event_ms_median"] * 1e-3
+            ent = {"workload": name, "value": round(s["elems"] / (s["ms"] * 1e-3), 1),
+                   "unit": "elements/s", "ms_per_step": round(s["ms"], 4),
+                   "hbm_GBps": round(s["bytes"] / es / 1e9, 1),
+                   "hbm_frac": round(s["bytes"] / es / 1e9 / HBM_PEAK_GBS, 4)}
+            if s["kind"] == "ssd":
+                ent["mfma_TFLOPs"] = round(s["ops"] / es / 1e12, 1)
+                ent["mfma_frac_bf16"] = round(s["ops"] / es / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+            else:
+                ent["fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
+            sec.append(ent)
+            del s
+            torch.cuda.empty_cache()
+        out["secondary"] = sec
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        if kind == "s6":
+            out["cpu_baseline"] = cpu_baseline_s6(args.workload)
+        else:
+            out["cpu_baseline"] = cpu_baseline_units(args.workload, 16)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * ssm_scan.h -- C interface of libssmscan.so, the MI355X (gfx950) forward
+ * selective state-space scan library.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor is a caller-owned, contiguous, row-major device buffer on
+ *    the current HIP device.  The library allocates and frees nothing and
+ *    never synchronises; work is enqueued on `stream` and the call returns.
+ *    A device fault therefore surfaces at the caller's next synchronisation.
+ *  - Arguments are validated before any HIP call.  On a bad argument the
+ *    function returns a negative ssm_status_t and nothing is launched;
+ *    ssm_last_error() then holds "<entry point or kernel>: <reason>".
+ *  - Optional inputs (dt_bias, D, h0) may be NULL, meaning zero.  h_final may
+ *    be NULL (not written).  h0 == h_final is allowed (the state is carried
+ *    in place); y must not alias any input.
+ *  - All pointers must be 16-byte aligned (torch allocations are).
+ *  - dt is the raw time step before softplus: delta = softplus(dt + dt_bias)
+ *    is formed inside the kernels, exactly once.
+ *  - Results are bitwise reproducible run to run (no floating-point atomics).
+ *
+ * Citations name the page and the section (source file and function) of the
+ * prior art that defines each operation:
+ *   [BF-S6]   @seanhogg/builderforce-memory-engine 2026.6.18,
+ *             package/dist/kernels/selective_scan.js (header comment,
+ *             softplus, discretise_A, discretise_B, forward_scan,
+ *             forward_reduce)
+ *   [BF-SSD]  same package, package/dist/kernels/ssd.js and ssd.d.ts
+ *             (header comment, ssd_chunk_forward)
+ *   [BF-CSSD] same package, package/src/kernels/complex_ssd.ts (header
+ *             comment, et_bbar_re/et_bbar_im, complex_ssd_forward)
+ *   [RS-M1]   mamba-rs 0.4.0, src/mamba_ssm/gpu/forward.rs
+ *             (gpu_forward_mamba_layer, step F4d, and GpuMambaDims)
+ *   [RS-M3]   mamba-rs 0.2.1, src/mamba3_siso/gpu/mamba3_gpu.rs
+ *             (gpu_forward_mamba3_layer, step F6, kernels K2-K5 and the
+ *             final-state writeback)
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of the large inputs (u or x, B, C); everything else is fp32 */
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_INVALID_ARG = -1,  /* NULL required pointer, dim <= 0, H % G != 0, ... */
+    SSM_ERR_UNSUPPORTED = -2,  /* a size or alignment outside what the kernels support */
+    SSM_ERR_WORKSPACE = -3,    /* workspace missing or smaller than *_workspace_size() */
+    SSM_ERR_HIP = -4           /* a launch failed; the message carries hipGetErrorString */
+} ssm_status_t;
+
+/* flags bit-field.
+ * Bits 0-1 pick the input scale that multiplies B_t * u_t:
+ *   SSM_BBAR_ZOH  exact zero-order hold, (exp(delta*A) - 1)/A  [BF-S6 discretise_B;
+ *                 for A -> 0 it tends to delta]
+ *   SSM_BBAR_DT   delta (the first-order limit of the hold)  [BF-S6 comment on
+ *                 discretise; RS-M3 gamma = dt at trap = 1]
+ *   SSM_BBAR_ONE  1 (B_t * x_t unscaled, as the SSD page kernel writes it) [BF-SSD]
+ * Bits 2-3 pick how the complex entry point reads A_log[h] = [l, phi]:
+ *   SSM_CPLX_STABLE  lambda = -exp(l) + i*phi  (decay times rotation; stable)
+ *   SSM_CPLX_DOC     lambda = exp(l) * exp(i*phi)  (the page's header comment)
+ *   SSM_CPLX_CODE    Abar = exp(delta*(l + i*phi)), beta = (Abar - 1)*exp(-l - i*phi)
+ *                    (the page kernel taken literally)
+ * Bit 4: SSM_CPLX_CONJ_C gives y = Re(conj(C).h) instead of Re(C.h). */
+#define SSM_BBAR_ZOH    0x0u
+#define SSM_BBAR_DT     0x1u
+#define SSM_BBAR_ONE    0x2u
+#define SSM_CPLX_STABLE 0x0u
+#define SSM_CPLX_DOC    0x4u
+#define SSM_CPLX_CODE   0x8u
+#define SSM_CPLX_CONJ_C 0x10u
+
+/* Largest state size any entry point accepts. */
+#define SSM_MAX_D_STATE 256
+
+/* Message of the last failing call made by this thread ("" if none). */
+const char *ssm_last_error(void);
+
+/* ------------------------------------------------------------------ S6 ----
+ * Mamba-1 selective scan with a diagonal state per channel [BF-S6 header,
+ * forward_scan, forward_reduce; RS-M1 F4d]:
+ *   delta[b,t,d] = softplus(dt[b,t,d] + dt_bias[d])
+ *   A[d,n]       = -exp(A_log[d,n])
+ *   h_t[n]       = exp(delta*A[d,n]) * h_{t-1}[n] + beta(delta, A[d,n]) * B[b,t,n] * u[b,t,d]
+ *   y[b,t,d]     = sum_n C[b,t,n] * h_t[n] + D[d] * u[b,t,d]
+ * with h_{-1} = h0 (or 0) and h_final = h_{L-1}.  beta follows flags bits 0-1
+ * (default SSM_BBAR_ZOH).  B and C are shared by all channels.
+ *
+ * Layouts: u (batch, L, d_inner) [in_dtype]; dt (batch, L, d_inner) fp32;
+ * dt_bias, D (d_inner) fp32; A_log (d_inner, d_state) fp32;
+ * B, C (batch, L, d_state) [in_dtype]; y (batch, L, d_inner) fp32;
+ * h0, h_final (batch, d_inner, d_state) fp32.
+ * Limits: 1 <= d_state <= 256; any L >= 1.  No workspace is needed
+ * (ssm_s6_scan_fwd_workspace_size returns 0; workspace may be NULL). */
+size_t ssm_s6_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state);
+
+int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                    const void *B, const void *C, const float *D, float *y,
+                    const float *h0, float *h_final,
+                    int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                    ssm_dtype_t in_dtype, uint32_t flags,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------- SSD ----
+ * Mamba-2 state-space dual scan with a scalar A per head [BF-SSD header and
+ * ssd_chunk_forward; RS-M3 F6 K2-K5]:
+ *   delta[b,t,h] = softplus(dt[b,t,h] + dt_bias[h]),  a = delta * A_h,  A_h = -exp(A_log[h])
+ *   S_t[p,n]     = exp(a) * S_{t-1}[p,n] + sigma_t * x[b,t,h,p] * B[b,t,g,n]
+ *   y[b,t,h,p]   = sum_n C[b,t,g,n] * S_t[p,n] + D[h] * x[b,t,h,p]
+ * with group g = floor(h * ngroups / nheads), S_{-1} = h0 (or 0) and
+ * h_final = S_{L-1}.  sigma follows flags bits 0-1 (default SSM_BBAR_DT,
+ * i.e. sigma = delta).  The sequence is cut into chunks of chunk_len steps (the
+ * last may be partial); the result does not depend on chunk_len beyond
+ * rounding.
+ *
+ * Layouts: x (batch, L, nheads, headdim) bf16; dt (batch, L, nheads) fp32;
+ * dt_bias, A_log, D (nheads) fp32; B, C (batch, L, ngroups, d_state) bf16;
+ * y (batch, L, nheads, headdim) fp32; h0, h_final (batch, nheads, headdim, d_state) fp32.
+ * in_dtype must be SSM_BF16 (the contractions run on bf16 MFMA; SSM_F32 returns
+ * SSM_ERR_UNSUPPORTED).  Limits: nheads % ngroups == 0; headdim in {32, 64, 128};
+ * d_state a multiple of 32, <= 256; chunk_len in {64, 128, 256}.
+ * Workspace: ssd_chunk_scan_fwd_workspace_size() bytes (chunk states). */
+size_t ssd_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                         int64_t d_state, int64_t ngroups, int64_t chunk_len);
+
+int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, const float *A_log,
+                       const void *B, const void *C, const float *D, float *y,
+                       const float *h0, float *h_final,
+                       int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                       int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------- complex SSD ----
+ * Mamba-3-style SSD with a complex diagonal state [BF-CSSD header,
+ * et_bbar_re/et_bbar_im, complex_ssd_forward]:
+ *   lambda_h from A_log[h] = [l, phi] per flags bits 2-3 (default STABLE)
+ *   Abar_t   = exp(delta_t * lambda_h),  beta_t = (Abar_t - 1)/lambda_h  (exact ET)
+ *   h_t[p,n] = Abar_t * h_{t-1}[p,n] + beta_t * B[b,t,g,n] * x[b,t,h,p]   (complex)
+ *   y[b,t,h,p] = Re(sum_n C[b,t,g,n] * h_t[p,n]) + D[h] * x[b,t,h,p]
+ * flags bits 0-1 may replace beta by delta (DT) or 1 (ONE); SSM_CPLX_CONJ_C
+ * uses conj(C).
+ *
+ * Layouts (all fp32): x (batch, L, nheads, headdim); dt (batch, L, nheads);
+ * dt_bias, D (nheads); A_log (nheads, 2); B, C (batch, L, ngroups, n_complex, 2)
+ * interleaved (re, im); y (batch, L, nheads, headdim);
+ * h0, h_final (batch, nheads, headdim, n_complex, 2).
+ * Limits: nheads % ngroups == 0; headdim in {32, 64, 128}; n_complex a
+ * multiple of 8, <= 128; chunk_len in {32, 64, 128}.
+ * Workspace: ssd_cplx_chunk_scan_fwd_workspace_size() bytes. */
+size_t ssd_cplx_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads,
+                                              int64_t headdim, int64_t n_complex, int64_t ngroups,
+                                              int64_t chunk_len);
+
+int ssd_cplx_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bias,
+                            const float *A_log, const float *B, const float *C, const float *D,
+                            float *y, const float *h0, float *h_final,
+                            int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                            int64_t n_complex, int64_t ngroups, int64_t chunk_len, uint32_t flags,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,216 @@
+"""MI355X-native forward selective state-space scans (S6, SSD, complex SSD).
+
+Thin Python binding over ``libssmscan.so`` (include/ssm_scan.h).  The functions
+carry the names of the C entry points and only marshal arguments: they check
+dtypes, shapes and contiguity, allocate outputs and workspace with torch (when
+the caller does not pass them), and hand device pointers plus the current HIP
+stream to the library.  Every step of the computation runs in the HIP kernels;
+there is no fallback path: if the library is missing, importing this package
+fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "ssm_s6_scan_fwd", "ssd_chunk_scan_fwd", "ssd_cplx_chunk_scan_fwd",
+    "ssm_s6_scan_fwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
+    "ssd_cplx_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
+    "SSM_BBAR_ZOH", "SSM_BBAR_DT", "SSM_BBAR_ONE", "SSM_CPLX_STABLE", "SSM_CPLX_DOC",
+    "SSM_CPLX_CODE", "SSM_CPLX_CONJ_C", "SSM_F32", "SSM_BF16",
+]
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_BBAR_ZOH, SSM_BBAR_DT, SSM_BBAR_ONE = 0x0, 0x1, 0x2
+SSM_CPLX_STABLE, SSM_CPLX_DOC, SSM_CPLX_CODE, SSM_CPLX_CONJ_C = 0x0, 0x4, 0x8, 0x10
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssmscan.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m selective_state_space_s6_amd.build` "
+        "(there is no non-HIP fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I, _Z = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+_lib.ssm_last_error.restype = ctypes.c_char_p
+_lib.ssm_s6_scan_fwd_workspace_size.argtypes = [_I] * 4
+_lib.ssm_s6_scan_fwd_workspace_size.restype = _Z
+_lib.ssm_s6_scan_fwd.argtypes = [_P] * 10 + [_I] * 4 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
+_lib.ssm_s6_scan_fwd.restype = ctypes.c_int
+_lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
+_lib.ssd_chunk_scan_fwd_workspace_size.restype = _Z
+_lib.ssd_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
+_lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
+_lib.ssd_cplx_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
+_lib.ssd_cplx_chunk_scan_fwd_workspace_size.restype = _Z
+_lib.ssd_cplx_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_uint32, _P, _Z, _P]
+_lib.ssd_cplx_chunk_scan_fwd.restype = ctypes.c_int
+
+
+class SsmError(RuntimeError):
+    """A library call returned a negative status; ``code`` holds it."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def ssm_last_error() -> str:
+    return _lib.ssm_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise SsmError(rc, ssm_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _req(t, name, dtype, shape, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _opt(t, name, dtype, shape, device):
+    return None if t is None else _req(t, name, dtype, shape, device)
+
+
+def _in_dtype(t):
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"input dtype {t.dtype}: expected float32 or bfloat16")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def ssm_s6_scan_fwd_workspace_size(batch, L, d_inner, d_state) -> int:
+    return int(_lib.ssm_s6_scan_fwd_workspace_size(batch, L, d_inner, d_state))
+
+
+def ssd_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups, chunk_len) -> int:
+    return int(_lib.ssd_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups,
+                                                      chunk_len))
+
+
+def ssd_cplx_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, n_complex, ngroups,
+                                           chunk_len) -> int:
+    return int(_lib.ssd_cplx_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, n_complex,
+                                                           ngroups, chunk_len))
+
+
+def ssm_s6_scan_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, *, flags=SSM_BBAR_ZOH,
+                    return_final=False, y=None, h_final=None):
+    """S6 forward scan.  u (batch, L, d_inner) fp32|bf16; dt fp32 (same shape);
+    dt_bias, D (d_inner) fp32 or None; A_log (d_inner, d_state) fp32;
+    B, C (batch, L, d_state) in u's dtype; h0 (batch, d_inner, d_state) fp32 or None.
+    Returns y (fp32), or (y, h_final) when return_final."""
+    dev = u.device
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    dty = u.dtype
+    _req(u, "u", dty, (batch, L, Dm), dev)
+    _req(dt, "dt", torch.float32, (batch, L, Dm), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (Dm,), dev)
+    _req(A_log, "A_log", torch.float32, (Dm, N), dev)
+    _req(B, "B", dty, (batch, L, N), dev)
+    _req(C, "C", dty, (batch, L, N), dev)
+    _opt(D, "D", torch.float32, (Dm,), dev)
+    _opt(h0, "h0", torch.float32, (batch, Dm, N), dev)
+    if y is None:
+        y = torch.empty((batch, L, Dm), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, (batch, L, Dm), dev)
+    if return_final and h_final is None:
+        h_final = torch.empty((batch, Dm, N), dtype=torch.float32, device=dev)
+    _opt(h_final, "h_final", torch.float32, (batch, Dm, N), dev)
+    rc = _lib.ssm_s6_scan_fwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                              _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L, Dm, N,
+                              _in_dtype(u), flags, None, 0, _stream(dev))
+    _check(rc)
+    return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ssd_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=256,
+                       flags=SSM_BBAR_DT, return_final=False, y=None, h_final=None, workspace=None):
+    """SSD chunked forward scan.  x (batch, L, H, P) bf16; dt (batch, L, H) fp32;
+    dt_bias, A_log, D (H,) fp32 (dt_bias, D may be None); B, C (batch, L, G, N) in x's
+    dtype; h0 (batch, H, P, N) fp32 or None.  Returns y fp32 (and h_final)."""
+    dev = x.device
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dty = x.dtype
+    _req(x, "x", dty, (batch, L, H, P), dev)
+    _req(dt, "dt", torch.float32, (batch, L, H), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    _req(A_log, "A_log", torch.float32, (H,), dev)
+    _req(B, "B", dty, (batch, L, G, N), dev)
+    _req(C, "C", dty, (batch, L, G, N), dev)
+    _opt(D, "D", torch.float32, (H,), dev)
+    _opt(h0, "h0", torch.float32, (batch, H, P, N), dev)
+    if y is None:
+        y = torch.empty((batch, L, H, P), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, (batch, L, H, P), dev)
+    if return_final and h_final is None:
+        h_final = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    _opt(h_final, "h_final", torch.float32, (batch, H, P, N), dev)
+    ws = ssd_chunk_scan_fwd_workspace_size(batch, L, H, P, N, G, chunk_len)
+    if workspace is None:
+        workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+    rc = _lib.ssd_chunk_scan_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L, H, P, N, G,
+                                 chunk_len, _in_dtype(x), flags, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ssd_cplx_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=64,
+                            flags=SSM_BBAR_ZOH | SSM_CPLX_STABLE, return_final=False, y=None,
+                            h_final=None, workspace=None):
+    """Complex-state SSD forward scan.  x (batch, L, H, P) fp32; dt (batch, L, H);
+    A_log (H, 2) = [log|A|, arg A]; B, C (batch, L, G, Nc, 2) fp32 interleaved (re, im);
+    h0 (batch, H, P, Nc, 2) or None.  Returns y (and h_final)."""
+    dev = x.device
+    batch, L, H, P = x.shape
+    G, Nc = B.shape[2], B.shape[3]
+    f32 = torch.float32
+    _req(x, "x", f32, (batch, L, H, P), dev)
+    _req(dt, "dt", f32, (batch, L, H), dev)
+    _opt(dt_bias, "dt_bias", f32, (H,), dev)
+    _req(A_log, "A_log", f32, (H, 2), dev)
+    _req(B, "B", f32, (batch, L, G, Nc, 2), dev)
+    _req(C, "C", f32, (batch, L, G, Nc, 2), dev)
+    _opt(D, "D", f32, (H,), dev)
+    _opt(h0, "h0", f32, (batch, H, P, Nc, 2), dev)
+    if y is None:
+        y = torch.empty((batch, L, H, P), dtype=f32, device=dev)
+    _req(y, "y", f32, (batch, L, H, P), dev)
+    if return_final and h_final is None:
+        h_final = torch.empty((batch, H, P, Nc, 2), dtype=f32, device=dev)
+    _opt(h_final, "h_final", f32, (batch, H, P, Nc, 2), dev)
+    ws = ssd_cplx_chunk_scan_fwd_workspace_size(batch, L, H, P, Nc, G, chunk_len)
+    if workspace is None:
+        workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+    rc = _lib.ssd_cplx_chunk_scan_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B),
+                                      _ptr(C), _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L,
+                                      H, P, Nc, G, chunk_len, flags, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return (y, h_final) if (return_final or h_final is not None) else y

@@ -1,0 +1,200 @@
+// abi.hip -- the extern "C" boundary of libssmscan.so (declared in
+// include/ssm_scan.h): argument validation, workspace sizing, error strings,
+// and dispatch to the kernel launchers.  Every check runs before any HIP call.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdarg.h>
+#include <string.h>
+
+#include "../../include/ssm_scan.h"
+#include "launchers.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE_PTR(entry, p)                                                        \
+    do {                                                                             \
+        if ((p) == nullptr) return fail(SSM_ERR_INVALID_ARG, "%s: %s is NULL", entry, #p); \
+    } while (0)
+#define REQUIRE_POS(entry, v)                                                                  \
+    do {                                                                                       \
+        if ((v) <= 0) return fail(SSM_ERR_INVALID_ARG, "%s: %s must be > 0 (got %lld)", entry, \
+                                  #v, (long long)(v));                                         \
+    } while (0)
+#define REQUIRE_ALIGN(entry, p)                                                                 \
+    do {                                                                                        \
+        if (!aligned16(p)) return fail(SSM_ERR_UNSUPPORTED, "%s: %s is not 16-byte aligned", \
+                                       entry, #p);                                              \
+    } while (0)
+
+int launched(const char *entry, hipError_t e, const char *kernel) {
+    if (e != hipSuccess)
+        return fail(SSM_ERR_HIP, "%s: launch of %s failed: %s", entry, kernel, hipGetErrorString(e));
+    g_err[0] = '\0';
+    return SSM_OK;
+}
+
+// elements of a tensor must stay addressable with 64-bit offsets and the grid
+// with 32-bit block counts
+bool too_big(int64_t a, int64_t b, int64_t c, int64_t d) {
+    const double n = (double)a * (double)b * (double)c * (double)d;
+    return n > 9.0e15;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ssm_last_error(void) { return g_err; }
+
+size_t ssm_s6_scan_fwd_workspace_size(int64_t, int64_t, int64_t, int64_t) { return 0; }
+
+int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                    const void *B, const void *C, const float *D, float *y,
+                    const float *h0, float *h_final,
+                    int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                    ssm_dtype_t in_dtype, uint32_t flags,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace; (void)workspace_bytes;
+    const char *E = "ssm_s6_scan_fwd";
+    REQUIRE_PTR(E, u); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
+    REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
+    REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, d_inner); REQUIRE_POS(E, d_state);
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if ((flags & ~0x3u) != 0 || (flags & 0x3u) == 0x3u)
+        return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x: only SSM_BBAR_ZOH/DT/ONE apply", E, flags);
+    if (d_state > SSM_MAX_D_STATE)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld > %d", E, (long long)d_state, SSM_MAX_D_STATE);
+    if (too_big(batch, L, d_inner, 1) || batch * ((d_inner + 255) / 16) > 0x7fffffffLL)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    REQUIRE_ALIGN(E, u); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
+    REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
+    REQUIRE_ALIGN(E, h0); REQUIRE_ALIGN(E, h_final);
+    if ((const void *)y == u || (const void *)y == (const void *)dt || (const void *)y == B ||
+        (const void *)y == C)
+        return fail(SSM_ERR_INVALID_ARG, "%s: y aliases an input", E);
+    ssm::S6Args a{u, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, d_inner, d_state,
+                  in_dtype == SSM_BF16, flags};
+    const char *kn = "s6";
+    return launched(E, ssm::launch_s6(a, stream, &kn), kn);
+}
+
+static int ssd_check_shape(const char *E, int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                           int64_t d_state, int64_t ngroups, int64_t chunk_len) {
+    REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, nheads); REQUIRE_POS(E, headdim);
+    REQUIRE_POS(E, d_state); REQUIRE_POS(E, ngroups); REQUIRE_POS(E, chunk_len);
+    if (nheads % ngroups != 0)
+        return fail(SSM_ERR_INVALID_ARG, "%s: nheads %lld is not a multiple of ngroups %lld", E,
+                    (long long)nheads, (long long)ngroups);
+    if (too_big(batch, L, nheads, headdim) || too_big(batch, L, ngroups, d_state))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    return SSM_OK;
+}
+
+size_t ssd_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                         int64_t d_state, int64_t ngroups, int64_t chunk_len) {
+    (void)ngroups;
+    if (batch <= 0 || L <= 0 || nheads <= 0 || headdim <= 0 || d_state <= 0 || chunk_len <= 0) return 0;
+    return ssm::ssd_workspace_bytes(batch, L, nheads, headdim, d_state, chunk_len);
+}
+
+int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, const float *A_log,
+                       const void *B, const void *C, const float *D, float *y,
+                       const float *h0, float *h_final,
+                       int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                       int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssd_chunk_scan_fwd";
+    REQUIRE_PTR(E, x); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
+    REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
+    int rc = ssd_check_shape(E, batch, L, nheads, headdim, d_state, ngroups, chunk_len);
+    if (rc != SSM_OK) return rc;
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if (in_dtype != SSM_BF16)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: the MFMA path takes bf16 x, B, C (SSM_BF16)", E);
+    if ((flags & ~0x3u) != 0 || (flags & 0x3u) == 0x3u)
+        return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x: only SSM_BBAR_ZOH/DT/ONE apply", E, flags);
+    if (!(headdim == 32 || headdim == 64 || headdim == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: headdim %lld not in {32, 64, 128}", E, (long long)headdim);
+    if (d_state % 32 != 0 || d_state > SSM_MAX_D_STATE)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld must be a multiple of 32 and <= %d", E,
+                    (long long)d_state, SSM_MAX_D_STATE);
+    if (!(chunk_len == 64 || chunk_len == 128 || chunk_len == 256))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: chunk_len %lld not in {64, 128, 256}", E, (long long)chunk_len);
+    REQUIRE_ALIGN(E, x); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
+    REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
+    REQUIRE_ALIGN(E, h0); REQUIRE_ALIGN(E, h_final); REQUIRE_ALIGN(E, workspace);
+    if ((const void *)y == x || (const void *)y == (const void *)dt || (const void *)y == B ||
+        (const void *)y == C)
+        return fail(SSM_ERR_INVALID_ARG, "%s: y aliases an input", E);
+    const size_t need = ssm::ssd_workspace_bytes(batch, L, nheads, headdim, d_state, chunk_len);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    ssm::SsdArgs a{x, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, nheads, headdim,
+                   d_state, ngroups, chunk_len, in_dtype == SSM_BF16, flags, workspace};
+    const char *kn = "ssd";
+    return launched(E, ssm::launch_ssd(a, stream, &kn), kn);
+}
+
+size_t ssd_cplx_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads,
+                                              int64_t headdim, int64_t n_complex, int64_t ngroups,
+                                              int64_t chunk_len) {
+    (void)ngroups;
+    if (batch <= 0 || L <= 0 || nheads <= 0 || headdim <= 0 || n_complex <= 0 || chunk_len <= 0) return 0;
+    return ssm::cssd_workspace_bytes(batch, L, nheads, headdim, n_complex, chunk_len);
+}
+
+int ssd_cplx_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bias,
+                            const float *A_log, const float *B, const float *C, const float *D,
+                            float *y, const float *h0, float *h_final,
+                            int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                            int64_t n_complex, int64_t ngroups, int64_t chunk_len, uint32_t flags,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssd_cplx_chunk_scan_fwd";
+    REQUIRE_PTR(E, x); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
+    REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
+    int rc = ssd_check_shape(E, batch, L, nheads, headdim, n_complex, ngroups, chunk_len);
+    if (rc != SSM_OK) return rc;
+    if ((flags & ~0x1Fu) != 0 || (flags & 0x3u) == 0x3u || (flags & 0xCu) == 0xCu)
+        return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x not a valid combination", E, flags);
+    if ((flags & 0xCu) == SSM_CPLX_CODE && (flags & 0x3u) != SSM_BBAR_ZOH)
+        return fail(SSM_ERR_INVALID_ARG, "%s: SSM_CPLX_CODE fixes its own input scale; use SSM_BBAR_ZOH", E);
+    if (!(headdim == 32 || headdim == 64 || headdim == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: headdim %lld not in {32, 64, 128}", E, (long long)headdim);
+    if (n_complex % 8 != 0 || n_complex > 128)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: n_complex %lld must be a multiple of 8 and <= 128", E,
+                    (long long)n_complex);
+    if (!(chunk_len == 32 || chunk_len == 64 || chunk_len == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: chunk_len %lld not in {32, 64, 128}", E, (long long)chunk_len);
+    REQUIRE_ALIGN(E, x); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
+    REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
+    REQUIRE_ALIGN(E, h0); REQUIRE_ALIGN(E, h_final); REQUIRE_ALIGN(E, workspace);
+    if ((const void *)y == (const void *)x || (const void *)y == (const void *)dt ||
+        (const void *)y == (const void *)B || (const void *)y == (const void *)C)
+        return fail(SSM_ERR_INVALID_ARG, "%s: y aliases an input", E);
+    const size_t need = ssm::cssd_workspace_bytes(batch, L, nheads, headdim, n_complex, chunk_len);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    ssm::CssdArgs a{x, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, nheads, headdim,
+                    n_complex, ngroups, chunk_len, flags, workspace};
+    const char *kn = "cssd";
+    return launched(E, ssm::launch_cssd(a, stream, &kn), kn);
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// launchers.hpp -- host-side kernel launchers behind the C interface.
+// Arguments have been validated by abi.hip before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct S6Args {
+    const void *u; const float *dt; const float *dt_bias; const float *A_log;
+    const void *B; const void *C; const float *D; float *y;
+    const float *h0; float *h_final;
+    int64_t batch, L, d_inner, d_state;
+    bool bf16; uint32_t flags;
+};
+hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_name);
+
+struct SsdArgs {
+    const void *x; const float *dt; const float *dt_bias; const float *A_log;
+    const void *B; const void *C; const float *D; float *y;
+    const float *h0; float *h_final;
+    int64_t batch, L, nheads, headdim, d_state, ngroups, chunk_len;
+    bool bf16; uint32_t flags;
+    void *workspace;
+};
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                           int64_t d_state, int64_t chunk_len);
+hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_name);
+
+struct CssdArgs {
+    const float *x; const float *dt; const float *dt_bias; const float *A_log;
+    const float *B; const float *C; const float *D; float *y;
+    const float *h0; float *h_final;
+    int64_t batch, L, nheads, headdim, n_complex, ngroups, chunk_len;
+    uint32_t flags;
+    void *workspace;
+};
+size_t cssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                            int64_t n_complex, int64_t chunk_len);
+hipError_t launch_cssd(const CssdArgs &a, hipStream_t stream, const char **kernel_name);
+
+}  // namespace ssm

@@ -1,0 +1,447 @@
+// ssd_scan.hip -- Mamba-2 state-space-dual (SSD) chunked forward scan, gfx950.
+//
+// Implements the scalar-A-per-head recurrence of builderforce-memory-engine
+// ssd.js (header comment, ssd_chunk_forward) by the chunked decomposition whose
+// kernel sequence mamba-rs 0.2.1 mamba3_gpu.rs step F6 launches (K2 dA cumsum,
+// K3 chunk state, K4 state passing, K5 chunk scan, final-state writeback):
+//
+//   D1  per chunk: delta = softplus(dt + dt_bias), a = delta*A_h, cs = cumsum(a),
+//       input scale sigma (delta by default)                     [in K1 and K3]
+//   D2  chunk-local end state  Shat[p,n] = sum_s e^{cs_end-cs_s} sigma_s x_s[p] B_s[n]
+//       as a bf16 MFMA contraction over the chunk's time steps      [K1]
+//   D3  S_0 = h0, S_{c+1} = e^{cs_end(c)} S_c + Shat_c, h_final = S_nc [K2]
+//   D4  y_intra = ((C B^T) o Lmask) X with Lmask[t,s] = e^{cs_t-cs_s} sigma_s, s<=t
+//   D5  y += e^{cs_t} C_t S_c + D x_t                                  [K3]
+//
+// All contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the
+// decay mask is factorised per 32x32 tile so that every exponent is <= 0.
+// Inputs x, B, C are bf16 and enter the MFMA exactly.  Operands that are
+// products formed in fp32 (the decay-weighted inputs, the masked C.B^T, the
+// carried state) are split into bf16 hi + lo parts and contracted twice, so the
+// path keeps ~16 mantissa bits on them instead of bf16's 8.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace ssm {
+namespace {
+
+// bf16 operands are handled as raw 16-bit patterns in 32-bit lanes and only
+// reinterpreted as a whole vector at the MFMA: element-wise access to __bf16
+// vectors is avoided on purpose.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), low half = a
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// split fp32 pairs v = hi + lo with hi, lo bf16: the pair carries ~16 mantissa bits
+// returns {hi, lo}
+__device__ __forceinline__ uint2 split_bf16(float a, float b) {
+    const uint32_t hi = pack_bf16(a, b);
+    return make_uint2(hi, pack_bf16(a - lo_f(hi), b - hi_f(hi)));
+}
+
+// 8 consecutive bf16 from global memory (16 B), zero when !ok
+__device__ __forceinline__ u32x4 ld8(const uint16_t *p, bool ok) {
+    if (!ok) return u32x4{0u, 0u, 0u, 0u};
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+// 8 consecutive fp32 from global memory, split into bf16 hi and lo parts
+__device__ __forceinline__ void ld8f_split(const float *p, u32x4 &hi, u32x4 &lo) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    const uint2 s0 = split_bf16(a.x, a.y), s1 = split_bf16(a.z, a.w);
+    const uint2 s2 = split_bf16(b.x, b.y), s3 = split_bf16(b.z, b.w);
+    hi = u32x4{s0.x, s1.x, s2.x, s3.x};
+    lo = u32x4{s0.y, s1.y, s2.y, s3.y};
+}
+// element i (0..7) of 8 bf16 packed in a u32x4, as fp32
+__device__ __forceinline__ float elem_f(const u32x4 &v, int i) {
+    const uint32_t w = v[i >> 1];
+    return (i & 1) ? hi_f(w) : lo_f(w);
+}
+
+struct SsdKp {
+    const uint16_t *x; const float *dt; const float *dt_bias; const float *A_log;
+    const uint16_t *B; const uint16_t *C; const float *D; float *y;
+    const float *h0; float *h_final;
+    float *states;      // [batch][nc][H][P][N]  chunk-local end states, then entering states
+    float *chunk_a;     // [batch][H][nc]         sum of a over each chunk
+    int64_t batch, L, H, P, N, G, nc;
+    int mode;           // 0 ZOH, 1 DT, 2 ONE
+};
+
+// D1 for one chunk: fills cs[0..Q) (inclusive cumulative sum of a, zero past L)
+// and sig[0..Q) (input scale, zero past L).  Needs kThreads >= Q.
+template <int Q>
+__device__ __forceinline__ void chunk_scalars(const SsdKp &p, int64_t b, int64_t c, int64_t h,
+                                              float *cs, float *sig, float *wsum) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const float A = -expf(p.A_log[h]);
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    float a = 0.0f, sg = 0.0f;
+    const int64_t t = c * Q + tid;
+    if (tid < Q && t < p.L) {
+        const float dl = softplus(p.dt[(b * p.L + t) * p.H + h] + bias);
+        a = dl * A;
+        if (p.mode == 1) sg = dl;
+        else if (p.mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
+        else sg = 1.0f;
+    }
+    float v = a;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    float pre = 0.0f;
+    for (int w = 0; w < wid; ++w) pre += wsum[w];
+    v += pre;
+    if (tid < Q) { cs[tid] = v; sig[tid] = sg; }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------- K1: D1+D2
+// Shat^T[n][p] = sum_s B[s][n] * (w_s x[s][p]),  w_s = e^{cs_end - cs_s} sigma_s.
+// Both operands are staged transposed in LDS so that each lane reads 8
+// consecutive time steps (the contraction index) with one b128 read.  The
+// product w_s x[s][p] is not a bf16 number: it is carried as hi + lo bf16 parts
+// and contracted in two MFMA passes into the same fp32 accumulators.
+template <int Q, int P>
+__global__ void __launch_bounds__(kThreads)
+ssd_chunk_state_kernel(SsdKp p) {
+    constexpr int QS = Q + 8;           // padded row (bf16): row stride = 4 (mod 8) dwords
+    constexpr int NSLAB = 128;
+    constexpr int MAXT = (NSLAB / 32) * (P / 32) / 4;   // output tiles per wave per slab
+    __shared__ float cs[Q], sig[Q], wsum[4];
+    __shared__ __attribute__((aligned(16))) uint16_t Xt[P][QS];
+    __shared__ __attribute__((aligned(16))) uint16_t Bt[NSLAB][QS];
+
+    const int64_t nwork = p.batch * p.nc * p.H;
+    const int64_t work = xcd_swizzle(blockIdx.x, nwork);
+    const int64_t h = work % p.H;
+    const int64_t c = (work / p.H) % p.nc;
+    const int64_t b = work / (p.H * p.nc);
+    const int64_t g = h * p.G / p.H;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+
+    chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);
+    if (tid == 0) p.chunk_a[(b * p.H + h) * p.nc + c] = cs[Q - 1];
+    const float cs_end = cs[Q - 1];
+    const int col = lane & 31, hh = lane >> 5;
+
+    for (int n0s = 0; n0s < p.N; n0s += NSLAB) {
+        const int ns = min((int64_t)NSLAB, p.N - n0s);
+        const int ntile = (ns / 32) * (P / 32);
+        f32x16 acc[MAXT];
+#pragma unroll
+        for (int i = 0; i < MAXT; ++i) acc[i] = f32x16{};
+        __syncthreads();   // previous slab consumed
+        for (int e = tid; e < Q * (ns / 8); e += kThreads) {
+            const int s = e / (ns / 8), n8 = (e % (ns / 8)) * 8;
+            const int64_t t = c * Q + s;
+            const u32x4 v = ld8(p.B + ((b * p.L + t) * p.G + g) * p.N + n0s + n8, t < p.L);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Bt[n8 + 2 * i][s] = (uint16_t)(v[i] & 0xffffu);
+                Bt[n8 + 2 * i + 1][s] = (uint16_t)(v[i] >> 16);
+            }
+        }
+        for (int part = 0; part < 2; ++part) {
+            if (part) __syncthreads();   // hi pass done before lo overwrites Xt
+            for (int e = tid; e < Q * (P / 8); e += kThreads) {
+                const int s = e / (P / 8), p8 = (e % (P / 8)) * 8;
+                const int64_t t = c * Q + s;
+                const bool ok = t < p.L;
+                const float w = ok ? __expf(cs_end - cs[s]) * sig[s] : 0.0f;
+                const u32x4 v = ld8(p.x + ((b * p.L + t) * p.H + h) * p.P + p8, ok);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint2 sp = split_bf16(w * lo_f(v[i]), w * hi_f(v[i]));
+                    const uint32_t o = part ? sp.y : sp.x;
+                    Xt[p8 + 2 * i][s] = (uint16_t)(o & 0xffffu);
+                    Xt[p8 + 2 * i + 1][s] = (uint16_t)(o >> 16);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < MAXT; ++i) {
+                const int tile = wid + 4 * i;
+                if (tile >= ntile) break;
+                const int nt = tile / (P / 32), pt = tile % (P / 32);
+#pragma unroll 4
+                for (int k = 0; k < Q / 16; ++k) {
+                    const int s0 = k * 16 + hh * 8;
+                    const u32x4 A = *reinterpret_cast<const u32x4 *>(&Bt[nt * 32 + col][s0]);
+                    const u32x4 Bo = *reinterpret_cast<const u32x4 *>(&Xt[pt * 32 + col][s0]);
+                    acc[i] = mfma32(A, Bo, acc[i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MAXT; ++i) {
+            const int tile = wid + 4 * i;
+            if (tile >= ntile) break;
+            const int nt = tile / (P / 32), pt = tile % (P / 32);
+            // acc: column p = pt*32 + col, rows n = nt*32 + j*8 + hh*4 + (0..3)
+            float *dst = p.states + ((((b * p.nc + c) * p.H + h) * p.P + pt * 32 + col) * p.N) + n0s + nt * 32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<float4 *>(dst + j * 8 + hh * 4) =
+                    make_float4(acc[i][j * 4 + 0], acc[i][j * 4 + 1], acc[i][j * 4 + 2], acc[i][j * 4 + 3]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- K2: D3
+// One thread per (b, h, p, n): walk the chunks, replace each chunk-local end
+// state by the state entering that chunk, and write the final state.
+__global__ void __launch_bounds__(kThreads)
+ssd_state_pass_kernel(SsdKp p) {
+    const int64_t PN = p.P * p.N;
+    const int64_t per_bh = (PN + kThreads - 1) / kThreads;
+    const int64_t bh = blockIdx.x / per_bh;
+    const int64_t e = (blockIdx.x % per_bh) * kThreads + threadIdx.x;
+    if (e >= PN) return;
+    const int64_t b = bh / p.H, h = bh % p.H;
+    float S = p.h0 ? p.h0[bh * PN + e] : 0.0f;
+    const float *ca = p.chunk_a + bh * p.nc;
+    const int64_t cstride = p.H * PN;
+    float *st = p.states + (b * p.nc * p.H + h) * PN + e;
+    int64_t c = 0;
+    for (; c + 4 <= p.nc; c += 4) {
+        const float s0 = st[(c + 0) * cstride], s1 = st[(c + 1) * cstride];
+        const float s2 = st[(c + 2) * cstride], s3 = st[(c + 3) * cstride];
+        st[(c + 0) * cstride] = S; S = __expf(ca[c + 0]) * S + s0;
+        st[(c + 1) * cstride] = S; S = __expf(ca[c + 1]) * S + s1;
+        st[(c + 2) * cstride] = S; S = __expf(ca[c + 2]) * S + s2;
+        st[(c + 3) * cstride] = S; S = __expf(ca[c + 3]) * S + s3;
+    }
+    for (; c < p.nc; ++c) {
+        const float s0 = st[c * cstride];
+        st[c * cstride] = S;
+        S = __expf(ca[c]) * S + s0;
+    }
+    if (p.h_final) p.h_final[bh * PN + e] = S;
+}
+
+// ---------------------------------------------------------------- K3: D4+D5
+template <int Q, int P>
+__global__ void __launch_bounds__(kThreads)
+ssd_chunk_scan_kernel(SsdKp p) {
+    constexpr int QS = Q + 8;
+    constexpr int NTB = Q / 32;         // 32-row time blocks in a chunk
+    constexpr int PT = P / 32;          // 32-column blocks of the head dim
+    __shared__ float cs[Q], sig[Q], wsum[4];
+    __shared__ float gS[Q];             // e^{cs_e - cs_s} sigma_s, e = last step of s's block
+    __shared__ float ecs[Q];            // e^{cs_t}
+    __shared__ __attribute__((aligned(16))) uint16_t Xt[P][QS];
+
+    const int64_t nwork = p.batch * p.nc * p.H;
+    const int64_t work = xcd_swizzle(blockIdx.x, nwork);
+    const int64_t h = work % p.H;
+    const int64_t c = (work / p.H) % p.nc;
+    const int64_t b = work / (p.H * p.nc);
+    const int64_t g = h * p.G / p.H;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+
+    chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);
+    if (tid < Q) {
+        const int e = (tid | 31);
+        gS[tid] = __expf(cs[e] - cs[tid]) * sig[tid];
+        ecs[tid] = __expf(cs[tid]);
+    }
+    for (int e = tid; e < Q * (P / 8); e += kThreads) {
+        const int s = e / (P / 8), p8 = (e % (P / 8)) * 8;
+        const int64_t t = c * Q + s;
+        const u32x4 v = ld8(p.x + ((b * p.L + t) * p.H + h) * p.P + p8, t < p.L);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Xt[p8 + 2 * i][s] = (uint16_t)(v[i] & 0xffffu);
+            Xt[p8 + 2 * i + 1][s] = (uint16_t)(v[i] >> 16);
+        }
+    }
+    __syncthreads();
+
+    const float Dh = p.D ? p.D[h] : 0.0f;
+    const bool has_state = (c > 0) || (p.h0 != nullptr);
+    const int64_t rowBC = p.G * p.N;                       // elements between time steps of B/C
+    const uint16_t *Bbase = p.B + ((b * p.L + c * Q) * p.G + g) * p.N;
+    const uint16_t *Cbase = p.C + ((b * p.L + c * Q) * p.G + g) * p.N;
+    const int64_t tmax = p.L - c * Q;                      // valid rows in this chunk
+
+    for (int tb = 0; tb < NTB; ++tb) {
+        const int owner = ((tb / 4) & 1) ? 3 - (tb & 3) : (tb & 3);   // snake: balanced causal work
+        if (owner != wid) continue;
+        const int t0 = tb * 32;
+        const int trow = t0 + col;                          // this lane's time row (A-operand view)
+        f32x16 yacc[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x16{};
+
+        for (int sb = 0; sb <= tb; ++sb) {
+            const int s0 = sb * 32;
+            // G^T tile: rows s (this lane: s0 + j*8 + hh*4 + i), column t = trow
+            f32x16 gacc{};
+            const int srow = s0 + col;
+            for (int k = 0; k < p.N; k += 16) {
+                const u32x4 A = ld8(Bbase + srow * rowBC + k + hh * 8, srow < tmax);
+                const u32x4 Bo = ld8(Cbase + trow * rowBC + k + hh * 8, trow < tmax);
+                gacc = mfma32(A, Bo, gacc);
+            }
+            // M[t, s] = G[t, s] e^{cs_t - cs_s} sigma_s as hi + lo bf16 fragments
+            float mv[16];
+            if (sb < tb) {
+                const float ft = __expf(cs[trow] - cs[s0 + 31]);
+#pragma unroll
+                for (int idx = 0; idx < 16; ++idx) {
+                    const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
+                    mv[idx] = gacc[idx] * ft * gS[s];
+                }
+            } else {
+                const float ct = cs[trow];
+#pragma unroll
+                for (int idx = 0; idx < 16; ++idx) {
+                    const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
+                    mv[idx] = (s <= trow) ? gacc[idx] * __expf(ct - cs[s]) * sig[s] : 0.0f;
+                }
+            }
+            uint2 q[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = split_bf16(mv[2 * i], mv[2 * i + 1]);
+            const u32x4 m0h{q[0].x, q[1].x, q[2].x, q[3].x}, m0l{q[0].y, q[1].y, q[2].y, q[3].y};
+            const u32x4 m1h{q[4].x, q[5].x, q[6].x, q[7].x}, m1l{q[4].y, q[5].y, q[6].y, q[7].y};
+            // y[t, p] += sum_s M[t, s] X[s, p]; K-slot order matches the G^T layout
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const uint16_t *xr = &Xt[pt * 32 + col][0];
+                u32x4 x0, x1;
+                {
+                    const uint2 a = *reinterpret_cast<const uint2 *>(xr + s0 + hh * 4);
+                    const uint2 bq = *reinterpret_cast<const uint2 *>(xr + s0 + 8 + hh * 4);
+                    x0 = u32x4{a.x, a.y, bq.x, bq.y};
+                }
+                {
+                    const uint2 a = *reinterpret_cast<const uint2 *>(xr + s0 + 16 + hh * 4);
+                    const uint2 bq = *reinterpret_cast<const uint2 *>(xr + s0 + 24 + hh * 4);
+                    x1 = u32x4{a.x, a.y, bq.x, bq.y};
+                }
+                yacc[pt] = mfma32(m0h, x0, yacc[pt]);
+                yacc[pt] = mfma32(m0l, x0, yacc[pt]);
+                yacc[pt] = mfma32(m1h, x1, yacc[pt]);
+                yacc[pt] = mfma32(m1l, x1, yacc[pt]);
+            }
+        }
+
+        // D5: state entering the chunk, y[t, p] += e^{cs_t} sum_n C[t, n] S[p, n]
+        if (has_state) {
+            const float *Sb = p.states + ((b * p.nc + c) * p.H + h) * p.P * p.N;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                f32x16 sacc{};
+                for (int k = 0; k < p.N; k += 16) {
+                    const u32x4 A = ld8(Cbase + trow * rowBC + k + hh * 8, trow < tmax);
+                    u32x4 Sh, Sl;
+                    ld8f_split(Sb + (pt * 32 + col) * p.N + k + hh * 8, Sh, Sl);
+                    sacc = mfma32(A, Sh, sacc);
+                    sacc = mfma32(A, Sl, sacc);
+                }
+#pragma unroll
+                for (int idx = 0; idx < 16; ++idx) {
+                    const int t = t0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
+                    yacc[pt][idx] = fmaf(ecs[t], sacc[idx], yacc[pt][idx]);
+                }
+            }
+        }
+        // D skip and store: column p = pt*32 + col, rows t = t0 + j*8 + hh*4 + i
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int pc = pt * 32 + col;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tr = t0 + j * 8 + hh * 4;
+                const uint2 xv = *reinterpret_cast<const uint2 *>(&Xt[pc][tr]);
+                const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tr + i;
+                    if (t < tmax)
+                        p.y[((b * p.L + c * Q + t) * p.H + h) * p.P + pc] =
+                            fmaf(Dh, xs[i], yacc[pt][j * 4 + i]);
+                }
+            }
+        }
+    }
+}
+
+template <int Q, int P>
+hipError_t launch_qp(const SsdKp &kp, hipStream_t s) {
+    const int64_t nwork = kp.batch * kp.nc * kp.H;
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<Q, P>), dim3((unsigned)nwork), dim3(kThreads), 0, s, kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t per_bh = (kp.P * kp.N + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)(kp.batch * kp.H * per_bh)), dim3(kThreads), 0, s, kp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, P>), dim3((unsigned)nwork), dim3(kThreads), 0, s, kp);
+    return hipGetLastError();
+}
+
+template <int Q>
+hipError_t launch_q(const SsdKp &kp, hipStream_t s) {
+    if (kp.P == 32) return launch_qp<Q, 32>(kp, s);
+    if (kp.P == 64) return launch_qp<Q, 64>(kp, s);
+    return launch_qp<Q, 128>(kp, s);
+}
+
+}  // namespace
+
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                           int64_t d_state, int64_t chunk_len) {
+    const int64_t nc = (L + chunk_len - 1) / chunk_len;
+    const size_t st = (size_t)batch * nc * nheads * headdim * d_state * sizeof(float);
+    const size_t ca = (size_t)batch * nheads * nc * sizeof(float);
+    return ((st + 255) / 256) * 256 + ((ca + 255) / 256) * 256;
+}
+
+hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_name) {
+    *kernel_name = "ssd_chunk_state_kernel/ssd_state_pass_kernel/ssd_chunk_scan_kernel";
+    SsdKp p{};
+    p.x = static_cast<const uint16_t *>(a.x);
+    p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
+    p.B = static_cast<const uint16_t *>(a.B);
+    p.C = static_cast<const uint16_t *>(a.C);
+    p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
+    p.batch = a.batch; p.L = a.L; p.H = a.nheads; p.P = a.headdim; p.N = a.d_state; p.G = a.ngroups;
+    p.nc = (a.L + a.chunk_len - 1) / a.chunk_len;
+    const int64_t nc = p.nc;
+    const size_t st = (size_t)a.batch * nc * a.nheads * a.headdim * a.d_state * sizeof(float);
+    p.states = static_cast<float *>(a.workspace);
+    p.chunk_a = reinterpret_cast<float *>(static_cast<char *>(a.workspace) + ((st + 255) / 256) * 256);
+    p.mode = (int)(a.flags & 0x3u);
+    if (a.chunk_len == 64) return launch_q<64>(p, stream);
+    if (a.chunk_len == 128) return launch_q<128>(p, stream);
+    return launch_q<256>(p, stream);
+}
+
+}  // namespace ssm

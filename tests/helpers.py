@@ -1,0 +1,51 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the
+binding, run the oracle on the same inputs, compare with the north-star
+metric.  Nothing here does scan arithmetic."""
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+TOL_F32 = 1e-4     # max relative error, fp32 inputs
+TOL_BF16 = 2e-2    # max relative error, bf16 inputs with fp32 state
+
+
+def lib():
+    import selective_state_space_s6_amd as s
+    return s
+
+
+def report(name, **errs):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+
+
+def gpu_s6(inp, device, flags):
+    t = inp.torch(device)
+    y, hf = lib().ssm_s6_scan_fwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                  t["h0"], flags=flags, return_final=True)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), hf.cpu().numpy()
+
+
+def gpu_ssd(inp, device, flags, chunk_len):
+    t = inp.torch(device)
+    y, hf = lib().ssd_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"],
+                                     t["D"], t["h0"], chunk_len=chunk_len, flags=flags,
+                                     return_final=True)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), hf.cpu().numpy()
+
+
+def gpu_cssd(inp, device, flags, chunk_len):
+    t = inp.torch(device)
+    y, hf = lib().ssd_cplx_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"],
+                                          t["D"], t["h0"], chunk_len=chunk_len, flags=flags,
+                                          return_final=True)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), hf.cpu().numpy()
+
+
+def sample_units(rng, n0, n1, k):
+    idx = rng.choice(n0 * n1, size=min(k, n0 * n1), replace=False)
+    return np.stack([idx // n1, idx % n1], 1)

@@ -1,0 +1,50 @@
+"""GPU parity of ssd_cplx_chunk_scan_fwd (fp32) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import TOL_F32, gpu_cssd, report, sample_units
+
+pytestmark = pytest.mark.gpu
+
+STABLE, DOC, CODE, CONJ = oracle.CPLX_STABLE, oracle.CPLX_DOC, oracle.CPLX_CODE, oracle.CPLX_CONJ_C
+ZOH, DT, ONE = oracle.BBAR_ZOH, oracle.BBAR_DT, oracle.BBAR_ONE
+
+CASES = [  # batch, L, H, P, Nc, G, Q, flags, h0
+    (2, 150, 4, 32, 8, 2, 32, STABLE | ZOH, True),
+    (1, 200, 2, 64, 32, 1, 64, STABLE | ZOH, True),
+    (1, 260, 2, 64, 16, 2, 128, STABLE | DT, False),
+    (1, 100, 2, 32, 8, 1, 64, STABLE | ONE, True),
+    (1, 120, 2, 32, 8, 1, 64, DOC | ZOH, True),
+    (1, 120, 2, 32, 8, 1, 64, CODE, True),
+    (1, 90, 2, 64, 32, 1, 64, STABLE | ZOH | CONJ, True),
+    (1, 1, 2, 32, 8, 1, 64, STABLE | ZOH, True),
+    (1, 64, 2, 128, 8, 1, 64, STABLE | ZOH, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"b{c[0]}L{c[1]}H{c[2]}P{c[3]}N{c[4]}G{c[5]}Q{c[6]}f{c[7]}")
+def test_cssd_shapes(cuda_device, case):
+    batch, L, H, P, Nc, G, Q, flags, h0 = case
+    inp = synth.cssd_inputs(batch, L, H, P, Nc, G, seed=(300 + L,), h0=h0)
+    y, hf = gpu_cssd(inp, cuda_device, flags, Q)
+    yo, ho = oracle.cssd_fwd(**inp.arrays, ngroups=G, flags=flags)
+    ey, eh = synth.max_rel_err(y, yo), synth.max_rel_err(hf, ho)
+    report(f"cssd {case}", y=ey, h_final=eh)
+    assert np.isfinite(y).all() and np.isfinite(hf).all()
+    assert ey <= TOL_F32 and eh <= TOL_F32
+
+
+def test_cssd_workload_sampled(cuda_device):
+    inp = synth.workload_inputs("cssd_mamba3")
+    w = synth.WORKLOADS["cssd_mamba3"]
+    y, hf = gpu_cssd(inp, cuda_device, STABLE | ZOH, w["chunk_len"])
+    rng = np.random.default_rng(2)
+    units = sample_units(rng, w["batch"], w["nheads"], 4)
+    yo, ho = oracle.cssd_fwd(**inp.arrays, ngroups=w["ngroups"], units=units)
+    yg = np.stack([y[b, :, h, :] for b, h in units])
+    hg = np.stack([hf[b, h] for b, h in units])
+    ey, eh = synth.max_rel_err(yg, yo), synth.max_rel_err(hg, ho)
+    report("cssd_mamba3 sampled", y=ey, h_final=eh)
+    assert ey <= TOL_F32 and eh <= TOL_F32

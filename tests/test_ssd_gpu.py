@@ -1,0 +1,75 @@
+"""GPU parity of ssd_chunk_scan_fwd (bf16 inputs, fp32 state) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import TOL_BF16, gpu_ssd, report, sample_units
+
+pytestmark = pytest.mark.gpu
+
+ZOH, DT, ONE = oracle.BBAR_ZOH, oracle.BBAR_DT, oracle.BBAR_ONE
+
+
+def _check(name, inp, device, flags, Q, tol=TOL_BF16):
+    y, hf = gpu_ssd(inp, device, flags, Q)
+    yo, ho = oracle.ssd_fwd(**inp.arrays, ngroups=inp.dims["ngroups"], flags=flags)
+    ey, eh = synth.max_rel_err(y, yo), synth.max_rel_err(hf, ho)
+    report(name, y=ey, h_final=eh)
+    assert np.isfinite(y).all() and np.isfinite(hf).all()
+    assert ey <= tol and eh <= tol
+    return y
+
+
+CASES = [  # batch, L, H, P, N, G, Q, flags, h0
+    (2, 300, 4, 64, 64, 2, 64, DT, True),
+    (2, 300, 4, 64, 128, 2, 128, DT, True),
+    (1, 600, 2, 64, 128, 1, 256, DT, True),
+    (1, 300, 3, 64, 128, 3, 256, ZOH, False),
+    (1, 200, 2, 32, 32, 1, 64, ONE, True),
+    (1, 130, 2, 128, 64, 2, 128, DT, True),
+    (1, 100, 2, 64, 256, 1, 64, DT, True),
+    (1, 1, 2, 64, 128, 1, 256, DT, True),
+    (1, 65, 2, 64, 128, 1, 64, ZOH, True),
+    (2, 513, 4, 64, 128, 1, 256, DT, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"b{c[0]}L{c[1]}H{c[2]}P{c[3]}N{c[4]}G{c[5]}Q{c[6]}f{c[7]}")
+def test_ssd_shapes(cuda_device, case):
+    batch, L, H, P, N, G, Q, flags, h0 = case
+    inp = synth.ssd_inputs(batch, L, H, P, N, G, seed=(200 + L,), h0=h0, D="normal")
+    _check(f"ssd {case}", inp, cuda_device, flags, Q)
+
+
+def test_ssd_chunk_len_invariance(cuda_device):
+    inp = synth.ssd_inputs(1, 700, 2, 64, 128, 1, seed=(5,), h0=True)
+    ys = [gpu_ssd(inp, cuda_device, DT, Q) for Q in (64, 128, 256)]
+    for y, hf in ys[1:]:
+        assert synth.max_rel_err(y, ys[0][0]) < TOL_BF16
+        assert synth.max_rel_err(hf, ys[0][1]) < TOL_BF16
+
+
+def test_ssd_bitwise_deterministic(cuda_device):
+    inp = synth.ssd_inputs(2, 1000, 4, 64, 128, 2, seed=(6,), h0=True)
+    a = gpu_ssd(inp, cuda_device, DT, 256)
+    b = gpu_ssd(inp, cuda_device, DT, 256)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name,k", [("ssd_mamba2", 4), ("ssd_long", 2)])
+def test_ssd_workloads_sampled(cuda_device, name, k):
+    """Full workload shape; k sampled (b, h) heads checked over the whole sequence."""
+    inp = synth.workload_inputs(name)
+    w = synth.WORKLOADS[name]
+    y, hf = gpu_ssd(inp, cuda_device, DT, w["chunk_len"])
+    a = inp.arrays
+    rng = np.random.default_rng(1)
+    units = sample_units(rng, w["batch"], w["nheads"], k)
+    yo, ho = oracle.ssd_fwd(**a, ngroups=w["ngroups"], units=units)
+    yg = np.stack([y[b, :, h, :] for b, h in units])
+    hg = np.stack([hf[b, h] for b, h in units])
+    ey, eh = synth.max_rel_err(yg, yo), synth.max_rel_err(hg, ho)
+    report(f"{name} sampled", y=ey, h_final=eh)
+    assert np.isfinite(y).all()
+    assert ey <= TOL_BF16 and eh <= TOL_BF16
