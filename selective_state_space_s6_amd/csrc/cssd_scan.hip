@@ -75,28 +75,32 @@ __device__ __forceinline__ cf input_scale(const CssdKp &p, int64_t h, cf mu, flo
 }
 
 // per-chunk scalars: Lam[t] = inclusive running sum of delta (0 past L),
-// bet[t] = beta_t (0 past L)
+// bet[t] = beta_t (0 past L).  The rotation angle phi*(Lam_t - Lam_s) turns an
+// absolute error of Lam into a relative error of the output, so delta and its
+// running sum are formed in double precision (Q values per chunk); every
+// difference of two Lam is taken in double and only then rounded to fp32.
 template <int Q>
 __device__ __forceinline__ void chunk_scalars(const CssdKp &p, int64_t b, int64_t c, int64_t h, cf mu,
-                                              float *Lam, float *bre, float *bim, float *wsum) {
+                                              double *Lam, float *bre, float *bim, double *wsum) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
-    float dl = 0.0f;
+    const double bias = p.dt_bias ? (double)p.dt_bias[h] : 0.0;
+    double dl = 0.0;
     cf be{0.0f, 0.0f};
     const int64_t t = c * Q + tid;
     if (tid < Q && t < p.L) {
-        dl = softplus(p.dt[(b * p.L + t) * p.H + h] + bias);
-        be = input_scale(p, h, mu, dl);
+        const double xv = (double)p.dt[(b * p.L + t) * p.H + h] + bias;
+        dl = xv > 0.0 ? xv + log1p(exp(-xv)) : log1p(exp(xv));   // softplus
+        be = input_scale(p, h, mu, (float)dl);
     }
-    float v = dl;
+    double v = dl;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(v, off, 64);
+        const double o = __shfl_up(v, off, 64);
         if (lane >= off) v += o;
     }
     if (lane == 63) wsum[wid] = v;
     __syncthreads();
-    float pre = 0.0f;
+    double pre = 0.0;
     for (int w = 0; w < wid; ++w) pre += wsum[w];
     if (tid < Q) { Lam[tid] = v + pre; bre[tid] = be.re; bim[tid] = be.im; }
     __syncthreads();
@@ -105,22 +109,23 @@ __device__ __forceinline__ void chunk_scalars(const CssdKp &p, int64_t b, int64_
 template <int Q>
 __global__ void __launch_bounds__(kThreads)
 cssd_chunk_state_kernel(CssdKp p) {
-    __shared__ float Lam[Q], bre[Q], bim[Q], wre[Q], wim[Q], wsum[4];
+    __shared__ double Lam[Q], wsum[4];
+    __shared__ float bre[Q], bim[Q], wre[Q], wim[Q];
     const int64_t work = xcd_swizzle(blockIdx.x, p.batch * p.nc * p.H);
     const int64_t h = work % p.H, c = (work / p.H) % p.nc, b = work / (p.H * p.nc);
     const int64_t g = h * p.G / p.H;
     const int tid = threadIdx.x;
     const cf mu = head_mu(p, h);
     chunk_scalars<Q>(p, b, c, h, mu, Lam, bre, bim, wsum);
-    const float Lend = Lam[Q - 1];
+    const double Lend = Lam[Q - 1];
     if (tid < Q) {   // w_s = exp(mu (Lambda_end - Lambda_s)) beta_s
-        const float dlam = Lend - Lam[tid];
+        const float dlam = (float)(Lend - Lam[tid]);
         const cf e = cexpf_(mu.re * dlam, mu.im * dlam);
         const cf w = cmul(e, cf{bre[tid], bim[tid]});
         wre[tid] = w.re; wim[tid] = w.im;
     }
     if (tid == 0) {
-        const cf e = cexpf_(mu.re * Lend, mu.im * Lend);
+        const cf e = cexpf_(mu.re * (float)Lend, mu.im * (float)Lend);
         p.cdec[((b * p.H + h) * p.nc + c) * 2] = e.re;
         p.cdec[((b * p.H + h) * p.nc + c) * 2 + 1] = e.im;
     }
@@ -128,17 +133,19 @@ cssd_chunk_state_kernel(CssdKp p) {
     const int64_t smax = min((int64_t)Q, p.L - c * Q);
     for (int64_t e = tid; e < p.P * p.Nc; e += kThreads) {
         const int64_t pp = e / p.Nc, n = e % p.Nc;
-        float are = 0.0f, aim = 0.0f;
+        // four interleaved partial sums: shorter fp32 rounding chains
+        float are[4] = {0.0f, 0.0f, 0.0f, 0.0f}, aim[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int64_t s = 0; s < smax; ++s) {
             const int64_t t = c * Q + s;
             const float xv = p.x[((b * p.L + t) * p.H + h) * p.P + pp];
             const float *Bs = p.B + (((b * p.L + t) * p.G + g) * p.Nc + n) * 2;
             const cf wb = cmul(cf{wre[s], wim[s]}, cf{Bs[0], Bs[1]});
-            are = fmaf(wb.re, xv, are);
-            aim = fmaf(wb.im, xv, aim);
+            are[s & 3] = fmaf(wb.re, xv, are[s & 3]);
+            aim[s & 3] = fmaf(wb.im, xv, aim[s & 3]);
         }
         float *dst = p.states + ((((b * p.nc + c) * p.H + h) * p.P + pp) * p.Nc + n) * 2;
-        dst[0] = are; dst[1] = aim;
+        dst[0] = (are[0] + are[1]) + (are[2] + are[3]);
+        dst[1] = (aim[0] + aim[1]) + (aim[2] + aim[3]);
     }
 }
 
@@ -167,7 +174,8 @@ cssd_state_pass_kernel(CssdKp p) {
 template <int Q>
 __global__ void __launch_bounds__(kThreads)
 cssd_chunk_scan_kernel(CssdKp p) {
-    __shared__ float Lam[Q], bre[Q], bim[Q], e0re[Q], e0im[Q], wsum[4];
+    __shared__ double Lam[Q], wsum[4];
+    __shared__ float bre[Q], bim[Q], e0re[Q], e0im[Q];
     __shared__ float M[Q][Q + 1];
     const int64_t work = xcd_swizzle(blockIdx.x, p.batch * p.nc * p.H);
     const int64_t h = work % p.H, c = (work / p.H) % p.nc, b = work / (p.H * p.nc);
@@ -177,7 +185,8 @@ cssd_chunk_scan_kernel(CssdKp p) {
     const float csign = (p.flags & 0x10u) ? -1.0f : 1.0f;   // conj(C)
     chunk_scalars<Q>(p, b, c, h, mu, Lam, bre, bim, wsum);
     if (tid < Q) {
-        const cf e = cexpf_(mu.re * Lam[tid], mu.im * Lam[tid]);
+        const float lt = (float)Lam[tid];
+        const cf e = cexpf_(mu.re * lt, mu.im * lt);
         e0re[tid] = e.re; e0im[tid] = e.im;
     }
     const int64_t tmax = min((int64_t)Q, p.L - c * Q);
@@ -188,14 +197,15 @@ cssd_chunk_scan_kernel(CssdKp p) {
         if (s <= t && t < tmax) {
             const float *Ct = p.C + ((b * p.L + c * Q + t) * p.G + g) * p.Nc * 2;
             const float *Bs = p.B + ((b * p.L + c * Q + s) * p.G + g) * p.Nc * 2;
-            float gre = 0.0f, gim = 0.0f;
+            float gre2[2] = {0.0f, 0.0f}, gim2[2] = {0.0f, 0.0f};
             for (int64_t n = 0; n < p.Nc; ++n) {
                 const float cr = Ct[2 * n], ci = csign * Ct[2 * n + 1];
                 const float br = Bs[2 * n], bi = Bs[2 * n + 1];
-                gre = fmaf(cr, br, fmaf(-ci, bi, gre));
-                gim = fmaf(cr, bi, fmaf(ci, br, gim));
+                gre2[n & 1] = fmaf(cr, br, fmaf(-ci, bi, gre2[n & 1]));
+                gim2[n & 1] = fmaf(cr, bi, fmaf(ci, br, gim2[n & 1]));
             }
-            const float dlam = Lam[t] - Lam[s];
+            const float gre = gre2[0] + gre2[1], gim = gim2[0] + gim2[1];
+            const float dlam = (float)(Lam[t] - Lam[s]);
             const cf ex = cexpf_(mu.re * dlam, mu.im * dlam);
             const cf k = cmul(cmul(cf{gre, gim}, ex), cf{bre[s], bim[s]});
             m = k.re;
@@ -208,19 +218,20 @@ cssd_chunk_scan_kernel(CssdKp p) {
     const float *Sb = p.states + ((b * p.nc + c) * p.H + h) * p.P * p.Nc * 2;
     for (int64_t e = tid; e < tmax * p.P; e += kThreads) {
         const int64_t t = e / p.P, pp = e % p.P;
-        float acc = 0.0f;
+        float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int64_t s = 0; s <= t; ++s)
-            acc = fmaf(M[t][s], p.x[((b * p.L + c * Q + s) * p.H + h) * p.P + pp], acc);
+            a4[s & 3] = fmaf(M[t][s], p.x[((b * p.L + c * Q + s) * p.H + h) * p.P + pp], a4[s & 3]);
+        float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
         if (has_state) {
             const float *Ct = p.C + ((b * p.L + c * Q + t) * p.G + g) * p.Nc * 2;
             const float *Sp = Sb + pp * p.Nc * 2;
             const cf e0{e0re[t], e0im[t]};
-            float sre = 0.0f;
+            float s2[2] = {0.0f, 0.0f};
             for (int64_t n = 0; n < p.Nc; ++n) {
                 const cf cc = cmul(cf{Ct[2 * n], csign * Ct[2 * n + 1]}, e0);
-                sre = fmaf(cc.re, Sp[2 * n], fmaf(-cc.im, Sp[2 * n + 1], sre));
+                s2[n & 1] = fmaf(cc.re, Sp[2 * n], fmaf(-cc.im, Sp[2 * n + 1], s2[n & 1]));
             }
-            acc += sre;
+            acc += s2[0] + s2[1];
         }
         const float xv = p.x[((b * p.L + c * Q + t) * p.H + h) * p.P + pp];
         p.y[((b * p.L + c * Q + t) * p.H + h) * p.P + pp] = fmaf(Dh, xv, acc);
