@@ -83,6 +83,7 @@ struct SsdKp {
     float *states;      // [batch][nc][H][P][N]  chunk-local end states, then entering states
     float *chunk_a;     // [batch][H][nc]         sum of a over each chunk
     int64_t batch, L, H, P, N, G, nc;
+    int64_t hb;         // heads per work item (a divisor of H / G)
     int mode;           // 0 ZOH, 1 DT, 2 ONE
 };
 
@@ -119,94 +120,118 @@ __device__ __forceinline__ void chunk_scalars(const SsdKp &p, int64_t b, int64_t
     __syncthreads();
 }
 
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
+// names a row of 4 consecutive 16-bit elements and receives element (i % 4) of
+// rows i/4, i/4 + 4, i/4 + 8, i/4 + 12.  Pointing row i at (step sb + i/4,
+// column cb + 4*(i%4)) of a row-major [step][column] tile therefore hands lane
+// i the four steps sb..sb+3 of column cb + i: the layout an MFMA operand needs
+// when the time step is the contraction index.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 tr_read(const uint16_t *tile, int pitch, int sb, int cb, int lane) {
+    const int i = lane & 15;
+    const uint16_t *a = tile + (sb + (i >> 2)) * pitch + cb + 4 * (i & 3);
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(a));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Head blocks: the heads of one work item share a group (so B and C), and C.B^T
+// is formed once per work item.
+__device__ __forceinline__ void decode_work(const SsdKp &p, int64_t &b, int64_t &c, int64_t &h0,
+                                            int64_t &g) {
+    const int64_t nhb = p.H / p.hb;
+    const int64_t nwork = p.batch * p.nc * nhb;
+    const int64_t work = xcd_swizzle(blockIdx.x, nwork);
+    const int64_t hbi = work % nhb;
+    c = (work / nhb) % p.nc;
+    b = work / (nhb * p.nc);
+    h0 = hbi * p.hb;
+    g = h0 * p.G / p.H;
+}
+
 // ---------------------------------------------------------------- K1: D1+D2
 // Shat^T[n][p] = sum_s B[s][n] * (w_s x[s][p]),  w_s = e^{cs_end - cs_s} sigma_s.
-// Both operands are staged transposed in LDS so that each lane reads 8
-// consecutive time steps (the contraction index) with one b128 read.  The
-// product w_s x[s][p] is not a bf16 number: it is carried as hi + lo bf16 parts
-// and contracted in two MFMA passes into the same fp32 accumulators.
+// B (one slab of up to 128 states) and the weighted inputs are staged in their
+// natural row-major layout; the MFMA operands, whose contraction index is the
+// time step, are read with transposed LDS reads.  w_s x[s][p] is carried as
+// bf16 hi + lo parts and contracted in two MFMA passes into fp32 accumulators.
 template <int Q, int P>
 __global__ void __launch_bounds__(kThreads)
 ssd_chunk_state_kernel(SsdKp p) {
-    constexpr int QS = Q + 8;           // padded row (bf16): row stride = 4 (mod 8) dwords
-    constexpr int NSLAB = 128;
-    constexpr int MAXT = (NSLAB / 32) * (P / 32) / 4;   // output tiles per wave per slab
+    constexpr int NSLAB = 128, BP = NSLAB + 8;        // B slab pitch (bf16)
+    constexpr int PH = P < 64 ? P : 64, XP = PH + 8;  // x column block and pitch
+    constexpr int MAXT = (NSLAB / 32) * (PH / 32) / 4 > 0 ? (NSLAB / 32) * (PH / 32) / 4 : 1;
     __shared__ float cs[Q], sig[Q], wsum[4];
-    __shared__ __attribute__((aligned(16))) uint16_t Xt[P][QS];
-    __shared__ __attribute__((aligned(16))) uint16_t Bt[NSLAB][QS];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[Q * BP];
+    __shared__ __attribute__((aligned(16))) uint16_t Xh[Q * XP];
+    __shared__ __attribute__((aligned(16))) uint16_t Xl[Q * XP];
 
-    const int64_t nwork = p.batch * p.nc * p.H;
-    const int64_t work = xcd_swizzle(blockIdx.x, nwork);
-    const int64_t h = work % p.H;
-    const int64_t c = (work / p.H) % p.nc;
-    const int64_t b = work / (p.H * p.nc);
-    const int64_t g = h * p.G / p.H;
+    int64_t b, c, hfirst, g;
+    decode_work(p, b, c, hfirst, g);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-
-    chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);
-    if (tid == 0) p.chunk_a[(b * p.H + h) * p.nc + c] = cs[Q - 1];
-    const float cs_end = cs[Q - 1];
-    const int col = lane & 31, hh = lane >> 5;
+    const int col = lane & 31, hh = lane >> 5, half = (lane >> 4) & 1;
 
     for (int n0s = 0; n0s < p.N; n0s += NSLAB) {
-        const int ns = min((int64_t)NSLAB, p.N - n0s);
-        const int ntile = (ns / 32) * (P / 32);
-        f32x16 acc[MAXT];
-#pragma unroll
-        for (int i = 0; i < MAXT; ++i) acc[i] = f32x16{};
+        const int ns = (int)min((int64_t)NSLAB, p.N - n0s);
         __syncthreads();   // previous slab consumed
         for (int e = tid; e < Q * (ns / 8); e += kThreads) {
             const int s = e / (ns / 8), n8 = (e % (ns / 8)) * 8;
             const int64_t t = c * Q + s;
-            const u32x4 v = ld8(p.B + ((b * p.L + t) * p.G + g) * p.N + n0s + n8, t < p.L);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Bt[n8 + 2 * i][s] = (uint16_t)(v[i] & 0xffffu);
-                Bt[n8 + 2 * i + 1][s] = (uint16_t)(v[i] >> 16);
-            }
+            *reinterpret_cast<u32x4 *>(&Bs[s * BP + n8]) =
+                ld8(p.B + ((b * p.L + t) * p.G + g) * p.N + n0s + n8, t < p.L);
         }
-        for (int part = 0; part < 2; ++part) {
-            if (part) __syncthreads();   // hi pass done before lo overwrites Xt
-            for (int e = tid; e < Q * (P / 8); e += kThreads) {
-                const int s = e / (P / 8), p8 = (e % (P / 8)) * 8;
-                const int64_t t = c * Q + s;
-                const bool ok = t < p.L;
-                const float w = ok ? __expf(cs_end - cs[s]) * sig[s] : 0.0f;
-                const u32x4 v = ld8(p.x + ((b * p.L + t) * p.H + h) * p.P + p8, ok);
+        for (int64_t h = hfirst; h < hfirst + p.hb; ++h) {
+            chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);   // starts and ends with a barrier
+            if (n0s == 0 && tid == 0) p.chunk_a[(b * p.H + h) * p.nc + c] = cs[Q - 1];
+            const float cs_end = cs[Q - 1];
+            for (int p0 = 0; p0 < P; p0 += PH) {
+                __syncthreads();   // previous x block consumed
+                for (int e = tid; e < Q * (PH / 8); e += kThreads) {
+                    const int s = e / (PH / 8), q8 = (e % (PH / 8)) * 8;
+                    const int64_t t = c * Q + s;
+                    const bool ok = t < p.L;
+                    const float w = ok ? __expf(cs_end - cs[s]) * sig[s] : 0.0f;
+                    const u32x4 v = ld8(p.x + ((b * p.L + t) * p.H + h) * p.P + p0 + q8, ok);
+                    u32x4 hi, lo;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint2 sp = split_bf16(w * lo_f(v[i]), w * hi_f(v[i]));
-                    const uint32_t o = part ? sp.y : sp.x;
-                    Xt[p8 + 2 * i][s] = (uint16_t)(o & 0xffffu);
-                    Xt[p8 + 2 * i + 1][s] = (uint16_t)(o >> 16);
+                    for (int i = 0; i < 4; ++i) {
+                        const uint2 sp = split_bf16(w * lo_f(v[i]), w * hi_f(v[i]));
+                        hi[i] = sp.x;
+                        lo[i] = sp.y;
+                    }
+                    *reinterpret_cast<u32x4 *>(&Xh[s * XP + q8]) = hi;
+                    *reinterpret_cast<u32x4 *>(&Xl[s * XP + q8]) = lo;
                 }
-            }
-            __syncthreads();
+                __syncthreads();
+                const int ntile = (ns / 32) * (PH / 32);
 #pragma unroll
-            for (int i = 0; i < MAXT; ++i) {
-                const int tile = wid + 4 * i;
-                if (tile >= ntile) break;
-                const int nt = tile / (P / 32), pt = tile % (P / 32);
+                for (int i = 0; i < MAXT; ++i) {
+                    const int tile = wid + 4 * i;
+                    if (tile >= ntile) break;
+                    const int nt = tile / (PH / 32), pt = tile % (PH / 32);
+                    f32x16 acc{};
 #pragma unroll 4
-                for (int k = 0; k < Q / 16; ++k) {
-                    const int s0 = k * 16 + hh * 8;
-                    const u32x4 A = *reinterpret_cast<const u32x4 *>(&Bt[nt * 32 + col][s0]);
-                    const u32x4 Bo = *reinterpret_cast<const u32x4 *>(&Xt[pt * 32 + col][s0]);
-                    acc[i] = mfma32(A, Bo, acc[i]);
+                    for (int k = 0; k < Q / 16; ++k) {
+                        const int sb = k * 16 + hh * 8;
+                        const uint2 a0 = tr_read(Bs, BP, sb, nt * 32 + half * 16, lane);
+                        const uint2 a1 = tr_read(Bs, BP, sb + 4, nt * 32 + half * 16, lane);
+                        const uint2 x0 = tr_read(Xh, XP, sb, pt * 32 + half * 16, lane);
+                        const uint2 x1 = tr_read(Xh, XP, sb + 4, pt * 32 + half * 16, lane);
+                        const uint2 l0 = tr_read(Xl, XP, sb, pt * 32 + half * 16, lane);
+                        const uint2 l1 = tr_read(Xl, XP, sb + 4, pt * 32 + half * 16, lane);
+                        const u32x4 A = {a0.x, a0.y, a1.x, a1.y};
+                        acc = mfma32(A, u32x4{x0.x, x0.y, x1.x, x1.y}, acc);
+                        acc = mfma32(A, u32x4{l0.x, l0.y, l1.x, l1.y}, acc);
+                    }
+                    // acc: column p = p0 + pt*32 + col, rows n = n0s + nt*32 + j*8 + hh*4 + (0..3)
+                    float *dst = p.states + ((((b * p.nc + c) * p.H + h) * p.P + p0 + pt * 32 + col) * p.N) +
+                                 n0s + nt * 32;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<float4 *>(dst + j * 8 + hh * 4) =
+                            make_float4(acc[j * 4 + 0], acc[j * 4 + 1], acc[j * 4 + 2], acc[j * 4 + 3]);
                 }
             }
-        }
-#pragma unroll
-        for (int i = 0; i < MAXT; ++i) {
-            const int tile = wid + 4 * i;
-            if (tile >= ntile) break;
-            const int nt = tile / (P / 32), pt = tile % (P / 32);
-            // acc: column p = pt*32 + col, rows n = nt*32 + j*8 + hh*4 + (0..3)
-            float *dst = p.states + ((((b * p.nc + c) * p.H + h) * p.P + pt * 32 + col) * p.N) + n0s + nt * 32;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<float4 *>(dst + j * 8 + hh * 4) =
-                    make_float4(acc[i][j * 4 + 0], acc[i][j * 4 + 1], acc[i][j * 4 + 2], acc[i][j * 4 + 3]);
         }
     }
 }
@@ -244,70 +269,108 @@ ssd_state_pass_kernel(SsdKp p) {
 }
 
 // ---------------------------------------------------------------- K3: D4+D5
+// Work item = (batch, chunk, block of heads of one group).  C.B^T of the chunk
+// is formed once, from B and C staged in slabs, and kept in registers: each
+// wave owns a balanced set of 32x32 causal tiles (time blocks w and NTB-1-w).
+// Then, per head: decay mask, (C.B^T o L) X, e^{cs_t} C S_c and D x, with x
+// staged row-major and read transposed.
+template <int Q> struct Plan;
+template <> struct Plan<256> { static constexpr int NSLOT = 9; };   // blocks w, 7-w: (w+1) + (8-w) tiles
+template <> struct Plan<128> { static constexpr int NSLOT = 4; };   // block w: w+1 tiles
+template <> struct Plan<64> { static constexpr int NSLOT = 2; };    // block w (w < 2): w+1 tiles
+
+// slot -> (time block, source block) of wave w; false when the slot is unused
+template <int Q>
+__device__ __forceinline__ bool slot_tile(int w, int slot, int &tb, int &sb) {
+    if constexpr (Q == 256) {
+        if (slot <= w) { tb = w; sb = slot; }
+        else { tb = 7 - w; sb = slot - w - 1; }
+        return true;
+    } else {
+        tb = w; sb = slot;
+        return (tb < Q / 32) && (slot <= w);
+    }
+}
+
 template <int Q, int P>
 __global__ void __launch_bounds__(kThreads)
 ssd_chunk_scan_kernel(SsdKp p) {
-    constexpr int QS = Q + 8;
-    constexpr int NTB = Q / 32;         // 32-row time blocks in a chunk
-    constexpr int PT = P / 32;          // 32-column blocks of the head dim
-    __shared__ float cs[Q], sig[Q], wsum[4];
-    __shared__ float gS[Q];             // e^{cs_e - cs_s} sigma_s, e = last step of s's block
-    __shared__ float ecs[Q];            // e^{cs_t}
-    __shared__ __attribute__((aligned(16))) uint16_t Xt[P][QS];
+    constexpr int NS = 64, BCP = NS + 8;                // B/C slab width and pitch (bf16)
+    constexpr int XP = P + 8;                           // x tile pitch (bf16)
+    constexpr int PT = P / 32;
+    constexpr int NSLOT = Plan<Q>::NSLOT;
+    constexpr int SLAB_E = 2 * Q * BCP, X_E = Q * XP;
+    constexpr int ARENA = SLAB_E > X_E ? SLAB_E : X_E;
+    __shared__ float cs[Q], sig[Q], gS[Q], ecs[Q], wsum[4];
+    __shared__ __attribute__((aligned(16))) uint16_t arena[ARENA];
+    uint16_t *Bs = arena, *Cs = arena + Q * BCP, *Xs = arena;
 
-    const int64_t nwork = p.batch * p.nc * p.H;
-    const int64_t work = xcd_swizzle(blockIdx.x, nwork);
-    const int64_t h = work % p.H;
-    const int64_t c = (work / p.H) % p.nc;
-    const int64_t b = work / (p.H * p.nc);
-    const int64_t g = h * p.G / p.H;
+    int64_t b, c, hfirst, g;
+    decode_work(p, b, c, hfirst, g);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int col = lane & 31, hh = lane >> 5;
-
-    chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);
-    if (tid < Q) {
-        const int e = (tid | 31);
-        gS[tid] = __expf(cs[e] - cs[tid]) * sig[tid];
-        ecs[tid] = __expf(cs[tid]);
-    }
-    for (int e = tid; e < Q * (P / 8); e += kThreads) {
-        const int s = e / (P / 8), p8 = (e % (P / 8)) * 8;
-        const int64_t t = c * Q + s;
-        const u32x4 v = ld8(p.x + ((b * p.L + t) * p.H + h) * p.P + p8, t < p.L);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Xt[p8 + 2 * i][s] = (uint16_t)(v[i] & 0xffffu);
-            Xt[p8 + 2 * i + 1][s] = (uint16_t)(v[i] >> 16);
-        }
-    }
-    __syncthreads();
-
-    const float Dh = p.D ? p.D[h] : 0.0f;
-    const bool has_state = (c > 0) || (p.h0 != nullptr);
+    const int col = lane & 31, hh = lane >> 5, half = (lane >> 4) & 1;
     const int64_t rowBC = p.G * p.N;                       // elements between time steps of B/C
     const uint16_t *Bbase = p.B + ((b * p.L + c * Q) * p.G + g) * p.N;
     const uint16_t *Cbase = p.C + ((b * p.L + c * Q) * p.G + g) * p.N;
     const int64_t tmax = p.L - c * Q;                      // valid rows in this chunk
 
-    for (int tb = 0; tb < NTB; ++tb) {
-        const int owner = ((tb / 4) & 1) ? 3 - (tb & 3) : (tb & 3);   // snake: balanced causal work
-        if (owner != wid) continue;
-        const int t0 = tb * 32;
-        const int trow = t0 + col;                          // this lane's time row (A-operand view)
+    // ---- C.B^T tiles of this wave, accumulated over slabs of the state index
+    f32x16 G[NSLOT];
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) G[i] = f32x16{};
+    for (int n0 = 0; n0 < p.N; n0 += NS) {
+        const int ns = (int)min((int64_t)NS, p.N - n0);
+        __syncthreads();
+        for (int e = tid; e < Q * (ns / 8); e += kThreads) {
+            const int s = e / (ns / 8), n8 = (e % (ns / 8)) * 8;
+            const bool ok = s < tmax;
+            *reinterpret_cast<u32x4 *>(&Bs[s * BCP + n8]) = ld8(Bbase + s * rowBC + n0 + n8, ok);
+            *reinterpret_cast<u32x4 *>(&Cs[s * BCP + n8]) = ld8(Cbase + s * rowBC + n0 + n8, ok);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int slot = 0; slot < NSLOT; ++slot) {
+            int tb, sb;
+            if (!slot_tile<Q>(wid, slot, tb, sb)) continue;
+            for (int k = 0; k < ns; k += 16) {
+                const u32x4 A = *reinterpret_cast<const u32x4 *>(&Bs[(sb * 32 + col) * BCP + k + hh * 8]);
+                const u32x4 Bo = *reinterpret_cast<const u32x4 *>(&Cs[(tb * 32 + col) * BCP + k + hh * 8]);
+                G[slot] = mfma32(A, Bo, G[slot]);   // G^T[s][t]: lane column t, rows s
+            }
+        }
+    }
+
+    const bool has_state_c = c > 0;
+    for (int64_t h = hfirst; h < hfirst + p.hb; ++h) {
+        chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);    // barrier at entry: arena free for x
+        if (tid < Q) {
+            const int e = (tid | 31);
+            gS[tid] = __expf(cs[e] - cs[tid]) * sig[tid];
+            ecs[tid] = __expf(cs[tid]);
+        }
+        for (int e = tid; e < Q * (P / 8); e += kThreads) {
+            const int s = e / (P / 8), q8 = (e % (P / 8)) * 8;
+            *reinterpret_cast<u32x4 *>(&Xs[s * XP + q8]) =
+                ld8(p.x + ((b * p.L + c * Q + s) * p.H + h) * p.P + q8, s < tmax);
+        }
+        __syncthreads();
+
+        const float Dh = p.D ? p.D[h] : 0.0f;
+        const bool has_state = has_state_c || (p.h0 != nullptr);
+        const float *Sb = p.states + ((b * p.nc + c) * p.H + h) * p.P * p.N;
+        int cur_tb = -1;
         f32x16 yacc[PT];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x16{};
-
-        for (int sb = 0; sb <= tb; ++sb) {
-            const int s0 = sb * 32;
-            // G^T tile: rows s (this lane: s0 + j*8 + hh*4 + i), column t = trow
-            f32x16 gacc{};
-            const int srow = s0 + col;
-            for (int k = 0; k < p.N; k += 16) {
-                const u32x4 A = ld8(Bbase + srow * rowBC + k + hh * 8, srow < tmax);
-                const u32x4 Bo = ld8(Cbase + trow * rowBC + k + hh * 8, trow < tmax);
-                gacc = mfma32(A, Bo, gacc);
+        for (int slot = 0; slot < NSLOT; ++slot) {
+            int tb, sb;
+            if (!slot_tile<Q>(wid, slot, tb, sb)) continue;
+            if (tb != cur_tb) {
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x16{};
+                cur_tb = tb;
             }
+            const int t0 = tb * 32, s0 = sb * 32;
+            const int trow = t0 + col;
             // M[t, s] = G[t, s] e^{cs_t - cs_s} sigma_s as hi + lo bf16 fragments
             float mv[16];
             if (sb < tb) {
@@ -315,14 +378,14 @@ ssd_chunk_scan_kernel(SsdKp p) {
 #pragma unroll
                 for (int idx = 0; idx < 16; ++idx) {
                     const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
-                    mv[idx] = gacc[idx] * ft * gS[s];
+                    mv[idx] = G[slot][idx] * ft * gS[s];
                 }
             } else {
                 const float ct = cs[trow];
 #pragma unroll
                 for (int idx = 0; idx < 16; ++idx) {
                     const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
-                    mv[idx] = (s <= trow) ? gacc[idx] * __expf(ct - cs[s]) * sig[s] : 0.0f;
+                    mv[idx] = (s <= trow) ? G[slot][idx] * __expf(ct - cs[s]) * sig[s] : 0.0f;
                 }
             }
             uint2 q[8];
@@ -330,63 +393,57 @@ ssd_chunk_scan_kernel(SsdKp p) {
             for (int i = 0; i < 8; ++i) q[i] = split_bf16(mv[2 * i], mv[2 * i + 1]);
             const u32x4 m0h{q[0].x, q[1].x, q[2].x, q[3].x}, m0l{q[0].y, q[1].y, q[2].y, q[3].y};
             const u32x4 m1h{q[4].x, q[5].x, q[6].x, q[7].x}, m1l{q[4].y, q[5].y, q[6].y, q[7].y};
-            // y[t, p] += sum_s M[t, s] X[s, p]; K-slot order matches the G^T layout
+            // y[t, p] += sum_s M[t, s] x[s, p]; the K-slot order follows the G^T layout
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const uint16_t *xr = &Xt[pt * 32 + col][0];
-                u32x4 x0, x1;
-                {
-                    const uint2 a = *reinterpret_cast<const uint2 *>(xr + s0 + hh * 4);
-                    const uint2 bq = *reinterpret_cast<const uint2 *>(xr + s0 + 8 + hh * 4);
-                    x0 = u32x4{a.x, a.y, bq.x, bq.y};
-                }
-                {
-                    const uint2 a = *reinterpret_cast<const uint2 *>(xr + s0 + 16 + hh * 4);
-                    const uint2 bq = *reinterpret_cast<const uint2 *>(xr + s0 + 24 + hh * 4);
-                    x1 = u32x4{a.x, a.y, bq.x, bq.y};
-                }
+                const int cb = pt * 32 + half * 16;
+                const uint2 a0 = tr_read(Xs, XP, s0 + hh * 4, cb, lane);
+                const uint2 a1 = tr_read(Xs, XP, s0 + 8 + hh * 4, cb, lane);
+                const uint2 b0 = tr_read(Xs, XP, s0 + 16 + hh * 4, cb, lane);
+                const uint2 b1 = tr_read(Xs, XP, s0 + 24 + hh * 4, cb, lane);
+                const u32x4 x0{a0.x, a0.y, a1.x, a1.y}, x1{b0.x, b0.y, b1.x, b1.y};
                 yacc[pt] = mfma32(m0h, x0, yacc[pt]);
                 yacc[pt] = mfma32(m0l, x0, yacc[pt]);
                 yacc[pt] = mfma32(m1h, x1, yacc[pt]);
                 yacc[pt] = mfma32(m1l, x1, yacc[pt]);
             }
-        }
+            if (sb != tb) continue;   // the diagonal tile is the last of its time block
 
-        // D5: state entering the chunk, y[t, p] += e^{cs_t} sum_n C[t, n] S[p, n]
-        if (has_state) {
-            const float *Sb = p.states + ((b * p.nc + c) * p.H + h) * p.P * p.N;
+            // D5: y[t, p] += e^{cs_t} sum_n C[t, n] S[p, n]
+            if (has_state) {
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                f32x16 sacc{};
-                for (int k = 0; k < p.N; k += 16) {
-                    const u32x4 A = ld8(Cbase + trow * rowBC + k + hh * 8, trow < tmax);
-                    u32x4 Sh, Sl;
-                    ld8f_split(Sb + (pt * 32 + col) * p.N + k + hh * 8, Sh, Sl);
-                    sacc = mfma32(A, Sh, sacc);
-                    sacc = mfma32(A, Sl, sacc);
-                }
+                for (int pt = 0; pt < PT; ++pt) {
+                    f32x16 sacc{};
+                    for (int k = 0; k < p.N; k += 16) {
+                        const u32x4 A = ld8(Cbase + trow * rowBC + k + hh * 8, trow < tmax);
+                        u32x4 Sh, Sl;
+                        ld8f_split(Sb + (pt * 32 + col) * p.N + k + hh * 8, Sh, Sl);
+                        sacc = mfma32(A, Sh, sacc);
+                        sacc = mfma32(A, Sl, sacc);
+                    }
 #pragma unroll
-                for (int idx = 0; idx < 16; ++idx) {
-                    const int t = t0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
-                    yacc[pt][idx] = fmaf(ecs[t], sacc[idx], yacc[pt][idx]);
+                    for (int idx = 0; idx < 16; ++idx) {
+                        const int t = t0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
+                        yacc[pt][idx] = fmaf(ecs[t], sacc[idx], yacc[pt][idx]);
+                    }
                 }
             }
-        }
-        // D skip and store: column p = pt*32 + col, rows t = t0 + j*8 + hh*4 + i
+            // D skip and store: column p = pt*32 + col, rows t = t0 + j*8 + hh*4 + i
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const int pc = pt * 32 + col;
+            for (int pt = 0; pt < PT; ++pt) {
+                const int pc = pt * 32 + col;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tr = t0 + j * 8 + hh * 4;
-                const uint2 xv = *reinterpret_cast<const uint2 *>(&Xt[pc][tr]);
-                const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
+                for (int j = 0; j < 4; ++j) {
+                    const int tr = t0 + j * 8 + hh * 4;
+                    const uint2 xv = tr_read(Xs, XP, tr, pt * 32 + half * 16, lane);
+                    const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tr + i;
-                    if (t < tmax)
-                        p.y[((b * p.L + c * Q + t) * p.H + h) * p.P + pc] =
-                            fmaf(Dh, xs[i], yacc[pt][j * 4 + i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = tr + i;
+                        if (t < tmax)
+                            p.y[((b * p.L + c * Q + t) * p.H + h) * p.P + pc] =
+                                fmaf(Dh, xs[i], yacc[pt][j * 4 + i]);
+                    }
                 }
             }
         }
@@ -395,7 +452,7 @@ ssd_chunk_scan_kernel(SsdKp p) {
 
 template <int Q, int P>
 hipError_t launch_qp(const SsdKp &kp, hipStream_t s) {
-    const int64_t nwork = kp.batch * kp.nc * kp.H;
+    const int64_t nwork = kp.batch * kp.nc * (kp.H / kp.hb);
     hipLaunchKernelGGL((ssd_chunk_state_kernel<Q, P>), dim3((unsigned)nwork), dim3(kThreads), 0, s, kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -412,6 +469,17 @@ hipError_t launch_q(const SsdKp &kp, hipStream_t s) {
     if (kp.P == 32) return launch_qp<Q, 32>(kp, s);
     if (kp.P == 64) return launch_qp<Q, 64>(kp, s);
     return launch_qp<Q, 128>(kp, s);
+}
+
+// Heads per work item: a divisor of the heads of one group, as large as keeps at
+// least ~2 work items per compute unit.
+int64_t pick_head_block(int64_t batch, int64_t nc, int64_t H, int64_t G) {
+    const int64_t hpg = H / G;
+    for (int64_t hb = hpg; hb >= 1; --hb) {
+        if (hpg % hb != 0) continue;
+        if (batch * nc * (H / hb) >= 512) return hb;
+    }
+    return 1;
 }
 
 }  // namespace
@@ -434,6 +502,7 @@ hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_
     p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
     p.batch = a.batch; p.L = a.L; p.H = a.nheads; p.P = a.headdim; p.N = a.d_state; p.G = a.ngroups;
     p.nc = (a.L + a.chunk_len - 1) / a.chunk_len;
+    p.hb = pick_head_block(p.batch, p.nc, p.H, p.G);
     const int64_t nc = p.nc;
     const size_t st = (size_t)a.batch * nc * a.nheads * a.headdim * a.d_state * sizeof(float);
     p.states = static_cast<float *>(a.workspace);
