@@ -102,7 +102,7 @@ s6_scan_kernel(S6Kp p) {
     constexpr int EPT = 16 / G;          // (t, d) elements per thread per tile
     __shared__ __attribute__((aligned(16))) float sD[2][CW][kTS];
     __shared__ __attribute__((aligned(16))) float sU[2][CW][kTS];
-    __shared__ __attribute__((aligned(16))) float sY[2][G][CW][kTS];
+    __shared__ __attribute__((aligned(16))) float sY[2][G][kT][CW];
 
     const int tid = threadIdx.x;
     const int row = tid >> 4, k = tid & 15;
@@ -131,10 +131,12 @@ s6_scan_kernel(S6Kp p) {
     }
     // per-element constants of the (t, d) elements this thread stages/reduces
     float biasv[EPT], Dv[EPT];
+    bool cval[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int c = (tid + kThreads * i) % CW;
         const bool ok = d0 + c < p.Dm;
+        cval[i] = ok;
         biasv[i] = (ok && p.dt_bias) ? p.dt_bias[d0 + c] : 0.0f;
         Dv[i] = (ok && p.D) ? p.D[d0 + c] : 0.0f;
     }
@@ -169,12 +171,13 @@ s6_scan_kernel(S6Kp p) {
     Raw<TIN, G, SPL> RA, RB;
     float du_prev[EPT], du_cur[EPT];
 
-    auto stage = [&](int buf, int64_t t0, const Raw<TIN, G, SPL> &R) __attribute__((always_inline)) {
+    auto stage = [&](int buf, int64_t t0, const Raw<TIN, G, SPL> &R, auto chkTag) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int e = tid + kThreads * i;
             const int tl = e / CW, c = e % CW;
-            const bool ok = t0 + tl < p.L && d0 + c < p.Dm;
+            bool ok = cval[i];
+            if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < p.L);
             const float dl = ok ? softplus(R.dt[i] + biasv[i]) : 0.0f;
             const float uu = ok ? R.u[i] : 0.0f;
             sD[buf][c][tl] = dl;
@@ -226,20 +229,22 @@ s6_scan_kernel(S6Kp p) {
                 }
                 yp[t] = ys;
             });
-            *reinterpret_cast<float4 *>(&sY[buf][g][cl][4 * q]) =
-                make_float4(yp[4 * q], yp[4 * q + 1], yp[4 * q + 2], yp[4 * q + 3]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sY[buf][g][4 * q + i][cl] = yp[4 * q + i];
         });
     };
 
-    auto reduce = [&](int buf, int64_t t0) __attribute__((always_inline)) {
+    auto reduce = [&](int buf, int64_t t0, auto chkTag) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int e = tid + kThreads * i;
             const int tl = e / CW, c = e % CW;
             float s = du_prev[i];
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg) s += sY[buf][gg][c][tl];
-            if (t0 + tl < p.L && d0 + c < p.Dm) q.y[i][t0 * p.Dm] = s;
+            for (int gg = 0; gg < G; ++gg) s += sY[buf][gg][tl][c];
+            bool ok = cval[i];
+            if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < p.L);
+            if (ok) q.y[i][t0 * p.Dm] = s;
         }
     };
 
@@ -251,10 +256,10 @@ s6_scan_kernel(S6Kp p) {
         __attribute__((always_inline)) {
         const int buf = (int)(kt & 1);
         compute(buf, Rk, accTag);
-        reduce(buf ^ 1, (kt - 1) * kT);
+        reduce(buf ^ 1, (kt - 1) * kT, std::false_type{});
 #pragma unroll
         for (int i = 0; i < EPT; ++i) du_prev[i] = du_cur[i];
-        stage(buf ^ 1, (kt + 1) * kT, Rn);
+        stage(buf ^ 1, (kt + 1) * kT, Rn, std::false_type{});
         load_raw<false>(Rk, q, p, (kt + 2) * kT, tid, k);
         __syncthreads();
     };
@@ -262,10 +267,10 @@ s6_scan_kernel(S6Kp p) {
         __attribute__((always_inline)) {
         const int buf = (int)(kt & 1);
         compute(buf, Rk, accTag);
-        if (kt >= 1) reduce(buf ^ 1, (kt - 1) * kT);
+        if (kt >= 1) reduce(buf ^ 1, (kt - 1) * kT, std::true_type{});
 #pragma unroll
         for (int i = 0; i < EPT; ++i) du_prev[i] = du_cur[i];
-        if (kt + 1 < ntiles) stage(buf ^ 1, (kt + 1) * kT, Rn);
+        if (kt + 1 < ntiles) stage(buf ^ 1, (kt + 1) * kT, Rn, std::true_type{});
         if (kt + 2 < ntiles) load_raw<true>(Rk, q, p, (kt + 2) * kT, tid, k);
         __syncthreads();
     };
@@ -286,11 +291,11 @@ s6_scan_kernel(S6Kp p) {
 
     load_raw<true>(RA, q, p, 0, tid, k);
     if (ntiles > 1) load_raw<true>(RB, q, p, kT, tid, k);
-    stage(0, 0, RA);
+    stage(0, 0, RA, std::true_type{});
     __syncthreads();
     if (acc_wave) run(std::true_type{});
     else run(std::false_type{});
-    reduce((int)((ntiles - 1) & 1), (ntiles - 1) * kT);
+    reduce((int)((ntiles - 1) & 1), (ntiles - 1) * kT, std::true_type{});
 
     if (p.h_final) {
 #pragma unroll

@@ -295,15 +295,22 @@ __device__ __forceinline__ bool slot_tile(int w, int slot, int &tb, int &sb) {
 template <int Q, int P>
 __global__ void __launch_bounds__(kThreads)
 ssd_chunk_scan_kernel(SsdKp p) {
-    constexpr int NS = 64, BCP = NS + 8;                // B/C slab width and pitch (bf16)
+    constexpr int NS1 = 64, SP1 = NS1 + 8;              // B/C slab (phase 1) width and pitch
+    constexpr int NS2 = P <= 64 ? 128 : 64, SP2 = NS2 + 8;  // C and S slab (phase 2)
     constexpr int XP = P + 8;                           // x tile pitch (bf16)
     constexpr int PT = P / 32;
     constexpr int NSLOT = Plan<Q>::NSLOT;
-    constexpr int SLAB_E = 2 * Q * BCP, X_E = Q * XP;
-    constexpr int ARENA = SLAB_E > X_E ? SLAB_E : X_E;
+    constexpr int NTBW = (Q == 256) ? 2 : 1;            // time blocks per wave
+    // LDS arena: phase 1 holds B and C slabs; phase 2 holds x, a C slab and the
+    // hi/lo parts of a slab of the entering state S[p][n]
+    constexpr int PH1 = 2 * Q * SP1;
+    constexpr int PH2 = Q * XP + Q * SP2 + 2 * P * SP2;
+    constexpr int ARENA = PH1 > PH2 ? PH1 : PH2;
     __shared__ float cs[Q], sig[Q], gS[Q], ecs[Q], wsum[4];
     __shared__ __attribute__((aligned(16))) uint16_t arena[ARENA];
-    uint16_t *Bs = arena, *Cs = arena + Q * BCP, *Xs = arena;
+    uint16_t *Bs = arena, *Cs1 = arena + Q * SP1;                  // phase 1
+    uint16_t *Xs = arena, *Cs = arena + Q * XP;                    // phase 2
+    uint16_t *Sh = Cs + Q * SP2, *Sl = Sh + P * SP2;
 
     int64_t b, c, hfirst, g;
     decode_work(p, b, c, hfirst, g);
@@ -314,35 +321,38 @@ ssd_chunk_scan_kernel(SsdKp p) {
     const uint16_t *Cbase = p.C + ((b * p.L + c * Q) * p.G + g) * p.N;
     const int64_t tmax = p.L - c * Q;                      // valid rows in this chunk
 
+    auto stage_rows = [&](uint16_t *dst, int pitch, const uint16_t *src, int n0, int ns) {
+        for (int e = tid; e < Q * (ns / 8); e += kThreads) {
+            const int s = e / (ns / 8), n8 = (e % (ns / 8)) * 8;
+            *reinterpret_cast<u32x4 *>(&dst[s * pitch + n8]) = ld8(src + s * rowBC + n0 + n8, s < tmax);
+        }
+    };
+
     // ---- C.B^T tiles of this wave, accumulated over slabs of the state index
     f32x16 G[NSLOT];
 #pragma unroll
     for (int i = 0; i < NSLOT; ++i) G[i] = f32x16{};
-    for (int n0 = 0; n0 < p.N; n0 += NS) {
-        const int ns = (int)min((int64_t)NS, p.N - n0);
+    for (int n0 = 0; n0 < p.N; n0 += NS1) {
+        const int ns = (int)min((int64_t)NS1, p.N - n0);
         __syncthreads();
-        for (int e = tid; e < Q * (ns / 8); e += kThreads) {
-            const int s = e / (ns / 8), n8 = (e % (ns / 8)) * 8;
-            const bool ok = s < tmax;
-            *reinterpret_cast<u32x4 *>(&Bs[s * BCP + n8]) = ld8(Bbase + s * rowBC + n0 + n8, ok);
-            *reinterpret_cast<u32x4 *>(&Cs[s * BCP + n8]) = ld8(Cbase + s * rowBC + n0 + n8, ok);
-        }
+        stage_rows(Bs, SP1, Bbase, n0, ns);
+        stage_rows(Cs1, SP1, Cbase, n0, ns);
         __syncthreads();
 #pragma unroll
         for (int slot = 0; slot < NSLOT; ++slot) {
             int tb, sb;
             if (!slot_tile<Q>(wid, slot, tb, sb)) continue;
             for (int k = 0; k < ns; k += 16) {
-                const u32x4 A = *reinterpret_cast<const u32x4 *>(&Bs[(sb * 32 + col) * BCP + k + hh * 8]);
-                const u32x4 Bo = *reinterpret_cast<const u32x4 *>(&Cs[(tb * 32 + col) * BCP + k + hh * 8]);
+                const u32x4 A = *reinterpret_cast<const u32x4 *>(&Bs[(sb * 32 + col) * SP1 + k + hh * 8]);
+                const u32x4 Bo = *reinterpret_cast<const u32x4 *>(&Cs1[(tb * 32 + col) * SP1 + k + hh * 8]);
                 G[slot] = mfma32(A, Bo, G[slot]);   // G^T[s][t]: lane column t, rows s
             }
         }
     }
 
-    const bool has_state_c = c > 0;
+    const bool one_slab = p.N <= NS2;
     for (int64_t h = hfirst; h < hfirst + p.hb; ++h) {
-        chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);    // barrier at entry: arena free for x
+        chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);    // barrier at entry: arena free
         if (tid < Q) {
             const int e = (tid | 31);
             gS[tid] = __expf(cs[e] - cs[tid]) * sig[tid];
@@ -353,100 +363,127 @@ ssd_chunk_scan_kernel(SsdKp p) {
             *reinterpret_cast<u32x4 *>(&Xs[s * XP + q8]) =
                 ld8(p.x + ((b * p.L + c * Q + s) * p.H + h) * p.P + q8, s < tmax);
         }
-        __syncthreads();
-
-        const float Dh = p.D ? p.D[h] : 0.0f;
-        const bool has_state = has_state_c || (p.h0 != nullptr);
+        const bool has_state = (c > 0) || (p.h0 != nullptr);
         const float *Sb = p.states + ((b * p.nc + c) * p.H + h) * p.P * p.N;
-        int cur_tb = -1;
-        f32x16 yacc[PT];
-#pragma unroll
-        for (int slot = 0; slot < NSLOT; ++slot) {
-            int tb, sb;
-            if (!slot_tile<Q>(wid, slot, tb, sb)) continue;
-            if (tb != cur_tb) {
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x16{};
-                cur_tb = tb;
+        // entering state slab -> bf16 hi/lo parts, row-major [p][n]
+        auto stage_state = [&](int n0, int ns) {
+            for (int e = tid; e < P * (ns / 4); e += kThreads) {
+                const int pp = e / (ns / 4), n4 = (e % (ns / 4)) * 4;
+                const float4 v = *reinterpret_cast<const float4 *>(Sb + pp * p.N + n0 + n4);
+                const uint2 s0 = split_bf16(v.x, v.y), s1 = split_bf16(v.z, v.w);
+                *reinterpret_cast<uint2 *>(&Sh[pp * SP2 + n4]) = make_uint2(s0.x, s1.x);
+                *reinterpret_cast<uint2 *>(&Sl[pp * SP2 + n4]) = make_uint2(s0.y, s1.y);
             }
-            const int t0 = tb * 32, s0 = sb * 32;
-            const int trow = t0 + col;
-            // M[t, s] = G[t, s] e^{cs_t - cs_s} sigma_s as hi + lo bf16 fragments
-            float mv[16];
-            if (sb < tb) {
-                const float ft = __expf(cs[trow] - cs[s0 + 31]);
-#pragma unroll
-                for (int idx = 0; idx < 16; ++idx) {
-                    const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
-                    mv[idx] = G[slot][idx] * ft * gS[s];
-                }
-            } else {
-                const float ct = cs[trow];
-#pragma unroll
-                for (int idx = 0; idx < 16; ++idx) {
-                    const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
-                    mv[idx] = (s <= trow) ? G[slot][idx] * __expf(ct - cs[s]) * sig[s] : 0.0f;
-                }
-            }
-            uint2 q[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = split_bf16(mv[2 * i], mv[2 * i + 1]);
-            const u32x4 m0h{q[0].x, q[1].x, q[2].x, q[3].x}, m0l{q[0].y, q[1].y, q[2].y, q[3].y};
-            const u32x4 m1h{q[4].x, q[5].x, q[6].x, q[7].x}, m1l{q[4].y, q[5].y, q[6].y, q[7].y};
-            // y[t, p] += sum_s M[t, s] x[s, p]; the K-slot order follows the G^T layout
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const int cb = pt * 32 + half * 16;
-                const uint2 a0 = tr_read(Xs, XP, s0 + hh * 4, cb, lane);
-                const uint2 a1 = tr_read(Xs, XP, s0 + 8 + hh * 4, cb, lane);
-                const uint2 b0 = tr_read(Xs, XP, s0 + 16 + hh * 4, cb, lane);
-                const uint2 b1 = tr_read(Xs, XP, s0 + 24 + hh * 4, cb, lane);
-                const u32x4 x0{a0.x, a0.y, a1.x, a1.y}, x1{b0.x, b0.y, b1.x, b1.y};
-                yacc[pt] = mfma32(m0h, x0, yacc[pt]);
-                yacc[pt] = mfma32(m0l, x0, yacc[pt]);
-                yacc[pt] = mfma32(m1h, x1, yacc[pt]);
-                yacc[pt] = mfma32(m1l, x1, yacc[pt]);
-            }
-            if (sb != tb) continue;   // the diagonal tile is the last of its time block
+        };
+        if (has_state && one_slab) {
+            stage_rows(Cs, SP2, Cbase, 0, (int)p.N);
+            stage_state(0, (int)p.N);
+        }
+        __syncthreads();
+        const float Dh = p.D ? p.D[h] : 0.0f;
 
-            // D5: y[t, p] += e^{cs_t} sum_n C[t, n] S[p, n]
-            if (has_state) {
+        // one time block of this wave: state term, intra-chunk term, skip, store
+        // Every wave runs do_block (the slab loop below has barriers); waves
+        // without a time block of their own (short chunks) only take part in
+        // the barriers and staging.
+        auto do_block = [&](int i) __attribute__((always_inline)) {
+            const int tb = (i == 0) ? wid : 7 - wid;
+            const bool active = tb < Q / 32;
+            const int t0 = active ? tb * 32 : 0;
+            f32x16 yacc[PT];
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    f32x16 sacc{};
-                    for (int k = 0; k < p.N; k += 16) {
-                        const u32x4 A = ld8(Cbase + trow * rowBC + k + hh * 8, trow < tmax);
-                        u32x4 Sh, Sl;
-                        ld8f_split(Sb + (pt * 32 + col) * p.N + k + hh * 8, Sh, Sl);
-                        sacc = mfma32(A, Sh, sacc);
-                        sacc = mfma32(A, Sl, sacc);
+            for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x16{};
+            // D5: yacc = e^{cs_t} sum_n C[t, n] S[p, n]
+            if (has_state) {
+                for (int n0 = 0; n0 < p.N; n0 += NS2) {
+                    const int ns = (int)min((int64_t)NS2, p.N - n0);
+                    if (!one_slab) {
+                        __syncthreads();
+                        stage_rows(Cs, SP2, Cbase, n0, ns);
+                        stage_state(n0, ns);
+                        __syncthreads();
                     }
+                    if (active)
+                    for (int k = 0; k < ns; k += 16) {
+                        const u32x4 A = *reinterpret_cast<const u32x4 *>(&Cs[(t0 + col) * SP2 + k + hh * 8]);
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt) {
+                            const u32x4 Shv = *reinterpret_cast<const u32x4 *>(&Sh[(pt * 32 + col) * SP2 + k + hh * 8]);
+                            const u32x4 Slv = *reinterpret_cast<const u32x4 *>(&Sl[(pt * 32 + col) * SP2 + k + hh * 8]);
+                            yacc[pt] = mfma32(A, Shv, yacc[pt]);
+                            yacc[pt] = mfma32(A, Slv, yacc[pt]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int idx = 0; idx < 16; ++idx)
+                        yacc[pt][idx] *= ecs[t0 + (idx >> 2) * 8 + hh * 4 + (idx & 3)];
+            }
+            if (!active) return;
+            // D4: yacc += sum_s M[t, s] x[s, p], M = G o L as hi + lo bf16 fragments
+#pragma unroll
+            for (int slot = 0; slot < NSLOT; ++slot) {
+                int tbs, sb;
+                if (!slot_tile<Q>(wid, slot, tbs, sb) || tbs != tb) continue;
+                const int s0 = sb * 32;
+                const int trow = t0 + col;
+                float mv[16];
+                if (sb < tb) {
+                    const float ft = __expf(cs[trow] - cs[s0 + 31]);
 #pragma unroll
                     for (int idx = 0; idx < 16; ++idx) {
-                        const int t = t0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
-                        yacc[pt][idx] = fmaf(ecs[t], sacc[idx], yacc[pt][idx]);
+                        const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
+                        mv[idx] = G[slot][idx] * ft * gS[s];
                     }
+                } else {
+                    const float ct = cs[trow];
+#pragma unroll
+                    for (int idx = 0; idx < 16; ++idx) {
+                        const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
+                        mv[idx] = (s <= trow) ? G[slot][idx] * __expf(ct - cs[s]) * sig[s] : 0.0f;
+                    }
+                }
+                uint2 q[8];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) q[ii] = split_bf16(mv[2 * ii], mv[2 * ii + 1]);
+                const u32x4 m0h{q[0].x, q[1].x, q[2].x, q[3].x}, m0l{q[0].y, q[1].y, q[2].y, q[3].y};
+                const u32x4 m1h{q[4].x, q[5].x, q[6].x, q[7].x}, m1l{q[4].y, q[5].y, q[6].y, q[7].y};
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const int cb = pt * 32 + half * 16;
+                    const uint2 a0 = tr_read(Xs, XP, s0 + hh * 4, cb, lane);
+                    const uint2 a1 = tr_read(Xs, XP, s0 + 8 + hh * 4, cb, lane);
+                    const uint2 b0 = tr_read(Xs, XP, s0 + 16 + hh * 4, cb, lane);
+                    const uint2 b1 = tr_read(Xs, XP, s0 + 24 + hh * 4, cb, lane);
+                    const u32x4 x0{a0.x, a0.y, a1.x, a1.y}, x1{b0.x, b0.y, b1.x, b1.y};
+                    yacc[pt] = mfma32(m0h, x0, yacc[pt]);
+                    yacc[pt] = mfma32(m0l, x0, yacc[pt]);
+                    yacc[pt] = mfma32(m1h, x1, yacc[pt]);
+                    yacc[pt] = mfma32(m1l, x1, yacc[pt]);
                 }
             }
             // D skip and store: column p = pt*32 + col, rows t = t0 + j*8 + hh*4 + i
+            float *yb = p.y + ((b * p.L + c * Q + t0) * p.H + h) * p.P;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int pc = pt * 32 + col;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int tr = t0 + j * 8 + hh * 4;
-                    const uint2 xv = tr_read(Xs, XP, tr, pt * 32 + half * 16, lane);
+                    const int tr = j * 8 + hh * 4;
+                    const uint2 xv = tr_read(Xs, XP, t0 + tr, pt * 32 + half * 16, lane);
                     const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = tr + i;
-                        if (t < tmax)
-                            p.y[((b * p.L + c * Q + t) * p.H + h) * p.P + pc] =
-                                fmaf(Dh, xs[i], yacc[pt][j * 4 + i]);
+                    for (int ii = 0; ii < 4; ++ii) {
+                        if (t0 + tr + ii < tmax)
+                            yb[(int64_t)(tr + ii) * p.H * p.P + pc] = fmaf(Dh, xs[ii], yacc[pt][j * 4 + ii]);
                     }
                 }
             }
-        }
+        };
+        do_block(0);
+        if constexpr (NTBW == 2) do_block(1);
     }
 }
 
