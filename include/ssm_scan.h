@@ -117,9 +117,11 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
  *   y[b,t,h,p]   = sum_n C[b,t,g,n] * S_t[p,n] + D[h] * x[b,t,h,p]
  * with group g = floor(h * ngroups / nheads), S_{-1} = h0 (or 0) and
  * h_final = S_{L-1}.  sigma follows flags bits 0-1 (default SSM_BBAR_DT,
- * i.e. sigma = delta).  The sequence is cut into chunks of chunk_len steps (the
- * last may be partial); the result does not depend on chunk_len beyond
- * rounding.
+ * i.e. sigma = delta).  The method cuts the sequence into chunks; the result
+ * does not depend on the chunk length beyond rounding.  chunk_len is checked
+ * against the limits below and otherwise only names the caller's model
+ * setting: the kernel walks the sequence in its own 32-step blocks, carrying
+ * the state of each (batch, head) on chip from block to block.
  *
  * Layouts: x (batch, L, nheads, headdim) bf16; dt (batch, L, nheads) fp32;
  * dt_bias, A_log, D (nheads) fp32; B, C (batch, L, ngroups, d_state) bf16;
@@ -127,7 +129,8 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
  * in_dtype must be SSM_BF16 (the contractions run on bf16 MFMA; SSM_F32 returns
  * SSM_ERR_UNSUPPORTED).  Limits: nheads % ngroups == 0; headdim in {32, 64, 128};
  * d_state a multiple of 32, <= 256; chunk_len in {64, 128, 256}.
- * Workspace: ssd_chunk_scan_fwd_workspace_size() bytes (chunk states). */
+ * No workspace is needed (ssd_chunk_scan_fwd_workspace_size returns 0;
+ * workspace may be NULL). */
 size_t ssd_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                                          int64_t d_state, int64_t ngroups, int64_t chunk_len);
 

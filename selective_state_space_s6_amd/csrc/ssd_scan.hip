@@ -1,132 +1,75 @@
-// ssd_scan.hip -- Mamba-2 state-space-dual (SSD) chunked forward scan, gfx950.
+// ssd_scan.hip -- Mamba-2 state-space-dual (SSD) forward scan, gfx950.
 //
 // Implements the scalar-A-per-head recurrence of builderforce-memory-engine
-// ssd.js (header comment, ssd_chunk_forward) by the chunked decomposition whose
-// kernel sequence mamba-rs 0.2.1 mamba3_gpu.rs step F6 launches (K2 dA cumsum,
-// K3 chunk state, K4 state passing, K5 chunk scan, final-state writeback):
+// ssd.js (header comment, ssd_chunk_forward) by the chunked decomposition that
+// mamba-rs 0.2.1 mamba3_gpu.rs step F6 launches as separate kernels (dA
+// cumsum, chunk state, state passing, chunk scan, final-state writeback).  Here
+// the whole decomposition runs in one kernel over 32-step chunks:
 //
 //   D1  per chunk: delta = softplus(dt + dt_bias), a = delta*A_h, cs = cumsum(a),
-//       input scale sigma (delta by default)                     [in K1 and K3]
-//   D2  chunk-local end state  Shat[p,n] = sum_s e^{cs_end-cs_s} sigma_s x_s[p] B_s[n]
-//       as a bf16 MFMA contraction over the chunk's time steps      [K1]
-//   D3  S_0 = h0, S_{c+1} = e^{cs_end(c)} S_c + Shat_c, h_final = S_nc [K2]
-//   D4  y_intra = ((C B^T) o Lmask) X with Lmask[t,s] = e^{cs_t-cs_s} sigma_s, s<=t
-//   D5  y += e^{cs_t} C_t S_c + D x_t                                  [K3]
+//       input scale sigma (delta by default)
+//   D4  y_intra = ((C B^T) o L) X with L[t,s] = e^{cs_t-cs_s} sigma_s, s <= t
+//   D5  y += e^{cs_t} C_t S + D x_t
+//   D2  chunk-local state  B^T (w o X),  w_s = e^{cs_end-cs_s} sigma_s
+//   D3  S <- e^{cs_end} S + B^T (w o X); after the last chunk S is h_final
 //
-// All contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the
-// decay mask is factorised per 32x32 tile so that every exponent is <= 0.
-// Inputs x, B, C are bf16 and enter the MFMA exactly.  Operands that are
-// products formed in fp32 (the decay-weighted inputs, the masked C.B^T, the
-// carried state) are split into bf16 hi + lo parts and contracted twice, so the
-// path keeps ~16 mantissa bits on them instead of bf16's 8.
+// A work item is (batch, head, 32 head channels); each of its two waves owns 16
+// channels and keeps its N x 16 slice of the fp32 state in MFMA accumulators
+// for the whole sequence, so the inter-chunk pass (D3) never leaves registers
+// and x, B, C are read once.  Every contraction is a bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation.  x, B, C are bf16 and
+// exact; products formed in fp32 (w o X, the masked C.B^T, the state) are
+// split into bf16 hi + lo parts and contracted twice, keeping ~16 mantissa
+// bits.  Chunks are double-buffered in LDS; loads of chunk j+1 are in flight
+// while chunk j is computed.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace ssm {
 namespace {
 
-// bf16 operands are handled as raw 16-bit patterns in 32-bit lanes and only
-// reinterpreted as a whole vector at the MFMA: element-wise access to __bf16
+// bf16 operands travel as raw 16-bit patterns in 32-bit lanes and are
+// reinterpreted as whole vectors at the MFMA: element-wise access to __bf16
 // vectors is avoided on purpose.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kT = 32;           // steps per chunk
+constexpr int kWaves = 2;        // waves per work item
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPW = 16 * kWaves; // head channels per work item
 
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-
-// two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), low half = a
+// two fp32 -> two bf16 (round to nearest even), low half = a
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     const bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
     return __builtin_bit_cast(uint32_t, r);
 }
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// split fp32 pairs v = hi + lo with hi, lo bf16: the pair carries ~16 mantissa bits
-// returns {hi, lo}
+// v = hi + lo with hi, lo bf16; returns {hi pair, lo pair}
 __device__ __forceinline__ uint2 split_bf16(float a, float b) {
     const uint32_t hi = pack_bf16(a, b);
     return make_uint2(hi, pack_bf16(a - lo_f(hi), b - hi_f(hi)));
 }
-
-// 8 consecutive bf16 from global memory (16 B), zero when !ok
 __device__ __forceinline__ u32x4 ld8(const uint16_t *p, bool ok) {
     if (!ok) return u32x4{0u, 0u, 0u, 0u};
     return *reinterpret_cast<const u32x4 *>(p);
-}
-// 8 consecutive fp32 from global memory, split into bf16 hi and lo parts
-__device__ __forceinline__ void ld8f_split(const float *p, u32x4 &hi, u32x4 &lo) {
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    const uint2 s0 = split_bf16(a.x, a.y), s1 = split_bf16(a.z, a.w);
-    const uint2 s2 = split_bf16(b.x, b.y), s3 = split_bf16(b.z, b.w);
-    hi = u32x4{s0.x, s1.x, s2.x, s3.x};
-    lo = u32x4{s0.y, s1.y, s2.y, s3.y};
-}
-// element i (0..7) of 8 bf16 packed in a u32x4, as fp32
-__device__ __forceinline__ float elem_f(const u32x4 &v, int i) {
-    const uint32_t w = v[i >> 1];
-    return (i & 1) ? hi_f(w) : lo_f(w);
-}
-
-struct SsdKp {
-    const uint16_t *x; const float *dt; const float *dt_bias; const float *A_log;
-    const uint16_t *B; const uint16_t *C; const float *D; float *y;
-    const float *h0; float *h_final;
-    float *states;      // [batch][nc][H][P][N]  chunk-local end states, then entering states
-    float *chunk_a;     // [batch][H][nc]         sum of a over each chunk
-    int64_t batch, L, H, P, N, G, nc;
-    int64_t hb;         // heads per work item (a divisor of H / G)
-    int mode;           // 0 ZOH, 1 DT, 2 ONE
-};
-
-// D1 for one chunk: fills cs[0..Q) (inclusive cumulative sum of a, zero past L)
-// and sig[0..Q) (input scale, zero past L).  Needs kThreads >= Q.
-template <int Q>
-__device__ __forceinline__ void chunk_scalars(const SsdKp &p, int64_t b, int64_t c, int64_t h,
-                                              float *cs, float *sig, float *wsum) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
-    const float A = -expf(p.A_log[h]);
-    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
-    float a = 0.0f, sg = 0.0f;
-    const int64_t t = c * Q + tid;
-    if (tid < Q && t < p.L) {
-        const float dl = softplus(p.dt[(b * p.L + t) * p.H + h] + bias);
-        a = dl * A;
-        if (p.mode == 1) sg = dl;
-        else if (p.mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
-        else sg = 1.0f;
-    }
-    float v = a;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
-    if (lane == 63) wsum[wid] = v;
-    __syncthreads();
-    float pre = 0.0f;
-    for (int w = 0; w < wid; ++w) pre += wsum[w];
-    v += pre;
-    if (tid < Q) { cs[tid] = v; sig[tid] = sg; }
-    __syncthreads();
 }
 
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
 // names a row of 4 consecutive 16-bit elements and receives element (i % 4) of
 // rows i/4, i/4 + 4, i/4 + 8, i/4 + 12.  Pointing row i at (step sb + i/4,
-// column cb + 4*(i%4)) of a row-major [step][column] tile therefore hands lane
-// i the four steps sb..sb+3 of column cb + i: the layout an MFMA operand needs
-// when the time step is the contraction index.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// column cb + 4*(i%4)) of a row-major [step][column] tile hands lane i the four
+// steps sb..sb+3 of column cb + i: the layout an MFMA operand needs when the
+// time step is the contraction index.
 __device__ __forceinline__ uint2 tr_read(const uint16_t *tile, int pitch, int sb, int cb, int lane) {
     const int i = lane & 15;
     const uint16_t *a = tile + (sb + (i >> 2)) * pitch + cb + 4 * (i & 3);
@@ -135,402 +78,323 @@ __device__ __forceinline__ uint2 tr_read(const uint16_t *tile, int pitch, int sb
     return __builtin_bit_cast(uint2, v);
 }
 
-// Head blocks: the heads of one work item share a group (so B and C), and C.B^T
-// is formed once per work item.
-__device__ __forceinline__ void decode_work(const SsdKp &p, int64_t &b, int64_t &c, int64_t &h0,
-                                            int64_t &g) {
-    const int64_t nhb = p.H / p.hb;
-    const int64_t nwork = p.batch * p.nc * nhb;
+struct SsdKp {
+    const uint16_t *x; const float *dt; const float *dt_bias; const float *A_log;
+    const uint16_t *B; const uint16_t *C; const float *D; float *y;
+    const float *h0; float *h_final;
+    int64_t batch, L, H, P, N, G;
+    int mode;           // 0 ZOH, 1 DT, 2 ONE
+};
+
+// per-chunk scalars in LDS
+struct Scal {
+    float cs[kT];    // inclusive cumulative sum of a from the chunk start
+    float ecs[kT];   // e^{cs_t}
+    float sig[kT];   // input scale
+    float w[kT];     // e^{cs_end - cs_s} sigma_s
+    float end;       // e^{cs_end}
+};
+
+// D1 for one chunk, by one wave (lanes 0..31 hold steps 0..31).
+__device__ __forceinline__ void chunk_scalars(Scal &sc, float dtv, bool valid, float bias, float A,
+                                              int mode, int lane) {
+    float a = 0.0f, sg = 0.0f;
+    if (valid) {
+        const float dl = softplus(dtv + bias);
+        a = dl * A;
+        if (mode == 1) sg = dl;
+        else if (mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
+        else sg = 1.0f;
+    }
+    float v = a;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+        const float o = __shfl_up(v, off, 32);
+        if ((lane & 31) >= off) v += o;
+    }
+    const float cend = __shfl(v, 31, 32);
+    if (lane < kT) {
+        sc.cs[lane] = v;
+        sc.ecs[lane] = __expf(v);
+        sc.sig[lane] = sg;
+        sc.w[lane] = __expf(cend - v) * sg;
+    }
+    if (lane == 0) sc.end = __expf(cend);
+}
+
+template <int NMAX, bool EXACT>
+__global__ void __launch_bounds__(kThreads)
+ssd_scan_kernel(SsdKp p) {
+    constexpr int NT = NMAX / 16;          // state tiles (16 states each) per wave
+    // B/C row pitch (bf16): the row stride in dwords is 12 (mod 64) for NMAX >= 128
+    // and 36 for NMAX = 64, so that 16 lanes reading 16 rows (b128) and the four
+    // rows of a transposed read (8 dwords each) both fall on distinct banks
+    constexpr int BCP = NMAX == 64 ? 72 : 2 * (NMAX / 2 + 12);
+    constexpr int XP = 16 + 8;             // per-wave x row pitch (bf16): 12 dwords
+    constexpr int LDN = NMAX / 8;          // 16-byte pieces per B/C row
+    constexpr int PER_T = kT * LDN / kThreads;   // B (and C) pieces per thread
+    static_assert(kT * LDN % kThreads == 0 && kThreads % LDN == 0, "B/C pieces must divide evenly");
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * BCP];
+    __shared__ __attribute__((aligned(16))) uint16_t Cs[2][kT * BCP];
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[kWaves][2][kT * XP];
+    __shared__ __attribute__((aligned(16))) uint16_t Wh[kWaves][kT * XP];
+    __shared__ __attribute__((aligned(16))) uint16_t Wl[kWaves][kT * XP];
+    __shared__ Scal scal[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int c16 = lane & 15, q = lane >> 4;
+    // work item -> (b, h, channel block); items sharing B and C (same batch row
+    // and group) are consecutive and land on one XCD
+    const int64_t npb = p.P / kPW;
+    const int64_t nwork = p.batch * p.H * npb;
     const int64_t work = xcd_swizzle(blockIdx.x, nwork);
-    const int64_t hbi = work % nhb;
-    c = (work / nhb) % p.nc;
-    b = work / (nhb * p.nc);
-    h0 = hbi * p.hb;
-    g = h0 * p.G / p.H;
-}
+    const int64_t pb = work % npb;
+    const int64_t h = (work / npb) % p.H;
+    const int64_t b = work / (npb * p.H);
+    const int64_t g = h * p.G / p.H;
+    const int64_t p0 = pb * kPW + wid * 16;   // this wave's first head channel
+    const int N = EXACT ? NMAX : (int)p.N;   // compile-time when the state size is exact
+    const float A = -expf(p.A_log[h]);
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const float Dh = p.D ? p.D[h] : 0.0f;
+    const int64_t rowBC = p.G * p.N;
+    const int64_t rowX = p.H * p.P;
+    const uint16_t *Bg = p.B + (b * p.L * p.G + g) * p.N;
+    const uint16_t *Cg = p.C + (b * p.L * p.G + g) * p.N;
+    const uint16_t *Xg = p.x + (b * p.L * p.H + h) * p.P + p0;
+    const float *DTg = p.dt + b * p.L * p.H + h;
+    float *Yg = p.y + (b * p.L * p.H + h) * p.P + p0;
 
-// ---------------------------------------------------------------- K1: D1+D2
-// Shat^T[n][p] = sum_s B[s][n] * (w_s x[s][p]),  w_s = e^{cs_end - cs_s} sigma_s.
-// B (one slab of up to 128 states) and the weighted inputs are staged in their
-// natural row-major layout; the MFMA operands, whose contraction index is the
-// time step, are read with transposed LDS reads.  w_s x[s][p] is carried as
-// bf16 hi + lo parts and contracted in two MFMA passes into fp32 accumulators.
-template <int Q, int P>
-__global__ void __launch_bounds__(kThreads)
-ssd_chunk_state_kernel(SsdKp p) {
-    constexpr int NSLAB = 128, BP = NSLAB + 8;        // B slab pitch (bf16)
-    constexpr int PH = P < 64 ? P : 64, XP = PH + 8;  // x column block and pitch
-    constexpr int MAXT = (NSLAB / 32) * (PH / 32) / 4 > 0 ? (NSLAB / 32) * (PH / 32) / 4 : 1;
-    __shared__ float cs[Q], sig[Q], wsum[4];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[Q * BP];
-    __shared__ __attribute__((aligned(16))) uint16_t Xh[Q * XP];
-    __shared__ __attribute__((aligned(16))) uint16_t Xl[Q * XP];
-
-    int64_t b, c, hfirst, g;
-    decode_work(p, b, c, hfirst, g);
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int col = lane & 31, hh = lane >> 5, half = (lane >> 4) & 1;
-
-    for (int n0s = 0; n0s < p.N; n0s += NSLAB) {
-        const int ns = (int)min((int64_t)NSLAB, p.N - n0s);
-        __syncthreads();   // previous slab consumed
-        for (int e = tid; e < Q * (ns / 8); e += kThreads) {
-            const int s = e / (ns / 8), n8 = (e % (ns / 8)) * 8;
-            const int64_t t = c * Q + s;
-            *reinterpret_cast<u32x4 *>(&Bs[s * BP + n8]) =
-                ld8(p.B + ((b * p.L + t) * p.G + g) * p.N + n0s + n8, t < p.L);
+    // state slice S[n][p] for n < N, p in this wave's 16 channels, in the MFMA
+    // output layout: tile nt, lane (column c16, rows q*4 .. q*4+3)
+    f32x4 S[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        S[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.h0 && nt * 16 < N) {
+            const float *src = p.h0 + ((b * p.H + h) * p.P + p0 + c16) * p.N + nt * 16 + q * 4;
+            const float4 v = *reinterpret_cast<const float4 *>(src);
+            S[nt] = f32x4{v.x, v.y, v.z, v.w};
         }
-        for (int64_t h = hfirst; h < hfirst + p.hb; ++h) {
-            chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);   // starts and ends with a barrier
-            if (n0s == 0 && tid == 0) p.chunk_a[(b * p.H + h) * p.nc + c] = cs[Q - 1];
-            const float cs_end = cs[Q - 1];
-            for (int p0 = 0; p0 < P; p0 += PH) {
-                __syncthreads();   // previous x block consumed
-                for (int e = tid; e < Q * (PH / 8); e += kThreads) {
-                    const int s = e / (PH / 8), q8 = (e % (PH / 8)) * 8;
-                    const int64_t t = c * Q + s;
-                    const bool ok = t < p.L;
-                    const float w = ok ? __expf(cs_end - cs[s]) * sig[s] : 0.0f;
-                    const u32x4 v = ld8(p.x + ((b * p.L + t) * p.H + h) * p.P + p0 + q8, ok);
-                    u32x4 hi, lo;
+    }
+
+    // ---- loads of one chunk into registers
+    u32x4 rB[PER_T], rC[PER_T], rX;
+    float rdt;
+    // Loads are unconditional so they stay in flight across a chunk.  Full
+    // chunks use per-thread base pointers plus a uniform offset; a chunk that
+    // crosses L clamps its step index into the tensors (rows past L never
+    // contribute: their sigma and w are 0 and their outputs are not stored).
+    const int sB = tid / LDN, nB = (tid % LDN) * 8;           // piece 0 of this thread
+    constexpr int SB_STEP = kThreads / LDN;                    // steps between pieces i, i+1
+    const uint16_t *Bt = Bg + sB * rowBC + min(nB, N - 8);
+    const uint16_t *Ct = Cg + sB * rowBC + min(nB, N - 8);
+    const uint16_t *Xt = Xg + (lane >> 1) * rowX + (lane & 1) * 8;
+    const float *Dt = DTg + (lane & 31) * p.H;
+    auto load_chunk = [&](int64_t t0) __attribute__((always_inline)) {
+        if (t0 + kT <= p.L) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint2 sp = split_bf16(w * lo_f(v[i]), w * hi_f(v[i]));
-                        hi[i] = sp.x;
-                        lo[i] = sp.y;
-                    }
-                    *reinterpret_cast<u32x4 *>(&Xh[s * XP + q8]) = hi;
-                    *reinterpret_cast<u32x4 *>(&Xl[s * XP + q8]) = lo;
-                }
-                __syncthreads();
-                const int ntile = (ns / 32) * (PH / 32);
-#pragma unroll
-                for (int i = 0; i < MAXT; ++i) {
-                    const int tile = wid + 4 * i;
-                    if (tile >= ntile) break;
-                    const int nt = tile / (PH / 32), pt = tile % (PH / 32);
-                    f32x16 acc{};
-#pragma unroll 4
-                    for (int k = 0; k < Q / 16; ++k) {
-                        const int sb = k * 16 + hh * 8;
-                        const uint2 a0 = tr_read(Bs, BP, sb, nt * 32 + half * 16, lane);
-                        const uint2 a1 = tr_read(Bs, BP, sb + 4, nt * 32 + half * 16, lane);
-                        const uint2 x0 = tr_read(Xh, XP, sb, pt * 32 + half * 16, lane);
-                        const uint2 x1 = tr_read(Xh, XP, sb + 4, pt * 32 + half * 16, lane);
-                        const uint2 l0 = tr_read(Xl, XP, sb, pt * 32 + half * 16, lane);
-                        const uint2 l1 = tr_read(Xl, XP, sb + 4, pt * 32 + half * 16, lane);
-                        const u32x4 A = {a0.x, a0.y, a1.x, a1.y};
-                        acc = mfma32(A, u32x4{x0.x, x0.y, x1.x, x1.y}, acc);
-                        acc = mfma32(A, u32x4{l0.x, l0.y, l1.x, l1.y}, acc);
-                    }
-                    // acc: column p = p0 + pt*32 + col, rows n = n0s + nt*32 + j*8 + hh*4 + (0..3)
-                    float *dst = p.states + ((((b * p.nc + c) * p.H + h) * p.P + p0 + pt * 32 + col) * p.N) +
-                                 n0s + nt * 32;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        *reinterpret_cast<float4 *>(dst + j * 8 + hh * 4) =
-                            make_float4(acc[j * 4 + 0], acc[j * 4 + 1], acc[j * 4 + 2], acc[j * 4 + 3]);
-                }
+            for (int i = 0; i < PER_T; ++i) {
+                const int64_t off = (t0 + SB_STEP * i) * rowBC;
+                rB[i] = *reinterpret_cast<const u32x4 *>(Bt + off);
+                rC[i] = *reinterpret_cast<const u32x4 *>(Ct + off);
             }
-        }
-    }
-}
-
-// ---------------------------------------------------------------- K2: D3
-// One thread per (b, h, p, n): walk the chunks, replace each chunk-local end
-// state by the state entering that chunk, and write the final state.
-__global__ void __launch_bounds__(kThreads)
-ssd_state_pass_kernel(SsdKp p) {
-    const int64_t PN = p.P * p.N;
-    const int64_t per_bh = (PN + kThreads - 1) / kThreads;
-    const int64_t bh = blockIdx.x / per_bh;
-    const int64_t e = (blockIdx.x % per_bh) * kThreads + threadIdx.x;
-    if (e >= PN) return;
-    const int64_t b = bh / p.H, h = bh % p.H;
-    float S = p.h0 ? p.h0[bh * PN + e] : 0.0f;
-    const float *ca = p.chunk_a + bh * p.nc;
-    const int64_t cstride = p.H * PN;
-    float *st = p.states + (b * p.nc * p.H + h) * PN + e;
-    int64_t c = 0;
-    for (; c + 4 <= p.nc; c += 4) {
-        const float s0 = st[(c + 0) * cstride], s1 = st[(c + 1) * cstride];
-        const float s2 = st[(c + 2) * cstride], s3 = st[(c + 3) * cstride];
-        st[(c + 0) * cstride] = S; S = __expf(ca[c + 0]) * S + s0;
-        st[(c + 1) * cstride] = S; S = __expf(ca[c + 1]) * S + s1;
-        st[(c + 2) * cstride] = S; S = __expf(ca[c + 2]) * S + s2;
-        st[(c + 3) * cstride] = S; S = __expf(ca[c + 3]) * S + s3;
-    }
-    for (; c < p.nc; ++c) {
-        const float s0 = st[c * cstride];
-        st[c * cstride] = S;
-        S = __expf(ca[c]) * S + s0;
-    }
-    if (p.h_final) p.h_final[bh * PN + e] = S;
-}
-
-// ---------------------------------------------------------------- K3: D4+D5
-// Work item = (batch, chunk, block of heads of one group).  C.B^T of the chunk
-// is formed once, from B and C staged in slabs, and kept in registers: each
-// wave owns a balanced set of 32x32 causal tiles (time blocks w and NTB-1-w).
-// Then, per head: decay mask, (C.B^T o L) X, e^{cs_t} C S_c and D x, with x
-// staged row-major and read transposed.
-template <int Q> struct Plan;
-template <> struct Plan<256> { static constexpr int NSLOT = 9; };   // blocks w, 7-w: (w+1) + (8-w) tiles
-template <> struct Plan<128> { static constexpr int NSLOT = 4; };   // block w: w+1 tiles
-template <> struct Plan<64> { static constexpr int NSLOT = 2; };    // block w (w < 2): w+1 tiles
-
-// slot -> (time block, source block) of wave w; false when the slot is unused
-template <int Q>
-__device__ __forceinline__ bool slot_tile(int w, int slot, int &tb, int &sb) {
-    if constexpr (Q == 256) {
-        if (slot <= w) { tb = w; sb = slot; }
-        else { tb = 7 - w; sb = slot - w - 1; }
-        return true;
-    } else {
-        tb = w; sb = slot;
-        return (tb < Q / 32) && (slot <= w);
-    }
-}
-
-template <int Q, int P>
-__global__ void __launch_bounds__(kThreads)
-ssd_chunk_scan_kernel(SsdKp p) {
-    constexpr int NS1 = 64, SP1 = NS1 + 8;              // B/C slab (phase 1) width and pitch
-    constexpr int NS2 = P <= 64 ? 128 : 64, SP2 = NS2 + 8;  // C and S slab (phase 2)
-    constexpr int XP = P + 8;                           // x tile pitch (bf16)
-    constexpr int PT = P / 32;
-    constexpr int NSLOT = Plan<Q>::NSLOT;
-    constexpr int NTBW = (Q == 256) ? 2 : 1;            // time blocks per wave
-    // LDS arena: phase 1 holds B and C slabs; phase 2 holds x, a C slab and the
-    // hi/lo parts of a slab of the entering state S[p][n]
-    constexpr int PH1 = 2 * Q * SP1;
-    constexpr int PH2 = Q * XP + Q * SP2 + 2 * P * SP2;
-    constexpr int ARENA = PH1 > PH2 ? PH1 : PH2;
-    __shared__ float cs[Q], sig[Q], gS[Q], ecs[Q], wsum[4];
-    __shared__ __attribute__((aligned(16))) uint16_t arena[ARENA];
-    uint16_t *Bs = arena, *Cs1 = arena + Q * SP1;                  // phase 1
-    uint16_t *Xs = arena, *Cs = arena + Q * XP;                    // phase 2
-    uint16_t *Sh = Cs + Q * SP2, *Sl = Sh + P * SP2;
-
-    int64_t b, c, hfirst, g;
-    decode_work(p, b, c, hfirst, g);
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int col = lane & 31, hh = lane >> 5, half = (lane >> 4) & 1;
-    const int64_t rowBC = p.G * p.N;                       // elements between time steps of B/C
-    const uint16_t *Bbase = p.B + ((b * p.L + c * Q) * p.G + g) * p.N;
-    const uint16_t *Cbase = p.C + ((b * p.L + c * Q) * p.G + g) * p.N;
-    const int64_t tmax = p.L - c * Q;                      // valid rows in this chunk
-
-    auto stage_rows = [&](uint16_t *dst, int pitch, const uint16_t *src, int n0, int ns) {
-        for (int e = tid; e < Q * (ns / 8); e += kThreads) {
-            const int s = e / (ns / 8), n8 = (e % (ns / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(&dst[s * pitch + n8]) = ld8(src + s * rowBC + n0 + n8, s < tmax);
+            rX = *reinterpret_cast<const u32x4 *>(Xt + t0 * rowX);
+            rdt = Dt[t0 * p.H];
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int s = sB + SB_STEP * i;
+                const int64_t off = (min(t0 + s, p.L - 1) - sB) * rowBC;   // Bt is at step sB
+                rB[i] = *reinterpret_cast<const u32x4 *>(Bt + off);
+                rC[i] = *reinterpret_cast<const u32x4 *>(Ct + off);
+            }
+            const int s = lane >> 1;
+            rX = *reinterpret_cast<const u32x4 *>(Xt + (min(t0 + s, p.L - 1) - s) * rowX);
+            const int sd = lane & 31;
+            rdt = Dt[(min(t0 + sd, p.L - 1) - sd) * p.H];
         }
     };
+    auto store_chunk = [&](int buf, int64_t t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int o = (sB + SB_STEP * i) * BCP + nB;
+            *reinterpret_cast<u32x4 *>(&Bs[buf][o]) = rB[i];
+            *reinterpret_cast<u32x4 *>(&Cs[buf][o]) = rC[i];
+        }
+        {
+            const int s = lane >> 1, c8 = (lane & 1) * 8;
+            *reinterpret_cast<u32x4 *>(&Xs[wid][buf][s * XP + c8]) = rX;
+        }
+        if (wid == 0) chunk_scalars(scal[buf], rdt, t0 + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane);
+    };
 
-    // ---- C.B^T tiles of this wave, accumulated over slabs of the state index
-    f32x16 G[NSLOT];
+    const int64_t nchunks = (p.L + kT - 1) / kT;
+    load_chunk(0);
+    store_chunk(0, 0);
+    if (nchunks > 1) load_chunk(kT);
+    __syncthreads();
+
+    for (int64_t j = 0; j < nchunks; ++j) {
+        const int buf = (int)(j & 1);
+        const int64_t t0 = j * kT;
+        const uint16_t *B_ = Bs[buf], *C_ = Cs[buf], *X_ = Xs[wid][buf];
+        const Scal &sc = scal[buf];
+
+        // decay-weighted inputs w_s x[s][p] of this wave's channels, as hi/lo bf16
+        {
+            const int s = lane >> 1, c8 = (lane & 1) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(&X_[s * XP + c8]);
+            const float ws = sc.w[s];
+            u32x4 hi, lo;
 #pragma unroll
-    for (int i = 0; i < NSLOT; ++i) G[i] = f32x16{};
-    for (int n0 = 0; n0 < p.N; n0 += NS1) {
-        const int ns = (int)min((int64_t)NS1, p.N - n0);
-        __syncthreads();
-        stage_rows(Bs, SP1, Bbase, n0, ns);
-        stage_rows(Cs1, SP1, Cbase, n0, ns);
-        __syncthreads();
+            for (int i = 0; i < 4; ++i) {
+                const uint2 sp = split_bf16(ws * lo_f(v[i]), ws * hi_f(v[i]));
+                hi[i] = sp.x;
+                lo[i] = sp.y;
+            }
+            *reinterpret_cast<u32x4 *>(&Wh[wid][s * XP + c8]) = hi;
+            *reinterpret_cast<u32x4 *>(&Wl[wid][s * XP + c8]) = lo;
+            // the same wave reads these rows back (transposed) below: LDS
+            // operations of one wave complete in order, and this keeps the
+            // compiler from moving the reads above the writes
+            asm volatile("" ::: "memory");
+        }
+
+        // D5: yacc[tt] = C[t][:] S[:][p] for t in time tile tt, then scaled by e^{cs_t}
+        f32x4 yacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-        for (int slot = 0; slot < NSLOT; ++slot) {
-            int tb, sb;
-            if (!slot_tile<Q>(wid, slot, tb, sb)) continue;
-            for (int k = 0; k < ns; k += 16) {
-                const u32x4 A = *reinterpret_cast<const u32x4 *>(&Bs[(sb * 32 + col) * SP1 + k + hh * 8]);
-                const u32x4 Bo = *reinterpret_cast<const u32x4 *>(&Cs1[(tb * 32 + col) * SP1 + k + hh * 8]);
-                G[slot] = mfma32(A, Bo, G[slot]);   // G^T[s][t]: lane column t, rows s
+        for (int k = 0; k < NT / 2; ++k) {
+            if (k * 32 >= N) break;
+            const uint2 s0 = split_bf16(S[2 * k][0], S[2 * k][1]);
+            const uint2 s1 = split_bf16(S[2 * k][2], S[2 * k][3]);
+            const uint2 s2 = split_bf16(S[2 * k + 1][0], S[2 * k + 1][1]);
+            const uint2 s3 = split_bf16(S[2 * k + 1][2], S[2 * k + 1][3]);
+            const u32x4 Sh{s0.x, s1.x, s2.x, s3.x}, Sl{s0.y, s1.y, s2.y, s3.y};
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const uint16_t *cr = C_ + (tt * 16 + c16) * BCP + k * 32 + q * 4;
+                const uint2 a0 = *reinterpret_cast<const uint2 *>(cr);
+                const uint2 a1 = *reinterpret_cast<const uint2 *>(cr + 16);
+                const u32x4 Af{a0.x, a0.y, a1.x, a1.y};
+                yacc[tt] = mfma16(Af, Sh, yacc[tt]);
+                yacc[tt] = mfma16(Af, Sl, yacc[tt]);
             }
         }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const float4 e = *reinterpret_cast<const float4 *>(&sc.ecs[tt * 16 + q * 4]);
+            yacc[tt][0] *= e.x; yacc[tt][1] *= e.y; yacc[tt][2] *= e.z; yacc[tt][3] *= e.w;
+        }
+
+        // D4: G^T[s][t] = B[s].C[t] for the causal tile pairs (s-tile, t-tile)
+        // (0,0), (0,1), (1,1); lane holds column t, rows s = q*4 .. q*4+3
+        f32x4 G00{0.0f, 0.0f, 0.0f, 0.0f}, G01{0.0f, 0.0f, 0.0f, 0.0f}, G11{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < NMAX; k += 32) {
+            if (k >= N) break;
+            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(&B_[c16 * BCP + k + q * 8]);
+            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(&B_[(16 + c16) * BCP + k + q * 8]);
+            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(&C_[c16 * BCP + k + q * 8]);
+            const u32x4 c1 = *reinterpret_cast<const u32x4 *>(&C_[(16 + c16) * BCP + k + q * 8]);
+            G00 = mfma16(b0, c0, G00);
+            G01 = mfma16(b0, c1, G01);
+            G11 = mfma16(b1, c1, G11);
+        }
+        // M[t][s] = G[t][s] e^{cs_t - cs_s} sigma_s (s <= t) -> A fragments of M X with
+        // K slots q*8+i <-> s = q*4+i (i < 4) and 16+q*4+(i-4) (i >= 4)
+        {
+            const float4 cs0 = *reinterpret_cast<const float4 *>(&sc.cs[q * 4]);
+            const float4 cs1 = *reinterpret_cast<const float4 *>(&sc.cs[16 + q * 4]);
+            const float4 sg0 = *reinterpret_cast<const float4 *>(&sc.sig[q * 4]);
+            const float4 sg1 = *reinterpret_cast<const float4 *>(&sc.sig[16 + q * 4]);
+            const float csA[4] = {cs0.x, cs0.y, cs0.z, cs0.w}, csB[4] = {cs1.x, cs1.y, cs1.z, cs1.w};
+            const float sgA[4] = {sg0.x, sg0.y, sg0.z, sg0.w}, sgB[4] = {sg1.x, sg1.y, sg1.z, sg1.w};
+            const float ct0 = sc.cs[c16], ct1 = sc.cs[16 + c16];
+            float m0[8], m1[8];     // time tile 0 (t = c16) and 1 (t = 16 + c16)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sA = q * 4 + i, sB = 16 + q * 4 + i;
+                m0[i] = (sA <= c16) ? G00[i] * __expf(ct0 - csA[i]) * sgA[i] : 0.0f;
+                m0[4 + i] = 0.0f;                                   // s >= 16 > t
+                m1[i] = G01[i] * __expf(ct1 - csA[i]) * sgA[i];     // s < 16 <= t
+                m1[4 + i] = (sB <= 16 + c16) ? G11[i] * __expf(ct1 - csB[i]) * sgB[i] : 0.0f;
+            }
+            // D4: yacc[tt] += M X, X fragments read transposed from this wave's x tile
+            const uint2 xa0 = tr_read(X_, XP, q * 4, 0, lane);
+            const uint2 xa1 = tr_read(X_, XP, 16 + q * 4, 0, lane);
+            const u32x4 Xf{xa0.x, xa0.y, xa1.x, xa1.y};
+            {
+                const uint2 u0 = split_bf16(m0[0], m0[1]), u1 = split_bf16(m0[2], m0[3]);
+                const u32x4 Mh{u0.x, u1.x, 0u, 0u}, Ml{u0.y, u1.y, 0u, 0u};
+                yacc[0] = mfma16(Mh, Xf, yacc[0]);
+                yacc[0] = mfma16(Ml, Xf, yacc[0]);
+            }
+            {
+                const uint2 u0 = split_bf16(m1[0], m1[1]), u1 = split_bf16(m1[2], m1[3]);
+                const uint2 u2 = split_bf16(m1[4], m1[5]), u3 = split_bf16(m1[6], m1[7]);
+                const u32x4 Mh{u0.x, u1.x, u2.x, u3.x}, Ml{u0.y, u1.y, u2.y, u3.y};
+                yacc[1] = mfma16(Mh, Xf, yacc[1]);
+                yacc[1] = mfma16(Ml, Xf, yacc[1]);
+            }
+        }
+
+        // skip term and store: lane (column c16, rows t = tt*16 + q*4 + i)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const uint2 xv = tr_read(X_, XP, tt * 16 + q * 4, 0, lane);
+            const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
+            float *yr = Yg + (t0 + tt * 16 + q * 4) * rowX + c16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (t0 + tt * 16 + q * 4 + i < p.L) yr[i * rowX] = fmaf(Dh, xs[i], yacc[tt][i]);
+            }
+        }
+
+        // D2+D3: S <- e^{cs_end} S + B^T (w o X); A = B^T via transposed reads
+        {
+            const float e = sc.end;
+            const uint2 wh0 = tr_read(Wh[wid], XP, q * 8, 0, lane);
+            const uint2 wh1 = tr_read(Wh[wid], XP, q * 8 + 4, 0, lane);
+            const uint2 wl0 = tr_read(Wl[wid], XP, q * 8, 0, lane);
+            const uint2 wl1 = tr_read(Wl[wid], XP, q * 8 + 4, 0, lane);
+            const u32x4 Whf{wh0.x, wh0.y, wh1.x, wh1.y}, Wlf{wl0.x, wl0.y, wl1.x, wl1.y};
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (nt * 16 >= N) break;
+                S[nt] *= e;
+                const uint2 a0 = tr_read(B_, BCP, q * 8, nt * 16, lane);
+                const uint2 a1 = tr_read(B_, BCP, q * 8 + 4, nt * 16, lane);
+                const u32x4 Af{a0.x, a0.y, a1.x, a1.y};
+                S[nt] = mfma16(Af, Whf, S[nt]);
+                S[nt] = mfma16(Af, Wlf, S[nt]);
+            }
+        }
+
+        // stage chunk j+1, start loading chunk j+2
+        if (j + 1 < nchunks) {
+            store_chunk(buf ^ 1, t0 + kT);
+            if (j + 2 < nchunks) load_chunk(t0 + 2 * kT);
+        }
+        __syncthreads();
     }
 
-    const bool one_slab = p.N <= NS2;
-    for (int64_t h = hfirst; h < hfirst + p.hb; ++h) {
-        chunk_scalars<Q>(p, b, c, h, cs, sig, wsum);    // barrier at entry: arena free
-        if (tid < Q) {
-            const int e = (tid | 31);
-            gS[tid] = __expf(cs[e] - cs[tid]) * sig[tid];
-            ecs[tid] = __expf(cs[tid]);
+    if (p.h_final) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            if (nt * 16 >= N) break;
+            float *dst = p.h_final + ((b * p.H + h) * p.P + p0 + c16) * p.N + nt * 16 + q * 4;
+            *reinterpret_cast<float4 *>(dst) = make_float4(S[nt][0], S[nt][1], S[nt][2], S[nt][3]);
         }
-        for (int e = tid; e < Q * (P / 8); e += kThreads) {
-            const int s = e / (P / 8), q8 = (e % (P / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(&Xs[s * XP + q8]) =
-                ld8(p.x + ((b * p.L + c * Q + s) * p.H + h) * p.P + q8, s < tmax);
-        }
-        const bool has_state = (c > 0) || (p.h0 != nullptr);
-        const float *Sb = p.states + ((b * p.nc + c) * p.H + h) * p.P * p.N;
-        // entering state slab -> bf16 hi/lo parts, row-major [p][n]
-        auto stage_state = [&](int n0, int ns) {
-            for (int e = tid; e < P * (ns / 4); e += kThreads) {
-                const int pp = e / (ns / 4), n4 = (e % (ns / 4)) * 4;
-                const float4 v = *reinterpret_cast<const float4 *>(Sb + pp * p.N + n0 + n4);
-                const uint2 s0 = split_bf16(v.x, v.y), s1 = split_bf16(v.z, v.w);
-                *reinterpret_cast<uint2 *>(&Sh[pp * SP2 + n4]) = make_uint2(s0.x, s1.x);
-                *reinterpret_cast<uint2 *>(&Sl[pp * SP2 + n4]) = make_uint2(s0.y, s1.y);
-            }
-        };
-        if (has_state && one_slab) {
-            stage_rows(Cs, SP2, Cbase, 0, (int)p.N);
-            stage_state(0, (int)p.N);
-        }
-        __syncthreads();
-        const float Dh = p.D ? p.D[h] : 0.0f;
-
-        // one time block of this wave: state term, intra-chunk term, skip, store
-        // Every wave runs do_block (the slab loop below has barriers); waves
-        // without a time block of their own (short chunks) only take part in
-        // the barriers and staging.
-        auto do_block = [&](int i) __attribute__((always_inline)) {
-            const int tb = (i == 0) ? wid : 7 - wid;
-            const bool active = tb < Q / 32;
-            const int t0 = active ? tb * 32 : 0;
-            f32x16 yacc[PT];
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x16{};
-            // D5: yacc = e^{cs_t} sum_n C[t, n] S[p, n]
-            if (has_state) {
-                for (int n0 = 0; n0 < p.N; n0 += NS2) {
-                    const int ns = (int)min((int64_t)NS2, p.N - n0);
-                    if (!one_slab) {
-                        __syncthreads();
-                        stage_rows(Cs, SP2, Cbase, n0, ns);
-                        stage_state(n0, ns);
-                        __syncthreads();
-                    }
-                    if (active)
-                    for (int k = 0; k < ns; k += 16) {
-                        const u32x4 A = *reinterpret_cast<const u32x4 *>(&Cs[(t0 + col) * SP2 + k + hh * 8]);
-#pragma unroll
-                        for (int pt = 0; pt < PT; ++pt) {
-                            const u32x4 Shv = *reinterpret_cast<const u32x4 *>(&Sh[(pt * 32 + col) * SP2 + k + hh * 8]);
-                            const u32x4 Slv = *reinterpret_cast<const u32x4 *>(&Sl[(pt * 32 + col) * SP2 + k + hh * 8]);
-                            yacc[pt] = mfma32(A, Shv, yacc[pt]);
-                            yacc[pt] = mfma32(A, Slv, yacc[pt]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                    for (int idx = 0; idx < 16; ++idx)
-                        yacc[pt][idx] *= ecs[t0 + (idx >> 2) * 8 + hh * 4 + (idx & 3)];
-            }
-            if (!active) return;
-            // D4: yacc += sum_s M[t, s] x[s, p], M = G o L as hi + lo bf16 fragments
-#pragma unroll
-            for (int slot = 0; slot < NSLOT; ++slot) {
-                int tbs, sb;
-                if (!slot_tile<Q>(wid, slot, tbs, sb) || tbs != tb) continue;
-                const int s0 = sb * 32;
-                const int trow = t0 + col;
-                float mv[16];
-                if (sb < tb) {
-                    const float ft = __expf(cs[trow] - cs[s0 + 31]);
-#pragma unroll
-                    for (int idx = 0; idx < 16; ++idx) {
-                        const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
-                        mv[idx] = G[slot][idx] * ft * gS[s];
-                    }
-                } else {
-                    const float ct = cs[trow];
-#pragma unroll
-                    for (int idx = 0; idx < 16; ++idx) {
-                        const int s = s0 + (idx >> 2) * 8 + hh * 4 + (idx & 3);
-                        mv[idx] = (s <= trow) ? G[slot][idx] * __expf(ct - cs[s]) * sig[s] : 0.0f;
-                    }
-                }
-                uint2 q[8];
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii) q[ii] = split_bf16(mv[2 * ii], mv[2 * ii + 1]);
-                const u32x4 m0h{q[0].x, q[1].x, q[2].x, q[3].x}, m0l{q[0].y, q[1].y, q[2].y, q[3].y};
-                const u32x4 m1h{q[4].x, q[5].x, q[6].x, q[7].x}, m1l{q[4].y, q[5].y, q[6].y, q[7].y};
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const int cb = pt * 32 + half * 16;
-                    const uint2 a0 = tr_read(Xs, XP, s0 + hh * 4, cb, lane);
-                    const uint2 a1 = tr_read(Xs, XP, s0 + 8 + hh * 4, cb, lane);
-                    const uint2 b0 = tr_read(Xs, XP, s0 + 16 + hh * 4, cb, lane);
-                    const uint2 b1 = tr_read(Xs, XP, s0 + 24 + hh * 4, cb, lane);
-                    const u32x4 x0{a0.x, a0.y, a1.x, a1.y}, x1{b0.x, b0.y, b1.x, b1.y};
-                    yacc[pt] = mfma32(m0h, x0, yacc[pt]);
-                    yacc[pt] = mfma32(m0l, x0, yacc[pt]);
-                    yacc[pt] = mfma32(m1h, x1, yacc[pt]);
-                    yacc[pt] = mfma32(m1l, x1, yacc[pt]);
-                }
-            }
-            // D skip and store: column p = pt*32 + col, rows t = t0 + j*8 + hh*4 + i
-            float *yb = p.y + ((b * p.L + c * Q + t0) * p.H + h) * p.P;
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const int pc = pt * 32 + col;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int tr = j * 8 + hh * 4;
-                    const uint2 xv = tr_read(Xs, XP, t0 + tr, pt * 32 + half * 16, lane);
-                    const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        if (t0 + tr + ii < tmax)
-                            yb[(int64_t)(tr + ii) * p.H * p.P + pc] = fmaf(Dh, xs[ii], yacc[pt][j * 4 + ii]);
-                    }
-                }
-            }
-        };
-        do_block(0);
-        if constexpr (NTBW == 2) do_block(1);
     }
-}
-
-template <int Q, int P>
-hipError_t launch_qp(const SsdKp &kp, hipStream_t s) {
-    const int64_t nwork = kp.batch * kp.nc * (kp.H / kp.hb);
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<Q, P>), dim3((unsigned)nwork), dim3(kThreads), 0, s, kp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t per_bh = (kp.P * kp.N + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)(kp.batch * kp.H * per_bh)), dim3(kThreads), 0, s, kp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ssd_chunk_scan_kernel<Q, P>), dim3((unsigned)nwork), dim3(kThreads), 0, s, kp);
-    return hipGetLastError();
-}
-
-template <int Q>
-hipError_t launch_q(const SsdKp &kp, hipStream_t s) {
-    if (kp.P == 32) return launch_qp<Q, 32>(kp, s);
-    if (kp.P == 64) return launch_qp<Q, 64>(kp, s);
-    return launch_qp<Q, 128>(kp, s);
-}
-
-// Heads per work item: a divisor of the heads of one group, as large as keeps at
-// least ~2 work items per compute unit.
-int64_t pick_head_block(int64_t batch, int64_t nc, int64_t H, int64_t G) {
-    const int64_t hpg = H / G;
-    for (int64_t hb = hpg; hb >= 1; --hb) {
-        if (hpg % hb != 0) continue;
-        if (batch * nc * (H / hb) >= 512) return hb;
-    }
-    return 1;
 }
 
 }  // namespace
 
-size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
-                           int64_t d_state, int64_t chunk_len) {
-    const int64_t nc = (L + chunk_len - 1) / chunk_len;
-    const size_t st = (size_t)batch * nc * nheads * headdim * d_state * sizeof(float);
-    const size_t ca = (size_t)batch * nheads * nc * sizeof(float);
-    return ((st + 255) / 256) * 256 + ((ca + 255) / 256) * 256;
-}
+size_t ssd_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
 
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_name) {
-    *kernel_name = "ssd_chunk_state_kernel/ssd_state_pass_kernel/ssd_chunk_scan_kernel";
+    *kernel_name = "ssd_scan_kernel";
     SsdKp p{};
     p.x = static_cast<const uint16_t *>(a.x);
     p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
@@ -538,16 +402,16 @@ hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_
     p.C = static_cast<const uint16_t *>(a.C);
     p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
     p.batch = a.batch; p.L = a.L; p.H = a.nheads; p.P = a.headdim; p.N = a.d_state; p.G = a.ngroups;
-    p.nc = (a.L + a.chunk_len - 1) / a.chunk_len;
-    p.hb = pick_head_block(p.batch, p.nc, p.H, p.G);
-    const int64_t nc = p.nc;
-    const size_t st = (size_t)a.batch * nc * a.nheads * a.headdim * a.d_state * sizeof(float);
-    p.states = static_cast<float *>(a.workspace);
-    p.chunk_a = reinterpret_cast<float *>(static_cast<char *>(a.workspace) + ((st + 255) / 256) * 256);
     p.mode = (int)(a.flags & 0x3u);
-    if (a.chunk_len == 64) return launch_q<64>(p, stream);
-    if (a.chunk_len == 128) return launch_q<128>(p, stream);
-    return launch_q<256>(p, stream);
+    const int64_t nwork = p.batch * p.H * (p.P / kPW);
+    const dim3 grid((unsigned)nwork), block(kThreads);
+    if (p.N == 64) hipLaunchKernelGGL((ssd_scan_kernel<64, true>), grid, block, 0, stream, p);
+    else if (p.N == 128) hipLaunchKernelGGL((ssd_scan_kernel<128, true>), grid, block, 0, stream, p);
+    else if (p.N == 256) hipLaunchKernelGGL((ssd_scan_kernel<256, true>), grid, block, 0, stream, p);
+    else if (p.N < 64) hipLaunchKernelGGL((ssd_scan_kernel<64, false>), grid, block, 0, stream, p);
+    else if (p.N < 128) hipLaunchKernelGGL((ssd_scan_kernel<128, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((ssd_scan_kernel<256, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace ssm
