@@ -274,11 +274,14 @@ s6_scan_kernel(S6Kp p) {
         if (kt + 2 < ntiles) load_raw<true>(Rk, q, p, (kt + 2) * kT, tid, k);
         __syncthreads();
     };
+    // The unchecked body of tile kt loads tile kt+2, so a pair (kt, kt+1) of
+    // unchecked bodies needs tiles up to kt+3 to lie wholly inside the sequence.
+    const int64_t nfull = p.L / kT;
     auto run = [&](auto accTag) __attribute__((always_inline)) {
         int64_t kt = 0;
         if (ntiles >= 4) {
             body_checked(0, RA, RB, accTag);
-            for (kt = 1; kt + 3 < ntiles; kt += 2) {   // tiles kt (set RB) and kt+1 (set RA)
+            for (kt = 1; kt + 4 <= nfull; kt += 2) {   // tiles kt (set RB) and kt+1 (set RA)
                 body_full(kt, RB, RA, accTag);
                 body_full(kt + 1, RA, RB, accTag);
             }
