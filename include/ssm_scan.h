@@ -120,8 +120,10 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
  * i.e. sigma = delta).  The method cuts the sequence into chunks; the result
  * does not depend on the chunk length beyond rounding.  chunk_len is checked
  * against the limits below and otherwise only names the caller's model
- * setting: the kernel walks the sequence in its own 32-step blocks, carrying
- * the state of each (batch, head) on chip from block to block.
+ * setting: the kernels walk the sequence in their own 32-step chunks, carrying
+ * the state on chip from chunk to chunk.  A long sequence is first cut into a
+ * few segments whose own final states and entering states go through the
+ * workspace, so that many (batch, segment, head) groups run at once.
  *
  * Layouts: x (batch, L, nheads, headdim) bf16; dt (batch, L, nheads) fp32;
  * dt_bias, A_log, D (nheads) fp32; B, C (batch, L, ngroups, d_state) bf16;
@@ -129,8 +131,11 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
  * in_dtype must be SSM_BF16 (the contractions run on bf16 MFMA; SSM_F32 returns
  * SSM_ERR_UNSUPPORTED).  Limits: nheads % ngroups == 0; headdim in {32, 64, 128};
  * d_state a multiple of 32, <= 256; chunk_len in {64, 128, 256}.
- * No workspace is needed (ssd_chunk_scan_fwd_workspace_size returns 0;
- * workspace may be NULL). */
+ * Workspace: ssd_chunk_scan_fwd_workspace_size() bytes, 16-byte aligned,
+ * owned by the caller and reused freely between calls on one stream (one fp32
+ * headdim x d_state state and one decay per (batch, head, segment)); the size
+ * is a function of the shape only, and 0 when the sequence is one segment
+ * (workspace may then be NULL). */
 size_t ssd_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                                          int64_t d_state, int64_t ngroups, int64_t chunk_len);
 

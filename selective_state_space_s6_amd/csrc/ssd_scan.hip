@@ -3,27 +3,36 @@
 // Implements the scalar-A-per-head recurrence of builderforce-memory-engine
 // ssd.js (header comment, ssd_chunk_forward) by the chunked decomposition that
 // mamba-rs 0.2.1 mamba3_gpu.rs step F6 launches as separate kernels (dA
-// cumsum, chunk state, state passing, chunk scan, final-state writeback).  Here
-// the whole decomposition runs in one kernel over 32-step chunks:
+// cumsum, chunk state, state passing, chunk scan, final-state writeback).
 //
-//   D1  per chunk: delta = softplus(dt + dt_bias), a = delta*A_h, cs = cumsum(a),
-//       input scale sigma (delta by default)
-//   D4  y_intra = ((C B^T) o L) X with L[t,s] = e^{cs_t-cs_s} sigma_s, s <= t
-//   D5  y += e^{cs_t} C_t S + D x_t
-//   D2  chunk-local state  B^T (w o X),  w_s = e^{cs_end-cs_s} sigma_s
-//   D3  S <- e^{cs_end} S + B^T (w o X); after the last chunk S is h_final
+// The sequence of every (batch, head) is cut into a few long segments so that
+// enough work groups exist to fill the chip; inside a segment the state is
+// carried on chip from one 32-step chunk to the next:
 //
-// A work item is (batch, head, 32 head channels); each of its two waves owns 16
-// channels and keeps its N x 16 slice of the fp32 state in MFMA accumulators
-// for the whole sequence, so the inter-chunk pass (D3) never leaves registers
-// and x, B, C are read once.  Every contraction is a bf16 MFMA
+//   ssd_state_kernel   per (batch, segment, head), all segments but the last:
+//                      the segment's own final state from a zero start (D2 and
+//                      D3 inside the segment) and its total decay e^{sum a}
+//   ssd_pass_kernel    per (batch, head): the state entering every segment,
+//                      S_in[k+1] = e^{sum a over k} S_in[k] + S_local[k]  (D3)
+//   ssd_scan_kernel    per (batch, segment, head): from S_in[k], per chunk
+//     D1  delta = softplus(dt + dt_bias), a = delta*A_h, cs = cumsum(a), sigma
+//     D4  y_intra = ((C B^T) o L) X with L[t,s] = e^{cs_t-cs_s} sigma_s, s <= t
+//     D5  y += e^{cs_t} C_t S + D x_t
+//     D2  S <- e^{cs_end} S + B^T (w o X), w_s = e^{cs_end-cs_s} sigma_s  (D3)
+//     and after the last chunk of the last segment S is h_final.
+//
+// A work group holds one head: headdim/16 waves, each owning 16 head channels
+// and keeping their N x 16 slice of the fp32 state in MFMA accumulators.  The
+// chunk's C.B^T and decay mask (D4) are computed once per group, split over
+// the first waves, and shared through LDS.  Every contraction is a bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16) with fp32 accumulation.  x, B, C are bf16 and
-// exact; products formed in fp32 (w o X, the masked C.B^T, the state) are
-// split into bf16 hi + lo parts and contracted twice, keeping ~16 mantissa
-// bits.  Chunks are double-buffered in LDS; loads of chunk j+1 are in flight
+// exact; products formed in fp32 (w o X, the masked C.B^T, the state) are split
+// into bf16 hi + lo parts and contracted twice, keeping ~16 mantissa bits.
+// Chunks are double-buffered in LDS; the loads of chunk j+2 are in flight
 // while chunk j is computed.
 #include "device_common.hpp"
 #include "launchers.hpp"
+#include <algorithm>
 
 namespace ssm {
 namespace {
@@ -38,10 +47,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kT = 32;           // steps per chunk
-constexpr int kWaves = 2;        // waves per work item
-constexpr int kThreads = 64 * kWaves;
-constexpr int kPW = 16 * kWaves; // head channels per work item
+constexpr int kT = 32;              // steps per chunk
+constexpr int kTargetWaves = 3072;  // enough resident waves to hide latency (3 per SIMD)
+constexpr int kMinSeg = 256;        // shortest segment worth a state round trip
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -58,10 +66,6 @@ __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0
 __device__ __forceinline__ uint2 split_bf16(float a, float b) {
     const uint32_t hi = pack_bf16(a, b);
     return make_uint2(hi, pack_bf16(a - lo_f(hi), b - hi_f(hi)));
-}
-__device__ __forceinline__ u32x4 ld8(const uint16_t *p, bool ok) {
-    if (!ok) return u32x4{0u, 0u, 0u, 0u};
-    return *reinterpret_cast<const u32x4 *>(p);
 }
 
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
@@ -82,7 +86,10 @@ struct SsdKp {
     const uint16_t *x; const float *dt; const float *dt_bias; const float *A_log;
     const uint16_t *B; const uint16_t *C; const float *D; float *y;
     const float *h0; float *h_final;
+    float *ws_state;    // (batch, H, nseg, P, N): local, then entering, segment states
+    float *ws_decay;    // (batch, H, nseg): e^{sum of a} over a segment
     int64_t batch, L, H, P, N, G;
+    int64_t Ls, nseg;   // segment length (a multiple of kT) and count
     int mode;           // 0 ZOH, 1 DT, 2 ONE
 };
 
@@ -93,6 +100,7 @@ struct Scal {
     float sig[kT];   // input scale
     float w[kT];     // e^{cs_end - cs_s} sigma_s
     float end;       // e^{cs_end}
+    float csend;     // cs_end
 };
 
 // D1 for one chunk, by one wave (lanes 0..31 hold steps 0..31).
@@ -119,147 +127,330 @@ __device__ __forceinline__ void chunk_scalars(Scal &sc, float dtv, bool valid, f
         sc.sig[lane] = sg;
         sc.w[lane] = __expf(cend - v) * sg;
     }
-    if (lane == 0) sc.end = __expf(cend);
+    if (lane == 0) {
+        sc.end = __expf(cend);
+        sc.csend = cend;
+    }
 }
 
-template <int NMAX, bool EXACT>
-__global__ void __launch_bounds__(kThreads)
-ssd_scan_kernel(SsdKp p) {
-    constexpr int NT = NMAX / 16;          // state tiles (16 states each) per wave
-    // B/C row pitch (bf16): the row stride in dwords is 12 (mod 64) for NMAX >= 128
-    // and 36 for NMAX = 64, so that 16 lanes reading 16 rows (b128) and the four
-    // rows of a transposed read (8 dwords each) both fall on distinct banks
-    constexpr int BCP = NMAX == 64 ? 72 : 2 * (NMAX / 2 + 12);
-    constexpr int XP = 16 + 8;             // per-wave x row pitch (bf16): 12 dwords
-    constexpr int LDN = NMAX / 8;          // 16-byte pieces per B/C row
-    constexpr int PER_T = kT * LDN / kThreads;   // B (and C) pieces per thread
-    static_assert(kT * LDN % kThreads == 0 && kThreads % LDN == 0, "B/C pieces must divide evenly");
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * BCP];
-    __shared__ __attribute__((aligned(16))) uint16_t Cs[2][kT * BCP];
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[kWaves][2][kT * XP];
-    __shared__ __attribute__((aligned(16))) uint16_t Wh[kWaves][kT * XP];
-    __shared__ __attribute__((aligned(16))) uint16_t Wl[kWaves][kT * XP];
-    __shared__ Scal scal[2];
+// x tile row pitch (bf16) for P head channels: the row stride in dwords is
+// 24, 36 or 12 (mod 64), so that the four rows of a transposed read (8 dwords
+// each) and the rows of a b128 read fall on distinct banks
+constexpr int x_pitch(int P) { return P == 32 ? 48 : P == 64 ? 72 : 152; }
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int c16 = lane & 15, q = lane >> 4;
-    // work item -> (b, h, channel block); items sharing B and C (same batch row
-    // and group) are consecutive and land on one XCD
-    const int64_t npb = p.P / kPW;
-    const int64_t nwork = p.batch * p.H * npb;
-    const int64_t work = xcd_swizzle(blockIdx.x, nwork);
-    const int64_t pb = work % npb;
-    const int64_t h = (work / npb) % p.H;
-    const int64_t b = work / (npb * p.H);
-    const int64_t g = h * p.G / p.H;
-    const int64_t p0 = pb * kPW + wid * 16;   // this wave's first head channel
-    const int N = EXACT ? NMAX : (int)p.N;   // compile-time when the state size is exact
-    const float A = -expf(p.A_log[h]);
-    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
-    const float Dh = p.D ? p.D[h] : 0.0f;
-    const int64_t rowBC = p.G * p.N;
-    const int64_t rowX = p.H * p.P;
-    const uint16_t *Bg = p.B + (b * p.L * p.G + g) * p.N;
-    const uint16_t *Cg = p.C + (b * p.L * p.G + g) * p.N;
-    const uint16_t *Xg = p.x + (b * p.L * p.H + h) * p.P + p0;
-    const float *DTg = p.dt + b * p.L * p.H + h;
-    float *Yg = p.y + (b * p.L * p.H + h) * p.P + p0;
+// LDS and register staging of one chunk of x, B (and C), dt for a work group
+// of NW waves holding head (b, h).  Loads are unconditional so they stay in
+// flight across a chunk.  Full chunks use per-thread base pointers plus a
+// uniform offset; a chunk that crosses L clamps its step index into the
+// tensors (rows past L never contribute: their sigma and w are 0 and their
+// outputs are not stored).
+template <int NMAX, int NW, bool WITH_C>
+struct Stager {
+    static constexpr int NTHR = 64 * NW;
+    static constexpr int P = 16 * NW;
+    static constexpr int BCP = NMAX == 64 ? 72 : 2 * (NMAX / 2 + 12);  // B/C row pitch (bf16)
+    static constexpr int XP = x_pitch(P);
+    static constexpr int LDN = NMAX / 8;                // 16-byte pieces per B/C row
+    static constexpr int PER_T = kT * LDN / NTHR;       // B (and C) pieces per thread
+    static constexpr int SB_STEP = NTHR / LDN;          // steps between pieces i, i+1
+    static constexpr int XPR = P / 8;                   // 16-byte pieces per x row
+    static_assert(PER_T >= 1 && kT * LDN % NTHR == 0 && NTHR % LDN == 0, "B/C pieces must divide evenly");
+    static_assert(kT * XPR == NTHR, "one x piece per thread");
 
-    // state slice S[n][p] for n < N, p in this wave's 16 channels, in the MFMA
-    // output layout: tile nt, lane (column c16, rows q*4 .. q*4+3)
-    f32x4 S[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        S[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.h0 && nt * 16 < N) {
-            const float *src = p.h0 + ((b * p.H + h) * p.P + p0 + c16) * p.N + nt * 16 + q * 4;
-            const float4 v = *reinterpret_cast<const float4 *>(src);
-            S[nt] = f32x4{v.x, v.y, v.z, v.w};
-        }
-    }
-
-    // ---- loads of one chunk into registers
     u32x4 rB[PER_T], rC[PER_T], rX;
     float rdt;
-    // Loads are unconditional so they stay in flight across a chunk.  Full
-    // chunks use per-thread base pointers plus a uniform offset; a chunk that
-    // crosses L clamps its step index into the tensors (rows past L never
-    // contribute: their sigma and w are 0 and their outputs are not stored).
-    const int sB = tid / LDN, nB = (tid % LDN) * 8;           // piece 0 of this thread
-    constexpr int SB_STEP = kThreads / LDN;                    // steps between pieces i, i+1
-    const uint16_t *Bt = Bg + sB * rowBC + min(nB, N - 8);
-    const uint16_t *Ct = Cg + sB * rowBC + min(nB, N - 8);
-    const uint16_t *Xt = Xg + (lane >> 1) * rowX + (lane & 1) * 8;
-    const float *Dt = DTg + (lane & 31) * p.H;
-    auto load_chunk = [&](int64_t t0) __attribute__((always_inline)) {
-        if (t0 + kT <= p.L) {
+    const uint16_t *Bt, *Ct, *Xt;
+    const float *Dt;
+    int sB, nB, sX, cX;
+    int64_t rowBC, rowX, H, L;
+
+    __device__ __forceinline__ void init(const SsdKp &p, int64_t b, int64_t h, int64_t g, int N, int tid) {
+        rowBC = p.G * p.N;
+        rowX = p.H * p.P;
+        H = p.H;
+        L = p.L;
+        sB = tid / LDN;
+        nB = (tid % LDN) * 8;
+        sX = tid / XPR;
+        cX = (tid % XPR) * 8;
+        const int64_t bg = (b * p.L * p.G + g) * p.N + min(nB, N - 8);
+        Bt = p.B + bg + sB * rowBC;
+        Ct = p.C + bg + sB * rowBC;
+        Xt = p.x + (b * p.L * p.H + h) * p.P + cX + sX * rowX;
+        Dt = p.dt + b * p.L * p.H + h + (tid & 31) * p.H;
+    }
+    __device__ __forceinline__ void load(int64_t t0) {
+        if (t0 + kT <= L) {
 #pragma unroll
             for (int i = 0; i < PER_T; ++i) {
                 const int64_t off = (t0 + SB_STEP * i) * rowBC;
                 rB[i] = *reinterpret_cast<const u32x4 *>(Bt + off);
-                rC[i] = *reinterpret_cast<const u32x4 *>(Ct + off);
+                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const u32x4 *>(Ct + off);
             }
             rX = *reinterpret_cast<const u32x4 *>(Xt + t0 * rowX);
-            rdt = Dt[t0 * p.H];
+            rdt = Dt[t0 * H];
         } else {
 #pragma unroll
             for (int i = 0; i < PER_T; ++i) {
                 const int s = sB + SB_STEP * i;
-                const int64_t off = (min(t0 + s, p.L - 1) - sB) * rowBC;   // Bt is at step sB
+                const int64_t off = (min(t0 + s, L - 1) - sB) * rowBC;   // Bt is at step sB
                 rB[i] = *reinterpret_cast<const u32x4 *>(Bt + off);
-                rC[i] = *reinterpret_cast<const u32x4 *>(Ct + off);
+                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const u32x4 *>(Ct + off);
             }
-            const int s = lane >> 1;
-            rX = *reinterpret_cast<const u32x4 *>(Xt + (min(t0 + s, p.L - 1) - s) * rowX);
-            const int sd = lane & 31;
-            rdt = Dt[(min(t0 + sd, p.L - 1) - sd) * p.H];
+            rX = *reinterpret_cast<const u32x4 *>(Xt + (min(t0 + sX, L - 1) - sX) * rowX);
+            const int sd = threadIdx.x & 31;
+            rdt = Dt[(min(t0 + sd, L - 1) - sd) * H];
         }
-    };
-    auto store_chunk = [&](int buf, int64_t t0) __attribute__((always_inline)) {
+    }
+    __device__ __forceinline__ void store(uint16_t *Bs, uint16_t *Cs, uint16_t *Xs) {
 #pragma unroll
         for (int i = 0; i < PER_T; ++i) {
             const int o = (sB + SB_STEP * i) * BCP + nB;
-            *reinterpret_cast<u32x4 *>(&Bs[buf][o]) = rB[i];
-            *reinterpret_cast<u32x4 *>(&Cs[buf][o]) = rC[i];
+            *reinterpret_cast<u32x4 *>(&Bs[o]) = rB[i];
+            if constexpr (WITH_C) *reinterpret_cast<u32x4 *>(&Cs[o]) = rC[i];
         }
-        {
-            const int s = lane >> 1, c8 = (lane & 1) * 8;
-            *reinterpret_cast<u32x4 *>(&Xs[wid][buf][s * XP + c8]) = rX;
-        }
-        if (wid == 0) chunk_scalars(scal[buf], rdt, t0 + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane);
-    };
+        *reinterpret_cast<u32x4 *>(&Xs[sX * XP + cX]) = rX;
+    }
+};
 
-    const int64_t nchunks = (p.L + kT - 1) / kT;
-    load_chunk(0);
-    store_chunk(0, 0);
-    if (nchunks > 1) load_chunk(kT);
+// Decay-weighted inputs w_s x[s][p] of one wave's 16 channels as hi/lo bf16
+// into the wave's own [step][channel] tiles.
+template <int XP>
+__device__ __forceinline__ void weighted_x(const uint16_t *Xs, int p0, const Scal &sc, uint16_t *Wh,
+                                           uint16_t *Wl, int lane) {
+    constexpr int WP = 16 + 8;
+    const int s = lane >> 1, c8 = (lane & 1) * 8;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(&Xs[s * XP + p0 + c8]);
+    const float ws = sc.w[s];
+    u32x4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint2 sp = split_bf16(ws * lo_f(v[i]), ws * hi_f(v[i]));
+        hi[i] = sp.x;
+        lo[i] = sp.y;
+    }
+    *reinterpret_cast<u32x4 *>(&Wh[s * WP + c8]) = hi;
+    *reinterpret_cast<u32x4 *>(&Wl[s * WP + c8]) = lo;
+    // the same wave reads these rows back (transposed): LDS operations of one
+    // wave complete in order, and this keeps the compiler from moving the reads
+    // above the writes
+    asm volatile("" ::: "memory");
+}
+
+// D2+D3 for one wave: S <- e^{cs_end} S + B^T (w o X); A = B^T via transposed reads
+template <int NT, int BCP>
+__device__ __forceinline__ void state_update(f32x4 (&S)[NT], const uint16_t *B_, const uint16_t *Wh,
+                                             const uint16_t *Wl, float e, int N, int lane) {
+    constexpr int WP = 16 + 8;
+    const int q = lane >> 4;
+    const uint2 wh0 = tr_read(Wh, WP, q * 8, 0, lane);
+    const uint2 wh1 = tr_read(Wh, WP, q * 8 + 4, 0, lane);
+    const uint2 wl0 = tr_read(Wl, WP, q * 8, 0, lane);
+    const uint2 wl1 = tr_read(Wl, WP, q * 8 + 4, 0, lane);
+    const u32x4 Whf{wh0.x, wh0.y, wh1.x, wh1.y}, Wlf{wl0.x, wl0.y, wl1.x, wl1.y};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (nt * 16 >= N) break;
+        S[nt] *= e;
+        const uint2 a0 = tr_read(B_, BCP, q * 8, nt * 16, lane);
+        const uint2 a1 = tr_read(B_, BCP, q * 8 + 4, nt * 16, lane);
+        const u32x4 Af{a0.x, a0.y, a1.x, a1.y};
+        S[nt] = mfma16(Af, Whf, S[nt]);
+        S[nt] = mfma16(Af, Wlf, S[nt]);
+    }
+}
+
+// work index -> (b, segment, h); heads of one (batch, segment) are consecutive,
+// so the groups that share B and C rows land on one XCD
+struct Work {
+    int64_t b, k, h;
+    __device__ __forceinline__ Work(int64_t work, int64_t H, int64_t nseg)
+        : b(work / (H * nseg)), k((work / H) % nseg), h(work % H) {}
+};
+
+// ---- the segment's own final state (zero start) and total decay; every
+// segment but the last, all of whose chunks are whole
+template <int NMAX, bool EXACT, int NW>
+__global__ void __launch_bounds__(64 * NW)
+ssd_state_kernel(SsdKp p) {
+    using St = Stager<NMAX, NW, false>;
+    constexpr int NT = NMAX / 16;
+    constexpr int WP = 16 + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * St::BCP];
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kT * St::XP];
+    __shared__ __attribute__((aligned(16))) uint16_t Wh[NW][kT * WP];
+    __shared__ __attribute__((aligned(16))) uint16_t Wl[NW][kT * WP];
+    __shared__ Scal scal[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int c16 = lane & 15, q = lane >> 4;
+    const int64_t nseg1 = p.nseg - 1;
+    const Work wk(xcd_swizzle(blockIdx.x, p.batch * nseg1 * p.H), p.H, nseg1);
+    const int64_t g = wk.h * p.G / p.H;
+    const int p0 = wid * 16;
+    const int N = EXACT ? NMAX : (int)p.N;
+    const float A = -expf(p.A_log[wk.h]);
+    const float bias = p.dt_bias ? p.dt_bias[wk.h] : 0.0f;
+
+    f32x4 S[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) S[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    St st;
+    st.init(p, wk.b, wk.h, g, N, tid);
+    const int64_t tb = wk.k * p.Ls;
+    const int64_t nchunks = p.Ls / kT;
+    st.load(tb);
+    st.store(Bs[0], nullptr, Xs[0]);
+    if (wid == 0) chunk_scalars(scal[0], st.rdt, lane < kT, bias, A, p.mode, lane);
+    if (nchunks > 1) st.load(tb + kT);
+    __syncthreads();
+
+    float cstot = 0.0f;
+    for (int64_t j = 0; j < nchunks; ++j) {
+        const int buf = (int)(j & 1);
+        const Scal &sc = scal[buf];
+        weighted_x<St::XP>(Xs[buf], p0, sc, Wh[wid], Wl[wid], lane);
+        cstot += sc.csend;
+        state_update<NT, St::BCP>(S, Bs[buf], Wh[wid], Wl[wid], sc.end, N, lane);
+        if (j + 1 < nchunks) {
+            st.store(Bs[buf ^ 1], nullptr, Xs[buf ^ 1]);
+            if (wid == 0) chunk_scalars(scal[buf ^ 1], st.rdt, lane < kT, bias, A, p.mode, lane);
+            if (j + 2 < nchunks) st.load(tb + (j + 2) * kT);
+        }
+        __syncthreads();
+    }
+
+    const int64_t slot = (wk.b * p.H + wk.h) * p.nseg + wk.k;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (nt * 16 >= N) break;
+        float *dst = p.ws_state + (slot * p.P + p0 + c16) * p.N + nt * 16 + q * 4;
+        *reinterpret_cast<float4 *>(dst) = make_float4(S[nt][0], S[nt][1], S[nt][2], S[nt][3]);
+    }
+    if (tid == 0) p.ws_decay[slot] = __expf(cstot);
+}
+
+// ---- D3 across segments: the state entering each segment, in place of the
+// segment-local states.  One thread per 4 consecutive (p, n) of one (b, h).
+__global__ void __launch_bounds__(256)
+ssd_pass_kernel(SsdKp p) {
+    const int64_t per = p.P * p.N / 4;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= p.batch * p.H * per) return;
+    const int64_t bh = i / per, e = i % per;
+    float4 S = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (p.h0) S = reinterpret_cast<const float4 *>(p.h0)[bh * per + e];
+    float4 *ws = reinterpret_cast<float4 *>(p.ws_state) + bh * p.nseg * per + e;
+    for (int64_t k = 0; k + 1 < p.nseg; ++k) {
+        const float4 loc = ws[k * per];
+        const float d = p.ws_decay[bh * p.nseg + k];
+        ws[k * per] = S;
+        S = make_float4(fmaf(d, S.x, loc.x), fmaf(d, S.y, loc.y), fmaf(d, S.z, loc.z), fmaf(d, S.w, loc.w));
+    }
+    ws[(p.nseg - 1) * per] = S;
+}
+
+// ---- outputs of one segment from the state entering it
+template <int NMAX, bool EXACT, int NW>
+__global__ void __launch_bounds__(64 * NW)
+ssd_scan_kernel(SsdKp p) {
+    using St = Stager<NMAX, NW, true>;
+    constexpr int NT = NMAX / 16;          // state tiles (16 states each) per wave
+    constexpr int BCP = St::BCP, XP = St::XP;
+    constexpr int WP = 16 + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * BCP];
+    __shared__ __attribute__((aligned(16))) uint16_t Cs[2][kT * BCP];
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kT * XP];
+    __shared__ __attribute__((aligned(16))) uint16_t Wh[NW][kT * WP];
+    __shared__ __attribute__((aligned(16))) uint16_t Wl[NW][kT * WP];
+    // masked C.B^T of the chunk as the A operand of M X: [time tile][hi, lo][lane]
+    __shared__ __attribute__((aligned(16))) u32x4 Ms[2][2][64];
+    __shared__ Scal scal[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int c16 = lane & 15, q = lane >> 4;
+    const Work wk(xcd_swizzle(blockIdx.x, p.batch * p.nseg * p.H), p.H, p.nseg);
+    const int64_t g = wk.h * p.G / p.H;
+    const int p0 = wid * 16;                 // this wave's first head channel
+    const int N = EXACT ? NMAX : (int)p.N;   // compile-time when the state size is exact
+    const float A = -expf(p.A_log[wk.h]);
+    const float bias = p.dt_bias ? p.dt_bias[wk.h] : 0.0f;
+    const float Dh = p.D ? p.D[wk.h] : 0.0f;
+    const int64_t rowX = p.H * p.P;
+    float *Yg = p.y + (wk.b * p.L * p.H + wk.h) * p.P + p0;
+
+    // state slice S[n][p] for n < N, p in this wave's 16 channels, in the MFMA
+    // output layout: tile nt, lane (column c16, rows q*4 .. q*4+3)
+    const float *Sin = p.nseg > 1 ? p.ws_state + ((wk.b * p.H + wk.h) * p.nseg + wk.k) * p.P * p.N
+                                  : (p.h0 ? p.h0 + (wk.b * p.H + wk.h) * p.P * p.N : nullptr);
+    f32x4 S[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        S[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (Sin && nt * 16 < N) {
+            const float4 v = *reinterpret_cast<const float4 *>(Sin + (p0 + c16) * p.N + nt * 16 + q * 4);
+            S[nt] = f32x4{v.x, v.y, v.z, v.w};
+        }
+    }
+
+    St st;
+    st.init(p, wk.b, wk.h, g, N, tid);
+    const int64_t tb = wk.k * p.Ls;
+    const int64_t te = min(tb + p.Ls, p.L);
+    const int64_t nchunks = (te - tb + kT - 1) / kT;
+    st.load(tb);
+    st.store(Bs[0], Cs[0], Xs[0]);
+    if (wid == 0) chunk_scalars(scal[0], st.rdt, tb + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane);
+    if (nchunks > 1) st.load(tb + kT);
     __syncthreads();
 
     for (int64_t j = 0; j < nchunks; ++j) {
         const int buf = (int)(j & 1);
-        const int64_t t0 = j * kT;
-        const uint16_t *B_ = Bs[buf], *C_ = Cs[buf], *X_ = Xs[wid][buf];
+        const int64_t t0 = tb + j * kT;
+        const uint16_t *B_ = Bs[buf], *C_ = Cs[buf], *X_ = Xs[buf];
         const Scal &sc = scal[buf];
 
-        // decay-weighted inputs w_s x[s][p] of this wave's channels, as hi/lo bf16
-        {
-            const int s = lane >> 1, c8 = (lane & 1) * 8;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(&X_[s * XP + c8]);
-            const float ws = sc.w[s];
-            u32x4 hi, lo;
+        // D4, shared: G^T[s][t] = B[s].C[t] for the causal tile pairs (s-tile,
+        // t-tile) (0,0), (0,1), (1,1), one per wave (wave tau % NW); lane holds
+        // column t, rows s = q*4 .. q*4+3.  M[t][s] = G[t][s] e^{cs_t - cs_s}
+        // sigma_s (s <= t) goes to LDS as the A fragments of M X, with K slots
+        // q*8+i <-> s = q*4+i (i < 4) and 16+q*4+(i-4) (i >= 4).
+#pragma unroll
+        for (int tau = 0; tau < 3; ++tau) {
+            if (tau % NW != wid) continue;
+            const int sT = tau == 2 ? 1 : 0, tT = tau == 0 ? 0 : 1;
+            f32x4 G{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < NMAX; kk += 32) {
+                if (kk >= N) break;
+                const u32x4 bf = *reinterpret_cast<const u32x4 *>(&B_[(sT * 16 + c16) * BCP + kk + q * 8]);
+                const u32x4 cf = *reinterpret_cast<const u32x4 *>(&C_[(tT * 16 + c16) * BCP + kk + q * 8]);
+                G = mfma16(bf, cf, G);
+            }
+            const float4 cs4 = *reinterpret_cast<const float4 *>(&sc.cs[sT * 16 + q * 4]);
+            const float4 sg4 = *reinterpret_cast<const float4 *>(&sc.sig[sT * 16 + q * 4]);
+            const float csA[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, sgA[4] = {sg4.x, sg4.y, sg4.z, sg4.w};
+            const float ct = sc.cs[tT * 16 + c16];
+            float m[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint2 sp = split_bf16(ws * lo_f(v[i]), ws * hi_f(v[i]));
-                hi[i] = sp.x;
-                lo[i] = sp.y;
+                const bool keep = (sT < tT) || (q * 4 + i <= c16);     // s <= t
+                m[i] = keep ? G[i] * __expf(ct - csA[i]) * sgA[i] : 0.0f;
             }
-            *reinterpret_cast<u32x4 *>(&Wh[wid][s * XP + c8]) = hi;
-            *reinterpret_cast<u32x4 *>(&Wl[wid][s * XP + c8]) = lo;
-            // the same wave reads these rows back (transposed) below: LDS
-            // operations of one wave complete in order, and this keeps the
-            // compiler from moving the reads above the writes
-            asm volatile("" ::: "memory");
+            const uint2 u0 = split_bf16(m[0], m[1]), u1 = split_bf16(m[2], m[3]);
+            uint32_t *mh = reinterpret_cast<uint32_t *>(&Ms[tT][0][lane]);
+            uint32_t *ml = reinterpret_cast<uint32_t *>(&Ms[tT][1][lane]);
+            const int dw = sT * 2;       // K slots 0-3 hold s-tile 0, slots 4-7 s-tile 1
+            *reinterpret_cast<uint2 *>(mh + dw) = make_uint2(u0.x, u1.x);
+            *reinterpret_cast<uint2 *>(ml + dw) = make_uint2(u0.y, u1.y);
+            if (tau == 0) {              // s-tile 1 lies above the diagonal of t-tile 0
+                *reinterpret_cast<uint2 *>(mh + 2) = make_uint2(0u, 0u);
+                *reinterpret_cast<uint2 *>(ml + 2) = make_uint2(0u, 0u);
+            }
         }
+
+        weighted_x<XP>(X_, p0, sc, Wh[wid], Wl[wid], lane);
 
         // D5: yacc[tt] = C[t][:] S[:][p] for t in time tile tt, then scaled by e^{cs_t}
         f32x4 yacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -287,111 +478,105 @@ ssd_scan_kernel(SsdKp p) {
             yacc[tt][0] *= e.x; yacc[tt][1] *= e.y; yacc[tt][2] *= e.z; yacc[tt][3] *= e.w;
         }
 
-        // D4: G^T[s][t] = B[s].C[t] for the causal tile pairs (s-tile, t-tile)
-        // (0,0), (0,1), (1,1); lane holds column t, rows s = q*4 .. q*4+3
-        f32x4 G00{0.0f, 0.0f, 0.0f, 0.0f}, G01{0.0f, 0.0f, 0.0f, 0.0f}, G11{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int k = 0; k < NMAX; k += 32) {
-            if (k >= N) break;
-            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(&B_[c16 * BCP + k + q * 8]);
-            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(&B_[(16 + c16) * BCP + k + q * 8]);
-            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(&C_[c16 * BCP + k + q * 8]);
-            const u32x4 c1 = *reinterpret_cast<const u32x4 *>(&C_[(16 + c16) * BCP + k + q * 8]);
-            G00 = mfma16(b0, c0, G00);
-            G01 = mfma16(b0, c1, G01);
-            G11 = mfma16(b1, c1, G11);
-        }
-        // M[t][s] = G[t][s] e^{cs_t - cs_s} sigma_s (s <= t) -> A fragments of M X with
-        // K slots q*8+i <-> s = q*4+i (i < 4) and 16+q*4+(i-4) (i >= 4)
+        __syncthreads();   // the shared M fragments are complete
+
+        // D4: yacc[tt] += M X, X fragments read transposed from the x tile
         {
-            const float4 cs0 = *reinterpret_cast<const float4 *>(&sc.cs[q * 4]);
-            const float4 cs1 = *reinterpret_cast<const float4 *>(&sc.cs[16 + q * 4]);
-            const float4 sg0 = *reinterpret_cast<const float4 *>(&sc.sig[q * 4]);
-            const float4 sg1 = *reinterpret_cast<const float4 *>(&sc.sig[16 + q * 4]);
-            const float csA[4] = {cs0.x, cs0.y, cs0.z, cs0.w}, csB[4] = {cs1.x, cs1.y, cs1.z, cs1.w};
-            const float sgA[4] = {sg0.x, sg0.y, sg0.z, sg0.w}, sgB[4] = {sg1.x, sg1.y, sg1.z, sg1.w};
-            const float ct0 = sc.cs[c16], ct1 = sc.cs[16 + c16];
-            float m0[8], m1[8];     // time tile 0 (t = c16) and 1 (t = 16 + c16)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sA = q * 4 + i, sB = 16 + q * 4 + i;
-                m0[i] = (sA <= c16) ? G00[i] * __expf(ct0 - csA[i]) * sgA[i] : 0.0f;
-                m0[4 + i] = 0.0f;                                   // s >= 16 > t
-                m1[i] = G01[i] * __expf(ct1 - csA[i]) * sgA[i];     // s < 16 <= t
-                m1[4 + i] = (sB <= 16 + c16) ? G11[i] * __expf(ct1 - csB[i]) * sgB[i] : 0.0f;
-            }
-            // D4: yacc[tt] += M X, X fragments read transposed from this wave's x tile
-            const uint2 xa0 = tr_read(X_, XP, q * 4, 0, lane);
-            const uint2 xa1 = tr_read(X_, XP, 16 + q * 4, 0, lane);
+            const uint2 xa0 = tr_read(X_, XP, q * 4, p0, lane);
+            const uint2 xa1 = tr_read(X_, XP, 16 + q * 4, p0, lane);
             const u32x4 Xf{xa0.x, xa0.y, xa1.x, xa1.y};
-            {
-                const uint2 u0 = split_bf16(m0[0], m0[1]), u1 = split_bf16(m0[2], m0[3]);
-                const u32x4 Mh{u0.x, u1.x, 0u, 0u}, Ml{u0.y, u1.y, 0u, 0u};
-                yacc[0] = mfma16(Mh, Xf, yacc[0]);
-                yacc[0] = mfma16(Ml, Xf, yacc[0]);
-            }
-            {
-                const uint2 u0 = split_bf16(m1[0], m1[1]), u1 = split_bf16(m1[2], m1[3]);
-                const uint2 u2 = split_bf16(m1[4], m1[5]), u3 = split_bf16(m1[6], m1[7]);
-                const u32x4 Mh{u0.x, u1.x, u2.x, u3.x}, Ml{u0.y, u1.y, u2.y, u3.y};
-                yacc[1] = mfma16(Mh, Xf, yacc[1]);
-                yacc[1] = mfma16(Ml, Xf, yacc[1]);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                yacc[tt] = mfma16(Ms[tt][0][lane], Xf, yacc[tt]);
+                yacc[tt] = mfma16(Ms[tt][1][lane], Xf, yacc[tt]);
             }
         }
 
         // skip term and store: lane (column c16, rows t = tt*16 + q*4 + i)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const uint2 xv = tr_read(X_, XP, tt * 16 + q * 4, 0, lane);
+            const uint2 xv = tr_read(X_, XP, tt * 16 + q * 4, p0, lane);
             const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
             float *yr = Yg + (t0 + tt * 16 + q * 4) * rowX + c16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (t0 + tt * 16 + q * 4 + i < p.L) yr[i * rowX] = fmaf(Dh, xs[i], yacc[tt][i]);
+                if (t0 + tt * 16 + q * 4 + i < te) yr[i * rowX] = fmaf(Dh, xs[i], yacc[tt][i]);
             }
         }
 
-        // D2+D3: S <- e^{cs_end} S + B^T (w o X); A = B^T via transposed reads
-        {
-            const float e = sc.end;
-            const uint2 wh0 = tr_read(Wh[wid], XP, q * 8, 0, lane);
-            const uint2 wh1 = tr_read(Wh[wid], XP, q * 8 + 4, 0, lane);
-            const uint2 wl0 = tr_read(Wl[wid], XP, q * 8, 0, lane);
-            const uint2 wl1 = tr_read(Wl[wid], XP, q * 8 + 4, 0, lane);
-            const u32x4 Whf{wh0.x, wh0.y, wh1.x, wh1.y}, Wlf{wl0.x, wl0.y, wl1.x, wl1.y};
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                if (nt * 16 >= N) break;
-                S[nt] *= e;
-                const uint2 a0 = tr_read(B_, BCP, q * 8, nt * 16, lane);
-                const uint2 a1 = tr_read(B_, BCP, q * 8 + 4, nt * 16, lane);
-                const u32x4 Af{a0.x, a0.y, a1.x, a1.y};
-                S[nt] = mfma16(Af, Whf, S[nt]);
-                S[nt] = mfma16(Af, Wlf, S[nt]);
-            }
-        }
+        // D2+D3
+        state_update<NT, BCP>(S, B_, Wh[wid], Wl[wid], sc.end, N, lane);
 
         // stage chunk j+1, start loading chunk j+2
         if (j + 1 < nchunks) {
-            store_chunk(buf ^ 1, t0 + kT);
-            if (j + 2 < nchunks) load_chunk(t0 + 2 * kT);
+            st.store(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1]);
+            if (wid == 0)
+                chunk_scalars(scal[buf ^ 1], st.rdt, t0 + kT + (lane & 31) < p.L && lane < kT, bias, A,
+                              p.mode, lane);
+            if (j + 2 < nchunks) st.load(t0 + 2 * kT);
         }
         __syncthreads();
     }
 
-    if (p.h_final) {
+    if (p.h_final && wk.k == p.nseg - 1) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (nt * 16 >= N) break;
-            float *dst = p.h_final + ((b * p.H + h) * p.P + p0 + c16) * p.N + nt * 16 + q * 4;
+            float *dst = p.h_final + ((wk.b * p.H + wk.h) * p.P + p0 + c16) * p.N + nt * 16 + q * 4;
             *reinterpret_cast<float4 *>(dst) = make_float4(S[nt][0], S[nt][1], S[nt][2], S[nt][3]);
         }
     }
 }
 
+struct Plan {
+    int64_t nseg, Ls;
+};
+// Segments: enough (batch, segment, head) groups for kTargetWaves waves, no
+// segment shorter than kMinSeg steps, lengths a multiple of the chunk.
+Plan plan(int64_t batch, int64_t L, int64_t H, int64_t P) {
+    const int64_t waves = batch * H * (P / 16);
+    int64_t nseg = (kTargetWaves + waves - 1) / waves;
+    nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, L / kMinSeg));
+    const int64_t Ls = ((L + nseg - 1) / nseg + kT - 1) / kT * kT;
+    return Plan{(L + Ls - 1) / Ls, Ls};
+}
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+template <int NMAX, bool EXACT, int NW>
+void launch_all(const SsdKp &p, hipStream_t stream) {
+    if (p.nseg > 1) {
+        const int64_t n1 = p.batch * (p.nseg - 1) * p.H;
+        hipLaunchKernelGGL((ssd_state_kernel<NMAX, EXACT, NW>), dim3((unsigned)n1), dim3(64 * NW), 0, stream, p);
+        const int64_t nt = p.batch * p.H * p.P * p.N / 4;
+        hipLaunchKernelGGL(ssd_pass_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream, p);
+    }
+    const int64_t n = p.batch * p.nseg * p.H;
+    hipLaunchKernelGGL((ssd_scan_kernel<NMAX, EXACT, NW>), dim3((unsigned)n), dim3(64 * NW), 0, stream, p);
+}
+
+template <int NW>
+void launch_n(const SsdKp &p, hipStream_t stream) {
+    // the B/C tile is at least P wide so that its pieces divide over the group
+    constexpr int NMIN = 16 * NW < 64 ? 64 : 16 * NW;
+    if constexpr (NMIN == 64) {
+        if (p.N == 64) return launch_all<64, true, NW>(p, stream);
+        if (p.N < 64) return launch_all<64, false, NW>(p, stream);
+    }
+    if (p.N == 128) return launch_all<128, true, NW>(p, stream);
+    if (p.N < 128) return launch_all<128, false, NW>(p, stream);
+    if (p.N == 256) return launch_all<256, true, NW>(p, stream);
+    launch_all<256, false, NW>(p, stream);
+}
+
 }  // namespace
 
-size_t ssd_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                           int64_t) {
+    const Plan pl = plan(batch, L, nheads, headdim);
+    if (pl.nseg <= 1) return 0;
+    return align256((size_t)(batch * nheads * pl.nseg * headdim * d_state) * sizeof(float)) +
+           (size_t)(batch * nheads * pl.nseg) * sizeof(float);
+}
 
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_name) {
     *kernel_name = "ssd_scan_kernel";
@@ -403,14 +588,18 @@ hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_
     p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
     p.batch = a.batch; p.L = a.L; p.H = a.nheads; p.P = a.headdim; p.N = a.d_state; p.G = a.ngroups;
     p.mode = (int)(a.flags & 0x3u);
-    const int64_t nwork = p.batch * p.H * (p.P / kPW);
-    const dim3 grid((unsigned)nwork), block(kThreads);
-    if (p.N == 64) hipLaunchKernelGGL((ssd_scan_kernel<64, true>), grid, block, 0, stream, p);
-    else if (p.N == 128) hipLaunchKernelGGL((ssd_scan_kernel<128, true>), grid, block, 0, stream, p);
-    else if (p.N == 256) hipLaunchKernelGGL((ssd_scan_kernel<256, true>), grid, block, 0, stream, p);
-    else if (p.N < 64) hipLaunchKernelGGL((ssd_scan_kernel<64, false>), grid, block, 0, stream, p);
-    else if (p.N < 128) hipLaunchKernelGGL((ssd_scan_kernel<128, false>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((ssd_scan_kernel<256, false>), grid, block, 0, stream, p);
+    const Plan pl = plan(p.batch, p.L, p.H, p.P);
+    p.nseg = pl.nseg;
+    p.Ls = pl.Ls;
+    if (p.nseg > 1) {
+        p.ws_state = static_cast<float *>(a.workspace);
+        p.ws_decay = reinterpret_cast<float *>(
+            static_cast<char *>(a.workspace) +
+            align256((size_t)(p.batch * p.H * p.nseg * p.P * p.N) * sizeof(float)));
+    }
+    if (p.P == 32) launch_n<2>(p, stream);
+    else if (p.P == 64) launch_n<4>(p, stream);
+    else launch_n<8>(p, stream);
     return hipGetLastError();
 }
 

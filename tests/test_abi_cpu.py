@@ -88,8 +88,11 @@ def test_ssd_argument_checks(lib):
     assert _ssd(lib, dims=(2, 300, 4, 64, 128, 2, 0)) == INVALID
     assert _ssd(lib, dtype=0) == UNSUPPORTED and "bf16" in _err(lib)
     assert _ssd(lib, flags=0x8) == INVALID
-    # the SSD kernel carries the state in registers: no workspace
+    # short sequences run as one segment (no workspace); long ones keep one
+    # (P x N) fp32 state per (batch, head, segment) plus a decay per segment
     assert lib.ssd_chunk_scan_fwd_workspace_size(2, 300, 4, 64, 128, 2, 256) == 0
+    ws = lib.ssd_chunk_scan_fwd_workspace_size(8, 4096, 24, 64, 128, 1, 256)
+    assert ws >= 8 * 24 * 2 * 64 * 128 * 4 and ws % 4 == 0
     assert lib.ssd_chunk_scan_fwd_workspace_size(0, 300, 4, 64, 128, 2, 256) == 0
 
 

@@ -32,6 +32,11 @@ CASES = [  # batch, L, H, P, N, G, Q, flags, h0
     (1, 1, 2, 64, 128, 1, 256, DT, True),
     (1, 65, 2, 64, 128, 1, 64, ZOH, True),
     (2, 513, 4, 64, 128, 1, 256, DT, False),
+    # long enough to be cut into segments (state kernel + pass + scan), last segment partial
+    (1, 2000, 2, 64, 128, 1, 256, DT, True),
+    (1, 1500, 1, 32, 64, 1, 64, ZOH, True),
+    (1, 777, 3, 128, 128, 3, 128, DT, True),
+    (1, 1100, 2, 64, 96, 2, 64, ONE, False),
 ]
 
 
@@ -73,3 +78,40 @@ def test_ssd_workloads_sampled(cuda_device, name, k):
     report(f"{name} sampled", y=ey, h_final=eh)
     assert np.isfinite(y).all()
     assert ey <= TOL_BF16 and eh <= TOL_BF16
+
+
+def test_ssd_in_place_state(cuda_device):
+    """h0 and h_final may be the same buffer (the carried state is updated in place)."""
+    import torch
+    from helpers import lib
+    inp = synth.ssd_inputs(1, 1800, 2, 64, 128, 1, seed=(7,), h0=True)
+    t = inp.torch(cuda_device)
+    ref = lib().ssd_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                   t["h0"], return_final=True)
+    state = t["h0"].clone()
+    y = lib().ssd_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                 state, h_final=state)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref[0]) and torch.equal(state, ref[1])
+
+
+def test_ssd_carry_composition(cuda_device):
+    """Scanning [0, L1) then [L1, L) from the carried state matches one scan of [0, L)."""
+    import torch
+    from helpers import lib
+    inp = synth.ssd_inputs(1, 1600, 2, 64, 128, 1, seed=(8,), h0=True)
+    t = inp.torch(cuda_device)
+    whole = lib().ssd_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                     t["h0"], return_final=True)
+    L1 = 700
+    part = lambda a, lo, hi: a[:, lo:hi].contiguous()
+    first = lib().ssd_chunk_scan_fwd(part(t["x"], 0, L1), part(t["dt"], 0, L1), t["dt_bias"], t["A_log"],
+                                     part(t["B"], 0, L1), part(t["C"], 0, L1), t["D"], t["h0"],
+                                     return_final=True)
+    second = lib().ssd_chunk_scan_fwd(part(t["x"], L1, None), part(t["dt"], L1, None), t["dt_bias"],
+                                      t["A_log"], part(t["B"], L1, None), part(t["C"], L1, None), t["D"],
+                                      first[1], return_final=True)
+    torch.cuda.synchronize()
+    y = torch.cat([first[0], second[0]], 1).cpu().numpy()
+    assert synth.max_rel_err(y, whole[0].cpu().numpy()) <= TOL_BF16
+    assert synth.max_rel_err(second[1].cpu().numpy(), whole[1].cpu().numpy()) <= TOL_BF16
