@@ -98,7 +98,7 @@ def make_runner(name, dev):
             t = copies[i % N_ROTATE]
             lib.ssd_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
                                    None, chunk_len=w["chunk_len"], y=y, h_final=hf, workspace=ws)
-        return step, dims, w, ["ssd_chunk_state_kernel", "ssd_state_pass_kernel", "ssd_chunk_scan_kernel"]
+        return step, dims, w, ["ssd_state_kernel", "ssd_pass_kernel", "ssd_scan_kernel"]
     t0 = copies[0]
     y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
     hf = torch.empty((dims["batch"], dims["nheads"], dims["headdim"], dims["n_complex"], 2),

@@ -19,8 +19,11 @@ LIB = os.path.join(HERE, "libssmscan.so")
 SOURCES = ["abi.hip", "s6_scan.hip", "ssd_scan.hip", "cssd_scan.hip"]
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 # Packed fp32 ops are switched off: the compiler must not emit v_pk_{add,mul,fma}_f32.
+# MFMA accumulators are kept in ordinary VGPRs, so the fp32 state that the SSD
+# kernels scale and split between contractions needs no AGPR round trips.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wno-unused-command-line-argument"]
 
 

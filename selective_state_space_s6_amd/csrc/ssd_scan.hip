@@ -93,6 +93,22 @@ struct SsdKp {
     int mode;           // 0 ZOH, 1 DT, 2 ONE
 };
 
+// Inclusive prefix sum over each 32-lane half of a wave with DPP: row_shr 1,
+// 2, 4, 8 with zero fill scans each 16-lane row, then row_bcast:15 adds the
+// last lane of rows 0 and 2 to rows 1 and 3.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float scan32(float v) {
+    v += dpp_f<0x111>(v);
+    v += dpp_f<0x112>(v);
+    v += dpp_f<0x114>(v);
+    v += dpp_f<0x118>(v);
+    v += dpp_f<0x142, 0xa>(v);
+    return v;
+}
+
 // per-chunk scalars in LDS
 struct Scal {
     float cs[kT];    // inclusive cumulative sum of a from the chunk start
@@ -114,13 +130,8 @@ __device__ __forceinline__ void chunk_scalars(Scal &sc, float dtv, bool valid, f
         else if (mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
         else sg = 1.0f;
     }
-    float v = a;
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
-        const float o = __shfl_up(v, off, 32);
-        if ((lane & 31) >= off) v += o;
-    }
-    const float cend = __shfl(v, 31, 32);
+    const float v = scan32(a);
+    const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
     if (lane < kT) {
         sc.cs[lane] = v;
         sc.ecs[lane] = __expf(v);
@@ -140,11 +151,11 @@ constexpr int x_pitch(int P) { return P == 32 ? 48 : P == 64 ? 72 : 152; }
 
 // LDS and register staging of one chunk of x, B (and C), dt for a work group
 // of NW waves holding head (b, h).  Loads are unconditional so they stay in
-// flight across a chunk.  Full chunks use per-thread base pointers plus a
-// uniform offset; a chunk that crosses L clamps its step index into the
-// tensors (rows past L never contribute: their sigma and w are 0 and their
-// outputs are not stored).
-template <int NMAX, int NW, bool WITH_C>
+// flight across a chunk.  Addresses are a uniform base (the chunk's first row)
+// plus a 32-bit per-thread offset; a chunk that crosses L clamps its step
+// index into the tensors (rows past L never contribute: their sigma and w are
+// 0 and their outputs are not stored).
+template <int NMAX, int NW, bool WITH_C, int NS = 1>
 struct Stager {
     static constexpr int NTHR = 64 * NW;
     static constexpr int P = 16 * NW;
@@ -157,11 +168,13 @@ struct Stager {
     static_assert(PER_T >= 1 && kT * LDN % NTHR == 0 && NTHR % LDN == 0, "B/C pieces must divide evenly");
     static_assert(kT * XPR == NTHR, "one x piece per thread");
 
-    u32x4 rB[PER_T], rC[PER_T], rX;
-    float rdt;
-    const uint16_t *Bt, *Ct, *Xt;
-    const float *Dt;
-    int sB, nB, sX, cX;
+    // NS register stages: a chunk is loaded NS chunks before it is staged to LDS
+    u32x4 rB[NS][PER_T], rC[NS][PER_T], rX[NS];
+    float rdt[NS];
+    const uint16_t *Bb, *Cb, *Xb;   // step 0 of this (batch, group) / (batch, head)
+    const float *Db;
+    uint32_t colB;                  // this thread's B/C column (clamped into the state)
+    int sB, nB, sX, cX, sD;
     int64_t rowBC, rowX, H, L;
 
     __device__ __forceinline__ void init(const SsdKp &p, int64_t b, int64_t h, int64_t g, int N, int tid) {
@@ -173,55 +186,60 @@ struct Stager {
         nB = (tid % LDN) * 8;
         sX = tid / XPR;
         cX = (tid % XPR) * 8;
-        const int64_t bg = (b * p.L * p.G + g) * p.N + min(nB, N - 8);
-        Bt = p.B + bg + sB * rowBC;
-        Ct = p.C + bg + sB * rowBC;
-        Xt = p.x + (b * p.L * p.H + h) * p.P + cX + sX * rowX;
-        Dt = p.dt + b * p.L * p.H + h + (tid & 31) * p.H;
+        sD = tid & 31;
+        colB = (uint32_t)min(nB, N - 8);
+        Bb = p.B + (b * p.L * p.G + g) * p.N;
+        Cb = p.C + (b * p.L * p.G + g) * p.N;
+        Xb = p.x + (b * p.L * p.H + h) * p.P;
+        Db = p.dt + b * p.L * p.H + h;
     }
+    template <int S>
     __device__ __forceinline__ void load(int64_t t0) {
+        const uint16_t *Bu = Bb + t0 * rowBC, *Cu = Cb + t0 * rowBC, *Xu = Xb + t0 * rowX;
+        const float *Du = Db + t0 * H;
         if (t0 + kT <= L) {
 #pragma unroll
             for (int i = 0; i < PER_T; ++i) {
-                const int64_t off = (t0 + SB_STEP * i) * rowBC;
-                rB[i] = *reinterpret_cast<const u32x4 *>(Bt + off);
-                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const u32x4 *>(Ct + off);
+                const uint32_t o = (uint32_t)(sB * rowBC) + colB;
+                rB[S][i] = *reinterpret_cast<const u32x4 *>(Bu + SB_STEP * i * rowBC + o);
+                if constexpr (WITH_C) rC[S][i] = *reinterpret_cast<const u32x4 *>(Cu + SB_STEP * i * rowBC + o);
             }
-            rX = *reinterpret_cast<const u32x4 *>(Xt + t0 * rowX);
-            rdt = Dt[t0 * H];
+            rX[S] = *reinterpret_cast<const u32x4 *>(Xu + (uint32_t)(sX * rowX + cX));
+            rdt[S] = Du[(uint32_t)(sD * H)];
         } else {
+            const int last = (int)(L - 1 - t0);   // last valid step of the chunk
 #pragma unroll
             for (int i = 0; i < PER_T; ++i) {
-                const int s = sB + SB_STEP * i;
-                const int64_t off = (min(t0 + s, L - 1) - sB) * rowBC;   // Bt is at step sB
-                rB[i] = *reinterpret_cast<const u32x4 *>(Bt + off);
-                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const u32x4 *>(Ct + off);
+                const uint32_t o = (uint32_t)(min(sB + SB_STEP * i, last) * rowBC) + colB;
+                rB[S][i] = *reinterpret_cast<const u32x4 *>(Bu + o);
+                if constexpr (WITH_C) rC[S][i] = *reinterpret_cast<const u32x4 *>(Cu + o);
             }
-            rX = *reinterpret_cast<const u32x4 *>(Xt + (min(t0 + sX, L - 1) - sX) * rowX);
-            const int sd = threadIdx.x & 31;
-            rdt = Dt[(min(t0 + sd, L - 1) - sd) * H];
+            rX[S] = *reinterpret_cast<const u32x4 *>(Xu + (uint32_t)(min(sX, last) * rowX + cX));
+            rdt[S] = Du[(uint32_t)(min(sD, last) * H)];
         }
     }
+    template <int S>
     __device__ __forceinline__ void store(uint16_t *Bs, uint16_t *Cs, uint16_t *Xs) {
 #pragma unroll
         for (int i = 0; i < PER_T; ++i) {
             const int o = (sB + SB_STEP * i) * BCP + nB;
-            *reinterpret_cast<u32x4 *>(&Bs[o]) = rB[i];
-            if constexpr (WITH_C) *reinterpret_cast<u32x4 *>(&Cs[o]) = rC[i];
+            *reinterpret_cast<u32x4 *>(&Bs[o]) = rB[S][i];
+            if constexpr (WITH_C) *reinterpret_cast<u32x4 *>(&Cs[o]) = rC[S][i];
         }
-        *reinterpret_cast<u32x4 *>(&Xs[sX * XP + cX]) = rX;
+        *reinterpret_cast<u32x4 *>(&Xs[sX * XP + cX]) = rX[S];
     }
 };
 
 // Decay-weighted inputs w_s x[s][p] of one wave's 16 channels as hi/lo bf16
-// into the wave's own [step][channel] tiles.
+// into the wave's own [step][channel] tiles (row pitch 16: the four rows of a
+// transposed read are 32 consecutive dwords, so no bank is hit twice).
+constexpr int WP = 16;
 template <int XP>
-__device__ __forceinline__ void weighted_x(const uint16_t *Xs, int p0, const Scal &sc, uint16_t *Wh,
+__device__ __forceinline__ void weighted_x(const uint16_t *Xs, int p0, const float *w, uint16_t *Wh,
                                            uint16_t *Wl, int lane) {
-    constexpr int WP = 16 + 8;
     const int s = lane >> 1, c8 = (lane & 1) * 8;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(&Xs[s * XP + p0 + c8]);
-    const float ws = sc.w[s];
+    const float ws = w[s];
     u32x4 hi, lo;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -241,7 +259,6 @@ __device__ __forceinline__ void weighted_x(const uint16_t *Xs, int p0, const Sca
 template <int NT, int BCP>
 __device__ __forceinline__ void state_update(f32x4 (&S)[NT], const uint16_t *B_, const uint16_t *Wh,
                                              const uint16_t *Wl, float e, int N, int lane) {
-    constexpr int WP = 16 + 8;
     const int q = lane >> 4;
     const uint2 wh0 = tr_read(Wh, WP, q * 8, 0, lane);
     const uint2 wh1 = tr_read(Wh, WP, q * 8 + 4, 0, lane);
@@ -269,20 +286,34 @@ struct Work {
 };
 
 // ---- the segment's own final state (zero start) and total decay; every
-// segment but the last, all of whose chunks are whole
+// segment but the last, all of whose chunks are whole.
+//   S_local[p][n] = sum_s e^{sum_{r > s} a_r} sigma_s x_s[p] B_s[n]
+// The segment is walked backwards, so the weight of step s is one exp of the
+// running suffix sum of a (same-signed terms, no cancellation) and the state
+// needs no rescaling between chunks; the contraction over s is a plain GEMM.
+// Chunks are loaded NS = 3 chunks ahead.
+template <int NS, int I, typename F>
+__device__ __forceinline__ void unroll_stages(F &&f) {
+    if constexpr (I < NS) {
+        f(std::integral_constant<int, I>{});
+        unroll_stages<NS, I + 1>(f);
+    }
+}
+
 template <int NMAX, bool EXACT, int NW>
 __global__ void __launch_bounds__(64 * NW)
 ssd_state_kernel(SsdKp p) {
-    using St = Stager<NMAX, NW, false>;
+    constexpr int NS = 3;
+    using St = Stager<NMAX, NW, false, NS>;
     constexpr int NT = NMAX / 16;
-    constexpr int WP = 16 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * St::BCP];
     __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kT * St::XP];
     __shared__ __attribute__((aligned(16))) uint16_t Wh[NW][kT * WP];
     __shared__ __attribute__((aligned(16))) uint16_t Wl[NW][kT * WP];
-    __shared__ Scal scal[2];
+    __shared__ __attribute__((aligned(16))) float wsc[2][kT];
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int c16 = lane & 15, q = lane >> 4;
     const int64_t nseg1 = p.nseg - 1;
     const Work wk(xcd_swizzle(blockIdx.x, p.batch * nseg1 * p.H), p.H, nseg1);
@@ -298,27 +329,51 @@ ssd_state_kernel(SsdKp p) {
 
     St st;
     st.init(p, wk.b, wk.h, g, N, tid);
-    const int64_t tb = wk.k * p.Ls;
-    const int64_t nchunks = p.Ls / kT;
-    st.load(tb);
-    st.store(Bs[0], nullptr, Xs[0]);
-    if (wid == 0) chunk_scalars(scal[0], st.rdt, lane < kT, bias, A, p.mode, lane);
-    if (nchunks > 1) st.load(tb + kT);
+    st.sD = kT - 1 - (tid & 31);                           // dt lanes in reverse step order
+    const int64_t nch = p.Ls / kT;
+    const int64_t tlast = wk.k * p.Ls + (nch - 1) * kT;   // first step of the last chunk
+    // weights of one chunk from its dt (wave 0; lane i holds step 31 - i, so
+    // the lane-order prefix sum is the step-order suffix sum); R is the sum of
+    // a over the later steps of the segment, kept by wave 0
+    float R = 0.0f;
+    auto weights = [&](float *w, float dtv) __attribute__((always_inline)) {
+        const float dl = softplus(dtv + bias);
+        const float a = dl * A;
+        float sg;
+        if (p.mode == 1) sg = dl;
+        else if (p.mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
+        else sg = 1.0f;
+        const float v = scan32(a);                     // sum of a over steps >= this step
+        if (lane < kT) w[kT - 1 - lane] = __expf(R + (v - a)) * sg;
+        R += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    };
+
+    unroll_stages<NS, 0>([&](auto sTag) __attribute__((always_inline)) {
+        constexpr int S_ = decltype(sTag)::value;
+        if (S_ < nch) st.template load<S_>(tlast - S_ * kT);
+    });
+    st.template store<0>(Bs[0], nullptr, Xs[0]);
+    if (wid == 0) weights(wsc[0], st.rdt[0]);
+    if (NS < nch) st.template load<0>(tlast - NS * kT);
     __syncthreads();
 
-    float cstot = 0.0f;
-    for (int64_t j = 0; j < nchunks; ++j) {
-        const int buf = (int)(j & 1);
-        const Scal &sc = scal[buf];
-        weighted_x<St::XP>(Xs[buf], p0, sc, Wh[wid], Wl[wid], lane);
-        cstot += sc.csend;
-        state_update<NT, St::BCP>(S, Bs[buf], Wh[wid], Wl[wid], sc.end, N, lane);
-        if (j + 1 < nchunks) {
-            st.store(Bs[buf ^ 1], nullptr, Xs[buf ^ 1]);
-            if (wid == 0) chunk_scalars(scal[buf ^ 1], st.rdt, lane < kT, bias, A, p.mode, lane);
-            if (j + 2 < nchunks) st.load(tb + (j + 2) * kT);
-        }
-        __syncthreads();
+    // chunk c (c = 0 is the last chunk of the segment) is in register stage c % NS
+    for (int64_t c0 = 0; c0 < nch; c0 += NS) {
+        unroll_stages<NS, 0>([&](auto sTag) __attribute__((always_inline)) {
+            constexpr int S_ = decltype(sTag)::value;
+            const int64_t c = c0 + S_;
+            if (c >= nch) return;
+            const int buf = (int)(c & 1);
+            weighted_x<St::XP>(Xs[buf], p0, wsc[buf], Wh[wid], Wl[wid], lane);
+            state_update<NT, St::BCP>(S, Bs[buf], Wh[wid], Wl[wid], 1.0f, N, lane);
+            if (c + 1 < nch) {
+                constexpr int SN = (S_ + 1) % NS;
+                st.template store<SN>(Bs[buf ^ 1], nullptr, Xs[buf ^ 1]);
+                if (wid == 0) weights(wsc[buf ^ 1], st.rdt[SN]);
+                if (c + 1 + NS < nch) st.template load<SN>(tlast - (c + 1 + NS) * kT);
+            }
+            __syncthreads();
+        });
     }
 
     const int64_t slot = (wk.b * p.H + wk.h) * p.nseg + wk.k;
@@ -328,7 +383,7 @@ ssd_state_kernel(SsdKp p) {
         float *dst = p.ws_state + (slot * p.P + p0 + c16) * p.N + nt * 16 + q * 4;
         *reinterpret_cast<float4 *>(dst) = make_float4(S[nt][0], S[nt][1], S[nt][2], S[nt][3]);
     }
-    if (tid == 0) p.ws_decay[slot] = __expf(cstot);
+    if (tid == 0) p.ws_decay[slot] = __expf(R);
 }
 
 // ---- D3 across segments: the state entering each segment, in place of the
@@ -358,17 +413,21 @@ ssd_scan_kernel(SsdKp p) {
     using St = Stager<NMAX, NW, true>;
     constexpr int NT = NMAX / 16;          // state tiles (16 states each) per wave
     constexpr int BCP = St::BCP, XP = St::XP;
-    constexpr int WP = 16 + 8;
+    // Once a chunk's C tile has been consumed (after the first barrier of the
+    // chunk) it holds the waves' weighted inputs, when they fit; that keeps
+    // three groups of four waves resident per CU.
+    constexpr bool W_IN_C = NW * 2 * kT * WP <= kT * BCP;
+    constexpr int WSEP = W_IN_C ? 1 : NW;
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * BCP];
     __shared__ __attribute__((aligned(16))) uint16_t Cs[2][kT * BCP];
     __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kT * XP];
-    __shared__ __attribute__((aligned(16))) uint16_t Wh[NW][kT * WP];
-    __shared__ __attribute__((aligned(16))) uint16_t Wl[NW][kT * WP];
+    __shared__ __attribute__((aligned(16))) uint16_t Wsep[WSEP][2 * kT * WP];
     // masked C.B^T of the chunk as the A operand of M X: [time tile][hi, lo][lane]
     __shared__ __attribute__((aligned(16))) u32x4 Ms[2][2][64];
     __shared__ Scal scal[2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int c16 = lane & 15, q = lane >> 4;
     const Work wk(xcd_swizzle(blockIdx.x, p.batch * p.nseg * p.H), p.H, p.nseg);
     const int64_t g = wk.h * p.G / p.H;
@@ -379,6 +438,7 @@ ssd_scan_kernel(SsdKp p) {
     const float Dh = p.D ? p.D[wk.h] : 0.0f;
     const int64_t rowX = p.H * p.P;
     float *Yg = p.y + (wk.b * p.L * p.H + wk.h) * p.P + p0;
+    const uint32_t ylane = (uint32_t)(q * 4 * rowX + c16) * 4u;   // byte offset of the lane's element
 
     // state slice S[n][p] for n < N, p in this wave's 16 channels, in the MFMA
     // output layout: tile nt, lane (column c16, rows q*4 .. q*4+3)
@@ -399,10 +459,10 @@ ssd_scan_kernel(SsdKp p) {
     const int64_t tb = wk.k * p.Ls;
     const int64_t te = min(tb + p.Ls, p.L);
     const int64_t nchunks = (te - tb + kT - 1) / kT;
-    st.load(tb);
-    st.store(Bs[0], Cs[0], Xs[0]);
-    if (wid == 0) chunk_scalars(scal[0], st.rdt, tb + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane);
-    if (nchunks > 1) st.load(tb + kT);
+    st.template load<0>(tb);
+    st.template store<0>(Bs[0], Cs[0], Xs[0]);
+    if (wid == NW - 1) chunk_scalars(scal[0], st.rdt[0], tb + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane);
+    if (nchunks > 1) st.template load<0>(tb + kT);
     __syncthreads();
 
     for (int64_t j = 0; j < nchunks; ++j) {
@@ -450,8 +510,6 @@ ssd_scan_kernel(SsdKp p) {
             }
         }
 
-        weighted_x<XP>(X_, p0, sc, Wh[wid], Wl[wid], lane);
-
         // D5: yacc[tt] = C[t][:] S[:][p] for t in time tile tt, then scaled by e^{cs_t}
         f32x4 yacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
@@ -478,7 +536,11 @@ ssd_scan_kernel(SsdKp p) {
             yacc[tt][0] *= e.x; yacc[tt][1] *= e.y; yacc[tt][2] *= e.z; yacc[tt][3] *= e.w;
         }
 
-        __syncthreads();   // the shared M fragments are complete
+        __syncthreads();   // the shared M fragments are complete; C is consumed
+
+        uint16_t *Wh = W_IN_C ? Cs[buf] + wid * 2 * kT * WP : Wsep[W_IN_C ? 0 : wid];
+        uint16_t *Wl = Wh + kT * WP;
+        weighted_x<XP>(X_, p0, sc.w, Wh, Wl, lane);
 
         // D4: yacc[tt] += M X, X fragments read transposed from the x tile
         {
@@ -492,28 +554,43 @@ ssd_scan_kernel(SsdKp p) {
             }
         }
 
-        // skip term and store: lane (column c16, rows t = tt*16 + q*4 + i)
+        // skip term and store: lane (column c16, rows t = tt*16 + q*4 + i); the
+        // row base is uniform, the lane adds a 32-bit byte offset
+        float yv[2][4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const uint2 xv = tr_read(X_, XP, tt * 16 + q * 4, p0, lane);
             const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
-            float *yr = Yg + (t0 + tt * 16 + q * 4) * rowX + c16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (t0 + tt * 16 + q * 4 + i < te) yr[i * rowX] = fmaf(Dh, xs[i], yacc[tt][i]);
-            }
+            for (int i = 0; i < 4; ++i) yv[tt][i] = fmaf(Dh, xs[i], yacc[tt][i]);
+        }
+        if (t0 + kT <= te) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + i) * rowX) + ylane) =
+                        yv[tt][i];
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t0 + tt * 16 + q * 4 + i < te)
+                        *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + i) * rowX) + ylane) =
+                            yv[tt][i];
         }
 
         // D2+D3
-        state_update<NT, BCP>(S, B_, Wh[wid], Wl[wid], sc.end, N, lane);
+        state_update<NT, BCP>(S, B_, Wh, Wl, sc.end, N, lane);
 
         // stage chunk j+1, start loading chunk j+2
         if (j + 1 < nchunks) {
-            st.store(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1]);
-            if (wid == 0)
-                chunk_scalars(scal[buf ^ 1], st.rdt, t0 + kT + (lane & 31) < p.L && lane < kT, bias, A,
+            st.template store<0>(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1]);
+            if (wid == NW - 1)   // the wave with the least decay-mask work
+                chunk_scalars(scal[buf ^ 1], st.rdt[0], t0 + kT + (lane & 31) < p.L && lane < kT, bias, A,
                               p.mode, lane);
-            if (j + 2 < nchunks) st.load(t0 + 2 * kT);
+            if (j + 2 < nchunks) st.template load<0>(t0 + 2 * kT);
         }
         __syncthreads();
     }
