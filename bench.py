@@ -24,6 +24,17 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (no sparsity), TFLOP/s
 FP32_VALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, non-packed fp32
+# fp32 VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz lane-slots/s (a wave64 op takes 4 cycles)
+VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+# one ZOH state update (b, t, d, n) of S6: x = dl*A, Abar = exp2(x), beta = fma, B*u, beta*(B u),
+# h = fma, y += C*h: 6 single-rate fp32 ops + v_exp_f32 at half rate = 8 slots, 9 flops
+S6_SLOTS_PER_UPDATE = 8
+S6_FLOPS_PER_UPDATE = 9
+S6_ALU_PEAK_TFLOPS = VALU_SLOTS_PER_S / S6_SLOTS_PER_UPDATE * S6_FLOPS_PER_UPDATE / 1e12
+# HBM bytes per launch of s6_scan_kernel on s6_mamba1, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch) scaled by a 1 GiB device copy (fetch x 2.0, write x 1.0);
+# valid only for the kernel source with this sha1
+S6_TRAFFIC = {"src_sha1": "20e7683cc01827a37f589679373fbf43546fb491", "bytes": (100207 * 2.0 + 99077.2 * 1.0) * 1024}
 N_ROTATE = 3                     # input copies rotated between steps (> Infinity Cache)
 
 
@@ -37,7 +48,7 @@ def s6_model(d):
     elems = B * L * D
     isz = 4
     bytes_ = elems * (isz + 4 + 4) + 2 * B * L * N * isz + D * N * 4 + 2 * D * 4 + B * D * N * 4
-    ops = elems * N * 10           # per (b,t,d,n): 9 flops + 1 exp
+    ops = elems * N * S6_FLOPS_PER_UPDATE   # per (b,t,d,n) state update
     return elems, bytes_, ops
 
 
@@ -172,6 +183,16 @@ def cpu_baseline_units(name, n_units):
                       f"({elems} elements, {sec:.2f} s wall)"}
 
 
+def s6_traffic(name):
+    """Counter-measured HBM bytes per launch, or None if the kernel changed since."""
+    import hashlib
+    src = os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", "s6_scan.hip")
+    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
+    if name != "s6_mamba1" or sha != S6_TRAFFIC["src_sha1"]:
+        return None
+    return round(S6_TRAFFIC["bytes"])
+
+
 def measure(name, dev, steps, warmup):
     step, dims, w, kernels = make_runner(name, dev)
     wall, per = time_steps(step, steps, warmup)
@@ -214,10 +235,13 @@ def main():
     ev_s = m["event_ms_median"] * 1e-3
     gbs = m["bytes"] / ev_s / 1e9
     if kind == "s6":
-        roof = {"bound": "alu", "achieved": round(m["ops"] / ev_s / 1e12, 3),
-                "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(m["ops"] / ev_s / 1e12 / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+        tf = m["ops"] / ev_s / 1e12
+        roof = {"bound": "alu", "achieved": round(tf, 3), "peak": round(S6_ALU_PEAK_TFLOPS, 2),
+                "unit": "TFLOP/s", "frac": round(tf / S6_ALU_PEAK_TFLOPS, 4),
+                "traffic": s6_traffic(args.workload),
+                "peak_basis": "fp32 VALU issue 39.3 T lane-slots/s; 8 slots and 9 flops per state update",
                 "kernel": "s6_scan_kernel", "kernel_ms": round(m["event_ms_median"], 5),
+                "fma_peak": FP32_VALU_PEAK_TFLOPS, "fma_frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
                 "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
