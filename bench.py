@@ -122,7 +122,7 @@ def make_runner(name, dev):
         t = copies[i % N_ROTATE]
         lib.ssd_cplx_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
                                     None, chunk_len=w["chunk_len"], y=y, h_final=hf, workspace=ws)
-    return step, dims, w, ["cssd_chunk_state_kernel", "cssd_state_pass_kernel", "cssd_chunk_scan_kernel"]
+    return step, dims, w, ["cssd_state_kernel", "cssd_pass_kernel", "cssd_scan_kernel"]
 
 
 def time_steps(step, steps, warmup):

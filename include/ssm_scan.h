@@ -161,8 +161,13 @@ int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, con
  * interleaved (re, im); y (batch, L, nheads, headdim);
  * h0, h_final (batch, nheads, headdim, n_complex, 2).
  * Limits: nheads % ngroups == 0; headdim in {32, 64, 128}; n_complex a
- * multiple of 8, <= 128; chunk_len in {32, 64, 128}.
- * Workspace: ssd_cplx_chunk_scan_fwd_workspace_size() bytes. */
+ * multiple of 8, <= 64; chunk_len in {32, 64, 128} (checked; the kernels use
+ * their own 32-step chunks, and the result does not depend on it beyond
+ * rounding).  Contractions run in fp32 on the matrix cores.
+ * Workspace: ssd_cplx_chunk_scan_fwd_workspace_size() bytes, 16-byte aligned,
+ * owned by the caller (one complex headdim x n_complex state and one complex
+ * decay per (batch, head, segment) when the sequence is cut into segments;
+ * 0 when it is one segment, and workspace may then be NULL). */
 size_t ssd_cplx_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads,
                                               int64_t headdim, int64_t n_complex, int64_t ngroups,
                                               int64_t chunk_len);

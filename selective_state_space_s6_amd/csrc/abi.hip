@@ -176,8 +176,8 @@ int ssd_cplx_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bia
         return fail(SSM_ERR_INVALID_ARG, "%s: SSM_CPLX_CODE fixes its own input scale; use SSM_BBAR_ZOH", E);
     if (!(headdim == 32 || headdim == 64 || headdim == 128))
         return fail(SSM_ERR_UNSUPPORTED, "%s: headdim %lld not in {32, 64, 128}", E, (long long)headdim);
-    if (n_complex % 8 != 0 || n_complex > 128)
-        return fail(SSM_ERR_UNSUPPORTED, "%s: n_complex %lld must be a multiple of 8 and <= 128", E,
+    if (n_complex % 8 != 0 || n_complex > 64)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: n_complex %lld must be a multiple of 8 and <= 64", E,
                     (long long)n_complex);
     if (!(chunk_len == 32 || chunk_len == 64 || chunk_len == 128))
         return fail(SSM_ERR_UNSUPPORTED, "%s: chunk_len %lld not in {32, 64, 128}", E, (long long)chunk_len);

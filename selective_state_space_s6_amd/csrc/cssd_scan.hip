@@ -1,37 +1,49 @@
-// cssd_scan.hip -- complex-state SSD (Mamba-3 SISO style) chunked forward scan.
+// cssd_scan.hip -- complex-state SSD (Mamba-3 SISO style) forward scan, gfx950.
 //
 // Follows builderforce-memory-engine complex_ssd.ts (header comment,
 // et_bbar_re/et_bbar_im, complex_ssd_forward): a complex diagonal state per
 // (head channel p, complex state n), complex decay Abar_t = exp(delta_t*mu),
 // complex input scale beta_t, output Re(C.h) + D x.  With a head-constant mu the
-// decay from step s to step t is exp(mu * (Lambda_t - Lambda_s)), Lambda the
-// running sum of delta, so the same chunked decomposition as the real SSD
-// applies:
-//   K1  Shat_c[p,n] = sum_s exp(mu(Lambda_end - Lambda_s)) beta_s B_s[n] x_s[p]
-//   K2  S_{c+1} = exp(mu Lambda_end(c)) S_c + Shat_c,  h_final = S_nc
-//   K3  y_t[p] = sum_{s<=t} Re(G[t,s] exp(mu(Lambda_t-Lambda_s)) beta_s) x_s[p]
-//              + Re(sum_n C_t[n] exp(mu Lambda_t) S_c[p,n]) + D x_t[p],
-//       G[t,s] = sum_n C_t[n] B_s[n]
-// Every decay factor is taken between two steps of one chunk (or from the chunk
-// start), so for the stable reading of A no exponent is positive.
-// Arithmetic is fp32 on the vector ALUs.
+// decay from step s to step t is exp(mu (Lam_t - Lam_s)), Lam the running sum
+// of delta, so the chunked decomposition of the real SSD applies with complex
+// scalars.  Inside a 32-step chunk, with Lam counted from the chunk start and
+// S the state entering the chunk:
+//   y_t[p]  = Re(sum_n C_t[n] e^{mu Lam_t} S[p,n])                       (D5)
+//           + sum_{s<=t} Re(G[t,s] e^{mu(Lam_t-Lam_s)} beta_s) x_s[p]   (D4)
+//           + D x_t[p],   G[t,s] = sum_n C_t[n] B_s[n]
+//   S'[p,n] = e^{mu Lam_end} S[p,n] + sum_s e^{mu(Lam_end-Lam_s)} beta_s B_s[n] x_s[p]   (D2, D3)
+// Every decay is taken between two steps of one chunk (or from its start), so
+// for the stable reading of A no exponent is positive.
+//
+// Layout of the work: as for the real SSD, the sequence of every (batch, head)
+// is cut into segments (cssd_state_kernel: segment-local states and decays;
+// cssd_pass_kernel: entering states; cssd_scan_kernel: outputs), and a work
+// group holds one head with one wave per 16 head channels.  The complex state
+// is stored as real pairs, k = 2n + (0 re, 1 im), and a wave keeps its
+// 2Nc x 16 slice in fp32 MFMA accumulators (v_mfma_f32_16x16x4_f32).  Every
+// contraction is a real fp32 GEMM on the matrix cores: complex products become
+// sums over k of real products whose signs and re/im pairing are folded into
+// the operands as they are read from LDS.  The 1e-4 tolerance of fp32 inputs
+// rules out bf16 operands.  Running sums of delta are formed in double, so a
+// rotation angle phi (Lam_t - Lam_s) carries only the rounding of its fp32
+// difference.
 #include "device_common.hpp"
 #include "launchers.hpp"
+#include <algorithm>
+#include <type_traits>
 
 namespace ssm {
 namespace {
 
-constexpr int kThreads = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-struct CssdKp {
-    const float *x; const float *dt; const float *dt_bias; const float *A_log;
-    const float *B; const float *C; const float *D; float *y;
-    const float *h0; float *h_final;
-    float *states;      // [batch][nc][H][P][Nc][2]
-    float *cdec;        // [batch][H][nc][2]   exp(mu * Lambda_end) per chunk
-    int64_t batch, L, H, P, Nc, G, nc;
-    uint32_t flags;
-};
+constexpr int kT = 32;              // steps per chunk
+constexpr int kTargetWaves = 3072;  // enough resident waves to hide latency
+constexpr int kMinSeg = 256;        // shortest segment worth a state round trip
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 struct cf { float re, im; };
 __device__ __forceinline__ cf cmul(cf a, cf b) { return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; }
@@ -53,6 +65,17 @@ __device__ __forceinline__ cf cdiv(cf a, cf b) {
     return {(a.re * b.re + a.im * b.im) / den, (a.im * b.re - a.re * b.im) / den};
 }
 
+struct CssdKp {
+    const float *x; const float *dt; const float *dt_bias; const float *A_log;
+    const float *B; const float *C; const float *D; float *y;
+    const float *h0; float *h_final;
+    float *ws_state;    // (batch, H, nseg, P, 2 Nc): local, then entering, segment states
+    float *ws_decay;    // (batch, H, nseg, 2): complex decay over a segment
+    int64_t batch, L, H, P, Nc, G;
+    int64_t Ls, nseg;   // segment length (a multiple of kT) and count
+    uint32_t flags;
+};
+
 // mu (the per-unit-delta complex rate) of head h for the selected reading
 __device__ __forceinline__ cf head_mu(const CssdKp &p, int64_t h) {
     const float ell = p.A_log[2 * h], phi = p.A_log[2 * h + 1];
@@ -62,7 +85,7 @@ __device__ __forceinline__ cf head_mu(const CssdKp &p, int64_t h) {
     return {-expf(ell), phi};
 }
 
-__device__ __forceinline__ cf input_scale(const CssdKp &p, int64_t h, cf mu, float dl) {
+__device__ __forceinline__ cf input_scale(const CssdKp &p, cf mu, float dl) {
     const uint32_t am = p.flags & 0xCu, bm = p.flags & 0x3u;
     if (am == 0x8u) {   // literal page kernel: (exp(delta*mu) - 1) * exp(-l - i*phi)
         const cf e1 = cexpm1f_(dl * mu.re, dl * mu.im);
@@ -74,208 +97,559 @@ __device__ __forceinline__ cf input_scale(const CssdKp &p, int64_t h, cf mu, flo
     return cdiv(cexpm1f_(dl * mu.re, dl * mu.im), mu);   // (exp(delta*lambda) - 1)/lambda
 }
 
-// per-chunk scalars: Lam[t] = inclusive running sum of delta (0 past L),
-// bet[t] = beta_t (0 past L).  The rotation angle phi*(Lam_t - Lam_s) turns an
-// absolute error of Lam into a relative error of the output, so delta and its
-// running sum are formed in double precision (Q values per chunk); every
-// difference of two Lam is taken in double and only then rounded to fp32.
-template <int Q>
-__device__ __forceinline__ void chunk_scalars(const CssdKp &p, int64_t b, int64_t c, int64_t h, cf mu,
-                                              double *Lam, float *bre, float *bim, double *wsum) {
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const double bias = p.dt_bias ? (double)p.dt_bias[h] : 0.0;
+// per-chunk scalars of one head, in LDS
+struct CScal {
+    double lam[kT];   // running sum of delta from the chunk start (inclusive)
+    float2 bet[kT];   // beta_t
+    float2 et[kT];    // e^{mu lam_t}
+    float2 w[kT];     // e^{mu (lam_end - lam_s)} beta_s
+    float2 E;         // e^{mu lam_end}
+    double lend;      // lam_end
+};
+
+// Scalars of one chunk by one wave (lane = step within each 32-lane half; the
+// upper half repeats the lower).  Steps past L have delta = beta = 0.
+__device__ __forceinline__ void chunk_scalars(CScal &sc, const CssdKp &p, cf mu, double bias, float dtv,
+                                              bool valid, int lane) {
     double dl = 0.0;
     cf be{0.0f, 0.0f};
-    const int64_t t = c * Q + tid;
-    if (tid < Q && t < p.L) {
-        const double xv = (double)p.dt[(b * p.L + t) * p.H + h] + bias;
+    if (valid) {
+        const double xv = (double)dtv + bias;
         dl = xv > 0.0 ? xv + log1p(exp(-xv)) : log1p(exp(xv));   // softplus
-        be = input_scale(p, h, mu, (float)dl);
+        be = input_scale(p, mu, (float)dl);
     }
     double v = dl;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
+    for (int off = 1; off < 32; off <<= 1) {
+        const double o = __shfl_up(v, off, 32);
+        if ((lane & 31) >= off) v += o;
     }
-    if (lane == 63) wsum[wid] = v;
-    __syncthreads();
-    double pre = 0.0;
-    for (int w = 0; w < wid; ++w) pre += wsum[w];
-    if (tid < Q) { Lam[tid] = v + pre; bre[tid] = be.re; bim[tid] = be.im; }
-    __syncthreads();
+    const double lend = __shfl(v, 31, 32);
+    if (lane < kT) {
+        const float lt = (float)v, lr = (float)(lend - v);
+        const cf e = cexpf_(mu.re * lt, mu.im * lt);
+        const cf w = cmul(cexpf_(mu.re * lr, mu.im * lr), be);
+        sc.lam[lane] = v;
+        sc.bet[lane] = make_float2(be.re, be.im);
+        sc.et[lane] = make_float2(e.re, e.im);
+        sc.w[lane] = make_float2(w.re, w.im);
+    }
+    if (lane == 0) {
+        const float le = (float)lend;
+        const cf E = cexpf_(mu.re * le, mu.im * le);
+        sc.E = make_float2(E.re, E.im);
+        sc.lend = lend;
+    }
 }
 
-template <int Q>
-__global__ void __launch_bounds__(kThreads)
-cssd_chunk_state_kernel(CssdKp p) {
-    __shared__ double Lam[Q], wsum[4];
-    __shared__ float bre[Q], bim[Q], wre[Q], wim[Q];
-    const int64_t work = xcd_swizzle(blockIdx.x, p.batch * p.nc * p.H);
-    const int64_t h = work % p.H, c = (work / p.H) % p.nc, b = work / (p.H * p.nc);
-    const int64_t g = h * p.G / p.H;
-    const int tid = threadIdx.x;
-    const cf mu = head_mu(p, h);
-    chunk_scalars<Q>(p, b, c, h, mu, Lam, bre, bim, wsum);
-    const double Lend = Lam[Q - 1];
-    if (tid < Q) {   // w_s = exp(mu (Lambda_end - Lambda_s)) beta_s
-        const float dlam = (float)(Lend - Lam[tid]);
-        const cf e = cexpf_(mu.re * dlam, mu.im * dlam);
-        const cf w = cmul(e, cf{bre[tid], bim[tid]});
-        wre[tid] = w.re; wim[tid] = w.im;
+// Register and LDS staging of one chunk of x, B (and C), dt for a work group of
+// NW waves holding head (b, h).  Rows are fp32; tiles have a padded pitch of
+// KC + 4 (B, C) and P + 4 (x) floats.  Loads are unconditional so they stay in
+// flight across a chunk; a chunk that crosses L clamps its step index into the
+// tensors (rows past L never contribute: their delta and beta are 0 and their
+// outputs are not stored).
+template <int KC, int NW, bool WITH_C>
+struct Stager {
+    static constexpr int NTHR = 64 * NW;
+    static constexpr int P = 16 * NW;
+    static constexpr int CP = KC + 4;
+    static constexpr int XP = P + 4;
+    static constexpr int LDN = KC / 4;                          // 16-byte pieces per B/C row
+    static constexpr int NBC = kT * LDN;                        // pieces per B (C) tile
+    static constexpr int PBC = (NBC + NTHR - 1) / NTHR;
+    static constexpr int XPR = P / 4;
+    static constexpr int NX = kT * XPR;
+    static constexpr int PX = NX / NTHR;
+    static_assert(NX % NTHR == 0, "x pieces must divide over the group");
+
+    float4 rB[PBC], rC[PBC], rX[PX];
+    float rdt;
+    const float *Bb, *Cb, *Xb, *Db;
+    uint32_t oBC[PBC], oX[PX];   // per-piece offsets (floats) at chunk row 0
+    int rBC[PBC], rXr[PX];       // per-piece rows
+    int lBC[PBC], lX[PX];        // per-piece LDS offsets
+    bool vBC[PBC];
+    int sD;
+    int64_t rowBC, rowX, H, L;
+
+    __device__ __forceinline__ void init(const CssdKp &p, int64_t b, int64_t h, int64_t g, int tid) {
+        rowBC = p.G * p.Nc * 2;
+        rowX = p.H * p.P;
+        H = p.H;
+        L = p.L;
+        const int K = (int)(2 * p.Nc);
+#pragma unroll
+        for (int i = 0; i < PBC; ++i) {
+            const int pc = tid + NTHR * i;
+            vBC[i] = pc < NBC;
+            const int pcc = min(pc, NBC - 1);
+            const int r = pcc / LDN, c = (pcc % LDN) * 4;
+            rBC[i] = r;
+            oBC[i] = (uint32_t)(r * rowBC + min(c, K - 4));
+            lBC[i] = r * CP + c;
+        }
+#pragma unroll
+        for (int i = 0; i < PX; ++i) {
+            const int pc = tid + NTHR * i;
+            const int r = pc / XPR, c = (pc % XPR) * 4;
+            rXr[i] = r;
+            oX[i] = (uint32_t)(r * rowX + c);
+            lX[i] = r * XP + c;
+        }
+        sD = tid & 31;
+        Bb = p.B + (b * p.L * p.G + g) * p.Nc * 2;
+        Cb = p.C + (b * p.L * p.G + g) * p.Nc * 2;
+        Xb = p.x + (b * p.L * p.H + h) * p.P;
+        Db = p.dt + b * p.L * p.H + h;
+    }
+    __device__ __forceinline__ void load(int64_t t0) {
+        const float *Bu = Bb + t0 * rowBC, *Cu = Cb + t0 * rowBC, *Xu = Xb + t0 * rowX;
+        const float *Du = Db + t0 * H;
+        if (t0 + kT <= L) {
+#pragma unroll
+            for (int i = 0; i < PBC; ++i) {
+                rB[i] = *reinterpret_cast<const float4 *>(Bu + oBC[i]);
+                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const float4 *>(Cu + oBC[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < PX; ++i) rX[i] = *reinterpret_cast<const float4 *>(Xu + oX[i]);
+            rdt = Du[(uint32_t)(sD * H)];
+        } else {
+            const int last = (int)(L - 1 - t0);   // last valid step of the chunk
+#pragma unroll
+            for (int i = 0; i < PBC; ++i) {
+                const uint32_t o = oBC[i] - (uint32_t)((rBC[i] - min(rBC[i], last)) * rowBC);
+                rB[i] = *reinterpret_cast<const float4 *>(Bu + o);
+                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const float4 *>(Cu + o);
+            }
+#pragma unroll
+            for (int i = 0; i < PX; ++i) {
+                const uint32_t o = oX[i] - (uint32_t)((rXr[i] - min(rXr[i], last)) * rowX);
+                rX[i] = *reinterpret_cast<const float4 *>(Xu + o);
+            }
+            rdt = Du[(uint32_t)(min(sD, last) * H)];
+        }
+    }
+    __device__ __forceinline__ void store(float *Bs, float *Cs, float *Xs) {
+#pragma unroll
+        for (int i = 0; i < PBC; ++i) {
+            if (PBC * NTHR == NBC || vBC[i]) {
+                *reinterpret_cast<float4 *>(&Bs[lBC[i]]) = rB[i];
+                if constexpr (WITH_C) *reinterpret_cast<float4 *>(&Cs[lBC[i]]) = rC[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PX; ++i) *reinterpret_cast<float4 *>(&Xs[lX[i]]) = rX[i];
+    }
+};
+
+// S <- E S (complex, the (re, im) pairs of a state tile sit in registers (0,1)
+// and (2,3) of one lane)
+template <int NTK>
+__device__ __forceinline__ void decay_state(f32x4 (&S)[NTK], float2 E, int K) {
+#pragma unroll
+    for (int kt = 0; kt < NTK; ++kt) {
+        if (kt * 16 >= K) break;
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+            const float re = S[kt][j], im = S[kt][j + 1];
+            S[kt][j] = E.x * re - E.y * im;
+            S[kt][j + 1] = E.x * im + E.y * re;
+        }
+    }
+}
+
+// D2: S[k][p] += sum_s (w B)_r[s][k] x[s][p] for one wave's 16 channels.  The A
+// operand (row k = kt*16 + lane%16, K slot s = sb*16 + 4*(lane/16) + m) is the
+// real or imaginary part of w_s B_s[n], n = k/2, formed as it is read.
+template <int NTK, int CP, int XP>
+__device__ __forceinline__ void state_add(f32x4 (&S)[NTK], const float *Bs, const float *Xs, const CScal &sc,
+                                          int p0, int K, int lane) {
+    const int c16 = lane & 15, q = lane >> 4;
+    const bool odd = c16 & 1;
+    // the chunk's contribution is summed on its own and added once, so its
+    // roundings are relative to it and not to the (larger) state
+    f32x4 dS[NTK];
+#pragma unroll
+    for (int kt = 0; kt < NTK; ++kt) dS[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int s = sb * 16 + 4 * q + m;
+            const float2 w = sc.w[s];
+            // even k: Re(w b) = w.re b.re - w.im b.im ; odd k: Im(w b) = w.im b.re + w.re b.im
+            const float al = odd ? w.y : w.x, be = odd ? w.x : -w.y;
+            const float xv = Xs[s * XP + p0 + c16];
+#pragma unroll
+            for (int kt = 0; kt < NTK; ++kt) {
+                if (kt * 16 >= K) break;
+                const float2 b = *reinterpret_cast<const float2 *>(&Bs[s * CP + kt * 16 + (c16 & ~1)]);
+                dS[kt] = mfma4(fmaf(al, b.x, be * b.y), xv, dS[kt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int kt = 0; kt < NTK; ++kt) {
+        if (kt * 16 >= K) break;
+        S[kt] += dS[kt];
+    }
+}
+
+// work index -> (b, segment, h); heads of one (batch, segment) are consecutive
+struct Work {
+    int64_t b, k, h;
+    __device__ __forceinline__ Work(int64_t work, int64_t H, int64_t nseg)
+        : b(work / (H * nseg)), k((work / H) % nseg), h(work % H) {}
+};
+
+// e^{mu lam} for a long running sum lam (double): the phase is reduced in double
+__device__ __forceinline__ float2 cexp_long(cf mu, double lam) {
+    double ph = (double)mu.im * lam;
+    ph -= 6.283185307179586 * rint(ph * 0.15915494309189535);
+    const cf e = cexpf_((float)((double)mu.re * lam), (float)ph);
+    return make_float2(e.re, e.im);
+}
+
+// ---- segment-local final states (zero start) and the segment decay; every
+// segment but the last, all of whose chunks are whole
+template <int KC, bool EXACT, int NW>
+__global__ void __launch_bounds__(64 * NW)
+cssd_state_kernel(CssdKp p) {
+    using St = Stager<KC, NW, false>;
+    constexpr int NTK = KC / 16;
+    constexpr int CP = St::CP, XP = St::XP;
+    __shared__ __attribute__((aligned(16))) float Bs[2][kT * CP];
+    __shared__ __attribute__((aligned(16))) float Xs[2][kT * XP];
+    __shared__ CScal scal[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15, q = lane >> 4;
+    const int64_t nseg1 = p.nseg - 1;
+    const Work wk(xcd_swizzle(blockIdx.x, p.batch * nseg1 * p.H), p.H, nseg1);
+    const int64_t g = wk.h * p.G / p.H;
+    const int p0 = wid * 16;
+    const int K = EXACT ? KC : (int)(2 * p.Nc);
+    const cf mu = head_mu(p, wk.h);
+    const double bias = p.dt_bias ? (double)p.dt_bias[wk.h] : 0.0;
+
+    f32x4 S[NTK];
+#pragma unroll
+    for (int kt = 0; kt < NTK; ++kt) S[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    St st;
+    st.init(p, wk.b, wk.h, g, tid);
+    const int64_t tb = wk.k * p.Ls;
+    const int64_t nchunks = p.Ls / kT;
+    st.load(tb);
+    st.store(Bs[0], nullptr, Xs[0]);
+    if (wid == 0) chunk_scalars(scal[0], p, mu, bias, st.rdt, true, lane);
+    if (nchunks > 1) st.load(tb + kT);
+    __syncthreads();
+
+    double lseg = 0.0;
+    for (int64_t j = 0; j < nchunks; ++j) {
+        const int buf = (int)(j & 1);
+        const CScal &sc = scal[buf];
+        lseg += sc.lend;
+        decay_state<NTK>(S, sc.E, K);
+        state_add<NTK, CP, XP>(S, Bs[buf], Xs[buf], sc, p0, K, lane);
+        if (j + 1 < nchunks) {
+            st.store(Bs[buf ^ 1], nullptr, Xs[buf ^ 1]);
+            if (wid == 0) chunk_scalars(scal[buf ^ 1], p, mu, bias, st.rdt, true, lane);
+            if (j + 2 < nchunks) st.load(tb + (j + 2) * kT);
+        }
+        __syncthreads();
+    }
+
+    const int64_t slot = (wk.b * p.H + wk.h) * p.nseg + wk.k;
+#pragma unroll
+    for (int kt = 0; kt < NTK; ++kt) {
+        if (kt * 16 >= K) break;
+        float *dst = p.ws_state + (slot * p.P + p0 + c16) * (2 * p.Nc) + kt * 16 + q * 4;
+        *reinterpret_cast<float4 *>(dst) = make_float4(S[kt][0], S[kt][1], S[kt][2], S[kt][3]);
     }
     if (tid == 0) {
-        const cf e = cexpf_(mu.re * (float)Lend, mu.im * (float)Lend);
-        p.cdec[((b * p.H + h) * p.nc + c) * 2] = e.re;
-        p.cdec[((b * p.H + h) * p.nc + c) * 2 + 1] = e.im;
-    }
-    __syncthreads();
-    const int64_t smax = min((int64_t)Q, p.L - c * Q);
-    for (int64_t e = tid; e < p.P * p.Nc; e += kThreads) {
-        const int64_t pp = e / p.Nc, n = e % p.Nc;
-        // four interleaved partial sums: shorter fp32 rounding chains
-        float are[4] = {0.0f, 0.0f, 0.0f, 0.0f}, aim[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int64_t s = 0; s < smax; ++s) {
-            const int64_t t = c * Q + s;
-            const float xv = p.x[((b * p.L + t) * p.H + h) * p.P + pp];
-            const float *Bs = p.B + (((b * p.L + t) * p.G + g) * p.Nc + n) * 2;
-            const cf wb = cmul(cf{wre[s], wim[s]}, cf{Bs[0], Bs[1]});
-            are[s & 3] = fmaf(wb.re, xv, are[s & 3]);
-            aim[s & 3] = fmaf(wb.im, xv, aim[s & 3]);
-        }
-        float *dst = p.states + ((((b * p.nc + c) * p.H + h) * p.P + pp) * p.Nc + n) * 2;
-        dst[0] = (are[0] + are[1]) + (are[2] + are[3]);
-        dst[1] = (aim[0] + aim[1]) + (aim[2] + aim[3]);
+        const float2 d = cexp_long(mu, lseg);
+        p.ws_decay[2 * slot] = d.x;
+        p.ws_decay[2 * slot + 1] = d.y;
     }
 }
 
-__global__ void __launch_bounds__(kThreads)
-cssd_state_pass_kernel(CssdKp p) {
-    const int64_t PN = p.P * p.Nc;
-    const int64_t per_bh = (PN + kThreads - 1) / kThreads;
-    const int64_t bh = blockIdx.x / per_bh;
-    const int64_t e = (blockIdx.x % per_bh) * kThreads + threadIdx.x;
-    if (e >= PN) return;
-    const int64_t b = bh / p.H, h = bh % p.H;
-    cf S{0.0f, 0.0f};
-    if (p.h0) { S.re = p.h0[(bh * PN + e) * 2]; S.im = p.h0[(bh * PN + e) * 2 + 1]; }
-    for (int64_t c = 0; c < p.nc; ++c) {
-        float *st = p.states + (((b * p.nc + c) * p.H + h) * PN + e) * 2;
-        const cf loc{st[0], st[1]};
-        st[0] = S.re; st[1] = S.im;
-        const float *d = p.cdec + ((b * p.H + h) * p.nc + c) * 2;
-        const cf dec{d[0], d[1]};
-        const cf n = cmul(dec, S);
-        S = {n.re + loc.re, n.im + loc.im};
+// ---- D3 across segments: the state entering each segment, in place of the
+// segment-local states.  One thread per 2 complex (p, n) of one (b, h).
+__global__ void __launch_bounds__(256)
+cssd_pass_kernel(CssdKp p) {
+    const int64_t per = p.P * p.Nc / 2;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= p.batch * p.H * per) return;
+    const int64_t bh = i / per, e = i % per;
+    float4 S = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (p.h0) S = reinterpret_cast<const float4 *>(p.h0)[bh * per + e];
+    float4 *ws = reinterpret_cast<float4 *>(p.ws_state) + bh * p.nseg * per + e;
+    for (int64_t k = 0; k + 1 < p.nseg; ++k) {
+        const float4 loc = ws[k * per];
+        const float dr = p.ws_decay[2 * (bh * p.nseg + k)], di = p.ws_decay[2 * (bh * p.nseg + k) + 1];
+        ws[k * per] = S;
+        S = make_float4(dr * S.x - di * S.y + loc.x, dr * S.y + di * S.x + loc.y,
+                        dr * S.z - di * S.w + loc.z, dr * S.w + di * S.z + loc.w);
     }
-    if (p.h_final) { p.h_final[(bh * PN + e) * 2] = S.re; p.h_final[(bh * PN + e) * 2 + 1] = S.im; }
+    ws[(p.nseg - 1) * per] = S;
 }
 
-template <int Q>
-__global__ void __launch_bounds__(kThreads)
-cssd_chunk_scan_kernel(CssdKp p) {
-    __shared__ double Lam[Q], wsum[4];
-    __shared__ float bre[Q], bim[Q], e0re[Q], e0im[Q];
-    __shared__ float M[Q][Q + 1];
-    const int64_t work = xcd_swizzle(blockIdx.x, p.batch * p.nc * p.H);
-    const int64_t h = work % p.H, c = (work / p.H) % p.nc, b = work / (p.H * p.nc);
-    const int64_t g = h * p.G / p.H;
-    const int tid = threadIdx.x;
-    const cf mu = head_mu(p, h);
+// ---- outputs of one segment from the state entering it
+template <int KC, bool EXACT, int NW>
+__global__ void __launch_bounds__(64 * NW)
+cssd_scan_kernel(CssdKp p) {
+    using St = Stager<KC, NW, true>;
+    constexpr int NTK = KC / 16;
+    constexpr int CP = St::CP, XP = St::XP;
+    __shared__ __attribute__((aligned(16))) float Bs[2][kT * CP];
+    __shared__ __attribute__((aligned(16))) float Cs[2][kT * CP];
+    __shared__ __attribute__((aligned(16))) float Xs[2][kT * XP];
+    // the chunk's causal tiles of M[t][s] = Re(G[t,s] e^{mu(lam_t-lam_s)} beta_s) as
+    // the A fragments of M X: tile tau = (s-tile, t-tile) (0,0), (0,1), (1,1)
+    __shared__ __attribute__((aligned(16))) f32x4 Ms[3][64];
+    __shared__ CScal scal[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15, q = lane >> 4;
+    const Work wk(xcd_swizzle(blockIdx.x, p.batch * p.nseg * p.H), p.H, p.nseg);
+    const int64_t g = wk.h * p.G / p.H;
+    const int p0 = wid * 16;
+    const int K = EXACT ? KC : (int)(2 * p.Nc);
+    const cf mu = head_mu(p, wk.h);
+    const double bias = p.dt_bias ? (double)p.dt_bias[wk.h] : 0.0;
     const float csign = (p.flags & 0x10u) ? -1.0f : 1.0f;   // conj(C)
-    chunk_scalars<Q>(p, b, c, h, mu, Lam, bre, bim, wsum);
-    if (tid < Q) {
-        const float lt = (float)Lam[tid];
-        const cf e = cexpf_(mu.re * lt, mu.im * lt);
-        e0re[tid] = e.re; e0im[tid] = e.im;
-    }
-    const int64_t tmax = min((int64_t)Q, p.L - c * Q);
-    // M[t][s] = Re(G[t,s] exp(mu(Lambda_t - Lambda_s)) beta_s), s <= t
-    for (int e = tid; e < Q * Q; e += kThreads) {
-        const int t = e / Q, s = e % Q;
-        float m = 0.0f;
-        if (s <= t && t < tmax) {
-            const float *Ct = p.C + ((b * p.L + c * Q + t) * p.G + g) * p.Nc * 2;
-            const float *Bs = p.B + ((b * p.L + c * Q + s) * p.G + g) * p.Nc * 2;
-            float gre2[2] = {0.0f, 0.0f}, gim2[2] = {0.0f, 0.0f};
-            for (int64_t n = 0; n < p.Nc; ++n) {
-                const float cr = Ct[2 * n], ci = csign * Ct[2 * n + 1];
-                const float br = Bs[2 * n], bi = Bs[2 * n + 1];
-                gre2[n & 1] = fmaf(cr, br, fmaf(-ci, bi, gre2[n & 1]));
-                gim2[n & 1] = fmaf(cr, bi, fmaf(ci, br, gim2[n & 1]));
-            }
-            const float gre = gre2[0] + gre2[1], gim = gim2[0] + gim2[1];
-            const float dlam = (float)(Lam[t] - Lam[s]);
-            const cf ex = cexpf_(mu.re * dlam, mu.im * dlam);
-            const cf k = cmul(cmul(cf{gre, gim}, ex), cf{bre[s], bim[s]});
-            m = k.re;
+    const float Dh = p.D ? p.D[wk.h] : 0.0f;
+    const int64_t rowX = p.H * p.P;
+    float *Yg = p.y + (wk.b * p.L * p.H + wk.h) * p.P + p0;
+    const uint32_t ylane = (uint32_t)(q * 4 * rowX + c16) * 4u;   // byte offset of the lane's element
+
+    // state slice S_r[k][p], k = 2n + (re, im), p in this wave's 16 channels, in
+    // the MFMA output layout: tile kt, lane (column p = c16, rows k = kt*16 + q*4 + v)
+    const float *Sin = p.nseg > 1 ? p.ws_state + ((wk.b * p.H + wk.h) * p.nseg + wk.k) * p.P * 2 * p.Nc
+                                  : (p.h0 ? p.h0 + (wk.b * p.H + wk.h) * p.P * 2 * p.Nc : nullptr);
+    f32x4 S[NTK];
+#pragma unroll
+    for (int kt = 0; kt < NTK; ++kt) {
+        S[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (Sin && kt * 16 < K) {
+            const float4 v = *reinterpret_cast<const float4 *>(Sin + (p0 + c16) * 2 * p.Nc + kt * 16 + q * 4);
+            S[kt] = f32x4{v.x, v.y, v.z, v.w};
         }
-        M[t][s] = m;
     }
+
+    St st;
+    st.init(p, wk.b, wk.h, g, tid);
+    const int64_t tb = wk.k * p.Ls;
+    const int64_t te = min(tb + p.Ls, p.L);
+    const int64_t nchunks = (te - tb + kT - 1) / kT;
+    st.load(tb);
+    st.store(Bs[0], Cs[0], Xs[0]);
+    if (wid == NW - 1) chunk_scalars(scal[0], p, mu, bias, st.rdt, tb + (lane & 31) < p.L, lane);
+    if (nchunks > 1) st.load(tb + kT);
     __syncthreads();
-    const float Dh = p.D ? p.D[h] : 0.0f;
-    const bool has_state = (c > 0) || (p.h0 != nullptr);
-    const float *Sb = p.states + ((b * p.nc + c) * p.H + h) * p.P * p.Nc * 2;
-    for (int64_t e = tid; e < tmax * p.P; e += kThreads) {
-        const int64_t t = e / p.P, pp = e % p.P;
-        float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int64_t s = 0; s <= t; ++s)
-            a4[s & 3] = fmaf(M[t][s], p.x[((b * p.L + c * Q + s) * p.H + h) * p.P + pp], a4[s & 3]);
-        float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-        if (has_state) {
-            const float *Ct = p.C + ((b * p.L + c * Q + t) * p.G + g) * p.Nc * 2;
-            const float *Sp = Sb + pp * p.Nc * 2;
-            const cf e0{e0re[t], e0im[t]};
-            float s2[2] = {0.0f, 0.0f};
-            for (int64_t n = 0; n < p.Nc; ++n) {
-                const cf cc = cmul(cf{Ct[2 * n], csign * Ct[2 * n + 1]}, e0);
-                s2[n & 1] = fmaf(cc.re, Sp[2 * n], fmaf(-cc.im, Sp[2 * n + 1], s2[n & 1]));
+
+    for (int64_t j = 0; j < nchunks; ++j) {
+        const int buf = (int)(j & 1);
+        const int64_t t0 = tb + j * kT;
+        const float *B_ = Bs[buf], *C_ = Cs[buf], *X_ = Xs[buf];
+        const CScal &sc = scal[buf];
+
+        // D4, shared: G^T[s][t] (re and im) for the causal tile pairs, one per
+        // wave (wave tau % NW).  Lane holds column t = tT*16 + c16, rows
+        // s = sT*16 + q*4 + v.  K slot (q, m) of block kb is k = kb*16 + 4q + m.
+        //   Re G = sum_n B_re C_re - B_im C_im,  Im G = sum_n B_re C_im + B_im C_re
+        // (C_im -> -C_im for conj(C)).
+#pragma unroll
+        for (int tau = 0; tau < 3; ++tau) {
+            if (tau % NW != wid) continue;
+            const int sT = tau == 2 ? 1 : 0, tT = tau == 0 ? 0 : 1;
+            f32x4 Gr{0.0f, 0.0f, 0.0f, 0.0f}, Gi{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb < NTK; ++kb) {
+                if (kb * 16 >= K) break;
+                const float4 bq = *reinterpret_cast<const float4 *>(&B_[(sT * 16 + c16) * CP + kb * 16 + 4 * q]);
+                const float4 cq = *reinterpret_cast<const float4 *>(&C_[(tT * 16 + c16) * CP + kb * 16 + 4 * q]);
+                const float c1 = csign * cq.y, c3 = csign * cq.w;
+                Gr = mfma4(bq.x, cq.x, Gr);
+                Gr = mfma4(-bq.y, c1, Gr);
+                Gr = mfma4(bq.z, cq.z, Gr);
+                Gr = mfma4(-bq.w, c3, Gr);
+                Gi = mfma4(bq.y, cq.x, Gi);
+                Gi = mfma4(bq.x, c1, Gi);
+                Gi = mfma4(bq.w, cq.z, Gi);
+                Gi = mfma4(bq.z, c3, Gi);
             }
-            acc += s2[0] + s2[1];
+            const int t = tT * 16 + c16;
+            const double lt = sc.lam[t];
+            f32x4 mv;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int s = sT * 16 + 4 * q + v;
+                float m = 0.0f;
+                if (s <= t) {
+                    const float dl = (float)(lt - sc.lam[s]);
+                    const float2 bs = sc.bet[s];
+                    const cf f = cmul(cexpf_(mu.re * dl, mu.im * dl), cf{bs.x, bs.y});
+                    m = Gr[v] * f.re - Gi[v] * f.im;
+                }
+                mv[v] = m;
+            }
+            Ms[tau][lane] = mv;
         }
-        const float xv = p.x[((b * p.L + c * Q + t) * p.H + h) * p.P + pp];
-        p.y[((b * p.L + c * Q + t) * p.H + h) * p.P + pp] = fmaf(Dh, xv, acc);
+
+        // D5: ys[tt] = sum_k Chat[t][k] S_r[k][p], Chat = (Re, -Im) of C_t[n] e^{mu lam_t};
+        // two partial sums (even and odd state tiles) shorten the fp32 chains
+        f32x4 ys[2][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            ys[tt][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            ys[tt][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const float2 e = sc.et[tt * 16 + c16];
+#pragma unroll
+            for (int kt = 0; kt < NTK; ++kt) {
+                if (kt * 16 >= K) break;
+                const float4 cq = *reinterpret_cast<const float4 *>(&C_[(tt * 16 + c16) * CP + kt * 16 + 4 * q]);
+                const float ci0 = csign * cq.y, ci1 = csign * cq.w;
+                f32x4 &a = ys[tt][kt & 1];
+                a = mfma4(cq.x * e.x - ci0 * e.y, S[kt][0], a);
+                a = mfma4(-(cq.x * e.y + ci0 * e.x), S[kt][1], a);
+                a = mfma4(cq.z * e.x - ci1 * e.y, S[kt][2], a);
+                a = mfma4(-(cq.z * e.y + ci1 * e.x), S[kt][3], a);
+            }
+        }
+
+        __syncthreads();   // the shared M fragments are complete
+
+        // D4: acc[tt] = sum_{s-tile <= tt} M X
+        f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int tau = 0; tau < 3; ++tau) {
+            const int sT = tau == 2 ? 1 : 0, tT = tau == 0 ? 0 : 1;
+            const f32x4 mv = Ms[tau][lane];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                acc[tT] = mfma4(mv[m], X_[(sT * 16 + 4 * q + m) * XP + p0 + c16], acc[tT]);
+        }
+
+        // skip term and store: lane (column p0 + c16, rows t = tt*16 + q*4 + v)
+        float yv[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                yv[tt][v] = fmaf(Dh, X_[(tt * 16 + 4 * q + v) * XP + p0 + c16],
+                                 (ys[tt][0][v] + ys[tt][1][v]) + acc[tt][v]);
+        if (t0 + kT <= te) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + v) * rowX) + ylane) =
+                        yv[tt][v];
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (t0 + tt * 16 + q * 4 + v < te)
+                        *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + v) * rowX) + ylane) =
+                            yv[tt][v];
+        }
+
+        // D2 + D3
+        decay_state<NTK>(S, sc.E, K);
+        state_add<NTK, CP, XP>(S, B_, X_, sc, p0, K, lane);
+
+        // stage chunk j+1, start loading chunk j+2
+        if (j + 1 < nchunks) {
+            st.store(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1]);
+            if (wid == NW - 1)   // the wave with no decay-mask tile (or the least)
+                chunk_scalars(scal[buf ^ 1], p, mu, bias, st.rdt, t0 + kT + (lane & 31) < p.L, lane);
+            if (j + 2 < nchunks) st.load(t0 + 2 * kT);
+        }
+        __syncthreads();
+    }
+
+    if (p.h_final && wk.k == p.nseg - 1) {
+#pragma unroll
+        for (int kt = 0; kt < NTK; ++kt) {
+            if (kt * 16 >= K) break;
+            float *dst = p.h_final + ((wk.b * p.H + wk.h) * p.P + p0 + c16) * 2 * p.Nc + kt * 16 + q * 4;
+            *reinterpret_cast<float4 *>(dst) = make_float4(S[kt][0], S[kt][1], S[kt][2], S[kt][3]);
+        }
     }
 }
 
-template <int Q>
-hipError_t launch_q(const CssdKp &kp, hipStream_t s) {
-    const int64_t nwork = kp.batch * kp.nc * kp.H;
-    hipLaunchKernelGGL((cssd_chunk_state_kernel<Q>), dim3((unsigned)nwork), dim3(kThreads), 0, s, kp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t per_bh = (kp.P * kp.Nc + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(cssd_state_pass_kernel, dim3((unsigned)(kp.batch * kp.H * per_bh)), dim3(kThreads), 0, s, kp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((cssd_chunk_scan_kernel<Q>), dim3((unsigned)nwork), dim3(kThreads), 0, s, kp);
-    return hipGetLastError();
+struct Plan {
+    int64_t nseg, Ls;
+};
+Plan plan(int64_t batch, int64_t L, int64_t H, int64_t P) {
+    const int64_t waves = batch * H * (P / 16);
+    int64_t nseg = (kTargetWaves + waves - 1) / waves;
+    nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, L / kMinSeg));
+    const int64_t Ls = ((L + nseg - 1) / nseg + kT - 1) / kT * kT;
+    return Plan{(L + Ls - 1) / Ls, Ls};
+}
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+template <int KC, bool EXACT, int NW>
+void launch_all(const CssdKp &p, hipStream_t stream) {
+    if (p.nseg > 1) {
+        const int64_t n1 = p.batch * (p.nseg - 1) * p.H;
+        hipLaunchKernelGGL((cssd_state_kernel<KC, EXACT, NW>), dim3((unsigned)n1), dim3(64 * NW), 0, stream, p);
+        const int64_t nt = p.batch * p.H * p.P * p.Nc / 2;
+        hipLaunchKernelGGL(cssd_pass_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream, p);
+    }
+    const int64_t n = p.batch * p.nseg * p.H;
+    hipLaunchKernelGGL((cssd_scan_kernel<KC, EXACT, NW>), dim3((unsigned)n), dim3(64 * NW), 0, stream, p);
+}
+
+template <int NW>
+void launch_k(const CssdKp &p, hipStream_t stream) {
+    const int64_t K = 2 * p.Nc;
+    if (K == 16) return launch_all<16, true, NW>(p, stream);
+    if (K == 32) return launch_all<32, true, NW>(p, stream);
+    if (K == 64) return launch_all<64, true, NW>(p, stream);
+    if (K < 64) return launch_all<64, false, NW>(p, stream);
+    if (K == 128) return launch_all<128, true, NW>(p, stream);
+    launch_all<128, false, NW>(p, stream);
 }
 
 }  // namespace
 
-size_t cssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
-                            int64_t n_complex, int64_t chunk_len) {
-    const int64_t nc = (L + chunk_len - 1) / chunk_len;
-    const size_t st = (size_t)batch * nc * nheads * headdim * n_complex * 2 * sizeof(float);
-    const size_t cd = (size_t)batch * nheads * nc * 2 * sizeof(float);
-    return ((st + 255) / 256) * 256 + ((cd + 255) / 256) * 256;
+size_t cssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t n_complex,
+                            int64_t) {
+    const Plan pl = plan(batch, L, nheads, headdim);
+    if (pl.nseg <= 1) return 0;
+    return align256((size_t)(batch * nheads * pl.nseg * headdim * n_complex * 2) * sizeof(float)) +
+           (size_t)(batch * nheads * pl.nseg * 2) * sizeof(float);
 }
 
 hipError_t launch_cssd(const CssdArgs &a, hipStream_t stream, const char **kernel_name) {
-    *kernel_name = "cssd_chunk_state_kernel/cssd_state_pass_kernel/cssd_chunk_scan_kernel";
+    *kernel_name = "cssd_scan_kernel";
     CssdKp p{};
     p.x = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log; p.B = a.B; p.C = a.C;
     p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
     p.batch = a.batch; p.L = a.L; p.H = a.nheads; p.P = a.headdim; p.Nc = a.n_complex; p.G = a.ngroups;
-    p.nc = (a.L + a.chunk_len - 1) / a.chunk_len;
-    const size_t st = (size_t)a.batch * p.nc * a.nheads * a.headdim * a.n_complex * 2 * sizeof(float);
-    p.states = static_cast<float *>(a.workspace);
-    p.cdec = reinterpret_cast<float *>(static_cast<char *>(a.workspace) + ((st + 255) / 256) * 256);
     p.flags = a.flags;
-    if (a.chunk_len == 32) return launch_q<32>(p, stream);
-    if (a.chunk_len == 64) return launch_q<64>(p, stream);
-    return launch_q<128>(p, stream);
+    const Plan pl = plan(p.batch, p.L, p.H, p.P);
+    p.nseg = pl.nseg;
+    p.Ls = pl.Ls;
+    if (p.nseg > 1) {
+        p.ws_state = static_cast<float *>(a.workspace);
+        p.ws_decay = reinterpret_cast<float *>(
+            static_cast<char *>(a.workspace) +
+            align256((size_t)(p.batch * p.H * p.nseg * p.P * p.Nc * 2) * sizeof(float)));
+    }
+    if (p.P == 32) launch_k<2>(p, stream);
+    else if (p.P == 64) launch_k<4>(p, stream);
+    else launch_k<8>(p, stream);
+    return hipGetLastError();
 }
 
 }  // namespace ssm

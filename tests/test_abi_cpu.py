@@ -110,4 +110,11 @@ def test_cssd_argument_checks(lib):
     assert _cssd(lib, flags=0x8 | 0x1) == INVALID and "CODE" in _err(lib)
     assert _cssd(lib, flags=0xC) == INVALID
     assert _cssd(lib, flags=0x20) == INVALID
-    assert _cssd(lib, ws=None) == WORKSPACE
+    assert _cssd(lib, dims=(2, 100, 4, 64, 72, 2, 64)) == UNSUPPORTED and "n_complex" in _err(lib)
+    # long sequences are cut into segments whose states go through the workspace
+    long_dims = (4, 8192, 32, 64, 32, 1, 64)
+    need = lib.ssd_cplx_chunk_scan_fwd_workspace_size(*long_dims)
+    assert need >= 4 * 32 * 2 * 64 * 32 * 2 * 4
+    assert lib.ssd_cplx_chunk_scan_fwd_workspace_size(2, 100, 4, 64, 32, 2, 64) == 0
+    assert _cssd(lib, dims=long_dims, ws=None) == WORKSPACE
+    assert _cssd(lib, dims=long_dims, wsb=need - 1) == WORKSPACE

@@ -21,6 +21,11 @@ CASES = [  # batch, L, H, P, Nc, G, Q, flags, h0
     (1, 90, 2, 64, 32, 1, 64, STABLE | ZOH | CONJ, True),
     (1, 1, 2, 32, 8, 1, 64, STABLE | ZOH, True),
     (1, 64, 2, 128, 8, 1, 64, STABLE | ZOH, False),
+    # long enough to be cut into segments (state kernel + pass + scan), last segment partial
+    (1, 1000, 2, 64, 24, 1, 64, STABLE | ZOH, True),
+    (1, 800, 2, 64, 32, 1, 64, STABLE | ZOH | CONJ, True),
+    (2, 700, 3, 128, 64, 3, 128, STABLE | DT, False),
+    (1, 513, 1, 32, 40, 1, 32, STABLE | ONE, True),
 ]
 
 
