@@ -16,6 +16,9 @@ Parity status of each function (what pins it is listed in the tests):
             reduction to S6, group replication, hand case.
   cssd_fwd  pinned: reduction to the real SSD at zero phase, L=1 closed form,
             brute-force complex semiseparable matrix, conjugate-C identity.
+  s6_bwd    pinned: exact adjoint identities for the inputs the outputs are
+            linear in (u, B, C, D, h0) and central finite differences of
+            s6_fwd for the rest (dt, dt_bias, A_log), in all beta modes.
 """
 from __future__ import annotations
 
@@ -58,8 +61,11 @@ def _load():
     lib.oracle_s6_fwd.argtypes = common + [I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_ssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_cssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
-    for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd):
+    lib.oracle_s6_bwd.argtypes = [P] * 10 + [I, I, I, I, ctypes.c_uint32, I, I, I, I] + [P] * 8 + [ctypes.c_int]
+    for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd, lib.oracle_s6_bwd):
         f.restype = None
+    lib.oracle_dphi1.argtypes = [ctypes.c_double]
+    lib.oracle_dphi1.restype = ctypes.c_double
     lib.oracle_softplus.argtypes = [ctypes.c_double]
     lib.oracle_softplus.restype = ctypes.c_double
     lib.oracle_phi1.argtypes = [ctypes.c_double]
@@ -92,6 +98,10 @@ def softplus(x: float) -> float:
 
 def phi1(z: float) -> float:
     return _load().oracle_phi1(float(z))
+
+
+def dphi1(z: float) -> float:
+    return _load().oracle_dphi1(float(z))
 
 
 def _units(units, n0, n1):
@@ -176,3 +186,32 @@ def cssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_ZOH 
         return (y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(),
                 hf.reshape(batch, H, P, Nc, 2))
     return y, hf
+
+
+def s6_bwd(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, flags=BBAR_ZOH, b_range=None,
+           d_range=None, nthreads=None):
+    """Gradients of the S6 scan in fp64 (reverse-time chain rule of s6_fwd).
+
+    dy: (batch, L, d_inner) = dL/dy; dh_final: (batch, d_inner, N) or None.
+    Units are b in b_range, d in d_range (default: all); sums over b or d run
+    over those ranges.  Returns a dict: du, ddt (nb, L, nd); dB, dC (nb, L, N);
+    dA_log (nd, N); dD, ddt_bias (nd,); dh0 (nb, nd, N).
+    """
+    u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final = map(
+        _f32, (u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final))
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    b_lo, b_hi = b_range if b_range is not None else (0, batch)
+    d_lo, d_hi = d_range if d_range is not None else (0, Dm)
+    if not (0 <= b_lo < b_hi <= batch and 0 <= d_lo < d_hi <= Dm):
+        raise ValueError("unit range out of bounds")
+    nb, nd = b_hi - b_lo, d_hi - d_lo
+    out = dict(du=np.empty((nb, L, nd)), ddt=np.empty((nb, L, nd)), dB=np.empty((nb, L, N)),
+               dC=np.empty((nb, L, N)), dA_log=np.empty((nd, N)), dD=np.empty((nd,)),
+               ddt_bias=np.empty((nd,)), dh0=np.empty((nb, nd, N)))
+    _load().oracle_s6_bwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                          _ptr(h0), _ptr(dy), _ptr(dh_final), batch, L, Dm, N, flags,
+                          b_lo, b_hi, d_lo, d_hi,
+                          *(_ptr(out[k]) for k in ("du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")),
+                          nthreads or default_threads())
+    return out

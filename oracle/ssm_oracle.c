@@ -340,6 +340,189 @@ void oracle_cssd_fwd(const float *x, const float *dt, const float *dt_bias, cons
     run_units(2, &j, n_units, nthreads);
 }
 
+/* ------------------------------------------------------- S6 backward --- */
+/*
+ * Gradient of a loss L with respect to every input of the S6 forward scan,
+ * given dy = dL/dy (batch, L, d_inner) and optionally dL/dh_final.  This is
+ * the chain rule applied to the sequential recurrence above, step by step in
+ * reverse time (the reverse scan the S6 page lays out in backward_scan of
+ * selective_scan.js, completed with the terms that page leaves out: beta's
+ * dependence on A and the sums over channels for the shared B and C):
+ *
+ *   g_t      = dL/dh_t = g_{t+1} Abar_{t+1} + C_t dy_t   (g_L = dL/dh_final)
+ *   dC_t[n] += dy_t[d] h_t[n]                 (summed over d)
+ *   dB_t[n] += g_t beta_t u_t[d]              (summed over d)
+ *   du_t[d]  = D dy_t + sum_n g_t beta_t B_t[n]
+ *   ddelta_t = sum_n g_t (h_{t-1} dAbar/ddelta + B_t u_t dbeta/ddelta)
+ *   dA[d,n] += g_t (h_{t-1} dAbar/dA + B_t u_t dbeta/dA)   (summed over b, t)
+ *   Abar = e^{delta A}:  dAbar/ddelta = A Abar,  dAbar/dA = delta Abar
+ *   ZOH beta = delta phi1(delta A): dbeta/ddelta = Abar, dbeta/dA = delta^2 phi1'(delta A)
+ *   DT beta = delta: 1, 0;   ONE beta = 1: 0, 0
+ *   ddt = ddelta * sigmoid(dt + dt_bias) (softplus' = sigmoid); ddt_bias = sum ddt
+ *   dA_log = dA * A (A = -exp(A_log));  dD[d] = sum dy u;  dh0 = g_0 Abar_0
+ *
+ * Units are (b, d) for b in [b_lo, b_hi), d in [d_lo, d_hi); sums over b or d
+ * run over those ranges only, so a caller can take complete sums by passing
+ * full ranges.  Outputs are double:
+ *   du, ddt [nb][L][nd];  dB, dC [nb][L][N];  dA_log [nd][N];
+ *   dD, ddt_bias [nd];  dh0 [nb][nd][N]
+ */
+
+/* phi1'(z) = (e^z (z - 1) + 1)/z^2 = (expm1(z)(z - 1) + z)/z^2, phi1'(0) = 1/2;
+ * below |z| = 1e-3 its Taylor series sum_m (m+1) z^m/(m+2)! (to z^4). */
+static double dphi1(double z)
+{
+    if (fabs(z) < 1e-3) return 0.5 + z * (1.0 / 3.0 + z * (1.0 / 8.0 + z * (1.0 / 30.0 + z / 144.0)));
+    return (expm1(z) * (z - 1.0) + z) / (z * z);
+}
+
+static double sigm(double x)
+{
+    if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+    const double e = exp(x);
+    return e / (1.0 + e);
+}
+
+typedef struct {
+    const float *u, *dt, *dt_bias, *A_log, *B, *C, *D, *h0, *dy, *dhf;
+    int64_t batch, L, Dm, N, b_lo, b_hi, d_lo, d_hi;
+    uint32_t flags;
+    double *du, *ddt, *dB, *dC, *dA_log, *dD, *ddtb, *dh0;   /* shared outputs */
+} s6b_job;
+
+typedef struct {
+    const s6b_job *j;
+    int tid, nthreads;
+    double *dB, *dC, *dA, *dD, *ddtb;   /* this thread's partial sums */
+} s6b_arg;
+
+static void s6b_unit(const s6b_job *j, s6b_arg *w, int64_t b, int64_t d)
+{
+    const int64_t L = j->L, Dm = j->Dm, N = j->N;
+    const int64_t nd = j->d_hi - j->d_lo, bi = b - j->b_lo, di = d - j->d_lo;
+    const int mode = (int)(j->flags & OR_BBAR_MASK);
+    double *A = (double *)malloc(sizeof(double) * (size_t)N);
+    double *g = (double *)malloc(sizeof(double) * (size_t)N);
+    double *h = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N));   /* h[t+1] = h_t, h[0] = h0 */
+    for (int64_t n = 0; n < N; ++n) {
+        A[n] = -exp((double)j->A_log[d * N + n]);
+        h[n] = j->h0 ? (double)j->h0[(b * Dm + d) * N + n] : 0.0;
+        g[n] = j->dhf ? (double)j->dhf[(b * Dm + d) * N + n] : 0.0;
+    }
+    const double bias = j->dt_bias ? (double)j->dt_bias[d] : 0.0;
+    const double Dd = j->D ? (double)j->D[d] : 0.0;
+    /* forward, keeping every state */
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t e = (b * L + t) * Dm + d;
+        const double delta = sp((double)j->dt[e] + bias);
+        const double uu = (double)j->u[e];
+        const float *Bt = j->B + (b * L + t) * N;
+        for (int64_t n = 0; n < N; ++n) {
+            const double z = delta * A[n];
+            double beta;
+            if (mode == OR_BBAR_ZOH) beta = delta * phi1(z);
+            else if (mode == OR_BBAR_DT) beta = delta;
+            else beta = 1.0;
+            h[(t + 1) * N + n] = exp(z) * h[t * N + n] + beta * (double)Bt[n] * uu;
+        }
+    }
+    /* reverse */
+    for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t e = (b * L + t) * Dm + d;
+        const double x = (double)j->dt[e] + bias;
+        const double delta = sp(x);
+        const double uu = (double)j->u[e];
+        const double dyv = (double)j->dy[e];
+        const float *Bt = j->B + (b * L + t) * N;
+        const float *Ct = j->C + (b * L + t) * N;
+        double ddelta = 0.0, duv = Dd * dyv;
+        for (int64_t n = 0; n < N; ++n) {
+            const double z = delta * A[n];
+            const double Ab = exp(z);
+            double beta, bD, bA;
+            if (mode == OR_BBAR_ZOH) { beta = delta * phi1(z); bD = Ab; bA = delta * delta * dphi1(z); }
+            else if (mode == OR_BBAR_DT) { beta = delta; bD = 1.0; bA = 0.0; }
+            else { beta = 1.0; bD = 0.0; bA = 0.0; }
+            g[n] += (double)Ct[n] * dyv;
+            const double hp = h[t * N + n], ht = h[(t + 1) * N + n];
+            const double Bu = (double)Bt[n] * uu;
+            w->dC[(bi * L + t) * N + n] += dyv * ht;
+            w->dB[(bi * L + t) * N + n] += g[n] * beta * uu;
+            duv += g[n] * beta * (double)Bt[n];
+            ddelta += g[n] * (hp * A[n] * Ab + Bu * bD);
+            w->dA[di * N + n] += g[n] * (hp * delta * Ab + Bu * bA);
+            g[n] *= Ab;
+        }
+        const double ddt = ddelta * sigm(x);
+        j->ddt[(bi * L + t) * nd + di] = ddt;
+        j->du[(bi * L + t) * nd + di] = duv;
+        w->ddtb[di] += ddt;
+        w->dD[di] += dyv * uu;
+    }
+    if (j->dh0)
+        for (int64_t n = 0; n < N; ++n) j->dh0[(bi * nd + di) * N + n] = g[n];
+    free(A);
+    free(g);
+    free(h);
+}
+
+static void *s6b_worker(void *p)
+{
+    s6b_arg *w = (s6b_arg *)p;
+    const s6b_job *j = w->j;
+    const int64_t nd = j->d_hi - j->d_lo, nu = (j->b_hi - j->b_lo) * nd;
+    for (int64_t k = w->tid; k < nu; k += w->nthreads)
+        s6b_unit(j, w, j->b_lo + k / nd, j->d_lo + k % nd);
+    return NULL;
+}
+
+void oracle_s6_bwd(const float *u, const float *dt, const float *dt_bias, const float *A_log,
+                   const float *B, const float *C, const float *D, const float *h0,
+                   const float *dy, const float *dh_final,
+                   int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, uint32_t flags,
+                   int64_t b_lo, int64_t b_hi, int64_t d_lo, int64_t d_hi,
+                   double *du, double *ddt, double *dB, double *dC, double *dA_log, double *dD,
+                   double *ddt_bias, double *dh0, int nthreads)
+{
+    const int64_t nb = b_hi - b_lo, nd = d_hi - d_lo, N = d_state;
+    s6b_job j = {u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, batch, L, d_inner, d_state,
+                 b_lo, b_hi, d_lo, d_hi, flags, du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0};
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > nb * nd) nthreads = (int)(nb * nd > 0 ? nb * nd : 1);
+    const size_t nbc = (size_t)(nb * L * N);
+    s6b_arg args[256];
+    pthread_t th[256];
+    for (int i = 0; i < nthreads; ++i) {
+        args[i].j = &j; args[i].tid = i; args[i].nthreads = nthreads;
+        args[i].dB = (double *)calloc(nbc, sizeof(double));
+        args[i].dC = (double *)calloc(nbc, sizeof(double));
+        args[i].dA = (double *)calloc((size_t)(nd * N), sizeof(double));
+        args[i].dD = (double *)calloc((size_t)nd, sizeof(double));
+        args[i].ddtb = (double *)calloc((size_t)nd, sizeof(double));
+    }
+    if (nthreads == 1) s6b_worker(&args[0]);
+    else {
+        for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, s6b_worker, &args[i]);
+        for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    }
+    memset(dB, 0, nbc * sizeof(double));
+    memset(dC, 0, nbc * sizeof(double));
+    memset(dA_log, 0, (size_t)(nd * N) * sizeof(double));
+    memset(dD, 0, (size_t)nd * sizeof(double));
+    memset(ddt_bias, 0, (size_t)nd * sizeof(double));
+    for (int i = 0; i < nthreads; ++i) {   /* fixed order: the result does not depend on timing */
+        for (size_t k = 0; k < nbc; ++k) { dB[k] += args[i].dB[k]; dC[k] += args[i].dC[k]; }
+        for (int64_t k = 0; k < nd * N; ++k) dA_log[k] += args[i].dA[k];
+        for (int64_t k = 0; k < nd; ++k) { dD[k] += args[i].dD[k]; ddt_bias[k] += args[i].ddtb[k]; }
+        free(args[i].dB); free(args[i].dC); free(args[i].dA); free(args[i].dD); free(args[i].ddtb);
+    }
+    for (int64_t di = 0; di < nd; ++di)   /* dA -> dA_log: dA/dA_log = A */
+        for (int64_t n = 0; n < N; ++n)
+            dA_log[di * N + n] *= -exp((double)A_log[(d_lo + di) * N + n]);
+}
+
 /* elementary functions, exported so the tests can pin them on their own */
 double oracle_softplus(double x) { return sp(x); }
 double oracle_phi1(double z) { return phi1(z); }
+double oracle_dphi1(double z) { return dphi1(z); }
