@@ -35,6 +35,9 @@ S6_ALU_PEAK_TFLOPS = VALU_SLOTS_PER_S / S6_SLOTS_PER_UPDATE * S6_FLOPS_PER_UPDAT
 # WRITE_SIZE (KiB per dispatch) scaled by a 1 GiB device copy (fetch x 2.0, write x 1.0);
 # valid only for the kernel source with this sha1
 S6_TRAFFIC = {"src_sha1": "20e7683cc01827a37f589679373fbf43546fb491", "bytes": (100207 * 2.0 + 99077.2 * 1.0) * 1024}
+# adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
+# (products and fmas, 24 flops) plus the recomputed Abar, beta, phi1' (not counted again)
+S6_BWD_FLOPS_PER_UPDATE = 24
 N_ROTATE = 3                     # input copies rotated between steps (> Infinity Cache)
 
 
@@ -49,6 +52,17 @@ def s6_model(d):
     isz = 4
     bytes_ = elems * (isz + 4 + 4) + 2 * B * L * N * isz + D * N * 4 + 2 * D * 4 + B * D * N * 4
     ops = elems * N * S6_FLOPS_PER_UPDATE   # per (b,t,d,n) state update
+    return elems, bytes_, ops
+
+
+def s6_bwd_model(d):
+    """Algorithmic bytes of one S6 backward call: read u, dt, dy, B, C, write du, ddt,
+    dB, dC, dA_log, dD, ddt_bias, dh0 (and read dh_final); ops: one forward state
+    update (to have h) plus the adjoint update per (b, t, d, n)."""
+    B, L, D, N = d["batch"], d["L"], d["d_inner"], d["d_state"]
+    elems = B * L * D
+    bytes_ = elems * 4 * 5 + 4 * B * L * N * 4 + 2 * B * D * N * 4 + D * N * 8 + 3 * D * 4
+    ops = elems * N * (S6_FLOPS_PER_UPDATE + S6_BWD_FLOPS_PER_UPDATE)
     return elems, bytes_, ops
 
 
@@ -79,6 +93,9 @@ def make_runner(name, dev):
     import torch
     import selective_state_space_s6_amd as lib
     import synth
+    bwd = name.endswith("_bwd")
+    if bwd:
+        name = name[: -len("_bwd")]
     w = dict(synth.WORKLOADS[name])
     kind = w["kind"]
     copies = []
@@ -86,6 +103,25 @@ def make_runner(name, dev):
         inp = synth.workload_inputs(name, seed=(r,))
         copies.append(inp.torch(dev))
         dims = inp.dims
+    if kind == "s6" and bwd:
+        d = dims
+        for r, t in enumerate(copies):
+            dy, dhf = synth.s6_cotangents(d["batch"], d["L"], d["d_inner"], d["d_state"], seed=(r,))
+            t["dy"], t["dhf"] = torch.from_numpy(dy).to(dev), torch.from_numpy(dhf).to(dev)
+        shapes = dict(du=(d["batch"], d["L"], d["d_inner"]), ddt=(d["batch"], d["L"], d["d_inner"]),
+                      dB=(d["batch"], d["L"], d["d_state"]), dC=(d["batch"], d["L"], d["d_state"]),
+                      dA_log=(d["d_inner"], d["d_state"]), dD=(d["d_inner"],),
+                      ddt_bias=(d["d_inner"],), dh0=(d["batch"], d["d_inner"], d["d_state"]))
+        out = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+        ws = torch.empty(lib.ssm_s6_scan_bwd_workspace_size(d["batch"], d["L"], d["d_inner"],
+                                                            d["d_state"]), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            lib.ssm_s6_scan_bwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                None, t["dy"], t["dhf"], out=out, workspace=ws)
+        w["kind"] = "s6_bwd"
+        return step, dims, w, ["s6_bwd_kernel", "s6_bwd_reduce_kernel"]
     if kind == "s6":
         t0 = copies[0]
         y = torch.empty_like(t0["u"], dtype=torch.float32)
@@ -162,6 +198,24 @@ def cpu_baseline_s6(name):
             "sample": f"whole {name} workload ({elems} elements, fp64, {sec:.2f} s wall on {nthr} threads)"}
 
 
+def cpu_baseline_s6_bwd(name, n_rows=2):
+    """The fp64 backward oracle on the first n_rows batch rows of the workload."""
+    import oracle
+    import synth
+    inp = synth.workload_inputs(name, seed=(0,))
+    d = inp.dims
+    dy, dhf = synth.s6_cotangents(d["batch"], d["L"], d["d_inner"], d["d_state"], seed=(0,))
+    nthr = oracle.default_threads()
+    n_rows = min(n_rows, d["batch"])
+    t0 = time.perf_counter()
+    oracle.s6_bwd(**inp.arrays, dy=dy, dh_final=dhf, b_range=(0, n_rows), nthreads=nthr)
+    sec = time.perf_counter() - t0
+    elems = n_rows * d["L"] * d["d_inner"]
+    return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{n_rows} of {d['batch']} batch rows of the {name} backward "
+                      f"({elems} elements, fp64, {sec:.2f} s wall)"}
+
+
 def cpu_baseline_units(name, n_units):
     """The fp64 oracle on a bounded sample of (b, h) units of an SSD-type workload."""
     import numpy as np
@@ -201,6 +255,8 @@ def measure(name, dev, steps, warmup):
     dims = dict(dims, chunk_len=w.get("chunk_len"))
     if kind == "s6":
         elems, bytes_, ops = s6_model(dims)
+    elif kind == "s6_bwd":
+        elems, bytes_, ops = s6_bwd_model(dims)
     elif kind == "ssd":
         elems, bytes_, ops = ssd_model(dims)
     else:
@@ -266,7 +322,8 @@ def main():
     }
     if not args.no_secondary and args.workload == "s6_mamba1":
         sec = []
-        for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5)):
+        for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
+                            ("s6_mamba1_bwd", 10)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
             es = s["event_ms_median"] * 1e-3
@@ -274,7 +331,10 @@ def main():
                    "unit": "elements/s", "ms_per_step": round(s["ms"], 4),
                    "hbm_GBps": round(s["bytes"] / es / 1e9, 1),
                    "hbm_frac": round(s["bytes"] / es / 1e9 / HBM_PEAK_GBS, 4)}
-            if s["kind"] == "ssd":
+            if s["kind"] == "s6_bwd":
+                ent["fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
+                ent["kernel_ms"] = round(s["event_ms_median"], 4)
+            elif s["kind"] == "ssd":
                 ent["mfma_TFLOPs"] = round(s["ops"] / es / 1e12, 1)
                 ent["mfma_frac_bf16"] = round(s["ops"] / es / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
             else:
@@ -287,6 +347,8 @@ def main():
         log("[bench] cpu baseline (oracle)")
         if kind == "s6":
             out["cpu_baseline"] = cpu_baseline_s6(args.workload)
+        elif kind == "s6_bwd":
+            out["cpu_baseline"] = cpu_baseline_s6_bwd(args.workload[: -len("_bwd")])
         else:
             out["cpu_baseline"] = cpu_baseline_units(args.workload, 16)
     print(json.dumps(out), flush=True)

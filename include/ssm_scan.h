@@ -109,6 +109,45 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
                     ssm_dtype_t in_dtype, uint32_t flags,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* --------------------------------------------------------- S6 backward ----
+ * Gradients of a scalar loss through the S6 scan above, given dy = dL/dy and
+ * optionally dh_final = dL/dh_final: the reverse-time chain rule of the
+ * recurrence [BF-S6 backward_scan, completed with beta's dependence on A and
+ * the sums over channels for the shared B and C].  With g_t = dL/dh_t
+ * (g_{L-1} = C_{L-1} dy_{L-1} + dh_final, g_t = C_t dy_t + exp(delta_{t+1} A) g_{t+1}):
+ *   du[b,t,d]   = D[d] dy + sum_n g_t beta_t B[b,t,n]
+ *   ddt[b,t,d]  = sigmoid(dt + dt_bias) * sum_n g_t (h_{t-1} A Abar_t + B u dbeta/ddelta)
+ *   dB[b,t,n]   = sum_d g_t beta_t u[b,t,d]         dC[b,t,n] = sum_d dy[b,t,d] h_t[n]
+ *   dA_log[d,n] = A sum_{b,t} g_t (h_{t-1} delta Abar_t + B u dbeta/dA)
+ *   dD[d] = sum_{b,t} dy u,   ddt_bias[d] = sum_{b,t} ddt,   dh0 = g_0 Abar_0
+ * (dbeta/ddelta, dbeta/dA = Abar, delta^2 phi1'(delta A) for SSM_BBAR_ZOH;
+ * 1, 0 for SSM_BBAR_DT; 0, 0 for SSM_BBAR_ONE.)
+ *
+ * Inputs: those of ssm_s6_scan_fwd (same layouts, in_dtype and flags), plus
+ * dy (batch, L, d_inner) fp32 and dh_final (batch, d_inner, d_state) fp32 or NULL.
+ * Outputs (fp32, caller-owned, fully overwritten): du, ddt (batch, L, d_inner);
+ * dB, dC (batch, L, d_state); dA_log (d_inner, d_state); dD, ddt_bias (d_inner);
+ * dh0 (batch, d_inner, d_state).  dD, ddt_bias and dh0 may be NULL (not
+ * written); the others are required.  No output may alias an input or
+ * another output.
+ * Limits: 1 <= d_state <= 16; 1 <= L < 2^31 - 16; d_inner < 2^25.
+ * Workspace: ssm_s6_scan_bwd_workspace_size() bytes, 16-byte aligned, owned by
+ * the caller and reused freely between calls on one stream: the state entering
+ * every 16-step tile (batch * ceil(L/16) * d_inner * d_state fp32) and
+ * per-block partial sums, added in a fixed order by a second kernel. */
+#define SSM_S6_BWD_MAX_D_STATE 16
+
+size_t ssm_s6_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state);
+
+int ssm_s6_scan_bwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                    const void *B, const void *C, const float *D, const float *h0,
+                    const float *dy, const float *dh_final,
+                    float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                    float *dD, float *ddt_bias, float *dh0,
+                    int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                    ssm_dtype_t in_dtype, uint32_t flags,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------- SSD ----
  * Mamba-2 state-space dual scan with a scalar A per head [BF-SSD header and
  * ssd_chunk_forward; RS-M3 F6 K2-K5]:

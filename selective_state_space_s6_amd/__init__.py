@@ -16,8 +16,8 @@ import os
 import torch
 
 __all__ = [
-    "ssm_s6_scan_fwd", "ssd_chunk_scan_fwd", "ssd_cplx_chunk_scan_fwd",
-    "ssm_s6_scan_fwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
+    "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssd_chunk_scan_fwd", "ssd_cplx_chunk_scan_fwd",
+    "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
     "ssd_cplx_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
     "SSM_BBAR_ZOH", "SSM_BBAR_DT", "SSM_BBAR_ONE", "SSM_CPLX_STABLE", "SSM_CPLX_DOC",
     "SSM_CPLX_CODE", "SSM_CPLX_CONJ_C", "SSM_F32", "SSM_BF16",
@@ -30,7 +30,7 @@ SSM_CPLX_STABLE, SSM_CPLX_DOC, SSM_CPLX_CODE, SSM_CPLX_CONJ_C = 0x0, 0x4, 0x8, 0
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssmscan.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m selective_state_space_s6_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python selective_state_space_s6_amd/build.py` "
         "(there is no non-HIP fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -40,6 +40,10 @@ _lib.ssm_s6_scan_fwd_workspace_size.argtypes = [_I] * 4
 _lib.ssm_s6_scan_fwd_workspace_size.restype = _Z
 _lib.ssm_s6_scan_fwd.argtypes = [_P] * 10 + [_I] * 4 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
 _lib.ssm_s6_scan_fwd.restype = ctypes.c_int
+_lib.ssm_s6_scan_bwd_workspace_size.argtypes = [_I] * 4
+_lib.ssm_s6_scan_bwd_workspace_size.restype = _Z
+_lib.ssm_s6_scan_bwd.argtypes = [_P] * 18 + [_I] * 4 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
+_lib.ssm_s6_scan_bwd.restype = ctypes.c_int
 _lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
@@ -105,6 +109,10 @@ def ssm_s6_scan_fwd_workspace_size(batch, L, d_inner, d_state) -> int:
     return int(_lib.ssm_s6_scan_fwd_workspace_size(batch, L, d_inner, d_state))
 
 
+def ssm_s6_scan_bwd_workspace_size(batch, L, d_inner, d_state) -> int:
+    return int(_lib.ssm_s6_scan_bwd_workspace_size(batch, L, d_inner, d_state))
+
+
 def ssd_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups, chunk_len) -> int:
     return int(_lib.ssd_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups,
                                                       chunk_len))
@@ -145,6 +153,52 @@ def ssm_s6_scan_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, *, flags=SSM_BBAR_Z
                               _in_dtype(u), flags, None, 0, _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y
+
+
+_S6_GRADS = ("du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")
+
+
+def ssm_s6_scan_bwd(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, *, flags=SSM_BBAR_ZOH,
+                    out=None, workspace=None):
+    """Gradients of the S6 forward scan.  Inputs as ssm_s6_scan_fwd, plus
+    dy (batch, L, d_inner) fp32 and dh_final (batch, d_inner, d_state) fp32 or None.
+    Returns a dict of fp32 tensors: du, ddt (batch, L, d_inner); dB, dC
+    (batch, L, d_state); dA_log (d_inner, d_state); dD, ddt_bias (d_inner);
+    dh0 (batch, d_inner, d_state).  `out` may hold preallocated tensors under
+    those names; `workspace` a uint8 tensor of ssm_s6_scan_bwd_workspace_size bytes."""
+    dev = u.device
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    dty = u.dtype
+    _req(u, "u", dty, (batch, L, Dm), dev)
+    _req(dt, "dt", torch.float32, (batch, L, Dm), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (Dm,), dev)
+    _req(A_log, "A_log", torch.float32, (Dm, N), dev)
+    _req(B, "B", dty, (batch, L, N), dev)
+    _req(C, "C", dty, (batch, L, N), dev)
+    _opt(D, "D", torch.float32, (Dm,), dev)
+    _opt(h0, "h0", torch.float32, (batch, Dm, N), dev)
+    _req(dy, "dy", torch.float32, (batch, L, Dm), dev)
+    _opt(dh_final, "dh_final", torch.float32, (batch, Dm, N), dev)
+    shapes = dict(du=(batch, L, Dm), ddt=(batch, L, Dm), dB=(batch, L, N), dC=(batch, L, N),
+                  dA_log=(Dm, N), dD=(Dm,), ddt_bias=(Dm,), dh0=(batch, Dm, N))
+    g = dict(out or {})
+    for k in _S6_GRADS:
+        if g.get(k) is None:
+            g[k] = torch.empty(shapes[k], dtype=torch.float32, device=dev)
+        _req(g[k], k, torch.float32, shapes[k], dev)
+    need = ssm_s6_scan_bwd_workspace_size(batch, L, Dm, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    rc = _lib.ssm_s6_scan_bwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                              _ptr(D), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                              *(_ptr(g[k]) for k in _S6_GRADS), batch, L, Dm, N, _in_dtype(u),
+                              flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(dev))
+    _check(rc)
+    return g
 
 
 def ssd_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=256,

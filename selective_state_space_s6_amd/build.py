@@ -1,6 +1,6 @@
 """Build libssmscan.so (gfx950) from the HIP sources in csrc/.
 
-Usage: python -m selective_state_space_s6_amd.build   (or build() from Python)
+Usage: python selective_state_space_s6_amd/build.py   (or __graft_entry__.build())
 Each source is compiled to an object in parallel, then linked into a shared
 library next to this file.  Always recompiles (no staleness heuristics).
 """
@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libssmscan.so")
-SOURCES = ["abi.hip", "s6_scan.hip", "ssd_scan.hip", "cssd_scan.hip"]
+SOURCES = ["abi.hip", "s6_scan.hip", "s6_bwd.hip", "ssd_scan.hip", "cssd_scan.hip"]
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 # Packed fp32 ops are switched off: the compiler must not emit v_pk_{add,mul,fma}_f32.
 # MFMA accumulators are kept in ordinary VGPRs, so the fp32 state that the SSD

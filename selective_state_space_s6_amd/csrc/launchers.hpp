@@ -15,6 +15,18 @@ struct S6Args {
 };
 hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_name);
 
+struct S6BwdArgs {
+    const void *u; const float *dt; const float *dt_bias; const float *A_log;
+    const void *B; const void *C; const float *D; const float *h0;
+    const float *dy; const float *dh_final;
+    float *du, *ddt, *dB, *dC, *dA_log, *dD, *ddt_bias, *dh0;
+    int64_t batch, L, d_inner, d_state;
+    bool bf16; uint32_t flags;
+    void *workspace;
+};
+size_t s6_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state);
+hipError_t launch_s6_bwd(const S6BwdArgs &a, hipStream_t stream, const char **kernel_name);
+
 struct SsdArgs {
     const void *x; const float *dt; const float *dt_bias; const float *A_log;
     const void *B; const void *C; const float *D; float *y;

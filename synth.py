@@ -123,6 +123,15 @@ def s6_inputs(batch, L, d_inner, d_state, *, seed=(0,), dtype="f32", dt_bias="un
                   dict(u=u, dt=dt, dt_bias=bias, A_log=A_log, B=B, C=C, D=Dv, h0=h0a), bf)
 
 
+def s6_cotangents(batch, L, d_inner, d_state, *, seed=(0,), dh_final=True):
+    """Seeded dL/dy (batch, L, d_inner) and dL/dh_final (batch, d_inner, d_state),
+    both N(0, 1) fp32, for the backward pass (dh_final None when not asked)."""
+    key = (4, *seed)
+    dy = _normal(_rng(key, 0), (batch, L, d_inner))
+    dhf = _normal(_rng(key, 1), (batch, d_inner, d_state)) if dh_final else None
+    return dy, dhf
+
+
 def ssd_inputs(batch, L, nheads, headdim, d_state, ngroups, *, seed=(0,), dtype="bf16",
                h0=False, dt_bias=True, D="one") -> Inputs:
     key = (2, *seed)

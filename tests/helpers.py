@@ -9,6 +9,15 @@ import synth
 
 TOL_F32 = 1e-4     # max relative error, fp32 inputs
 TOL_BF16 = 2e-2    # max relative error, bf16 inputs with fp32 state
+# Backward pass (fp32 arithmetic on the exact input values, bf16 or fp32): its outputs
+# are sums over up to d_inner channels (dB, dC), batch*L steps (dA_log) or 16 states
+# (du, ddt) of products of fp32 states and cotangents, each carrying a relative rounding
+# error eps of a few ulp (~3e-7) accumulated over the recurrence's memory.  A K-term sum of
+# random-sign terms has rms ~ sqrt(K)|term| and error ~ eps sqrt(K)|term|, so near a zero
+# of the result the metric's floor 0.01*rms turns it into ~eps*z/0.01 with z ~ 5 the largest
+# deviate among 1e5-1e7 elements: ~2e-4.  A plain fp32 computation of the same gradients
+# (numpy, each op rounded) scores 1.3e-4 to 1e-3 at the Mamba-1 layer shape.
+TOL_BWD = 1e-3
 
 
 def lib():

@@ -28,7 +28,8 @@ def lib():
     L.ssm_s6_scan_fwd.argtypes = [P] * 10 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_cplx_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_uint32, P, Z, P]
-    for f in ("ssm_s6_scan_fwd_workspace_size",):
+    L.ssm_s6_scan_bwd.argtypes = [P] * 18 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
+    for f in ("ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size"):
         getattr(L, f).argtypes = [I] * 4
         getattr(L, f).restype = Z
     for f in ("ssd_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd_workspace_size"):
@@ -42,6 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M))
     names = {n for n in names if n.startswith(("ssm_", "ssd_"))}
     assert names == {"ssm_last_error", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_fwd",
+                     "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
                      "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd"}
     for n in names:
@@ -70,6 +72,37 @@ def test_s6_argument_checks(lib):
     assert _s6(lib, B=MIS) == UNSUPPORTED and "aligned" in _err(lib)
     assert _s6(lib, y=FAKE, u=FAKE) == INVALID and "alias" in _err(lib)
     assert lib.ssm_s6_scan_fwd_workspace_size(8, 2048, 1536, 16) == 0
+
+
+def _s6b(lib, dims=(2, 40, 20, 16), dtype=0, flags=0, ws=ctypes.c_void_p(0x900000), wsb=1 << 40,
+         **kw):
+    names = ["u", "dt", "dt_bias", "A_log", "B", "C", "D", "h0", "dy", "dh_final",
+             "du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0"]
+    required = {"u", "dt", "A_log", "B", "C", "dy", "du", "ddt", "dB", "dC", "dA_log"}
+    # distinct aligned fake addresses for the required pointers, NULL for the optional ones
+    ptrs = {n: (ctypes.c_void_p(0x100000 * (i + 1)) if n in required else None)
+            for i, n in enumerate(names)}
+    ptrs.update(kw)
+    return lib.ssm_s6_scan_bwd(*(ptrs[n] for n in names), *dims, dtype, flags, ws, wsb, None)
+
+
+def test_s6_bwd_argument_checks(lib):
+    assert _s6b(lib, dy=None) == INVALID and "dy is NULL" in _err(lib)
+    assert _s6b(lib, dA_log=None) == INVALID and "dA_log is NULL" in _err(lib)
+    assert _s6b(lib, dims=(0, 40, 20, 16)) == INVALID and "batch" in _err(lib)
+    assert _s6b(lib, dims=(2, 40, 20, 17)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _s6b(lib, dtype=3) == INVALID and "in_dtype" in _err(lib)
+    assert _s6b(lib, flags=0x3) == INVALID and "flags" in _err(lib)
+    assert _s6b(lib, dB=MIS) == UNSUPPORTED and "aligned" in _err(lib)
+    assert _s6b(lib, du=ctypes.c_void_p(0x100000)) == INVALID and "alias" in _err(lib)   # du == u
+    assert _s6b(lib, dD=ctypes.c_void_p(0xB00000)) == INVALID and "alias" in _err(lib)   # dD == du
+    need = lib.ssm_s6_scan_bwd_workspace_size(2, 40, 20, 16)
+    # the state entering each of the 3 tiles of 16 steps, per (batch, channel, state)
+    assert need >= 2 * 3 * 20 * 16 * 4 and need % 256 == 0
+    assert _s6b(lib, ws=None) == WORKSPACE and "workspace" in _err(lib)
+    assert _s6b(lib, wsb=need - 1) == WORKSPACE
+    assert lib.ssm_s6_scan_bwd_workspace_size(0, 40, 20, 16) == 0
+    assert lib.ssm_s6_scan_bwd_workspace_size(8, 2048, 1536, 16) >= 8 * 128 * 1536 * 16 * 4
 
 
 def _ssd(lib, dims=(2, 300, 4, 64, 128, 2, 256), dtype=1, flags=1, ws=FAKE, wsb=1 << 40, x=FAKE,
