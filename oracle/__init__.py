@@ -19,6 +19,9 @@ Parity status of each function (what pins it is listed in the tests):
   s6_bwd    pinned: exact adjoint identities for the inputs the outputs are
             linear in (u, B, C, D, h0) and central finite differences of
             s6_fwd for the rest (dt, dt_bias, A_log), in all beta modes.
+  ssd_bwd   pinned: the same two kinds of checks against ssd_fwd (with groups
+            and h0), and equality with s6_bwd on the SSD shapes that are an S6
+            scan (headdim 1, one group, A shared over the states).
 """
 from __future__ import annotations
 
@@ -62,7 +65,9 @@ def _load():
     lib.oracle_ssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_cssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_s6_bwd.argtypes = [P] * 10 + [I, I, I, I, ctypes.c_uint32, I, I, I, I] + [P] * 8 + [ctypes.c_int]
-    for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd, lib.oracle_s6_bwd):
+    lib.oracle_ssd_bwd.argtypes = [P] * 10 + [I] * 6 + [ctypes.c_uint32, P, I] + [P] * 8 + [ctypes.c_int]
+    for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd, lib.oracle_s6_bwd,
+              lib.oracle_ssd_bwd):
         f.restype = None
     lib.oracle_dphi1.argtypes = [ctypes.c_double]
     lib.oracle_dphi1.restype = ctypes.c_double
@@ -160,6 +165,49 @@ def ssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_DT, u
     if full:
         return (y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(), hf.reshape(batch, H, P, N))
     return y, hf
+
+
+def ssd_bwd(x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, ngroups=1, flags=BBAR_DT,
+            units=None, nthreads=None):
+    """Gradients of the SSD recurrence in fp64 (reverse-time chain rule of ssd_fwd).
+
+    dy: (batch, L, H, P) = dL/dy; dh_final: (batch, H, P, N) or None.
+    Without units, returns a dict of full gradients: dx (batch, L, H, P);
+    dB, dC (batch, L, G, N) (summed over each group's heads); ddt (batch, L, H);
+    dA_log, dD, ddt_bias (H,) (summed over the batch); dh0 (batch, H, P, N).
+    With (b, h) units, returns the per-unit pieces: dx (n, L, P), dB, dC (n, L, N)
+    (that head's share), ddt (n, L), dh0 (n, P, N), dA_log, dD, ddt_bias (n,).
+    """
+    x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final = map(
+        _f32, (x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final))
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert G == ngroups and H % G == 0
+    uu, full = _units(units, batch, H)
+    nu = uu.shape[0]
+    out = dict(dx=np.empty((nu, L, P)), dB=np.empty((nu, L, N)), dC=np.empty((nu, L, N)),
+               ddt=np.empty((nu, L)), dh0=np.empty((nu, P, N)), dA_log=np.empty(nu),
+               dD=np.empty(nu), ddt_bias=np.empty(nu))
+    _load().oracle_ssd_bwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                           _ptr(h0), _ptr(dy), _ptr(dh_final), batch, L, H, P, N, G, flags,
+                           _ptr(uu), nu,
+                           *(_ptr(out[k]) for k in ("dx", "dB", "dC", "ddt", "dh0", "dA_log", "dD",
+                                                    "ddt_bias")),
+                           nthreads or default_threads())
+    if not full:
+        return out
+    hpg = H // G
+    dBu = out["dB"].reshape(batch, H, L, N)
+    dCu = out["dC"].reshape(batch, H, L, N)
+    return dict(
+        dx=out["dx"].reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(),
+        dB=dBu.reshape(batch, G, hpg, L, N).sum(2).transpose(0, 2, 1, 3).copy(),
+        dC=dCu.reshape(batch, G, hpg, L, N).sum(2).transpose(0, 2, 1, 3).copy(),
+        ddt=out["ddt"].reshape(batch, H, L).transpose(0, 2, 1).copy(),
+        dh0=out["dh0"].reshape(batch, H, P, N),
+        dA_log=out["dA_log"].reshape(batch, H).sum(0),
+        dD=out["dD"].reshape(batch, H).sum(0),
+        ddt_bias=out["ddt_bias"].reshape(batch, H).sum(0))
 
 
 def cssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_ZOH | CPLX_STABLE,

@@ -272,11 +272,152 @@ static void cssd_unit(const cssd_job *j, int64_t k)
 /* ------------------------------------------------------------ threads --- */
 
 typedef struct {
-    int kind;               /* 0 S6, 1 SSD, 2 complex */
+    int kind;               /* 0 S6, 1 SSD, 2 complex, 3 SSD backward */
     const void *job;
     int64_t n_units;
     int tid, nthreads;
 } worker_arg;
+
+/* ------------------------------------------------------- SSD backward --- */
+/*
+ * Gradients of a loss L through the SSD recurrence above, given dy = dL/dy
+ * and optionally dh_final = dL/dS_{L-1}: the reverse-time chain rule of the
+ * sequential recurrence (the page's ssd.js pairs its forward with a chunk
+ * backward; this is the plain definition that any such scheme must match).
+ * Per unit (b, h), with G_t = dL/dS_t (P x N):
+ *   G_{L-1} = dh_final + dy_{L-1} (x) C_{L-1};  G_{t-1} = e^{a_t} G_t + dy_{t-1} (x) C_{t-1}
+ *   dx_t[p]  = D dy_t[p] + sigma_t sum_n G_t[p,n] B_t[n]
+ *   dB_t[n] += sigma_t sum_p x_t[p] G_t[p,n]        (summed over the heads of group g)
+ *   dC_t[n] += sum_p dy_t[p] S_t[p,n]              (likewise)
+ *   da_t     = e^{a_t} sum_{p,n} G_t[p,n] S_{t-1}[p,n],  dsigma_t = sum_{p,n} G_t x_t[p] B_t[n]
+ *   ddelta_t = da_t A + dsigma_t dsigma/ddelta,  dA += da_t delta_t + dsigma_t dsigma/dA
+ *   (DT: dsigma/ddelta = 1, dsigma/dA = 0;  ZOH: e^{a}, delta^2 phi1'(a);  ONE: 0, 0)
+ *   ddt_t = ddelta_t sigmoid(dt + dt_bias);  dA_log = A dA;  dD = sum dy x;  dh0 = e^{a_0} G_0
+ * S_{t-1} is re-run from checkpoints every KSEG steps (S_{-1} = h0), so memory
+ * stays at (L/KSEG + KSEG) P N doubles per unit.
+ * Outputs per unit k (double): dx [L][P], dB, dC [L][N] (this head's share),
+ * ddt [L], dh0 [P][N], and the scalars dA_log, dD, ddt_bias of this (b, h).
+ */
+#define SSDB_KSEG 256
+
+typedef struct {
+    const float *x, *dt, *dt_bias, *A_log, *B, *C, *D, *h0, *dy, *dhf;
+    int64_t batch, L, H, P, N, G;
+    uint32_t flags;
+    const int64_t *units;
+    int64_t n_units;
+    double *dx, *dB, *dC, *ddt, *dh0, *dA_log, *dD, *ddtb;
+} ssdb_job;
+
+static double dphi1(double z);
+static double sigm(double x);
+
+static void ssdb_unit(const ssdb_job *j, int64_t k)
+{
+    const int64_t b = j->units[2 * k], hh = j->units[2 * k + 1];
+    const int64_t L = j->L, H = j->H, P = j->P, N = j->N, G = j->G, PN = P * N;
+    const int64_t g = hh * G / H;
+    const int mode = (int)(j->flags & OR_BBAR_MASK);
+    const double A = -exp((double)j->A_log[hh]);
+    const double bias = j->dt_bias ? (double)j->dt_bias[hh] : 0.0;
+    const double Dh = j->D ? (double)j->D[hh] : 0.0;
+    const int64_t nseg = (L + SSDB_KSEG - 1) / SSDB_KSEG;
+    double *ck = (double *)malloc(sizeof(double) * (size_t)(nseg * PN));   /* S entering segment */
+    double *Ss = (double *)malloc(sizeof(double) * (size_t)((SSDB_KSEG + 1) * PN));
+    double *Gm = (double *)malloc(sizeof(double) * (size_t)PN);
+    double *ut = (double *)malloc(sizeof(double) * (size_t)P);
+    /* per-step scalars */
+    #define SSDB_X(t) (j->x + ((b * L + (t)) * H + hh) * P)
+    #define SSDB_B(t) (j->B + ((b * L + (t)) * G + g) * N)
+    #define SSDB_C(t) (j->C + ((b * L + (t)) * G + g) * N)
+    #define SSDB_DY(t) (j->dy + ((b * L + (t)) * H + hh) * P)
+    /* forward: checkpoints */
+    double *S = Ss;
+    for (int64_t i = 0; i < PN; ++i) S[i] = j->h0 ? (double)j->h0[(b * H + hh) * PN + i] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        if (t % SSDB_KSEG == 0) memcpy(ck + (t / SSDB_KSEG) * PN, S, sizeof(double) * (size_t)PN);
+        const double delta = sp((double)j->dt[(b * L + t) * H + hh] + bias);
+        const double a = delta * A;
+        const double sigma = mode == OR_BBAR_DT ? delta : (mode == OR_BBAR_ZOH ? delta * phi1(a) : 1.0);
+        const double dec = exp(a);
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n)
+                S[p * N + n] = dec * S[p * N + n] + sigma * (double)SSDB_X(t)[p] * (double)SSDB_B(t)[n];
+    }
+    /* backward */
+    for (int64_t i = 0; i < PN; ++i) Gm[i] = j->dhf ? (double)j->dhf[(b * H + hh) * PN + i] : 0.0;
+    double dA = 0.0, dD = 0.0, ddtb = 0.0;
+    for (int64_t sgi = nseg - 1; sgi >= 0; --sgi) {
+        const int64_t t0 = sgi * SSDB_KSEG, t1 = (t0 + SSDB_KSEG < L) ? t0 + SSDB_KSEG : L;
+        /* Ss[0] = S_{t0-1}, Ss[i+1] = S_{t0+i} */
+        memcpy(Ss, ck + sgi * PN, sizeof(double) * (size_t)PN);
+        for (int64_t t = t0; t < t1; ++t) {
+            const double delta = sp((double)j->dt[(b * L + t) * H + hh] + bias);
+            const double a = delta * A;
+            const double sigma = mode == OR_BBAR_DT ? delta : (mode == OR_BBAR_ZOH ? delta * phi1(a) : 1.0);
+            const double dec = exp(a);
+            const double *Sp = Ss + (t - t0) * PN;
+            double *Sn = Ss + (t - t0 + 1) * PN;
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t n = 0; n < N; ++n)
+                    Sn[p * N + n] = dec * Sp[p * N + n] + sigma * (double)SSDB_X(t)[p] * (double)SSDB_B(t)[n];
+        }
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+            const double xdt = (double)j->dt[(b * L + t) * H + hh] + bias;
+            const double delta = sp(xdt);
+            const double a = delta * A;
+            double sigma, dsd, dsa;
+            if (mode == OR_BBAR_DT) { sigma = delta; dsd = 1.0; dsa = 0.0; }
+            else if (mode == OR_BBAR_ZOH) { sigma = delta * phi1(a); dsd = exp(a); dsa = delta * delta * dphi1(a); }
+            else { sigma = 1.0; dsd = 0.0; dsa = 0.0; }
+            const double dec = exp(a);
+            const float *xt = SSDB_X(t), *Bt = SSDB_B(t), *Ct = SSDB_C(t), *dyt = SSDB_DY(t);
+            const double *St = Ss + (t - t0 + 1) * PN, *Sprev = Ss + (t - t0) * PN;
+            /* G_t: add this step's output cotangent */
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t n = 0; n < N; ++n) Gm[p * N + n] += (double)dyt[p] * (double)Ct[n];
+            double *dBt = j->dB + (k * L + t) * N, *dCt = j->dC + (k * L + t) * N;
+            for (int64_t n = 0; n < N; ++n) {
+                double sb = 0.0, sc = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    sb += (double)xt[p] * Gm[p * N + n];
+                    sc += (double)dyt[p] * St[p * N + n];
+                }
+                dBt[n] = sigma * sb;
+                dCt[n] = sc;
+            }
+            double dsig = 0.0, da = 0.0;
+            for (int64_t p = 0; p < P; ++p) {
+                double s = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    s += Gm[p * N + n] * (double)Bt[n];
+                    da += Gm[p * N + n] * Sprev[p * N + n];
+                }
+                ut[p] = s;
+                dsig += (double)xt[p] * s;
+                j->dx[(k * L + t) * P + p] = Dh * (double)dyt[p] + sigma * s;
+                dD += (double)dyt[p] * (double)xt[p];
+            }
+            da *= dec;
+            const double ddelta = da * A + dsig * dsd;
+            dA += da * delta + dsig * dsa;
+            const double ddt = ddelta * sigm(xdt);
+            j->ddt[k * L + t] = ddt;
+            ddtb += ddt;
+            /* G_{t-1} part carried from G_t */
+            for (int64_t i = 0; i < PN; ++i) Gm[i] *= dec;
+        }
+    }
+    memcpy(j->dh0 + k * PN, Gm, sizeof(double) * (size_t)PN);
+    j->dA_log[k] = dA * A;
+    j->dD[k] = dD;
+    j->ddtb[k] = ddtb;
+    #undef SSDB_X
+    #undef SSDB_B
+    #undef SSDB_C
+    #undef SSDB_DY
+    free(ck); free(Ss); free(Gm); free(ut);
+}
 
 static void *worker(void *p)
 {
@@ -284,7 +425,8 @@ static void *worker(void *p)
     for (int64_t k = w->tid; k < w->n_units; k += w->nthreads) {
         if (w->kind == 0) s6_unit((const s6_job *)w->job, k);
         else if (w->kind == 1) ssd_unit((const ssd_job *)w->job, k);
-        else cssd_unit((const cssd_job *)w->job, k);
+        else if (w->kind == 2) cssd_unit((const cssd_job *)w->job, k);
+        else ssdb_unit((const ssdb_job *)w->job, k);
     }
     return NULL;
 }
@@ -523,6 +665,19 @@ void oracle_s6_bwd(const float *u, const float *dt, const float *dt_bias, const 
 }
 
 /* elementary functions, exported so the tests can pin them on their own */
+void oracle_ssd_bwd(const float *x, const float *dt, const float *dt_bias, const float *A_log,
+                    const float *B, const float *C, const float *D, const float *h0,
+                    const float *dy, const float *dh_final,
+                    int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                    int64_t ngroups, uint32_t flags, const int64_t *units, int64_t n_units,
+                    double *dx, double *dB, double *dC, double *ddt, double *dh0,
+                    double *dA_log, double *dD, double *ddt_bias, int nthreads)
+{
+    ssdb_job j = {x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, batch, L, nheads, headdim,
+                  d_state, ngroups, flags, units, n_units, dx, dB, dC, ddt, dh0, dA_log, dD, ddt_bias};
+    run_units(3, &j, n_units, nthreads);
+}
+
 double oracle_softplus(double x) { return sp(x); }
 double oracle_phi1(double z) { return phi1(z); }
 double oracle_dphi1(double z) { return dphi1(z); }
