@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (no sparsity), TFLOP/s
+FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 MFMA
 FP32_VALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, non-packed fp32
 # fp32 VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz lane-slots/s (a wave64 op takes 4 cycles)
 VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
@@ -66,6 +67,22 @@ def s6_bwd_model(d):
     return elems, bytes_, ops
 
 
+def ssd_bwd_model(d):
+    """Algorithmic bytes of one SSD backward call (read x, B, C, dt, dy; write dx, ddt, dB, dC)
+    and the fp32 MFMA flops its kernels execute.  Per (batch, head) and 32-step chunk each of
+    the three walks issues 3P/4 + 3N/4 + PN/16 16x16x4 MFMAs (2048 flops each; 656 at P = 64,
+    N = 128), and the two state-only walks PN/32 each over all segments but one."""
+    B, L, H, P, N, G = d["batch"], d["L"], d["nheads"], d["headdim"], d["d_state"], d["ngroups"]
+    elems = B * L * H * P
+    bytes_ = (elems * 2 + 2 * B * L * G * N * 2 + B * L * H * 4 + elems * 4 + elems * 4 +
+              B * L * H * 4 + 2 * B * L * G * N * 4)
+    nseg = d.get("nseg", 1)
+    units = B * H * (-(-L // 32))
+    walk = 3 * P // 4 + 3 * N // 4 + P * N // 16
+    mfmas = units * 3 * walk + units * (P * N // 16) * (nseg - 1) // nseg
+    return elems, bytes_, mfmas * 2048
+
+
 def ssd_model(d):
     B, L, H, P, N, G, Q = (d["batch"], d["L"], d["nheads"], d["headdim"], d["d_state"], d["ngroups"],
                            d["chunk_len"])
@@ -90,6 +107,7 @@ def cssd_model(d):
 
 def make_runner(name, dev):
     """Returns (step_fn(i), dims, kernel names) with N_ROTATE resident input copies."""
+    import numpy as np
     import torch
     import selective_state_space_s6_amd as lib
     import synth
@@ -132,6 +150,28 @@ def make_runner(name, dev):
             lib.ssm_s6_scan_fwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
                                 None, y=y, h_final=hf)
         return step, dims, w, ["s6_scan_kernel"]
+    if kind == "ssd" and bwd:
+        d = dims
+        for r, t in enumerate(copies):
+            rng = np.random.default_rng([5, r])
+            t["dy"] = torch.from_numpy(rng.standard_normal(
+                (d["batch"], d["L"], d["nheads"], d["headdim"]), dtype=np.float32)).to(dev)
+            t["dhf"] = torch.from_numpy(rng.standard_normal(
+                (d["batch"], d["nheads"], d["headdim"], d["d_state"]), dtype=np.float32)).to(dev)
+        ws = torch.empty(lib.ssd_chunk_scan_bwd_workspace_size(
+            d["batch"], d["L"], d["nheads"], d["headdim"], d["d_state"], d["ngroups"], w["chunk_len"]),
+            dtype=torch.uint8, device=dev)
+        out = {}
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            g = lib.ssd_chunk_scan_bwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                       None, t["dy"], t["dhf"], chunk_len=w["chunk_len"],
+                                       out=out or None, workspace=ws)
+            out.update(g)
+        w["kind"] = "ssd_bwd"
+        return step, dims, w, ["ssdb_walk_f", "ssdb_walk_r1", "ssdb_walk_r2", "ssdb_pass_f", "ssdb_pass_r",
+                               "ssdb_reduce_heads", "ssdb_scal", "ssdb_final"]
     if kind == "ssd":
         t0 = copies[0]
         y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
@@ -216,6 +256,15 @@ def cpu_baseline_s6_bwd(name, n_rows=2):
                       f"({elems} elements, fp64, {sec:.2f} s wall)"}
 
 
+def ssd_bwd_nseg(d):
+    """Segments per (batch, head) the SSD backward uses (mirrors its launch plan)."""
+    waves = d["batch"] * d["nheads"] * (d["d_state"] // 32)
+    nseg = max(1, min(-(-3072 // waves), d["L"] // 256))
+    nseg = max(nseg, -(-d["L"] // 512))
+    Ls = -(-(-(-d["L"] // nseg)) // 32) * 32
+    return -(-d["L"] // Ls)
+
+
 def cpu_baseline_units(name, n_units):
     """The fp64 oracle on a bounded sample of (b, h) units of an SSD-type workload."""
     import numpy as np
@@ -257,6 +306,8 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = s6_model(dims)
     elif kind == "s6_bwd":
         elems, bytes_, ops = s6_bwd_model(dims)
+    elif kind == "ssd_bwd":
+        elems, bytes_, ops = ssd_bwd_model(dict(dims, nseg=ssd_bwd_nseg(dims)))
     elif kind == "ssd":
         elems, bytes_, ops = ssd_model(dims)
     else:
@@ -323,7 +374,7 @@ def main():
     if not args.no_secondary and args.workload == "s6_mamba1":
         sec = []
         for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
-                            ("s6_mamba1_bwd", 10)):
+                            ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
             es = s["event_ms_median"] * 1e-3
@@ -333,6 +384,10 @@ def main():
                    "hbm_frac": round(s["bytes"] / es / 1e9 / HBM_PEAK_GBS, 4)}
             if s["kind"] == "s6_bwd":
                 ent["fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
+                ent["kernel_ms"] = round(s["event_ms_median"], 4)
+            elif s["kind"] == "ssd_bwd":
+                ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
+                ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
                 ent["kernel_ms"] = round(s["event_ms_median"], 4)
             elif s["kind"] == "ssd":
                 ent["mfma_TFLOPs"] = round(s["ops"] / es / 1e12, 1)

@@ -185,6 +185,46 @@ int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, con
                        int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* -------------------------------------------------------- SSD backward ----
+ * Gradients of a scalar loss through the SSD scan above, given dy = dL/dy and
+ * optionally dh_final = dL/dh_final: the reverse-time chain rule of the
+ * recurrence [BF-SSD ssd_chunk_forward; the page's per-chunk backward,
+ * ssd_chunk_backward, completed with the carry from later chunks].  With
+ * G_t = dL/dS_t (G_{L-1} = dh_final + dy_{L-1} (x) C_{L-1}, G_t = e^{a_{t+1}} G_{t+1} + dy_t (x) C_t):
+ *   dx[b,t,h,p] = D[h] dy + sigma_t sum_n G_t[p,n] B[b,t,g,n]
+ *   dB[b,t,g,n] = sum over the group's heads of sigma_t sum_p x[b,t,h,p] G_t[p,n]
+ *   dC[b,t,g,n] = sum over the group's heads of sum_p dy[b,t,h,p] S_t[p,n]
+ *   ddt[b,t,h]  = sigmoid(dt + dt_bias) (da_t A + dsigma_t dsigma/ddelta),
+ *                 da_t = e^{a_t} sum_{p,n} G_t S_{t-1},  dsigma_t = sum_{p,n} G_t x_t[p] B_t[n]
+ *   dA_log[h]   = A sum_{b,t} (da_t delta_t + dsigma_t dsigma/dA)
+ *   dD[h] = sum dy x,   ddt_bias[h] = sum ddt,   dh0 = e^{a_0} G_0
+ *
+ * Inputs: those of ssd_chunk_scan_fwd (same layouts, bf16 x, B, C; flags as
+ * there), plus dy (batch, L, nheads, headdim) fp32 and dh_final
+ * (batch, nheads, headdim, d_state) fp32 or NULL.
+ * Outputs (fp32, caller-owned, fully overwritten): dx (batch, L, nheads, headdim);
+ * ddt (batch, L, nheads); dB, dC (batch, L, ngroups, d_state); dA_log, dD,
+ * ddt_bias (nheads); dh0 (batch, nheads, headdim, d_state).  dD, ddt_bias and
+ * dh0 may be NULL (not written); the others are required.  No output may
+ * alias an input or another output.
+ * Limits: nheads % ngroups == 0; headdim in {32, 64, 128}; d_state in
+ * {32, 64, 128}; chunk_len in {64, 128, 256} (checked; the kernels use their
+ * own 32-step chunks).  in_dtype must be SSM_BF16.
+ * Workspace: ssd_chunk_scan_bwd_workspace_size() bytes, 16-byte aligned, owned
+ * by the caller: segment states in both directions, each head's share of dB
+ * and dC (2 * batch * L * nheads * d_state fp32) and per-step scalars. */
+size_t ssd_chunk_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                         int64_t d_state, int64_t ngroups, int64_t chunk_len);
+
+int ssd_chunk_scan_bwd(const void *x, const float *dt, const float *dt_bias, const float *A_log,
+                       const void *B, const void *C, const float *D, const float *h0,
+                       const float *dy, const float *dh_final,
+                       float *dx, float *ddt, float *dB, float *dC, float *dA_log,
+                       float *dD, float *ddt_bias, float *dh0,
+                       int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                       int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* --------------------------------------------------------- complex SSD ----
  * Mamba-3-style SSD with a complex diagonal state [BF-CSSD header,
  * et_bbar_re/et_bbar_im, complex_ssd_forward]:

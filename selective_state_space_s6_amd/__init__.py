@@ -16,8 +16,9 @@ import os
 import torch
 
 __all__ = [
-    "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssd_chunk_scan_fwd", "ssd_cplx_chunk_scan_fwd",
-    "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
+    "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssd_chunk_scan_fwd", "ssd_chunk_scan_bwd",
+    "ssd_cplx_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size",
+    "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
     "ssd_cplx_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
     "SSM_BBAR_ZOH", "SSM_BBAR_DT", "SSM_BBAR_ONE", "SSM_CPLX_STABLE", "SSM_CPLX_DOC",
     "SSM_CPLX_CODE", "SSM_CPLX_CONJ_C", "SSM_F32", "SSM_BF16",
@@ -48,6 +49,10 @@ _lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
 _lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
+_lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [_I] * 7
+_lib.ssd_chunk_scan_bwd_workspace_size.restype = _Z
+_lib.ssd_chunk_scan_bwd.argtypes = [_P] * 18 + [_I] * 7 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
+_lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_cplx_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_uint32, _P, _Z, _P]
@@ -115,6 +120,11 @@ def ssm_s6_scan_bwd_workspace_size(batch, L, d_inner, d_state) -> int:
 
 def ssd_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups, chunk_len) -> int:
     return int(_lib.ssd_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups,
+                                                      chunk_len))
+
+
+def ssd_chunk_scan_bwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups, chunk_len) -> int:
+    return int(_lib.ssd_chunk_scan_bwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups,
                                                       chunk_len))
 
 
@@ -233,6 +243,52 @@ def ssd_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=256
                                  workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y
+
+
+_SSD_GRADS = ("dx", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")
+
+
+def ssd_chunk_scan_bwd(x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, *, chunk_len=256,
+                       flags=SSM_BBAR_DT, out=None, workspace=None):
+    """Gradients of the SSD forward scan.  Inputs as ssd_chunk_scan_fwd (bf16 x, B, C),
+    plus dy (batch, L, H, P) fp32 and dh_final (batch, H, P, N) fp32 or None.
+    Returns a dict of fp32 tensors: dx (batch, L, H, P); ddt (batch, L, H);
+    dB, dC (batch, L, G, N); dA_log, dD, ddt_bias (H,); dh0 (batch, H, P, N).
+    `out` may hold preallocated tensors under those names; `workspace` a uint8
+    tensor of ssd_chunk_scan_bwd_workspace_size bytes."""
+    dev = x.device
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dty = x.dtype
+    _req(x, "x", dty, (batch, L, H, P), dev)
+    _req(dt, "dt", torch.float32, (batch, L, H), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    _req(A_log, "A_log", torch.float32, (H,), dev)
+    _req(B, "B", dty, (batch, L, G, N), dev)
+    _req(C, "C", dty, (batch, L, G, N), dev)
+    _opt(D, "D", torch.float32, (H,), dev)
+    _opt(h0, "h0", torch.float32, (batch, H, P, N), dev)
+    _req(dy, "dy", torch.float32, (batch, L, H, P), dev)
+    _opt(dh_final, "dh_final", torch.float32, (batch, H, P, N), dev)
+    shapes = dict(dx=(batch, L, H, P), ddt=(batch, L, H), dB=(batch, L, G, N), dC=(batch, L, G, N),
+                  dA_log=(H,), dD=(H,), ddt_bias=(H,), dh0=(batch, H, P, N))
+    g = dict(out or {})
+    for k in _SSD_GRADS:
+        if g.get(k) is None:
+            g[k] = torch.empty(shapes[k], dtype=torch.float32, device=dev)
+        _req(g[k], k, torch.float32, shapes[k], dev)
+    need = ssd_chunk_scan_bwd_workspace_size(batch, L, H, P, N, G, chunk_len)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    rc = _lib.ssd_chunk_scan_bwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                                 *(_ptr(g[k]) for k in _SSD_GRADS), batch, L, H, P, N, G, chunk_len,
+                                 _in_dtype(x), flags, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return g
 
 
 def ssd_cplx_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=64,

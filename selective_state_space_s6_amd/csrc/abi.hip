@@ -206,6 +206,68 @@ int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, con
     return launched(E, ssm::launch_ssd(a, stream, &kn), kn);
 }
 
+size_t ssd_chunk_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                         int64_t d_state, int64_t ngroups, int64_t chunk_len) {
+    (void)ngroups; (void)chunk_len;
+    if (batch <= 0 || L <= 0 || nheads <= 0 || headdim <= 0 || d_state <= 0) return 0;
+    return ssm::ssd_bwd_workspace_bytes(batch, L, nheads, headdim, d_state);
+}
+
+int ssd_chunk_scan_bwd(const void *x, const float *dt, const float *dt_bias, const float *A_log,
+                       const void *B, const void *C, const float *D, const float *h0,
+                       const float *dy, const float *dh_final,
+                       float *dx, float *ddt, float *dB, float *dC, float *dA_log,
+                       float *dD, float *ddt_bias, float *dh0,
+                       int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                       int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssd_chunk_scan_bwd";
+    REQUIRE_PTR(E, x); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
+    REQUIRE_PTR(E, C); REQUIRE_PTR(E, dy);
+    REQUIRE_PTR(E, dx); REQUIRE_PTR(E, ddt); REQUIRE_PTR(E, dB); REQUIRE_PTR(E, dC);
+    REQUIRE_PTR(E, dA_log);
+    int rc = ssd_check_shape(E, batch, L, nheads, headdim, d_state, ngroups, chunk_len);
+    if (rc != SSM_OK) return rc;
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if (in_dtype != SSM_BF16)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: x, B, C must be bf16 (SSM_BF16)", E);
+    if ((flags & ~0x3u) != 0 || (flags & 0x3u) == 0x3u)
+        return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x: only SSM_BBAR_ZOH/DT/ONE apply", E, flags);
+    if (!(headdim == 32 || headdim == 64 || headdim == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: headdim %lld not in {32, 64, 128}", E, (long long)headdim);
+    if (!(d_state == 32 || d_state == 64 || d_state == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld not in {32, 64, 128}", E, (long long)d_state);
+    if (!(chunk_len == 64 || chunk_len == 128 || chunk_len == 256))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: chunk_len %lld not in {64, 128, 256}", E, (long long)chunk_len);
+    if (batch * nheads * ((L + 31) / 32) > 0x7fffffffLL)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    REQUIRE_ALIGN(E, x); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
+    REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, h0);
+    REQUIRE_ALIGN(E, dy); REQUIRE_ALIGN(E, dh_final);
+    REQUIRE_ALIGN(E, dx); REQUIRE_ALIGN(E, ddt); REQUIRE_ALIGN(E, dB); REQUIRE_ALIGN(E, dC);
+    REQUIRE_ALIGN(E, dA_log); REQUIRE_ALIGN(E, dD); REQUIRE_ALIGN(E, ddt_bias); REQUIRE_ALIGN(E, dh0);
+    REQUIRE_ALIGN(E, workspace);
+    const void *ins[] = {x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, workspace};
+    const void *outs[] = {dx, ddt, dB, dC, dA_log, dD, ddt_bias, dh0};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        if (outs[i] == nullptr) continue;
+        for (size_t j = 0; j < sizeof(ins) / sizeof(ins[0]); ++j)
+            if (outs[i] == ins[j]) return fail(SSM_ERR_INVALID_ARG, "%s: an output aliases an input", E);
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (outs[i] == outs[j]) return fail(SSM_ERR_INVALID_ARG, "%s: two outputs alias", E);
+    }
+    const size_t need = ssm::ssd_bwd_workspace_bytes(batch, L, nheads, headdim, d_state);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    ssm::SsdBwdArgs a{x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final,
+                      dx, ddt, dB, dC, dA_log, dD, ddt_bias, dh0,
+                      batch, L, nheads, headdim, d_state, ngroups, flags, workspace};
+    const char *kn = "ssd_bwd";
+    return launched(E, ssm::launch_ssd_bwd(a, stream, &kn), kn);
+}
+
 size_t ssd_cplx_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads,
                                               int64_t headdim, int64_t n_complex, int64_t ngroups,
                                               int64_t chunk_len) {

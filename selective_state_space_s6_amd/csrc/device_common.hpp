@@ -56,6 +56,22 @@ __device__ __forceinline__ float row_bcast(float v) {
                                                                  0x150 + K, 0xf, 0xf, true));
 }
 
+// Inclusive prefix sum over each 32-lane half of a wave with DPP: row_shr 1,
+// 2, 4, 8 with zero fill scans each 16-lane row, then row_bcast:15 adds the
+// last lane of rows 0 and 2 to rows 1 and 3.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float scan32(float v) {
+    v += dpp_f<0x111>(v);
+    v += dpp_f<0x112>(v);
+    v += dpp_f<0x114>(v);
+    v += dpp_f<0x118>(v);
+    v += dpp_f<0x142, 0xa>(v);
+    return v;
+}
+
 // Block index -> work index such that consecutive work indices land on the
 // same XCD (blocks are dealt round-robin over the 8 XCDs of an MI355X).
 __device__ __forceinline__ int64_t xcd_swizzle(int64_t bid, int64_t nblk) {

@@ -35,6 +35,19 @@ struct SsdArgs {
     bool bf16; uint32_t flags;
     void *workspace;
 };
+struct SsdBwdArgs {
+    const void *x; const float *dt; const float *dt_bias; const float *A_log;
+    const void *B; const void *C; const float *D; const float *h0;
+    const float *dy; const float *dh_final;
+    float *dx, *ddt, *dB, *dC, *dA_log, *dD, *ddt_bias, *dh0;
+    int64_t batch, L, nheads, headdim, d_state, ngroups;
+    uint32_t flags;
+    void *workspace;
+};
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                               int64_t d_state);
+hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t stream, const char **kernel_name);
+
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                            int64_t d_state, int64_t chunk_len);
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_name);

@@ -1,0 +1,881 @@
+// ssd_bwd.hip -- backward pass of the Mamba-2 SSD scan, gfx950.
+//
+// Gradients of a loss through the scalar-A-per-head recurrence of
+// builderforce-memory-engine ssd.js (header comment, ssd_chunk_forward; the
+// same package pairs it with a per-chunk backward, ssd_chunk_backward), given
+// dy = dL/dy and optionally dh_final = dL/dS_{L-1}.  With G_t = dL/dS_t
+// (P x N per (batch, head)):
+//   G_t = e^{a_{t+1}} G_{t+1} + dy_t (x) C_t          (G after the last step: dh_final)
+//   dx_t  = D dy_t + sigma_t G_t B_t                  dB_t = sigma_t x_t G_t   (summed over
+//   dC_t  = dy_t S_t                                  the heads of the group)
+//   dh0   = e^{a_0} G_0
+// The decay and input-scale gradients come from per-step scalars: with
+// cs_t = sum_{k<=t} a_k,
+//   dL/dcs_t = dy_t . y_t - x_t . dx_t  (+ <dh_final, h_final> at t = L-1)
+//            = C_t . (dy_t S_t) - sigma_t x_t . (G_t B_t)   (the D terms cancel exactly), and
+//   da_t = sum_{t' >= t} dL/dcs_t',   dsigma_t = x_t . (G_t B_t)
+//   ddelta_t = da_t A + dsigma_t dsigma/ddelta,  dA = sum da_t delta_t + dsigma_t dsigma/dA.
+//
+// The sequence of every (batch, head) is cut into segments as in the forward.
+// Three walk kernels run over a segment's 32-step chunks with a state in fp32
+// MFMA accumulators (v_mfma_f32_16x16x4_f32; every product is exact in fp32):
+//   ssdb_walk_f   forward, state S[p][n] (a wave owns 32 columns n):
+//                 dC_t = e^{cs_t} dy_t S_in + ((dY X^T) o L) B, the head's share
+//   ssdb_walk_r1  backward, state G[p][n] (a wave owns 32 columns n):
+//                 dB_t = sigma_t (e^{cs_end-cs_t} x_t G_in + ((X dY^T) o E) C)
+//   ssdb_walk_r2  backward, state G^T[n][p] (a wave owns 16 columns p):
+//                 u_t = e^{cs_end-cs_t} B_t G_in^T + ((B C^T) o E) dY;  dx = sigma u + D dy
+// with L[t,s] = e^{cs_t-cs_s} sigma_s (s <= t) and E[t,t'] = e^{cs_t'-cs_t} (t' >= t).
+// In each the accumulator's row index is the contraction index of the
+// product that reads it, so it feeds the matrix core without a transpose.
+// State-only variants of walk_f and walk_r1 give the segments' own states;
+// ssdb_pass_f / ssdb_pass_r turn them into the states entering each segment
+// from the left (S) and from the right (G), and ssdb_bnd dots them into the
+// exact dL/da at every segment boundary.  ssdb_reduce_heads adds the heads'
+// dB, dC shares per group; ssdb_scal runs the reverse sum of dL/dcs over each
+// segment from the next boundary's exact value (segments are at most 512 steps,
+// which bounds the rounding that sum gathers) and the chain rule for dt,
+// A_log, D, dt_bias; ssdb_final adds those over batch and segments.  Every sum
+// runs in a fixed order.
+#include "device_common.hpp"
+#include "launchers.hpp"
+#include <algorithm>
+
+namespace ssm {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQ = 32;              // steps per chunk
+constexpr int kTargetWaves = 3072;  // resident waves wanted (3 per SIMD)
+constexpr int kMinSeg = 256;        // shortest segment worth a state round trip
+constexpr int kMaxSeg = 512;        // longest segment: bounds the reverse sum behind each ddt
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+struct SbKp {
+    const uint16_t *x; const float *dt; const float *dt_bias; const float *A_log;
+    const uint16_t *B; const uint16_t *C; const float *D; const float *h0;
+    const float *dy; const float *dhf;
+    float *dx, *ddt, *dB, *dC, *dA_log, *dD, *ddt_bias, *dh0;
+    float *Sseg, *Gseg, *dec;          // (batch, H, nseg, P, N) x2, (batch, H, nseg)
+    float *dBh, *dCh;                  // (batch, L, H, N): each head's share
+    float *dyy, *dsig, *dyx;           // (batch, L, H)
+    float *hfdot;                      // (batch, H)
+    double *bnd;                       // (batch, H, nseg): exact dL/da at each segment's first step
+    float *pA, *pD, *pT;               // (batch, nseg, H) partial sums
+    int64_t batch, L, H, P, N, G, Ls, nseg;
+    int mode;                          // 0 ZOH, 1 DT, 2 ONE
+};
+
+__device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// per-chunk scalars in LDS
+struct Scal {
+    float cs[kQ];     // inclusive cumulative sum of a from the chunk start
+    float sig[kQ];    // input scale
+    float ecs[kQ];    // e^{cs_t}
+    float eme[kQ];    // e^{cs_end - cs_t}
+    float csend;
+};
+
+// One wave: lanes 0..31 hold steps t0..t0+31 (steps at or past te carry a = 0, sigma = 0).
+__device__ __forceinline__ void chunk_scalars(Scal &sc, const SbKp &p, int64_t b, int64_t h,
+                                              int64_t t0, int64_t te, float bias, float A, int lane) {
+    const int64_t t = t0 + (lane & 31);
+    float a = 0.0f, sg = 0.0f;
+    if (lane < kQ && t < te) {
+        const float dl = softplus(p.dt[(b * p.L + t) * p.H + h] + bias);
+        a = dl * A;
+        sg = p.mode == 1 ? dl : (p.mode == 0 ? (a == 0.0f ? dl : dl * (expm1f(a) / a)) : 1.0f);
+    }
+    const float v = scan32(a);
+    const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    if (lane < kQ) {
+        sc.cs[lane] = v;
+        sc.sig[lane] = sg;
+        sc.ecs[lane] = __expf(v);
+        sc.eme[lane] = __expf(cend - v);
+    }
+    if (lane == 0) sc.csend = cend;
+}
+
+// Sum over the 16 lanes of each DPP row; the total lands in lane 15 of the row.
+__device__ __forceinline__ float row_total16(float v) {
+    v += dpp_f<0x111>(v);
+    v += dpp_f<0x112>(v);
+    v += dpp_f<0x114>(v);
+    v += dpp_f<0x118>(v);
+    return v;
+}
+
+// stage rows t0..t0+31 of a (batch, L, R, COLS) tensor slice (row index rr) into LDS as fp32;
+// rows at or past te are zero.  COLS is a multiple of 4.
+template <int COLS, int PITCH>
+__device__ __forceinline__ void stage_bf16(float (*dst)[PITCH], const uint16_t *src, int64_t b, int64_t L,
+                                           int64_t R, int64_t rr, int64_t t0, int64_t te, int tid, int nthr) {
+    constexpr int Q4 = COLS / 4;
+    for (int i = tid; i < kQ * Q4; i += nthr) {
+        const int tr = i / Q4, c4 = (i % Q4) * 4;
+        const int64_t t = t0 + tr;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < te) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(src + ((b * L + t) * R + rr) * COLS + c4);
+            v = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+        }
+        *reinterpret_cast<float4 *>(&dst[tr][c4]) = v;
+    }
+}
+template <int COLS, int PITCH>
+__device__ __forceinline__ void stage_f32(float (*dst)[PITCH], const float *src, int64_t b, int64_t L,
+                                          int64_t R, int64_t rr, int64_t t0, int64_t te, int tid, int nthr) {
+    constexpr int Q4 = COLS / 4;
+    for (int i = tid; i < kQ * Q4; i += nthr) {
+        const int tr = i / Q4, c4 = (i % Q4) * 4;
+        const int64_t t = t0 + tr;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < te) v = *reinterpret_cast<const float4 *>(src + ((b * L + t) * R + rr) * COLS + c4);
+        *reinterpret_cast<float4 *>(&dst[tr][c4]) = v;
+    }
+}
+
+__device__ __forceinline__ int64_t seg_off(const SbKp &p, int64_t b, int64_t h, int64_t k) {
+    return ((b * p.H + h) * p.nseg + k) * p.P * p.N;
+}
+
+// ------------------------------------------------------------------ walk F
+// STATE: segments 0..nseg-2 from a zero state, writing their own final states
+// and decays.  Otherwise: every segment from its entering state, writing the
+// head's dC share, the per-step scalar C_t . dC_t, and <dh_final, h_final>.
+template <int P, int N, bool STATE>
+__global__ void __launch_bounds__(64 * (N / 32))
+ssdb_walk_f(SbKp p) {
+    constexpr int NW = N / 32, PT = P / 16, NTH = 64 * NW;
+    __shared__ __attribute__((aligned(16))) float sX[kQ][P + 4];
+    __shared__ __attribute__((aligned(16))) float sY[STATE ? 1 : kQ][P + 4];
+    __shared__ __attribute__((aligned(16))) float sB[kQ][N + 4];
+    __shared__ __attribute__((aligned(16))) float sM[STATE ? 1 : kQ][kQ + 4];
+    __shared__ float sRed[NW][kQ];
+    __shared__ Scal sc;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane >> 4, c16 = lane & 15;
+    const int64_t nsl = STATE ? p.nseg - 1 : p.nseg;
+    const int64_t k = blockIdx.x % nsl, bh = blockIdx.x / nsl;
+    const int64_t b = bh / p.H, h = bh % p.H, g = h * p.G / p.H;
+    const int64_t T0 = k * p.Ls, T1 = min(T0 + p.Ls, p.L);
+    const float A = -expf(p.A_log[h]);
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+
+    // S tile (pt, nt): rows p = 16 pt + 4 r + v, column n = 32 w + 16 nt + c16
+    f32x4 S[PT][2];
+    {
+        const float *src = nullptr;
+        if constexpr (!STATE) src = k == 0 ? p.h0 + (p.h0 ? (b * p.H + h) * P * N : 0) : p.Sseg + seg_off(p, b, h, k);
+        if (k == 0 && !p.h0) src = nullptr;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    S[pt][nt][v] = src ? src[(16 * pt + 4 * r + v) * N + 32 * w + 16 * nt + c16] : 0.0f;
+    }
+    float sumA = 0.0f;
+    for (int64_t t0 = T0; t0 < T1; t0 += kQ) {
+        stage_bf16<P, P + 4>(sX, p.x, b, p.L, p.H, h, t0, T1, tid, NTH);
+        stage_bf16<N, N + 4>(sB, p.B, b, p.L, p.G, g, t0, T1, tid, NTH);
+        if constexpr (!STATE) stage_f32<P, P + 4>(sY, p.dy, b, p.L, p.H, h, t0, T1, tid, NTH);
+        if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane);
+        __syncthreads();
+        const float csend = sc.csend;
+        if constexpr (!STATE) {
+            // (dY X^T) o L, lower-triangular tiles (0,0), (1,0), (1,1) of [t][s]
+            for (int tau = w; tau < 3; tau += NW) {
+                const int ti = tau == 0 ? 0 : 1, si = tau == 2 ? 1 : 0;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(&sY[16 * ti + c16][16 * pt + 4 * r]);
+                    const float4 b4 = *reinterpret_cast<const float4 *>(&sX[16 * si + c16][16 * pt + 4 * r]);
+                    acc = mfma4(a4.x, b4.x, acc);
+                    acc = mfma4(a4.y, b4.y, acc);
+                    acc = mfma4(a4.z, b4.z, acc);
+                    acc = mfma4(a4.w, b4.w, acc);
+                }
+                const int s = 16 * si + c16;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int t = 16 * ti + 4 * r + v;
+                    sM[t][s] = s <= t ? acc[v] * __expf(sc.cs[t] - sc.cs[s]) * sc.sig[s] : 0.0f;
+                }
+            }
+            __syncthreads();
+            // dC tiles (ti, nt): state part scaled by e^{cs_t}, then the intra-chunk part
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) {
+                float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const float4 a4 = *reinterpret_cast<const float4 *>(&sY[16 * ti + c16][16 * pt + 4 * r]);
+                        acc = mfma4(a4.x, S[pt][nt][0], acc);
+                        acc = mfma4(a4.y, S[pt][nt][1], acc);
+                        acc = mfma4(a4.z, S[pt][nt][2], acc);
+                        acc = mfma4(a4.w, S[pt][nt][3], acc);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] *= sc.ecs[16 * ti + 4 * r + v];
+                    const int n = 32 * w + 16 * nt + c16;
+#pragma unroll
+                    for (int si = 0; si <= ti; ++si) {
+                        const float4 a4 = *reinterpret_cast<const float4 *>(&sM[16 * ti + c16][16 * si + 4 * r]);
+                        acc = mfma4(a4.x, sB[16 * si + 4 * r + 0][n], acc);
+                        acc = mfma4(a4.y, sB[16 * si + 4 * r + 1][n], acc);
+                        acc = mfma4(a4.z, sB[16 * si + 4 * r + 2][n], acc);
+                        acc = mfma4(a4.w, sB[16 * si + 4 * r + 3][n], acc);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int64_t t = t0 + 16 * ti + 4 * r + v;
+                        if (t < T1) {
+                            p.dCh[((b * p.L + t) * p.H + h) * N + n] = acc[v];
+                            part[v] += bf(p.C[((b * p.L + t) * p.G + g) * N + n]) * acc[v];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float tot = row_total16(part[v]);
+                    if (c16 == 15) sRed[w][16 * ti + 4 * r + v] = tot;
+                }
+            }
+        }
+        // S <- e^{cs_end} S + X^T (w o B), w_s = e^{cs_end - cs_s} sigma_s
+        const float eend = __expf(csend);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) S[pt][nt] *= eend;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int s = 16 * st + 4 * r + v;
+                const float ws = sc.eme[s] * sc.sig[s];
+                const float b0 = sB[s][32 * w + c16] * ws, b1 = sB[s][32 * w + 16 + c16] * ws;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const float a = sX[s][16 * pt + c16];
+                    S[pt][0] = mfma4(a, b0, S[pt][0]);
+                    S[pt][1] = mfma4(a, b1, S[pt][1]);
+                }
+            }
+        sumA += csend;
+        __syncthreads();
+        if constexpr (!STATE) {
+            if (tid < kQ && t0 + tid < T1) {
+                float s = 0.0f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) s += sRed[ww][tid];
+                p.dyy[(b * p.L + t0 + tid) * p.H + h] = s;
+            }
+        }
+    }
+    if constexpr (STATE) {
+        float *dst = p.Sseg + seg_off(p, b, h, k);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dst[(16 * pt + 4 * r + v) * N + 32 * w + 16 * nt + c16] = S[pt][nt][v];
+        if (tid == 0) p.dec[(b * p.H + h) * p.nseg + k] = expf(sumA);
+    } else {
+        if (k == p.nseg - 1) {
+            // <dh_final, h_final>
+            float part = 0.0f;
+            if (p.dhf) {
+                const float *src = p.dhf + (b * p.H + h) * P * N;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            part += src[(16 * pt + 4 * r + v) * N + 32 * w + 16 * nt + c16] * S[pt][nt][v];
+            }
+            // wave total (lanes in a fixed order), then over waves; sRed may still
+            // be read for the last chunk's per-step sums until every wave is here
+            part = row_total16(part);
+            __syncthreads();
+            if (c16 == 15) sRed[w][r] = part;
+            __syncthreads();
+            if (tid == 0) {
+                float s = 0.0f;
+                for (int ww = 0; ww < NW; ++ww)
+                    for (int rr = 0; rr < 4; ++rr) s += sRed[ww][rr];
+                p.hfdot[b * p.H + h] = s;
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------- walk R1
+// STATE: segments 1..nseg-1 backward from a zero gradient, writing their own
+// gradient states (and the last segment's decay).  Otherwise: every segment
+// backward from the gradient entering from the right, writing the head's dB
+// share and, at the start of the sequence, dh0.
+template <int P, int N, bool STATE>
+__global__ void __launch_bounds__(64 * (N / 32))
+ssdb_walk_r1(SbKp p) {
+    constexpr int NW = N / 32, PT = P / 16, NTH = 64 * NW;
+    __shared__ __attribute__((aligned(16))) float sX[STATE ? 1 : kQ][P + 4];
+    __shared__ __attribute__((aligned(16))) float sY[kQ][P + 4];
+    __shared__ __attribute__((aligned(16))) float sC[kQ][N + 4];
+    __shared__ __attribute__((aligned(16))) float sM[STATE ? 1 : kQ][kQ + 4];
+    __shared__ Scal sc;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane >> 4, c16 = lane & 15;
+    const int64_t nsl = STATE ? p.nseg - 1 : p.nseg;
+    const int64_t k = (STATE ? 1 : 0) + blockIdx.x % nsl, bh = blockIdx.x / nsl;
+    const int64_t b = bh / p.H, h = bh % p.H, g = h * p.G / p.H;
+    const int64_t T0 = k * p.Ls, T1 = min(T0 + p.Ls, p.L);
+    const float A = -expf(p.A_log[h]);
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+
+    // G tile (pt, nt): rows p = 16 pt + 4 r + v, column n = 32 w + 16 nt + c16
+    f32x4 Gs[PT][2];
+    {
+        const float *src = nullptr;
+        if constexpr (!STATE) {
+            if (k == p.nseg - 1) src = p.dhf ? p.dhf + (b * p.H + h) * P * N : nullptr;
+            else src = p.Gseg + seg_off(p, b, h, k);
+        }
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    Gs[pt][nt][v] = src ? src[(16 * pt + 4 * r + v) * N + 32 * w + 16 * nt + c16] : 0.0f;
+    }
+    float sumA = 0.0f;
+    const int64_t nch = (T1 - T0 + kQ - 1) / kQ;
+    for (int64_t ci = nch - 1; ci >= 0; --ci) {
+        const int64_t t0 = T0 + ci * kQ;
+        stage_f32<P, P + 4>(sY, p.dy, b, p.L, p.H, h, t0, T1, tid, NTH);
+        stage_bf16<N, N + 4>(sC, p.C, b, p.L, p.G, g, t0, T1, tid, NTH);
+        if constexpr (!STATE) stage_bf16<P, P + 4>(sX, p.x, b, p.L, p.H, h, t0, T1, tid, NTH);
+        if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane);
+        __syncthreads();
+        const float csend = sc.csend;
+        if constexpr (!STATE) {
+            // (X dY^T) o E, upper-triangular tiles (0,0), (0,1), (1,1) of [t][t']
+            for (int tau = w; tau < 3; tau += NW) {
+                const int ti = tau == 2 ? 1 : 0, tj = tau == 0 ? 0 : 1;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(&sX[16 * ti + c16][16 * pt + 4 * r]);
+                    const float4 b4 = *reinterpret_cast<const float4 *>(&sY[16 * tj + c16][16 * pt + 4 * r]);
+                    acc = mfma4(a4.x, b4.x, acc);
+                    acc = mfma4(a4.y, b4.y, acc);
+                    acc = mfma4(a4.z, b4.z, acc);
+                    acc = mfma4(a4.w, b4.w, acc);
+                }
+                const int tp = 16 * tj + c16;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int t = 16 * ti + 4 * r + v;
+                    sM[t][tp] = tp >= t ? acc[v] * __expf(sc.cs[tp] - sc.cs[t]) : 0.0f;
+                }
+            }
+            __syncthreads();
+            // dB tiles (ti, nt)
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const float4 a4 = *reinterpret_cast<const float4 *>(&sX[16 * ti + c16][16 * pt + 4 * r]);
+                        acc = mfma4(a4.x, Gs[pt][nt][0], acc);
+                        acc = mfma4(a4.y, Gs[pt][nt][1], acc);
+                        acc = mfma4(a4.z, Gs[pt][nt][2], acc);
+                        acc = mfma4(a4.w, Gs[pt][nt][3], acc);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] *= sc.eme[16 * ti + 4 * r + v];
+                    const int n = 32 * w + 16 * nt + c16;
+#pragma unroll
+                    for (int tj = ti; tj < 2; ++tj) {
+                        const float4 a4 = *reinterpret_cast<const float4 *>(&sM[16 * ti + c16][16 * tj + 4 * r]);
+                        acc = mfma4(a4.x, sC[16 * tj + 4 * r + 0][n], acc);
+                        acc = mfma4(a4.y, sC[16 * tj + 4 * r + 1][n], acc);
+                        acc = mfma4(a4.z, sC[16 * tj + 4 * r + 2][n], acc);
+                        acc = mfma4(a4.w, sC[16 * tj + 4 * r + 3][n], acc);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int tl = 16 * ti + 4 * r + v;
+                        const int64_t t = t0 + tl;
+                        if (t < T1) p.dBh[((b * p.L + t) * p.H + h) * N + n] = acc[v] * sc.sig[tl];
+                    }
+                }
+        }
+        // G <- e^{cs_end} G + (e^{cs} o dY)^T C
+        const float eend = __expf(csend);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) Gs[pt][nt] *= eend;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int s = 16 * st + 4 * r + v;
+                const float es = sc.ecs[s];
+                const float b0 = sC[s][32 * w + c16], b1 = sC[s][32 * w + 16 + c16];
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const float a = sY[s][16 * pt + c16] * es;
+                    Gs[pt][0] = mfma4(a, b0, Gs[pt][0]);
+                    Gs[pt][1] = mfma4(a, b1, Gs[pt][1]);
+                }
+            }
+        sumA += csend;
+        __syncthreads();
+    }
+    if constexpr (STATE) {
+        float *dst = p.Gseg + seg_off(p, b, h, k);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dst[(16 * pt + 4 * r + v) * N + 32 * w + 16 * nt + c16] = Gs[pt][nt][v];
+        if (tid == 0 && k == p.nseg - 1) p.dec[(b * p.H + h) * p.nseg + k] = expf(sumA);
+    } else if (k == 0 && p.dh0) {
+        float *dst = p.dh0 + (b * p.H + h) * P * N;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dst[(16 * pt + 4 * r + v) * N + 32 * w + 16 * nt + c16] = Gs[pt][nt][v];
+    }
+}
+
+// ----------------------------------------------------------------- walk R2
+// Every segment backward from the gradient entering from the right, with the
+// gradient held transposed (G^T[n][p]; a wave owns 16 columns p): writes dx
+// and the per-step scalars x . u and dy . x.
+template <int P, int N>
+__global__ void __launch_bounds__(64 * (P / 16))
+ssdb_walk_r2(SbKp p) {
+    constexpr int NW = P / 16, NT = N / 16, NTH = 64 * NW;
+    __shared__ __attribute__((aligned(16))) float sB[kQ][N + 4];
+    __shared__ __attribute__((aligned(16))) float sC[kQ][N + 4];
+    __shared__ __attribute__((aligned(16))) float sY[kQ][P + 4];
+    __shared__ __attribute__((aligned(16))) float sM[kQ][kQ + 4];
+    __shared__ float sRed[NW][2][kQ];
+    __shared__ Scal sc;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane >> 4, c16 = lane & 15;
+    const int64_t k = blockIdx.x % p.nseg, bh = blockIdx.x / p.nseg;
+    const int64_t b = bh / p.H, h = bh % p.H, g = h * p.G / p.H;
+    const int64_t T0 = k * p.Ls, T1 = min(T0 + p.Ls, p.L);
+    const float A = -expf(p.A_log[h]);
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const float Dh = p.D ? p.D[h] : 0.0f;
+    const int pc = 16 * w + c16;                       // this lane's column p
+
+    // G^T tile nt: rows n = 16 nt + 4 r + v, column p = 16 w + c16
+    f32x4 Gt[NT];
+    {
+        const float *src = k == p.nseg - 1 ? (p.dhf ? p.dhf + (b * p.H + h) * P * N : nullptr)
+                                           : p.Gseg + seg_off(p, b, h, k);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Gt[nt][v] = src ? src[pc * N + 16 * nt + 4 * r + v] : 0.0f;
+    }
+    const int64_t nch = (T1 - T0 + kQ - 1) / kQ;
+    for (int64_t ci = nch - 1; ci >= 0; --ci) {
+        const int64_t t0 = T0 + ci * kQ;
+        stage_bf16<N, N + 4>(sB, p.B, b, p.L, p.G, g, t0, T1, tid, NTH);
+        stage_bf16<N, N + 4>(sC, p.C, b, p.L, p.G, g, t0, T1, tid, NTH);
+        stage_f32<P, P + 4>(sY, p.dy, b, p.L, p.H, h, t0, T1, tid, NTH);
+        if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane);
+        __syncthreads();
+        const float csend = sc.csend;
+        // (B C^T) o E, upper-triangular tiles (0,0), (0,1), (1,1) of [t][t']
+        for (int tau = w; tau < 3; tau += NW) {
+            const int ti = tau == 2 ? 1 : 0, tj = tau == 0 ? 0 : 1;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < NT; ++kt) {
+                const float4 a4 = *reinterpret_cast<const float4 *>(&sB[16 * ti + c16][16 * kt + 4 * r]);
+                const float4 b4 = *reinterpret_cast<const float4 *>(&sC[16 * tj + c16][16 * kt + 4 * r]);
+                acc = mfma4(a4.x, b4.x, acc);
+                acc = mfma4(a4.y, b4.y, acc);
+                acc = mfma4(a4.z, b4.z, acc);
+                acc = mfma4(a4.w, b4.w, acc);
+            }
+            const int tp = 16 * tj + c16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = 16 * ti + 4 * r + v;
+                sM[t][tp] = tp >= t ? acc[v] * __expf(sc.cs[tp] - sc.cs[t]) : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float4 a4 = *reinterpret_cast<const float4 *>(&sB[16 * ti + c16][16 * nt + 4 * r]);
+                acc = mfma4(a4.x, Gt[nt][0], acc);
+                acc = mfma4(a4.y, Gt[nt][1], acc);
+                acc = mfma4(a4.z, Gt[nt][2], acc);
+                acc = mfma4(a4.w, Gt[nt][3], acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] *= sc.eme[16 * ti + 4 * r + v];
+#pragma unroll
+            for (int tj = ti; tj < 2; ++tj) {
+                const float4 a4 = *reinterpret_cast<const float4 *>(&sM[16 * ti + c16][16 * tj + 4 * r]);
+                acc = mfma4(a4.x, sY[16 * tj + 4 * r + 0][pc], acc);
+                acc = mfma4(a4.y, sY[16 * tj + 4 * r + 1][pc], acc);
+                acc = mfma4(a4.z, sY[16 * tj + 4 * r + 2][pc], acc);
+                acc = mfma4(a4.w, sY[16 * tj + 4 * r + 3][pc], acc);
+            }
+            // u = acc: dx = sigma u + D dy and the per-step sums over p
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tl = 16 * ti + 4 * r + v;
+                const int64_t t = t0 + tl;
+                const float dyv = sY[tl][pc];
+                float xv = 0.0f, dxv = 0.0f;
+                if (t < T1) {
+                    xv = bf(p.x[((b * p.L + t) * p.H + h) * P + pc]);
+                    dxv = fmaf(sc.sig[tl], acc[v], Dh * dyv);
+                    p.dx[((b * p.L + t) * p.H + h) * P + pc] = dxv;
+                }
+                const float s0 = row_total16(xv * acc[v]);
+                const float s2 = row_total16(dyv * xv);
+                if (c16 == 15) {
+                    sRed[w][0][tl] = s0;
+                    sRed[w][1][tl] = s2;
+                }
+            }
+        }
+        // G^T <- e^{cs_end} G^T + C^T (e^{cs} o dY)
+        const float eend = __expf(csend);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) Gt[nt] *= eend;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int s = 16 * st + 4 * r + v;
+                const float bb = sY[s][pc] * sc.ecs[s];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) Gt[nt] = mfma4(sC[s][16 * nt + c16], bb, Gt[nt]);
+            }
+        __syncthreads();
+        if (tid < kQ && t0 + tid < T1) {
+            float s0 = 0.0f, s2 = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) { s0 += sRed[ww][0][tid]; s2 += sRed[ww][1][tid]; }
+            const int64_t o = (b * p.L + t0 + tid) * p.H + h;
+            p.dsig[o] = s0;
+            p.dyx[o] = s2;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ passes
+// S entering each segment: S_in[0] = h0, S_in[k+1] = dec[k] S_in[k] + S_loc[k].
+__global__ void __launch_bounds__(256) ssdb_pass_f(SbKp p) {
+    const int64_t PN = p.P * p.N, tot = p.batch * p.H * PN;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= tot) return;
+    const int64_t bh = i / PN, e = i % PN;
+    float s = p.h0 ? p.h0[bh * PN + e] : 0.0f;
+    for (int64_t k = 0; k < p.nseg; ++k) {
+        float *q = p.Sseg + (bh * p.nseg + k) * PN + e;
+        const float loc = k < p.nseg - 1 ? *q : 0.0f;
+        *q = s;
+        if (k < p.nseg - 1) s = fmaf(p.dec[bh * p.nseg + k], s, loc);
+    }
+}
+// G entering each segment from the right: G_in[nseg-1] = dh_final,
+// G_in[k-1] = dec[k] G_in[k] + G_loc[k].
+__global__ void __launch_bounds__(256) ssdb_pass_r(SbKp p) {
+    const int64_t PN = p.P * p.N, tot = p.batch * p.H * PN;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= tot) return;
+    const int64_t bh = i / PN, e = i % PN;
+    float gv = p.dhf ? p.dhf[bh * PN + e] : 0.0f;
+    for (int64_t k = p.nseg - 1; k >= 0; --k) {
+        float *q = p.Gseg + (bh * p.nseg + k) * PN + e;
+        const float loc = k >= 1 ? *q : 0.0f;
+        *q = gv;
+        if (k >= 1) gv = fmaf(p.dec[bh * p.nseg + k], gv, loc);
+    }
+}
+
+// dB, dC: the heads' shares added per group, heads in order
+__global__ void __launch_bounds__(256) ssdb_reduce_heads(SbKp p) {
+    const int64_t tot = p.batch * p.L * p.G * p.N;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= tot) return;
+    const int64_t n = i % p.N, rest = i / p.N, g = rest % p.G, bt = rest / p.G;
+    const int64_t hpg = p.H / p.G;
+    float sb = 0.0f, scv = 0.0f;
+    for (int64_t j = 0; j < hpg; ++j) {
+        const int64_t o = (bt * p.H + g * hpg + j) * p.N + n;
+        sb += p.dBh[o];
+        scv += p.dCh[o];
+    }
+    p.dB[i] = sb;
+    p.dC[i] = scv;
+}
+
+// phi1'(z) for the zero-order hold's dsigma/dA: series below |z| = 1/4
+// (truncation < 2e-9 relative), the closed form above.
+__device__ __forceinline__ float dphi1f(float z) {
+    if (fabsf(z) < 0.25f) {
+        float q = fmaf(z, 1.0f / 5760.0f, 1.0f / 840.0f);
+        q = fmaf(z, q, 1.0f / 144.0f);
+        q = fmaf(z, q, 1.0f / 30.0f);
+        q = fmaf(z, q, 1.0f / 8.0f);
+        q = fmaf(z, q, 1.0f / 3.0f);
+        return fmaf(z, q, 0.5f);
+    }
+    const float e = __expf(z);
+    return fmaf(e, z - 1.0f, 1.0f) / (z * z);
+}
+
+// dL/da at the first step T0 of every segment k >= 1, exactly:
+// e^{a_T0} <G_T0, S_{T0-1}> = <G entering segment k-1 from the right, S entering segment k>.
+// One block per (batch, head, k); a fixed-order tree over the P*N products.
+constexpr int kBndThreads = 256;
+__global__ void __launch_bounds__(kBndThreads) ssdb_bnd(SbKp p) {
+    __shared__ double sR[kBndThreads];
+    const int tid = threadIdx.x;
+    const int64_t k = 1 + blockIdx.x % (p.nseg - 1), bh = blockIdx.x / (p.nseg - 1);
+    const int64_t PN = p.P * p.N;
+    const float *gs = p.Gseg + (bh * p.nseg + k - 1) * PN;
+    const float *ss = p.Sseg + (bh * p.nseg + k) * PN;
+    double acc = 0.0;
+    for (int64_t e = tid; e < PN; e += kBndThreads) acc += (double)gs[e] * (double)ss[e];
+    sR[tid] = acc;
+    __syncthreads();
+    for (int st = kBndThreads / 2; st > 0; st >>= 1) {
+        if (tid < st) sR[tid] += sR[tid + st];
+        __syncthreads();
+    }
+    if (tid == 0) p.bnd[bh * p.nseg + k] = sR[0];
+}
+
+// Per (batch, segment, head), one 64-thread block; thread j owns a contiguous
+// run of the segment's steps.  The reverse sum of dL/dcs over the segment,
+// started from the exact boundary value of the next segment (0 after the
+// last), gives da_t (runs summed in fp64, a fixed-order suffix over the
+// threads); then the chain rule to ddt and the segment's partial sums of
+// dA_log / A, dD and ddt_bias.
+constexpr int kScalThreads = 64;
+__global__ void __launch_bounds__(kScalThreads) ssdb_scal(SbKp p) {
+    __shared__ double sTot[kScalThreads];
+    __shared__ float sR[3][kScalThreads];
+    const int tid = threadIdx.x;
+    const int64_t i = blockIdx.x;
+    const int64_t h = i % p.H, bk = i / p.H, k = bk % p.nseg, b = bk / p.nseg;
+    const int64_t bh = b * p.H + h;
+    const float A = -expf(p.A_log[h]);
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const int64_t T0 = k * p.Ls, T1 = min(T0 + p.Ls, p.L);
+    const int64_t per = (T1 - T0 + kScalThreads - 1) / kScalThreads;
+    const int64_t lo = min(T1, T0 + tid * per), hi = min(T1, lo + per);
+    // dL/dcs_t = dy_t.y_t - x_t.dx_t = C_t.dC_t - sigma_t x_t.u_t: the skip term D
+    // cancels exactly, so it is left out rather than added and subtracted in fp32
+    auto sigma = [&](float dl, float a) __attribute__((always_inline)) {
+        return p.mode == 1 ? dl : (p.mode == 0 ? (a == 0.0f ? dl : dl * (expm1f(a) / a)) : 1.0f);
+    };
+    auto dcs = [&](int64_t t, float sg) __attribute__((always_inline)) {
+        const int64_t o = (b * p.L + t) * p.H + h;
+        double v = (double)p.dyy[o] - (double)sg * (double)p.dsig[o];
+        if (t == p.L - 1) v += (double)p.hfdot[bh];
+        return v;
+    };
+    double loc = 0.0;
+    for (int64_t t = hi - 1; t >= lo; --t) {
+        const float dl = softplus(p.dt[(b * p.L + t) * p.H + h] + bias);
+        loc += dcs(t, sigma(dl, dl * A));
+    }
+    sTot[tid] = loc;
+    __syncthreads();
+    double carry = k + 1 < p.nseg ? p.bnd[bh * p.nseg + k + 1] : 0.0;
+    for (int j = kScalThreads - 1; j > tid; --j) carry += sTot[j];
+    float aA = 0.0f, aD = 0.0f, aT = 0.0f;
+    for (int64_t t = hi - 1; t >= lo; --t) {
+        const int64_t o = (b * p.L + t) * p.H + h;
+        const float x = p.dt[o] + bias;
+        const float dl = softplus(x);
+        const float a = dl * A;
+        const float sg = sigma(dl, a);
+        float dsd, dsa;
+        if (p.mode == 1) { dsd = 1.0f; dsa = 0.0f; }
+        else if (p.mode == 0) { dsd = __expf(a); dsa = dl * dl * dphi1f(a); }
+        else { dsd = 0.0f; dsa = 0.0f; }
+        carry += dcs(t, sg);                         // da_t = sum_{t' >= t} dL/dcs_t'
+        const float da = (float)carry;
+        const float ds = p.dsig[o];
+        const float ddl = fmaf(da, A, ds * dsd);
+        aA = fmaf(da, dl, fmaf(ds, dsa, aA));
+        const float g = ddl * (1.0f / (1.0f + __expf(-x)));
+        p.ddt[o] = g;
+        aT += g;
+        aD += p.dyx[o];
+    }
+    sR[0][tid] = aA;
+    sR[1][tid] = aD;
+    sR[2][tid] = aT;
+    __syncthreads();
+    if (tid == 0) {
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+        for (int j = 0; j < kScalThreads; ++j) { s0 += sR[0][j]; s1 += sR[1][j]; s2 += sR[2][j]; }
+        p.pA[i] = s0;
+        p.pD[i] = s1;
+        p.pT[i] = s2;
+    }
+}
+
+// dA_log = A * sum over (batch, segment), dD, ddt_bias = sums over (batch, segment)
+__global__ void __launch_bounds__(256) ssdb_final(SbKp p) {
+    const int64_t h = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (h >= p.H) return;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+    for (int64_t bk = 0; bk < p.batch * p.nseg; ++bk) {
+        s0 += p.pA[bk * p.H + h];
+        s1 += p.pD[bk * p.H + h];
+        s2 += p.pT[bk * p.H + h];
+    }
+    p.dA_log[h] = s0 * -expf(p.A_log[h]);
+    if (p.dD) p.dD[h] = s1;
+    if (p.ddt_bias) p.ddt_bias[h] = s2;
+}
+
+struct Plan { int64_t nseg, Ls; };
+Plan plan(int64_t batch, int64_t L, int64_t H, int64_t N) {
+    const int64_t waves = batch * H * (N / 32);
+    int64_t nseg = (kTargetWaves + waves - 1) / waves;
+    nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, L / kMinSeg));
+    nseg = std::max<int64_t>(nseg, (L + kMaxSeg - 1) / kMaxSeg);
+    const int64_t Ls = ((L + nseg - 1) / nseg + kQ - 1) / kQ * kQ;
+    return Plan{(L + Ls - 1) / Ls, Ls};
+}
+size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct WsLayout { size_t Sseg, Gseg, dec, bnd, dBh, dCh, dyy, dsig, dyx, hfdot, pA, pD, pT, total; };
+WsLayout layout(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t nseg) {
+    WsLayout w{};
+    size_t o = 0;
+    const size_t seg = nseg > 1 ? (size_t)(batch * H * nseg * P * N) * 4 : 0;
+    w.Sseg = o; o += al256(seg);
+    w.Gseg = o; o += al256(seg);
+    w.dec = o;  o += al256((size_t)(batch * H * nseg) * 4);
+    w.bnd = o;  o += al256((size_t)(batch * H * nseg) * 8);
+    w.dBh = o;  o += al256((size_t)(batch * L * H * N) * 4);
+    w.dCh = o;  o += al256((size_t)(batch * L * H * N) * 4);
+    w.dyy = o;  o += al256((size_t)(batch * L * H) * 4);
+    w.dsig = o; o += al256((size_t)(batch * L * H) * 4);
+    w.dyx = o;  o += al256((size_t)(batch * L * H) * 4);
+    w.hfdot = o; o += al256((size_t)(batch * H) * 4);
+    w.pA = o;   o += al256((size_t)(batch * nseg * H) * 4);
+    w.pD = o;   o += al256((size_t)(batch * nseg * H) * 4);
+    w.pT = o;   o += al256((size_t)(batch * nseg * H) * 4);
+    w.total = o;
+    return w;
+}
+
+template <int P, int N>
+void launch_pn(const SbKp &p, hipStream_t s) {
+    const unsigned bh = (unsigned)(p.batch * p.H);
+    if (p.nseg > 1) {
+        hipLaunchKernelGGL((ssdb_walk_f<P, N, true>), dim3(bh * (unsigned)(p.nseg - 1)), dim3(64 * (N / 32)), 0, s, p);
+        hipLaunchKernelGGL((ssdb_walk_r1<P, N, true>), dim3(bh * (unsigned)(p.nseg - 1)), dim3(64 * (N / 32)), 0, s, p);
+        const int64_t tot = p.batch * p.H * p.P * p.N;
+        hipLaunchKernelGGL(ssdb_pass_f, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(ssdb_pass_r, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(ssdb_bnd, dim3(bh * (unsigned)(p.nseg - 1)), dim3(kBndThreads), 0, s, p);
+    }
+    hipLaunchKernelGGL((ssdb_walk_f<P, N, false>), dim3(bh * (unsigned)p.nseg), dim3(64 * (N / 32)), 0, s, p);
+    hipLaunchKernelGGL((ssdb_walk_r1<P, N, false>), dim3(bh * (unsigned)p.nseg), dim3(64 * (N / 32)), 0, s, p);
+    hipLaunchKernelGGL((ssdb_walk_r2<P, N>), dim3(bh * (unsigned)p.nseg), dim3(64 * (P / 16)), 0, s, p);
+    const int64_t nr = p.batch * p.L * p.G * p.N;
+    hipLaunchKernelGGL(ssdb_reduce_heads, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(ssdb_scal, dim3((unsigned)(p.batch * p.nseg * p.H)), dim3(kScalThreads), 0, s, p);
+    hipLaunchKernelGGL(ssdb_final, dim3((unsigned)((p.H + 255) / 256)), dim3(256), 0, s, p);
+}
+
+template <int P>
+void launch_p(const SbKp &p, hipStream_t s) {
+    if (p.N == 32) launch_pn<P, 32>(p, s);
+    else if (p.N == 64) launch_pn<P, 64>(p, s);
+    else launch_pn<P, 128>(p, s);
+}
+
+}  // namespace
+
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state) {
+    const Plan pl = plan(batch, L, nheads, d_state);
+    return layout(batch, L, nheads, headdim, d_state, pl.nseg).total;
+}
+
+hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t stream, const char **kernel_name) {
+    *kernel_name = "ssdb_walk_f";
+    SbKp p{};
+    p.x = static_cast<const uint16_t *>(a.x);
+    p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
+    p.B = static_cast<const uint16_t *>(a.B);
+    p.C = static_cast<const uint16_t *>(a.C);
+    p.D = a.D; p.h0 = a.h0; p.dy = a.dy; p.dhf = a.dh_final;
+    p.dx = a.dx; p.ddt = a.ddt; p.dB = a.dB; p.dC = a.dC; p.dA_log = a.dA_log; p.dD = a.dD;
+    p.ddt_bias = a.ddt_bias; p.dh0 = a.dh0;
+    p.batch = a.batch; p.L = a.L; p.H = a.nheads; p.P = a.headdim; p.N = a.d_state; p.G = a.ngroups;
+    p.mode = (int)(a.flags & 0x3u);
+    const Plan pl = plan(a.batch, a.L, a.nheads, a.d_state);
+    p.nseg = pl.nseg;
+    p.Ls = pl.Ls;
+    const WsLayout w = layout(a.batch, a.L, a.nheads, a.headdim, a.d_state, pl.nseg);
+    char *ws = static_cast<char *>(a.workspace);
+    p.Sseg = reinterpret_cast<float *>(ws + w.Sseg);
+    p.Gseg = reinterpret_cast<float *>(ws + w.Gseg);
+    p.dec = reinterpret_cast<float *>(ws + w.dec);
+    p.dBh = reinterpret_cast<float *>(ws + w.dBh);
+    p.dCh = reinterpret_cast<float *>(ws + w.dCh);
+    p.dyy = reinterpret_cast<float *>(ws + w.dyy);
+    p.dsig = reinterpret_cast<float *>(ws + w.dsig);
+    p.dyx = reinterpret_cast<float *>(ws + w.dyx);
+    p.hfdot = reinterpret_cast<float *>(ws + w.hfdot);
+    p.bnd = reinterpret_cast<double *>(ws + w.bnd);
+    p.pA = reinterpret_cast<float *>(ws + w.pA);
+    p.pD = reinterpret_cast<float *>(ws + w.pD);
+    p.pT = reinterpret_cast<float *>(ws + w.pT);
+    if (p.P == 32) launch_p<32>(p, stream);
+    else if (p.P == 64) launch_p<64>(p, stream);
+    else launch_p<128>(p, stream);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

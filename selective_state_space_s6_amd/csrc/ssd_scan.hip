@@ -93,21 +93,6 @@ struct SsdKp {
     int mode;           // 0 ZOH, 1 DT, 2 ONE
 };
 
-// Inclusive prefix sum over each 32-lane half of a wave with DPP: row_shr 1,
-// 2, 4, 8 with zero fill scans each 16-lane row, then row_bcast:15 adds the
-// last lane of rows 0 and 2 to rows 1 and 3.
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, true));
-}
-__device__ __forceinline__ float scan32(float v) {
-    v += dpp_f<0x111>(v);
-    v += dpp_f<0x112>(v);
-    v += dpp_f<0x114>(v);
-    v += dpp_f<0x118>(v);
-    v += dpp_f<0x142, 0xa>(v);
-    return v;
-}
 
 // per-chunk scalars in LDS
 struct Scal {

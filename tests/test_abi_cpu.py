@@ -29,10 +29,12 @@ def lib():
     L.ssd_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_cplx_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_uint32, P, Z, P]
     L.ssm_s6_scan_bwd.argtypes = [P] * 18 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
+    L.ssd_chunk_scan_bwd.argtypes = [P] * 18 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     for f in ("ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size"):
         getattr(L, f).argtypes = [I] * 4
         getattr(L, f).restype = Z
-    for f in ("ssd_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd_workspace_size"):
+    for f in ("ssd_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd_workspace_size",
+              "ssd_chunk_scan_bwd_workspace_size"):
         getattr(L, f).argtypes = [I] * 7
         getattr(L, f).restype = Z
     return L
@@ -45,6 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert names == {"ssm_last_error", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_fwd",
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
+                     "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
                      "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd"}
     for n in names:
         assert hasattr(lib, n), n
@@ -127,6 +130,33 @@ def test_ssd_argument_checks(lib):
     ws = lib.ssd_chunk_scan_fwd_workspace_size(8, 4096, 24, 64, 128, 1, 256)
     assert ws >= 8 * 24 * 2 * 64 * 128 * 4 and ws % 4 == 0
     assert lib.ssd_chunk_scan_fwd_workspace_size(0, 300, 4, 64, 128, 2, 256) == 0
+
+
+def _ssdb(lib, dims=(2, 300, 4, 64, 128, 2, 256), dtype=1, flags=1, ws=ctypes.c_void_p(0x9000000),
+          wsb=1 << 40, **kw):
+    names = ["x", "dt", "dt_bias", "A_log", "B", "C", "D", "h0", "dy", "dh_final",
+             "dx", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0"]
+    required = {"x", "dt", "A_log", "B", "C", "dy", "dx", "ddt", "dB", "dC", "dA_log"}
+    ptrs = {n: (ctypes.c_void_p(0x100000 * (i + 1)) if n in required else None)
+            for i, n in enumerate(names)}
+    ptrs.update(kw)
+    return lib.ssd_chunk_scan_bwd(*(ptrs[n] for n in names), *dims, dtype, flags, ws, wsb, None)
+
+
+def test_ssd_bwd_argument_checks(lib):
+    assert _ssdb(lib, dy=None) == INVALID and "dy is NULL" in _err(lib)
+    assert _ssdb(lib, dims=(2, 300, 6, 64, 128, 4, 256)) == INVALID and "ngroups" in _err(lib)
+    assert _ssdb(lib, dims=(2, 300, 4, 48, 128, 2, 256)) == UNSUPPORTED and "headdim" in _err(lib)
+    assert _ssdb(lib, dims=(2, 300, 4, 64, 256, 2, 256)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _ssdb(lib, dims=(2, 300, 4, 64, 128, 2, 100)) == UNSUPPORTED and "chunk_len" in _err(lib)
+    assert _ssdb(lib, dtype=0) == UNSUPPORTED and "bf16" in _err(lib)
+    assert _ssdb(lib, flags=0x3) == INVALID
+    assert _ssdb(lib, dx=ctypes.c_void_p(0x100000)) == INVALID and "alias" in _err(lib)   # dx == x
+    need = lib.ssd_chunk_scan_bwd_workspace_size(2, 300, 4, 64, 128, 2, 256)
+    # each head's share of dB and dC: 2 * batch * L * H * N fp32
+    assert need >= 2 * 2 * 300 * 4 * 128 * 4
+    assert _ssdb(lib, ws=None) == WORKSPACE
+    assert _ssdb(lib, wsb=need - 1) == WORKSPACE and "workspace" in _err(lib)
 
 
 def _cssd(lib, dims=(2, 100, 4, 64, 32, 2, 64), flags=0, ws=FAKE, wsb=1 << 40):
