@@ -22,6 +22,9 @@ Parity status of each function (what pins it is listed in the tests):
   ssd_bwd   pinned: the same two kinds of checks against ssd_fwd (with groups
             and h0), and equality with s6_bwd on the SSD shapes that are an S6
             scan (headdim 1, one group, A shared over the states).
+  trap_fwd  pinned: reduction to ssd_fwd at trap = 1, brute-force semiseparable
+            matrix (diagonal gamma, off-diagonal gamma + next step's
+            dt (1 - trap)), hand case, carry composition across calls.
 """
 from __future__ import annotations
 
@@ -66,8 +69,9 @@ def _load():
     lib.oracle_cssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_s6_bwd.argtypes = [P] * 10 + [I, I, I, I, ctypes.c_uint32, I, I, I, I] + [P] * 8 + [ctypes.c_int]
     lib.oracle_ssd_bwd.argtypes = [P] * 10 + [I] * 6 + [ctypes.c_uint32, P, I] + [P] * 8 + [ctypes.c_int]
+    lib.oracle_trap_fwd.argtypes = [P] * 10 + [I] * 5 + [P, I, P, P, ctypes.c_int]
     for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd, lib.oracle_s6_bwd,
-              lib.oracle_ssd_bwd):
+              lib.oracle_ssd_bwd, lib.oracle_trap_fwd):
         f.restype = None
     lib.oracle_dphi1.argtypes = [ctypes.c_double]
     lib.oracle_dphi1.restype = ctypes.c_double
@@ -162,6 +166,29 @@ def ssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_DT, u
     _load().oracle_ssd_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
                            _ptr(h0), batch, L, H, P, N, G, flags, _ptr(uu), nu, _ptr(y), _ptr(hf),
                            nthreads or default_threads())
+    if full:
+        return (y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(), hf.reshape(batch, H, P, N))
+    return y, hf
+
+
+def trap_fwd(x, k, q, dt, a, trap, D=None, h0=None, k_prev=None, x_prev=None, units=None,
+             nthreads=None):
+    """Sequential Mamba-3 trapezoidal recurrence in fp64 (per-head k, q).
+
+    x: (batch, L, H, P); k, q: (batch, L, H, N); dt, a, trap: (batch, L, H);
+    D: (H,); h0: (batch, H, P, N); k_prev: (batch, H, N); x_prev: (batch, H, P).
+    Returns y (batch, L, H, P), h_final (batch, H, P, N), or per-unit arrays."""
+    x, k, q, dt, a, trap, D, h0, k_prev, x_prev = map(
+        _f32, (x, k, q, dt, a, trap, D, h0, k_prev, x_prev))
+    batch, L, H, P = x.shape
+    N = k.shape[3]
+    uu, full = _units(units, batch, H)
+    nu = uu.shape[0]
+    y = np.empty((nu, L, P), np.float64)
+    hf = np.empty((nu, P, N), np.float64)
+    _load().oracle_trap_fwd(_ptr(x), _ptr(k), _ptr(q), _ptr(dt), _ptr(a), _ptr(trap), _ptr(D),
+                            _ptr(h0), _ptr(k_prev), _ptr(x_prev), batch, L, H, P, N, _ptr(uu), nu,
+                            _ptr(y), _ptr(hf), nthreads or default_threads())
     if full:
         return (y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(), hf.reshape(batch, H, P, N))
     return y, hf

@@ -272,11 +272,64 @@ static void cssd_unit(const cssd_job *j, int64_t k)
 /* ------------------------------------------------------------ threads --- */
 
 typedef struct {
-    int kind;               /* 0 S6, 1 SSD, 2 complex, 3 SSD backward */
+    int kind;               /* 0 S6, 1 SSD, 2 complex, 3 SSD backward, 4 trapezoidal SSD */
     const void *job;
     int64_t n_units;
     int tid, nthreads;
 } worker_arg;
+
+/* ---------------------------------------- Mamba-3 trapezoidal SSD --- */
+/*
+ * mamba-rs 0.2.1, src/mamba3_siso/gpu/mamba3_gpu.rs (module header; F5b
+ * m3_compute_abg; F6 m3_burnin_fwd and its persistent ssm/k/v states): per
+ * (b, h), with per-step dt_t, a_t (input-dependent A) and trap_t,
+ *   alpha_t = e^{a_t dt_t},  beta_t = alpha_t dt_t (1 - trap_t),  gamma_t = trap_t dt_t
+ *   h_t[p,n] = alpha_t h_{t-1}[p,n] + beta_t x_{t-1}[p] k_{t-1}[n] + gamma_t x_t[p] k_t[n]
+ *   y[b,t,h,p] = sum_n q_t[n] h_t[p,n] + D[h] x_t[p]
+ * with h_{-1} = h0, (x_{-1}, k_{-1}) = (x_prev, k_prev) (each 0 when absent).
+ * k, q are per head (B, L, H, N).  Outputs y [n_units][L][P], h_final [n_units][P][N].
+ */
+typedef struct {
+    const float *x, *k, *q, *dt, *a, *trap, *D, *h0, *k_prev, *x_prev;
+    int64_t batch, L, H, P, N;
+    const int64_t *units;
+    int64_t n_units;
+    double *y_out, *hf_out;
+} trap_job;
+
+static void trap_unit(const trap_job *j, int64_t u)
+{
+    const int64_t b = j->units[2 * u], hh = j->units[2 * u + 1];
+    const int64_t L = j->L, H = j->H, P = j->P, N = j->N;
+    const double Dh = j->D ? (double)j->D[hh] : 0.0;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(P * N));
+    double *xp = (double *)malloc(sizeof(double) * (size_t)P);
+    double *kp = (double *)malloc(sizeof(double) * (size_t)N);
+    for (int64_t i = 0; i < P * N; ++i) S[i] = j->h0 ? (double)j->h0[(b * H + hh) * P * N + i] : 0.0;
+    for (int64_t p = 0; p < P; ++p) xp[p] = j->x_prev ? (double)j->x_prev[(b * H + hh) * P + p] : 0.0;
+    for (int64_t n = 0; n < N; ++n) kp[n] = j->k_prev ? (double)j->k_prev[(b * H + hh) * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t o = (b * L + t) * H + hh;
+        const double dt = (double)j->dt[o], a = (double)j->a[o], tr = (double)j->trap[o];
+        const double alpha = exp(a * dt);
+        const double beta = alpha * dt * (1.0 - tr);
+        const double gamma = tr * dt;
+        const float *xt = j->x + o * P, *kt = j->k + o * N, *qt = j->q + o * N;
+        for (int64_t p = 0; p < P; ++p) {
+            double *Sp = S + p * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                Sp[n] = alpha * Sp[n] + beta * xp[p] * kp[n] + gamma * (double)xt[p] * (double)kt[n];
+                acc += (double)qt[n] * Sp[n];
+            }
+            j->y_out[(u * L + t) * P + p] = acc + Dh * (double)xt[p];
+        }
+        for (int64_t p = 0; p < P; ++p) xp[p] = (double)xt[p];
+        for (int64_t n = 0; n < N; ++n) kp[n] = (double)kt[n];
+    }
+    if (j->hf_out) memcpy(j->hf_out + u * P * N, S, sizeof(double) * (size_t)(P * N));
+    free(S); free(xp); free(kp);
+}
 
 /* ------------------------------------------------------- SSD backward --- */
 /*
@@ -426,7 +479,8 @@ static void *worker(void *p)
         if (w->kind == 0) s6_unit((const s6_job *)w->job, k);
         else if (w->kind == 1) ssd_unit((const ssd_job *)w->job, k);
         else if (w->kind == 2) cssd_unit((const cssd_job *)w->job, k);
-        else ssdb_unit((const ssdb_job *)w->job, k);
+        else if (w->kind == 3) ssdb_unit((const ssdb_job *)w->job, k);
+        else trap_unit((const trap_job *)w->job, k);
     }
     return NULL;
 }
@@ -676,6 +730,17 @@ void oracle_ssd_bwd(const float *x, const float *dt, const float *dt_bias, const
     ssdb_job j = {x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, batch, L, nheads, headdim,
                   d_state, ngroups, flags, units, n_units, dx, dB, dC, ddt, dh0, dA_log, dD, ddt_bias};
     run_units(3, &j, n_units, nthreads);
+}
+
+void oracle_trap_fwd(const float *x, const float *k, const float *q, const float *dt, const float *a,
+                     const float *trap, const float *D, const float *h0, const float *k_prev,
+                     const float *x_prev, int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                     int64_t d_state, const int64_t *units, int64_t n_units, double *y_out,
+                     double *hf_out, int nthreads)
+{
+    trap_job j = {x, k, q, dt, a, trap, D, h0, k_prev, x_prev, batch, L, nheads, headdim, d_state,
+                  units, n_units, y_out, hf_out};
+    run_units(4, &j, n_units, nthreads);
 }
 
 double oracle_softplus(double x) { return sp(x); }
