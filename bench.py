@@ -5,8 +5,8 @@ A step is one call of the scan entry point over one batch of synthetic input
 already resident in HBM (for S6: softplus, discretisation, recurrence, state
 reduction and skip term, all inside one kernel).  The headline workload is the
 S6 scan at a Mamba-1 layer shape (batch 8, L 2048, d_inner 1536, N 16, fp32);
-the SSD and complex-SSD workloads are measured the same way and reported under
-"secondary".  Prints ONE JSON line.
+the SSD, complex-SSD and trapezoidal (Mamba-3) SSD workloads and the two
+backward passes are measured the same way and reported under "secondary".  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
 """
@@ -95,6 +95,17 @@ def ssd_model(d):
     return elems, bytes_, flops
 
 
+def trap_model(d):
+    """Mamba-3 trapezoidal SSD: bf16 x, per-head bf16 k and q, fp32 dt, a, trap in; fp32 y and
+    final state out.  Flops as the SSD with one group per head (k.q^T per head)."""
+    B, L, H, P, N, Q = d["batch"], d["L"], d["nheads"], d["headdim"], d["d_state"], d["chunk_len"]
+    elems = B * L * H * P
+    nc = -(-L // Q)
+    bytes_ = elems * 2 + 2 * B * L * H * N * 2 + 3 * B * L * H * 4 + elems * 4 + B * H * P * N * 4
+    flops = 2 * B * nc * H * (Q * Q * N + Q * Q * P + 2 * Q * P * N)
+    return elems, bytes_, flops
+
+
 def cssd_model(d):
     B, L, H, P, Nc, G, Q = (d["batch"], d["L"], d["nheads"], d["headdim"], d["n_complex"],
                             d["ngroups"], d["chunk_len"])
@@ -172,6 +183,21 @@ def make_runner(name, dev):
         w["kind"] = "ssd_bwd"
         return step, dims, w, ["ssdb_walk_f", "ssdb_walk_r1", "ssdb_walk_r2", "ssdb_pass_f", "ssdb_pass_r",
                                "ssdb_reduce_heads", "ssdb_scal", "ssdb_final"]
+    if kind == "trap":
+        t0 = copies[0]
+        y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
+        hf = torch.empty((dims["batch"], dims["nheads"], dims["headdim"], dims["d_state"]),
+                         dtype=torch.float32, device=dev)
+        ws = torch.empty(lib.ssd_trap_chunk_scan_fwd_workspace_size(
+            dims["batch"], dims["L"], dims["nheads"], dims["headdim"], dims["d_state"],
+            w["chunk_len"]), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            lib.ssd_trap_chunk_scan_fwd(t["x"], t["k"], t["q"], t["dt"], t["a"], t["trap"], t["D"],
+                                        None, None, None, chunk_len=w["chunk_len"], y=y, h_final=hf,
+                                        workspace=ws)
+        return step, dims, w, ["ssd_state_kernel", "ssd_pass_kernel", "ssd_scan_kernel"]
     if kind == "ssd":
         t0 = copies[0]
         y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
@@ -276,9 +302,12 @@ def cpu_baseline_units(name, n_units):
     nthr = oracle.default_threads()
     n_units = min(n_units, d["batch"] * d["nheads"])
     units = np.stack([np.arange(n_units) % d["batch"], np.arange(n_units) // d["batch"]], 1)
-    fn = oracle.ssd_fwd if w["kind"] == "ssd" else oracle.cssd_fwd
     t0 = time.perf_counter()
-    fn(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
+    if w["kind"] == "trap":
+        oracle.trap_fwd(**inp.arrays, units=units, nthreads=nthr)
+    else:
+        fn = oracle.ssd_fwd if w["kind"] == "ssd" else oracle.cssd_fwd
+        fn(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
     sec = time.perf_counter() - t0
     elems = n_units * d["L"] * d["headdim"]
     return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
@@ -310,6 +339,8 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = ssd_bwd_model(dict(dims, nseg=ssd_bwd_nseg(dims)))
     elif kind == "ssd":
         elems, bytes_, ops = ssd_model(dims)
+    elif kind == "trap":
+        elems, bytes_, ops = trap_model(dims)
     else:
         elems, bytes_, ops = cssd_model(dims)
     ev_ms = sorted(per)[len(per) // 2]
@@ -374,7 +405,7 @@ def main():
     if not args.no_secondary and args.workload == "s6_mamba1":
         sec = []
         for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
-                            ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
+                            ("trap_mamba3", 5), ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
             es = s["event_ms_median"] * 1e-3
@@ -389,7 +420,7 @@ def main():
                 ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
                 ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
                 ent["kernel_ms"] = round(s["event_ms_median"], 4)
-            elif s["kind"] == "ssd":
+            elif s["kind"] in ("ssd", "trap"):
                 ent["mfma_TFLOPs"] = round(s["ops"] / es / 1e12, 1)
                 ent["mfma_frac_bf16"] = round(s["ops"] / es / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
             else:

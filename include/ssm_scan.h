@@ -225,6 +225,49 @@ int ssd_chunk_scan_bwd(const void *x, const float *dt, const float *dt_bias, con
                        int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------ trapezoidal SSD ----
+ * Mamba-3 SISO recurrence with the trapezoidal input rule, per-step decay and
+ * per-head k, q [RS-M3 module header, F5b m3_compute_abg, F6 and its carried
+ * ssm / k / v states]:
+ *   alpha_t = exp(a[b,t,h] * dt[b,t,h]),  beta_t = alpha_t dt_t (1 - trap_t),  gamma_t = trap_t dt_t
+ *   S_t[p,n] = alpha_t S_{t-1}[p,n] + beta_t x_{t-1}[p] k_{t-1}[n] + gamma_t x_t[p] k_t[n]
+ *   y[b,t,h,p] = sum_n q[b,t,h,n] S_t[p,n] + D[h] x[b,t,h,p]
+ * with S_{-1} = h0 (or 0), (x_{-1}, k_{-1}) = (x_prev, k_prev) (or 0) and
+ * h_final = S_{L-1}.  dt is the step as the model hands it over (already
+ * positive: no softplus or bias is applied here), a the per-step decay rate
+ * (a <= 0 for a contracting state) and trap the per-step blend in [0, 1]
+ * (1 gives the plain SSD scan with sigma = dt).  The data-dependent rotation
+ * of k and q is applied by the caller before this call.  A caller that cuts a
+ * sequence into pieces passes each piece's h_final and its last x and k as the
+ * next piece's h0, x_prev and k_prev.
+ * The kernels run the SSD chunked scan on the shifted state
+ * S'_t = S_t + dt_{t+1} (1 - trap_{t+1}) x_t (x) k_t, which follows the SSD
+ * recurrence with input scale gamma_t + dt_{t+1} (1 - trap_{t+1}) (gamma only at
+ * the last step) while the diagonal of each chunk uses gamma_t.
+ *
+ * Layouts: x (batch, L, nheads, headdim) bf16; k, q (batch, L, nheads, d_state)
+ * bf16; dt, a, trap (batch, L, nheads) fp32; D (nheads) fp32 or NULL;
+ * y (batch, L, nheads, headdim) fp32; h0, h_final (batch, nheads, headdim,
+ * d_state) fp32 or NULL; x_prev (batch, nheads, headdim) and k_prev
+ * (batch, nheads, d_state) bf16, both given or both NULL.  No output may
+ * alias an input; h0 == h_final is allowed.
+ * Limits: in_dtype SSM_BF16; headdim in {32, 64, 128}; d_state a multiple of
+ * 32, <= 256; chunk_len in {64, 128, 256} (checked; the kernels use their own
+ * 32-step chunks).
+ * Workspace: ssd_trap_chunk_scan_fwd_workspace_size() bytes, 16-byte aligned,
+ * owned by the caller, always required (segment states and decays as for
+ * ssd_chunk_scan_fwd, plus the entering state with the carried input folded
+ * in). */
+size_t ssd_trap_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                              int64_t d_state, int64_t chunk_len);
+
+int ssd_trap_chunk_scan_fwd(const void *x, const void *k, const void *q, const float *dt, const float *a,
+                            const float *trap, const float *D, float *y, const float *h0,
+                            const void *k_prev, const void *x_prev, float *h_final,
+                            int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                            int64_t chunk_len, ssm_dtype_t in_dtype,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* --------------------------------------------------------- complex SSD ----
  * Mamba-3-style SSD with a complex diagonal state [BF-CSSD header,
  * et_bbar_re/et_bbar_im, complex_ssd_forward]:

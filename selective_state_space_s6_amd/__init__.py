@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssd_chunk_scan_fwd", "ssd_chunk_scan_bwd",
-    "ssd_cplx_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size",
+    "ssd_cplx_chunk_scan_fwd", "ssd_trap_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size",
+    "ssm_s6_scan_bwd_workspace_size", "ssd_trap_chunk_scan_fwd_workspace_size",
     "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
     "ssd_cplx_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
     "SSM_BBAR_ZOH", "SSM_BBAR_DT", "SSM_BBAR_ONE", "SSM_CPLX_STABLE", "SSM_CPLX_DOC",
@@ -53,6 +54,10 @@ _lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_chunk_scan_bwd_workspace_size.restype = _Z
 _lib.ssd_chunk_scan_bwd.argtypes = [_P] * 18 + [_I] * 7 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
 _lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
+_lib.ssd_trap_chunk_scan_fwd_workspace_size.argtypes = [_I] * 6
+_lib.ssd_trap_chunk_scan_fwd_workspace_size.restype = _Z
+_lib.ssd_trap_chunk_scan_fwd.argtypes = [_P] * 12 + [_I] * 6 + [ctypes.c_int, _P, _Z, _P]
+_lib.ssd_trap_chunk_scan_fwd.restype = ctypes.c_int
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_cplx_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_uint32, _P, _Z, _P]
@@ -126,6 +131,11 @@ def ssd_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state, ngroup
 def ssd_chunk_scan_bwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups, chunk_len) -> int:
     return int(_lib.ssd_chunk_scan_bwd_workspace_size(batch, L, nheads, headdim, d_state, ngroups,
                                                       chunk_len))
+
+
+def ssd_trap_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state, chunk_len) -> int:
+    return int(_lib.ssd_trap_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, d_state,
+                                                           chunk_len))
 
 
 def ssd_cplx_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, n_complex, ngroups,
@@ -241,6 +251,43 @@ def ssd_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=256
                                  _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L, H, P, N, G,
                                  chunk_len, _in_dtype(x), flags, _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ssd_trap_chunk_scan_fwd(x, k, q, dt, a, trap, D=None, h0=None, k_prev=None, x_prev=None, *,
+                            chunk_len=64, return_final=False, y=None, h_final=None, workspace=None):
+    """Mamba-3 trapezoidal SSD forward.  x (batch, L, H, P) bf16; k, q (batch, L, H, N)
+    bf16; dt, a, trap (batch, L, H) fp32 (dt positive, used as given); D (H,) fp32 or
+    None; h0 (batch, H, P, N) fp32 or None; k_prev (batch, H, N), x_prev (batch, H, P)
+    bf16, both or neither.  Returns y fp32 (and h_final)."""
+    dev = x.device
+    batch, L, H, P = x.shape
+    N = k.shape[3]
+    dty = x.dtype
+    _req(x, "x", dty, (batch, L, H, P), dev)
+    _req(k, "k", dty, (batch, L, H, N), dev)
+    _req(q, "q", dty, (batch, L, H, N), dev)
+    for t, nm in ((dt, "dt"), (a, "a"), (trap, "trap")):
+        _req(t, nm, torch.float32, (batch, L, H), dev)
+    _opt(D, "D", torch.float32, (H,), dev)
+    _opt(h0, "h0", torch.float32, (batch, H, P, N), dev)
+    _opt(k_prev, "k_prev", dty, (batch, H, N), dev)
+    _opt(x_prev, "x_prev", dty, (batch, H, P), dev)
+    if y is None:
+        y = torch.empty((batch, L, H, P), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, (batch, L, H, P), dev)
+    if return_final and h_final is None:
+        h_final = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    _opt(h_final, "h_final", torch.float32, (batch, H, P, N), dev)
+    ws = ssd_trap_chunk_scan_fwd_workspace_size(batch, L, H, P, N, chunk_len)
+    if workspace is None:
+        workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+    rc = _lib.ssd_trap_chunk_scan_fwd(_ptr(x), _ptr(k), _ptr(q), _ptr(dt), _ptr(a), _ptr(trap),
+                                      _ptr(D), _ptr(y), _ptr(h0), _ptr(k_prev), _ptr(x_prev),
+                                      _ptr(h_final), batch, L, H, P, N, chunk_len, _in_dtype(x),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y
 

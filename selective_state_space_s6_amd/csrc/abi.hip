@@ -206,6 +206,55 @@ int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, con
     return launched(E, ssm::launch_ssd(a, stream, &kn), kn);
 }
 
+size_t ssd_trap_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                              int64_t d_state, int64_t chunk_len) {
+    (void)chunk_len;
+    if (batch <= 0 || L <= 0 || nheads <= 0 || headdim <= 0 || d_state <= 0) return 0;
+    return ssm::ssd_trap_workspace_bytes(batch, L, nheads, headdim, d_state);
+}
+
+int ssd_trap_chunk_scan_fwd(const void *x, const void *k, const void *q, const float *dt, const float *a,
+                            const float *trap, const float *D, float *y, const float *h0,
+                            const void *k_prev, const void *x_prev, float *h_final,
+                            int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                            int64_t chunk_len, ssm_dtype_t in_dtype,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssd_trap_chunk_scan_fwd";
+    REQUIRE_PTR(E, x); REQUIRE_PTR(E, k); REQUIRE_PTR(E, q); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, a);
+    REQUIRE_PTR(E, trap); REQUIRE_PTR(E, y);
+    int rc = ssd_check_shape(E, batch, L, nheads, headdim, d_state, nheads, chunk_len);
+    if (rc != SSM_OK) return rc;
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if (in_dtype != SSM_BF16)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: the MFMA path takes bf16 x, k, q (SSM_BF16)", E);
+    if ((k_prev == nullptr) != (x_prev == nullptr))
+        return fail(SSM_ERR_INVALID_ARG, "%s: k_prev and x_prev must be given together", E);
+    if (!(headdim == 32 || headdim == 64 || headdim == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: headdim %lld not in {32, 64, 128}", E, (long long)headdim);
+    if (d_state % 32 != 0 || d_state > SSM_MAX_D_STATE)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld must be a multiple of 32 and <= %d", E,
+                    (long long)d_state, SSM_MAX_D_STATE);
+    if (!(chunk_len == 64 || chunk_len == 128 || chunk_len == 256))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: chunk_len %lld not in {64, 128, 256}", E, (long long)chunk_len);
+    REQUIRE_ALIGN(E, x); REQUIRE_ALIGN(E, k); REQUIRE_ALIGN(E, q); REQUIRE_ALIGN(E, dt);
+    REQUIRE_ALIGN(E, a); REQUIRE_ALIGN(E, trap); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
+    REQUIRE_ALIGN(E, h0); REQUIRE_ALIGN(E, k_prev); REQUIRE_ALIGN(E, x_prev); REQUIRE_ALIGN(E, h_final);
+    REQUIRE_ALIGN(E, workspace);
+    const void *ins[] = {x, k, q, dt, a, trap, k_prev, x_prev};
+    for (size_t j = 0; j < sizeof(ins) / sizeof(ins[0]); ++j)
+        if ((const void *)y == ins[j] || (h_final && (const void *)h_final == ins[j]))
+            return fail(SSM_ERR_INVALID_ARG, "%s: an output aliases an input", E);
+    const size_t need = ssm::ssd_trap_workspace_bytes(batch, L, nheads, headdim, d_state);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    ssm::SsdTrapArgs args{x, k, q, dt, a, trap, D, y, h0, k_prev, x_prev, h_final,
+                          batch, L, nheads, headdim, d_state, workspace};
+    const char *kn = "ssd_trap";
+    return launched(E, ssm::launch_ssd_trap(args, stream, &kn), kn);
+}
+
 size_t ssd_chunk_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                                          int64_t d_state, int64_t ngroups, int64_t chunk_len) {
     (void)ngroups; (void)chunk_len;

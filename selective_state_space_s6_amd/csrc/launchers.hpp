@@ -35,6 +35,17 @@ struct SsdArgs {
     bool bf16; uint32_t flags;
     void *workspace;
 };
+struct SsdTrapArgs {
+    const void *x; const void *k; const void *q;
+    const float *dt; const float *a; const float *trap; const float *D; float *y;
+    const float *h0; const void *k_prev; const void *x_prev; float *h_final;
+    int64_t batch, L, nheads, headdim, d_state;
+    void *workspace;
+};
+size_t ssd_trap_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                int64_t d_state);
+hipError_t launch_ssd_trap(const SsdTrapArgs &a, hipStream_t stream, const char **kernel_name);
+
 struct SsdBwdArgs {
     const void *x; const float *dt; const float *dt_bias; const float *A_log;
     const void *B; const void *C; const float *D; const float *h0;

@@ -91,6 +91,10 @@ struct SsdKp {
     int64_t batch, L, H, P, N, G;
     int64_t Ls, nseg;   // segment length (a multiple of kT) and count
     int mode;           // 0 ZOH, 1 DT, 2 ONE
+    // Mamba-3 trapezoidal form (when trap is set): dt is used as given, a_t =
+    // dt_t aval_t, the input scale is gamma_t + dt_{t+1} (1 - trap_{t+1}) and the
+    // diagonal of the intra-chunk matrix uses gamma_t = trap_t dt_t
+    const float *aval, *trap;   // (batch, L, H)
 };
 
 
@@ -99,21 +103,32 @@ struct Scal {
     float cs[kT];    // inclusive cumulative sum of a from the chunk start
     float ecs[kT];   // e^{cs_t}
     float sig[kT];   // input scale
+    float gam[kT];   // input scale of the step's own output (differs from sig in the trapezoidal form)
     float w[kT];     // e^{cs_end - cs_s} sigma_s
     float end;       // e^{cs_end}
     float csend;     // cs_end
 };
 
 // D1 for one chunk, by one wave (lanes 0..31 hold steps 0..31).
+// Trapezoidal inputs of one step (used when the kernel runs that form).
+struct TrapIn { float av, tr, dtn, trn; bool nvalid; };
+
 __device__ __forceinline__ void chunk_scalars(Scal &sc, float dtv, bool valid, float bias, float A,
-                                              int mode, int lane) {
-    float a = 0.0f, sg = 0.0f;
+                                              int mode, int lane, const TrapIn *ti = nullptr) {
+    float a = 0.0f, sg = 0.0f, gm = 0.0f;
     if (valid) {
-        const float dl = softplus(dtv + bias);
-        a = dl * A;
-        if (mode == 1) sg = dl;
-        else if (mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
-        else sg = 1.0f;
+        if (ti) {
+            a = dtv * ti->av;
+            gm = ti->tr * dtv;
+            sg = gm + (ti->nvalid ? ti->dtn * (1.0f - ti->trn) : 0.0f);
+        } else {
+            const float dl = softplus(dtv + bias);
+            a = dl * A;
+            if (mode == 1) sg = dl;
+            else if (mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
+            else sg = 1.0f;
+            gm = sg;
+        }
     }
     const float v = scan32(a);
     const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
@@ -121,6 +136,7 @@ __device__ __forceinline__ void chunk_scalars(Scal &sc, float dtv, bool valid, f
         sc.cs[lane] = v;
         sc.ecs[lane] = __expf(v);
         sc.sig[lane] = sg;
+        sc.gam[lane] = gm;
         sc.w[lane] = __expf(cend - v) * sg;
     }
     if (lane == 0) {
@@ -140,7 +156,7 @@ constexpr int x_pitch(int P) { return P == 32 ? 48 : P == 64 ? 72 : 152; }
 // plus a 32-bit per-thread offset; a chunk that crosses L clamps its step
 // index into the tensors (rows past L never contribute: their sigma and w are
 // 0 and their outputs are not stored).
-template <int NMAX, int NW, bool WITH_C, int NS = 1>
+template <int NMAX, int NW, bool WITH_C, int NS = 1, bool TRAP = false>
 struct Stager {
     static constexpr int NTHR = 64 * NW;
     static constexpr int P = 16 * NW;
@@ -156,8 +172,9 @@ struct Stager {
     // NS register stages: a chunk is loaded NS chunks before it is staged to LDS
     u32x4 rB[NS][PER_T], rC[NS][PER_T], rX[NS];
     float rdt[NS];
+    TrapIn rtp[TRAP ? NS : 1];      // trapezoidal inputs of this thread's dt step
     const uint16_t *Bb, *Cb, *Xb;   // step 0 of this (batch, group) / (batch, head)
-    const float *Db;
+    const float *Db, *Ab, *Tb;
     uint32_t colB;                  // this thread's B/C column (clamped into the state)
     int sB, nB, sX, cX, sD;
     int64_t rowBC, rowX, H, L;
@@ -177,6 +194,20 @@ struct Stager {
         Cb = p.C + (b * p.L * p.G + g) * p.N;
         Xb = p.x + (b * p.L * p.H + h) * p.P;
         Db = p.dt + b * p.L * p.H + h;
+        Ab = p.aval ? p.aval + b * p.L * p.H + h : nullptr;
+        Tb = p.trap ? p.trap + b * p.L * p.H + h : nullptr;
+    }
+    // a, trap of step t0 + i and dt, trap of step t0 + i + 1 (clamped into the
+    // sequence; nvalid marks whether that next step exists)
+    template <int S>
+    __device__ __forceinline__ void load_trap(int64_t t0, int i) {
+        const int64_t t = min(t0 + i, L - 1), tn = t0 + i + 1;
+        const int64_t tc = min(tn, L - 1);
+        rtp[S].av = Ab[t * H];
+        rtp[S].tr = Tb[t * H];
+        rtp[S].dtn = Db[tc * H];
+        rtp[S].trn = Tb[tc * H];
+        rtp[S].nvalid = tn < L;
     }
     template <int S>
     __device__ __forceinline__ void load(int64_t t0) {
@@ -191,6 +222,7 @@ struct Stager {
             }
             rX[S] = *reinterpret_cast<const u32x4 *>(Xu + (uint32_t)(sX * rowX + cX));
             rdt[S] = Du[(uint32_t)(sD * H)];
+            if constexpr (TRAP) load_trap<S>(t0, sD);
         } else {
             const int last = (int)(L - 1 - t0);   // last valid step of the chunk
 #pragma unroll
@@ -201,6 +233,7 @@ struct Stager {
             }
             rX[S] = *reinterpret_cast<const u32x4 *>(Xu + (uint32_t)(min(sX, last) * rowX + cX));
             rdt[S] = Du[(uint32_t)(min(sD, last) * H)];
+            if constexpr (TRAP) load_trap<S>(t0, min(sD, last));
         }
     }
     template <int S>
@@ -285,11 +318,11 @@ __device__ __forceinline__ void unroll_stages(F &&f) {
     }
 }
 
-template <int NMAX, bool EXACT, int NW>
+template <int NMAX, bool EXACT, int NW, bool TRAP>
 __global__ void __launch_bounds__(64 * NW)
 ssd_state_kernel(SsdKp p) {
     constexpr int NS = 3;
-    using St = Stager<NMAX, NW, false, NS>;
+    using St = Stager<NMAX, NW, false, NS, TRAP>;
     constexpr int NT = NMAX / 16;
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * St::BCP];
     __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kT * St::XP];
@@ -305,7 +338,7 @@ ssd_state_kernel(SsdKp p) {
     const int64_t g = wk.h * p.G / p.H;
     const int p0 = wid * 16;
     const int N = EXACT ? NMAX : (int)p.N;
-    const float A = -expf(p.A_log[wk.h]);
+    const float A = p.A_log ? -expf(p.A_log[wk.h]) : 0.0f;
     const float bias = p.dt_bias ? p.dt_bias[wk.h] : 0.0f;
 
     f32x4 S[NT];
@@ -321,13 +354,18 @@ ssd_state_kernel(SsdKp p) {
     // the lane-order prefix sum is the step-order suffix sum); R is the sum of
     // a over the later steps of the segment, kept by wave 0
     float R = 0.0f;
-    auto weights = [&](float *w, float dtv) __attribute__((always_inline)) {
-        const float dl = softplus(dtv + bias);
-        const float a = dl * A;
-        float sg;
-        if (p.mode == 1) sg = dl;
-        else if (p.mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
-        else sg = 1.0f;
+    auto weights = [&](float *w, float dtv, const TrapIn &ti) __attribute__((always_inline)) {
+        float a, sg;
+        if constexpr (TRAP) {
+            a = dtv * ti.av;
+            sg = ti.tr * dtv + (ti.nvalid ? ti.dtn * (1.0f - ti.trn) : 0.0f);
+        } else {
+            const float dl = softplus(dtv + bias);
+            a = dl * A;
+            if (p.mode == 1) sg = dl;
+            else if (p.mode == 0) sg = (a == 0.0f) ? dl : dl * (expm1f(a) / a);
+            else sg = 1.0f;
+        }
         const float v = scan32(a);                     // sum of a over steps >= this step
         if (lane < kT) w[kT - 1 - lane] = __expf(R + (v - a)) * sg;
         R += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
@@ -338,7 +376,7 @@ ssd_state_kernel(SsdKp p) {
         if (S_ < nch) st.template load<S_>(tlast - S_ * kT);
     });
     st.template store<0>(Bs[0], nullptr, Xs[0]);
-    if (wid == 0) weights(wsc[0], st.rdt[0]);
+    if (wid == 0) weights(wsc[0], st.rdt[0], st.rtp[0]);
     if (NS < nch) st.template load<0>(tlast - NS * kT);
     __syncthreads();
 
@@ -354,7 +392,7 @@ ssd_state_kernel(SsdKp p) {
             if (c + 1 < nch) {
                 constexpr int SN = (S_ + 1) % NS;
                 st.template store<SN>(Bs[buf ^ 1], nullptr, Xs[buf ^ 1]);
-                if (wid == 0) weights(wsc[buf ^ 1], st.rdt[SN]);
+                if (wid == 0) weights(wsc[buf ^ 1], st.rdt[SN], st.rtp[SN]);
                 if (c + 1 + NS < nch) st.template load<SN>(tlast - (c + 1 + NS) * kT);
             }
             __syncthreads();
@@ -392,10 +430,10 @@ ssd_pass_kernel(SsdKp p) {
 }
 
 // ---- outputs of one segment from the state entering it
-template <int NMAX, bool EXACT, int NW>
+template <int NMAX, bool EXACT, int NW, bool TRAP>
 __global__ void __launch_bounds__(64 * NW)
 ssd_scan_kernel(SsdKp p) {
-    using St = Stager<NMAX, NW, true>;
+    using St = Stager<NMAX, NW, true, 1, TRAP>;
     constexpr int NT = NMAX / 16;          // state tiles (16 states each) per wave
     constexpr int BCP = St::BCP, XP = St::XP;
     // Once a chunk's C tile has been consumed (after the first barrier of the
@@ -418,7 +456,7 @@ ssd_scan_kernel(SsdKp p) {
     const int64_t g = wk.h * p.G / p.H;
     const int p0 = wid * 16;                 // this wave's first head channel
     const int N = EXACT ? NMAX : (int)p.N;   // compile-time when the state size is exact
-    const float A = -expf(p.A_log[wk.h]);
+    const float A = p.A_log ? -expf(p.A_log[wk.h]) : 0.0f;
     const float bias = p.dt_bias ? p.dt_bias[wk.h] : 0.0f;
     const float Dh = p.D ? p.D[wk.h] : 0.0f;
     const int64_t rowX = p.H * p.P;
@@ -446,7 +484,9 @@ ssd_scan_kernel(SsdKp p) {
     const int64_t nchunks = (te - tb + kT - 1) / kT;
     st.template load<0>(tb);
     st.template store<0>(Bs[0], Cs[0], Xs[0]);
-    if (wid == NW - 1) chunk_scalars(scal[0], st.rdt[0], tb + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane);
+    if (wid == NW - 1)
+        chunk_scalars(scal[0], st.rdt[0], tb + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane,
+                      TRAP ? &st.rtp[0] : nullptr);
     if (nchunks > 1) st.template load<0>(tb + kT);
     __syncthreads();
 
@@ -475,13 +515,16 @@ ssd_scan_kernel(SsdKp p) {
             }
             const float4 cs4 = *reinterpret_cast<const float4 *>(&sc.cs[sT * 16 + q * 4]);
             const float4 sg4 = *reinterpret_cast<const float4 *>(&sc.sig[sT * 16 + q * 4]);
+            const float4 gm4 = TRAP ? *reinterpret_cast<const float4 *>(&sc.gam[sT * 16 + q * 4]) : sg4;
             const float csA[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, sgA[4] = {sg4.x, sg4.y, sg4.z, sg4.w};
+            const float gmA[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
             const float ct = sc.cs[tT * 16 + c16];
             float m[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool keep = (sT < tT) || (q * 4 + i <= c16);     // s <= t
-                m[i] = keep ? G[i] * __expf(ct - csA[i]) * sgA[i] : 0.0f;
+                const bool diag = (sT == tT) && (q * 4 + i == c16);    // s == t
+                m[i] = keep ? G[i] * __expf(ct - csA[i]) * (diag ? gmA[i] : sgA[i]) : 0.0f;
             }
             const uint2 u0 = split_bf16(m[0], m[1]), u1 = split_bf16(m[2], m[3]);
             uint32_t *mh = reinterpret_cast<uint32_t *>(&Ms[tT][0][lane]);
@@ -574,7 +617,7 @@ ssd_scan_kernel(SsdKp p) {
             st.template store<0>(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1]);
             if (wid == NW - 1)   // the wave with the least decay-mask work
                 chunk_scalars(scal[buf ^ 1], st.rdt[0], t0 + kT + (lane & 31) < p.L && lane < kT, bias, A,
-                              p.mode, lane);
+                              p.mode, lane, TRAP ? &st.rtp[0] : nullptr);
             if (j + 2 < nchunks) st.template load<0>(t0 + 2 * kT);
         }
         __syncthreads();
@@ -588,6 +631,22 @@ ssd_scan_kernel(SsdKp p) {
             *reinterpret_cast<float4 *>(dst) = make_float4(S[nt][0], S[nt][1], S[nt][2], S[nt][3]);
         }
     }
+}
+
+// Trapezoidal form: the carried previous input enters the state before step 0,
+// h0' = h0 + dt_0 (1 - trap_0) x_prev (x) k_prev  (the shifted state of step -1).
+__global__ void __launch_bounds__(256)
+ssd_trap_h0_kernel(SsdKp p, const uint16_t *x_prev, const uint16_t *k_prev, float *h0p) {
+    const int64_t PN = p.P * p.N, tot = p.batch * p.H * PN;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= tot) return;
+    const int64_t bh = i / PN, e = i % PN, pp = e / p.N, n = e % p.N;
+    const int64_t b = bh / p.H, h = bh % p.H;
+    const int64_t o = b * p.L * p.H + h;                  // step 0 of (b, h)
+    const float c = p.dt[o] * (1.0f - p.trap[o]);
+    const float xv = __uint_as_float(((uint32_t)x_prev[bh * p.P + pp]) << 16);
+    const float kv = __uint_as_float(((uint32_t)k_prev[bh * p.N + n]) << 16);
+    h0p[i] = fmaf(c * xv, kv, p.h0 ? p.h0[i] : 0.0f);
 }
 
 struct Plan {
@@ -604,30 +663,30 @@ Plan plan(int64_t batch, int64_t L, int64_t H, int64_t P) {
 }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-template <int NMAX, bool EXACT, int NW>
+template <int NMAX, bool EXACT, int NW, bool TRAP>
 void launch_all(const SsdKp &p, hipStream_t stream) {
     if (p.nseg > 1) {
         const int64_t n1 = p.batch * (p.nseg - 1) * p.H;
-        hipLaunchKernelGGL((ssd_state_kernel<NMAX, EXACT, NW>), dim3((unsigned)n1), dim3(64 * NW), 0, stream, p);
+        hipLaunchKernelGGL((ssd_state_kernel<NMAX, EXACT, NW, TRAP>), dim3((unsigned)n1), dim3(64 * NW), 0, stream, p);
         const int64_t nt = p.batch * p.H * p.P * p.N / 4;
         hipLaunchKernelGGL(ssd_pass_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream, p);
     }
     const int64_t n = p.batch * p.nseg * p.H;
-    hipLaunchKernelGGL((ssd_scan_kernel<NMAX, EXACT, NW>), dim3((unsigned)n), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((ssd_scan_kernel<NMAX, EXACT, NW, TRAP>), dim3((unsigned)n), dim3(64 * NW), 0, stream, p);
 }
 
-template <int NW>
+template <int NW, bool TRAP>
 void launch_n(const SsdKp &p, hipStream_t stream) {
     // the B/C tile is at least P wide so that its pieces divide over the group
     constexpr int NMIN = 16 * NW < 64 ? 64 : 16 * NW;
     if constexpr (NMIN == 64) {
-        if (p.N == 64) return launch_all<64, true, NW>(p, stream);
-        if (p.N < 64) return launch_all<64, false, NW>(p, stream);
+        if (p.N == 64) return launch_all<64, true, NW, TRAP>(p, stream);
+        if (p.N < 64) return launch_all<64, false, NW, TRAP>(p, stream);
     }
-    if (p.N == 128) return launch_all<128, true, NW>(p, stream);
-    if (p.N < 128) return launch_all<128, false, NW>(p, stream);
-    if (p.N == 256) return launch_all<256, true, NW>(p, stream);
-    launch_all<256, false, NW>(p, stream);
+    if (p.N == 128) return launch_all<128, true, NW, TRAP>(p, stream);
+    if (p.N < 128) return launch_all<128, false, NW, TRAP>(p, stream);
+    if (p.N == 256) return launch_all<256, true, NW, TRAP>(p, stream);
+    launch_all<256, false, NW, TRAP>(p, stream);
 }
 
 }  // namespace
@@ -638,6 +697,45 @@ size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t hea
     if (pl.nseg <= 1) return 0;
     return align256((size_t)(batch * nheads * pl.nseg * headdim * d_state) * sizeof(float)) +
            (size_t)(batch * nheads * pl.nseg) * sizeof(float);
+}
+
+size_t ssd_trap_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state) {
+    return align256(ssd_workspace_bytes(batch, L, nheads, headdim, d_state, 0)) +
+           align256((size_t)(batch * nheads * headdim * d_state) * sizeof(float));
+}
+
+hipError_t launch_ssd_trap(const SsdTrapArgs &a, hipStream_t stream, const char **kernel_name) {
+    *kernel_name = "ssd_scan_kernel";
+    SsdKp p{};
+    p.x = static_cast<const uint16_t *>(a.x);
+    p.dt = a.dt; p.dt_bias = nullptr; p.A_log = nullptr;
+    p.B = static_cast<const uint16_t *>(a.k);
+    p.C = static_cast<const uint16_t *>(a.q);
+    p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
+    p.batch = a.batch; p.L = a.L; p.H = a.nheads; p.P = a.headdim; p.N = a.d_state; p.G = a.nheads;
+    p.mode = 1;
+    p.aval = a.a; p.trap = a.trap;
+    const Plan pl = plan(p.batch, p.L, p.H, p.P);
+    p.nseg = pl.nseg;
+    p.Ls = pl.Ls;
+    char *ws = static_cast<char *>(a.workspace);
+    if (p.nseg > 1) {
+        p.ws_state = reinterpret_cast<float *>(ws);
+        p.ws_decay = reinterpret_cast<float *>(ws + align256((size_t)(p.batch * p.H * p.nseg * p.P * p.N) * sizeof(float)));
+    }
+    if (a.x_prev) {
+        float *h0p = reinterpret_cast<float *>(ws + align256(ssd_workspace_bytes(p.batch, p.L, p.H, p.P, p.N, 0)));
+        const int64_t tot = p.batch * p.H * p.P * p.N;
+        *kernel_name = "ssd_trap_h0_kernel";
+        hipLaunchKernelGGL(ssd_trap_h0_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, p,
+                           static_cast<const uint16_t *>(a.x_prev), static_cast<const uint16_t *>(a.k_prev), h0p);
+        p.h0 = h0p;
+        *kernel_name = "ssd_scan_kernel";
+    }
+    if (p.P == 32) launch_n<2, true>(p, stream);
+    else if (p.P == 64) launch_n<4, true>(p, stream);
+    else launch_n<8, true>(p, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_name) {
@@ -659,9 +757,9 @@ hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_
             static_cast<char *>(a.workspace) +
             align256((size_t)(p.batch * p.H * p.nseg * p.P * p.N) * sizeof(float)));
     }
-    if (p.P == 32) launch_n<2>(p, stream);
-    else if (p.P == 64) launch_n<4>(p, stream);
-    else launch_n<8>(p, stream);
+    if (p.P == 32) launch_n<2, false>(p, stream);
+    else if (p.P == 64) launch_n<4, false>(p, stream);
+    else launch_n<8, false>(p, stream);
     return hipGetLastError();
 }
 

@@ -29,6 +29,9 @@ WORKLOADS = {
     # SSD long context: 2 x 32768, 80 heads x 64, N=128, G=8, Q=256, bf16, with final state
     "ssd_long": dict(kind="ssd", batch=2, L=32768, nheads=80, headdim=64, d_state=128, ngroups=8,
                      chunk_len=256, dtype="bf16"),
+    # Mamba-3 trapezoidal SSD: 4 x 8192, 32 heads x 64, N=128, per-head k/q, Q=64, bf16
+    "trap_mamba3": dict(kind="trap", batch=4, L=8192, nheads=32, headdim=64, d_state=128,
+                        chunk_len=64, dtype="bf16"),
     # complex-state SSD: 4 x 8192, 32 heads x 64, 32 complex states, Q=64, fp32
     "cssd_mamba3": dict(kind="cssd", batch=4, L=8192, nheads=32, headdim=64, n_complex=32,
                         ngroups=1, chunk_len=64, dtype="f32"),
@@ -176,6 +179,31 @@ def cssd_inputs(batch, L, nheads, headdim, n_complex, ngroups, *, seed=(0,), h0=
                   dict(x=x, dt=dt, dt_bias=bias, A_log=A_log, B=B, C=C, D=Dv, h0=h0a), ())
 
 
+def trap_inputs(batch, L, nheads, headdim, d_state, *, seed=(0,), h0=False, prev=False,
+                D="normal", trap="uniform") -> Inputs:
+    """Mamba-3 trapezoidal inputs: dt log-uniform on [1e-3, 1e-1] (a positive step, as
+    after softplus), a = -exp(U(0, log 16)) per step, trap U(0, 1) (as after a sigmoid)
+    or the constant 0 / 1; x, k, q, x_prev, k_prev N(0, 1) rounded to bf16."""
+    key = (5, *seed)
+    x = round_bf16(_normal(_rng(key, 0), (batch, L, nheads, headdim)))
+    k = round_bf16(_normal(_rng(key, 1), (batch, L, nheads, d_state)))
+    q = round_bf16(_normal(_rng(key, 2), (batch, L, nheads, d_state)))
+    dt = np.exp(_uniform(_rng(key, 3), (batch, L, nheads), math.log(1e-3), math.log(1e-1)))
+    a = -np.exp(_uniform(_rng(key, 4), (batch, L, nheads), 0.0, math.log(16.0)))
+    if trap == "uniform":
+        tr = _uniform(_rng(key, 5), (batch, L, nheads), 0.0, 1.0)
+    else:
+        tr = np.full((batch, L, nheads), float(trap), np.float32)
+    Dv = _normal(_rng(key, 6), (nheads,), 1.0, 0.1) if D == "normal" else None
+    h0a = _normal(_rng(key, 7), (batch, nheads, headdim, d_state)) if h0 else None
+    kp = round_bf16(_normal(_rng(key, 8), (batch, nheads, d_state))) if prev else None
+    xp = round_bf16(_normal(_rng(key, 9), (batch, nheads, headdim))) if prev else None
+    return Inputs("trap", dict(batch=batch, L=L, nheads=nheads, headdim=headdim, d_state=d_state),
+                  dict(x=x, k=k, q=q, dt=dt.astype(np.float32), a=a.astype(np.float32), trap=tr,
+                       D=Dv, h0=h0a, k_prev=kp, x_prev=xp),
+                  ("x", "k", "q", "k_prev", "x_prev"))
+
+
 def workload_inputs(name: str, seed=(0,)) -> Inputs:
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")
@@ -185,6 +213,8 @@ def workload_inputs(name: str, seed=(0,)) -> Inputs:
     if kind == "ssd":
         return ssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"],
                           w["ngroups"], seed=seed, dtype=w["dtype"])
+    if kind == "trap":
+        return trap_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"], seed=seed)
     return cssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["n_complex"],
                        w["ngroups"], seed=seed)
 

@@ -46,6 +46,15 @@ def gpu_ssd(inp, device, flags, chunk_len):
     return y.cpu().numpy(), hf.cpu().numpy()
 
 
+def gpu_trap(inp, device, chunk_len=64):
+    t = inp.torch(device)
+    y, hf = lib().ssd_trap_chunk_scan_fwd(t["x"], t["k"], t["q"], t["dt"], t["a"], t["trap"], t["D"],
+                                          t["h0"], t["k_prev"], t["x_prev"], chunk_len=chunk_len,
+                                          return_final=True)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), hf.cpu().numpy()
+
+
 def gpu_cssd(inp, device, flags, chunk_len):
     t = inp.torch(device)
     y, hf = lib().ssd_cplx_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"],

@@ -30,6 +30,9 @@ def lib():
     L.ssd_cplx_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_uint32, P, Z, P]
     L.ssm_s6_scan_bwd.argtypes = [P] * 18 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_chunk_scan_bwd.argtypes = [P] * 18 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
+    L.ssd_trap_chunk_scan_fwd.argtypes = [P] * 12 + [I] * 6 + [ctypes.c_int, P, Z, P]
+    L.ssd_trap_chunk_scan_fwd_workspace_size.argtypes = [I] * 6
+    L.ssd_trap_chunk_scan_fwd_workspace_size.restype = Z
     for f in ("ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size"):
         getattr(L, f).argtypes = [I] * 4
         getattr(L, f).restype = Z
@@ -48,6 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
                      "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
+                     "ssd_trap_chunk_scan_fwd_workspace_size", "ssd_trap_chunk_scan_fwd",
                      "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd"}
     for n in names:
         assert hasattr(lib, n), n
@@ -181,3 +185,35 @@ def test_cssd_argument_checks(lib):
     assert lib.ssd_cplx_chunk_scan_fwd_workspace_size(2, 100, 4, 64, 32, 2, 64) == 0
     assert _cssd(lib, dims=long_dims, ws=None) == WORKSPACE
     assert _cssd(lib, dims=long_dims, wsb=need - 1) == WORKSPACE
+
+
+def _trap(lib, dims=(2, 300, 4, 64, 128, 64), dtype=1, ws=ctypes.c_void_p(0x9000000), wsb=1 << 40,
+          **kw):
+    names = ["x", "k", "q", "dt", "a", "trap", "D", "y", "h0", "k_prev", "x_prev", "h_final"]
+    required = {"x", "k", "q", "dt", "a", "trap", "y"}
+    ptrs = {n: (ctypes.c_void_p(0x100000 * (i + 1)) if n in required else None)
+            for i, n in enumerate(names)}
+    ptrs.update(kw)
+    return lib.ssd_trap_chunk_scan_fwd(*(ptrs[n] for n in names), *dims, dtype, ws, wsb, None)
+
+
+def test_trap_argument_checks(lib):
+    assert _trap(lib, trap=None) == INVALID and "trap is NULL" in _err(lib)
+    assert _trap(lib, q=None) == INVALID and "q is NULL" in _err(lib)
+    assert _trap(lib, dims=(2, 0, 4, 64, 128, 64)) == INVALID and "L" in _err(lib)
+    assert _trap(lib, dims=(2, 300, 4, 48, 128, 64)) == UNSUPPORTED and "headdim" in _err(lib)
+    assert _trap(lib, dims=(2, 300, 4, 64, 96 + 8, 64)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _trap(lib, dims=(2, 300, 4, 64, 128, 32)) == UNSUPPORTED and "chunk_len" in _err(lib)
+    assert _trap(lib, dtype=0) == UNSUPPORTED and "bf16" in _err(lib)
+    assert _trap(lib, dtype=5) == INVALID and "in_dtype" in _err(lib)
+    # the carried previous input comes as a pair
+    assert _trap(lib, k_prev=ctypes.c_void_p(0xA000000)) == INVALID and "together" in _err(lib)
+    assert _trap(lib, a=MIS) == UNSUPPORTED and "aligned" in _err(lib)
+    assert _trap(lib, y=ctypes.c_void_p(0x200000)) == INVALID and "alias" in _err(lib)       # y == k
+    assert _trap(lib, h_final=ctypes.c_void_p(0x600000)) == INVALID and "alias" in _err(lib)  # == trap
+    need = lib.ssd_trap_chunk_scan_fwd_workspace_size(2, 300, 4, 64, 128, 64)
+    # always at least the entering state with the carried input folded in
+    assert need >= 2 * 4 * 64 * 128 * 4
+    assert _trap(lib, ws=None) == WORKSPACE and "workspace" in _err(lib)
+    assert _trap(lib, wsb=need - 1) == WORKSPACE
+    assert lib.ssd_trap_chunk_scan_fwd_workspace_size(2, 0, 4, 64, 128, 64) == 0
