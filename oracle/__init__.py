@@ -70,6 +70,7 @@ def _load():
     lib.oracle_s6_bwd.argtypes = [P] * 10 + [I, I, I, I, ctypes.c_uint32, I, I, I, I] + [P] * 8 + [ctypes.c_int]
     lib.oracle_ssd_bwd.argtypes = [P] * 10 + [I] * 6 + [ctypes.c_uint32, P, I] + [P] * 8 + [ctypes.c_int]
     lib.oracle_trap_fwd.argtypes = [P] * 10 + [I] * 5 + [P, I, P, P, ctypes.c_int]
+    lib.oracle_trap_rotate.argtypes = [P] * 5 + [I] * 5 + [P] * 3
     for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd, lib.oracle_s6_bwd,
               lib.oracle_ssd_bwd, lib.oracle_trap_fwd):
         f.restype = None
@@ -192,6 +193,24 @@ def trap_fwd(x, k, q, dt, a, trap, D=None, h0=None, k_prev=None, x_prev=None, un
     if full:
         return (y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(), hf.reshape(batch, H, P, N))
     return y, hf
+
+
+def trap_rotate(k, q, angles, dt, angle_state=None):
+    """Data-dependent rotation of k and q in fp64 (Mamba-3 angle accumulation + RoPE).
+
+    k, q: (batch, L, H, N); angles: (batch, L, n_angles), 2 n_angles <= N; dt: (batch, L, H);
+    angle_state: (batch, H, n_angles) or None.  Returns k', q' (batch, L, H, N) and the
+    final angles (batch, H, n_angles)."""
+    k, q, angles, dt, angle_state = map(_f32, (k, q, angles, dt, angle_state))
+    batch, L, H, N = k.shape
+    NA = angles.shape[2]
+    assert 2 * NA <= N and angles.shape[:2] == (batch, L) and dt.shape == (batch, L, H)
+    ko = np.empty((batch, L, H, N), np.float64)
+    qo = np.empty((batch, L, H, N), np.float64)
+    so = np.empty((batch, H, NA), np.float64)
+    _load().oracle_trap_rotate(_ptr(k), _ptr(q), _ptr(angles), _ptr(dt), _ptr(angle_state),
+                               batch, L, H, N, NA, _ptr(ko), _ptr(qo), _ptr(so))
+    return ko, qo, so
 
 
 def ssd_bwd(x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, ngroups=1, flags=BBAR_DT,

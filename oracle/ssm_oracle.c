@@ -743,6 +743,51 @@ void oracle_trap_fwd(const float *x, const float *k, const float *q, const float
     run_units(4, &j, n_units, nthreads);
 }
 
+/* ------------------------------------- Mamba-3 data-dependent rotation --- */
+/*
+ * mamba-rs 0.2.1, src/mamba3_siso/gpu/mamba3_gpu.rs, F5 (m3_angle_dt_fwd_seq:
+ * angle * dt accumulated step by step per batch row, carried in angle_state)
+ * and F4e+f (rope_fwd: k, q rotated by the accumulated angles).  Per (b, h)
+ * and angle j < n_angles:
+ *   theta_t[j] = angle_state[b,h,j] + sum_{s<=t} angles[b,s,j] dt[b,s,h]
+ *   (k'[2j], k'[2j+1]) = (k[2j] cos theta - k[2j+1] sin theta,
+ *                         k[2j] sin theta + k[2j+1] cos theta)
+ * and the same for q; components 2 n_angles .. d_state-1 are unchanged.
+ * state_out[b,h,j] = theta_{L-1}[j] (angle_state when L == 0).
+ * k, q, k_out, q_out (B, L, H, N); angles (B, L, n_angles); dt (B, L, H);
+ * angle_state, state_out (B, H, n_angles).
+ */
+void oracle_trap_rotate(const float *k, const float *q, const float *angles, const float *dt,
+                        const float *angle_state, int64_t batch, int64_t L, int64_t nheads,
+                        int64_t d_state, int64_t n_angles, double *k_out, double *q_out,
+                        double *state_out)
+{
+    const int64_t H = nheads, N = d_state, NA = n_angles;
+    double *th = (double *)malloc(sizeof(double) * (size_t)(NA > 0 ? NA : 1));
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+            for (int64_t j = 0; j < NA; ++j)
+                th[j] = angle_state ? (double)angle_state[(b * H + h) * NA + j] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const double d = (double)dt[(b * L + t) * H + h];
+                const int64_t o = ((b * L + t) * H + h) * N;
+                for (int64_t j = 0; j < NA; ++j) th[j] += (double)angles[(b * L + t) * NA + j] * d;
+                for (int64_t n = 0; n < N; ++n) { k_out[o + n] = (double)k[o + n]; q_out[o + n] = (double)q[o + n]; }
+                for (int64_t j = 0; j < NA; ++j) {
+                    const double c = cos(th[j]), sn = sin(th[j]);
+                    const double k0 = (double)k[o + 2 * j], k1 = (double)k[o + 2 * j + 1];
+                    const double q0 = (double)q[o + 2 * j], q1 = (double)q[o + 2 * j + 1];
+                    k_out[o + 2 * j] = k0 * c - k1 * sn;
+                    k_out[o + 2 * j + 1] = k0 * sn + k1 * c;
+                    q_out[o + 2 * j] = q0 * c - q1 * sn;
+                    q_out[o + 2 * j + 1] = q0 * sn + q1 * c;
+                }
+            }
+            for (int64_t j = 0; j < NA; ++j) state_out[(b * H + h) * NA + j] = th[j];
+        }
+    free(th);
+}
+
 double oracle_softplus(double x) { return sp(x); }
 double oracle_phi1(double z) { return phi1(z); }
 double oracle_dphi1(double z) { return dphi1(z); }
