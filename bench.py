@@ -106,6 +106,15 @@ def trap_model(d):
     return elems, bytes_, flops
 
 
+def trap_rot_model(d):
+    """Rotation of k and q: read k, q (bf16), angles, dt and the angle state; write k, q and
+    the final angles.  Elements are (b, t, h, head channel) as for the scan it feeds."""
+    B, L, H, P, N, NA = d["batch"], d["L"], d["nheads"], d["headdim"], d["d_state"], d["n_angles"]
+    elems = B * L * H * P
+    bytes_ = 4 * B * L * H * N * 2 + B * L * NA * 4 + B * L * H * 4 + 2 * B * H * NA * 4
+    return elems, bytes_, 0
+
+
 def cssd_model(d):
     B, L, H, P, Nc, G, Q = (d["batch"], d["L"], d["nheads"], d["headdim"], d["n_complex"],
                             d["ngroups"], d["chunk_len"])
@@ -183,6 +192,26 @@ def make_runner(name, dev):
         w["kind"] = "ssd_bwd"
         return step, dims, w, ["ssdb_walk_f", "ssdb_walk_r1", "ssdb_walk_r2", "ssdb_pass_f", "ssdb_pass_r",
                                "ssdb_reduce_heads", "ssdb_scal", "ssdb_final"]
+    if kind == "trap_rot":
+        t0 = copies[0]
+        angs = []
+        for r in range(N_ROTATE):
+            ang, st = synth.rotation_inputs(dims["batch"], dims["L"], dims["nheads"], w["n_angles"],
+                                            seed=(r,))
+            angs.append((torch.from_numpy(ang).to(dev), torch.from_numpy(st).to(dev)))
+        ko, qo = torch.empty_like(t0["k"]), torch.empty_like(t0["q"])
+        so = torch.empty_like(angs[0][1])
+        ws = torch.empty(max(1, lib.ssd_trap_rotate_qk_workspace_size(
+            dims["batch"], dims["L"], dims["nheads"], dims["d_state"], w["n_angles"])),
+            dtype=torch.uint8, device=dev)
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            ang, st = angs[i % N_ROTATE]
+            lib.ssd_trap_rotate_qk(t["k"], t["q"], ang, t["dt"], st, k=ko, q=qo, angle_state_out=so,
+                                   workspace=ws)
+        dims = dict(dims, n_angles=w["n_angles"])
+        return step, dims, w, ["trap_rot_sums4_kernel", "trap_rot_apply4_kernel"]
     if kind == "trap":
         t0 = copies[0]
         y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
@@ -302,6 +331,15 @@ def cpu_baseline_units(name, n_units):
     nthr = oracle.default_threads()
     n_units = min(n_units, d["batch"] * d["nheads"])
     units = np.stack([np.arange(n_units) % d["batch"], np.arange(n_units) // d["batch"]], 1)
+    if w["kind"] == "trap_rot":      # one batch row of the rotation (single-threaded oracle)
+        a = inp.arrays
+        ang, st = synth.rotation_inputs(1, d["L"], d["nheads"], w["n_angles"])
+        t0 = time.perf_counter()
+        oracle.trap_rotate(a["k"][:1], a["q"][:1], ang, a["dt"][:1], st)
+        sec = time.perf_counter() - t0
+        elems = d["L"] * d["nheads"] * d["headdim"]
+        return {"value": elems / sec, "unit": "elements/s", "cores": 1, "kind": "oracle",
+                "sample": f"1 of {d['batch']} batch rows of {name} ({elems} elements, {sec:.2f} s wall)"}
     t0 = time.perf_counter()
     if w["kind"] == "trap":
         oracle.trap_fwd(**inp.arrays, units=units, nthreads=nthr)
@@ -341,6 +379,8 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = ssd_model(dims)
     elif kind == "trap":
         elems, bytes_, ops = trap_model(dims)
+    elif kind == "trap_rot":
+        elems, bytes_, ops = trap_rot_model(dims)
     else:
         elems, bytes_, ops = cssd_model(dims)
     ev_ms = sorted(per)[len(per) // 2]
@@ -405,7 +445,8 @@ def main():
     if not args.no_secondary and args.workload == "s6_mamba1":
         sec = []
         for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
-                            ("trap_mamba3", 5), ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
+                            ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("s6_mamba1_bwd", 10),
+                            ("ssd_mamba2_bwd", 5)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
             es = s["event_ms_median"] * 1e-3

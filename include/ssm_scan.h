@@ -1,6 +1,6 @@
 /*
- * ssm_scan.h -- C interface of libssmscan.so, the MI355X (gfx950) forward
- * selective state-space scan library.
+ * ssm_scan.h -- C interface of libssmscan.so, the MI355X (gfx950) selective
+ * state-space scan library (forward scans and their gradients).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -32,8 +32,8 @@
  *   [RS-M1]   mamba-rs 0.4.0, src/mamba_ssm/gpu/forward.rs
  *             (gpu_forward_mamba_layer, step F4d, and GpuMambaDims)
  *   [RS-M3]   mamba-rs 0.2.1, src/mamba3_siso/gpu/mamba3_gpu.rs
- *             (gpu_forward_mamba3_layer, step F6, kernels K2-K5 and the
- *             final-state writeback)
+ *             (module header; gpu_forward_mamba3_layer, steps F4e+f, F5,
+ *             F5b and F6, kernels K2-K5 and the final-state writeback)
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
@@ -267,6 +267,39 @@ int ssd_trap_chunk_scan_fwd(const void *x, const void *k, const void *q, const f
                             int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
                             int64_t chunk_len, ssm_dtype_t in_dtype,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------- Mamba-3 k, q rotation ----
+ * Data-dependent rotation of k and q ahead of ssd_trap_chunk_scan_fwd [RS-M3
+ * F5 m3_angle_dt_fwd_seq (angle * dt accumulated per step, carried in the
+ * layer's angle state) and F4e+f rope_fwd (k and q turned by the accumulated
+ * angles)].  Per (b, h) and angle j < n_angles:
+ *   theta_t[j] = angle_state[b,h,j] + sum_{s<=t} angles[b,s,j] * dt[b,s,h]
+ *   (k[2j], k[2j+1]) = (kr[2j] cos theta - kr[2j+1] sin theta, kr[2j] sin theta + kr[2j+1] cos theta)
+ * and the same for q; pairs j >= n_angles are copied unchanged, and
+ * angle_state_out[b,h,j] = theta_{L-1}[j].  The page shows these launches but
+ * not their bodies: the pairing (2j, 2j+1) and the direction of the turn are
+ * the reading under which a rotated scan with trap = 1 is the complex-diagonal
+ * SSD with lambda = -exp(l) + i phi for angles = -phi.
+ * Arithmetic is fp32 (the angle is accumulated per segment of the sequence,
+ * then step by step), the outputs are rounded once to bf16.
+ *
+ * Layouts: k_raw, q_raw, k, q (batch, L, nheads, d_state) bf16; angles
+ * (batch, L, n_angles) fp32, shared by the heads; dt (batch, L, nheads) fp32
+ * (as given to the scan); angle_state, angle_state_out (batch, nheads,
+ * n_angles) fp32 or NULL (zero / not written).  k may be k_raw and q may be
+ * q_raw (in place); angle_state_out may be angle_state; no other aliasing.
+ * Limits: in_dtype SSM_BF16; d_state even, <= 256; 0 <= n_angles <= d_state/2
+ * (0 copies k and q; angles may then be NULL).
+ * Workspace: ssd_trap_rotate_qk_workspace_size() bytes, 16-byte aligned, owned
+ * by the caller (one fp32 angle sum per (batch, segment, head, angle) and a
+ * copy of the entering angle state). */
+size_t ssd_trap_rotate_qk_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t d_state,
+                                         int64_t n_angles);
+
+int ssd_trap_rotate_qk(const void *k_raw, const void *q_raw, const float *angles, const float *dt,
+                       const float *angle_state, void *k, void *q, float *angle_state_out,
+                       int64_t batch, int64_t L, int64_t nheads, int64_t d_state, int64_t n_angles,
+                       ssm_dtype_t in_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------- complex SSD ----
  * Mamba-3-style SSD with a complex diagonal state [BF-CSSD header,

@@ -19,6 +19,7 @@ __all__ = [
     "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssd_chunk_scan_fwd", "ssd_chunk_scan_bwd",
     "ssd_cplx_chunk_scan_fwd", "ssd_trap_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size",
     "ssm_s6_scan_bwd_workspace_size", "ssd_trap_chunk_scan_fwd_workspace_size",
+    "ssd_trap_rotate_qk", "ssd_trap_rotate_qk_workspace_size",
     "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
     "ssd_cplx_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
     "SSM_BBAR_ZOH", "SSM_BBAR_DT", "SSM_BBAR_ONE", "SSM_CPLX_STABLE", "SSM_CPLX_DOC",
@@ -58,6 +59,10 @@ _lib.ssd_trap_chunk_scan_fwd_workspace_size.argtypes = [_I] * 6
 _lib.ssd_trap_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_trap_chunk_scan_fwd.argtypes = [_P] * 12 + [_I] * 6 + [ctypes.c_int, _P, _Z, _P]
 _lib.ssd_trap_chunk_scan_fwd.restype = ctypes.c_int
+_lib.ssd_trap_rotate_qk_workspace_size.argtypes = [_I] * 5
+_lib.ssd_trap_rotate_qk_workspace_size.restype = _Z
+_lib.ssd_trap_rotate_qk.argtypes = [_P] * 8 + [_I] * 5 + [ctypes.c_int, _P, _Z, _P]
+_lib.ssd_trap_rotate_qk.restype = ctypes.c_int
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_cplx_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_uint32, _P, _Z, _P]
@@ -290,6 +295,42 @@ def ssd_trap_chunk_scan_fwd(x, k, q, dt, a, trap, D=None, h0=None, k_prev=None, 
                                       _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ssd_trap_rotate_qk_workspace_size(batch, L, nheads, d_state, n_angles) -> int:
+    return int(_lib.ssd_trap_rotate_qk_workspace_size(batch, L, nheads, d_state, n_angles))
+
+
+def ssd_trap_rotate_qk(k_raw, q_raw, angles, dt, angle_state=None, *, k=None, q=None,
+                       angle_state_out=None, return_state=False, workspace=None):
+    """Mamba-3 data-dependent rotation of k and q.  k_raw, q_raw (batch, L, H, N) bf16;
+    angles (batch, L, n_angles) fp32 (2 n_angles <= N); dt (batch, L, H) fp32; angle_state
+    (batch, H, n_angles) fp32 or None.  Returns (k, q), or (k, q, angle_state_out) when
+    return_state.  k=k_raw, q=q_raw and angle_state_out=angle_state update in place."""
+    dev = k_raw.device
+    batch, L, H, N = k_raw.shape
+    NA = angles.shape[2]
+    _req(k_raw, "k_raw", torch.bfloat16, (batch, L, H, N), dev)
+    _req(q_raw, "q_raw", torch.bfloat16, (batch, L, H, N), dev)
+    _req(angles, "angles", torch.float32, (batch, L, NA), dev)
+    _req(dt, "dt", torch.float32, (batch, L, H), dev)
+    _opt(angle_state, "angle_state", torch.float32, (batch, H, NA), dev)
+    k = torch.empty_like(k_raw) if k is None else k
+    q = torch.empty_like(q_raw) if q is None else q
+    _req(k, "k", torch.bfloat16, (batch, L, H, N), dev)
+    _req(q, "q", torch.bfloat16, (batch, L, H, N), dev)
+    if return_state and angle_state_out is None:
+        angle_state_out = torch.empty((batch, H, NA), dtype=torch.float32, device=dev)
+    _opt(angle_state_out, "angle_state_out", torch.float32, (batch, H, NA), dev)
+    ws = ssd_trap_rotate_qk_workspace_size(batch, L, H, N, NA)
+    if workspace is None:
+        workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+    rc = _lib.ssd_trap_rotate_qk(_ptr(k_raw), _ptr(q_raw), _ptr(angles), _ptr(dt), _ptr(angle_state),
+                                 _ptr(k), _ptr(q), _ptr(angle_state_out), batch, L, H, N, NA,
+                                 _in_dtype(k_raw), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return (k, q, angle_state_out) if (return_state or angle_state_out is not None) else (k, q)
 
 
 _SSD_GRADS = ("dx", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")

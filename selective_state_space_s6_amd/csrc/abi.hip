@@ -255,6 +255,60 @@ int ssd_trap_chunk_scan_fwd(const void *x, const void *k, const void *q, const f
     return launched(E, ssm::launch_ssd_trap(args, stream, &kn), kn);
 }
 
+size_t ssd_trap_rotate_qk_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t d_state,
+                                         int64_t n_angles) {
+    if (batch <= 0 || L <= 0 || nheads <= 0 || d_state <= 0 || n_angles < 0) return 0;
+    return ssm::trap_rotate_workspace_bytes(batch, L, nheads, d_state, n_angles);
+}
+
+int ssd_trap_rotate_qk(const void *k_raw, const void *q_raw, const float *angles, const float *dt,
+                       const float *angle_state, void *k, void *q, float *angle_state_out,
+                       int64_t batch, int64_t L, int64_t nheads, int64_t d_state, int64_t n_angles,
+                       ssm_dtype_t in_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssd_trap_rotate_qk";
+    REQUIRE_PTR(E, k_raw); REQUIRE_PTR(E, q_raw); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, k); REQUIRE_PTR(E, q);
+    REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, nheads); REQUIRE_POS(E, d_state);
+    if (n_angles < 0)
+        return fail(SSM_ERR_INVALID_ARG, "%s: n_angles must be >= 0 (got %lld)", E, (long long)n_angles);
+    if (n_angles > 0) REQUIRE_PTR(E, angles);
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if (in_dtype != SSM_BF16)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: k and q are bf16 (SSM_BF16)", E);
+    if (d_state % 2 != 0 || d_state > SSM_MAX_D_STATE)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld must be even and <= %d", E, (long long)d_state,
+                    SSM_MAX_D_STATE);
+    if (2 * n_angles > d_state)
+        return fail(SSM_ERR_INVALID_ARG, "%s: 2 * n_angles (%lld) exceeds d_state (%lld)", E,
+                    (long long)(2 * n_angles), (long long)d_state);
+    if (too_big(batch, L, nheads, d_state)) return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    REQUIRE_ALIGN(E, k_raw); REQUIRE_ALIGN(E, q_raw); REQUIRE_ALIGN(E, angles); REQUIRE_ALIGN(E, dt);
+    REQUIRE_ALIGN(E, angle_state); REQUIRE_ALIGN(E, k); REQUIRE_ALIGN(E, q); REQUIRE_ALIGN(E, angle_state_out);
+    REQUIRE_ALIGN(E, workspace);
+    // k may be k_raw and q may be q_raw (rotated in place), and angle_state_out may
+    // be angle_state; no other output may share memory with an input or output.
+    {
+        const void *so = angle_state_out;
+        const void *others_k[] = {q, q_raw, angles, dt, angle_state, so};
+        const void *others_q[] = {k, k_raw, angles, dt, angle_state, so};
+        const void *others_s[] = {k_raw, q_raw, angles, dt, k, q};
+        for (const void *o : others_k)
+            if (o && o == k) return fail(SSM_ERR_INVALID_ARG, "%s: k aliases another argument", E);
+        for (const void *o : others_q)
+            if (o && o == q) return fail(SSM_ERR_INVALID_ARG, "%s: q aliases another argument", E);
+        for (const void *o : others_s)
+            if (so && o == so) return fail(SSM_ERR_INVALID_ARG, "%s: angle_state_out aliases another argument", E);
+    }
+    const size_t need = ssm::trap_rotate_workspace_bytes(batch, L, nheads, d_state, n_angles);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    ssm::TrapRotArgs args{k_raw, q_raw, angles, dt, angle_state, k, q, angle_state_out,
+                          batch, L, nheads, d_state, n_angles, workspace};
+    const char *kn = "trap_rotate";
+    return launched(E, ssm::launch_trap_rotate(args, stream, &kn), kn);
+}
+
 size_t ssd_chunk_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                                          int64_t d_state, int64_t ngroups, int64_t chunk_len) {
     (void)ngroups; (void)chunk_len;

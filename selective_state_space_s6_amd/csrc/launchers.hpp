@@ -35,6 +35,16 @@ struct SsdArgs {
     bool bf16; uint32_t flags;
     void *workspace;
 };
+struct TrapRotArgs {
+    const void *k_raw; const void *q_raw; const float *angles; const float *dt;
+    const float *angle_state; void *k; void *q; float *angle_state_out;
+    int64_t batch, L, nheads, d_state, n_angles;
+    void *workspace;
+};
+size_t trap_rotate_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t d_state,
+                                   int64_t n_angles);
+hipError_t launch_trap_rotate(const TrapRotArgs &a, hipStream_t stream, const char **kernel_name);
+
 struct SsdTrapArgs {
     const void *x; const void *k; const void *q;
     const float *dt; const float *a; const float *trap; const float *D; float *y;

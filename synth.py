@@ -32,6 +32,9 @@ WORKLOADS = {
     # Mamba-3 trapezoidal SSD: 4 x 8192, 32 heads x 64, N=128, per-head k/q, Q=64, bf16
     "trap_mamba3": dict(kind="trap", batch=4, L=8192, nheads=32, headdim=64, d_state=128,
                         chunk_len=64, dtype="bf16"),
+    # Mamba-3 rotation of k and q ahead of that scan: 64 angles (every pair of N=128 turns)
+    "trap_rot_mamba3": dict(kind="trap_rot", batch=4, L=8192, nheads=32, headdim=64, d_state=128,
+                            n_angles=64, chunk_len=64, dtype="bf16"),
     # complex-state SSD: 4 x 8192, 32 heads x 64, 32 complex states, Q=64, fp32
     "cssd_mamba3": dict(kind="cssd", batch=4, L=8192, nheads=32, headdim=64, n_complex=32,
                         ngroups=1, chunk_len=64, dtype="f32"),
@@ -183,7 +186,8 @@ def trap_inputs(batch, L, nheads, headdim, d_state, *, seed=(0,), h0=False, prev
                 D="normal", trap="uniform") -> Inputs:
     """Mamba-3 trapezoidal inputs: dt log-uniform on [1e-3, 1e-1] (a positive step, as
     after softplus), a = -exp(U(0, log 16)) per step, trap U(0, 1) (as after a sigmoid)
-    or the constant 0 / 1; x, k, q, x_prev, k_prev N(0, 1) rounded to bf16."""
+    or the constant 0 / 1; x, k, q, x_prev, k_prev N(0, 1) rounded to bf16.  k and q are
+    the scan's inputs (already rotated); rotation_inputs draws the angles for them."""
     key = (5, *seed)
     x = round_bf16(_normal(_rng(key, 0), (batch, L, nheads, headdim)))
     k = round_bf16(_normal(_rng(key, 1), (batch, L, nheads, d_state)))
@@ -204,6 +208,15 @@ def trap_inputs(batch, L, nheads, headdim, d_state, *, seed=(0,), h0=False, prev
                   ("x", "k", "q", "k_prev", "x_prev"))
 
 
+def rotation_inputs(batch, L, nheads, n_angles, *, seed=(0,), angle_state=True):
+    """Angles for the Mamba-3 rotation of k and q: per-step angles U(-pi, pi) shared by the
+    heads (batch, L, n_angles) and an entering angle state U(-pi, pi) (batch, nheads, n_angles)."""
+    key = (6, *seed)
+    ang = _uniform(_rng(key, 0), (batch, L, n_angles), -math.pi, math.pi)
+    st = _uniform(_rng(key, 1), (batch, nheads, n_angles), -math.pi, math.pi) if angle_state else None
+    return ang, st
+
+
 def workload_inputs(name: str, seed=(0,)) -> Inputs:
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")
@@ -213,7 +226,7 @@ def workload_inputs(name: str, seed=(0,)) -> Inputs:
     if kind == "ssd":
         return ssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"],
                           w["ngroups"], seed=seed, dtype=w["dtype"])
-    if kind == "trap":
+    if kind in ("trap", "trap_rot"):
         return trap_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"], seed=seed)
     return cssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["n_complex"],
                        w["ngroups"], seed=seed)

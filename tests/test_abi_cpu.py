@@ -33,6 +33,9 @@ def lib():
     L.ssd_trap_chunk_scan_fwd.argtypes = [P] * 12 + [I] * 6 + [ctypes.c_int, P, Z, P]
     L.ssd_trap_chunk_scan_fwd_workspace_size.argtypes = [I] * 6
     L.ssd_trap_chunk_scan_fwd_workspace_size.restype = Z
+    L.ssd_trap_rotate_qk.argtypes = [P] * 8 + [I] * 5 + [ctypes.c_int, P, Z, P]
+    L.ssd_trap_rotate_qk_workspace_size.argtypes = [I] * 5
+    L.ssd_trap_rotate_qk_workspace_size.restype = Z
     for f in ("ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size"):
         getattr(L, f).argtypes = [I] * 4
         getattr(L, f).restype = Z
@@ -52,6 +55,7 @@ def test_every_declared_symbol_is_exported(lib):
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
                      "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
                      "ssd_trap_chunk_scan_fwd_workspace_size", "ssd_trap_chunk_scan_fwd",
+                     "ssd_trap_rotate_qk_workspace_size", "ssd_trap_rotate_qk",
                      "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd"}
     for n in names:
         assert hasattr(lib, n), n
@@ -217,3 +221,31 @@ def test_trap_argument_checks(lib):
     assert _trap(lib, ws=None) == WORKSPACE and "workspace" in _err(lib)
     assert _trap(lib, wsb=need - 1) == WORKSPACE
     assert lib.ssd_trap_chunk_scan_fwd_workspace_size(2, 0, 4, 64, 128, 64) == 0
+
+
+def _rot(lib, dims=(2, 300, 4, 128, 64), dtype=1, ws=ctypes.c_void_p(0x9000000), wsb=1 << 40, **kw):
+    names = ["k_raw", "q_raw", "angles", "dt", "angle_state", "k", "q", "angle_state_out"]
+    required = {"k_raw", "q_raw", "angles", "dt", "k", "q"}
+    ptrs = {n: (ctypes.c_void_p(0x100000 * (i + 1)) if n in required else None)
+            for i, n in enumerate(names)}
+    ptrs.update(kw)
+    return lib.ssd_trap_rotate_qk(*(ptrs[n] for n in names), *dims, dtype, ws, wsb, None)
+
+
+def test_rotate_argument_checks(lib):
+    assert _rot(lib, dt=None) == INVALID and "dt is NULL" in _err(lib)
+    assert _rot(lib, angles=None) == INVALID and "angles is NULL" in _err(lib)
+    assert _rot(lib, dims=(2, 300, 4, 127, 60)) == UNSUPPORTED and "even" in _err(lib)
+    assert _rot(lib, dims=(2, 300, 4, 128, 65)) == INVALID and "n_angles" in _err(lib)
+    assert _rot(lib, dims=(2, 300, 4, 128, -1)) == INVALID and "n_angles" in _err(lib)
+    assert _rot(lib, dims=(2, 0, 4, 128, 64)) == INVALID
+    assert _rot(lib, dtype=0) == UNSUPPORTED and "bf16" in _err(lib)
+    assert _rot(lib, k=ctypes.c_void_p(0x700000)) == INVALID and "k aliases" in _err(lib)      # k == q
+    assert _rot(lib, q=ctypes.c_void_p(0x100000)) == INVALID and "q aliases" in _err(lib)      # q == k_raw
+    assert _rot(lib, angle_state_out=ctypes.c_void_p(0x400000)) == INVALID                      # == dt
+    assert _rot(lib, angles=MIS) == UNSUPPORTED and "aligned" in _err(lib)
+    need = lib.ssd_trap_rotate_qk_workspace_size(2, 300, 4, 128, 64)
+    assert need >= 2 * 4 * 64 * 4
+    assert _rot(lib, ws=None) == WORKSPACE and "workspace" in _err(lib)
+    assert _rot(lib, wsb=need - 1) == WORKSPACE
+    assert lib.ssd_trap_rotate_qk_workspace_size(2, 300, 4, 128, -1) == 0
