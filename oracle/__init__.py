@@ -71,6 +71,7 @@ def _load():
     lib.oracle_ssd_bwd.argtypes = [P] * 10 + [I] * 6 + [ctypes.c_uint32, P, I] + [P] * 8 + [ctypes.c_int]
     lib.oracle_trap_fwd.argtypes = [P] * 10 + [I] * 5 + [P, I, P, P, ctypes.c_int]
     lib.oracle_trap_rotate.argtypes = [P] * 5 + [I] * 5 + [P] * 3
+    lib.oracle_s6_layer_fwd.argtypes = [P] * 12 + [I] * 5 + [ctypes.c_uint32, P, I] + [P] * 4 + [ctypes.c_int]
     for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd, lib.oracle_s6_bwd,
               lib.oracle_ssd_bwd, lib.oracle_trap_fwd):
         f.restype = None
@@ -145,6 +146,37 @@ def s6_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, flags=BBAR_ZOH, units=None, 
     if full:
         return (y.reshape(batch, Dm, L).transpose(0, 2, 1).copy(), hf.reshape(batch, Dm, N))
     return y, hf
+
+
+def s6_layer_fwd(x, conv_w, conv_b, dt, dt_bias, A_log, B, C, D, h0=None, conv_state=None, z=None,
+                 flags=BBAR_ZOH, units=None, nthreads=None):
+    """Causal depthwise conv1d + SiLU, the S6 scan, and SiLU(z) gating, in fp64.
+
+    x, dt, z: (batch, L, d_inner); conv_w (d_inner, K); conv_b (d_inner,) or None;
+    conv_state (batch, d_inner, K-1) or None (zeros); other inputs as s6_fwd.
+    Returns y, h_final, u (the scan's input), conv_state_out: full arrays
+    (batch, L, d_inner), (batch, d_inner, N), (batch, L, d_inner), (batch, d_inner, K-1),
+    or per-unit arrays (n, L), (n, N), (n, L), (n, K-1) with (b, d) units."""
+    x, conv_w, conv_b, conv_state, z, dt, dt_bias, A_log, B, C, D, h0 = map(
+        _f32, (x, conv_w, conv_b, conv_state, z, dt, dt_bias, A_log, B, C, D, h0))
+    batch, L, Dm = x.shape
+    N, K = A_log.shape[1], conv_w.shape[1]
+    assert conv_w.shape == (Dm, K) and K >= 1
+    uu, full = _units(units, batch, Dm)
+    nu = uu.shape[0]
+    y = np.empty((nu, L), np.float64)
+    hf = np.empty((nu, N), np.float64)
+    u = np.empty((nu, L), np.float64)
+    cs = np.empty((nu, max(K - 1, 1)), np.float64)
+    _load().oracle_s6_layer_fwd(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(z),
+                                _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(h0), batch, L, Dm, N, K, flags, _ptr(uu), nu, _ptr(y), _ptr(hf),
+                                _ptr(u), _ptr(cs) if K > 1 else None, nthreads or default_threads())
+    cs = cs[:, :K - 1]
+    if full:
+        return (y.reshape(batch, Dm, L).transpose(0, 2, 1).copy(), hf.reshape(batch, Dm, N),
+                u.reshape(batch, Dm, L).transpose(0, 2, 1).copy(), cs.reshape(batch, Dm, K - 1))
+    return y, hf, u, cs
 
 
 def ssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_DT, units=None,

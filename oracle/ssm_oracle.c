@@ -76,7 +76,23 @@ typedef struct {
     int64_t n_units;
     double *y_out;          /* [n_units][L] */
     double *hf_out;         /* [n_units][N] or NULL */
+    /* layer form (oracle_s6_layer_fwd): u from a causal conv of x, gated output */
+    const float *conv_w, *conv_b, *conv_state, *z;   /* conv_w NULL: plain scan of u */
+    int64_t K;
+    double *u_out;          /* [n_units][L] or NULL */
+    double *cs_out;         /* [n_units][K-1] or NULL */
 } s6_job;
+
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* x of unit (b, d) at time t, extended to t < 0 by the carried conv state
+ * (conv_state[b, d, K-1+t], oldest first) or zeros */
+static double conv_x(const s6_job *j, int64_t b, int64_t d, int64_t t)
+{
+    if (t >= 0) return (double)j->u[(b * j->L + t) * j->Dm + d];
+    if (!j->conv_state) return 0.0;
+    return (double)j->conv_state[(b * j->Dm + d) * (j->K - 1) + (j->K - 1) + t];
+}
 
 static void s6_unit(const s6_job *j, int64_t k)
 {
@@ -94,7 +110,15 @@ static void s6_unit(const s6_job *j, int64_t k)
     for (int64_t t = 0; t < L; ++t) {
         const int64_t e = (b * L + t) * Dm + d;
         const double delta = sp((double)j->dt[e] + bias);
-        const double uu = (double)j->u[e];
+        double uu;
+        if (j->conv_w) {      /* u_t = SiLU(sum_k w[d,k] x_{t-k} + bias[d]) */
+            double pre = j->conv_b ? (double)j->conv_b[d] : 0.0;
+            for (int64_t q = 0; q < j->K; ++q) pre += (double)j->conv_w[d * j->K + q] * conv_x(j, b, d, t - q);
+            uu = silu(pre);
+            if (j->u_out) j->u_out[k * L + t] = uu;
+        } else {
+            uu = (double)j->u[e];
+        }
         const float *Bt = j->B + (b * L + t) * N;
         const float *Ct = j->C + (b * L + t) * N;
         double yv = 0.0;
@@ -107,10 +131,13 @@ static void s6_unit(const s6_job *j, int64_t k)
             h[n] = exp(z) * h[n] + beta * (double)Bt[n] * uu;
             yv += (double)Ct[n] * h[n];
         }
-        j->y_out[k * L + t] = yv + Dd * uu;
+        const double yt = yv + Dd * uu;
+        j->y_out[k * L + t] = (j->conv_w && j->z) ? yt * silu((double)j->z[e]) : yt;
     }
     if (j->hf_out)
         for (int64_t n = 0; n < N; ++n) j->hf_out[k * N + n] = h[n];
+    if (j->conv_w && j->cs_out)
+        for (int64_t q = 0; q < j->K - 1; ++q) j->cs_out[k * (j->K - 1) + q] = conv_x(j, b, d, L - (j->K - 1) + q);
     free(A);
     free(h);
 }
@@ -511,6 +538,29 @@ void oracle_s6_fwd(const float *u, const float *dt, const float *dt_bias, const 
 {
     s6_job j = {u, dt, dt_bias, A_log, B, C, D, h0, batch, L, d_inner, d_state, flags,
                 units, n_units, y_out, hf_out};
+    run_units(0, &j, n_units, nthreads);
+}
+
+/*
+ * Mamba-1 layer around the scan (builderforce-memory-engine conv1d.ts header
+ * and conv1d_forward; mamba-rs 0.4.0 forward.rs F4a conv1d burn-in with fused
+ * SiLU and carried conv state, F4d scan, F4e gating):
+ *   u[b,t,d] = SiLU(sum_{k<K} conv_w[d,k] x[b,t-k,d] + conv_b[d]),
+ *              x[b,t',d] for t' < 0 from conv_state[b,d,K-1+t'] (oldest first) or 0
+ *   y        = the S6 scan of u (D u included), times SiLU(z[b,t,d]) when z is given
+ * u_out [n_units][L], cs_out [n_units][K-1] (x of the last K-1 steps, the state
+ * a next call carries) may be NULL.
+ */
+void oracle_s6_layer_fwd(const float *x, const float *conv_w, const float *conv_b,
+                         const float *conv_state, const float *z, const float *dt,
+                         const float *dt_bias, const float *A_log, const float *B, const float *C,
+                         const float *D, const float *h0, int64_t batch, int64_t L, int64_t d_inner,
+                         int64_t d_state, int64_t d_conv, uint32_t flags, const int64_t *units,
+                         int64_t n_units, double *y_out, double *hf_out, double *u_out, double *cs_out,
+                         int nthreads)
+{
+    s6_job j = {x, dt, dt_bias, A_log, B, C, D, h0, batch, L, d_inner, d_state, flags,
+                units, n_units, y_out, hf_out, conv_w, conv_b, conv_state, z, d_conv, u_out, cs_out};
     run_units(0, &j, n_units, nthreads);
 }
 
