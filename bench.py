@@ -56,6 +56,16 @@ def s6_model(d):
     return elems, bytes_, ops
 
 
+def s6_layer_model(d):
+    """The fused layer: read x, z, dt (fp32), B, C, the conv state and h0; write y, h_final
+    and the conv state.  Operations: the scan's state updates (the conv, SiLU and gate
+    are ~0.1 % of them at N = 16, not counted)."""
+    B, L, D, N, K = d["batch"], d["L"], d["d_inner"], d["d_state"], d["d_conv"]
+    elems = B * L * D
+    bytes_ = elems * 4 * 4 + 2 * B * L * N * 4 + 2 * B * D * (K - 1) * 4 + 2 * B * D * N * 4 + D * N * 4
+    return elems, bytes_, elems * N * S6_FLOPS_PER_UPDATE
+
+
 def s6_bwd_model(d):
     """Algorithmic bytes of one S6 backward call: read u, dt, dy, B, C, write du, ddt,
     dB, dC, dA_log, dD, ddt_bias, dh0 (and read dh_final); ops: one forward state
@@ -160,6 +170,17 @@ def make_runner(name, dev):
                                 None, t["dy"], t["dhf"], out=out, workspace=ws)
         w["kind"] = "s6_bwd"
         return step, dims, w, ["s6_bwd_kernel", "s6_bwd_reduce_kernel"]
+    if kind == "s6_layer":
+        t0 = copies[0]
+        y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
+        states = [(t["h0"].clone(), t["conv_state"].clone()) for t in copies]
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            h, cs = states[i % N_ROTATE]     # carried in place, as a decode loop does
+            lib.ssm_s6_fused_fwd(t["x"], t["conv_w"], t["conv_b"], t["dt"], t["dt_bias"], t["A_log"], t["B"],
+                                 t["C"], t["D"], h, cs, t["z"], y=y, h_final=h, conv_state_out=cs)
+        return step, dims, w, ["s6_scan_kernel", "s6_conv_state_kernel"]
     if kind == "s6":
         t0 = copies[0]
         y = torch.empty_like(t0["u"], dtype=torch.float32)
@@ -293,6 +314,22 @@ def cpu_baseline_s6(name):
             "sample": f"whole {name} workload ({elems} elements, fp64, {sec:.2f} s wall on {nthr} threads)"}
 
 
+def cpu_baseline_s6_layer(name):
+    """The fp64 layer oracle (conv + SiLU, scan, gate), untuned, on the whole workload."""
+    import oracle
+    import synth
+    inp = synth.workload_inputs(name, seed=(0,))
+    a, d = inp.arrays, inp.dims
+    nthr = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.s6_layer_fwd(a["x"], a["conv_w"], a["conv_b"], a["dt"], a["dt_bias"], a["A_log"], a["B"], a["C"],
+                        a["D"], a["h0"], a["conv_state"], a["z"], nthreads=nthr)
+    sec = time.perf_counter() - t0
+    elems = d["batch"] * d["L"] * d["d_inner"]
+    return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
+            "sample": f"whole {name} workload ({elems} elements, fp64, {sec:.2f} s wall on {nthr} threads)"}
+
+
 def cpu_baseline_s6_bwd(name, n_rows=2):
     """The fp64 backward oracle on the first n_rows batch rows of the workload."""
     import oracle
@@ -353,11 +390,18 @@ def cpu_baseline_units(name, n_units):
                       f"({elems} elements, {sec:.2f} s wall)"}
 
 
+def s6_kernel_sha1():
+    """sha1 of the S6 forward kernel's sources (the kernel template and its instantiation)."""
+    import hashlib
+    h = hashlib.sha1()
+    for f in ("s6_kernel.hpp", "s6_scan.hip"):
+        h.update(open(os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def s6_traffic(name):
     """Counter-measured HBM bytes per launch, or None if the kernel changed since."""
-    import hashlib
-    src = os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", "s6_scan.hip")
-    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
+    sha = s6_kernel_sha1()
     if name != "s6_mamba1" or sha != S6_TRAFFIC["src_sha1"]:
         return None
     return round(S6_TRAFFIC["bytes"])
@@ -371,6 +415,8 @@ def measure(name, dev, steps, warmup):
     dims = dict(dims, chunk_len=w.get("chunk_len"))
     if kind == "s6":
         elems, bytes_, ops = s6_model(dims)
+    elif kind == "s6_layer":
+        elems, bytes_, ops = s6_layer_model(dims)
     elif kind == "s6_bwd":
         elems, bytes_, ops = s6_bwd_model(dims)
     elif kind == "ssd_bwd":
@@ -445,8 +491,8 @@ def main():
     if not args.no_secondary and args.workload == "s6_mamba1":
         sec = []
         for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
-                            ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("s6_mamba1_bwd", 10),
-                            ("ssd_mamba2_bwd", 5)):
+                            ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("s6_layer_mamba1", 10),
+                            ("s6_decode_mamba1", 50), ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
             es = s["event_ms_median"] * 1e-3
@@ -457,6 +503,11 @@ def main():
             if s["kind"] == "s6_bwd":
                 ent["fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
                 ent["kernel_ms"] = round(s["event_ms_median"], 4)
+            elif s["kind"] == "s6_layer":
+                ent["kernel_ms"] = round(s["event_ms_median"], 4)
+                ent["alu_frac"] = round(s["ops"] / es / 1e12 / S6_ALU_PEAK_TFLOPS, 4)
+                if s["dims"]["L"] == 1:
+                    ent["us_per_token_step"] = round(s["event_ms_median"] * 1e3, 2)
             elif s["kind"] == "ssd_bwd":
                 ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
                 ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
@@ -476,6 +527,8 @@ def main():
             out["cpu_baseline"] = cpu_baseline_s6(args.workload)
         elif kind == "s6_bwd":
             out["cpu_baseline"] = cpu_baseline_s6_bwd(args.workload[: -len("_bwd")])
+        elif kind == "s6_layer":
+            out["cpu_baseline"] = cpu_baseline_s6_layer(args.workload)
         else:
             out["cpu_baseline"] = cpu_baseline_units(args.workload, 16)
     print(json.dumps(out), flush=True)

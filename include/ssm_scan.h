@@ -27,10 +27,12 @@
  *             forward_reduce)
  *   [BF-SSD]  same package, package/dist/kernels/ssd.js and ssd.d.ts
  *             (header comment, ssd_chunk_forward)
+ *   [BF-CONV] same package, package/src/kernels/conv1d.ts (header comment,
+ *             conv1d_forward)
  *   [BF-CSSD] same package, package/src/kernels/complex_ssd.ts (header
  *             comment, et_bbar_re/et_bbar_im, complex_ssd_forward)
  *   [RS-M1]   mamba-rs 0.4.0, src/mamba_ssm/gpu/forward.rs
- *             (gpu_forward_mamba_layer, step F4d, and GpuMambaDims)
+ *             (gpu_forward_mamba_layer, steps F4a, F4d and F4e, and GpuMambaDims)
  *   [RS-M3]   mamba-rs 0.2.1, src/mamba3_siso/gpu/mamba3_gpu.rs
  *             (module header; gpu_forward_mamba3_layer, steps F4e+f, F5,
  *             F5b and F6, kernels K2-K5 and the final-state writeback)
@@ -108,6 +110,35 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
                     int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
                     ssm_dtype_t in_dtype, uint32_t flags,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------ S6 with its layer ----
+ * The Mamba-1 layer's steps on either side of the scan, fused into it
+ * [BF-CONV header and conv1d_forward; RS-M1 F4a (conv1d burn-in with fused
+ * SiLU and a carried conv state), F4d, F4e (gating)]:
+ *   u[b,t,d] = SiLU(conv_b[d] + sum_{k<d_conv} conv_w[d,k] * x[b,t-k,d]),
+ *              x[b,t',d] for t' < 0 taken from conv_state[b,d,d_conv-1+t'] (or 0)
+ *   y[b,t,d] = (S6 scan of u as in ssm_s6_scan_fwd, D u included) * SiLU(z[b,t,d])
+ * with SiLU(v) = v / (1 + exp(-v)); without z the output is not gated.
+ * conv_state_out[b,d,j] = x at time L-(d_conv-1)+j (the old state's tail when
+ * L < d_conv-1): what the next call carries.  One call with L = 1, with
+ * h_final == h0 and conv_state_out == conv_state, is one decode step.
+ *
+ * Layouts: x, z (batch, L, d_inner) [in_dtype]; conv_w (d_inner, d_conv) fp32
+ * (tap k multiplies x[t-k]); conv_b (d_inner) fp32 or NULL; conv_state,
+ * conv_state_out (batch, d_inner, d_conv-1) fp32, oldest step first, or NULL;
+ * u_out (batch, L, d_inner) fp32 or NULL (the scan's input, for a backward);
+ * the rest as ssm_s6_scan_fwd.  h_final may be h0 and conv_state_out may be
+ * conv_state; no other output may alias an input or another output.
+ * Limits: 1 <= d_conv <= SSM_MAX_D_CONV; the rest as ssm_s6_scan_fwd.  No
+ * workspace.  Arithmetic: fp32 (conv, SiLU and gate in the scan kernel). */
+#define SSM_MAX_D_CONV 4
+
+int ssm_s6_fused_fwd(const void *x, const float *conv_w, const float *conv_b, const float *conv_state,
+                     const void *z, const float *dt, const float *dt_bias, const float *A_log,
+                     const void *B, const void *C, const float *D, float *y,
+                     const float *h0, float *h_final, float *u_out, float *conv_state_out,
+                     int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t d_conv,
+                     ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream);
 
 /* --------------------------------------------------------- S6 backward ----
  * Gradients of a scalar loss through the S6 scan above, given dy = dL/dy and

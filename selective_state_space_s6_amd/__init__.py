@@ -16,7 +16,8 @@ import os
 import torch
 
 __all__ = [
-    "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssd_chunk_scan_fwd", "ssd_chunk_scan_bwd",
+    "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssm_s6_fused_fwd", "ssd_chunk_scan_fwd",
+    "ssd_chunk_scan_bwd",
     "ssd_cplx_chunk_scan_fwd", "ssd_trap_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size",
     "ssm_s6_scan_bwd_workspace_size", "ssd_trap_chunk_scan_fwd_workspace_size",
     "ssd_trap_rotate_qk", "ssd_trap_rotate_qk_workspace_size",
@@ -43,6 +44,8 @@ _lib.ssm_s6_scan_fwd_workspace_size.argtypes = [_I] * 4
 _lib.ssm_s6_scan_fwd_workspace_size.restype = _Z
 _lib.ssm_s6_scan_fwd.argtypes = [_P] * 10 + [_I] * 4 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
 _lib.ssm_s6_scan_fwd.restype = ctypes.c_int
+_lib.ssm_s6_fused_fwd.argtypes = [_P] * 16 + [_I] * 5 + [ctypes.c_int, ctypes.c_uint32, _P]
+_lib.ssm_s6_fused_fwd.restype = ctypes.c_int
 _lib.ssm_s6_scan_bwd_workspace_size.argtypes = [_I] * 4
 _lib.ssm_s6_scan_bwd_workspace_size.restype = _Z
 _lib.ssm_s6_scan_bwd.argtypes = [_P] * 18 + [_I] * 4 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
@@ -178,6 +181,50 @@ def ssm_s6_scan_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, *, flags=SSM_BBAR_Z
                               _in_dtype(u), flags, None, 0, _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ssm_s6_fused_fwd(x, conv_w, conv_b, dt, dt_bias, A_log, B, C, D, h0=None, conv_state=None, z=None,
+                     *, flags=SSM_BBAR_ZOH, return_final=False, y=None, h_final=None, u_out=None,
+                     conv_state_out=None):
+    """Causal conv1d + SiLU, the S6 scan and SiLU(z) gating in one pass.
+    x, z (batch, L, d_inner) fp32|bf16 (z may be None); conv_w (d_inner, d_conv) fp32;
+    conv_b (d_inner,) fp32 or None; conv_state (batch, d_inner, d_conv-1) fp32 or None;
+    the rest as ssm_s6_scan_fwd.  Returns y, or (y, h_final, conv_state_out) when
+    return_final (h_final=h0 and conv_state_out=conv_state carry in place).
+    u_out (batch, L, d_inner) fp32 receives the scan's input when given."""
+    dev = x.device
+    batch, L, Dm = x.shape
+    N, K = A_log.shape[1], conv_w.shape[1]
+    dty = x.dtype
+    _req(x, "x", dty, (batch, L, Dm), dev)
+    _req(conv_w, "conv_w", torch.float32, (Dm, K), dev)
+    _opt(conv_b, "conv_b", torch.float32, (Dm,), dev)
+    _opt(conv_state, "conv_state", torch.float32, (batch, Dm, K - 1), dev)
+    _opt(z, "z", dty, (batch, L, Dm), dev)
+    _req(dt, "dt", torch.float32, (batch, L, Dm), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (Dm,), dev)
+    _req(A_log, "A_log", torch.float32, (Dm, N), dev)
+    _req(B, "B", dty, (batch, L, N), dev)
+    _req(C, "C", dty, (batch, L, N), dev)
+    _opt(D, "D", torch.float32, (Dm,), dev)
+    _opt(h0, "h0", torch.float32, (batch, Dm, N), dev)
+    if y is None:
+        y = torch.empty((batch, L, Dm), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, (batch, L, Dm), dev)
+    if return_final:
+        if h_final is None:
+            h_final = torch.empty((batch, Dm, N), dtype=torch.float32, device=dev)
+        if conv_state_out is None and K > 1:
+            conv_state_out = torch.empty((batch, Dm, K - 1), dtype=torch.float32, device=dev)
+    _opt(h_final, "h_final", torch.float32, (batch, Dm, N), dev)
+    _opt(u_out, "u_out", torch.float32, (batch, L, Dm), dev)
+    _opt(conv_state_out, "conv_state_out", torch.float32, (batch, Dm, K - 1), dev)
+    rc = _lib.ssm_s6_fused_fwd(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(z), _ptr(dt),
+                               _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(y), _ptr(h0),
+                               _ptr(h_final), _ptr(u_out), _ptr(conv_state_out), batch, L, Dm, N, K,
+                               _in_dtype(x), flags, _stream(dev))
+    _check(rc)
+    return (y, h_final, conv_state_out) if return_final else y
 
 
 _S6_GRADS = ("du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")

@@ -92,6 +92,51 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
     return launched(E, ssm::launch_s6(a, stream, &kn), kn);
 }
 
+int ssm_s6_fused_fwd(const void *x, const float *conv_w, const float *conv_b, const float *conv_state,
+                     const void *z, const float *dt, const float *dt_bias, const float *A_log,
+                     const void *B, const void *C, const float *D, float *y,
+                     const float *h0, float *h_final, float *u_out, float *conv_state_out,
+                     int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t d_conv,
+                     ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream) {
+    const char *E = "ssm_s6_fused_fwd";
+    REQUIRE_PTR(E, x); REQUIRE_PTR(E, conv_w); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
+    REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
+    REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, d_inner); REQUIRE_POS(E, d_state);
+    REQUIRE_POS(E, d_conv);
+    if (d_conv > SSM_MAX_D_CONV)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_conv %lld > %d", E, (long long)d_conv, SSM_MAX_D_CONV);
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if ((flags & ~0x3u) != 0 || (flags & 0x3u) == 0x3u)
+        return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x: only SSM_BBAR_ZOH/DT/ONE apply", E, flags);
+    if (d_state > SSM_MAX_D_STATE)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld > %d", E, (long long)d_state, SSM_MAX_D_STATE);
+    if (too_big(batch, L, d_inner, 1) || batch * ((d_inner + 255) / 16) > 0x7fffffffLL)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    REQUIRE_ALIGN(E, x); REQUIRE_ALIGN(E, conv_w); REQUIRE_ALIGN(E, conv_b); REQUIRE_ALIGN(E, conv_state);
+    REQUIRE_ALIGN(E, z); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
+    REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
+    REQUIRE_ALIGN(E, h0); REQUIRE_ALIGN(E, h_final); REQUIRE_ALIGN(E, u_out); REQUIRE_ALIGN(E, conv_state_out);
+    // h_final may be h0 and conv_state_out may be conv_state (carried in place);
+    // no other output may share memory with an input or another output
+    {
+        const void *ins[] = {x, conv_w, conv_b, conv_state, z, dt, dt_bias, A_log, B, C, D, h0};
+        const void *outs[] = {y, h_final, u_out, conv_state_out};
+        for (size_t i = 0; i < 4; ++i) {
+            if (!outs[i]) continue;
+            for (const void *in : ins)
+                if (in == outs[i] && !(i == 1 && in == (const void *)h0) && !(i == 3 && in == (const void *)conv_state))
+                    return fail(SSM_ERR_INVALID_ARG, "%s: an output aliases an input", E);
+            for (size_t j = 0; j < i; ++j)
+                if (outs[j] == outs[i]) return fail(SSM_ERR_INVALID_ARG, "%s: two outputs alias", E);
+        }
+    }
+    ssm::S6FusedArgs a{x, conv_w, conv_b, conv_state, z, dt, dt_bias, A_log, B, C, D, y, h0, h_final, u_out,
+                       conv_state_out, batch, L, d_inner, d_state, d_conv, in_dtype == SSM_BF16, flags};
+    const char *kn = "s6_fused";
+    return launched(E, ssm::launch_s6_fused(a, stream, &kn), kn);
+}
+
 size_t ssm_s6_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state) {
     if (batch <= 0 || L <= 0 || d_inner <= 0 || d_state <= 0) return 0;
     return ssm::s6_bwd_workspace_bytes(batch, L, d_inner, d_state);

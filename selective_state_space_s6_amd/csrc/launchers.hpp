@@ -15,6 +15,17 @@ struct S6Args {
 };
 hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_name);
 
+// Mamba-1 layer around the scan: u = SiLU(causal conv1d(x)), y = scan(u) * SiLU(z)
+struct S6FusedArgs {
+    const void *x; const float *conv_w; const float *conv_b; const float *conv_state; const void *z;
+    const float *dt; const float *dt_bias; const float *A_log;
+    const void *B; const void *C; const float *D; float *y;
+    const float *h0; float *h_final; float *u_out; float *conv_state_out;
+    int64_t batch, L, d_inner, d_state, d_conv;
+    bool bf16; uint32_t flags;
+};
+hipError_t launch_s6_fused(const S6FusedArgs &a, hipStream_t stream, const char **kernel_name);
+
 struct S6BwdArgs {
     const void *u; const float *dt; const float *dt_bias; const float *A_log;
     const void *B; const void *C; const float *D; const float *h0;

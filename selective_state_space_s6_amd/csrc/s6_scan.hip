@@ -1,353 +1,17 @@
-// s6_scan.hip -- fused Mamba-1 (S6) forward selective scan for gfx950.
-//
-// Computes, per batch b and channel d, the diagonal recurrence of
-// builderforce-memory-engine selective_scan.js (header comment, softplus,
-// discretise_A/discretise_B, forward_scan + forward_reduce) and mamba-rs 0.4.0
-// forward.rs step F4d, in ONE kernel: softplus of dt, exact zero-order-hold
-// discretisation, the recurrence over time, the reduction over the state index
-// and the D skip term.  Nothing but y (and h_final) is written to memory.
-//
-// Work decomposition (the path is bound by VALU issue, not by HBM: every
-// (t, d, n) needs one exp and ~6 fp32 operations):
-//  * a 256-thread block owns CW = 256/G channels of one batch row and walks the
-//    whole sequence in tiles of 16 time steps;
-//  * the N states of a channel are spread over G lanes (SPL = N/G states per
-//    lane), so G*CW = 256 lanes each hold a few states in registers;
-//  * a 16-lane DPP row is 16 channels that share one state group; B[t, n] and
-//    C[t, n] of the 16 steps of a tile are held one step per lane and handed
-//    to the whole row with DPP row_newbcast, folded into the multiply;
-//  * delta = softplus(dt + dt_bias) and u are staged once per (t, d) through LDS
-//    (b128 reads), the per-lane partial sums C.h go back through LDS and one
-//    thread per (t, d) adds the G partials, adds D*u and writes y;
-//  * global loads of the tile after next are in flight while a tile is scanned.
-#include "device_common.hpp"
-#include "launchers.hpp"
-#include <type_traits>
-#include <utility>
+// s6_scan.hip -- the Mamba-1 (S6) forward selective scan of ssm_s6_scan_fwd:
+// the plain instantiations of the kernel in s6_kernel.hpp.
+#include "s6_kernel.hpp"
 
 namespace ssm {
-namespace {
-
-constexpr int kThreads = 256;
-constexpr int kT = 16;        // time steps per tile == lanes per DPP row
-constexpr int kTS = kT + 4;   // padded LDS row: conflict-free b128 reads by 16 lanes
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
-struct S6Kp {
-    const void *u; const float *dt; const float *dt_bias; const float *A_log;
-    const void *B; const void *C; const float *D; float *y;
-    const float *h0; float *h_final;
-    int64_t batch, L, Dm, N;
-    int64_t n_cblk;   // channel blocks per batch row
-};
-
-template <typename TIN, int G, int SPL>
-struct Raw {          // one tile of raw inputs held in registers
-    float dt[16 / G];
-    float u[16 / G];
-    float B[SPL];
-    float C[SPL];
-};
-
-// Per-thread base pointers of the tensors this thread loads or stores, at
-// time step 0 of the block's channels; a tile adds a uniform 64-bit offset.
-template <typename TIN, int G, int SPL>
-struct Ptrs {
-    const float *dt[16 / G];
-    const TIN *u[16 / G];
-    float *y[16 / G];
-    const TIN *B;     // row t = k (this lane's step in a tile), column 0
-    const TIN *C;
-    int nidx[SPL];    // this lane's state columns, clamped into [0, N)
-};
-
-// Loads of one tile.  They are unconditional so the compiler can keep them in
-// flight across the scan of the previous tile.  A tile that may cross L
-// (CHECK) clamps its time index into the tensors; values of steps past L,
-// channels past d_inner and states past N are masked where they are consumed
-// (channel and state indices are clamped once, in the base pointers).
-template <bool CHECK, typename TIN, int G, int SPL>
-__device__ __forceinline__ void load_raw(Raw<TIN, G, SPL> &r, const Ptrs<TIN, G, SPL> &q,
-                                         const S6Kp &p, int64_t t0, int tid, int k) {
-    constexpr int CW = kThreads / G;
-    constexpr int EPT = 16 / G;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int tl = (tid + kThreads * i) / CW;
-        int64_t off = t0 * p.Dm;
-        if constexpr (CHECK) off = (min(t0 + tl, p.L - 1) - tl) * p.Dm;
-        r.dt[i] = q.dt[i][off];
-        r.u[i] = In<TIN>::ld(q.u[i], off);
-    }
-    int64_t off = t0 * p.N;
-    if constexpr (CHECK) off = (min(t0 + k, p.L - 1) - k) * p.N;
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        r.B[j] = In<TIN>::ld(q.B, off + q.nidx[j]);
-        r.C[j] = In<TIN>::ld(q.C, off + q.nidx[j]);
-    }
-}
-
-template <typename TIN, int G, int SPL, int MODE>
-__global__ void __launch_bounds__(kThreads)
-s6_scan_kernel(S6Kp p) {
-    constexpr int CW = kThreads / G;     // channels per block
-    constexpr int EPT = 16 / G;          // (t, d) elements per thread per tile
-    __shared__ __attribute__((aligned(16))) float sD[2][CW][kTS];
-    __shared__ __attribute__((aligned(16))) float sU[2][CW][kTS];
-    __shared__ __attribute__((aligned(16))) float sY[2][G][kT][CW];
-
-    const int tid = threadIdx.x;
-    const int row = tid >> 4, k = tid & 15;
-    const int g = row % G;
-    const int cl = (row / G) * 16 + k;                 // this lane's channel in the block
-    const int64_t work = xcd_swizzle(blockIdx.x, gridDim.x);
-    const int64_t b = work / p.n_cblk;
-    const int64_t d0 = (work % p.n_cblk) * CW;
-    const int64_t d = d0 + cl;
-    const bool dok = d < p.Dm;
-
-    // per-lane constants of the states this lane owns
-    float A2[SPL], iA[SPL], h[SPL];
-    bool nval[SPL];
-    bool small = false;
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        const int64_t n = (int64_t)g * SPL + j;
-        nval[j] = n < p.N;
-        const bool ok = dok && n < p.N;
-        const float al = ok ? p.A_log[d * p.N + n] : 0.0f;
-        A2[j] = ok ? -expf(al) * kLog2e : 0.0f;        // A*log2(e), A = -exp(A_log)
-        iA[j] = ok ? -expf(-al) : 0.0f;                // 1/A
-        h[j] = (ok && p.h0) ? p.h0[(b * p.Dm + d) * p.N + n] : 0.0f;
-        small |= ok && (expf(al) < 0.125f);
-    }
-    // per-element constants of the (t, d) elements this thread stages/reduces
-    float biasv[EPT], Dv[EPT];
-    bool cval[EPT];
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int c = (tid + kThreads * i) % CW;
-        const bool ok = d0 + c < p.Dm;
-        cval[i] = ok;
-        biasv[i] = (ok && p.dt_bias) ? p.dt_bias[d0 + c] : 0.0f;
-        Dv[i] = (ok && p.D) ? p.D[d0 + c] : 0.0f;
-    }
-    Ptrs<TIN, G, SPL> q;
-    {
-        const TIN *u = static_cast<const TIN *>(p.u);
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int e = tid + kThreads * i;
-            const int tl = e / CW, c = e % CW;
-            const int64_t dd = min(d0 + c, p.Dm - 1);
-            const int64_t off = (b * p.L + tl) * p.Dm + dd;     // time step tl of tile 0
-            q.dt[i] = p.dt + off;
-            q.u[i] = u + off;
-            q.y[i] = p.y + (b * p.L + tl) * p.Dm + d0 + c;
-        }
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) q.nidx[j] = (int)min((int64_t)g * SPL + j, p.N - 1);
-        const int64_t off = (b * p.L + k) * p.N;
-        q.B = static_cast<const TIN *>(p.B) + off;
-        q.C = static_cast<const TIN *>(p.C) + off;
-    }
-    // ZOH with |A| small: (e^z - 1)/A loses digits as z -> 0; such waves take a
-    // path that switches to a series for phi1 when |z| < 1/16.
-    const bool acc_wave = (MODE == 0) && (__builtin_amdgcn_ballot_w64(small) != 0);
-
-    const int64_t ntiles = (p.L + kT - 1) / kT;
-    // Two register sets alternate between even and odd tiles, so that loads in
-    // flight are never copied (a copy would force a wait on them).  The set of
-    // tile k is loaded while tile k-2 is scanned; its dt/u are staged to LDS
-    // while tile k-1 is scanned and its B/C are used when tile k is scanned.
-    Raw<TIN, G, SPL> RA, RB;
-    float du_prev[EPT], du_cur[EPT];
-
-    auto stage = [&](int buf, int64_t t0, const Raw<TIN, G, SPL> &R, auto chkTag) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int e = tid + kThreads * i;
-            const int tl = e / CW, c = e % CW;
-            bool ok = cval[i];
-            if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < p.L);
-            const float dl = ok ? softplus(R.dt[i] + biasv[i]) : 0.0f;
-            const float uu = ok ? R.u[i] : 0.0f;
-            sD[buf][c][tl] = dl;
-            sU[buf][c][tl] = uu;
-            du_cur[i] = Dv[i] * uu;
-        }
-    };
-
-    auto compute = [&](int buf, const Raw<TIN, G, SPL> &R, auto accTag) __attribute__((always_inline)) {
-        constexpr bool ACC = decltype(accTag)::value;
-        float Bm[SPL], Cm[SPL];          // this tile's B, C (state-padding lanes zeroed)
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-            Bm[j] = nval[j] ? R.B[j] : 0.0f;
-            Cm[j] = nval[j] ? R.C[j] : 0.0f;
-        }
-        float yp[kT];
-        static_for<0, kT / 4>([&](auto qi) __attribute__((always_inline)) {
-            constexpr int q = decltype(qi)::value;
-            const float4 dq = *reinterpret_cast<const float4 *>(&sD[buf][cl][4 * q]);
-            const float4 uq = *reinterpret_cast<const float4 *>(&sU[buf][cl][4 * q]);
-            const float dl4[4] = {dq.x, dq.y, dq.z, dq.w};
-            const float uu4[4] = {uq.x, uq.y, uq.z, uq.w};
-            static_for<0, 4>([&](auto ii) __attribute__((always_inline)) {
-                constexpr int i = decltype(ii)::value;
-                constexpr int t = 4 * q + i;
-                const float dl = dl4[i], uu = uu4[i];
-                float ys = 0.0f;
-#pragma unroll
-                for (int j = 0; j < SPL; ++j) {
-                    const float x = dl * A2[j];                 // delta*A*log2(e)
-                    const float ab = exp2_fast(x);              // Abar = exp(delta*A)
-                    float beta;
-                    if constexpr (MODE == 0) {
-                        beta = fmaf(ab, iA[j], -iA[j]);         // (Abar - 1)/A
-                        if constexpr (ACC) {
-                            const float z = x * kLn2;
-                            if (fabsf(z) < 0.0625f) beta = dl * phi1_small(z);
-                        }
-                    } else if constexpr (MODE == 1) {
-                        beta = dl;
-                    } else {
-                        beta = 1.0f;
-                    }
-                    const float bu = row_bcast<t>(Bm[j]) * uu;   // B[t, n] * u[t, d]
-                    h[j] = fmaf(ab, h[j], beta * bu);
-                    if (j == 0) ys = row_bcast<t>(Cm[j]) * h[j];
-                    else ys = fmaf(row_bcast<t>(Cm[j]), h[j], ys);
-                }
-                yp[t] = ys;
-            });
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sY[buf][g][4 * q + i][cl] = yp[4 * q + i];
-        });
-    };
-
-    auto reduce = [&](int buf, int64_t t0, auto chkTag) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int e = tid + kThreads * i;
-            const int tl = e / CW, c = e % CW;
-            float s = du_prev[i];
-#pragma unroll
-            for (int gg = 0; gg < G; ++gg) s += sY[buf][gg][tl][c];
-            bool ok = cval[i];
-            if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < p.L);
-            if (ok) q.y[i][t0 * p.Dm] = s;
-        }
-    };
-
-    // One tile: scan tile kt (its B/C in Rk), reduce tile kt-1, stage tile kt+1
-    // (its dt/u in Rn), start loading tile kt+2 into Rk.  The steady-state body
-    // is branch-free so that the loads stay in flight across iterations; the
-    // first tile and the last few go through the checked body.
-    auto body_full = [&](int64_t kt, Raw<TIN, G, SPL> &Rk, const Raw<TIN, G, SPL> &Rn, auto accTag)
-        __attribute__((always_inline)) {
-        const int buf = (int)(kt & 1);
-        compute(buf, Rk, accTag);
-        reduce(buf ^ 1, (kt - 1) * kT, std::false_type{});
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) du_prev[i] = du_cur[i];
-        stage(buf ^ 1, (kt + 1) * kT, Rn, std::false_type{});
-        load_raw<false>(Rk, q, p, (kt + 2) * kT, tid, k);
-        __syncthreads();
-    };
-    auto body_checked = [&](int64_t kt, Raw<TIN, G, SPL> &Rk, const Raw<TIN, G, SPL> &Rn, auto accTag)
-        __attribute__((always_inline)) {
-        const int buf = (int)(kt & 1);
-        compute(buf, Rk, accTag);
-        if (kt >= 1) reduce(buf ^ 1, (kt - 1) * kT, std::true_type{});
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) du_prev[i] = du_cur[i];
-        if (kt + 1 < ntiles) stage(buf ^ 1, (kt + 1) * kT, Rn, std::true_type{});
-        if (kt + 2 < ntiles) load_raw<true>(Rk, q, p, (kt + 2) * kT, tid, k);
-        __syncthreads();
-    };
-    // The unchecked body of tile kt loads tile kt+2, so a pair (kt, kt+1) of
-    // unchecked bodies needs tiles up to kt+3 to lie wholly inside the sequence.
-    const int64_t nfull = p.L / kT;
-    auto run = [&](auto accTag) __attribute__((always_inline)) {
-        int64_t kt = 0;
-        if (ntiles >= 4) {
-            body_checked(0, RA, RB, accTag);
-            for (kt = 1; kt + 4 <= nfull; kt += 2) {   // tiles kt (set RB) and kt+1 (set RA)
-                body_full(kt, RB, RA, accTag);
-                body_full(kt + 1, RA, RB, accTag);
-            }
-        }
-        for (; kt < ntiles; ++kt) {
-            if (kt & 1) body_checked(kt, RB, RA, accTag);
-            else body_checked(kt, RA, RB, accTag);
-        }
-    };
-
-    load_raw<true>(RA, q, p, 0, tid, k);
-    if (ntiles > 1) load_raw<true>(RB, q, p, kT, tid, k);
-    stage(0, 0, RA, std::true_type{});
-    __syncthreads();
-    if (acc_wave) run(std::true_type{});
-    else run(std::false_type{});
-    reduce((int)((ntiles - 1) & 1), (ntiles - 1) * kT, std::true_type{});
-
-    if (p.h_final) {
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-            const int64_t n = (int64_t)g * SPL + j;
-            if (dok && n < p.N) p.h_final[(b * p.Dm + d) * p.N + n] = h[j];
-        }
-    }
-}
-
-template <typename TIN, int G, int SPL, int MODE>
-hipError_t launch_t(const S6Kp &kp, hipStream_t s) {
-    constexpr int CW = kThreads / G;
-    S6Kp p = kp;
-    p.n_cblk = (p.Dm + CW - 1) / CW;
-    const int64_t nblk = p.batch * p.n_cblk;
-    hipLaunchKernelGGL((s6_scan_kernel<TIN, G, SPL, MODE>), dim3((unsigned)nblk), dim3(kThreads), 0, s, p);
-    return hipGetLastError();
-}
-
-template <typename TIN, int G, int SPL>
-hipError_t launch_mode(const S6Kp &kp, int mode, hipStream_t s) {
-    if (mode == 0) return launch_t<TIN, G, SPL, 0>(kp, s);
-    if (mode == 1) return launch_t<TIN, G, SPL, 1>(kp, s);
-    return launch_t<TIN, G, SPL, 2>(kp, s);
-}
-
-template <typename TIN>
-hipError_t launch_shape(const S6Kp &kp, int mode, hipStream_t s) {
-    const int64_t N = kp.N;
-    if (N <= 1) return launch_mode<TIN, 1, 1>(kp, mode, s);
-    if (N <= 2) return launch_mode<TIN, 2, 1>(kp, mode, s);
-    if (N <= 4) return launch_mode<TIN, 4, 1>(kp, mode, s);
-    if (N <= 8) return launch_mode<TIN, 8, 1>(kp, mode, s);
-    if (N <= 16) return launch_mode<TIN, 16, 1>(kp, mode, s);
-    if (N <= 32) return launch_mode<TIN, 16, 2>(kp, mode, s);
-    if (N <= 64) return launch_mode<TIN, 16, 4>(kp, mode, s);
-    if (N <= 128) return launch_mode<TIN, 16, 8>(kp, mode, s);
-    return launch_mode<TIN, 16, 16>(kp, mode, s);
-}
-
-}  // namespace
 
 hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_name) {
     *kernel_name = "s6_scan_kernel";
-    S6Kp p{a.u, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.y, a.h0, a.h_final,
-           a.batch, a.L, a.d_inner, a.d_state, 0};
+    S6Kp p{};
+    p.u = a.u; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log; p.B = a.B; p.C = a.C;
+    p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
+    p.batch = a.batch; p.L = a.L; p.Dm = a.d_inner; p.N = a.d_state;
     const int mode = (int)(a.flags & 0x3u);
-    return a.bf16 ? launch_shape<uint16_t>(p, mode, stream) : launch_shape<float>(p, mode, stream);
+    return a.bf16 ? launch_shape<uint16_t, false>(p, mode, stream) : launch_shape<float, false>(p, mode, stream);
 }
 
 }  // namespace ssm

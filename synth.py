@@ -23,6 +23,12 @@ WORKLOADS = {
     # S6 at a Mamba-1 layer shape: 8 x 2048 x 1536, N=16, fp32
     "s6_mamba1": dict(kind="s6", batch=8, L=2048, d_inner=1536, d_state=16, dtype="f32",
                       dt_bias="uniform", D="normal"),
+    # the Mamba-1 layer around that scan: conv1d (K=4) + SiLU before, SiLU(z) gating after
+    "s6_layer_mamba1": dict(kind="s6_layer", batch=8, L=2048, d_inner=1536, d_state=16, d_conv=4,
+                            dtype="f32"),
+    # one decode step of that layer for a serving batch of 64: L = 1, state carried in place
+    "s6_decode_mamba1": dict(kind="s6_layer", batch=64, L=1, d_inner=1536, d_state=16, d_conv=4,
+                             dtype="f32"),
     # SSD at a Mamba-2 layer shape: 8 x 4096, 24 heads x 64, N=128, G=1, Q=256, bf16
     "ssd_mamba2": dict(kind="ssd", batch=8, L=4096, nheads=24, headdim=64, d_state=128, ngroups=1,
                        chunk_len=256, dtype="bf16"),
@@ -129,6 +135,27 @@ def s6_inputs(batch, L, d_inner, d_state, *, seed=(0,), dtype="f32", dt_bias="un
                   dict(u=u, dt=dt, dt_bias=bias, A_log=A_log, B=B, C=C, D=Dv, h0=h0a), bf)
 
 
+def layer_inputs(batch, L, d_inner, d_state, d_conv=4, *, seed=(0,), dtype="f32", conv_state=True,
+                 gate=True, h0=False) -> Inputs:
+    """The Mamba-1 layer around the scan: s6_inputs with u renamed x (the conv's input),
+    plus conv_w, conv_b ~ U(-1/sqrt(K), 1/sqrt(K)) (a depthwise conv's default init),
+    conv_state (batch, d_inner, K-1) ~ N(0, 1) and the gate z ~ N(0, 1)."""
+    inp = s6_inputs(batch, L, d_inner, d_state, seed=seed, dtype=dtype, h0=h0)
+    a = dict(inp.arrays)
+    key = (7, *seed)
+    bound = 1.0 / math.sqrt(d_conv)
+    a["x"] = a.pop("u")
+    a["conv_w"] = _uniform(_rng(key, 0), (d_inner, d_conv), -bound, bound)
+    a["conv_b"] = _uniform(_rng(key, 1), (d_inner,), -bound, bound)
+    a["conv_state"] = _normal(_rng(key, 2), (batch, d_inner, d_conv - 1)) if conv_state and d_conv > 1 else None
+    z = _normal(_rng(key, 3), (batch, L, d_inner)) if gate else None
+    if z is not None and dtype == "bf16":
+        z = round_bf16(z)
+    a["z"] = z
+    bf = tuple("x" if n == "u" else n for n in inp.bf16) + (("z",) if dtype == "bf16" else ())
+    return Inputs("s6_layer", dict(inp.dims, d_conv=d_conv), a, bf)
+
+
 def s6_cotangents(batch, L, d_inner, d_state, *, seed=(0,), dh_final=True):
     """Seeded dL/dy (batch, L, d_inner) and dL/dh_final (batch, d_inner, d_state),
     both N(0, 1) fp32, for the backward pass (dh_final None when not asked)."""
@@ -226,6 +253,9 @@ def workload_inputs(name: str, seed=(0,)) -> Inputs:
     if kind == "ssd":
         return ssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"],
                           w["ngroups"], seed=seed, dtype=w["dtype"])
+    if kind == "s6_layer":
+        return layer_inputs(w["batch"], w["L"], w["d_inner"], w["d_state"], w["d_conv"], seed=seed,
+                            dtype=w["dtype"], h0=True)
     if kind in ("trap", "trap_rot"):
         return trap_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"], seed=seed)
     return cssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["n_complex"],

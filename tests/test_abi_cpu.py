@@ -34,6 +34,7 @@ def lib():
     L.ssd_trap_chunk_scan_fwd_workspace_size.argtypes = [I] * 6
     L.ssd_trap_chunk_scan_fwd_workspace_size.restype = Z
     L.ssd_trap_rotate_qk.argtypes = [P] * 8 + [I] * 5 + [ctypes.c_int, P, Z, P]
+    L.ssm_s6_fused_fwd.argtypes = [P] * 16 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P]
     L.ssd_trap_rotate_qk_workspace_size.argtypes = [I] * 5
     L.ssd_trap_rotate_qk_workspace_size.restype = Z
     for f in ("ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size"):
@@ -51,6 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M))
     names = {n for n in names if n.startswith(("ssm_", "ssd_"))}
     assert names == {"ssm_last_error", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_fwd",
+                     "ssm_s6_fused_fwd",
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
                      "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
@@ -249,3 +251,27 @@ def test_rotate_argument_checks(lib):
     assert _rot(lib, ws=None) == WORKSPACE and "workspace" in _err(lib)
     assert _rot(lib, wsb=need - 1) == WORKSPACE
     assert lib.ssd_trap_rotate_qk_workspace_size(2, 300, 4, 128, -1) == 0
+
+
+def _fused(lib, dims=(2, 40, 20, 16, 4), dtype=0, flags=0, **kw):
+    names = ["x", "conv_w", "conv_b", "conv_state", "z", "dt", "dt_bias", "A_log", "B", "C", "D", "y",
+             "h0", "h_final", "u_out", "conv_state_out"]
+    required = {"x", "conv_w", "dt", "A_log", "B", "C", "y"}
+    ptrs = {n: (ctypes.c_void_p(0x100000 * (i + 1)) if n in required else None)
+            for i, n in enumerate(names)}
+    ptrs.update(kw)
+    return lib.ssm_s6_fused_fwd(*(ptrs[n] for n in names), *dims, dtype, flags, None)
+
+
+def test_fused_argument_checks(lib):
+    assert _fused(lib, conv_w=None) == INVALID and "conv_w is NULL" in _err(lib)
+    assert _fused(lib, x=None) == INVALID and "x is NULL" in _err(lib)
+    assert _fused(lib, dims=(2, 40, 20, 16, 0)) == INVALID and "d_conv" in _err(lib)
+    assert _fused(lib, dims=(2, 40, 20, 16, 5)) == UNSUPPORTED and "d_conv" in _err(lib)
+    assert _fused(lib, dims=(2, 40, 20, 300, 4)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _fused(lib, dtype=4) == INVALID and "in_dtype" in _err(lib)
+    assert _fused(lib, flags=0x3) == INVALID and "flags" in _err(lib)
+    assert _fused(lib, z=MIS) == UNSUPPORTED and "aligned" in _err(lib)
+    assert _fused(lib, y=ctypes.c_void_p(0x100000)) == INVALID and "alias" in _err(lib)            # y == x
+    assert _fused(lib, u_out=ctypes.c_void_p(0xC00000)) == INVALID and "alias" in _err(lib)        # == y
+    assert _fused(lib, conv_state_out=ctypes.c_void_p(0x200000)) == INVALID and "alias" in _err(lib)  # == conv_w
