@@ -34,8 +34,8 @@ S6_FLOPS_PER_UPDATE = 9
 S6_ALU_PEAK_TFLOPS = VALU_SLOTS_PER_S / S6_SLOTS_PER_UPDATE * S6_FLOPS_PER_UPDATE / 1e12
 # HBM bytes per launch of s6_scan_kernel on s6_mamba1, from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch) scaled by a 1 GiB device copy (fetch x 2.0, write x 1.0);
-# valid only for the kernel source with this sha1
-S6_TRAFFIC = {"src_sha1": "20e7683cc01827a37f589679373fbf43546fb491", "bytes": (100207 * 2.0 + 99077.2 * 1.0) * 1024}
+# valid only for the kernel sources (s6_kernel.hpp + s6_scan.hip) with this sha1
+S6_TRAFFIC = {"src_sha1": "7d4f019bc6588fb8de24b09ef77881eaeeb7a0ff", "bytes": (100213.4 * 2.0 + 99079.1 * 1.0) * 1024}
 # adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
 # (products and fmas, 24 flops) plus the recomputed Abar, beta, phi1' (not counted again)
 S6_BWD_FLOPS_PER_UPDATE = 24
@@ -180,7 +180,7 @@ def make_runner(name, dev):
             h, cs = states[i % N_ROTATE]     # carried in place, as a decode loop does
             lib.ssm_s6_fused_fwd(t["x"], t["conv_w"], t["conv_b"], t["dt"], t["dt_bias"], t["A_log"], t["B"],
                                  t["C"], t["D"], h, cs, t["z"], y=y, h_final=h, conv_state_out=cs)
-        return step, dims, w, ["s6_scan_kernel", "s6_conv_state_kernel"]
+        return step, dims, w, (["s6_step4_kernel"] if dims["L"] == 1 else ["s6_scan_kernel", "s6_conv_state_kernel"])
     if kind == "s6":
         t0 = copies[0]
         y = torch.empty_like(t0["u"], dtype=torch.float32)

@@ -35,6 +35,9 @@ __device__ __forceinline__ float phi1_small(float z) {
     return fmaf(z, p, 1.0f);
 }
 
+// SiLU(v) = v / (1 + e^-v); for very negative v, e^-v overflows and the result is -0
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+
 // bf16 <-> fp32 (bf16 is the high half of an fp32 word)
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
     return __uint_as_float(((uint32_t)v) << 16);

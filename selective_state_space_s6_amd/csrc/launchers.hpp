@@ -25,6 +25,8 @@ struct S6FusedArgs {
     bool bf16; uint32_t flags;
 };
 hipError_t launch_s6_fused(const S6FusedArgs &a, hipStream_t stream, const char **kernel_name);
+// one step (L = 1) of either entry point; fused picks the conv + gate form
+hipError_t launch_s6_step(const S6FusedArgs &a, bool fused, hipStream_t stream, const char **kernel_name);
 
 struct S6BwdArgs {
     const void *u; const float *dt; const float *dt_bias; const float *A_log;

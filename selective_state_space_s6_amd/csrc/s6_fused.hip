@@ -48,6 +48,7 @@ hipError_t launch_s6_fused(const S6FusedArgs &a, hipStream_t stream, const char 
     p.batch = a.batch; p.L = a.L; p.Dm = a.d_inner; p.N = a.d_state;
     p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.conv_state = a.conv_state; p.z = a.z;
     p.u_out = a.u_out; p.K = (int)a.d_conv;
+    if (a.L == 1) return launch_s6_step(a, true, stream, kernel_name);   // a decode step
     const int mode = (int)(a.flags & 0x3u);
     hipError_t e = a.bf16 ? launch_shape<uint16_t, true>(p, mode, stream)
                           : launch_shape<float, true>(p, mode, stream);

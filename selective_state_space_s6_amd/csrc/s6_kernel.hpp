@@ -35,9 +35,6 @@
 namespace ssm {
 namespace {
 
-// SiLU(v) = v / (1 + e^-v); for very negative v, e^-v overflows and the result is -0
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
-
 constexpr int kThreads = 256;
 constexpr int kT = 16;        // time steps per tile == lanes per DPP row
 constexpr int kTS = kT + 4;   // padded LDS row: conflict-free b128 reads by 16 lanes

@@ -11,6 +11,11 @@ hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_na
     p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
     p.batch = a.batch; p.L = a.L; p.Dm = a.d_inner; p.N = a.d_state;
     const int mode = (int)(a.flags & 0x3u);
+    if (a.L == 1) {      // a decode step: one thread per channel (s6_decode.hip)
+        S6FusedArgs f{a.u, nullptr, nullptr, nullptr, nullptr, a.dt, a.dt_bias, a.A_log, a.B, a.C, a.D, a.y,
+                      a.h0, a.h_final, nullptr, nullptr, a.batch, a.L, a.d_inner, a.d_state, 1, a.bf16, a.flags};
+        return launch_s6_step(f, false, stream, kernel_name);
+    }
     return a.bf16 ? launch_shape<uint16_t, false>(p, mode, stream) : launch_shape<float, false>(p, mode, stream);
 }
 

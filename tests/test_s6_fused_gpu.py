@@ -148,3 +148,28 @@ def test_fused_mamba1_workload_sampled(cuda_device):
     report("s6_layer_mamba1 sampled", y=ey, h_final=eh, u=eu)
     assert ey <= TOL_S6_LAYER and eh <= TOL_F32 and eu <= TOL_F32
     assert np.array_equal(np.stack([cs[b, d] for b, d in units]), cso.astype(np.float32))
+
+
+def test_plain_decode_steps_in_place(cuda_device):
+    """ssm_s6_scan_fwd with L = 1 (the one-thread-per-channel step kernel), h carried in
+    place over T calls, against the fp64 S6 oracle over the T steps; bf16 and fp32, all three
+    input scales, a state size that is not a multiple of 4."""
+    import torch
+    T = 20
+    m = lib()
+    for dtype, N, flags in (("f32", 16, ZOH), ("bf16", 16, DT), ("f32", 6, ONE), ("f32", 64, ZOH)):
+        inp = synth.s6_inputs(3, T, 40, N, seed=(54, N), dtype=dtype, h0=True)
+        yo, ho = oracle.s6_fwd(**inp.arrays, flags=flags)
+        t = inp.torch(cuda_device)
+        h = t["h0"].clone()
+        ys = []
+        for s in range(T):
+            sl = {n: t[n][:, s:s + 1].contiguous() for n in ("u", "dt", "B", "C")}
+            ys.append(m.ssm_s6_scan_fwd(sl["u"], sl["dt"], t["dt_bias"], t["A_log"], sl["B"], sl["C"], t["D"],
+                                        h, flags=flags, h_final=h)[0])
+        torch.cuda.synchronize()
+        ey = synth.max_rel_err(torch.cat(ys, dim=1).cpu().numpy(), yo)
+        eh = synth.max_rel_err(h.cpu().numpy(), ho)
+        report(f"s6 plain decode {dtype} N={N} flags={flags}", y=ey, h_final=eh)
+        tol = TOL_F32 if dtype == "f32" else TOL_BF16
+        assert ey <= tol and eh <= tol
