@@ -99,6 +99,8 @@ def ssd_model(d):
     elems = B * L * H * P
     nc = -(-L // Q)
     bytes_ = elems * 2 + 2 * B * L * G * N * 2 + B * L * H * 4 + elems * 4 + B * H * P * N * 4
+    if d.get("carry"):            # the entering state is read too
+        bytes_ += B * H * P * N * 4
     # dense-square MFMA flops: C.B^T once per (b, chunk, group); (G o L) X, chunk states and
     # state->output per (b, chunk, head)
     flops = 2 * B * nc * (G * Q * Q * N + H * (Q * Q * P + 2 * Q * P * N))
@@ -112,6 +114,8 @@ def trap_model(d):
     elems = B * L * H * P
     nc = -(-L // Q)
     bytes_ = elems * 2 + 2 * B * L * H * N * 2 + 3 * B * L * H * 4 + elems * 4 + B * H * P * N * 4
+    if d.get("carry"):            # the entering state and the previous x, k are read too
+        bytes_ += B * H * P * N * 4 + B * H * (P + N) * 2
     flops = 2 * B * nc * H * (Q * Q * N + Q * Q * P + 2 * Q * P * N)
     return elems, bytes_, flops
 
@@ -242,6 +246,17 @@ def make_runner(name, dev):
             dims["batch"], dims["L"], dims["nheads"], dims["headdim"], dims["d_state"],
             w["chunk_len"]), dtype=torch.uint8, device=dev)
 
+        if w.get("carry"):            # decode: the state carried in place, previous x, k passed
+            states = [t["h0"].clone() for t in copies]
+
+            def step(i):
+                t = copies[i % N_ROTATE]
+                h = states[i % N_ROTATE]
+                lib.ssd_trap_chunk_scan_fwd(t["x"], t["k"], t["q"], t["dt"], t["a"], t["trap"], t["D"], h,
+                                            t["k_prev"], t["x_prev"], chunk_len=w["chunk_len"], y=y,
+                                            h_final=h, workspace=ws)
+            return step, dims, w, ["ssd_trap_step_kernel"]
+
         def step(i):
             t = copies[i % N_ROTATE]
             lib.ssd_trap_chunk_scan_fwd(t["x"], t["k"], t["q"], t["dt"], t["a"], t["trap"], t["D"],
@@ -256,6 +271,16 @@ def make_runner(name, dev):
         ws = torch.empty(lib.ssd_chunk_scan_fwd_workspace_size(
             dims["batch"], dims["L"], dims["nheads"], dims["headdim"], dims["d_state"],
             dims["ngroups"], w["chunk_len"]), dtype=torch.uint8, device=dev)
+
+        if w.get("carry"):            # decode: the state carried in place
+            states = [t["h0"].clone() for t in copies]
+
+            def step(i):
+                t = copies[i % N_ROTATE]
+                h = states[i % N_ROTATE]
+                lib.ssd_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                       h, chunk_len=w["chunk_len"], y=y, h_final=h, workspace=ws)
+            return step, dims, w, ["ssd_step_kernel"]
 
         def step(i):
             t = copies[i % N_ROTATE]
@@ -413,6 +438,8 @@ def measure(name, dev, steps, warmup):
     ms = wall * 1e3 / steps
     kind = w["kind"]
     dims = dict(dims, chunk_len=w.get("chunk_len"))
+    if w.get("carry"):
+        dims["carry"] = True
     if kind == "s6":
         elems, bytes_, ops = s6_model(dims)
     elif kind == "s6_layer":
@@ -492,7 +519,8 @@ def main():
         sec = []
         for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
                             ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("s6_layer_mamba1", 10),
-                            ("s6_decode_mamba1", 50), ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
+                            ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
+                            ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
             es = s["event_ms_median"] * 1e-3
@@ -512,6 +540,9 @@ def main():
                 ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
                 ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
                 ent["kernel_ms"] = round(s["event_ms_median"], 4)
+            elif s["kind"] in ("ssd", "trap") and s["dims"]["L"] == 1:
+                ent["kernel_ms"] = round(s["event_ms_median"], 4)
+                ent["us_per_token_step"] = round(s["event_ms_median"] * 1e3, 2)
             elif s["kind"] in ("ssd", "trap"):
                 ent["mfma_TFLOPs"] = round(s["ops"] / es / 1e12, 1)
                 ent["mfma_frac_bf16"] = round(s["ops"] / es / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)

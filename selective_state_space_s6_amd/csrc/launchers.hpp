@@ -48,6 +48,9 @@ struct SsdArgs {
     bool bf16; uint32_t flags;
     void *workspace;
 };
+// one step (L = 1) of the SSD scan / its trapezoidal form (ssd_decode.hip)
+hipError_t launch_ssd_step(const SsdArgs &a, hipStream_t stream, const char **kernel_name);
+
 struct TrapRotArgs {
     const void *k_raw; const void *q_raw; const float *angles; const float *dt;
     const float *angle_state; void *k; void *q; float *angle_state_out;
@@ -65,6 +68,7 @@ struct SsdTrapArgs {
     int64_t batch, L, nheads, headdim, d_state;
     void *workspace;
 };
+hipError_t launch_ssd_trap_step(const SsdTrapArgs &a, hipStream_t stream, const char **kernel_name);
 size_t ssd_trap_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                                 int64_t d_state);
 hipError_t launch_ssd_trap(const SsdTrapArgs &a, hipStream_t stream, const char **kernel_name);

@@ -705,6 +705,7 @@ size_t ssd_trap_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_
 }
 
 hipError_t launch_ssd_trap(const SsdTrapArgs &a, hipStream_t stream, const char **kernel_name) {
+    if (a.L == 1) return launch_ssd_trap_step(a, stream, kernel_name);   // a decode step
     *kernel_name = "ssd_scan_kernel";
     SsdKp p{};
     p.x = static_cast<const uint16_t *>(a.x);
@@ -739,6 +740,7 @@ hipError_t launch_ssd_trap(const SsdTrapArgs &a, hipStream_t stream, const char 
 }
 
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_name) {
+    if (a.L == 1) return launch_ssd_step(a, stream, kernel_name);   // a decode step (ssd_decode.hip)
     *kernel_name = "ssd_scan_kernel";
     SsdKp p{};
     p.x = static_cast<const uint16_t *>(a.x);

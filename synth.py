@@ -35,9 +35,16 @@ WORKLOADS = {
     # SSD long context: 2 x 32768, 80 heads x 64, N=128, G=8, Q=256, bf16, with final state
     "ssd_long": dict(kind="ssd", batch=2, L=32768, nheads=80, headdim=64, d_state=128, ngroups=8,
                      chunk_len=256, dtype="bf16"),
+    # one decode step of that layer for a serving batch of 64: L = 1, state carried in place
+    "ssd_decode_mamba2": dict(kind="ssd", batch=64, L=1, nheads=24, headdim=64, d_state=128, ngroups=1,
+                              chunk_len=256, dtype="bf16", carry=True),
     # Mamba-3 trapezoidal SSD: 4 x 8192, 32 heads x 64, N=128, per-head k/q, Q=64, bf16
     "trap_mamba3": dict(kind="trap", batch=4, L=8192, nheads=32, headdim=64, d_state=128,
                         chunk_len=64, dtype="bf16"),
+    # one decode step of the trapezoidal layer for a serving batch of 64 (state and the
+    # previous x, k carried)
+    "trap_decode_mamba3": dict(kind="trap", batch=64, L=1, nheads=32, headdim=64, d_state=128,
+                               chunk_len=64, dtype="bf16", carry=True),
     # Mamba-3 rotation of k and q ahead of that scan: 64 angles (every pair of N=128 turns)
     "trap_rot_mamba3": dict(kind="trap_rot", batch=4, L=8192, nheads=32, headdim=64, d_state=128,
                             n_angles=64, chunk_len=64, dtype="bf16"),
@@ -252,12 +259,14 @@ def workload_inputs(name: str, seed=(0,)) -> Inputs:
                          dtype=w["dtype"], dt_bias=w["dt_bias"], D=w["D"])
     if kind == "ssd":
         return ssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"],
-                          w["ngroups"], seed=seed, dtype=w["dtype"])
+                          w["ngroups"], seed=seed, dtype=w["dtype"], h0=w.get("carry", False))
     if kind == "s6_layer":
         return layer_inputs(w["batch"], w["L"], w["d_inner"], w["d_state"], w["d_conv"], seed=seed,
                             dtype=w["dtype"], h0=True)
     if kind in ("trap", "trap_rot"):
-        return trap_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"], seed=seed)
+        carry = w.get("carry", False)
+        return trap_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"], seed=seed,
+                           h0=carry, prev=carry)
     return cssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["n_complex"],
                        w["ngroups"], seed=seed)
 
