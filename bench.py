@@ -35,7 +35,7 @@ S6_ALU_PEAK_TFLOPS = VALU_SLOTS_PER_S / S6_SLOTS_PER_UPDATE * S6_FLOPS_PER_UPDAT
 # HBM bytes per launch of s6_scan_kernel on s6_mamba1, from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch) scaled by a 1 GiB device copy (fetch x 2.0, write x 1.0);
 # valid only for the kernel sources (s6_kernel.hpp + s6_scan.hip) with this sha1
-S6_TRAFFIC = {"src_sha1": "7d4f019bc6588fb8de24b09ef77881eaeeb7a0ff", "bytes": (100213.4 * 2.0 + 99079.1 * 1.0) * 1024}
+S6_TRAFFIC = {"src_sha1": "f913e893c1df0b78458b262d01c0712a30613396", "bytes": (100238.2 * 2.0 + 99077.1 * 1.0) * 1024}
 # adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
 # (products and fmas, 24 flops) plus the recomputed Abar, beta, phi1' (not counted again)
 S6_BWD_FLOPS_PER_UPDATE = 24

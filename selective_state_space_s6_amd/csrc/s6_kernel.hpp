@@ -138,7 +138,12 @@ s6_scan_kernel(S6Kp p) {
     constexpr int EPT = 16 / G;          // (t, d) elements per thread per tile
     __shared__ __attribute__((aligned(16))) float sD[2][CW][kTS];
     __shared__ __attribute__((aligned(16))) float sU[2][CW][kTS];
-    __shared__ __attribute__((aligned(16))) float sY[2][G][kT][CW];
+    // per-state-group partial sums C.h of a tile, [g][t * CW + channel]: a wave's
+    // writes cover 4 state groups at once, so the group stride is padded by 16
+    // floats off a multiple of the 64 banks (no 4-way write conflict); the
+    // reduction reads 64 consecutive floats of one group
+    constexpr int kYS = kT * CW + 16;
+    __shared__ __attribute__((aligned(16))) float sY[2][G][kYS];
 
     const int tid = threadIdx.x;
     const int row = tid >> 4, k = tid & 15;
@@ -307,7 +312,7 @@ s6_scan_kernel(S6Kp p) {
                 yp[t] = ys;
             });
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sY[buf][g][4 * q + i][cl] = yp[4 * q + i];
+            for (int i = 0; i < 4; ++i) sY[buf][g][(4 * q + i) * CW + cl] = yp[4 * q + i];
         });
     };
 
@@ -318,7 +323,7 @@ s6_scan_kernel(S6Kp p) {
             const int tl = e / CW, c = e % CW;
             float s = du_prev[i];
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg) s += sY[buf][gg][tl][c];
+            for (int gg = 0; gg < G; ++gg) s += sY[buf][gg][tl * CW + c];
             if constexpr (FUSE) s *= gate_prev[i];
             bool ok = cval[i];
             if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < p.L);
