@@ -179,6 +179,27 @@ def s6_layer_fwd(x, conv_w, conv_b, dt, dt_bias, A_log, B, C, D, h0=None, conv_s
     return y, hf, u, cs
 
 
+def causal_conv1d(x, w, b=None, state=None, silu=False):
+    """Causal depthwise conv1d in fp64 (builderforce-memory-engine conv1d.ts header and
+    conv1d_forward; mamba-rs 0.4.0 forward.rs F4a for the fused SiLU and the carried state):
+        y[b,t,c] = bias[c] + sum_{k<K} w[c,k] x[b,t-k,c],  x[b,t',c] for t' < 0 from
+        state[b,c,K-1+t'] (oldest first) or 0;  then SiLU if silu.
+    x (batch, L, D); w (D, K); b (D,) or None; state (batch, D, K-1) or None.
+    Returns y (batch, L, D) and the outgoing state (batch, D, K-1) (the last K-1 inputs)."""
+    x, w, b, state = map(_f32, (x, w, b, state))
+    batch, L, Dc = x.shape
+    K = w.shape[1]
+    prev = (state.astype(np.float64).transpose(0, 2, 1) if state is not None
+            else np.zeros((batch, K - 1, Dc)))
+    xe = np.concatenate([prev, x.astype(np.float64)], axis=1)        # times -(K-1) .. L-1
+    y = np.zeros((batch, L, Dc)) + (b.astype(np.float64) if b is not None else 0.0)
+    for k in range(K):             # tap k multiplies x[t - k]
+        y += w[:, k].astype(np.float64) * xe[:, K - 1 - k:K - 1 - k + L, :]
+    if silu:
+        y = y / (1.0 + np.exp(-y))
+    return y, xe[:, L:, :].transpose(0, 2, 1).copy()
+
+
 def ssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_DT, units=None,
             nthreads=None):
     """Sequential SSD (scalar A per head) recurrence in fp64.
