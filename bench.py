@@ -129,6 +129,14 @@ def trap_rot_model(d):
     return elems, bytes_, 0
 
 
+def conv_model(d):
+    """Causal conv1d: read x, write y (dtype size each), weights, bias and the states."""
+    B, L, Cc, K = d["batch"], d["L"], d["channels"], d["d_conv"]
+    isz = 2 if d.get("bf16") else 4
+    elems = B * L * Cc
+    return elems, elems * isz * 2 + Cc * (K + 1) * 4 + 2 * B * Cc * (K - 1) * 4, elems * (2 * K + 4)
+
+
 def cssd_model(d):
     B, L, H, P, Nc, G, Q = (d["batch"], d["L"], d["nheads"], d["headdim"], d["n_complex"],
                             d["ngroups"], d["chunk_len"])
@@ -174,6 +182,16 @@ def make_runner(name, dev):
                                 None, t["dy"], t["dhf"], out=out, workspace=ws)
         w["kind"] = "s6_bwd"
         return step, dims, w, ["s6_bwd_kernel", "s6_bwd_reduce_kernel"]
+    if kind == "conv":
+        t0 = copies[0]
+        y = torch.empty_like(t0["x"])
+        so = torch.empty_like(t0["state"])
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            lib.ssm_causal_conv1d_fwd(t["x"], t["w"], t["bias"], t["state"], silu=w["silu"], y=y, state_out=so)
+        dims = dict(dims, bf16=w["dtype"] == "bf16")
+        return step, dims, w, ["conv1d_kernel", "conv_state_out_kernel"]
     if kind == "s6_layer":
         t0 = copies[0]
         y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
@@ -390,6 +408,15 @@ def cpu_baseline_units(name, n_units):
     inp = synth.workload_inputs(name, seed=(0,))
     d = inp.dims
     w = synth.WORKLOADS[name]
+    if w["kind"] == "conv":          # one batch row of the conv (numpy oracle)
+        a = inp.arrays
+        t0 = time.perf_counter()
+        oracle.causal_conv1d(a["x"][:1], a["w"], a["bias"], None if a["state"] is None else a["state"][:1],
+                             silu=w["silu"])
+        sec = time.perf_counter() - t0
+        elems = d["L"] * d["channels"]
+        return {"value": elems / sec, "unit": "elements/s", "cores": 1, "kind": "oracle",
+                "sample": f"1 of {d['batch']} batch rows of {name} ({elems} elements, {sec:.2f} s wall)"}
     nthr = oracle.default_threads()
     n_units = min(n_units, d["batch"] * d["nheads"])
     units = np.stack([np.arange(n_units) % d["batch"], np.arange(n_units) // d["batch"]], 1)
@@ -454,6 +481,8 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = trap_model(dims)
     elif kind == "trap_rot":
         elems, bytes_, ops = trap_rot_model(dims)
+    elif kind == "conv":
+        elems, bytes_, ops = conv_model(dims)
     else:
         elems, bytes_, ops = cssd_model(dims)
     ev_ms = sorted(per)[len(per) // 2]
@@ -518,7 +547,7 @@ def main():
     if not args.no_secondary and args.workload == "s6_mamba1":
         sec = []
         for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
-                            ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("s6_layer_mamba1", 10),
+                            ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
                             ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
                             ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
             log(f"[bench] secondary {name}")

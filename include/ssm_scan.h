@@ -140,6 +140,25 @@ int ssm_s6_fused_fwd(const void *x, const float *conv_w, const float *conv_b, co
                      int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t d_conv,
                      ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream);
 
+/* ---------------------------------------------- causal conv1d alone ----
+ * The causal depthwise convolution before a scan, on its own [BF-CONV header
+ * and conv1d_forward; RS-M1 F4a for the fused SiLU and the carried state],
+ * e.g. Mamba-2's convolution over the concatenated x, B, C channels:
+ *   y[b,t,c] = bias[c] + sum_{k<d_conv} w[c,k] * x[b,t-k,c],
+ *              x[b,t',c] for t' < 0 from state_in[b,c,d_conv-1+t'] (or 0),
+ * followed by SiLU(v) = v / (1 + exp(-v)) when silu == 1.
+ * state_out[b,c,j] = x at time L-(d_conv-1)+j (the old state's tail when
+ * L < d_conv-1).
+ * Layouts: x, y (batch, L, channels) [dtype] (y rounded to bf16 once when
+ * dtype is SSM_BF16); w (channels, d_conv) fp32 (tap k multiplies x[t-k]);
+ * bias (channels) fp32 or NULL; state_in, state_out (batch, channels,
+ * d_conv-1) fp32, oldest step first, or NULL.  state_out may be state_in; y
+ * may not alias any input (later steps re-read earlier inputs).
+ * Limits: 1 <= d_conv <= SSM_MAX_D_CONV.  No workspace.  fp32 arithmetic. */
+int ssm_causal_conv1d_fwd(const void *x, const float *w, const float *bias, const float *state_in, void *y,
+                          float *state_out, int64_t batch, int64_t L, int64_t channels, int64_t d_conv,
+                          int silu, ssm_dtype_t dtype, hipStream_t stream);
+
 /* --------------------------------------------------------- S6 backward ----
  * Gradients of a scalar loss through the S6 scan above, given dy = dL/dy and
  * optionally dh_final = dL/dh_final: the reverse-time chain rule of the

@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = [
-    "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssm_s6_fused_fwd", "ssd_chunk_scan_fwd",
+    "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd", "ssd_chunk_scan_fwd",
     "ssd_chunk_scan_bwd",
     "ssd_cplx_chunk_scan_fwd", "ssd_trap_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size",
     "ssm_s6_scan_bwd_workspace_size", "ssd_trap_chunk_scan_fwd_workspace_size",
@@ -46,6 +46,8 @@ _lib.ssm_s6_scan_fwd.argtypes = [_P] * 10 + [_I] * 4 + [ctypes.c_int, ctypes.c_u
 _lib.ssm_s6_scan_fwd.restype = ctypes.c_int
 _lib.ssm_s6_fused_fwd.argtypes = [_P] * 16 + [_I] * 5 + [ctypes.c_int, ctypes.c_uint32, _P]
 _lib.ssm_s6_fused_fwd.restype = ctypes.c_int
+_lib.ssm_causal_conv1d_fwd.argtypes = [_P] * 6 + [_I] * 4 + [ctypes.c_int, ctypes.c_int, _P]
+_lib.ssm_causal_conv1d_fwd.restype = ctypes.c_int
 _lib.ssm_s6_scan_bwd_workspace_size.argtypes = [_I] * 4
 _lib.ssm_s6_scan_bwd_workspace_size.restype = _Z
 _lib.ssm_s6_scan_bwd.argtypes = [_P] * 18 + [_I] * 4 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
@@ -225,6 +227,31 @@ def ssm_s6_fused_fwd(x, conv_w, conv_b, dt, dt_bias, A_log, B, C, D, h0=None, co
                                _in_dtype(x), flags, _stream(dev))
     _check(rc)
     return (y, h_final, conv_state_out) if return_final else y
+
+
+def ssm_causal_conv1d_fwd(x, w, bias=None, state_in=None, *, silu=False, y=None, state_out=None,
+                          return_state=False):
+    """Causal depthwise conv1d (+ SiLU).  x (batch, L, channels) fp32|bf16; w (channels, K)
+    fp32; bias (channels,) fp32 or None; state_in (batch, channels, K-1) fp32 or None.
+    Returns y (x's dtype), or (y, state_out) when return_state or state_out is given
+    (state_out=state_in updates the state in place)."""
+    dev = x.device
+    batch, L, Dc = x.shape
+    K = w.shape[1]
+    _req(x, "x", x.dtype, (batch, L, Dc), dev)
+    _req(w, "w", torch.float32, (Dc, K), dev)
+    _opt(bias, "bias", torch.float32, (Dc,), dev)
+    _opt(state_in, "state_in", torch.float32, (batch, Dc, K - 1), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _req(y, "y", x.dtype, (batch, L, Dc), dev)
+    if return_state and state_out is None and K > 1:
+        state_out = torch.empty((batch, Dc, K - 1), dtype=torch.float32, device=dev)
+    _opt(state_out, "state_out", torch.float32, (batch, Dc, K - 1), dev)
+    rc = _lib.ssm_causal_conv1d_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(state_in), _ptr(y), _ptr(state_out),
+                                    batch, L, Dc, K, int(bool(silu)), _in_dtype(x), _stream(dev))
+    _check(rc)
+    return (y, state_out) if (return_state or state_out is not None) else y
 
 
 _S6_GRADS = ("du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")

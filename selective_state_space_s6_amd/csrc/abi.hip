@@ -137,6 +137,35 @@ int ssm_s6_fused_fwd(const void *x, const float *conv_w, const float *conv_b, co
     return launched(E, ssm::launch_s6_fused(a, stream, &kn), kn);
 }
 
+int ssm_causal_conv1d_fwd(const void *x, const float *w, const float *bias, const float *state_in, void *y,
+                          float *state_out, int64_t batch, int64_t L, int64_t channels, int64_t d_conv,
+                          int silu, ssm_dtype_t dtype, hipStream_t stream) {
+    const char *E = "ssm_causal_conv1d_fwd";
+    REQUIRE_PTR(E, x); REQUIRE_PTR(E, w); REQUIRE_PTR(E, y);
+    REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, channels); REQUIRE_POS(E, d_conv);
+    if (d_conv > SSM_MAX_D_CONV)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_conv %lld > %d", E, (long long)d_conv, SSM_MAX_D_CONV);
+    if (silu != 0 && silu != 1) return fail(SSM_ERR_INVALID_ARG, "%s: silu must be 0 or 1 (got %d)", E, silu);
+    if (dtype != SSM_F32 && dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: dtype %d is not SSM_F32 or SSM_BF16", E, (int)dtype);
+    if (too_big(batch, L, channels, 1) || batch * ((L + 31) / 32) * channels > 0x7fffffffLL * 256)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    REQUIRE_ALIGN(E, x); REQUIRE_ALIGN(E, w); REQUIRE_ALIGN(E, bias); REQUIRE_ALIGN(E, state_in);
+    REQUIRE_ALIGN(E, y); REQUIRE_ALIGN(E, state_out);
+    {
+        const void *ins[] = {x, w, bias, state_in};
+        for (const void *in : ins)
+            if (in && in == y) return fail(SSM_ERR_INVALID_ARG, "%s: y aliases an input", E);
+        const void *others[] = {x, w, bias, y};
+        for (const void *o : others)
+            if (state_out && o == (const void *)state_out)
+                return fail(SSM_ERR_INVALID_ARG, "%s: state_out aliases another argument", E);
+    }
+    ssm::Conv1dArgs a{x, w, bias, state_in, y, state_out, batch, L, channels, d_conv, silu == 1, dtype == SSM_BF16};
+    const char *kn = "conv1d";
+    return launched(E, ssm::launch_conv1d(a, stream, &kn), kn);
+}
+
 size_t ssm_s6_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state) {
     if (batch <= 0 || L <= 0 || d_inner <= 0 || d_state <= 0) return 0;
     return ssm::s6_bwd_workspace_bytes(batch, L, d_inner, d_state);

@@ -1,0 +1,167 @@
+// conv1d.hip -- causal depthwise conv1d (+ SiLU) with a carried state
+// (ssm_causal_conv1d_fwd): the step before the scan when it is not fused into
+// it, e.g. Mamba-2's convolution over the concatenated x, B, C channels.
+//
+// builderforce-memory-engine conv1d.ts (header, conv1d_forward) defines
+//   y[b,t,c] = bias[c] + sum_{k<K} w[c,k] x[b,t-k,c]   (zero left padding);
+// mamba-rs 0.4.0 forward.rs F4a fuses SiLU and carries the last K-1 inputs.
+//
+// The page runs one thread per (t, c) reading K inputs each; here a thread
+// walks a run of kRun steps for a vector of channels (16 bytes: 8 bf16 or 4
+// fp32), keeping the last K-1 inputs in registers, so every input is read
+// once from HBM (the K-1 steps before a run are cache hits, or the carried
+// state at the sequence start) and every output written once.  Loads run
+// eight steps ahead.  The outgoing state comes from conv_state.hpp.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "conv_state.hpp"
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kRun = 32;      // steps per thread
+constexpr int kAheadConv = 8;
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {   // round to nearest even (finite values)
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <typename T, int VW> struct VecIO;
+template <> struct VecIO<float, 4> {
+    __device__ __forceinline__ static void ld(const float *p, float (&v)[4]) {
+        const float4 q = *reinterpret_cast<const float4 *>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+    __device__ __forceinline__ static void st(float *p, const float (&v)[4]) {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+template <> struct VecIO<uint16_t, 8> {
+    __device__ __forceinline__ static void ld(const uint16_t *p, float (&v)[8]) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ __forceinline__ static void st(uint16_t *p, const float (&v)[8]) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+};
+template <typename T> struct VecIO<T, 1> {
+    __device__ __forceinline__ static void ld(const T *p, float (&v)[1]) { v[0] = In<T>::ld(p, 0); }
+    __device__ __forceinline__ static void st(T *p, const float (&v)[1]) {
+        if constexpr (sizeof(T) == 2) p[0] = f32_to_bf16(v[0]);
+        else p[0] = v[0];
+    }
+};
+
+struct ConvKp {
+    const void *x; const float *w, *bias, *st; void *y;
+    int64_t batch, L, Dc, nruns, ncv;
+    int K;
+};
+
+template <typename T, int VW, bool SILU>
+__global__ void __launch_bounds__(256) conv1d_kernel(ConvKp p) {
+    const int64_t gt = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (gt >= p.batch * p.nruns * p.ncv) return;
+    const int64_t cv = gt % p.ncv, br = gt / p.ncv, r = br % p.nruns, b = br / p.nruns;
+    const int64_t c0 = cv * VW;
+    const int64_t t0 = r * kRun, t1 = min(t0 + (int64_t)kRun, p.L);
+    const T *x = static_cast<const T *>(p.x);
+    T *y = static_cast<T *>(p.y);
+    float wv[kMaxConvTaps][VW], bv[VW];
+#pragma unroll
+    for (int j = 0; j < VW; ++j) {
+#pragma unroll
+        for (int k = 0; k < kMaxConvTaps; ++k) wv[k][j] = k < p.K ? p.w[(c0 + j) * p.K + k] : 0.0f;
+        bv[j] = p.bias ? p.bias[c0 + j] : 0.0f;
+    }
+    // hist[m] = x at t0 - 3 + m (hist[2] is the step just before)
+    float hist[kMaxConvTaps - 1][VW];
+#pragma unroll
+    for (int m = 0; m < kMaxConvTaps - 1; ++m) {
+        const int64_t tt = t0 - (kMaxConvTaps - 1) + m;
+        if (tt >= 0) {
+            VecIO<T, VW>::ld(x + (b * p.L + tt) * p.Dc + c0, hist[m]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < VW; ++j)
+                hist[m][j] = (p.st && tt >= -(p.K - 1)) ? p.st[(b * p.Dc + c0 + j) * (p.K - 1) + (p.K - 1) + tt] : 0.0f;
+        }
+    }
+    auto step = [&](const float (&xv)[VW], int64_t t) __attribute__((always_inline)) {
+        float out[VW];
+#pragma unroll
+        for (int j = 0; j < VW; ++j) {
+            float a = fmaf(wv[0][j], xv[j], bv[j]);
+            a = fmaf(wv[1][j], hist[2][j], a);
+            a = fmaf(wv[2][j], hist[1][j], a);
+            a = fmaf(wv[3][j], hist[0][j], a);
+            out[j] = SILU ? silu_f(a) : a;
+            hist[0][j] = hist[1][j];
+            hist[1][j] = hist[2][j];
+            hist[2][j] = xv[j];
+        }
+        VecIO<T, VW>::st(y + (b * p.L + t) * p.Dc + c0, out);
+    };
+    int64_t t = t0;
+    for (; t + kAheadConv <= t1; t += kAheadConv) {
+        float xv[kAheadConv][VW];
+#pragma unroll
+        for (int i = 0; i < kAheadConv; ++i) VecIO<T, VW>::ld(x + (b * p.L + t + i) * p.Dc + c0, xv[i]);
+#pragma unroll
+        for (int i = 0; i < kAheadConv; ++i) step(xv[i], t + i);
+    }
+    for (; t < t1; ++t) {
+        float xv[VW];
+        VecIO<T, VW>::ld(x + (b * p.L + t) * p.Dc + c0, xv);
+        step(xv, t);
+    }
+}
+
+template <typename T, int VW>
+void launch_vw(ConvKp p, bool silu, hipStream_t s) {
+    p.nruns = (p.L + kRun - 1) / kRun;
+    p.ncv = p.Dc / VW;
+    const int64_t n = p.batch * p.nruns * p.ncv;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (silu) hipLaunchKernelGGL((conv1d_kernel<T, VW, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((conv1d_kernel<T, VW, false>), grid, dim3(256), 0, s, p);
+}
+
+}  // namespace
+
+hipError_t launch_conv1d(const Conv1dArgs &a, hipStream_t stream, const char **kernel_name) {
+    *kernel_name = "conv1d_kernel";
+    ConvKp p{a.x, a.w, a.bias, a.state_in, a.y, a.batch, a.L, a.channels, 0, 0, (int)a.d_conv};
+    if (a.bf16) {
+        if (a.channels % 8 == 0) launch_vw<uint16_t, 8>(p, a.silu, stream);
+        else launch_vw<uint16_t, 1>(p, a.silu, stream);
+    } else {
+        if (a.channels % 4 == 0) launch_vw<float, 4>(p, a.silu, stream);
+        else launch_vw<float, 1>(p, a.silu, stream);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.state_out == nullptr || a.d_conv < 2) return e;
+    *kernel_name = "conv_state_out_kernel";
+    if (a.bf16)
+        launch_conv_state_out(static_cast<const uint16_t *>(a.x), a.state_in, a.state_out, a.batch, a.L, a.channels,
+                              (int)a.d_conv, stream);
+    else
+        launch_conv_state_out(static_cast<const float *>(a.x), a.state_in, a.state_out, a.batch, a.L, a.channels,
+                              (int)a.d_conv, stream);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -35,8 +35,9 @@ __device__ __forceinline__ float phi1_small(float z) {
     return fmaf(z, p, 1.0f);
 }
 
-// SiLU(v) = v / (1 + e^-v); for very negative v, e^-v overflows and the result is -0
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU(v) = v / (1 + e^-v), with the hardware reciprocal (about 1 ulp) in place of a
+// division; for very negative v, e^-v overflows, its reciprocal is 0 and the result -0
+__device__ __forceinline__ float silu_f(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // bf16 <-> fp32 (bf16 is the high half of an fp32 word)
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {

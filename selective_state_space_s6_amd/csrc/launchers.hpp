@@ -28,6 +28,14 @@ hipError_t launch_s6_fused(const S6FusedArgs &a, hipStream_t stream, const char 
 // one step (L = 1) of either entry point; fused picks the conv + gate form
 hipError_t launch_s6_step(const S6FusedArgs &a, bool fused, hipStream_t stream, const char **kernel_name);
 
+// causal depthwise conv1d (+ SiLU) with a carried state (conv1d.hip)
+struct Conv1dArgs {
+    const void *x; const float *w; const float *bias; const float *state_in; void *y; float *state_out;
+    int64_t batch, L, channels, d_conv;
+    bool silu, bf16;
+};
+hipError_t launch_conv1d(const Conv1dArgs &a, hipStream_t stream, const char **kernel_name);
+
 struct S6BwdArgs {
     const void *u; const float *dt; const float *dt_bias; const float *A_log;
     const void *B; const void *C; const float *D; const float *h0;

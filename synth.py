@@ -38,6 +38,8 @@ WORKLOADS = {
     # one decode step of that layer for a serving batch of 64: L = 1, state carried in place
     "ssd_decode_mamba2": dict(kind="ssd", batch=64, L=1, nheads=24, headdim=64, d_state=128, ngroups=1,
                               chunk_len=256, dtype="bf16", carry=True),
+    # the Mamba-2 layer's causal conv (K=4) + SiLU over x, B, C (1536 + 2 x 128 channels)
+    "conv_mamba2": dict(kind="conv", batch=8, L=4096, channels=1792, d_conv=4, dtype="bf16", silu=True),
     # Mamba-3 trapezoidal SSD: 4 x 8192, 32 heads x 64, N=128, per-head k/q, Q=64, bf16
     "trap_mamba3": dict(kind="trap", batch=4, L=8192, nheads=32, headdim=64, d_state=128,
                         chunk_len=64, dtype="bf16"),
@@ -163,6 +165,23 @@ def layer_inputs(batch, L, d_inner, d_state, d_conv=4, *, seed=(0,), dtype="f32"
     return Inputs("s6_layer", dict(inp.dims, d_conv=d_conv), a, bf)
 
 
+def conv_inputs(batch, L, channels, d_conv=4, *, seed=(0,), dtype="bf16", state=True) -> Inputs:
+    """Causal conv1d inputs: x ~ N(0, 1) (rounded to bf16 when dtype is bf16), w, bias ~
+    U(-1/sqrt(K), 1/sqrt(K)), the carried state ~ N(0, 1) (fp32, holding bf16 values when x is
+    bf16, as a state carried from earlier inputs would)."""
+    key = (8, *seed)
+    bound = 1.0 / math.sqrt(d_conv)
+    x = _normal(_rng(key, 0), (batch, L, channels))
+    st = _normal(_rng(key, 3), (batch, channels, d_conv - 1)) if state and d_conv > 1 else None
+    if dtype == "bf16":
+        x = round_bf16(x)
+        st = None if st is None else round_bf16(st)
+    return Inputs("conv", dict(batch=batch, L=L, channels=channels, d_conv=d_conv),
+                  dict(x=x, w=_uniform(_rng(key, 1), (channels, d_conv), -bound, bound),
+                       bias=_uniform(_rng(key, 2), (channels,), -bound, bound), state=st),
+                  ("x",) if dtype == "bf16" else ())
+
+
 def s6_cotangents(batch, L, d_inner, d_state, *, seed=(0,), dh_final=True):
     """Seeded dL/dy (batch, L, d_inner) and dL/dh_final (batch, d_inner, d_state),
     both N(0, 1) fp32, for the backward pass (dh_final None when not asked)."""
@@ -260,6 +279,8 @@ def workload_inputs(name: str, seed=(0,)) -> Inputs:
     if kind == "ssd":
         return ssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"],
                           w["ngroups"], seed=seed, dtype=w["dtype"], h0=w.get("carry", False))
+    if kind == "conv":
+        return conv_inputs(w["batch"], w["L"], w["channels"], w["d_conv"], seed=seed, dtype=w["dtype"])
     if kind == "s6_layer":
         return layer_inputs(w["batch"], w["L"], w["d_inner"], w["d_state"], w["d_conv"], seed=seed,
                             dtype=w["dtype"], h0=True)

@@ -35,6 +35,7 @@ def lib():
     L.ssd_trap_chunk_scan_fwd_workspace_size.restype = Z
     L.ssd_trap_rotate_qk.argtypes = [P] * 8 + [I] * 5 + [ctypes.c_int, P, Z, P]
     L.ssm_s6_fused_fwd.argtypes = [P] * 16 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P]
+    L.ssm_causal_conv1d_fwd.argtypes = [P] * 6 + [I] * 4 + [ctypes.c_int, ctypes.c_int, P]
     L.ssd_trap_rotate_qk_workspace_size.argtypes = [I] * 5
     L.ssd_trap_rotate_qk_workspace_size.restype = Z
     for f in ("ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size"):
@@ -52,7 +53,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M))
     names = {n for n in names if n.startswith(("ssm_", "ssd_"))}
     assert names == {"ssm_last_error", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_fwd",
-                     "ssm_s6_fused_fwd",
+                     "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd",
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
                      "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
@@ -275,3 +276,23 @@ def test_fused_argument_checks(lib):
     assert _fused(lib, y=ctypes.c_void_p(0x100000)) == INVALID and "alias" in _err(lib)            # y == x
     assert _fused(lib, u_out=ctypes.c_void_p(0xC00000)) == INVALID and "alias" in _err(lib)        # == y
     assert _fused(lib, conv_state_out=ctypes.c_void_p(0x200000)) == INVALID and "alias" in _err(lib)  # == conv_w
+
+
+def _conv(lib, dims=(2, 40, 24, 4), silu=1, dtype=1, **kw):
+    names = ["x", "w", "bias", "state_in", "y", "state_out"]
+    required = {"x", "w", "y"}
+    ptrs = {n: (ctypes.c_void_p(0x100000 * (i + 1)) if n in required else None) for i, n in enumerate(names)}
+    ptrs.update(kw)
+    return lib.ssm_causal_conv1d_fwd(*(ptrs[n] for n in names), *dims, silu, dtype, None)
+
+
+def test_conv1d_argument_checks(lib):
+    assert _conv(lib, w=None) == INVALID and "w is NULL" in _err(lib)
+    assert _conv(lib, dims=(2, 40, 24, 0)) == INVALID and "d_conv" in _err(lib)
+    assert _conv(lib, dims=(2, 40, 24, 5)) == UNSUPPORTED and "d_conv" in _err(lib)
+    assert _conv(lib, dims=(2, 0, 24, 4)) == INVALID
+    assert _conv(lib, silu=2) == INVALID and "silu" in _err(lib)
+    assert _conv(lib, dtype=9) == INVALID and "dtype" in _err(lib)
+    assert _conv(lib, bias=MIS) == UNSUPPORTED and "aligned" in _err(lib)
+    assert _conv(lib, y=ctypes.c_void_p(0x100000)) == INVALID and "alias" in _err(lib)            # y == x
+    assert _conv(lib, state_out=ctypes.c_void_p(0x500000)) == INVALID and "alias" in _err(lib)    # == y
