@@ -341,6 +341,33 @@ def time_steps(step, steps, warmup):
     return wall, per
 
 
+def graph_us_per_step(step, n=32, replays=20):
+    """Per-step time of n steps captured in one HIP graph and replayed (the launch-bound
+    decode loop without per-call host work): HIP events around the replays, on the stream
+    the graph runs on."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            step(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (replays * n)
+
+
 def cpu_baseline_s6(name):
     """The fp64 oracle, untuned, on the host cores: the whole workload."""
     import numpy as np
@@ -462,6 +489,7 @@ def s6_traffic(name):
 def measure(name, dev, steps, warmup):
     step, dims, w, kernels = make_runner(name, dev)
     wall, per = time_steps(step, steps, warmup)
+    graph_us = graph_us_per_step(step) if dims.get("L") == 1 else None
     ms = wall * 1e3 / steps
     kind = w["kind"]
     dims = dict(dims, chunk_len=w.get("chunk_len"))
@@ -487,7 +515,7 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = cssd_model(dims)
     ev_ms = sorted(per)[len(per) // 2]
     return dict(name=name, kind=kind, dims=dims, dtype=w["dtype"], ms=ms, event_ms_median=ev_ms,
-                event_ms=per, elems=elems, bytes=bytes_, ops=ops, kernels=kernels)
+                event_ms=per, elems=elems, bytes=bytes_, ops=ops, kernels=kernels, graph_us=graph_us)
 
 
 def main():
@@ -564,14 +592,15 @@ def main():
                 ent["kernel_ms"] = round(s["event_ms_median"], 4)
                 ent["alu_frac"] = round(s["ops"] / es / 1e12 / S6_ALU_PEAK_TFLOPS, 4)
                 if s["dims"]["L"] == 1:
-                    ent["us_per_token_step"] = round(s["event_ms_median"] * 1e3, 2)
+                    ent["us_per_step_eager"] = round(s["event_ms_median"] * 1e3, 2)
+                    ent["us_per_step_graph"] = round(s["graph_us"], 2)
             elif s["kind"] == "ssd_bwd":
                 ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
                 ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
                 ent["kernel_ms"] = round(s["event_ms_median"], 4)
             elif s["kind"] in ("ssd", "trap") and s["dims"]["L"] == 1:
-                ent["kernel_ms"] = round(s["event_ms_median"], 4)
-                ent["us_per_token_step"] = round(s["event_ms_median"] * 1e3, 2)
+                ent["us_per_step_eager"] = round(s["event_ms_median"] * 1e3, 2)
+                ent["us_per_step_graph"] = round(s["graph_us"], 2)
             elif s["kind"] in ("ssd", "trap"):
                 ent["mfma_TFLOPs"] = round(s["ops"] / es / 1e12, 1)
                 ent["mfma_frac_bf16"] = round(s["ops"] / es / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
