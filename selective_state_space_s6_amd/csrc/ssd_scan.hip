@@ -48,7 +48,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kT = 32;              // steps per chunk
-constexpr int kTargetWaves = 3072;  // enough resident waves to hide latency (3 per SIMD)
+constexpr int kCUs = 256;           // compute units of the chip
+constexpr int kWavesPerCU = 12;     // resident waves per CU at the kernels' register use (3 per SIMD)
+constexpr int kMaxSeg = 64;         // at most this many segments (bounds the workspace)
 constexpr int kMinSeg = 256;        // shortest segment worth a state round trip
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -652,14 +654,30 @@ ssd_trap_h0_kernel(SsdKp p, const uint16_t *x_prev, const uint16_t *k_prev, floa
 struct Plan {
     int64_t nseg, Ls;
 };
-// Segments: enough (batch, segment, head) groups for kTargetWaves waves, no
-// segment shorter than kMinSeg steps, lengths a multiple of the chunk.
+// Segments.  The (batch, segment, head) groups run in rounds of kResident
+// groups per CU (3 waves per SIMD), and a group walks its segment's chunks in
+// order, so the scan takes about rounds x segment length.  The count that
+// minimises that product is taken (a larger count must win by 3 %, as every
+// segment adds a state round trip); no segment is shorter than kMinSeg steps,
+// lengths are a multiple of the chunk.  A count whose groups spill a few past a
+// full round would run the whole chain twice.
 Plan plan(int64_t batch, int64_t L, int64_t H, int64_t P) {
-    const int64_t waves = batch * H * (P / 16);
-    int64_t nseg = (kTargetWaves + waves - 1) / waves;
-    nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, L / kMinSeg));
-    const int64_t Ls = ((L + nseg - 1) / nseg + kT - 1) / kT * kT;
-    return Plan{(L + Ls - 1) / Ls, Ls};
+    const int64_t nw = P / 16;                                        // waves per group
+    const int64_t per_round = kCUs * std::max<int64_t>(1, kWavesPerCU / nw);
+    const int64_t max_seg = std::max<int64_t>(1, std::min<int64_t>(L / kMinSeg, kMaxSeg));
+    Plan best{1, (L + kT - 1) / kT * kT};
+    int64_t best_cost = -1;
+    for (int64_t ns = 1; ns <= max_seg; ++ns) {
+        const int64_t Ls = ((L + ns - 1) / ns + kT - 1) / kT * kT;
+        const int64_t nseg = (L + Ls - 1) / Ls;
+        const int64_t rounds = (batch * H * nseg + per_round - 1) / per_round;
+        const int64_t cost = rounds * Ls;
+        if (best_cost < 0 || cost * 100 < best_cost * 97) {
+            best = Plan{nseg, Ls};
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
