@@ -71,6 +71,7 @@ def _load():
     lib.oracle_ssd_bwd.argtypes = [P] * 10 + [I] * 6 + [ctypes.c_uint32, P, I] + [P] * 8 + [ctypes.c_int]
     lib.oracle_trap_fwd.argtypes = [P] * 10 + [I] * 5 + [P, I, P, P, ctypes.c_int]
     lib.oracle_trap_rotate.argtypes = [P] * 5 + [I] * 5 + [P] * 3
+    lib.oracle_trap_bwd.argtypes = [P] * 12 + [I] * 5 + [P, I] + [P] * 10 + [ctypes.c_int]
     lib.oracle_s6_layer_fwd.argtypes = [P] * 12 + [I] * 5 + [ctypes.c_uint32, P, I] + [P] * 4 + [ctypes.c_int]
     for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd, lib.oracle_s6_bwd,
               lib.oracle_ssd_bwd, lib.oracle_trap_fwd):
@@ -264,6 +265,39 @@ def trap_rotate(k, q, angles, dt, angle_state=None):
     _load().oracle_trap_rotate(_ptr(k), _ptr(q), _ptr(angles), _ptr(dt), _ptr(angle_state),
                                batch, L, H, N, NA, _ptr(ko), _ptr(qo), _ptr(so))
     return ko, qo, so
+
+
+def trap_bwd(x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final=None, units=None, nthreads=None):
+    """Gradients of the Mamba-3 trapezoidal recurrence (trap_fwd) in fp64.
+
+    dy: (batch, L, H, P); dh_final: (batch, H, P, N) or None.  Without units returns a dict
+    of full gradients: dx (batch, L, H, P); dk, dq (batch, L, H, N); ddt, da, dtrap
+    (batch, L, H); dD (H,) (summed over the batch); dh0 (batch, H, P, N); dx_prev
+    (batch, H, P); dk_prev (batch, H, N).  With (b, h) units, the per-unit pieces
+    (dD per unit)."""
+    x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final = map(
+        _f32, (x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final))
+    batch, L, H, P = x.shape
+    N = k.shape[3]
+    uu, full = _units(units, batch, H)
+    nu = uu.shape[0]
+    out = dict(dx=np.empty((nu, L, P)), dk=np.empty((nu, L, N)), dq=np.empty((nu, L, N)),
+               ddt=np.empty((nu, L)), da=np.empty((nu, L)), dtrap=np.empty((nu, L)),
+               dh0=np.empty((nu, P, N)), dx_prev=np.empty((nu, P)), dk_prev=np.empty((nu, N)),
+               dD=np.empty((nu,)))
+    _load().oracle_trap_bwd(_ptr(x), _ptr(k), _ptr(q), _ptr(dt), _ptr(a), _ptr(trap), _ptr(D), _ptr(h0),
+                            _ptr(k_prev), _ptr(x_prev), _ptr(dy), _ptr(dh_final), batch, L, H, P, N,
+                            _ptr(uu), nu, *(_ptr(out[n]) for n in ("dx", "dk", "dq", "ddt", "da", "dtrap",
+                                                                    "dh0", "dx_prev", "dk_prev", "dD")),
+                            nthreads or default_threads())
+    if not full:
+        return out
+    r = lambda v, *shape: v.reshape(batch, H, *shape)
+    return dict(dx=r(out["dx"], L, P).transpose(0, 2, 1, 3).copy(), dk=r(out["dk"], L, N).transpose(0, 2, 1, 3).copy(),
+                dq=r(out["dq"], L, N).transpose(0, 2, 1, 3).copy(),
+                ddt=r(out["ddt"], L).transpose(0, 2, 1).copy(), da=r(out["da"], L).transpose(0, 2, 1).copy(),
+                dtrap=r(out["dtrap"], L).transpose(0, 2, 1).copy(), dh0=r(out["dh0"], P, N),
+                dx_prev=r(out["dx_prev"], P), dk_prev=r(out["dk_prev"], N), dD=out["dD"].reshape(batch, H).sum(0))
 
 
 def ssd_bwd(x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, ngroups=1, flags=BBAR_DT,

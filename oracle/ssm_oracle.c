@@ -299,7 +299,7 @@ static void cssd_unit(const cssd_job *j, int64_t k)
 /* ------------------------------------------------------------ threads --- */
 
 typedef struct {
-    int kind;               /* 0 S6, 1 SSD, 2 complex, 3 SSD backward, 4 trapezoidal SSD */
+    int kind;               /* 0 S6, 1 SSD, 2 complex, 3 SSD backward, 4 trapezoidal SSD, 5 its backward */
     const void *job;
     int64_t n_units;
     int tid, nthreads;
@@ -356,6 +356,141 @@ static void trap_unit(const trap_job *j, int64_t u)
     }
     if (j->hf_out) memcpy(j->hf_out + u * P * N, S, sizeof(double) * (size_t)(P * N));
     free(S); free(xp); free(kp);
+}
+
+/* ------------------------------------ Mamba-3 trapezoidal backward --- */
+/*
+ * Gradients of a loss through the trapezoidal recurrence above (mamba-rs
+ * 0.2.1 mamba3_gpu.rs pairs F6 with a chunked backward, B6; this is the plain
+ * reverse-time chain rule any such scheme must match), given dy = dL/dy and
+ * optionally dh_final.  Per unit (b, h), with G_t = dL/dh_t,
+ *   G_{L-1} = dh_final + dy_{L-1} (x) q_{L-1},  G_t = dy_t (x) q_t + alpha_{t+1} G_{t+1}
+ *   dq_t = h_t^T dy_t;  dx_t = D dy_t + gamma_t G_t k_t + beta_{t+1} G_{t+1} k_t
+ *   dk_t = gamma_t G_t^T x_t + beta_{t+1} G_{t+1}^T x_t   (step -1: x_prev, k_prev)
+ *   dalpha_t = <G_t, h_{t-1}>, dbeta_t = <G_t, x_{t-1} (x) k_{t-1}>, dgamma_t = <G_t, x_t (x) k_t>
+ *   da_t    = dalpha_t dt_t alpha_t + dbeta_t dt_t beta_t
+ *   ddt_t   = dalpha_t a_t alpha_t + dbeta_t (1 - trap_t) alpha_t (1 + a_t dt_t) + dgamma_t trap_t
+ *   dtrap_t = dgamma_t dt_t - dbeta_t alpha_t dt_t
+ *   dD = sum dy . x,  dh0 = alpha_0 G_0.
+ * States are recomputed from checkpoints every TRAPB_KSEG steps.  Outputs per
+ * unit: dx [L][P], dk, dq [L][N], ddt, da, dtrap [L], dh0 [P][N], dx_prev [P],
+ * dk_prev [N], dD [1].
+ */
+#define TRAPB_KSEG 256
+typedef struct {
+    const float *x, *k, *q, *dt, *a, *trap, *D, *h0, *k_prev, *x_prev, *dy, *dh_final;
+    int64_t batch, L, H, P, N;
+    const int64_t *units;
+    int64_t n_units;
+    double *dx, *dk, *dq, *ddt, *da, *dtrap, *dh0, *dx_prev, *dk_prev, *dD;
+} trapb_job;
+
+static void trapb_unit(const trapb_job *j, int64_t u)
+{
+    const int64_t b = j->units[2 * u], hh = j->units[2 * u + 1];
+    const int64_t L = j->L, H = j->H, P = j->P, N = j->N, PN = P * N;
+    const double Dh = j->D ? (double)j->D[hh] : 0.0;
+    const int64_t nck = (L + TRAPB_KSEG - 1) / TRAPB_KSEG;
+    double *ck = (double *)malloc(sizeof(double) * (size_t)(nck * PN));      /* state entering each segment */
+    double *Ss = (double *)malloc(sizeof(double) * (size_t)((TRAPB_KSEG + 1) * PN));
+    double *Gm = (double *)malloc(sizeof(double) * (size_t)PN);
+    double *S = (double *)malloc(sizeof(double) * (size_t)PN);
+    double *xm = (double *)malloc(sizeof(double) * (size_t)P);
+    double *km = (double *)malloc(sizeof(double) * (size_t)N);
+    #define TB_O(t) ((b * L + (t)) * H + hh)
+    /* x, k of step t (t = -1: the carried pair) */
+    #define TB_X(t, p) ((t) >= 0 ? (double)j->x[TB_O(t) * P + (p)] : (j->x_prev ? (double)j->x_prev[(b * H + hh) * P + (p)] : 0.0))
+    #define TB_K(t, n) ((t) >= 0 ? (double)j->k[TB_O(t) * N + (n)] : (j->k_prev ? (double)j->k_prev[(b * H + hh) * N + (n)] : 0.0))
+    /* forward: checkpoints */
+    for (int64_t i = 0; i < PN; ++i) S[i] = j->h0 ? (double)j->h0[(b * H + hh) * PN + i] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        if (t % TRAPB_KSEG == 0) memcpy(ck + (t / TRAPB_KSEG) * PN, S, sizeof(double) * (size_t)PN);
+        const double dt = (double)j->dt[TB_O(t)], a = (double)j->a[TB_O(t)], tr = (double)j->trap[TB_O(t)];
+        const double al = exp(a * dt), be = al * dt * (1.0 - tr), ga = tr * dt;
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n)
+                S[p * N + n] = al * S[p * N + n] + be * TB_X(t - 1, p) * TB_K(t - 1, n) + ga * TB_X(t, p) * TB_K(t, n);
+    }
+    /* reverse */
+    for (int64_t i = 0; i < PN; ++i) Gm[i] = j->dh_final ? (double)j->dh_final[(b * H + hh) * PN + i] : 0.0;
+    for (int64_t p = 0; p < P; ++p) xm[p] = 0.0;     /* pending dx of step t from step t+1's beta term */
+    for (int64_t n = 0; n < N; ++n) km[n] = 0.0;
+    double dD = 0.0;
+    for (int64_t c = nck - 1; c >= 0; --c) {
+        const int64_t T0 = c * TRAPB_KSEG, T1 = T0 + TRAPB_KSEG < L ? T0 + TRAPB_KSEG : L;
+        /* recompute the segment's states: Ss[i] = h_{T0-1+i} */
+        memcpy(Ss, ck + c * PN, sizeof(double) * (size_t)PN);
+        for (int64_t t = T0; t < T1; ++t) {
+            const double dt = (double)j->dt[TB_O(t)], a = (double)j->a[TB_O(t)], tr = (double)j->trap[TB_O(t)];
+            const double al = exp(a * dt), be = al * dt * (1.0 - tr), ga = tr * dt;
+            const double *Sp = Ss + (t - T0) * PN;
+            double *Sn = Ss + (t - T0 + 1) * PN;
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t n = 0; n < N; ++n)
+                    Sn[p * N + n] = al * Sp[p * N + n] + be * TB_X(t - 1, p) * TB_K(t - 1, n) + ga * TB_X(t, p) * TB_K(t, n);
+        }
+        for (int64_t t = T1 - 1; t >= T0; --t) {
+            const int64_t o = TB_O(t);
+            const double dt = (double)j->dt[o], a = (double)j->a[o], tr = (double)j->trap[o];
+            const double al = exp(a * dt), be = al * dt * (1.0 - tr), ga = tr * dt;
+            const float *dyt = j->dy + o * P, *qt = j->q + o * N;
+            const double *Ht = Ss + (t - T0 + 1) * PN, *Hp = Ss + (t - T0) * PN;
+            /* G_t = G_t (carried, already alpha_{t+1} G_{t+1} + dh_final) + dy_t (x) q_t */
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t n = 0; n < N; ++n) Gm[p * N + n] += (double)dyt[p] * (double)qt[n];
+            /* dq_t */
+            for (int64_t n = 0; n < N; ++n) {
+                double s = 0.0;
+                for (int64_t p = 0; p < P; ++p) s += Ht[p * N + n] * (double)dyt[p];
+                j->dq[(u * L + t) * N + n] = s;
+            }
+            /* dalpha, dbeta, dgamma */
+            double dal = 0.0, dbe = 0.0, dga = 0.0;
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t n = 0; n < N; ++n) {
+                    const double g = Gm[p * N + n];
+                    dal += g * Hp[p * N + n];
+                    dbe += g * TB_X(t - 1, p) * TB_K(t - 1, n);
+                    dga += g * TB_X(t, p) * TB_K(t, n);
+                }
+            /* dx_t, dk_t: own gamma term plus the pending beta term of step t+1 */
+            for (int64_t p = 0; p < P; ++p) {
+                double s = 0.0;
+                for (int64_t n = 0; n < N; ++n) s += Gm[p * N + n] * TB_K(t, n);
+                j->dx[(u * L + t) * P + p] = Dh * (double)dyt[p] + ga * s + xm[p];
+                dD += (double)dyt[p] * TB_X(t, p);
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                double s = 0.0;
+                for (int64_t p = 0; p < P; ++p) s += Gm[p * N + n] * TB_X(t, p);
+                j->dk[(u * L + t) * N + n] = ga * s + km[n];
+            }
+            /* this step's beta term, for step t-1 (or the carried pair) */
+            for (int64_t p = 0; p < P; ++p) {
+                double s = 0.0;
+                for (int64_t n = 0; n < N; ++n) s += Gm[p * N + n] * TB_K(t - 1, n);
+                xm[p] = be * s;
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                double s = 0.0;
+                for (int64_t p = 0; p < P; ++p) s += Gm[p * N + n] * TB_X(t - 1, p);
+                km[n] = be * s;
+            }
+            j->da[u * L + t] = dal * dt * al + dbe * dt * be;
+            j->ddt[u * L + t] = dal * a * al + dbe * (1.0 - tr) * al * (1.0 + a * dt) + dga * tr;
+            j->dtrap[u * L + t] = dga * dt - dbe * al * dt;
+            /* carry to step t-1 */
+            for (int64_t i = 0; i < PN; ++i) Gm[i] *= al;
+        }
+    }
+    memcpy(j->dh0 + u * PN, Gm, sizeof(double) * (size_t)PN);
+    memcpy(j->dx_prev + u * P, xm, sizeof(double) * (size_t)P);
+    memcpy(j->dk_prev + u * N, km, sizeof(double) * (size_t)N);
+    j->dD[u] = dD;
+    #undef TB_O
+    #undef TB_X
+    #undef TB_K
+    free(ck); free(Ss); free(Gm); free(S); free(xm); free(km);
 }
 
 /* ------------------------------------------------------- SSD backward --- */
@@ -507,7 +642,8 @@ static void *worker(void *p)
         else if (w->kind == 1) ssd_unit((const ssd_job *)w->job, k);
         else if (w->kind == 2) cssd_unit((const cssd_job *)w->job, k);
         else if (w->kind == 3) ssdb_unit((const ssdb_job *)w->job, k);
-        else trap_unit((const trap_job *)w->job, k);
+        else if (w->kind == 4) trap_unit((const trap_job *)w->job, k);
+        else trapb_unit((const trapb_job *)w->job, k);
     }
     return NULL;
 }
@@ -836,6 +972,18 @@ void oracle_trap_rotate(const float *k, const float *q, const float *angles, con
             for (int64_t j = 0; j < NA; ++j) state_out[(b * H + h) * NA + j] = th[j];
         }
     free(th);
+}
+
+void oracle_trap_bwd(const float *x, const float *k, const float *q, const float *dt, const float *a,
+                     const float *trap, const float *D, const float *h0, const float *k_prev,
+                     const float *x_prev, const float *dy, const float *dh_final, int64_t batch, int64_t L,
+                     int64_t nheads, int64_t headdim, int64_t d_state, const int64_t *units, int64_t n_units,
+                     double *dx, double *dk, double *dq, double *ddt, double *da, double *dtrap, double *dh0,
+                     double *dx_prev, double *dk_prev, double *dD, int nthreads)
+{
+    trapb_job j = {x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final, batch, L, nheads, headdim,
+                   d_state, units, n_units, dx, dk, dq, ddt, da, dtrap, dh0, dx_prev, dk_prev, dD};
+    run_units(5, &j, n_units, nthreads);
 }
 
 double oracle_softplus(double x) { return sp(x); }
