@@ -213,6 +213,28 @@ def make_runner(name, dev):
             lib.ssm_s6_scan_fwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
                                 None, y=y, h_final=hf)
         return step, dims, w, ["s6_scan_kernel"]
+    if kind == "trap" and bwd:
+        d = dims
+        for r, t in enumerate(copies):
+            rng = np.random.default_rng([9, r])
+            t["dy"] = torch.from_numpy(rng.standard_normal(
+                (d["batch"], d["L"], d["nheads"], d["headdim"]), dtype=np.float32)).to(dev)
+            t["dhf"] = torch.from_numpy(rng.standard_normal(
+                (d["batch"], d["nheads"], d["headdim"], d["d_state"]), dtype=np.float32)).to(dev)
+        ws = torch.empty(lib.ssd_trap_chunk_scan_bwd_workspace_size(
+            d["batch"], d["L"], d["nheads"], d["headdim"], d["d_state"], w["chunk_len"]), dtype=torch.uint8, device=dev)
+        out = {}
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            g = lib.ssd_trap_chunk_scan_bwd(t["x"], t["k"], t["q"], t["dt"], t["a"], t["trap"], t["D"], None, None,
+                                            None, t["dy"], t["dhf"], chunk_len=w["chunk_len"], out=out or None,
+                                            workspace=ws)
+            out.update({k: v for k, v in g.items() if v is not None})
+        w["kind"] = "trap_bwd"
+        return step, dims, w, ["ssdb_walk_f", "ssdb_walk_r1", "ssdb_walk_r2", "ssdb_pass_f", "ssdb_pass_r",
+                               "ssdb_reduce_heads", "ssdb_scal", "ssdb_final",
+                               "trapb_prev_kernel", "trapb_chain_kernel"]
     if kind == "ssd" and bwd:
         d = dims
         for r, t in enumerate(copies):
@@ -418,6 +440,34 @@ def cpu_baseline_s6_bwd(name, n_rows=2):
                       f"({elems} elements, fp64, {sec:.2f} s wall)"}
 
 
+def cpu_baseline_ssd_bwd(name, n_units=64):
+    """The fp64 backward oracle (SSD or trapezoidal) on a bounded sample of (b, head) units,
+    with the runner's cotangents."""
+    import numpy as np
+    import oracle
+    import synth
+    base = name[: -len("_bwd")]
+    inp = synth.workload_inputs(base, seed=(0,))
+    d = inp.dims
+    w = synth.WORKLOADS[base]
+    rng = np.random.default_rng([9 if w["kind"] == "trap" else 5, 0])
+    dy = rng.standard_normal((d["batch"], d["L"], d["nheads"], d["headdim"]), dtype=np.float32)
+    dhf = rng.standard_normal((d["batch"], d["nheads"], d["headdim"], d["d_state"]), dtype=np.float32)
+    nthr = oracle.default_threads()
+    n_units = min(n_units, d["batch"] * d["nheads"])
+    units = np.stack([np.arange(n_units) % d["batch"], np.arange(n_units) // d["batch"]], 1)
+    t0 = time.perf_counter()
+    if w["kind"] == "trap":
+        oracle.trap_bwd(**inp.arrays, dy=dy, dh_final=dhf, units=units, nthreads=nthr)
+    else:
+        oracle.ssd_bwd(**inp.arrays, dy=dy, dh_final=dhf, ngroups=d["ngroups"], units=units, nthreads=nthr)
+    sec = time.perf_counter() - t0
+    elems = n_units * d["L"] * d["headdim"]
+    return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{n_units} of {d['batch'] * d['nheads']} (b, head) units of the {base} backward "
+                      f"({elems} elements, fp64, {sec:.2f} s wall)"}
+
+
 def ssd_bwd_nseg(d):
     """Segments per (batch, head) the SSD backward uses (mirrors its launch plan)."""
     waves = d["batch"] * d["nheads"] * (d["d_state"] // 32)
@@ -503,6 +553,9 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = s6_bwd_model(dims)
     elif kind == "ssd_bwd":
         elems, bytes_, ops = ssd_bwd_model(dict(dims, nseg=ssd_bwd_nseg(dims)))
+    elif kind == "trap_bwd":       # the SSD backward with one group per head, plus the q.k pass
+        dd = dict(dims, ngroups=dims["nheads"])
+        elems, bytes_, ops = ssd_bwd_model(dict(dd, nseg=ssd_bwd_nseg(dd)))
     elif kind == "ssd":
         elems, bytes_, ops = ssd_model(dims)
     elif kind == "trap":
@@ -577,7 +630,7 @@ def main():
         for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
                             ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
                             ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
-                            ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5)):
+                            ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
             es = s["event_ms_median"] * 1e-3
@@ -594,7 +647,7 @@ def main():
                 if s["dims"]["L"] == 1:
                     ent["us_per_step_eager"] = round(s["event_ms_median"] * 1e3, 2)
                     ent["us_per_step_graph"] = round(s["graph_us"], 2)
-            elif s["kind"] == "ssd_bwd":
+            elif s["kind"] in ("ssd_bwd", "trap_bwd"):
                 ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
                 ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
                 ent["kernel_ms"] = round(s["event_ms_median"], 4)
@@ -618,6 +671,8 @@ def main():
             out["cpu_baseline"] = cpu_baseline_s6_bwd(args.workload[: -len("_bwd")])
         elif kind == "s6_layer":
             out["cpu_baseline"] = cpu_baseline_s6_layer(args.workload)
+        elif kind in ("ssd_bwd", "trap_bwd"):
+            out["cpu_baseline"] = cpu_baseline_ssd_bwd(args.workload)
         else:
             out["cpu_baseline"] = cpu_baseline_units(args.workload, 16)
     print(json.dumps(out), flush=True)

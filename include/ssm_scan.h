@@ -318,6 +318,48 @@ int ssd_trap_chunk_scan_fwd(const void *x, const void *k, const void *q, const f
                             int64_t chunk_len, ssm_dtype_t in_dtype,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* --------------------------------------- trapezoidal SSD backward ----
+ * Gradients of a scalar loss through ssd_trap_chunk_scan_fwd, given dy and
+ * optionally dh_final: the reverse-time chain rule of the trapezoidal
+ * recurrence [RS-M3 module header, F5b, F6 and its chunked backward].  With
+ * G_t = dL/dS_t (G_{L-1} = dh_final + dy_{L-1} (x) q_{L-1}, G_t = dy_t (x) q_t + alpha_{t+1} G_{t+1}):
+ *   dq_t = S_t^T dy_t,   dx_t = D dy_t + gamma_t G_t k_t + beta_{t+1} G_{t+1} k_t,
+ *   dk_t = gamma_t G_t^T x_t + beta_{t+1} G_{t+1}^T x_t   (the step before 0: x_prev, k_prev)
+ *   dalpha_t = <G_t, S_{t-1}>, dbeta_t = <G_t, x_{t-1} (x) k_{t-1}>, dgamma_t = <G_t, x_t (x) k_t>
+ *   da_t = dt_t (dalpha_t alpha_t + dbeta_t beta_t)
+ *   ddt_t = dalpha_t a_t alpha_t + dbeta_t (1 - trap_t) alpha_t (1 + a_t dt_t) + dgamma_t trap_t
+ *   dtrap_t = (dgamma_t - dbeta_t alpha_t) dt_t,  dD = sum dy x,  dh0 = alpha_0 G_0.
+ * The kernels run the SSD backward of the shifted state (input scale
+ * sigma_t = gamma_t + dt_{t+1}(1 - trap_{t+1}), k as B, q as C), add the
+ * gradient of each chunk diagonal's gamma in place of sigma, and chain the
+ * per-step gradients to dt, a and trap.
+ *
+ * Inputs: those of ssd_trap_chunk_scan_fwd (same layouts), dy (batch, L,
+ * nheads, headdim) fp32 and dh_final (batch, nheads, headdim, d_state) fp32 or
+ * NULL.  Outputs (fp32, caller-owned, fully overwritten): dx (batch, L,
+ * nheads, headdim); dk, dq (batch, L, nheads, d_state); ddt, da, dtrap (batch,
+ * L, nheads); dD (nheads) or NULL; dh0 (batch, nheads, headdim, d_state) or
+ * NULL; dk_prev (batch, nheads, d_state), dx_prev (batch, nheads, headdim) or
+ * NULL (written when the carried pair is given).  No output may alias an input
+ * or another output.
+ * Limits: in_dtype SSM_BF16; headdim and d_state in {32, 64, 128}; chunk_len in
+ * {64, 128, 256} (checked; the kernels use their own 32-step chunks).
+ * Workspace: ssd_trap_chunk_scan_bwd_workspace_size() bytes, 16-byte aligned,
+ * owned by the caller (the SSD backward's scratch without per-head shares, the
+ * entering state with the carried input folded in, its gradient, and one float
+ * per (b, t, h) for the diagonal's gradient). */
+size_t ssd_trap_chunk_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                              int64_t d_state, int64_t chunk_len);
+
+int ssd_trap_chunk_scan_bwd(const void *x, const void *k, const void *q, const float *dt, const float *a,
+                            const float *trap, const float *D, const float *h0, const void *k_prev,
+                            const void *x_prev, const float *dy, const float *dh_final,
+                            float *dx, float *dk, float *dq, float *ddt, float *da, float *dtrap, float *dD,
+                            float *dh0, float *dk_prev, float *dx_prev,
+                            int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                            int64_t chunk_len, ssm_dtype_t in_dtype,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------- Mamba-3 k, q rotation ----
  * Data-dependent rotation of k and q ahead of ssd_trap_chunk_scan_fwd [RS-M3
  * F5 m3_angle_dt_fwd_seq (angle * dt accumulated per step, carried in the

@@ -20,7 +20,8 @@ __all__ = [
     "ssd_chunk_scan_bwd",
     "ssd_cplx_chunk_scan_fwd", "ssd_trap_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size",
     "ssm_s6_scan_bwd_workspace_size", "ssd_trap_chunk_scan_fwd_workspace_size",
-    "ssd_trap_rotate_qk", "ssd_trap_rotate_qk_workspace_size",
+    "ssd_trap_rotate_qk", "ssd_trap_rotate_qk_workspace_size", "ssd_trap_chunk_scan_bwd",
+    "ssd_trap_chunk_scan_bwd_workspace_size",
     "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
     "ssd_cplx_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
     "SSM_BBAR_ZOH", "SSM_BBAR_DT", "SSM_BBAR_ONE", "SSM_CPLX_STABLE", "SSM_CPLX_DOC",
@@ -68,6 +69,10 @@ _lib.ssd_trap_rotate_qk_workspace_size.argtypes = [_I] * 5
 _lib.ssd_trap_rotate_qk_workspace_size.restype = _Z
 _lib.ssd_trap_rotate_qk.argtypes = [_P] * 8 + [_I] * 5 + [ctypes.c_int, _P, _Z, _P]
 _lib.ssd_trap_rotate_qk.restype = ctypes.c_int
+_lib.ssd_trap_chunk_scan_bwd_workspace_size.argtypes = [_I] * 6
+_lib.ssd_trap_chunk_scan_bwd_workspace_size.restype = _Z
+_lib.ssd_trap_chunk_scan_bwd.argtypes = [_P] * 22 + [_I] * 6 + [ctypes.c_int, _P, _Z, _P]
+_lib.ssd_trap_chunk_scan_bwd.restype = ctypes.c_int
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_cplx_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_uint32, _P, _Z, _P]
@@ -405,6 +410,58 @@ def ssd_trap_rotate_qk(k_raw, q_raw, angles, dt, angle_state=None, *, k=None, q=
                                  workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc)
     return (k, q, angle_state_out) if (return_state or angle_state_out is not None) else (k, q)
+
+
+def ssd_trap_chunk_scan_bwd_workspace_size(batch, L, nheads, headdim, d_state, chunk_len=64) -> int:
+    return int(_lib.ssd_trap_chunk_scan_bwd_workspace_size(batch, L, nheads, headdim, d_state, chunk_len))
+
+
+_TRAP_GRADS = ("dx", "dk", "dq", "ddt", "da", "dtrap", "dD", "dh0", "dk_prev", "dx_prev")
+
+
+def ssd_trap_chunk_scan_bwd(x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final=None, *, chunk_len=64,
+                            out=None, workspace=None):
+    """Gradients of ssd_trap_chunk_scan_fwd.  Inputs as there, plus dy (batch, L, H, P) fp32
+    and dh_final (batch, H, P, N) fp32 or None.  Returns a dict of fp32 tensors: dx; dk, dq;
+    ddt, da, dtrap; dD (H,); dh0 (batch, H, P, N); dk_prev, dx_prev (when the carried pair
+    is given, else None)."""
+    dev = x.device
+    batch, L, H, P = x.shape
+    N = k.shape[3]
+    dty = x.dtype
+    _req(x, "x", dty, (batch, L, H, P), dev)
+    _req(k, "k", dty, (batch, L, H, N), dev)
+    _req(q, "q", dty, (batch, L, H, N), dev)
+    for t_, nm in ((dt, "dt"), (a, "a"), (trap, "trap")):
+        _req(t_, nm, torch.float32, (batch, L, H), dev)
+    _opt(D, "D", torch.float32, (H,), dev)
+    _opt(h0, "h0", torch.float32, (batch, H, P, N), dev)
+    _opt(k_prev, "k_prev", dty, (batch, H, N), dev)
+    _opt(x_prev, "x_prev", dty, (batch, H, P), dev)
+    _req(dy, "dy", torch.float32, (batch, L, H, P), dev)
+    _opt(dh_final, "dh_final", torch.float32, (batch, H, P, N), dev)
+    prev = k_prev is not None
+    shapes = dict(dx=(batch, L, H, P), dk=(batch, L, H, N), dq=(batch, L, H, N), ddt=(batch, L, H),
+                  da=(batch, L, H), dtrap=(batch, L, H), dD=(H,), dh0=(batch, H, P, N),
+                  dk_prev=(batch, H, N) if prev else None, dx_prev=(batch, H, P) if prev else None)
+    g = dict(out or {})
+    for n_ in _TRAP_GRADS:
+        if shapes[n_] is None:
+            g[n_] = None
+            continue
+        if g.get(n_) is None:
+            g[n_] = torch.empty(shapes[n_], dtype=torch.float32, device=dev)
+        _req(g[n_], n_, torch.float32, shapes[n_], dev)
+    ws = ssd_trap_chunk_scan_bwd_workspace_size(batch, L, H, P, N, chunk_len)
+    if workspace is None:
+        workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+    rc = _lib.ssd_trap_chunk_scan_bwd(_ptr(x), _ptr(k), _ptr(q), _ptr(dt), _ptr(a), _ptr(trap), _ptr(D),
+                                      _ptr(h0), _ptr(k_prev), _ptr(x_prev), _ptr(dy), _ptr(dh_final),
+                                      *(_ptr(g[n_]) for n_ in _TRAP_GRADS), batch, L, H, P, N, chunk_len,
+                                      _in_dtype(x), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(dev))
+    _check(rc)
+    return g
 
 
 _SSD_GRADS = ("dx", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")

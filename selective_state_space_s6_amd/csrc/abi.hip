@@ -383,11 +383,69 @@ int ssd_trap_rotate_qk(const void *k_raw, const void *q_raw, const float *angles
     return launched(E, ssm::launch_trap_rotate(args, stream, &kn), kn);
 }
 
+size_t ssd_trap_chunk_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
+                                              int64_t d_state, int64_t chunk_len) {
+    (void)chunk_len;
+    if (batch <= 0 || L <= 0 || nheads <= 0 || headdim <= 0 || d_state <= 0) return 0;
+    return ssm::ssd_trap_bwd_workspace_bytes(batch, L, nheads, headdim, d_state);
+}
+
+int ssd_trap_chunk_scan_bwd(const void *x, const void *k, const void *q, const float *dt, const float *a,
+                            const float *trap, const float *D, const float *h0, const void *k_prev,
+                            const void *x_prev, const float *dy, const float *dh_final,
+                            float *dx, float *dk, float *dq, float *ddt, float *da, float *dtrap, float *dD,
+                            float *dh0, float *dk_prev, float *dx_prev,
+                            int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                            int64_t chunk_len, ssm_dtype_t in_dtype,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssd_trap_chunk_scan_bwd";
+    REQUIRE_PTR(E, x); REQUIRE_PTR(E, k); REQUIRE_PTR(E, q); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, a);
+    REQUIRE_PTR(E, trap); REQUIRE_PTR(E, dy);
+    REQUIRE_PTR(E, dx); REQUIRE_PTR(E, dk); REQUIRE_PTR(E, dq); REQUIRE_PTR(E, ddt); REQUIRE_PTR(E, da);
+    REQUIRE_PTR(E, dtrap);
+    int rc = ssd_check_shape(E, batch, L, nheads, headdim, d_state, nheads, chunk_len);
+    if (rc != SSM_OK) return rc;
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if (in_dtype != SSM_BF16)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: the MFMA path takes bf16 x, k, q (SSM_BF16)", E);
+    if ((k_prev == nullptr) != (x_prev == nullptr))
+        return fail(SSM_ERR_INVALID_ARG, "%s: k_prev and x_prev must be given together", E);
+    if (!(headdim == 32 || headdim == 64 || headdim == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: headdim %lld not in {32, 64, 128}", E, (long long)headdim);
+    if (!(d_state == 32 || d_state == 64 || d_state == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld not in {32, 64, 128}", E, (long long)d_state);
+    if (!(chunk_len == 64 || chunk_len == 128 || chunk_len == 256))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: chunk_len %lld not in {64, 128, 256}", E, (long long)chunk_len);
+    const void *ptrs[] = {x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final, dx, dk, dq, ddt, da, dtrap,
+                          dD, dh0, dk_prev, dx_prev, workspace};
+    for (const void *pp : ptrs)
+        if (!aligned16(pp)) return fail(SSM_ERR_UNSUPPORTED, "%s: a pointer is not 16-byte aligned", E);
+    const void *ins[] = {x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final};
+    const void *outs[] = {dx, dk, dq, ddt, da, dtrap, dD, dh0, dk_prev, dx_prev};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        if (!outs[i]) continue;
+        for (const void *in : ins)
+            if (in == outs[i]) return fail(SSM_ERR_INVALID_ARG, "%s: an output aliases an input", E);
+        for (size_t j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return fail(SSM_ERR_INVALID_ARG, "%s: two outputs alias", E);
+    }
+    const size_t need = ssm::ssd_trap_bwd_workspace_bytes(batch, L, nheads, headdim, d_state);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    ssm::SsdTrapBwdArgs args{x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final,
+                             dx, dk, dq, ddt, da, dtrap, dD, dh0, dk_prev, dx_prev,
+                             batch, L, nheads, headdim, d_state, workspace};
+    const char *kn = "ssd_trap_bwd";
+    return launched(E, ssm::launch_ssd_trap_bwd(args, stream, &kn), kn);
+}
+
 size_t ssd_chunk_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                                          int64_t d_state, int64_t ngroups, int64_t chunk_len) {
     (void)ngroups; (void)chunk_len;
     if (batch <= 0 || L <= 0 || nheads <= 0 || headdim <= 0 || d_state <= 0) return 0;
-    return ssm::ssd_bwd_workspace_bytes(batch, L, nheads, headdim, d_state);
+    return ssm::ssd_bwd_workspace_bytes(batch, L, nheads, headdim, d_state, ngroups);
 }
 
 int ssd_chunk_scan_bwd(const void *x, const float *dt, const float *dt_bias, const float *A_log,
@@ -434,7 +492,7 @@ int ssd_chunk_scan_bwd(const void *x, const float *dt, const float *dt_bias, con
         for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
             if (outs[i] == outs[j]) return fail(SSM_ERR_INVALID_ARG, "%s: two outputs alias", E);
     }
-    const size_t need = ssm::ssd_bwd_workspace_bytes(batch, L, nheads, headdim, d_state);
+    const size_t need = ssm::ssd_bwd_workspace_bytes(batch, L, nheads, headdim, d_state, ngroups);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
                     workspace ? workspace_bytes : (size_t)0);

@@ -91,7 +91,23 @@ struct SsdBwdArgs {
     void *workspace;
 };
 size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
-                               int64_t d_state);
+                               int64_t d_state, int64_t ngroups);
+
+// gradients of the Mamba-3 trapezoidal SSD (ssd_bwd.hip)
+struct SsdTrapBwdArgs {
+    const void *x; const void *k; const void *q;
+    const float *dt; const float *a; const float *trap; const float *D; const float *h0;
+    const void *k_prev; const void *x_prev; const float *dy; const float *dh_final;
+    float *dx, *dk, *dq, *ddt, *da, *dtrap, *dD, *dh0, *dk_prev, *dx_prev;
+    int64_t batch, L, nheads, headdim, d_state;
+    void *workspace;
+};
+size_t ssd_trap_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state);
+hipError_t launch_ssd_trap_bwd(const SsdTrapBwdArgs &a, hipStream_t stream, const char **kernel_name);
+// the trapezoidal form's entering state h0' = h0 + dt_0 (1 - trap_0) x_prev (x) k_prev (ssd_scan.hip)
+hipError_t launch_ssd_trap_h0(const void *x_prev, const void *k_prev, const float *dt, const float *trap,
+                              const float *h0, float *h0p, int64_t batch, int64_t L, int64_t nheads,
+                              int64_t headdim, int64_t d_state, hipStream_t stream);
 hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t stream, const char **kernel_name);
 
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,

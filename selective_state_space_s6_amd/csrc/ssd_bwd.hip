@@ -68,6 +68,13 @@ struct SbKp {
     float *pA, *pD, *pT;               // (batch, nseg, H) partial sums
     int64_t batch, L, H, P, N, G, Ls, nseg;
     int mode;                          // 0 ZOH, 1 DT, 2 ONE
+    // Mamba-3 trapezoidal form (when trap is set): dt is the step as given,
+    // a_t = dt_t aval_t, sigma_t = trap_t dt_t + dt_{t+1} (1 - trap_{t+1}) (the
+    // shifted state's input scale), and ssdb_scal leaves dL/da_t in dyy.  The
+    // walks also apply the diagonal's correction (its scale is gamma_t, not
+    // sigma_t) and walk R2 writes dgamma_t = (q_t.k_t)(dy_t.x_t) to dgam.
+    const float *aval, *trap;
+    float *dgam;                       // (batch, L, H)
 };
 
 __device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
@@ -78,24 +85,41 @@ struct Scal {
     float sig[kQ];    // input scale
     float ecs[kQ];    // e^{cs_t}
     float eme[kQ];    // e^{cs_end - cs_t}
+    float cd[kQ];     // trapezoidal form: gamma_t - sigma_t (times dy_t.x_t where asked for), else 0
     float csend;
 };
 
 // One wave: lanes 0..31 hold steps t0..t0+31 (steps at or past te carry a = 0, sigma = 0).
+// with_dyx: the trapezoidal coefficient is multiplied by dy_t.x_t (written by walk R2).
 __device__ __forceinline__ void chunk_scalars(Scal &sc, const SbKp &p, int64_t b, int64_t h,
-                                              int64_t t0, int64_t te, float bias, float A, int lane) {
+                                              int64_t t0, int64_t te, float bias, float A, int lane,
+                                              bool with_dyx = false) {
     const int64_t t = t0 + (lane & 31);
-    float a = 0.0f, sg = 0.0f;
+    float a = 0.0f, sg = 0.0f, cd = 0.0f;
     if (lane < kQ && t < te) {
-        const float dl = softplus(p.dt[(b * p.L + t) * p.H + h] + bias);
-        a = dl * A;
-        sg = p.mode == 1 ? dl : (p.mode == 0 ? (a == 0.0f ? dl : dl * (expm1f(a) / a)) : 1.0f);
+        const int64_t o = (b * p.L + t) * p.H + h;
+        if (p.trap) {
+            const float dlt = p.dt[o];
+            a = dlt * p.aval[o];
+            sg = p.trap[o] * dlt;
+            if (t + 1 < p.L) {
+                const float dn = p.dt[o + p.H], un = 1.0f - p.trap[o + p.H];
+                sg = fmaf(dn, un, sg);
+                cd = -(dn * un);
+            }
+            if (with_dyx) cd *= p.dyx[o];
+        } else {
+            const float dl = softplus(p.dt[o] + bias);
+            a = dl * A;
+            sg = p.mode == 1 ? dl : (p.mode == 0 ? (a == 0.0f ? dl : dl * (expm1f(a) / a)) : 1.0f);
+        }
     }
     const float v = scan32(a);
     const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
     if (lane < kQ) {
         sc.cs[lane] = v;
         sc.sig[lane] = sg;
+        sc.cd[lane] = cd;
         sc.ecs[lane] = __expf(v);
         sc.eme[lane] = __expf(cend - v);
     }
@@ -166,7 +190,7 @@ ssdb_walk_f(SbKp p) {
     const int64_t k = blockIdx.x % nsl, bh = blockIdx.x / nsl;
     const int64_t b = bh / p.H, h = bh % p.H, g = h * p.G / p.H;
     const int64_t T0 = k * p.Ls, T1 = min(T0 + p.Ls, p.L);
-    const float A = -expf(p.A_log[h]);
+    const float A = p.A_log ? -expf(p.A_log[h]) : 0.0f;
     const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
 
     // S tile (pt, nt): rows p = 16 pt + 4 r + v, column n = 32 w + 16 nt + c16
@@ -188,7 +212,7 @@ ssdb_walk_f(SbKp p) {
         stage_bf16<P, P + 4>(sX, p.x, b, p.L, p.H, h, t0, T1, tid, NTH);
         stage_bf16<N, N + 4>(sB, p.B, b, p.L, p.G, g, t0, T1, tid, NTH);
         if constexpr (!STATE) stage_f32<P, P + 4>(sY, p.dy, b, p.L, p.H, h, t0, T1, tid, NTH);
-        if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane);
+        if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane, !STATE);
         __syncthreads();
         const float csend = sc.csend;
         if constexpr (!STATE) {
@@ -241,9 +265,13 @@ ssdb_walk_f(SbKp p) {
                     }
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int64_t t = t0 + 16 * ti + 4 * r + v;
+                        const int tl = 16 * ti + 4 * r + v;
+                        const int64_t t = t0 + tl;
                         if (t < T1) {
-                            p.dCh[((b * p.L + t) * p.H + h) * N + n] = acc[v];
+                            // the trapezoidal diagonal's share, dq_t += (gamma_t - sigma_t)(dy_t.x_t) k_t,
+                            // is not part of C_t.dC_t (the decay does not act on the diagonal)
+                            const float dc = p.trap ? fmaf(sc.cd[tl], sB[tl][n], acc[v]) : acc[v];
+                            p.dCh[((b * p.L + t) * p.H + h) * N + n] = dc;
                             part[v] += bf(p.C[((b * p.L + t) * p.G + g) * N + n]) * acc[v];
                         }
                     }
@@ -345,7 +373,7 @@ ssdb_walk_r1(SbKp p) {
     const int64_t k = (STATE ? 1 : 0) + blockIdx.x % nsl, bh = blockIdx.x / nsl;
     const int64_t b = bh / p.H, h = bh % p.H, g = h * p.G / p.H;
     const int64_t T0 = k * p.Ls, T1 = min(T0 + p.Ls, p.L);
-    const float A = -expf(p.A_log[h]);
+    const float A = p.A_log ? -expf(p.A_log[h]) : 0.0f;
     const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
 
     // G tile (pt, nt): rows p = 16 pt + 4 r + v, column n = 32 w + 16 nt + c16
@@ -371,7 +399,7 @@ ssdb_walk_r1(SbKp p) {
         stage_f32<P, P + 4>(sY, p.dy, b, p.L, p.H, h, t0, T1, tid, NTH);
         stage_bf16<N, N + 4>(sC, p.C, b, p.L, p.G, g, t0, T1, tid, NTH);
         if constexpr (!STATE) stage_bf16<P, P + 4>(sX, p.x, b, p.L, p.H, h, t0, T1, tid, NTH);
-        if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane);
+        if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane, !STATE);
         __syncthreads();
         const float csend = sc.csend;
         if constexpr (!STATE) {
@@ -425,7 +453,11 @@ ssdb_walk_r1(SbKp p) {
                     for (int v = 0; v < 4; ++v) {
                         const int tl = 16 * ti + 4 * r + v;
                         const int64_t t = t0 + tl;
-                        if (t < T1) p.dBh[((b * p.L + t) * p.H + h) * N + n] = acc[v] * sc.sig[tl];
+                        if (t < T1) {
+                            // plus the trapezoidal diagonal's dk_t += (gamma_t - sigma_t)(dy_t.x_t) q_t
+                            const float db = acc[v] * sc.sig[tl];
+                            p.dBh[((b * p.L + t) * p.H + h) * N + n] = p.trap ? fmaf(sc.cd[tl], sC[tl][n], db) : db;
+                        }
                     }
                 }
         }
@@ -491,7 +523,7 @@ ssdb_walk_r2(SbKp p) {
     const int64_t k = blockIdx.x % p.nseg, bh = blockIdx.x / p.nseg;
     const int64_t b = bh / p.H, h = bh % p.H, g = h * p.G / p.H;
     const int64_t T0 = k * p.Ls, T1 = min(T0 + p.Ls, p.L);
-    const float A = -expf(p.A_log[h]);
+    const float A = p.A_log ? -expf(p.A_log[h]) : 0.0f;
     const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
     const float Dh = p.D ? p.D[h] : 0.0f;
     const int pc = 16 * w + c16;                       // this lane's column p
@@ -566,7 +598,10 @@ ssdb_walk_r2(SbKp p) {
                 float xv = 0.0f, dxv = 0.0f;
                 if (t < T1) {
                     xv = bf(p.x[((b * p.L + t) * p.H + h) * P + pc]);
-                    dxv = fmaf(sc.sig[tl], acc[v], Dh * dyv);
+                    // trapezoidal diagonal: dx_t += (gamma_t - sigma_t)(q_t.k_t) dy_t, with
+                    // q_t.k_t the diagonal of (B C^T) o E (its decay factor there is e^0)
+                    const float sk = p.trap ? fmaf(sc.cd[tl], sM[tl][tl], Dh) : Dh;
+                    dxv = fmaf(sc.sig[tl], acc[v], sk * dyv);
                     p.dx[((b * p.L + t) * p.H + h) * P + pc] = dxv;
                 }
                 const float s0 = row_total16(xv * acc[v]);
@@ -598,6 +633,7 @@ ssdb_walk_r2(SbKp p) {
             const int64_t o = (b * p.L + t0 + tid) * p.H + h;
             p.dsig[o] = s0;
             p.dyx[o] = s2;
+            if (p.trap) p.dgam[o] = sM[tid][tid] * s2;
         }
     }
 }
@@ -701,7 +737,7 @@ __global__ void __launch_bounds__(kScalThreads) ssdb_scal(SbKp p) {
     const int64_t i = blockIdx.x;
     const int64_t h = i % p.H, bk = i / p.H, k = bk % p.nseg, b = bk / p.nseg;
     const int64_t bh = b * p.H + h;
-    const float A = -expf(p.A_log[h]);
+    const float A = p.A_log ? -expf(p.A_log[h]) : 0.0f;
     const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
     const int64_t T0 = k * p.Ls, T1 = min(T0 + p.Ls, p.L);
     const int64_t per = (T1 - T0 + kScalThreads - 1) / kScalThreads;
@@ -717,17 +753,36 @@ __global__ void __launch_bounds__(kScalThreads) ssdb_scal(SbKp p) {
         if (t == p.L - 1) v += (double)p.hfdot[bh];
         return v;
     };
+    // trapezoidal form: sigma of step t from its own and the next step's inputs
+    auto sigma_trap = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t o = (b * p.L + t) * p.H + h;
+        float sg = p.trap[o] * p.dt[o];
+        if (t + 1 < p.L) sg = fmaf(p.dt[o + p.H], 1.0f - p.trap[o + p.H], sg);
+        return sg;
+    };
     double loc = 0.0;
     for (int64_t t = hi - 1; t >= lo; --t) {
-        const float dl = softplus(p.dt[(b * p.L + t) * p.H + h] + bias);
-        loc += dcs(t, sigma(dl, dl * A));
+        if (p.trap) {
+            loc += dcs(t, sigma_trap(t));
+        } else {
+            const float dl = softplus(p.dt[(b * p.L + t) * p.H + h] + bias);
+            loc += dcs(t, sigma(dl, dl * A));
+        }
     }
     sTot[tid] = loc;
     __syncthreads();
     double carry = k + 1 < p.nseg ? p.bnd[bh * p.nseg + k + 1] : 0.0;
     for (int j = kScalThreads - 1; j > tid; --j) carry += sTot[j];
     float aA = 0.0f, aD = 0.0f, aT = 0.0f;
-    for (int64_t t = hi - 1; t >= lo; --t) {
+    if (p.trap) {     // dL/da_t goes to dyy (read above for this step only); the chain to dt follows
+        for (int64_t t = hi - 1; t >= lo; --t) {
+            const int64_t o = (b * p.L + t) * p.H + h;
+            carry += dcs(t, sigma_trap(t));
+            p.dyy[o] = (float)carry;
+            aD += p.dyx[o];
+        }
+    }
+    for (int64_t t = p.trap ? lo - 1 : hi - 1; t >= lo; --t) {
         const int64_t o = (b * p.L + t) * p.H + h;
         const float x = p.dt[o] + bias;
         const float dl = softplus(x);
@@ -770,9 +825,71 @@ __global__ void __launch_bounds__(256) ssdb_final(SbKp p) {
         s1 += p.pD[bk * p.H + h];
         s2 += p.pT[bk * p.H + h];
     }
-    p.dA_log[h] = s0 * -expf(p.A_log[h]);
+    if (p.dA_log) p.dA_log[h] = s0 * -expf(p.A_log[h]);
     if (p.dD) p.dD[h] = s1;
     if (p.ddt_bias) p.ddt_bias[h] = s2;
+}
+
+// ---------------------------------------------------------------------------
+// Mamba-3 trapezoidal backward, after the SSD backward of the shifted state.
+// The forward is SSD(sigma) plus, at each step, (gamma_t - sigma_t)(q_t.k_t) x_t
+// (its chunk diagonal uses gamma), and its entering state is
+// h0' = h0 + c_0 x_prev (x) k_prev with c_t = dt_t (1 - trap_t).
+
+// The entering state's gradient dh0' = dL/dh0 (copied out) and, with the carried
+// pair, dx_prev = c_0 dh0' k_prev, dk_prev = c_0 dh0'^T x_prev and
+// dc_0 = <dh0', x_prev (x) k_prev>.  One group of 256 per (b, h), fixed-order sums.
+__global__ void __launch_bounds__(256) trapb_prev_kernel(SbKp p, const float *dh0p, const uint16_t *x_prev,
+                                                        const uint16_t *k_prev, float *dh0, float *dx_prev,
+                                                        float *dk_prev, float *dc0) {
+    __shared__ float sP[256];
+    const int64_t bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
+    const int tid = threadIdx.x;
+    const float *G = dh0p + bh * p.P * p.N;
+    if (dh0)
+        for (int64_t i = tid; i < p.P * p.N; i += 256) dh0[bh * p.P * p.N + i] = G[i];
+    if (!x_prev) return;
+    const int64_t o0 = b * p.L * p.H + h;         // step 0
+    const float c0 = p.dt[o0] * (1.0f - p.trap[o0]);
+    float part = 0.0f;                            // sum over this thread's rows p of x_prev[p] (G k_prev)[p]
+    for (int64_t i = tid; i < p.P; i += 256) {
+        float s = 0.0f;
+        for (int64_t n = 0; n < p.N; ++n) s = fmaf(G[i * p.N + n], bf(k_prev[bh * p.N + n]), s);
+        if (dx_prev) dx_prev[bh * p.P + i] = c0 * s;
+        part = fmaf(bf(x_prev[bh * p.P + i]), s, part);
+    }
+    for (int64_t n = tid; n < p.N; n += 256) {
+        float s = 0.0f;
+        for (int64_t i = 0; i < p.P; ++i) s = fmaf(G[i * p.N + n], bf(x_prev[bh * p.P + i]), s);
+        if (dk_prev) dk_prev[bh * p.N + n] = c0 * s;
+    }
+    sP[tid] = part;
+    __syncthreads();
+    if (tid == 0) {
+        float tot = 0.0f;
+        for (int j = 0; j < 256; ++j) tot += sP[j];
+        dc0[bh] = tot;
+    }
+}
+
+// The chain to the inputs, one thread per (b, t, h).  The SSD backward's dsigma_t
+// (in dsig) treats the diagonal as scaled by sigma_t; the input scale's true
+// gradient is dsigma_t - dgam_t (dgam_t = (q_t.k_t)(dy_t.x_t)), and the diagonal's
+// scale gamma_t gets dgam_t.  So with da_t = dL/da_t (in dyy),
+// dgamma_t = dsig_t and dc_t = dsig_{t-1} - dgam_{t-1} (dc_0 at t = 0):
+//   ddt = da aval + dgamma trap + dc (1 - trap),  dtrap = (dgamma - dc) dt,  daval = da dt.
+__global__ void __launch_bounds__(256) trapb_chain_kernel(SbKp p, const float *dc0, float *ddt, float *daval,
+                                                         float *dtrap) {
+    const int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (o >= p.batch * p.L * p.H) return;
+    const int64_t h = o % p.H, t = (o / p.H) % p.L, b = o / (p.H * p.L);
+    const float da = p.dyy[o];
+    const float dg = p.dsig[o];
+    const float dc = t > 0 ? p.dsig[o - p.H] - p.dgam[o - p.H] : (dc0 ? dc0[b * p.H + h] : 0.0f);
+    const float dtv = p.dt[o], tr = p.trap[o];
+    ddt[o] = fmaf(da, p.aval[o], fmaf(dg, tr, dc * (1.0f - tr)));
+    dtrap[o] = (dg - dc) * dtv;
+    daval[o] = da * dtv;
 }
 
 struct Plan { int64_t nseg, Ls; };
@@ -787,7 +904,9 @@ Plan plan(int64_t batch, int64_t L, int64_t H, int64_t N) {
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct WsLayout { size_t Sseg, Gseg, dec, bnd, dBh, dCh, dyy, dsig, dyx, hfdot, pA, pD, pT, total; };
-WsLayout layout(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t nseg) {
+// shares: each head's share of dB and dC is kept for the sum over a group's
+// heads; with one head per group the walks write dB and dC themselves
+WsLayout layout(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t nseg, bool shares) {
     WsLayout w{};
     size_t o = 0;
     const size_t seg = nseg > 1 ? (size_t)(batch * H * nseg * P * N) * 4 : 0;
@@ -795,8 +914,9 @@ WsLayout layout(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64
     w.Gseg = o; o += al256(seg);
     w.dec = o;  o += al256((size_t)(batch * H * nseg) * 4);
     w.bnd = o;  o += al256((size_t)(batch * H * nseg) * 8);
-    w.dBh = o;  o += al256((size_t)(batch * L * H * N) * 4);
-    w.dCh = o;  o += al256((size_t)(batch * L * H * N) * 4);
+    const size_t sh = shares ? (size_t)(batch * L * H * N) * 4 : 0;
+    w.dBh = o;  o += al256(sh);
+    w.dCh = o;  o += al256(sh);
     w.dyy = o;  o += al256((size_t)(batch * L * H) * 4);
     w.dsig = o; o += al256((size_t)(batch * L * H) * 4);
     w.dyx = o;  o += al256((size_t)(batch * L * H) * 4);
@@ -819,11 +939,14 @@ void launch_pn(const SbKp &p, hipStream_t s) {
         hipLaunchKernelGGL(ssdb_pass_r, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, p);
         hipLaunchKernelGGL(ssdb_bnd, dim3(bh * (unsigned)(p.nseg - 1)), dim3(kBndThreads), 0, s, p);
     }
+    // R2 first: the trapezoidal form's dq, dk corrections in F and R1 use its dy.x
+    hipLaunchKernelGGL((ssdb_walk_r2<P, N>), dim3(bh * (unsigned)p.nseg), dim3(64 * (P / 16)), 0, s, p);
     hipLaunchKernelGGL((ssdb_walk_f<P, N, false>), dim3(bh * (unsigned)p.nseg), dim3(64 * (N / 32)), 0, s, p);
     hipLaunchKernelGGL((ssdb_walk_r1<P, N, false>), dim3(bh * (unsigned)p.nseg), dim3(64 * (N / 32)), 0, s, p);
-    hipLaunchKernelGGL((ssdb_walk_r2<P, N>), dim3(bh * (unsigned)p.nseg), dim3(64 * (P / 16)), 0, s, p);
-    const int64_t nr = p.batch * p.L * p.G * p.N;
-    hipLaunchKernelGGL(ssdb_reduce_heads, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, s, p);
+    if (p.G != p.H) {
+        const int64_t nr = p.batch * p.L * p.G * p.N;
+        hipLaunchKernelGGL(ssdb_reduce_heads, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, s, p);
+    }
     hipLaunchKernelGGL(ssdb_scal, dim3((unsigned)(p.batch * p.nseg * p.H)), dim3(kScalThreads), 0, s, p);
     hipLaunchKernelGGL(ssdb_final, dim3((unsigned)((p.H + 255) / 256)), dim3(256), 0, s, p);
 }
@@ -837,13 +960,22 @@ void launch_p(const SbKp &p, hipStream_t s) {
 
 }  // namespace
 
-size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state) {
+size_t ssd_trap_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state) {
     const Plan pl = plan(batch, L, nheads, d_state);
-    return layout(batch, L, nheads, headdim, d_state, pl.nseg).total;
+    const size_t st = al256((size_t)(batch * nheads * headdim * d_state) * 4);
+    return layout(batch, L, nheads, headdim, d_state, pl.nseg, false).total + 2 * st +
+           al256((size_t)(batch * nheads) * 4) + al256((size_t)(batch * L * nheads) * 4);
 }
 
-hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t stream, const char **kernel_name) {
-    *kernel_name = "ssdb_walk_f";
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                               int64_t ngroups) {
+    const Plan pl = plan(batch, L, nheads, d_state);
+    return layout(batch, L, nheads, headdim, d_state, pl.nseg, ngroups != nheads).total;
+}
+
+namespace {
+// the parameter block and workspace views of one backward call
+SbKp make_params(const SsdBwdArgs &a) {
     SbKp p{};
     p.x = static_cast<const uint16_t *>(a.x);
     p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
@@ -857,13 +989,13 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t stream, const char **
     const Plan pl = plan(a.batch, a.L, a.nheads, a.d_state);
     p.nseg = pl.nseg;
     p.Ls = pl.Ls;
-    const WsLayout w = layout(a.batch, a.L, a.nheads, a.headdim, a.d_state, pl.nseg);
+    const WsLayout w = layout(a.batch, a.L, a.nheads, a.headdim, a.d_state, pl.nseg, a.ngroups != a.nheads);
     char *ws = static_cast<char *>(a.workspace);
     p.Sseg = reinterpret_cast<float *>(ws + w.Sseg);
     p.Gseg = reinterpret_cast<float *>(ws + w.Gseg);
     p.dec = reinterpret_cast<float *>(ws + w.dec);
-    p.dBh = reinterpret_cast<float *>(ws + w.dBh);
-    p.dCh = reinterpret_cast<float *>(ws + w.dCh);
+    p.dBh = a.ngroups == a.nheads ? a.dB : reinterpret_cast<float *>(ws + w.dBh);
+    p.dCh = a.ngroups == a.nheads ? a.dC : reinterpret_cast<float *>(ws + w.dCh);
     p.dyy = reinterpret_cast<float *>(ws + w.dyy);
     p.dsig = reinterpret_cast<float *>(ws + w.dsig);
     p.dyx = reinterpret_cast<float *>(ws + w.dyx);
@@ -872,9 +1004,57 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t stream, const char **
     p.pA = reinterpret_cast<float *>(ws + w.pA);
     p.pD = reinterpret_cast<float *>(ws + w.pD);
     p.pT = reinterpret_cast<float *>(ws + w.pT);
+    return p;
+}
+void launch_walks(const SbKp &p, hipStream_t stream) {
     if (p.P == 32) launch_p<32>(p, stream);
     else if (p.P == 64) launch_p<64>(p, stream);
     else launch_p<128>(p, stream);
+}
+}  // namespace
+
+hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t stream, const char **kernel_name) {
+    *kernel_name = "ssdb_walk_f";
+    const SbKp p = make_params(a);
+    launch_walks(p, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_ssd_trap_bwd(const SsdTrapBwdArgs &t, hipStream_t stream, const char **kernel_name) {
+    // the SSD backward of the shifted state: B = k, C = q, one group per head
+    const Plan pl = plan(t.batch, t.L, t.nheads, t.d_state);
+    char *ws = static_cast<char *>(t.workspace);
+    const size_t base = layout(t.batch, t.L, t.nheads, t.headdim, t.d_state, pl.nseg, false).total;
+    const size_t st = al256((size_t)(t.batch * t.nheads * t.headdim * t.d_state) * 4);
+    float *h0p = reinterpret_cast<float *>(ws + base);
+    float *dh0p = reinterpret_cast<float *>(ws + base + st);
+    float *dc0 = reinterpret_cast<float *>(ws + base + 2 * st);
+    float *dgam = reinterpret_cast<float *>(ws + base + 2 * st + al256((size_t)(t.batch * t.nheads) * 4));
+    const float *h0 = t.h0;
+    if (t.x_prev) {
+        *kernel_name = "ssd_trap_h0_kernel";
+        const hipError_t e = launch_ssd_trap_h0(t.x_prev, t.k_prev, t.dt, t.trap, t.h0, h0p, t.batch, t.L, t.nheads,
+                                                t.headdim, t.d_state, stream);
+        if (e != hipSuccess) return e;
+        h0 = h0p;
+    }
+    SsdBwdArgs a{t.x, t.dt, nullptr, nullptr, t.k, t.q, t.D, h0, t.dy, t.dh_final,
+                 t.dx, nullptr, t.dk, t.dq, nullptr, t.dD, nullptr, dh0p,
+                 t.batch, t.L, t.nheads, t.headdim, t.d_state, t.nheads, 0x1u, t.workspace};
+    SbKp p = make_params(a);
+    p.aval = t.a;
+    p.trap = t.trap;
+    p.dgam = dgam;
+    *kernel_name = "ssdb_walk_f";
+    launch_walks(p, stream);
+    *kernel_name = "trapb_prev_kernel";
+    hipLaunchKernelGGL(trapb_prev_kernel, dim3((unsigned)(t.batch * t.nheads)), dim3(256), 0, stream, p, dh0p,
+                       static_cast<const uint16_t *>(t.x_prev), static_cast<const uint16_t *>(t.k_prev), t.dh0,
+                       t.dx_prev, t.dk_prev, dc0);
+    *kernel_name = "trapb_chain_kernel";
+    const int64_t n = t.batch * t.L * t.nheads;
+    hipLaunchKernelGGL(trapb_chain_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p,
+                       t.x_prev ? dc0 : nullptr, t.ddt, t.da, t.dtrap);
     return hipGetLastError();
 }
 

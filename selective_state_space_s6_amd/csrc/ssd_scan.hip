@@ -757,6 +757,18 @@ hipError_t launch_ssd_trap(const SsdTrapArgs &a, hipStream_t stream, const char 
     return hipGetLastError();
 }
 
+hipError_t launch_ssd_trap_h0(const void *x_prev, const void *k_prev, const float *dt, const float *trap,
+                              const float *h0, float *h0p, int64_t batch, int64_t L, int64_t nheads,
+                              int64_t headdim, int64_t d_state, hipStream_t stream) {
+    SsdKp p{};
+    p.dt = dt; p.trap = trap; p.h0 = h0;
+    p.batch = batch; p.L = L; p.H = nheads; p.P = headdim; p.N = d_state;
+    const int64_t tot = batch * nheads * headdim * d_state;
+    hipLaunchKernelGGL(ssd_trap_h0_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, p,
+                       static_cast<const uint16_t *>(x_prev), static_cast<const uint16_t *>(k_prev), h0p);
+    return hipGetLastError();
+}
+
 hipError_t launch_ssd(const SsdArgs &a, hipStream_t stream, const char **kernel_name) {
     if (a.L == 1) return launch_ssd_step(a, stream, kernel_name);   // a decode step (ssd_decode.hip)
     *kernel_name = "ssd_scan_kernel";

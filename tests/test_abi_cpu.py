@@ -36,6 +36,9 @@ def lib():
     L.ssd_trap_rotate_qk.argtypes = [P] * 8 + [I] * 5 + [ctypes.c_int, P, Z, P]
     L.ssm_s6_fused_fwd.argtypes = [P] * 16 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P]
     L.ssm_causal_conv1d_fwd.argtypes = [P] * 6 + [I] * 4 + [ctypes.c_int, ctypes.c_int, P]
+    L.ssd_trap_chunk_scan_bwd.argtypes = [P] * 22 + [I] * 6 + [ctypes.c_int, P, Z, P]
+    L.ssd_trap_chunk_scan_bwd_workspace_size.argtypes = [I] * 6
+    L.ssd_trap_chunk_scan_bwd_workspace_size.restype = Z
     L.ssd_trap_rotate_qk_workspace_size.argtypes = [I] * 5
     L.ssd_trap_rotate_qk_workspace_size.restype = Z
     for f in ("ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_bwd_workspace_size"):
@@ -59,6 +62,7 @@ def test_every_declared_symbol_is_exported(lib):
                      "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
                      "ssd_trap_chunk_scan_fwd_workspace_size", "ssd_trap_chunk_scan_fwd",
                      "ssd_trap_rotate_qk_workspace_size", "ssd_trap_rotate_qk",
+                     "ssd_trap_chunk_scan_bwd_workspace_size", "ssd_trap_chunk_scan_bwd",
                      "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd"}
     for n in names:
         assert hasattr(lib, n), n
@@ -296,3 +300,28 @@ def test_conv1d_argument_checks(lib):
     assert _conv(lib, bias=MIS) == UNSUPPORTED and "aligned" in _err(lib)
     assert _conv(lib, y=ctypes.c_void_p(0x100000)) == INVALID and "alias" in _err(lib)            # y == x
     assert _conv(lib, state_out=ctypes.c_void_p(0x500000)) == INVALID and "alias" in _err(lib)    # == y
+
+
+def _trapb(lib, dims=(2, 300, 4, 64, 128, 64), dtype=1, ws=ctypes.c_void_p(0x9000000), wsb=1 << 40, **kw):
+    names = ["x", "k", "q", "dt", "a", "trap", "D", "h0", "k_prev", "x_prev", "dy", "dh_final",
+             "dx", "dk", "dq", "ddt", "da", "dtrap", "dD", "dh0", "dk_prev", "dx_prev"]
+    required = {"x", "k", "q", "dt", "a", "trap", "dy", "dx", "dk", "dq", "ddt", "da", "dtrap"}
+    ptrs = {n: (ctypes.c_void_p(0x100000 * (i + 1)) if n in required else None) for i, n in enumerate(names)}
+    ptrs.update(kw)
+    return lib.ssd_trap_chunk_scan_bwd(*(ptrs[n] for n in names), *dims, dtype, ws, wsb, None)
+
+
+def test_trap_bwd_argument_checks(lib):
+    assert _trapb(lib, dy=None) == INVALID and "dy is NULL" in _err(lib)
+    assert _trapb(lib, dtrap=None) == INVALID and "dtrap is NULL" in _err(lib)
+    assert _trapb(lib, dims=(2, 300, 4, 48, 128, 64)) == UNSUPPORTED and "headdim" in _err(lib)
+    assert _trapb(lib, dims=(2, 300, 4, 64, 256, 64)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _trapb(lib, dims=(2, 300, 4, 64, 128, 32)) == UNSUPPORTED and "chunk_len" in _err(lib)
+    assert _trapb(lib, dtype=0) == UNSUPPORTED and "bf16" in _err(lib)
+    assert _trapb(lib, x_prev=ctypes.c_void_p(0xA000000)) == INVALID and "together" in _err(lib)
+    assert _trapb(lib, dx=ctypes.c_void_p(0x100000)) == INVALID and "alias" in _err(lib)      # dx == x
+    assert _trapb(lib, da=MIS) == UNSUPPORTED and "aligned" in _err(lib)
+    need = lib.ssd_trap_chunk_scan_bwd_workspace_size(2, 300, 4, 64, 128, 64)
+    assert need >= 2 * 2 * 4 * 64 * 128 * 4
+    assert _trapb(lib, ws=None) == WORKSPACE
+    assert _trapb(lib, wsb=need - 1) == WORKSPACE and "workspace" in _err(lib)
