@@ -67,6 +67,7 @@ def _load():
     lib.oracle_s6_fwd.argtypes = common + [I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_ssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_cssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
+    lib.oracle_cssd_mimo_fwd.argtypes = [P] * 8 + [I] * 7 + [ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_s6_bwd.argtypes = [P] * 10 + [I, I, I, I, ctypes.c_uint32, I, I, I, I] + [P] * 8 + [ctypes.c_int]
     lib.oracle_ssd_bwd.argtypes = [P] * 10 + [I] * 6 + [ctypes.c_uint32, P, I] + [P] * 8 + [ctypes.c_int]
     lib.oracle_trap_fwd.argtypes = [P] * 10 + [I] * 5 + [P, I, P, P, ctypes.c_int]
@@ -365,6 +366,32 @@ def cssd_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_ZOH 
                             nthreads or default_threads())
     if full:
         return (y.reshape(batch, H, L, P).transpose(0, 2, 1, 3).copy(),
+                hf.reshape(batch, H, P, Nc, 2))
+    return y, hf
+
+
+def cssd_mimo_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, ngroups=1, flags=BBAR_ZOH | CPLX_STABLE,
+                  units=None, nthreads=None):
+    """Multi-input multi-output complex SSD in fp64 (rank R inputs and outputs per head
+    sharing one complex state; the stable reading of A).
+
+    x: (batch, L, R, H, P); dt: (batch, L, H); A_log: (H, 2); B, C: (batch, L, R, G, Nc, 2);
+    h0: (batch, H, P, Nc, 2).  Returns y (batch, L, R, H, P) and h_final (batch, H, P, Nc, 2),
+    or per-unit (n_units, L, R, P) / (n_units, P, Nc, 2) with (b, h) units."""
+    x, dt, dt_bias, A_log, B, C, D, h0 = map(_f32, (x, dt, dt_bias, A_log, B, C, D, h0))
+    batch, L, R, H, P = x.shape
+    G, Nc = B.shape[3], B.shape[4]
+    assert G == ngroups and B.shape[:3] == (batch, L, R) and B.shape[5] == 2
+    assert (flags & (CPLX_DOC | CPLX_CODE)) == CPLX_STABLE, "the MIMO form takes the stable reading of A"
+    uu, full = _units(units, batch, H)
+    nu = uu.shape[0]
+    y = np.empty((nu, L, R, P), np.float64)
+    hf = np.empty((nu, P, Nc, 2), np.float64)
+    _load().oracle_cssd_mimo_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                 _ptr(h0), batch, L, R, H, P, Nc, G, flags, _ptr(uu), nu, _ptr(y), _ptr(hf),
+                                 nthreads or default_threads())
+    if full:
+        return (y.reshape(batch, H, L, R, P).transpose(0, 2, 3, 1, 4).copy(),
                 hf.reshape(batch, H, P, Nc, 2))
     return y, hf
 

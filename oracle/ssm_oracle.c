@@ -296,6 +296,95 @@ static void cssd_unit(const cssd_job *j, int64_t k)
     free(S);
 }
 
+/* ------------------------------------------------- complex MIMO SSD --- */
+/*
+ * The multi-input multi-output form of the complex SSD (builderforce-memory-
+ * engine mamba3_block.ts, module header item 2 and the in_proj widths: each
+ * head takes R input vectors x^r_t and gives R outputs y^r_t, with B^r_t, C^r_t
+ * of Nc complex entries per rank index r).  Per (b, head), with the decay and
+ * the input scale of the complex SSD above:
+ *   S_t   = Abar_t S_{t-1} + beta_t sum_r (B^r_t x^r_t^T)
+ *   y^r_t = Re(C^r_t . S_t) + D x^r_t
+ * All R inputs of step t enter S_t before any output of step t is read.
+ * Layouts: x, y (batch, L, R, H, P); B, C (batch, L, R, G, Nc, 2); dt (batch, L, H).
+ */
+typedef struct {
+    const float *x, *dt, *dt_bias, *A_log, *B, *C, *D, *h0;
+    int64_t batch, L, R, H, P, Nc, G;
+    uint32_t flags;
+    const int64_t *units;
+    int64_t n_units;
+    double *y_out;          /* [n_units][L][R][P] */
+    double *hf_out;         /* [n_units][P][Nc][2] or NULL */
+} mimo_job;
+
+static void mimo_unit(const mimo_job *j, int64_t k)
+{
+    const int64_t b = j->units[2 * k], hh = j->units[2 * k + 1];
+    const int64_t L = j->L, R = j->R, H = j->H, P = j->P, Nc = j->Nc, G = j->G;
+    const int64_t g = hh * G / H;
+    const int bmode = (int)(j->flags & OR_BBAR_MASK);
+    const int conj_c = (j->flags & OR_CPLX_CONJ_C) != 0;
+    const double ell = (double)j->A_log[2 * hh], phi = (double)j->A_log[2 * hh + 1];
+    const double bias = j->dt_bias ? (double)j->dt_bias[hh] : 0.0;
+    const double Dh = j->D ? (double)j->D[hh] : 0.0;
+    const cplx lam = {-exp(ell), phi};               /* the stable reading of A */
+    cplx *S = (cplx *)malloc(sizeof(cplx) * (size_t)(P * Nc));
+    for (int64_t i = 0; i < P * Nc; ++i) {
+        if (j->h0) {
+            S[i].re = (double)j->h0[((b * H + hh) * P * Nc + i) * 2];
+            S[i].im = (double)j->h0[((b * H + hh) * P * Nc + i) * 2 + 1];
+        } else { S[i].re = 0.0; S[i].im = 0.0; }
+    }
+    #define MI_X(t, r) (j->x + (((b * L + (t)) * R + (r)) * H + hh) * P)
+    #define MI_BC(T, t, r) (j->T + (((b * L + (t)) * R + (r)) * G + g) * Nc * 2)
+    for (int64_t t = 0; t < L; ++t) {
+        const double delta = sp((double)j->dt[(b * L + t) * H + hh] + bias);
+        const cplx w = {delta * lam.re, delta * lam.im};
+        const cplx abar = cexp_(w);
+        cplx beta;
+        if (bmode == OR_BBAR_ZOH) { cplx f = cphi1(w); beta.re = delta * f.re; beta.im = delta * f.im; }
+        else if (bmode == OR_BBAR_DT) { beta.re = delta; beta.im = 0.0; }
+        else { beta.re = 1.0; beta.im = 0.0; }
+        /* the state update: decay, then every rank's input */
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < Nc; ++n) {
+                cplx hn = cmul(abar, S[p * Nc + n]);
+                for (int64_t r = 0; r < R; ++r) {
+                    const float *Bt = MI_BC(B, t, r);
+                    const cplx Bn = {(double)Bt[2 * n], (double)Bt[2 * n + 1]};
+                    const cplx inp = cmul(beta, Bn);
+                    const double xv = (double)MI_X(t, r)[p];
+                    hn.re += inp.re * xv;
+                    hn.im += inp.im * xv;
+                }
+                S[p * Nc + n] = hn;
+            }
+        /* the outputs of every rank from the updated state */
+        for (int64_t r = 0; r < R; ++r) {
+            const float *Ct = MI_BC(C, t, r);
+            double *yt = j->y_out + ((k * L + t) * R + r) * P;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < Nc; ++n) {
+                    const double cr = (double)Ct[2 * n], ci = (double)Ct[2 * n + 1];
+                    const cplx hn = S[p * Nc + n];
+                    acc += conj_c ? (cr * hn.re + ci * hn.im) : (cr * hn.re - ci * hn.im);
+                }
+                yt[p] = acc + Dh * (double)MI_X(t, r)[p];
+            }
+        }
+    }
+    #undef MI_X
+    #undef MI_BC
+    if (j->hf_out)
+        for (int64_t i = 0; i < P * Nc; ++i) {
+            j->hf_out[(k * P * Nc + i) * 2] = S[i].re;
+            j->hf_out[(k * P * Nc + i) * 2 + 1] = S[i].im;
+        }
+    free(S);
+}
+
 /* ------------------------------------------------------------ threads --- */
 
 typedef struct {
@@ -643,7 +732,8 @@ static void *worker(void *p)
         else if (w->kind == 2) cssd_unit((const cssd_job *)w->job, k);
         else if (w->kind == 3) ssdb_unit((const ssdb_job *)w->job, k);
         else if (w->kind == 4) trap_unit((const trap_job *)w->job, k);
-        else trapb_unit((const trapb_job *)w->job, k);
+        else if (w->kind == 5) trapb_unit((const trapb_job *)w->job, k);
+        else mimo_unit((const mimo_job *)w->job, k);
     }
     return NULL;
 }
@@ -720,6 +810,17 @@ void oracle_cssd_fwd(const float *x, const float *dt, const float *dt_bias, cons
     cssd_job j = {x, dt, dt_bias, A_log, B, C, D, h0, batch, L, nheads, headdim, n_complex, ngroups,
                   flags, units, n_units, y_out, hf_out};
     run_units(2, &j, n_units, nthreads);
+}
+
+void oracle_cssd_mimo_fwd(const float *x, const float *dt, const float *dt_bias, const float *A_log,
+                          const float *B, const float *C, const float *D, const float *h0,
+                          int64_t batch, int64_t L, int64_t rank, int64_t nheads, int64_t headdim,
+                          int64_t n_complex, int64_t ngroups, uint32_t flags, const int64_t *units,
+                          int64_t n_units, double *y_out, double *hf_out, int nthreads)
+{
+    mimo_job j = {x, dt, dt_bias, A_log, B, C, D, h0, batch, L, rank, nheads, headdim, n_complex, ngroups,
+                  flags, units, n_units, y_out, hf_out};
+    run_units(6, &j, n_units, nthreads);
 }
 
 /* ------------------------------------------------------- S6 backward --- */

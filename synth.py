@@ -53,6 +53,9 @@ WORKLOADS = {
     # complex-state SSD: 4 x 8192, 32 heads x 64, 32 complex states, Q=64, fp32
     "cssd_mamba3": dict(kind="cssd", batch=4, L=8192, nheads=32, headdim=64, n_complex=32,
                         ngroups=1, chunk_len=64, dtype="f32"),
+    # its multi-input multi-output form: rank 4 (4 inputs and outputs per head and step)
+    "cssd_mimo_mamba3": dict(kind="cssd_mimo", batch=4, L=4096, rank=4, nheads=32, headdim=64,
+                             n_complex=32, ngroups=1, chunk_len=64, dtype="f32"),
 }
 
 
@@ -235,6 +238,26 @@ def cssd_inputs(batch, L, nheads, headdim, n_complex, ngroups, *, seed=(0,), h0=
                   dict(x=x, dt=dt, dt_bias=bias, A_log=A_log, B=B, C=C, D=Dv, h0=h0a), ())
 
 
+def mimo_inputs(batch, L, rank, nheads, headdim, n_complex, ngroups=1, *, seed=(0,), h0=False) -> Inputs:
+    """Multi-input multi-output complex SSD inputs: the complex SSD recipe with a rank
+    axis on x (batch, L, rank, nheads, headdim) and on B, C (batch, L, rank, ngroups,
+    n_complex, 2); B, C entries N(0, 1/2) per part, so |B_n|^2 has mean 1."""
+    key = (11, *seed)
+    x = _normal(_rng(key, 0), (batch, L, rank, nheads, headdim))
+    dt = _normal(_rng(key, 1), (batch, L, nheads), -3.0, 0.5)
+    sd = np.float32(math.sqrt(0.5))
+    B = _normal(_rng(key, 2), (batch, L, rank, ngroups, n_complex, 2), 0.0, sd)
+    C = _normal(_rng(key, 3), (batch, L, rank, ngroups, n_complex, 2), 0.0, sd)
+    bias = _uniform(_rng(key, 4), (nheads,), -1.0, 0.0)
+    A_log = np.stack([_uniform(_rng(key, 5), (nheads,), -2.0, 1.0),
+                      _uniform(_rng(key, 6), (nheads,), -math.pi, math.pi)], axis=1).astype(np.float32)
+    Dv = np.ones((nheads,), np.float32)
+    h0a = _normal(_rng(key, 7), (batch, nheads, headdim, n_complex, 2), 0.0, sd) if h0 else None
+    return Inputs("cssd_mimo", dict(batch=batch, L=L, rank=rank, nheads=nheads, headdim=headdim,
+                                    n_complex=n_complex, ngroups=ngroups),
+                  dict(x=x, dt=dt, dt_bias=bias, A_log=A_log, B=B, C=C, D=Dv, h0=h0a), ())
+
+
 def trap_inputs(batch, L, nheads, headdim, d_state, *, seed=(0,), h0=False, prev=False,
                 D="normal", trap="uniform") -> Inputs:
     """Mamba-3 trapezoidal inputs: dt log-uniform on [1e-3, 1e-1] (a positive step, as
@@ -288,6 +311,9 @@ def workload_inputs(name: str, seed=(0,)) -> Inputs:
         carry = w.get("carry", False)
         return trap_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"], seed=seed,
                            h0=carry, prev=carry)
+    if kind == "cssd_mimo":
+        return mimo_inputs(w["batch"], w["L"], w["rank"], w["nheads"], w["headdim"], w["n_complex"],
+                           w["ngroups"], seed=seed)
     return cssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["n_complex"],
                        w["ngroups"], seed=seed)
 
