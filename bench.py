@@ -24,6 +24,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6   # dense bf16 MFMA (no sparsity), TFLOP/s
 FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 MFMA
+# the roof of each chunked path, priced at the dtype its contractions run in
+MFMA_PEAKS = {
+    "ssd": (BF16_MFMA_PEAK_TFLOPS, "dense bf16 MFMA (model flops of the chunked decomposition)"),
+    "trap": (BF16_MFMA_PEAK_TFLOPS, "dense bf16 MFMA (model flops of the chunked decomposition)"),
+    "cssd": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (model flops of the complex chunked decomposition)"),
+    "cssd_mimo": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (the complex model over L x rank rows)"),
+    "ssd_bwd": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (executed 16x16x4 MFMAs of the walks)"),
+    "trap_bwd": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (executed 16x16x4 MFMAs of the walks)"),
+}
 FP32_VALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, non-packed fp32
 # fp32 VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz lane-slots/s (a wave64 op takes 4 cycles)
 VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
@@ -144,6 +153,16 @@ def cssd_model(d):
     bytes_ = elems * 4 * 2 + 2 * B * L * G * Nc * 8 + B * L * H * 4 + B * H * P * Nc * 8
     nc = -(-L // Q)
     flops = 2 * B * nc * H * (4 * Q * Q * Nc + Q * Q * P + 2 * 4 * Q * P * Nc)
+    return elems, bytes_, flops
+
+
+def mimo_model(d):
+    """The complex SSD's model over L x rank rows (every row is an input and an output row);
+    elems counts output values, batch * L * rank * H * P."""
+    R = d["rank"]
+    dd = dict(d, L=d["L"] * R)
+    elems, bytes_, flops = cssd_model(dd)
+    bytes_ -= (R - 1) * d["batch"] * d["L"] * d["nheads"] * 4      # dt is read once per step
     return elems, bytes_, flops
 
 
@@ -331,6 +350,16 @@ def make_runner(name, dev):
     y = torch.empty(t0["x"].shape, dtype=torch.float32, device=dev)
     hf = torch.empty((dims["batch"], dims["nheads"], dims["headdim"], dims["n_complex"], 2),
                      dtype=torch.float32, device=dev)
+    if kind == "cssd_mimo":
+        ws = torch.empty(lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size(
+            dims["batch"], dims["L"], dims["rank"], dims["nheads"], dims["headdim"], dims["n_complex"],
+            dims["ngroups"], w["chunk_len"]), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            lib.ssd_cplx_mimo_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                             None, chunk_len=w["chunk_len"], y=y, h_final=hf, workspace=ws)
+        return step, dims, w, ["cssd_state_kernel", "cssd_pass_kernel", "cssd_scan_kernel"]
     ws = torch.empty(lib.ssd_cplx_chunk_scan_fwd_workspace_size(
         dims["batch"], dims["L"], dims["nheads"], dims["headdim"], dims["n_complex"],
         dims["ngroups"], w["chunk_len"]), dtype=torch.uint8, device=dev)
@@ -509,11 +538,13 @@ def cpu_baseline_units(name, n_units):
     t0 = time.perf_counter()
     if w["kind"] == "trap":
         oracle.trap_fwd(**inp.arrays, units=units, nthreads=nthr)
+    elif w["kind"] == "cssd_mimo":
+        oracle.cssd_mimo_fwd(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
     else:
         fn = oracle.ssd_fwd if w["kind"] == "ssd" else oracle.cssd_fwd
         fn(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
     sec = time.perf_counter() - t0
-    elems = n_units * d["L"] * d["headdim"]
+    elems = n_units * d["L"] * d.get("rank", 1) * d["headdim"]
     return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
             "sample": f"{n_units} of {d['batch'] * d['nheads']} (b, head) units of {name} "
                       f"({elems} elements, {sec:.2f} s wall)"}
@@ -564,6 +595,8 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = trap_rot_model(dims)
     elif kind == "conv":
         elems, bytes_, ops = conv_model(dims)
+    elif kind == "cssd_mimo":
+        elems, bytes_, ops = mimo_model(dims)
     else:
         elems, bytes_, ops = cssd_model(dims)
     ev_ms = sorted(per)[len(per) // 2]
@@ -604,6 +637,14 @@ def main():
                 "kernel": "s6_scan_kernel", "kernel_ms": round(m["event_ms_median"], 5),
                 "fma_peak": FP32_VALU_PEAK_TFLOPS, "fma_frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
                 "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    elif kind in MFMA_PEAKS and m["dims"]["L"] > 1:
+        # the chunked paths are contractions on the matrix cores (executed flops of the model)
+        tf = m["ops"] / ev_s / 1e12
+        pk, basis = MFMA_PEAKS[kind]
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": pk, "unit": "TFLOP/s",
+                "frac": round(tf / pk, 4), "traffic": None, "peak_basis": basis,
+                "kernel": "+".join(m["kernels"]), "kernel_ms": round(m["event_ms_median"], 5),
+                "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
@@ -627,7 +668,7 @@ def main():
     }
     if not args.no_secondary and args.workload == "s6_mamba1":
         sec = []
-        for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5),
+        for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5), ("cssd_mimo_mamba3", 5),
                             ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
                             ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
                             ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5)):
@@ -651,6 +692,9 @@ def main():
                 ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
                 ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
                 ent["kernel_ms"] = round(s["event_ms_median"], 4)
+            elif s["kind"] in ("cssd", "cssd_mimo"):
+                ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
+                ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
             elif s["kind"] in ("ssd", "trap") and s["dims"]["L"] == 1:
                 ent["us_per_step_eager"] = round(s["event_ms_median"] * 1e3, 2)
                 ent["us_per_step_graph"] = round(s["graph_us"], 2)

@@ -31,6 +31,9 @@
  *             conv1d_forward)
  *   [BF-CSSD] same package, package/src/kernels/complex_ssd.ts (header
  *             comment, et_bbar_re/et_bbar_im, complex_ssd_forward)
+ *   [BF-M3]   same package, package/src/model/mamba3_block.ts (module header
+ *             item 2, the weight shapes, Mamba3BlockConfig.mimoGroup), and
+ *             complex_ssd.ts header item 3
  *   [RS-M1]   mamba-rs 0.4.0, src/mamba_ssm/gpu/forward.rs
  *             (gpu_forward_mamba_layer, steps F4a, F4d and F4e, and GpuMambaDims)
  *   [RS-M3]   mamba-rs 0.2.1, src/mamba3_siso/gpu/mamba3_gpu.rs
@@ -425,6 +428,37 @@ int ssd_cplx_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bia
                             int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                             int64_t n_complex, int64_t ngroups, int64_t chunk_len, uint32_t flags,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------ complex SSD, multi-input multi-output ----
+ * The MIMO form of the complex SSD [BF-M3]: per head, R = rank input vectors
+ * and R outputs per step share one complex state (G x G blocks per head, with
+ * B and C widened to R sets of n_complex entries).  The pages describe it and
+ * leave it unimplemented; read as:
+ *   h_t[p,n]     = Abar_t * h_{t-1}[p,n] + beta_t * sum_r B[b,t,r,g,n] * x[b,t,r,h,p]
+ *   y[b,t,r,h,p] = Re(sum_n C[b,t,r,g,n] * h_t[p,n]) + D[h] * x[b,t,r,h,p]
+ * with Abar, beta, lambda as for ssd_cplx_chunk_scan_fwd (stable reading of A
+ * only).  Every input of step t enters h_t before any output of step t is
+ * read.  rank 1 is ssd_cplx_chunk_scan_fwd.
+ *
+ * Layouts (all fp32): x, y (batch, L, rank, nheads, headdim); dt (batch, L,
+ * nheads); dt_bias, D (nheads); A_log (nheads, 2); B, C (batch, L, rank,
+ * ngroups, n_complex, 2) interleaved (re, im); h0, h_final (batch, nheads,
+ * headdim, n_complex, 2).
+ * flags: SSM_BBAR_* and SSM_CPLX_CONJ_C (SSM_CPLX_DOC / SSM_CPLX_CODE are
+ * rejected).  Limits: rank in {1, 2, 4, 8, 16}; otherwise as for
+ * ssd_cplx_chunk_scan_fwd, with L x rank in place of L.
+ * Workspace: ssd_cplx_mimo_chunk_scan_fwd_workspace_size() bytes, as for
+ * ssd_cplx_chunk_scan_fwd over L x rank rows (0 for one segment). */
+size_t ssd_cplx_mimo_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t rank, int64_t nheads,
+                                                   int64_t headdim, int64_t n_complex, int64_t ngroups,
+                                                   int64_t chunk_len);
+
+int ssd_cplx_mimo_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bias,
+                                 const float *A_log, const float *B, const float *C, const float *D,
+                                 float *y, const float *h0, float *h_final,
+                                 int64_t batch, int64_t L, int64_t rank, int64_t nheads, int64_t headdim,
+                                 int64_t n_complex, int64_t ngroups, int64_t chunk_len, uint32_t flags,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,8 @@ __all__ = [
     "ssd_trap_rotate_qk", "ssd_trap_rotate_qk_workspace_size", "ssd_trap_chunk_scan_bwd",
     "ssd_trap_chunk_scan_bwd_workspace_size",
     "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
-    "ssd_cplx_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
+    "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_mimo_chunk_scan_fwd",
+    "ssd_cplx_mimo_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
     "SSM_BBAR_ZOH", "SSM_BBAR_DT", "SSM_BBAR_ONE", "SSM_CPLX_STABLE", "SSM_CPLX_DOC",
     "SSM_CPLX_CODE", "SSM_CPLX_CONJ_C", "SSM_F32", "SSM_BF16",
 ]
@@ -77,6 +78,10 @@ _lib.ssd_cplx_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_cplx_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_cplx_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_uint32, _P, _Z, _P]
 _lib.ssd_cplx_chunk_scan_fwd.restype = ctypes.c_int
+_lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size.argtypes = [_I] * 8
+_lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size.restype = _Z
+_lib.ssd_cplx_mimo_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 8 + [ctypes.c_uint32, _P, _Z, _P]
+_lib.ssd_cplx_mimo_chunk_scan_fwd.restype = ctypes.c_int
 
 
 class SsmError(RuntimeError):
@@ -541,5 +546,46 @@ def ssd_cplx_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_le
                                       _ptr(C), _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L,
                                       H, P, Nc, G, chunk_len, flags, _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ssd_cplx_mimo_chunk_scan_fwd_workspace_size(batch, L, rank, nheads, headdim, n_complex, ngroups,
+                                                chunk_len) -> int:
+    return int(_lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size(batch, L, rank, nheads, headdim, n_complex,
+                                                                ngroups, chunk_len))
+
+
+def ssd_cplx_mimo_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=64,
+                                 flags=SSM_BBAR_ZOH | SSM_CPLX_STABLE, return_final=False, y=None,
+                                 h_final=None, workspace=None):
+    """Multi-input multi-output complex SSD forward scan.  x (batch, L, R, H, P) fp32;
+    dt (batch, L, H); A_log (H, 2); B, C (batch, L, R, G, Nc, 2) fp32 interleaved (re, im);
+    h0 (batch, H, P, Nc, 2) or None.  Returns y (batch, L, R, H, P) (and h_final)."""
+    dev = x.device
+    batch, L, R, H, P = x.shape
+    G, Nc = B.shape[3], B.shape[4]
+    f32 = torch.float32
+    _req(x, "x", f32, (batch, L, R, H, P), dev)
+    _req(dt, "dt", f32, (batch, L, H), dev)
+    _opt(dt_bias, "dt_bias", f32, (H,), dev)
+    _req(A_log, "A_log", f32, (H, 2), dev)
+    _req(B, "B", f32, (batch, L, R, G, Nc, 2), dev)
+    _req(C, "C", f32, (batch, L, R, G, Nc, 2), dev)
+    _opt(D, "D", f32, (H,), dev)
+    _opt(h0, "h0", f32, (batch, H, P, Nc, 2), dev)
+    if y is None:
+        y = torch.empty((batch, L, R, H, P), dtype=f32, device=dev)
+    _req(y, "y", f32, (batch, L, R, H, P), dev)
+    if return_final and h_final is None:
+        h_final = torch.empty((batch, H, P, Nc, 2), dtype=f32, device=dev)
+    _opt(h_final, "h_final", f32, (batch, H, P, Nc, 2), dev)
+    ws = ssd_cplx_mimo_chunk_scan_fwd_workspace_size(batch, L, R, H, P, Nc, G, chunk_len)
+    if workspace is None:
+        workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+    rc = _lib.ssd_cplx_mimo_chunk_scan_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B),
+                                           _ptr(C), _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L,
+                                           R, H, P, Nc, G, chunk_len, flags, _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y

@@ -549,4 +549,55 @@ int ssd_cplx_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bia
     return launched(E, ssm::launch_cssd(a, stream, &kn), kn);
 }
 
+size_t ssd_cplx_mimo_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t rank, int64_t nheads,
+                                                   int64_t headdim, int64_t n_complex, int64_t ngroups,
+                                                   int64_t chunk_len) {
+    (void)ngroups;
+    if (batch <= 0 || L <= 0 || rank <= 0 || nheads <= 0 || headdim <= 0 || n_complex <= 0 || chunk_len <= 0)
+        return 0;
+    return ssm::cssd_workspace_bytes(batch, L * rank, nheads, headdim, n_complex, chunk_len);
+}
+
+int ssd_cplx_mimo_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bias,
+                                 const float *A_log, const float *B, const float *C, const float *D,
+                                 float *y, const float *h0, float *h_final,
+                                 int64_t batch, int64_t L, int64_t rank, int64_t nheads, int64_t headdim,
+                                 int64_t n_complex, int64_t ngroups, int64_t chunk_len, uint32_t flags,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssd_cplx_mimo_chunk_scan_fwd";
+    REQUIRE_PTR(E, x); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
+    REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
+    if (!(rank == 1 || rank == 2 || rank == 4 || rank == 8 || rank == 16))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: rank %lld not in {1, 2, 4, 8, 16}", E, (long long)rank);
+    REQUIRE_POS(E, L);
+    if (L > (int64_t(1) << 40) / rank)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: L x rank too large", E);
+    int rc = ssd_check_shape(E, batch, L * rank, nheads, headdim, n_complex, ngroups, chunk_len);   // rows
+    if (rc != SSM_OK) return rc;
+    if ((flags & ~0x13u) != 0 || (flags & 0x3u) == 0x3u)
+        return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x not a valid combination (stable reading of A only)", E,
+                    flags);
+    if (!(headdim == 32 || headdim == 64 || headdim == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: headdim %lld not in {32, 64, 128}", E, (long long)headdim);
+    if (n_complex % 8 != 0 || n_complex > 64)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: n_complex %lld must be a multiple of 8 and <= 64", E,
+                    (long long)n_complex);
+    if (!(chunk_len == 32 || chunk_len == 64 || chunk_len == 128))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: chunk_len %lld not in {32, 64, 128}", E, (long long)chunk_len);
+    REQUIRE_ALIGN(E, x); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
+    REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
+    REQUIRE_ALIGN(E, h0); REQUIRE_ALIGN(E, h_final); REQUIRE_ALIGN(E, workspace);
+    if ((const void *)y == (const void *)x || (const void *)y == (const void *)dt ||
+        (const void *)y == (const void *)B || (const void *)y == (const void *)C)
+        return fail(SSM_ERR_INVALID_ARG, "%s: y aliases an input", E);
+    const size_t need = ssm::cssd_workspace_bytes(batch, L * rank, nheads, headdim, n_complex, chunk_len);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    ssm::CssdArgs a{x, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, nheads, headdim,
+                    n_complex, ngroups, chunk_len, flags, workspace, rank};
+    const char *kn = "cssd";
+    return launched(E, ssm::launch_cssd(a, stream, &kn), kn);
+}
+
 }  // extern "C"

@@ -15,6 +15,11 @@
 // Every decay is taken between two steps of one chunk (or from its start), so
 // for the stable reading of A no exponent is positive.
 //
+// The multi-input multi-output form (builderforce-memory-engine mamba3_block.ts,
+// module header item 2: R inputs and outputs per head and step sharing the
+// state) runs through the same kernels: a step's R rows of x, y, B, C are
+// consecutive and the kernels walk rows (see CssdKp::lgR).
+//
 // Layout of the work: as for the real SSD, the sequence of every (batch, head)
 // is cut into segments (cssd_state_kernel: segment-local states and decays;
 // cssd_pass_kernel: entering states; cssd_scan_kernel: outputs), and a work
@@ -74,6 +79,13 @@ struct CssdKp {
     int64_t batch, L, H, P, Nc, G;
     int64_t Ls, nseg;   // segment length (a multiple of kT) and count
     uint32_t flags;
+    // Multi-input multi-output form: R = 2^lgR inputs and outputs per head and
+    // step, laid out as R consecutive rows of x, y, B, C per step.  The kernels
+    // walk those rows as steps (L above counts them: L = R x steps); a row takes
+    // dt of its step, the decay enters at the first row of a step only, every
+    // row of a step has the step's input scale, and the causal mask compares
+    // steps, so each output row of a step sees every input row of that step.
+    int lgR;
 };
 
 // mu (the per-unit-delta complex rate) of head h for the selected reading
@@ -118,7 +130,7 @@ __device__ __forceinline__ void chunk_scalars(CScal &sc, const CssdKp &p, cf mu,
         dl = xv > 0.0 ? xv + log1p(exp(-xv)) : log1p(exp(xv));   // softplus
         be = input_scale(p, mu, (float)dl);
     }
-    double v = dl;
+    double v = (lane & ((1 << p.lgR) - 1)) == 0 ? dl : 0.0;   // the decay: once per step
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) {
         const double o = __shfl_up(v, off, 32);
@@ -169,7 +181,7 @@ struct Stager {
     int rBC[PBC], rXr[PX];       // per-piece rows
     int lBC[PBC], lX[PX];        // per-piece LDS offsets
     bool vBC[PBC];
-    int sD;
+    int sD, lgR;
     int64_t rowBC, rowX, H, L;
 
     __device__ __forceinline__ void init(const CssdKp &p, int64_t b, int64_t h, int64_t g, int tid) {
@@ -200,11 +212,12 @@ struct Stager {
         Bb = p.B + (b * p.L * p.G + g) * p.Nc * 2;
         Cb = p.C + (b * p.L * p.G + g) * p.Nc * 2;
         Xb = p.x + (b * p.L * p.H + h) * p.P;
-        Db = p.dt + b * p.L * p.H + h;
+        Db = p.dt + b * (p.L >> p.lgR) * p.H + h;
+        lgR = p.lgR;
     }
     __device__ __forceinline__ void load(int64_t t0) {
         const float *Bu = Bb + t0 * rowBC, *Cu = Cb + t0 * rowBC, *Xu = Xb + t0 * rowX;
-        const float *Du = Db + t0 * H;
+        const float *Du = Db + (t0 >> lgR) * H;     // t0 is a multiple of kT, so of R
         if (t0 + kT <= L) {
 #pragma unroll
             for (int i = 0; i < PBC; ++i) {
@@ -213,7 +226,7 @@ struct Stager {
             }
 #pragma unroll
             for (int i = 0; i < PX; ++i) rX[i] = *reinterpret_cast<const float4 *>(Xu + oX[i]);
-            rdt = Du[(uint32_t)(sD * H)];
+            rdt = Du[(uint32_t)((sD >> lgR) * H)];
         } else {
             const int last = (int)(L - 1 - t0);   // last valid step of the chunk
 #pragma unroll
@@ -227,7 +240,7 @@ struct Stager {
                 const uint32_t o = oX[i] - (uint32_t)((rXr[i] - min(rXr[i], last)) * rowX);
                 rX[i] = *reinterpret_cast<const float4 *>(Xu + o);
             }
-            rdt = Du[(uint32_t)(min(sD, last) * H)];
+            rdt = Du[(uint32_t)((min(sD, last) >> lgR) * H)];
         }
     }
     __device__ __forceinline__ void store(float *Bs, float *Cs, float *Xs) {
@@ -491,7 +504,7 @@ cssd_scan_kernel(CssdKp p) {
             for (int v = 0; v < 4; ++v) {
                 const int s = sT * 16 + 4 * q + v;
                 float m = 0.0f;
-                if (s <= t) {
+                if ((s >> p.lgR) <= (t >> p.lgR)) {      // causal over steps
                     const float dl = (float)(lt - sc.lam[s]);
                     const float2 bs = sc.bet[s];
                     const cf f = cmul(cexpf_(mu.re * dl, mu.im * dl), cf{bs.x, bs.y});
@@ -635,8 +648,10 @@ hipError_t launch_cssd(const CssdArgs &a, hipStream_t stream, const char **kerne
     CssdKp p{};
     p.x = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log; p.B = a.B; p.C = a.C;
     p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
-    p.batch = a.batch; p.L = a.L; p.H = a.nheads; p.P = a.headdim; p.Nc = a.n_complex; p.G = a.ngroups;
+    p.batch = a.batch; p.L = a.L * a.rank; p.H = a.nheads; p.P = a.headdim; p.Nc = a.n_complex; p.G = a.ngroups;
     p.flags = a.flags;
+    p.lgR = 0;
+    while ((int64_t(1) << p.lgR) < a.rank) ++p.lgR;
     const Plan pl = plan(p.batch, p.L, p.H, p.P);
     p.nseg = pl.nseg;
     p.Ls = pl.Ls;

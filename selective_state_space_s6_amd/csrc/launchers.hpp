@@ -121,7 +121,9 @@ struct CssdArgs {
     int64_t batch, L, nheads, headdim, n_complex, ngroups, chunk_len;
     uint32_t flags;
     void *workspace;
+    int64_t rank = 1;   // multi-input multi-output rank (a power of two, at most 16)
 };
+// L counts steps x rank for the multi-input multi-output form
 size_t cssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                             int64_t n_complex, int64_t chunk_len);
 hipError_t launch_cssd(const CssdArgs &a, hipStream_t stream, const char **kernel_name);

@@ -28,6 +28,9 @@ def lib():
     L.ssm_s6_scan_fwd.argtypes = [P] * 10 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_cplx_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_uint32, P, Z, P]
+    L.ssd_cplx_mimo_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 8 + [ctypes.c_uint32, P, Z, P]
+    L.ssd_cplx_mimo_chunk_scan_fwd_workspace_size.argtypes = [I] * 8
+    L.ssd_cplx_mimo_chunk_scan_fwd_workspace_size.restype = Z
     L.ssm_s6_scan_bwd.argtypes = [P] * 18 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_chunk_scan_bwd.argtypes = [P] * 18 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_trap_chunk_scan_fwd.argtypes = [P] * 12 + [I] * 6 + [ctypes.c_int, P, Z, P]
@@ -63,7 +66,8 @@ def test_every_declared_symbol_is_exported(lib):
                      "ssd_trap_chunk_scan_fwd_workspace_size", "ssd_trap_chunk_scan_fwd",
                      "ssd_trap_rotate_qk_workspace_size", "ssd_trap_rotate_qk",
                      "ssd_trap_chunk_scan_bwd_workspace_size", "ssd_trap_chunk_scan_bwd",
-                     "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd"}
+                     "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_chunk_scan_fwd",
+                     "ssd_cplx_mimo_chunk_scan_fwd_workspace_size", "ssd_cplx_mimo_chunk_scan_fwd"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -196,6 +200,34 @@ def test_cssd_argument_checks(lib):
     assert lib.ssd_cplx_chunk_scan_fwd_workspace_size(2, 100, 4, 64, 32, 2, 64) == 0
     assert _cssd(lib, dims=long_dims, ws=None) == WORKSPACE
     assert _cssd(lib, dims=long_dims, wsb=need - 1) == WORKSPACE
+
+
+def _mimo(lib, dims=(2, 100, 4, 4, 64, 32, 2, 64), flags=0, ws=FAKE, wsb=1 << 40):
+    return lib.ssd_cplx_mimo_chunk_scan_fwd(FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
+                                            ctypes.c_void_p(0x200000), None, None, *dims, flags, ws, wsb,
+                                            None)
+
+
+def test_cssd_mimo_argument_checks(lib):
+    # every case below fails before any launch (the pointers are fake)
+    assert _mimo(lib, dims=(2, 100, 3, 4, 64, 32, 2, 64)) == UNSUPPORTED and "rank" in _err(lib)
+    assert _mimo(lib, dims=(2, 100, 32, 4, 64, 32, 2, 64)) == UNSUPPORTED and "rank" in _err(lib)
+    assert _mimo(lib, dims=(2, 100, 0, 4, 64, 32, 2, 64)) == UNSUPPORTED
+    assert _mimo(lib, dims=(2, 100, 4, 4, 64, 32, 3, 64)) == INVALID
+    assert _mimo(lib, dims=(2, 100, 4, 4, 40, 32, 2, 64)) == UNSUPPORTED and "headdim" in _err(lib)
+    assert _mimo(lib, dims=(2, 100, 4, 4, 64, 30, 2, 64)) == UNSUPPORTED and "n_complex" in _err(lib)
+    assert _mimo(lib, dims=(2, 100, 4, 4, 64, 32, 2, 256)) == UNSUPPORTED and "chunk_len" in _err(lib)
+    assert _mimo(lib, dims=(2, 0, 4, 4, 64, 32, 2, 64)) == INVALID
+    assert _mimo(lib, flags=0x4) == INVALID and "stable" in _err(lib)
+    assert _mimo(lib, flags=0x8) == INVALID
+    assert _mimo(lib, flags=0x3) == INVALID
+    # the workspace covers L x rank rows: the complex SSD's over that length
+    dims = (4, 2048, 4, 32, 64, 32, 1, 64)
+    need = lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size(*dims)
+    assert need == lib.ssd_cplx_chunk_scan_fwd_workspace_size(4, 8192, 32, 64, 32, 1, 64) > 0
+    assert lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size(2, 25, 4, 4, 64, 32, 2, 64) == 0
+    assert _mimo(lib, dims=dims, ws=None) == WORKSPACE
+    assert _mimo(lib, dims=dims, wsb=need - 1) == WORKSPACE
 
 
 def _trap(lib, dims=(2, 300, 4, 64, 128, 64), dtype=1, ws=ctypes.c_void_p(0x9000000), wsb=1 << 40,
