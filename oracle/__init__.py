@@ -73,6 +73,7 @@ def _load():
     lib.oracle_trap_fwd.argtypes = [P] * 10 + [I] * 5 + [P, I, P, P, ctypes.c_int]
     lib.oracle_trap_rotate.argtypes = [P] * 5 + [I] * 5 + [P] * 3
     lib.oracle_trap_bwd.argtypes = [P] * 12 + [I] * 5 + [P, I] + [P] * 10 + [ctypes.c_int]
+    lib.oracle_s6_grouped_fwd.argtypes = common + [I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_s6_layer_fwd.argtypes = [P] * 12 + [I] * 5 + [ctypes.c_uint32, P, I] + [P] * 4 + [ctypes.c_int]
     for f in (lib.oracle_s6_fwd, lib.oracle_ssd_fwd, lib.oracle_cssd_fwd, lib.oracle_s6_bwd,
               lib.oracle_ssd_bwd, lib.oracle_trap_fwd):
@@ -145,6 +146,26 @@ def s6_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, flags=BBAR_ZOH, units=None, 
     _load().oracle_s6_fwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
                           _ptr(h0), batch, L, Dm, N, flags, _ptr(uu), nu, _ptr(y), _ptr(hf),
                           nthreads or default_threads())
+    if full:
+        return (y.reshape(batch, Dm, L).transpose(0, 2, 1).copy(), hf.reshape(batch, Dm, N))
+    return y, hf
+
+
+def s6_grouped_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, flags=BBAR_ZOH, units=None, nthreads=None):
+    """The S6 recurrence in fp64 with B, C (batch, L, G, N) per group of channels: channel d
+    reads group d * G // d_inner (G = d_inner: per channel).  Returns as s6_fwd."""
+    u, dt, dt_bias, A_log, B, C, D, h0 = map(_f32, (u, dt, dt_bias, A_log, B, C, D, h0))
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    G = B.shape[2]
+    assert B.shape == (batch, L, G, N) and C.shape == B.shape and Dm % G == 0
+    uu, full = _units(units, batch, Dm)
+    nu = uu.shape[0]
+    y = np.empty((nu, L), np.float64)
+    hf = np.empty((nu, N), np.float64)
+    _load().oracle_s6_grouped_fwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                  _ptr(h0), batch, L, Dm, N, G, flags, _ptr(uu), nu, _ptr(y), _ptr(hf),
+                                  nthreads or default_threads())
     if full:
         return (y.reshape(batch, Dm, L).transpose(0, 2, 1).copy(), hf.reshape(batch, Dm, N))
     return y, hf

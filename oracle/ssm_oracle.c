@@ -81,6 +81,9 @@ typedef struct {
     int64_t K;
     double *u_out;          /* [n_units][L] or NULL */
     double *cs_out;         /* [n_units][K-1] or NULL */
+    /* grouped B, C (oracle_s6_grouped_fwd): (batch, L, G, N), channel d reads
+     * group d*G/Dm (G = Dm: per channel); 0 means one shared (batch, L, N) */
+    int64_t G;
 } s6_job;
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }
@@ -119,8 +122,9 @@ static void s6_unit(const s6_job *j, int64_t k)
         } else {
             uu = (double)j->u[e];
         }
-        const float *Bt = j->B + (b * L + t) * N;
-        const float *Ct = j->C + (b * L + t) * N;
+        const int64_t G = j->G > 0 ? j->G : 1, g = d * G / Dm;
+        const float *Bt = j->B + ((b * L + t) * G + g) * N;
+        const float *Ct = j->C + ((b * L + t) * G + g) * N;
         double yv = 0.0;
         for (int64_t n = 0; n < N; ++n) {
             const double z = delta * A[n];
@@ -764,6 +768,25 @@ void oracle_s6_fwd(const float *u, const float *dt, const float *dt_bias, const 
 {
     s6_job j = {u, dt, dt_bias, A_log, B, C, D, h0, batch, L, d_inner, d_state, flags,
                 units, n_units, y_out, hf_out};
+    run_units(0, &j, n_units, nthreads);
+}
+
+/*
+ * The S6 recurrence with B and C per group of channels (per channel when
+ * ngroups = d_inner): the variable B, C of the selective scan page's header
+ * taken per channel instead of shared (builderforce-memory-engine
+ * selective_scan.js header comment), with channel d reading group
+ * d * ngroups / d_inner.  B, C (batch, L, ngroups, d_state).
+ */
+void oracle_s6_grouped_fwd(const float *u, const float *dt, const float *dt_bias, const float *A_log,
+                           const float *B, const float *C, const float *D, const float *h0,
+                           int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                           uint32_t flags, const int64_t *units, int64_t n_units, double *y_out,
+                           double *hf_out, int nthreads)
+{
+    s6_job j = {u, dt, dt_bias, A_log, B, C, D, h0, batch, L, d_inner, d_state, flags,
+                units, n_units, y_out, hf_out};
+    j.G = ngroups;
     run_units(0, &j, n_units, nthreads);
 }
 

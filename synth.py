@@ -23,6 +23,9 @@ WORKLOADS = {
     # S6 at a Mamba-1 layer shape: 8 x 2048 x 1536, N=16, fp32
     "s6_mamba1": dict(kind="s6", batch=8, L=2048, d_inner=1536, d_state=16, dtype="f32",
                       dt_bias="uniform", D="normal"),
+    # that scan with B, C per channel (d_inner groups of one): 16x the B/C bytes
+    "s6_pc_mamba1": dict(kind="s6", batch=8, L=2048, d_inner=1536, d_state=16, dtype="f32",
+                         dt_bias="uniform", D="normal", ngroups=1536),
     # the Mamba-1 layer around that scan: conv1d (K=4) + SiLU before, SiLU(z) gating after
     "s6_layer_mamba1": dict(kind="s6_layer", batch=8, L=2048, d_inner=1536, d_state=16, d_conv=4,
                             dtype="f32"),
@@ -113,12 +116,15 @@ class Inputs:
 
 
 def s6_inputs(batch, L, d_inner, d_state, *, seed=(0,), dtype="f32", dt_bias="uniform",
-              D="normal", h0=False, a_log="index") -> Inputs:
+              D="normal", h0=False, a_log="index", ngroups=None) -> Inputs:
+    """ngroups: B, C (batch, L, ngroups, d_state) per group of channels (d_inner: per
+    channel) instead of one shared (batch, L, d_state)."""
     key = (1, *seed)
     u = _normal(_rng(key, 0), (batch, L, d_inner))
     dt = _normal(_rng(key, 1), (batch, L, d_inner), -3.0, 0.5)
-    B = _normal(_rng(key, 2), (batch, L, d_state))
-    C = _normal(_rng(key, 3), (batch, L, d_state))
+    bshape = (batch, L, d_state) if ngroups is None else (batch, L, ngroups, d_state)
+    B = _normal(_rng(key, 2), bshape)
+    C = _normal(_rng(key, 3), bshape)
     if dt_bias == "uniform":
         bias = _uniform(_rng(key, 4), (d_inner,), -1.0, 0.0)
     elif dt_bias == "zero":
@@ -143,8 +149,10 @@ def s6_inputs(batch, L, d_inner, d_state, *, seed=(0,), dtype="f32", dt_bias="un
     if dtype == "bf16":
         u, B, C = round_bf16(u), round_bf16(B), round_bf16(C)
         bf = ("u", "B", "C")
-    return Inputs("s6", dict(batch=batch, L=L, d_inner=d_inner, d_state=d_state),
-                  dict(u=u, dt=dt, dt_bias=bias, A_log=A_log, B=B, C=C, D=Dv, h0=h0a), bf)
+    dims = dict(batch=batch, L=L, d_inner=d_inner, d_state=d_state)
+    if ngroups is not None:
+        dims["ngroups"] = ngroups
+    return Inputs("s6", dims, dict(u=u, dt=dt, dt_bias=bias, A_log=A_log, B=B, C=C, D=Dv, h0=h0a), bf)
 
 
 def layer_inputs(batch, L, d_inner, d_state, d_conv=4, *, seed=(0,), dtype="f32", conv_state=True,
@@ -298,7 +306,7 @@ def workload_inputs(name: str, seed=(0,)) -> Inputs:
     kind = w.pop("kind")
     if kind == "s6":
         return s6_inputs(w["batch"], w["L"], w["d_inner"], w["d_state"], seed=seed,
-                         dtype=w["dtype"], dt_bias=w["dt_bias"], D=w["D"])
+                         dtype=w["dtype"], dt_bias=w["dt_bias"], D=w["D"], ngroups=w.get("ngroups"))
     if kind == "ssd":
         return ssd_inputs(w["batch"], w["L"], w["nheads"], w["headdim"], w["d_state"],
                           w["ngroups"], seed=seed, dtype=w["dtype"], h0=w.get("carry", False))
