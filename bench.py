@@ -65,6 +65,15 @@ def s6_model(d):
     return elems, bytes_, ops
 
 
+def s6_pc_model(d):
+    """S6 with B, C per group of channels: u, dt read and y written per (b, t, d); B, C
+    read once per (b, t, group, n); the same state updates as s6_model."""
+    B, L, D, N, G = d["batch"], d["L"], d["d_inner"], d["d_state"], d["ngroups"]
+    elems = B * L * D
+    bytes_ = elems * 12 + 2 * B * L * G * N * 4 + D * N * 4 + 2 * D * 4 + B * D * N * 4
+    return elems, bytes_, elems * N * S6_FLOPS_PER_UPDATE
+
+
 def s6_layer_model(d):
     """The fused layer: read x, z, dt (fp32), B, C, the conv state and h0; write y, h_final
     and the conv state.  Operations: the scan's state updates (the conv, SiLU and gate
@@ -222,6 +231,17 @@ def make_runner(name, dev):
             lib.ssm_s6_fused_fwd(t["x"], t["conv_w"], t["conv_b"], t["dt"], t["dt_bias"], t["A_log"], t["B"],
                                  t["C"], t["D"], h, cs, t["z"], y=y, h_final=h, conv_state_out=cs)
         return step, dims, w, (["s6_step4_kernel"] if dims["L"] == 1 else ["s6_scan_kernel", "s6_conv_state_kernel"])
+    if kind == "s6" and w.get("ngroups"):
+        t0 = copies[0]
+        y = torch.empty_like(t0["u"], dtype=torch.float32)
+        hf = torch.empty((dims["batch"], dims["d_inner"], dims["d_state"]), dtype=torch.float32, device=dev)
+
+        def step(i):
+            t = copies[i % N_ROTATE]
+            lib.ssm_s6_scan_grouped_fwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                        None, y=y, h_final=hf)
+        w["kind"] = "s6_pc"
+        return step, dims, w, ["s6_grouped_kernel"]
     if kind == "s6":
         t0 = copies[0]
         y = torch.empty_like(t0["u"], dtype=torch.float32)
@@ -428,7 +448,10 @@ def cpu_baseline_s6(name):
     d = inp.dims
     nthr = oracle.default_threads()
     t0 = time.perf_counter()
-    oracle.s6_fwd(**inp.arrays, nthreads=nthr)
+    if d.get("ngroups"):
+        oracle.s6_grouped_fwd(**inp.arrays, nthreads=nthr)
+    else:
+        oracle.s6_fwd(**inp.arrays, nthreads=nthr)
     sec = time.perf_counter() - t0
     elems = d["batch"] * d["L"] * d["d_inner"]
     return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
@@ -580,6 +603,8 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = s6_model(dims)
     elif kind == "s6_layer":
         elems, bytes_, ops = s6_layer_model(dims)
+    elif kind == "s6_pc":
+        elems, bytes_, ops = s6_pc_model(dims)
     elif kind == "s6_bwd":
         elems, bytes_, ops = s6_bwd_model(dims)
     elif kind == "ssd_bwd":
@@ -668,7 +693,7 @@ def main():
     }
     if not args.no_secondary and args.workload == "s6_mamba1":
         sec = []
-        for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5), ("cssd_mimo_mamba3", 5),
+        for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5), ("cssd_mimo_mamba3", 5), ("s6_pc_mamba1", 10),
                             ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
                             ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
                             ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5)):
@@ -709,7 +734,7 @@ def main():
         out["secondary"] = sec
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
-        if kind == "s6":
+        if kind in ("s6", "s6_pc"):
             out["cpu_baseline"] = cpu_baseline_s6(args.workload)
         elif kind == "s6_bwd":
             out["cpu_baseline"] = cpu_baseline_s6_bwd(args.workload[: -len("_bwd")])

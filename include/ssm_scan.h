@@ -85,6 +85,8 @@ typedef enum {
 
 /* Largest state size any entry point accepts. */
 #define SSM_MAX_D_STATE 256
+/* Largest state size of the S6 scan with B, C per group of channels. */
+#define SSM_MAX_D_STATE_GROUPED 32
 
 /* Message of the last failing call made by this thread ("" if none). */
 const char *ssm_last_error(void);
@@ -113,6 +115,24 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
                     int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
                     ssm_dtype_t in_dtype, uint32_t flags,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------- S6, B and C per channel group ----
+ * The S6 scan above with B and C per group of channels instead of shared
+ * [BF-S6 header: B and C are input-dependent; here they are also
+ * per-channel]: channel d reads row g = d * ngroups / d_inner,
+ *   h_t[n]   = exp(delta*A[d,n]) * h_{t-1}[n] + beta * B[b,t,g,n] * u[b,t,d]
+ *   y[b,t,d] = sum_n C[b,t,g,n] * h_t[n] + D[d] * u[b,t,d].
+ * ngroups = d_inner gives every channel its own B, C; ngroups = 1 is
+ * ssm_s6_scan_fwd (and runs its kernel).
+ *
+ * Layouts: B, C (batch, L, ngroups, d_state) [in_dtype]; the rest as
+ * ssm_s6_scan_fwd.  Limits: d_inner % ngroups == 0; d_state <= 32 when
+ * ngroups > 1 (SSM_MAX_D_STATE_GROUPED; 256 at ngroups = 1).  No workspace. */
+int ssm_s6_scan_grouped_fwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                            const void *B, const void *C, const float *D, float *y,
+                            const float *h0, float *h_final,
+                            int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                            ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream);
 
 /* ------------------------------------------------ S6 with its layer ----
  * The Mamba-1 layer's steps on either side of the scan, fused into it

@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = [
-    "ssm_s6_scan_fwd", "ssm_s6_scan_bwd", "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd", "ssd_chunk_scan_fwd",
+    "ssm_s6_scan_fwd", "ssm_s6_scan_grouped_fwd", "ssm_s6_scan_bwd", "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd", "ssd_chunk_scan_fwd",
     "ssd_chunk_scan_bwd",
     "ssd_cplx_chunk_scan_fwd", "ssd_trap_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size",
     "ssm_s6_scan_bwd_workspace_size", "ssd_trap_chunk_scan_fwd_workspace_size",
@@ -46,6 +46,8 @@ _lib.ssm_s6_scan_fwd_workspace_size.argtypes = [_I] * 4
 _lib.ssm_s6_scan_fwd_workspace_size.restype = _Z
 _lib.ssm_s6_scan_fwd.argtypes = [_P] * 10 + [_I] * 4 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
 _lib.ssm_s6_scan_fwd.restype = ctypes.c_int
+_lib.ssm_s6_scan_grouped_fwd.argtypes = [_P] * 10 + [_I] * 5 + [ctypes.c_int, ctypes.c_uint32, _P]
+_lib.ssm_s6_scan_grouped_fwd.restype = ctypes.c_int
 _lib.ssm_s6_fused_fwd.argtypes = [_P] * 16 + [_I] * 5 + [ctypes.c_int, ctypes.c_uint32, _P]
 _lib.ssm_s6_fused_fwd.restype = ctypes.c_int
 _lib.ssm_causal_conv1d_fwd.argtypes = [_P] * 6 + [_I] * 4 + [ctypes.c_int, ctypes.c_int, _P]
@@ -191,6 +193,36 @@ def ssm_s6_scan_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, *, flags=SSM_BBAR_Z
     rc = _lib.ssm_s6_scan_fwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
                               _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L, Dm, N,
                               _in_dtype(u), flags, None, 0, _stream(dev))
+    _check(rc)
+    return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ssm_s6_scan_grouped_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, *, flags=SSM_BBAR_ZOH,
+                            return_final=False, y=None, h_final=None):
+    """S6 forward scan with B, C (batch, L, ngroups, d_state) per group of channels
+    (ngroups = d_inner: per channel); the rest as ssm_s6_scan_fwd."""
+    dev = u.device
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    G = B.shape[2]
+    dty = u.dtype
+    _req(u, "u", dty, (batch, L, Dm), dev)
+    _req(dt, "dt", torch.float32, (batch, L, Dm), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (Dm,), dev)
+    _req(A_log, "A_log", torch.float32, (Dm, N), dev)
+    _req(B, "B", dty, (batch, L, G, N), dev)
+    _req(C, "C", dty, (batch, L, G, N), dev)
+    _opt(D, "D", torch.float32, (Dm,), dev)
+    _opt(h0, "h0", torch.float32, (batch, Dm, N), dev)
+    if y is None:
+        y = torch.empty((batch, L, Dm), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, (batch, L, Dm), dev)
+    if return_final and h_final is None:
+        h_final = torch.empty((batch, Dm, N), dtype=torch.float32, device=dev)
+    _opt(h_final, "h_final", torch.float32, (batch, Dm, N), dev)
+    rc = _lib.ssm_s6_scan_grouped_fwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L, Dm, N, G,
+                                      _in_dtype(u), flags, _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y
 

@@ -92,6 +92,41 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
     return launched(E, ssm::launch_s6(a, stream, &kn), kn);
 }
 
+int ssm_s6_scan_grouped_fwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                            const void *B, const void *C, const float *D, float *y,
+                            const float *h0, float *h_final,
+                            int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                            ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream) {
+    const char *E = "ssm_s6_scan_grouped_fwd";
+    REQUIRE_PTR(E, u); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
+    REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
+    REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, d_inner); REQUIRE_POS(E, d_state);
+    REQUIRE_POS(E, ngroups);
+    if (d_inner % ngroups != 0)
+        return fail(SSM_ERR_INVALID_ARG, "%s: d_inner %lld is not a multiple of ngroups %lld", E,
+                    (long long)d_inner, (long long)ngroups);
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if ((flags & ~0x3u) != 0 || (flags & 0x3u) == 0x3u)
+        return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x: only SSM_BBAR_ZOH/DT/ONE apply", E, flags);
+    if (d_state > (ngroups == 1 ? SSM_MAX_D_STATE : SSM_MAX_D_STATE_GROUPED))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld > %d", E, (long long)d_state,
+                    ngroups == 1 ? SSM_MAX_D_STATE : SSM_MAX_D_STATE_GROUPED);
+    if (too_big(batch, L, d_inner, 1) || too_big(batch, L, ngroups, d_state) ||
+        batch * ((d_inner + 255) / 16) > 0x7fffffffLL)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    REQUIRE_ALIGN(E, u); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
+    REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
+    REQUIRE_ALIGN(E, h0); REQUIRE_ALIGN(E, h_final);
+    if ((const void *)y == u || (const void *)y == (const void *)dt || (const void *)y == B ||
+        (const void *)y == C)
+        return fail(SSM_ERR_INVALID_ARG, "%s: y aliases an input", E);
+    ssm::S6Args a{u, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, d_inner, d_state,
+                  in_dtype == SSM_BF16, flags};
+    const char *kn = "s6_grouped";
+    return launched(E, ssm::launch_s6_grouped(a, ngroups, stream, &kn), kn);
+}
+
 int ssm_s6_fused_fwd(const void *x, const float *conv_w, const float *conv_b, const float *conv_state,
                      const void *z, const float *dt, const float *dt_bias, const float *A_log,
                      const void *B, const void *C, const float *D, float *y,

@@ -14,6 +14,9 @@ struct S6Args {
     bool bf16; uint32_t flags;
 };
 hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_name);
+// B, C (batch, L, ngroups, d_state): channel d reads group d * ngroups / d_inner
+// (one group goes to launch_s6)
+hipError_t launch_s6_grouped(const S6Args &a, int64_t ngroups, hipStream_t stream, const char **kernel_name);
 
 // Mamba-1 layer around the scan: u = SiLU(causal conv1d(x)), y = scan(u) * SiLU(z)
 struct S6FusedArgs {

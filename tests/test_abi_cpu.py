@@ -26,6 +26,7 @@ def lib():
     L.ssm_last_error.restype = ctypes.c_char_p
     I, P, Z = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     L.ssm_s6_scan_fwd.argtypes = [P] * 10 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
+    L.ssm_s6_scan_grouped_fwd.argtypes = [P] * 10 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P]
     L.ssd_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_cplx_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_uint32, P, Z, P]
     L.ssd_cplx_mimo_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 8 + [ctypes.c_uint32, P, Z, P]
@@ -59,6 +60,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M))
     names = {n for n in names if n.startswith(("ssm_", "ssd_"))}
     assert names == {"ssm_last_error", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_fwd",
+                     "ssm_s6_scan_grouped_fwd",
                      "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd",
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
@@ -200,6 +202,25 @@ def test_cssd_argument_checks(lib):
     assert lib.ssd_cplx_chunk_scan_fwd_workspace_size(2, 100, 4, 64, 32, 2, 64) == 0
     assert _cssd(lib, dims=long_dims, ws=None) == WORKSPACE
     assert _cssd(lib, dims=long_dims, wsb=need - 1) == WORKSPACE
+
+
+def _s6g(lib, dims=(2, 8, 16, 16, 16), dtype=0, flags=0, y=FAKE, u=FAKE, B=FAKE):
+    return lib.ssm_s6_scan_grouped_fwd(u, FAKE, None, FAKE, B, FAKE, None, y, None, None, *dims, dtype, flags,
+                                       None)
+
+
+def test_s6_grouped_argument_checks(lib):
+    # every case below fails before any launch (the pointers are fake)
+    assert _s6g(lib, dims=(2, 8, 16, 16, 3)) == INVALID and "multiple" in _err(lib)
+    assert _s6g(lib, dims=(2, 8, 16, 16, 0)) == INVALID
+    assert _s6g(lib, dims=(2, 8, 16, 33, 16)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _s6g(lib, dims=(2, 8, 16, 257, 1)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _s6g(lib, dims=(2, 0, 16, 16, 16)) == INVALID
+    assert _s6g(lib, dtype=7) == INVALID and "in_dtype" in _err(lib)
+    assert _s6g(lib, flags=0x3) == INVALID
+    assert _s6g(lib, flags=0x4) == INVALID
+    assert _s6g(lib, y=None) == INVALID
+    assert _s6g(lib, y=FAKE, u=FAKE, B=FAKE, flags=0x8) == INVALID
 
 
 def _mimo(lib, dims=(2, 100, 4, 4, 64, 32, 2, 64), flags=0, ws=FAKE, wsb=1 << 40):
