@@ -44,7 +44,7 @@ S6_ALU_PEAK_TFLOPS = VALU_SLOTS_PER_S / S6_SLOTS_PER_UPDATE * S6_FLOPS_PER_UPDAT
 # HBM bytes per launch of s6_scan_kernel on s6_mamba1, from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch) scaled by a 1 GiB device copy (fetch x 2.0, write x 1.0);
 # valid only for the kernel sources (s6_kernel.hpp + s6_scan.hip) with this sha1
-S6_TRAFFIC = {"src_sha1": "f913e893c1df0b78458b262d01c0712a30613396", "bytes": (100238.2 * 2.0 + 99077.1 * 1.0) * 1024}
+S6_TRAFFIC = {"src_sha1": "11d0001f54f53a72d99f6f2f881663881dc0a0a7", "bytes": (100242.0 * 2.0 + 99090.8 * 1.0) * 1024}
 # adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
 # (products and fmas, 24 flops) plus the recomputed Abar, beta, phi1' (not counted again)
 S6_BWD_FLOPS_PER_UPDATE = 24
@@ -181,6 +181,14 @@ def make_runner(name, dev):
     import torch
     import selective_state_space_s6_amd as lib
     import synth
+    # name suffixes: _bwd (the backward), _bwd_saved (the backward reading the forward's saved
+    # states), _fwd_save (the forward that saves them)
+    saved = name.endswith("_bwd_saved")
+    save = name.endswith("_fwd_save")
+    if saved:
+        name = name[: -len("_saved")]
+    if save:
+        name = name[: -len("_fwd_save")]
     bwd = name.endswith("_bwd")
     if bwd:
         name = name[: -len("_bwd")]
@@ -203,13 +211,35 @@ def make_runner(name, dev):
         out = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
         ws = torch.empty(lib.ssm_s6_scan_bwd_workspace_size(d["batch"], d["L"], d["d_inner"],
                                                             d["d_state"]), dtype=torch.uint8, device=dev)
+        if saved:      # each copy's states, saved once by the forward outside the timed region
+            for t in copies:
+                t["ck"] = lib.ssm_s6_scan_fwd_save(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"],
+                                                   t["D"], None)[2]
+
+            def step(i):
+                t = copies[i % N_ROTATE]
+                lib.ssm_s6_scan_bwd_saved(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                          None, t["dy"], t["dhf"], t["ck"], out=out, workspace=ws)
+        else:
+            def step(i):
+                t = copies[i % N_ROTATE]
+                lib.ssm_s6_scan_bwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                    None, t["dy"], t["dhf"], out=out, workspace=ws)
+        w["kind"] = "s6_bwd"
+        return step, dims, w, ["s6_bwd_kernel", "s6_bwd_reduce_kernel"]
+    if kind == "s6" and save:
+        t0 = copies[0]
+        y = torch.empty_like(t0["u"], dtype=torch.float32)
+        hf = torch.empty((dims["batch"], dims["d_inner"], dims["d_state"]), dtype=torch.float32, device=dev)
+        ck = torch.empty((dims["batch"], (dims["L"] + 15) // 16, dims["d_inner"], dims["d_state"]),
+                         dtype=torch.float32, device=dev)
 
         def step(i):
             t = copies[i % N_ROTATE]
-            lib.ssm_s6_scan_bwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
-                                None, t["dy"], t["dhf"], out=out, workspace=ws)
-        w["kind"] = "s6_bwd"
-        return step, dims, w, ["s6_bwd_kernel", "s6_bwd_reduce_kernel"]
+            lib.ssm_s6_scan_fwd_save(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                     None, y=y, h_final=hf, checkpoints=ck)
+        w["kind"] = "s6_save"
+        return step, dims, w, ["s6_scan_kernel"]
     if kind == "conv":
         t0 = copies[0]
         y = torch.empty_like(t0["x"])
@@ -605,6 +635,9 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = s6_layer_model(dims)
     elif kind == "s6_pc":
         elems, bytes_, ops = s6_pc_model(dims)
+    elif kind == "s6_save":      # the forward plus the saved states it writes
+        elems, bytes_, ops = s6_model(dims)
+        bytes_ += dims["batch"] * (-(-dims["L"] // 16)) * dims["d_inner"] * dims["d_state"] * 4
     elif kind == "s6_bwd":
         elems, bytes_, ops = s6_bwd_model(dims)
     elif kind == "ssd_bwd":
@@ -696,7 +729,8 @@ def main():
         for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5), ("cssd_mimo_mamba3", 5), ("s6_pc_mamba1", 10),
                             ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
                             ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
-                            ("s6_mamba1_bwd", 10), ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5)):
+                            ("s6_mamba1_bwd", 10), ("s6_mamba1_fwd_save", 10), ("s6_mamba1_bwd_saved", 10),
+                            ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
             es = s["event_ms_median"] * 1e-3
@@ -734,10 +768,15 @@ def main():
         out["secondary"] = sec
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
-        if kind in ("s6", "s6_pc"):
-            out["cpu_baseline"] = cpu_baseline_s6(args.workload)
+        base = args.workload
+        for suffix in ("_bwd_saved", "_fwd_save", "_bwd"):
+            if base.endswith(suffix):
+                base = base[: -len(suffix)]
+                break
+        if kind in ("s6", "s6_pc", "s6_save"):
+            out["cpu_baseline"] = cpu_baseline_s6(base)
         elif kind == "s6_bwd":
-            out["cpu_baseline"] = cpu_baseline_s6_bwd(args.workload[: -len("_bwd")])
+            out["cpu_baseline"] = cpu_baseline_s6_bwd(base)
         elif kind == "s6_layer":
             out["cpu_baseline"] = cpu_baseline_s6_layer(args.workload)
         elif kind in ("ssd_bwd", "trap_bwd"):

@@ -221,6 +221,42 @@ int ssm_s6_scan_bwd(const void *u, const float *dt, const float *dt_bias, const 
                     ssm_dtype_t in_dtype, uint32_t flags,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------- S6 with saved states ----
+ * The saved-state form of the pair above, for training: the backward needs
+ * the state entering each 16-step tile, and either recomputes it in a first
+ * pass (ssm_s6_scan_bwd) or reads what the forward saved (the backward's
+ * need for saved or recomputed states: [BF-S6 backward_scan]).
+ *
+ * ssm_s6_scan_fwd_save is ssm_s6_scan_fwd (same inputs, outputs, layouts and
+ * result, bit for bit when L > 1; at L = 1 the plain entry point runs its
+ * one-step kernel, whose rounding differs) that also writes checkpoints (batch, ceil(L/16), d_inner, d_state)
+ * fp32: entry [b, k, d, n] is the state h_{16k-1}[n] of channel d (h0, or 0,
+ * at k = 0).  checkpoints is caller-owned, ssm_s6_scan_checkpoint_size()
+ * bytes, 16-byte aligned, and aliases no other argument.  Limits: d_state <=
+ * SSM_S6_BWD_MAX_D_STATE.
+ *
+ * ssm_s6_scan_bwd_saved is ssm_s6_scan_bwd given those checkpoints (read
+ * only; the caller passes the same u, dt, dt_bias, A_log, B, h0 and flags as
+ * to the forward that wrote them): it skips the recomputing pass.  Same
+ * outputs, limits and workspace size as ssm_s6_scan_bwd (its checkpoint
+ * region is left unused). */
+size_t ssm_s6_scan_checkpoint_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state);
+
+int ssm_s6_scan_fwd_save(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                         const void *B, const void *C, const float *D, float *y,
+                         const float *h0, float *h_final, float *checkpoints,
+                         int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                         ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream);
+
+int ssm_s6_scan_bwd_saved(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                          const void *B, const void *C, const float *D, const float *h0,
+                          const float *dy, const float *dh_final, const float *checkpoints,
+                          float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                          float *dD, float *ddt_bias, float *dh0,
+                          int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                          ssm_dtype_t in_dtype, uint32_t flags,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------- SSD ----
  * Mamba-2 state-space dual scan with a scalar A per head [BF-SSD header and
  * ssd_chunk_forward; RS-M3 F6 K2-K5]:

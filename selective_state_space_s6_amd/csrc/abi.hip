@@ -92,6 +92,46 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
     return launched(E, ssm::launch_s6(a, stream, &kn), kn);
 }
 
+size_t ssm_s6_scan_checkpoint_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state) {
+    if (batch <= 0 || L <= 0 || d_inner <= 0 || d_state <= 0) return 0;
+    return (size_t)(batch * ((L + 15) / 16) * d_inner * d_state) * sizeof(float);
+}
+
+int ssm_s6_scan_fwd_save(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                         const void *B, const void *C, const float *D, float *y,
+                         const float *h0, float *h_final, float *checkpoints,
+                         int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                         ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream) {
+    const char *E = "ssm_s6_scan_fwd_save";
+    REQUIRE_PTR(E, u); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
+    REQUIRE_PTR(E, C); REQUIRE_PTR(E, y); REQUIRE_PTR(E, checkpoints);
+    REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, d_inner); REQUIRE_POS(E, d_state);
+    if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+        return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
+    if ((flags & ~0x3u) != 0 || (flags & 0x3u) == 0x3u)
+        return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x: only SSM_BBAR_ZOH/DT/ONE apply", E, flags);
+    if (d_state > SSM_S6_BWD_MAX_D_STATE)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld > %d (the backward's limit)", E, (long long)d_state,
+                    SSM_S6_BWD_MAX_D_STATE);
+    if (too_big(batch, L, d_inner, 1) || too_big(batch, (L + 15) / 16, d_inner, d_state) ||
+        batch * ((d_inner + 255) / 16) > 0x7fffffffLL)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    REQUIRE_ALIGN(E, u); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
+    REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
+    REQUIRE_ALIGN(E, h0); REQUIRE_ALIGN(E, h_final); REQUIRE_ALIGN(E, checkpoints);
+    const void *ins[] = {u, dt, dt_bias, A_log, B, C, D, h0};
+    for (const void *o : {(const void *)y, (const void *)checkpoints})
+        for (const void *in : ins)
+            if (o == in) return fail(SSM_ERR_INVALID_ARG, "%s: an output aliases an input", E);
+    if ((const void *)y == (const void *)checkpoints || (const void *)h_final == (const void *)checkpoints ||
+        (const void *)h_final == (const void *)y)
+        return fail(SSM_ERR_INVALID_ARG, "%s: two outputs alias", E);
+    ssm::S6Args a{u, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, d_inner, d_state,
+                  in_dtype == SSM_BF16, flags};
+    const char *kn = "s6_save";
+    return launched(E, ssm::launch_s6_save(a, checkpoints, stream, &kn), kn);
+}
+
 int ssm_s6_scan_grouped_fwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
                             const void *B, const void *C, const float *D, float *y,
                             const float *h0, float *h_final,
@@ -206,15 +246,14 @@ size_t ssm_s6_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner,
     return ssm::s6_bwd_workspace_bytes(batch, L, d_inner, d_state);
 }
 
-int ssm_s6_scan_bwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
-                    const void *B, const void *C, const float *D, const float *h0,
-                    const float *dy, const float *dh_final,
-                    float *du, float *ddt, float *dB, float *dC, float *dA_log,
-                    float *dD, float *ddt_bias, float *dh0,
-                    int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
-                    ssm_dtype_t in_dtype, uint32_t flags,
-                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    const char *E = "ssm_s6_scan_bwd";
+static int s6_bwd_call(const char *E, const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                       const void *B, const void *C, const float *D, const float *h0,
+                       const float *dy, const float *dh_final, const float *checkpoints,
+                       float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                       float *dD, float *ddt_bias, float *dh0,
+                       int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                       ssm_dtype_t in_dtype, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
     REQUIRE_PTR(E, u); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
     REQUIRE_PTR(E, C); REQUIRE_PTR(E, dy);
     REQUIRE_PTR(E, du); REQUIRE_PTR(E, ddt); REQUIRE_PTR(E, dB); REQUIRE_PTR(E, dC);
@@ -236,7 +275,8 @@ int ssm_s6_scan_bwd(const void *u, const float *dt, const float *dt_bias, const 
     REQUIRE_ALIGN(E, du); REQUIRE_ALIGN(E, ddt); REQUIRE_ALIGN(E, dB); REQUIRE_ALIGN(E, dC);
     REQUIRE_ALIGN(E, dA_log); REQUIRE_ALIGN(E, dD); REQUIRE_ALIGN(E, ddt_bias); REQUIRE_ALIGN(E, dh0);
     REQUIRE_ALIGN(E, workspace);
-    const void *ins[] = {u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, workspace};
+    REQUIRE_ALIGN(E, checkpoints);
+    const void *ins[] = {u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, workspace, checkpoints};
     const void *outs[] = {du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0};
     for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
         if (outs[i] == nullptr) continue;
@@ -251,9 +291,38 @@ int ssm_s6_scan_bwd(const void *u, const float *dt, const float *dt_bias, const 
                     workspace ? workspace_bytes : (size_t)0);
     ssm::S6BwdArgs a{u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final,
                      du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0,
-                     batch, L, d_inner, d_state, in_dtype == SSM_BF16, flags, workspace};
+                     batch, L, d_inner, d_state, in_dtype == SSM_BF16, flags, workspace, checkpoints};
     const char *kn = "s6_bwd";
     return launched(E, ssm::launch_s6_bwd(a, stream, &kn), kn);
+}
+
+
+int ssm_s6_scan_bwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                    const void *B, const void *C, const float *D, const float *h0,
+                    const float *dy, const float *dh_final,
+                    float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                    float *dD, float *ddt_bias, float *dh0,
+                    int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                    ssm_dtype_t in_dtype, uint32_t flags,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return s6_bwd_call("ssm_s6_scan_bwd", u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, nullptr,
+                       du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, batch, L, d_inner, d_state, in_dtype, flags,
+                       workspace, workspace_bytes, stream);
+}
+
+int ssm_s6_scan_bwd_saved(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                          const void *B, const void *C, const float *D, const float *h0,
+                          const float *dy, const float *dh_final, const float *checkpoints,
+                          float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                          float *dD, float *ddt_bias, float *dh0,
+                          int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                          ssm_dtype_t in_dtype, uint32_t flags,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssm_s6_scan_bwd_saved";
+    REQUIRE_PTR(E, checkpoints);
+    return s6_bwd_call(E, u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, checkpoints,
+                       du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, batch, L, d_inner, d_state, in_dtype, flags,
+                       workspace, workspace_bytes, stream);
 }
 
 static int ssd_check_shape(const char *E, int64_t batch, int64_t L, int64_t nheads, int64_t headdim,

@@ -14,6 +14,9 @@ struct S6Args {
     bool bf16; uint32_t flags;
 };
 hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_name);
+// the forward that also writes the state entering every 16-step tile, (batch,
+// ceil(L/16), d_inner, d_state) fp32, for the backward (d_state <= 16)
+hipError_t launch_s6_save(const S6Args &a, float *checkpoints, hipStream_t stream, const char **kernel_name);
 // B, C (batch, L, ngroups, d_state): channel d reads group d * ngroups / d_inner
 // (one group goes to launch_s6)
 hipError_t launch_s6_grouped(const S6Args &a, int64_t ngroups, hipStream_t stream, const char **kernel_name);
@@ -47,6 +50,7 @@ struct S6BwdArgs {
     int64_t batch, L, d_inner, d_state;
     bool bf16; uint32_t flags;
     void *workspace;
+    const float *checkpoints = nullptr;   // the forward's saved states (batch, ceil(L/16), d_inner, d_state)
 };
 size_t s6_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state);
 hipError_t launch_s6_bwd(const S6BwdArgs &a, hipStream_t stream, const char **kernel_name);

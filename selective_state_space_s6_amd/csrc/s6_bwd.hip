@@ -21,7 +21,8 @@
 // DPP row is 16 channels sharing one state (B[t, n], C[t, n] of a tile sit one
 // step per lane and reach the row with row_newbcast) and a wave holds 4 states.
 //   pass 1  forward over the sequence in 16-step tiles, storing the state that
-//           enters each tile (checkpoints);
+//           enters each tile (checkpoints) -- skipped when the forward saved
+//           them (ssm_s6_scan_fwd_save), the same layout read in place;
 //   pass 2  backward over the tiles: recompute the tile's 16 states from its
 //           checkpoint into registers, then run the adjoint.
 // Global loads of the next tile are issued before a tile is computed; delta,
@@ -61,6 +62,7 @@ struct S6BKp {
     const float *dy; const float *dhf;
     float *du, *ddt, *dB, *dC, *dA_log, *dD, *ddt_bias, *dh0;
     float *ck;            // (batch, ntiles, d_inner, N): state entering each tile
+    bool saved;           // ck holds the forward's saved states: pass 1 is skipped
     float *pB, *pC;       // (ncblk, batch, L, N): per channel-block partials
     float *pA;            // (batch, d_inner, N): per batch-row partials of dA (not yet times A)
     float *pDv, *pTb;     // (batch, d_inner): per batch-row partials of dD, ddt_bias
@@ -214,42 +216,52 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
     const float Bmask = n < p.N ? 1.0f : 0.0f;   // state-padding lanes carry zeros
     float h = (ok && p.h0) ? p.h0[(b * p.Dm + d) * p.N + n] : 0.0f;
 
-    // ---- pass 1: forward, checkpointing the state entering each tile
+    // ---- pass 1: forward, checkpointing the state entering each tile (or, with
+    // the forward's saved states, only the last tile's loads and staging)
     StageRaw RS, RSn;
     LaneRaw RL, RLn;
     RS.dy = RSn.dy = 0.0f;
     RL.C = RL.hin = RLn.C = RLn.hin = 0.0f;
-    load_stage(0, RS, ntiles == 1);
-    load_lane(0, RL, false);
-    stage(0, 0, RS, ntiles == 1);
-    __syncthreads();
-    for (int kt = 0; kt + 1 < ntiles; ++kt) {
-        const int buf = kt & 1;
-        if (ok) *at(ck_b + (int64_t)kt * ck_step_n(p), ck_off) = h;
-        const bool last = kt + 2 == ntiles;            // the next tile is the last one
-        load_stage(kt + 1, RSn, last);
-        load_lane(kt + 1, RLn, false);
-        if (last) RLn.C = In<TIN>::ld(at(C_b + (int64_t)(kt + 1) * kT * p.N, lane_e(kt + 1) * (uint32_t)sizeof(TIN)), 0);
-        const float Bv = RL.B * Bmask;
-        static_for<0, kT / 4>([&](auto qi) __attribute__((always_inline)) {
-            constexpr int q = decltype(qi)::value;
-            const float4 dq = *reinterpret_cast<const float4 *>(&sDl[buf][k][4 * q]);
-            const float4 uq = *reinterpret_cast<const float4 *>(&sU[buf][k][4 * q]);
-            const float dl4[4] = {dq.x, dq.y, dq.z, dq.w};
-            const float uu4[4] = {uq.x, uq.y, uq.z, uq.w};
-            static_for<0, 4>([&](auto ii) __attribute__((always_inline)) {
-                constexpr int i = decltype(ii)::value;
-                const float ab = exp2_fast(dl4[i] * A2);
-                const float bu = row_bcast<4 * q + i>(Bv) * uu4[i];
-                h = fmaf(ab, h, beta_of(dl4[i], ab) * bu);
-            });
-        });
-        stage(buf ^ 1, kt + 1, RSn, last);
+    if (p.saved) {
+        const int kl = ntiles - 1;
+        load_stage(kl, RS, true);
+        load_lane(kl, RL, true);          // B, C and the saved state entering tile kl
+        stage(kl & 1, kl, RS, true);
+        h = ok ? RL.hin : 0.0f;
         __syncthreads();
-        RS = RSn;
-        RL = RLn;
+    } else {
+        load_stage(0, RS, ntiles == 1);
+        load_lane(0, RL, false);
+        stage(0, 0, RS, ntiles == 1);
+        __syncthreads();
+        for (int kt = 0; kt + 1 < ntiles; ++kt) {
+            const int buf = kt & 1;
+            if (ok) *at(ck_b + (int64_t)kt * ck_step_n(p), ck_off) = h;
+            const bool last = kt + 2 == ntiles;            // the next tile is the last one
+            load_stage(kt + 1, RSn, last);
+            load_lane(kt + 1, RLn, false);
+            if (last) RLn.C = In<TIN>::ld(at(C_b + (int64_t)(kt + 1) * kT * p.N, lane_e(kt + 1) * (uint32_t)sizeof(TIN)), 0);
+            const float Bv = RL.B * Bmask;
+            static_for<0, kT / 4>([&](auto qi) __attribute__((always_inline)) {
+                constexpr int q = decltype(qi)::value;
+                const float4 dq = *reinterpret_cast<const float4 *>(&sDl[buf][k][4 * q]);
+                const float4 uq = *reinterpret_cast<const float4 *>(&sU[buf][k][4 * q]);
+                const float dl4[4] = {dq.x, dq.y, dq.z, dq.w};
+                const float uu4[4] = {uq.x, uq.y, uq.z, uq.w};
+                static_for<0, 4>([&](auto ii) __attribute__((always_inline)) {
+                    constexpr int i = decltype(ii)::value;
+                    const float ab = exp2_fast(dl4[i] * A2);
+                    const float bu = row_bcast<4 * q + i>(Bv) * uu4[i];
+                    h = fmaf(ab, h, beta_of(dl4[i], ab) * bu);
+                });
+            });
+            stage(buf ^ 1, kt + 1, RSn, last);
+            __syncthreads();
+            RS = RSn;
+            RL = RLn;
+        }
+        if (ntiles == 1) RL.C = In<TIN>::ld(at(C_b, lane_e(0) * (uint32_t)sizeof(TIN)), 0);
     }
-    if (ntiles == 1) RL.C = In<TIN>::ld(at(C_b, lane_e(0) * (uint32_t)sizeof(TIN)), 0);
 
     // ---- pass 2: backward over the tiles
     float g = (ok && p.dhf) ? p.dhf[(b * p.Dm + d) * p.N + n] : 0.0f;
@@ -491,7 +503,8 @@ hipError_t launch_s6_bwd(const S6BwdArgs &a, hipStream_t stream, const char **ke
     p.ncblk = (a.d_inner + kCW - 1) / kCW;
     const WsLayout w = layout(a.batch, a.L, a.d_inner, a.d_state);
     char *ws = static_cast<char *>(a.workspace);
-    p.ck = reinterpret_cast<float *>(ws + w.ck);
+    p.ck = a.checkpoints ? const_cast<float *>(a.checkpoints) : reinterpret_cast<float *>(ws + w.ck);
+    p.saved = a.checkpoints != nullptr;
     p.pB = reinterpret_cast<float *>(ws + w.pB);
     p.pC = reinterpret_cast<float *>(ws + w.pC);
     p.pA = reinterpret_cast<float *>(ws + w.pA);

@@ -59,6 +59,9 @@ struct S6Kp {
     const void *z;
     float *u_out;
     int K;
+    // SAVE form: the state entering every 16-step tile, (batch, ntiles, Dm, N) fp32
+    // (the saved states the S6 backward reads in place of recomputing them)
+    float *ck;
 };
 
 constexpr int kMaxConv = 4;   // longest causal convolution of the fused form
@@ -131,7 +134,7 @@ __device__ __forceinline__ void load_raw(Raw<TIN, G, SPL, FUSE> &r, const Ptrs<T
     }
 }
 
-template <typename TIN, int G, int SPL, int MODE, bool FUSE>
+template <typename TIN, int G, int SPL, int MODE, bool FUSE, bool SAVE = false>
 __global__ void __launch_bounds__(kThreads)
 s6_scan_kernel(S6Kp p) {
     constexpr int CW = kThreads / G;     // channels per block
@@ -343,9 +346,20 @@ s6_scan_kernel(S6Kp p) {
             for (int i = 0; i < EPT; ++i) gate_prev[i] = gate_cur[i];
         }
     };
+    // SAVE: the state entering tile kt, before the tile is scanned
+    auto save = [&](int64_t kt) __attribute__((always_inline)) {
+        if constexpr (SAVE) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const int64_t n = (int64_t)g * SPL + j;
+                if (dok && n < p.N) p.ck[((b * ntiles + kt) * p.Dm + d) * p.N + n] = h[j];
+            }
+        }
+    };
     auto body_full = [&](int64_t kt, Raw<TIN, G, SPL, FUSE> &Rk, const Raw<TIN, G, SPL, FUSE> &Rn, auto accTag)
         __attribute__((always_inline)) {
         const int buf = (int)(kt & 1);
+        save(kt);
         compute(buf, Rk, accTag);
         reduce(buf ^ 1, (kt - 1) * kT, std::false_type{});
         shift();
@@ -356,6 +370,7 @@ s6_scan_kernel(S6Kp p) {
     auto body_checked = [&](int64_t kt, Raw<TIN, G, SPL, FUSE> &Rk, const Raw<TIN, G, SPL, FUSE> &Rn, auto accTag)
         __attribute__((always_inline)) {
         const int buf = (int)(kt & 1);
+        save(kt);
         compute(buf, Rk, accTag);
         if (kt >= 1) reduce(buf ^ 1, (kt - 1) * kT, std::true_type{});
         shift();
@@ -398,21 +413,32 @@ s6_scan_kernel(S6Kp p) {
     }
 }
 
-template <typename TIN, int G, int SPL, int MODE, bool FUSE>
+template <typename TIN, int G, int SPL, int MODE, bool FUSE, bool SAVE = false>
 hipError_t launch_t(const S6Kp &kp, hipStream_t s) {
     constexpr int CW = kThreads / G;
     S6Kp p = kp;
     p.n_cblk = (p.Dm + CW - 1) / CW;
     const int64_t nblk = p.batch * p.n_cblk;
-    hipLaunchKernelGGL((s6_scan_kernel<TIN, G, SPL, MODE, FUSE>), dim3((unsigned)nblk), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((s6_scan_kernel<TIN, G, SPL, MODE, FUSE, SAVE>), dim3((unsigned)nblk), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <typename TIN, int G, int SPL, bool FUSE>
+template <typename TIN, int G, int SPL, bool FUSE, bool SAVE = false>
 hipError_t launch_mode(const S6Kp &kp, int mode, hipStream_t s) {
-    if (mode == 0) return launch_t<TIN, G, SPL, 0, FUSE>(kp, s);
-    if (mode == 1) return launch_t<TIN, G, SPL, 1, FUSE>(kp, s);
-    return launch_t<TIN, G, SPL, 2, FUSE>(kp, s);
+    if (mode == 0) return launch_t<TIN, G, SPL, 0, FUSE, SAVE>(kp, s);
+    if (mode == 1) return launch_t<TIN, G, SPL, 1, FUSE, SAVE>(kp, s);
+    return launch_t<TIN, G, SPL, 2, FUSE, SAVE>(kp, s);
+}
+
+// the SAVE form, for the state sizes the S6 backward takes (N <= 16)
+template <typename TIN>
+hipError_t launch_shape_save(const S6Kp &kp, int mode, hipStream_t s) {
+    const int64_t N = kp.N;
+    if (N <= 1) return launch_mode<TIN, 1, 1, false, true>(kp, mode, s);
+    if (N <= 2) return launch_mode<TIN, 2, 1, false, true>(kp, mode, s);
+    if (N <= 4) return launch_mode<TIN, 4, 1, false, true>(kp, mode, s);
+    if (N <= 8) return launch_mode<TIN, 8, 1, false, true>(kp, mode, s);
+    return launch_mode<TIN, 16, 1, false, true>(kp, mode, s);
 }
 
 template <typename TIN, bool FUSE>

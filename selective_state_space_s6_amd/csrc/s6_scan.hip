@@ -19,4 +19,15 @@ hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_na
     return a.bf16 ? launch_shape<uint16_t, false>(p, mode, stream) : launch_shape<float, false>(p, mode, stream);
 }
 
+hipError_t launch_s6_save(const S6Args &a, float *checkpoints, hipStream_t stream, const char **kernel_name) {
+    *kernel_name = "s6_scan_kernel";
+    S6Kp p{};
+    p.u = a.u; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log; p.B = a.B; p.C = a.C;
+    p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
+    p.batch = a.batch; p.L = a.L; p.Dm = a.d_inner; p.N = a.d_state;
+    p.ck = checkpoints;
+    const int mode = (int)(a.flags & 0x3u);
+    return a.bf16 ? launch_shape_save<uint16_t>(p, mode, stream) : launch_shape_save<float>(p, mode, stream);
+}
+
 }  // namespace ssm

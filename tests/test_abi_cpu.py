@@ -27,6 +27,10 @@ def lib():
     I, P, Z = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     L.ssm_s6_scan_fwd.argtypes = [P] * 10 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssm_s6_scan_grouped_fwd.argtypes = [P] * 10 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P]
+    L.ssm_s6_scan_fwd_save.argtypes = [P] * 11 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P]
+    L.ssm_s6_scan_bwd_saved.argtypes = [P] * 19 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
+    L.ssm_s6_scan_checkpoint_size.argtypes = [I] * 4
+    L.ssm_s6_scan_checkpoint_size.restype = Z
     L.ssd_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssd_cplx_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_uint32, P, Z, P]
     L.ssd_cplx_mimo_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 8 + [ctypes.c_uint32, P, Z, P]
@@ -60,7 +64,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M))
     names = {n for n in names if n.startswith(("ssm_", "ssd_"))}
     assert names == {"ssm_last_error", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_fwd",
-                     "ssm_s6_scan_grouped_fwd",
+                     "ssm_s6_scan_grouped_fwd", "ssm_s6_scan_fwd_save", "ssm_s6_scan_bwd_saved",
+                     "ssm_s6_scan_checkpoint_size",
                      "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd",
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
@@ -221,6 +226,33 @@ def test_s6_grouped_argument_checks(lib):
     assert _s6g(lib, flags=0x4) == INVALID
     assert _s6g(lib, y=None) == INVALID
     assert _s6g(lib, y=FAKE, u=FAKE, B=FAKE, flags=0x8) == INVALID
+
+
+def _fsave(lib, dims=(2, 40, 16, 16), ck=ctypes.c_void_p(0x7000000), y=ctypes.c_void_p(0x6000000), flags=0):
+    return lib.ssm_s6_scan_fwd_save(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, y, None, None, ck, *dims, 0, flags,
+                                    None)
+
+
+def _bsaved(lib, ck=ctypes.c_void_p(0xA000000), dims=(2, 40, 16, 16)):
+    # a one-byte workspace: a call that passes every other check is refused for it
+    o = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    return lib.ssm_s6_scan_bwd_saved(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, FAKE, None, ck, *o, *dims, 0, 0,
+                                     ctypes.c_void_p(0x9000000), 1, None)
+
+
+def test_s6_saved_argument_checks(lib):
+    # every case below fails before any launch (the pointers are fake)
+    assert lib.ssm_s6_scan_checkpoint_size(2, 40, 16, 16) == 2 * 3 * 16 * 16 * 4
+    assert lib.ssm_s6_scan_checkpoint_size(1, 16, 5, 3) == 1 * 1 * 5 * 3 * 4
+    assert lib.ssm_s6_scan_checkpoint_size(0, 16, 5, 3) == 0
+    assert _fsave(lib, ck=None) == INVALID and "checkpoints" in _err(lib)
+    assert _fsave(lib, dims=(2, 40, 16, 17)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _fsave(lib, flags=0x3) == INVALID
+    assert _fsave(lib, ck=ctypes.c_void_p(0x6000000)) == INVALID and "alias" in _err(lib)
+    assert _fsave(lib, ck=ctypes.c_void_p(0x7000004)) == UNSUPPORTED and "align" in _err(lib)
+    assert _bsaved(lib, ck=None) == INVALID and "checkpoints" in _err(lib)
+    # a workspace of 1 byte is refused before anything runs
+    assert _bsaved(lib) == WORKSPACE and "ssm_s6_scan_bwd_saved" in _err(lib)
 
 
 def _mimo(lib, dims=(2, 100, 4, 4, 64, 32, 2, 64), flags=0, ws=FAKE, wsb=1 << 40):
