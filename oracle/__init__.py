@@ -69,6 +69,8 @@ def _load():
     lib.oracle_cssd_fwd.argtypes = common + [I, I, I, I, I, I, ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_cssd_mimo_fwd.argtypes = [P] * 8 + [I] * 7 + [ctypes.c_uint32, P, I, P, P, ctypes.c_int]
     lib.oracle_s6_bwd.argtypes = [P] * 10 + [I, I, I, I, ctypes.c_uint32, I, I, I, I] + [P] * 8 + [ctypes.c_int]
+    lib.oracle_s6_grouped_bwd.argtypes = [P] * 10 + [I, I, I, I, I, ctypes.c_uint32, I, I, I, I] + [P] * 8 + \
+        [ctypes.c_int]
     lib.oracle_ssd_bwd.argtypes = [P] * 10 + [I] * 6 + [ctypes.c_uint32, P, I] + [P] * 8 + [ctypes.c_int]
     lib.oracle_trap_fwd.argtypes = [P] * 10 + [I] * 5 + [P, I, P, P, ctypes.c_int]
     lib.oracle_trap_rotate.argtypes = [P] * 5 + [I] * 5 + [P] * 3
@@ -320,6 +322,34 @@ def trap_bwd(x, k, q, dt, a, trap, D, h0, k_prev, x_prev, dy, dh_final=None, uni
                 ddt=r(out["ddt"], L).transpose(0, 2, 1).copy(), da=r(out["da"], L).transpose(0, 2, 1).copy(),
                 dtrap=r(out["dtrap"], L).transpose(0, 2, 1).copy(), dh0=r(out["dh0"], P, N),
                 dx_prev=r(out["dx_prev"], P), dk_prev=r(out["dk_prev"], N), dD=out["dD"].reshape(batch, H).sum(0))
+
+
+def s6_grouped_bwd(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, flags=BBAR_ZOH, b_range=None,
+                   d_range=None, nthreads=None):
+    """Gradients of s6_grouped_fwd (B, C (batch, L, G, N) per group of channels) in fp64.
+    Returns as s6_bwd, with dB, dC (nb, L, G, N) summed over each group's channels in the
+    unit range."""
+    u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final = map(
+        _f32, (u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final))
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    G = B.shape[2]
+    assert B.shape == (batch, L, G, N) and C.shape == B.shape and Dm % G == 0
+    b_lo, b_hi = b_range if b_range is not None else (0, batch)
+    d_lo, d_hi = d_range if d_range is not None else (0, Dm)
+    if not (0 <= b_lo < b_hi <= batch and 0 <= d_lo < d_hi <= Dm):
+        raise ValueError("unit range out of bounds")
+    nb, nd = b_hi - b_lo, d_hi - d_lo
+    out = dict(du=np.empty((nb, L, nd)), ddt=np.empty((nb, L, nd)), dB=np.empty((nb, L, G, N)),
+               dC=np.empty((nb, L, G, N)), dA_log=np.empty((nd, N)), dD=np.empty((nd,)),
+               ddt_bias=np.empty((nd,)), dh0=np.empty((nb, nd, N)))
+    _load().oracle_s6_grouped_bwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                  _ptr(h0), _ptr(dy), _ptr(dh_final), batch, L, Dm, N, G, flags,
+                                  b_lo, b_hi, d_lo, d_hi,
+                                  *(_ptr(out[k]) for k in ("du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias",
+                                                           "dh0")),
+                                  nthreads or default_threads())
+    return out
 
 
 def ssd_bwd(x, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, ngroups=1, flags=BBAR_DT,

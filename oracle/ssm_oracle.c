@@ -894,6 +894,7 @@ typedef struct {
     int64_t batch, L, Dm, N, b_lo, b_hi, d_lo, d_hi;
     uint32_t flags;
     double *du, *ddt, *dB, *dC, *dA_log, *dD, *ddtb, *dh0;   /* shared outputs */
+    int64_t G;   /* B, C per group of channels (batch, L, G, N), channel d in group d*G/Dm; 0: shared */
 } s6b_job;
 
 typedef struct {
@@ -905,6 +906,7 @@ typedef struct {
 static void s6b_unit(const s6b_job *j, s6b_arg *w, int64_t b, int64_t d)
 {
     const int64_t L = j->L, Dm = j->Dm, N = j->N;
+    const int64_t G = j->G > 0 ? j->G : 1, gi = d * G / Dm;   /* this channel's B, C row */
     const int64_t nd = j->d_hi - j->d_lo, bi = b - j->b_lo, di = d - j->d_lo;
     const int mode = (int)(j->flags & OR_BBAR_MASK);
     double *A = (double *)malloc(sizeof(double) * (size_t)N);
@@ -922,7 +924,7 @@ static void s6b_unit(const s6b_job *j, s6b_arg *w, int64_t b, int64_t d)
         const int64_t e = (b * L + t) * Dm + d;
         const double delta = sp((double)j->dt[e] + bias);
         const double uu = (double)j->u[e];
-        const float *Bt = j->B + (b * L + t) * N;
+        const float *Bt = j->B + ((b * L + t) * G + gi) * N;
         for (int64_t n = 0; n < N; ++n) {
             const double z = delta * A[n];
             double beta;
@@ -939,8 +941,8 @@ static void s6b_unit(const s6b_job *j, s6b_arg *w, int64_t b, int64_t d)
         const double delta = sp(x);
         const double uu = (double)j->u[e];
         const double dyv = (double)j->dy[e];
-        const float *Bt = j->B + (b * L + t) * N;
-        const float *Ct = j->C + (b * L + t) * N;
+        const float *Bt = j->B + ((b * L + t) * G + gi) * N;
+        const float *Ct = j->C + ((b * L + t) * G + gi) * N;
         double ddelta = 0.0, duv = Dd * dyv;
         for (int64_t n = 0; n < N; ++n) {
             const double z = delta * A[n];
@@ -952,8 +954,8 @@ static void s6b_unit(const s6b_job *j, s6b_arg *w, int64_t b, int64_t d)
             g[n] += (double)Ct[n] * dyv;
             const double hp = h[t * N + n], ht = h[(t + 1) * N + n];
             const double Bu = (double)Bt[n] * uu;
-            w->dC[(bi * L + t) * N + n] += dyv * ht;
-            w->dB[(bi * L + t) * N + n] += g[n] * beta * uu;
+            w->dC[((bi * L + t) * G + gi) * N + n] += dyv * ht;
+            w->dB[((bi * L + t) * G + gi) * N + n] += g[n] * beta * uu;
             duv += g[n] * beta * (double)Bt[n];
             ddelta += g[n] * (hp * A[n] * Ab + Bu * bD);
             w->dA[di * N + n] += g[n] * (hp * delta * Ab + Bu * bA);
@@ -982,21 +984,21 @@ static void *s6b_worker(void *p)
     return NULL;
 }
 
-void oracle_s6_bwd(const float *u, const float *dt, const float *dt_bias, const float *A_log,
-                   const float *B, const float *C, const float *D, const float *h0,
-                   const float *dy, const float *dh_final,
-                   int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, uint32_t flags,
-                   int64_t b_lo, int64_t b_hi, int64_t d_lo, int64_t d_hi,
-                   double *du, double *ddt, double *dB, double *dC, double *dA_log, double *dD,
-                   double *ddt_bias, double *dh0, int nthreads)
+static void s6_bwd_run(const float *u, const float *dt, const float *dt_bias, const float *A_log,
+                       const float *B, const float *C, const float *D, const float *h0,
+                       const float *dy, const float *dh_final,
+                       int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                       uint32_t flags, int64_t b_lo, int64_t b_hi, int64_t d_lo, int64_t d_hi,
+                       double *du, double *ddt, double *dB, double *dC, double *dA_log, double *dD,
+                       double *ddt_bias, double *dh0, int nthreads)
 {
     const int64_t nb = b_hi - b_lo, nd = d_hi - d_lo, N = d_state;
     s6b_job j = {u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, batch, L, d_inner, d_state,
-                 b_lo, b_hi, d_lo, d_hi, flags, du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0};
+                 b_lo, b_hi, d_lo, d_hi, flags, du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, ngroups};
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if ((int64_t)nthreads > nb * nd) nthreads = (int)(nb * nd > 0 ? nb * nd : 1);
-    const size_t nbc = (size_t)(nb * L * N);
+    const size_t nbc = (size_t)(nb * L * (ngroups > 0 ? ngroups : 1) * N);
     s6b_arg args[256];
     pthread_t th[256];
     for (int i = 0; i < nthreads; ++i) {
@@ -1026,6 +1028,33 @@ void oracle_s6_bwd(const float *u, const float *dt, const float *dt_bias, const 
     for (int64_t di = 0; di < nd; ++di)   /* dA -> dA_log: dA/dA_log = A */
         for (int64_t n = 0; n < N; ++n)
             dA_log[di * N + n] *= -exp((double)A_log[(d_lo + di) * N + n]);
+}
+
+
+void oracle_s6_bwd(const float *u, const float *dt, const float *dt_bias, const float *A_log,
+                   const float *B, const float *C, const float *D, const float *h0,
+                   const float *dy, const float *dh_final,
+                   int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, uint32_t flags,
+                   int64_t b_lo, int64_t b_hi, int64_t d_lo, int64_t d_hi,
+                   double *du, double *ddt, double *dB, double *dC, double *dA_log, double *dD,
+                   double *ddt_bias, double *dh0, int nthreads)
+{
+    s6_bwd_run(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, batch, L, d_inner, d_state, 0, flags,
+               b_lo, b_hi, d_lo, d_hi, du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, nthreads);
+}
+
+/* The backward of oracle_s6_grouped_fwd: dB, dC (nb, L, ngroups, N) summed over each
+ * group's channels in the unit range; the rest as oracle_s6_bwd. */
+void oracle_s6_grouped_bwd(const float *u, const float *dt, const float *dt_bias, const float *A_log,
+                           const float *B, const float *C, const float *D, const float *h0,
+                           const float *dy, const float *dh_final,
+                           int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                           uint32_t flags, int64_t b_lo, int64_t b_hi, int64_t d_lo, int64_t d_hi,
+                           double *du, double *ddt, double *dB, double *dC, double *dA_log, double *dD,
+                           double *ddt_bias, double *dh0, int nthreads)
+{
+    s6_bwd_run(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, batch, L, d_inner, d_state, ngroups, flags,
+               b_lo, b_hi, d_lo, d_hi, du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, nthreads);
 }
 
 /* elementary functions, exported so the tests can pin them on their own */
