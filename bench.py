@@ -89,8 +89,9 @@ def s6_bwd_model(d):
     dB, dC, dA_log, dD, ddt_bias, dh0 (and read dh_final); ops: one forward state
     update (to have h) plus the adjoint update per (b, t, d, n)."""
     B, L, D, N = d["batch"], d["L"], d["d_inner"], d["d_state"]
+    G = d.get("ngroups") or 1          # B, C and dB, dC per group of channels
     elems = B * L * D
-    bytes_ = elems * 4 * 5 + 4 * B * L * N * 4 + 2 * B * D * N * 4 + D * N * 8 + 3 * D * 4
+    bytes_ = elems * 4 * 5 + 4 * B * L * G * N * 4 + 2 * B * D * N * 4 + D * N * 8 + 3 * D * 4
     ops = elems * N * (S6_FLOPS_PER_UPDATE + S6_BWD_FLOPS_PER_UPDATE)
     return elems, bytes_, ops
 
@@ -204,13 +205,25 @@ def make_runner(name, dev):
         for r, t in enumerate(copies):
             dy, dhf = synth.s6_cotangents(d["batch"], d["L"], d["d_inner"], d["d_state"], seed=(r,))
             t["dy"], t["dhf"] = torch.from_numpy(dy).to(dev), torch.from_numpy(dhf).to(dev)
+        gsh = (d["ngroups"],) if d.get("ngroups") else ()
         shapes = dict(du=(d["batch"], d["L"], d["d_inner"]), ddt=(d["batch"], d["L"], d["d_inner"]),
-                      dB=(d["batch"], d["L"], d["d_state"]), dC=(d["batch"], d["L"], d["d_state"]),
+                      dB=(d["batch"], d["L"], *gsh, d["d_state"]), dC=(d["batch"], d["L"], *gsh, d["d_state"]),
                       dA_log=(d["d_inner"], d["d_state"]), dD=(d["d_inner"],),
                       ddt_bias=(d["d_inner"],), dh0=(d["batch"], d["d_inner"], d["d_state"]))
         out = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
         ws = torch.empty(lib.ssm_s6_scan_bwd_workspace_size(d["batch"], d["L"], d["d_inner"],
                                                             d["d_state"]), dtype=torch.uint8, device=dev)
+        if d.get("ngroups"):       # B, C per group of channels
+            ws = torch.empty(lib.ssm_s6_scan_grouped_bwd_workspace_size(d["batch"], d["L"], d["d_inner"],
+                                                                        d["d_state"], d["ngroups"]),
+                             dtype=torch.uint8, device=dev)
+
+            def step(i):
+                t = copies[i % N_ROTATE]
+                lib.ssm_s6_scan_grouped_bwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                            None, t["dy"], t["dhf"], out=out, workspace=ws)
+            w["kind"] = "s6_bwd"
+            return step, dims, w, ["s6_grouped_bwd_kernel", "s6_grouped_bwd_reduce"]
         if saved:      # each copy's states, saved once by the forward outside the timed region
             for t in copies:
                 t["ck"] = lib.ssm_s6_scan_fwd_save(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"],
@@ -514,7 +527,8 @@ def cpu_baseline_s6_bwd(name, n_rows=2):
     nthr = oracle.default_threads()
     n_rows = min(n_rows, d["batch"])
     t0 = time.perf_counter()
-    oracle.s6_bwd(**inp.arrays, dy=dy, dh_final=dhf, b_range=(0, n_rows), nthreads=nthr)
+    fn = oracle.s6_grouped_bwd if d.get("ngroups") else oracle.s6_bwd
+    fn(**inp.arrays, dy=dy, dh_final=dhf, b_range=(0, n_rows), nthreads=nthr)
     sec = time.perf_counter() - t0
     elems = n_rows * d["L"] * d["d_inner"]
     return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
@@ -730,6 +744,7 @@ def main():
                             ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
                             ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
                             ("s6_mamba1_bwd", 10), ("s6_mamba1_fwd_save", 10), ("s6_mamba1_bwd_saved", 10),
+                            ("s6_pc_mamba1_bwd", 5),
                             ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5)):
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)

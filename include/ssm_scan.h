@@ -221,6 +221,32 @@ int ssm_s6_scan_bwd(const void *u, const float *dt, const float *dt_bias, const 
                     ssm_dtype_t in_dtype, uint32_t flags,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------- S6 backward, B and C per channel group ----
+ * The backward of ssm_s6_scan_grouped_fwd: the chain rule of ssm_s6_scan_bwd
+ * with B, C read per group of channels (channel d: row d * ngroups / d_inner),
+ * and dB, dC (batch, L, ngroups, d_state) summed over each group's channels
+ * (per channel when ngroups = d_inner) [BF-S6 backward_scan, per channel].
+ * ngroups = 1 is ssm_s6_scan_bwd (and runs its kernels).
+ *
+ * Inputs, outputs and limits as ssm_s6_scan_bwd, with B, C, dB, dC of shape
+ * (batch, L, ngroups, d_state), d_inner % ngroups == 0 and, when ngroups > 1,
+ * d_inner * d_state < 2^26.
+ * Workspace: ssm_s6_scan_grouped_bwd_workspace_size() bytes, 16-byte aligned,
+ * caller-owned: the state entering every 16-step tile, per-batch-row partial
+ * sums and, when a group holds several channels, per-channel dB, dC shares
+ * (batch * L * d_inner * d_state fp32 each). */
+size_t ssm_s6_scan_grouped_bwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                                              int64_t ngroups);
+
+int ssm_s6_scan_grouped_bwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                            const void *B, const void *C, const float *D, const float *h0,
+                            const float *dy, const float *dh_final,
+                            float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                            float *dD, float *ddt_bias, float *dh0,
+                            int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                            ssm_dtype_t in_dtype, uint32_t flags,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------- S6 with saved states ----
  * The saved-state form of the pair above, for training: the backward needs
  * the state entering each 16-step tile, and either recomputes it in a first

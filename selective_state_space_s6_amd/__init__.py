@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "ssm_s6_scan_fwd", "ssm_s6_scan_grouped_fwd", "ssm_s6_scan_bwd", "ssm_s6_scan_fwd_save",
-    "ssm_s6_scan_bwd_saved", "ssm_s6_scan_checkpoint_size", "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd", "ssd_chunk_scan_fwd",
+    "ssm_s6_scan_bwd_saved", "ssm_s6_scan_checkpoint_size", "ssm_s6_scan_grouped_bwd",
+    "ssm_s6_scan_grouped_bwd_workspace_size", "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd", "ssd_chunk_scan_fwd",
     "ssd_chunk_scan_bwd",
     "ssd_cplx_chunk_scan_fwd", "ssd_trap_chunk_scan_fwd", "ssm_s6_scan_fwd_workspace_size",
     "ssm_s6_scan_bwd_workspace_size", "ssd_trap_chunk_scan_fwd_workspace_size",
@@ -61,6 +62,10 @@ _lib.ssm_s6_scan_bwd_saved.argtypes = [_P] * 19 + [_I] * 4 + [ctypes.c_int, ctyp
 _lib.ssm_s6_scan_bwd_saved.restype = ctypes.c_int
 _lib.ssm_s6_scan_fwd_save.argtypes = [_P] * 11 + [_I] * 4 + [ctypes.c_int, ctypes.c_uint32, _P]
 _lib.ssm_s6_scan_fwd_save.restype = ctypes.c_int
+_lib.ssm_s6_scan_grouped_bwd.argtypes = [_P] * 18 + [_I] * 5 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
+_lib.ssm_s6_scan_grouped_bwd.restype = ctypes.c_int
+_lib.ssm_s6_scan_grouped_bwd_workspace_size.argtypes = [_I] * 5
+_lib.ssm_s6_scan_grouped_bwd_workspace_size.restype = _Z
 _lib.ssm_s6_scan_checkpoint_size.argtypes = [_I] * 4
 _lib.ssm_s6_scan_checkpoint_size.restype = _Z
 _lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
@@ -304,6 +309,51 @@ def ssm_causal_conv1d_fwd(x, w, bias=None, state_in=None, *, silu=False, y=None,
 
 
 _S6_GRADS = ("du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")
+
+
+def ssm_s6_scan_grouped_bwd_workspace_size(batch, L, d_inner, d_state, ngroups) -> int:
+    return int(_lib.ssm_s6_scan_grouped_bwd_workspace_size(batch, L, d_inner, d_state, ngroups))
+
+
+def ssm_s6_scan_grouped_bwd(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, *, flags=SSM_BBAR_ZOH,
+                            out=None, workspace=None):
+    """Gradients of ssm_s6_scan_grouped_fwd.  Inputs as there, plus dy (batch, L, d_inner) fp32 and
+    dh_final (batch, d_inner, d_state) fp32 or None.  Returns a dict as ssm_s6_scan_bwd, with
+    dB, dC (batch, L, ngroups, d_state)."""
+    dev = u.device
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    G = B.shape[2]
+    dty = u.dtype
+    _req(u, "u", dty, (batch, L, Dm), dev)
+    _req(dt, "dt", torch.float32, (batch, L, Dm), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (Dm,), dev)
+    _req(A_log, "A_log", torch.float32, (Dm, N), dev)
+    _req(B, "B", dty, (batch, L, G, N), dev)
+    _req(C, "C", dty, (batch, L, G, N), dev)
+    _opt(D, "D", torch.float32, (Dm,), dev)
+    _opt(h0, "h0", torch.float32, (batch, Dm, N), dev)
+    _req(dy, "dy", torch.float32, (batch, L, Dm), dev)
+    _opt(dh_final, "dh_final", torch.float32, (batch, Dm, N), dev)
+    shapes = dict(du=(batch, L, Dm), ddt=(batch, L, Dm), dB=(batch, L, G, N), dC=(batch, L, G, N),
+                  dA_log=(Dm, N), dD=(Dm,), ddt_bias=(Dm,), dh0=(batch, Dm, N))
+    g = dict(out or {})
+    for k in _S6_GRADS:
+        if g.get(k) is None:
+            g[k] = torch.empty(shapes[k], dtype=torch.float32, device=dev)
+        _req(g[k], k, torch.float32, shapes[k], dev)
+    need = ssm_s6_scan_grouped_bwd_workspace_size(batch, L, Dm, N, G)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    rc = _lib.ssm_s6_scan_grouped_bwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                                      *(_ptr(g[k]) for k in _S6_GRADS), batch, L, Dm, N, G, _in_dtype(u),
+                                      flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(dev))
+    _check(rc)
+    return g
 
 
 def ssm_s6_scan_checkpoint_size(batch, L, d_inner, d_state) -> int:

@@ -246,8 +246,8 @@ size_t ssm_s6_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner,
     return ssm::s6_bwd_workspace_bytes(batch, L, d_inner, d_state);
 }
 
-static int s6_bwd_call(const char *E, const void *u, const float *dt, const float *dt_bias, const float *A_log,
-                       const void *B, const void *C, const float *D, const float *h0,
+static int s6_bwd_call(const char *E, int64_t ngroups, const void *u, const float *dt, const float *dt_bias,
+                       const float *A_log, const void *B, const void *C, const float *D, const float *h0,
                        const float *dy, const float *dh_final, const float *checkpoints,
                        float *du, float *ddt, float *dB, float *dC, float *dA_log,
                        float *dD, float *ddt_bias, float *dh0,
@@ -259,6 +259,10 @@ static int s6_bwd_call(const char *E, const void *u, const float *dt, const floa
     REQUIRE_PTR(E, du); REQUIRE_PTR(E, ddt); REQUIRE_PTR(E, dB); REQUIRE_PTR(E, dC);
     REQUIRE_PTR(E, dA_log);
     REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, d_inner); REQUIRE_POS(E, d_state);
+    REQUIRE_POS(E, ngroups);
+    if (d_inner % ngroups != 0)
+        return fail(SSM_ERR_INVALID_ARG, "%s: d_inner %lld is not a multiple of ngroups %lld", E,
+                    (long long)d_inner, (long long)ngroups);
     if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
         return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
     if ((flags & ~0x3u) != 0 || (flags & 0x3u) == 0x3u)
@@ -266,7 +270,9 @@ static int s6_bwd_call(const char *E, const void *u, const float *dt, const floa
     if (d_state > SSM_S6_BWD_MAX_D_STATE)
         return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld > %d", E, (long long)d_state,
                     SSM_S6_BWD_MAX_D_STATE);
-    if (too_big(batch, L, d_inner, 1) || too_big(batch, (L + 15) / 16, d_inner, d_state) ||
+    if ((ngroups > 1 && (too_big(batch, L, d_inner, d_state) ||   // the per-channel dB, dC shares
+                         d_inner * d_state >= (1LL << 26))) ||     // the grouped kernel's 32-bit offsets
+        too_big(batch, L, d_inner, 1) || too_big(batch, (L + 15) / 16, d_inner, d_state) ||
         batch * ((d_inner + 15) / 16) > 0x7fffffffLL || L > 0x7fffffefLL || d_inner >= (1LL << 25))
         return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
     REQUIRE_ALIGN(E, u); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
@@ -285,7 +291,7 @@ static int s6_bwd_call(const char *E, const void *u, const float *dt, const floa
         for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
             if (outs[i] == outs[j]) return fail(SSM_ERR_INVALID_ARG, "%s: two outputs alias", E);
     }
-    const size_t need = ssm::s6_bwd_workspace_bytes(batch, L, d_inner, d_state);
+    const size_t need = ssm::s6_grouped_bwd_workspace_bytes(batch, L, d_inner, d_state, ngroups);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -293,7 +299,7 @@ static int s6_bwd_call(const char *E, const void *u, const float *dt, const floa
                      du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0,
                      batch, L, d_inner, d_state, in_dtype == SSM_BF16, flags, workspace, checkpoints};
     const char *kn = "s6_bwd";
-    return launched(E, ssm::launch_s6_bwd(a, stream, &kn), kn);
+    return launched(E, ssm::launch_s6_grouped_bwd(a, ngroups, stream, &kn), kn);
 }
 
 
@@ -305,9 +311,28 @@ int ssm_s6_scan_bwd(const void *u, const float *dt, const float *dt_bias, const 
                     int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
                     ssm_dtype_t in_dtype, uint32_t flags,
                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return s6_bwd_call("ssm_s6_scan_bwd", u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, nullptr,
+    return s6_bwd_call("ssm_s6_scan_bwd", 1, u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, nullptr,
                        du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, batch, L, d_inner, d_state, in_dtype, flags,
                        workspace, workspace_bytes, stream);
+}
+
+size_t ssm_s6_scan_grouped_bwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                                              int64_t ngroups) {
+    if (batch <= 0 || L <= 0 || d_inner <= 0 || d_state <= 0 || ngroups <= 0) return 0;
+    return ssm::s6_grouped_bwd_workspace_bytes(batch, L, d_inner, d_state, ngroups);
+}
+
+int ssm_s6_scan_grouped_bwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                            const void *B, const void *C, const float *D, const float *h0,
+                            const float *dy, const float *dh_final,
+                            float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                            float *dD, float *ddt_bias, float *dh0,
+                            int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                            ssm_dtype_t in_dtype, uint32_t flags,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return s6_bwd_call("ssm_s6_scan_grouped_bwd", ngroups, u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final,
+                       nullptr, du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, batch, L, d_inner, d_state, in_dtype,
+                       flags, workspace, workspace_bytes, stream);
 }
 
 int ssm_s6_scan_bwd_saved(const void *u, const float *dt, const float *dt_bias, const float *A_log,
@@ -320,7 +345,7 @@ int ssm_s6_scan_bwd_saved(const void *u, const float *dt, const float *dt_bias, 
                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
     const char *E = "ssm_s6_scan_bwd_saved";
     REQUIRE_PTR(E, checkpoints);
-    return s6_bwd_call(E, u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, checkpoints,
+    return s6_bwd_call(E, 1, u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, checkpoints,
                        du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, batch, L, d_inner, d_state, in_dtype, flags,
                        workspace, workspace_bytes, stream);
 }

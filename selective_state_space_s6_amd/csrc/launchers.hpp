@@ -54,6 +54,9 @@ struct S6BwdArgs {
 };
 size_t s6_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state);
 hipError_t launch_s6_bwd(const S6BwdArgs &a, hipStream_t stream, const char **kernel_name);
+// the backward of launch_s6_grouped: dB, dC (batch, L, ngroups, d_state); d_state <= 16
+size_t s6_grouped_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups);
+hipError_t launch_s6_grouped_bwd(const S6BwdArgs &a, int64_t ngroups, hipStream_t stream, const char **kernel_name);
 
 struct SsdArgs {
     const void *x; const float *dt; const float *dt_bias; const float *A_log;

@@ -29,6 +29,9 @@ def lib():
     L.ssm_s6_scan_grouped_fwd.argtypes = [P] * 10 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P]
     L.ssm_s6_scan_fwd_save.argtypes = [P] * 11 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P]
     L.ssm_s6_scan_bwd_saved.argtypes = [P] * 19 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
+    L.ssm_s6_scan_grouped_bwd.argtypes = [P] * 18 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
+    L.ssm_s6_scan_grouped_bwd_workspace_size.argtypes = [I] * 5
+    L.ssm_s6_scan_grouped_bwd_workspace_size.restype = Z
     L.ssm_s6_scan_checkpoint_size.argtypes = [I] * 4
     L.ssm_s6_scan_checkpoint_size.restype = Z
     L.ssd_chunk_scan_fwd.argtypes = [P] * 10 + [I] * 7 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
@@ -65,7 +68,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = {n for n in names if n.startswith(("ssm_", "ssd_"))}
     assert names == {"ssm_last_error", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_fwd",
                      "ssm_s6_scan_grouped_fwd", "ssm_s6_scan_fwd_save", "ssm_s6_scan_bwd_saved",
-                     "ssm_s6_scan_checkpoint_size",
+                     "ssm_s6_scan_checkpoint_size", "ssm_s6_scan_grouped_bwd",
+                     "ssm_s6_scan_grouped_bwd_workspace_size",
                      "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd",
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
                      "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
@@ -253,6 +257,27 @@ def test_s6_saved_argument_checks(lib):
     assert _bsaved(lib, ck=None) == INVALID and "checkpoints" in _err(lib)
     # a workspace of 1 byte is refused before anything runs
     assert _bsaved(lib) == WORKSPACE and "ssm_s6_scan_bwd_saved" in _err(lib)
+
+
+def _gbwd(lib, dims=(2, 40, 32, 16, 32), wsb=1, dtype=0):
+    o = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    return lib.ssm_s6_scan_grouped_bwd(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, FAKE, None, *o, *dims, dtype,
+                                       0, ctypes.c_void_p(0x9000000), wsb, None)
+
+
+def test_s6_grouped_bwd_argument_checks(lib):
+    # every case below fails before any launch (the pointers are fake)
+    assert _gbwd(lib, dims=(2, 40, 32, 16, 5)) == INVALID and "multiple" in _err(lib)
+    assert _gbwd(lib, dims=(2, 40, 32, 17, 32)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _gbwd(lib, dims=(2, 40, 32, 16, 0)) == INVALID
+    assert _gbwd(lib, dtype=5) == INVALID
+    assert _gbwd(lib) == WORKSPACE and "ssm_s6_scan_grouped_bwd" in _err(lib)
+    # per channel: checkpoints and partials; groups of several channels add the shares
+    pc = lib.ssm_s6_scan_grouped_bwd_workspace_size(2, 40, 32, 16, 32)
+    grp = lib.ssm_s6_scan_grouped_bwd_workspace_size(2, 40, 32, 16, 8)
+    assert pc >= 2 * 3 * 32 * 16 * 4 and grp >= pc + 2 * 2 * 40 * 32 * 16 * 4
+    assert lib.ssm_s6_scan_grouped_bwd_workspace_size(2, 40, 32, 16, 1) == lib.ssm_s6_scan_bwd_workspace_size(
+        2, 40, 32, 16)
 
 
 def _mimo(lib, dims=(2, 100, 4, 4, 64, 32, 2, 64), flags=0, ws=FAKE, wsb=1 << 40):
