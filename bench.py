@@ -56,7 +56,8 @@ def log(msg):
 
 
 def s6_model(d):
-    """Algorithmic bytes and operations of one S6 call."""
+    """Algorithmic bytes and operations of one S6 call: u, dt read and y written per
+    (b, t, d); B, C read per (b, t, n); A_log, D, dt_bias and the final state once."""
     B, L, D, N = d["batch"], d["L"], d["d_inner"], d["d_state"]
     elems = B * L * D
     isz = 4

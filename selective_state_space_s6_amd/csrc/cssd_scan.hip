@@ -174,7 +174,9 @@ struct Stager {
     static constexpr int PX = NX / NTHR;
     static_assert(NX % NTHR == 0, "x pieces must divide over the group");
 
-    float4 rB[PBC], rC[PBC], rX[PX];
+    // clang vector types: arrays of HIP's float4 (a class holding a union) stayed in
+    // per-lane scratch memory, which also forced a wait on each prefetch
+    f32x4 rB[PBC], rC[PBC], rX[PX];
     float rdt;
     const float *Bb, *Cb, *Xb, *Db;
     uint32_t oBC[PBC], oX[PX];   // per-piece offsets (floats) at chunk row 0
@@ -221,24 +223,24 @@ struct Stager {
         if (t0 + kT <= L) {
 #pragma unroll
             for (int i = 0; i < PBC; ++i) {
-                rB[i] = *reinterpret_cast<const float4 *>(Bu + oBC[i]);
-                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const float4 *>(Cu + oBC[i]);
+                rB[i] = *reinterpret_cast<const f32x4 *>(Bu + oBC[i]);
+                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const f32x4 *>(Cu + oBC[i]);
             }
 #pragma unroll
-            for (int i = 0; i < PX; ++i) rX[i] = *reinterpret_cast<const float4 *>(Xu + oX[i]);
+            for (int i = 0; i < PX; ++i) rX[i] = *reinterpret_cast<const f32x4 *>(Xu + oX[i]);
             rdt = Du[(uint32_t)((sD >> lgR) * H)];
         } else {
             const int last = (int)(L - 1 - t0);   // last valid step of the chunk
 #pragma unroll
             for (int i = 0; i < PBC; ++i) {
                 const uint32_t o = oBC[i] - (uint32_t)((rBC[i] - min(rBC[i], last)) * rowBC);
-                rB[i] = *reinterpret_cast<const float4 *>(Bu + o);
-                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const float4 *>(Cu + o);
+                rB[i] = *reinterpret_cast<const f32x4 *>(Bu + o);
+                if constexpr (WITH_C) rC[i] = *reinterpret_cast<const f32x4 *>(Cu + o);
             }
 #pragma unroll
             for (int i = 0; i < PX; ++i) {
                 const uint32_t o = oX[i] - (uint32_t)((rXr[i] - min(rXr[i], last)) * rowX);
-                rX[i] = *reinterpret_cast<const float4 *>(Xu + o);
+                rX[i] = *reinterpret_cast<const f32x4 *>(Xu + o);
             }
             rdt = Du[(uint32_t)((min(sD, last) >> lgR) * H)];
         }
@@ -247,12 +249,12 @@ struct Stager {
 #pragma unroll
         for (int i = 0; i < PBC; ++i) {
             if (PBC * NTHR == NBC || vBC[i]) {
-                *reinterpret_cast<float4 *>(&Bs[lBC[i]]) = rB[i];
-                if constexpr (WITH_C) *reinterpret_cast<float4 *>(&Cs[lBC[i]]) = rC[i];
+                *reinterpret_cast<f32x4 *>(&Bs[lBC[i]]) = rB[i];
+                if constexpr (WITH_C) *reinterpret_cast<f32x4 *>(&Cs[lBC[i]]) = rC[i];
             }
         }
 #pragma unroll
-        for (int i = 0; i < PX; ++i) *reinterpret_cast<float4 *>(&Xs[lX[i]]) = rX[i];
+        for (int i = 0; i < PX; ++i) *reinterpret_cast<f32x4 *>(&Xs[lX[i]]) = rX[i];
     }
 };
 
