@@ -219,10 +219,21 @@ def make_runner(name, dev):
                                                                         d["d_state"], d["ngroups"]),
                              dtype=torch.uint8, device=dev)
 
-            def step(i):
-                t = copies[i % N_ROTATE]
-                lib.ssm_s6_scan_grouped_bwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
-                                            None, t["dy"], t["dhf"], out=out, workspace=ws)
+            if saved:  # each copy's states, saved once by the forward outside the timed region
+                for t in copies:
+                    t["ck"] = lib.ssm_s6_scan_grouped_fwd_save(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"],
+                                                               t["C"], t["D"], None)[2]
+
+                def step(i):
+                    t = copies[i % N_ROTATE]
+                    lib.ssm_s6_scan_grouped_bwd_saved(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"],
+                                                      t["D"], None, t["dy"], t["dhf"], t["ck"], out=out,
+                                                      workspace=ws)
+            else:
+                def step(i):
+                    t = copies[i % N_ROTATE]
+                    lib.ssm_s6_scan_grouped_bwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
+                                                None, t["dy"], t["dhf"], out=out, workspace=ws)
             w["kind"] = "s6_bwd"
             return step, dims, w, ["s6_grouped_bwd_kernel", "s6_grouped_bwd_reduce"]
         if saved:      # each copy's states, saved once by the forward outside the timed region
@@ -247,6 +258,14 @@ def make_runner(name, dev):
         hf = torch.empty((dims["batch"], dims["d_inner"], dims["d_state"]), dtype=torch.float32, device=dev)
         ck = torch.empty((dims["batch"], (dims["L"] + 15) // 16, dims["d_inner"], dims["d_state"]),
                          dtype=torch.float32, device=dev)
+
+        if dims.get("ngroups"):    # B, C per group of channels
+            def step(i):
+                t = copies[i % N_ROTATE]
+                lib.ssm_s6_scan_grouped_fwd_save(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"],
+                                                 t["D"], None, y=y, h_final=hf, checkpoints=ck)
+            w["kind"] = "s6_pc_save"
+            return step, dims, w, ["s6_grouped_kernel"]
 
         def step(i):
             t = copies[i % N_ROTATE]
@@ -650,8 +669,8 @@ def measure(name, dev, steps, warmup):
         elems, bytes_, ops = s6_layer_model(dims)
     elif kind == "s6_pc":
         elems, bytes_, ops = s6_pc_model(dims)
-    elif kind == "s6_save":      # the forward plus the saved states it writes
-        elems, bytes_, ops = s6_model(dims)
+    elif kind in ("s6_save", "s6_pc_save"):      # the forward plus the saved states it writes
+        elems, bytes_, ops = s6_model(dims) if kind == "s6_save" else s6_pc_model(dims)
         bytes_ += dims["batch"] * (-(-dims["L"] // 16)) * dims["d_inner"] * dims["d_state"] * 4
     elif kind == "s6_bwd":
         elems, bytes_, ops = s6_bwd_model(dims)
@@ -745,6 +764,7 @@ def main():
                             ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
                             ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
                             ("s6_mamba1_bwd", 10), ("s6_mamba1_fwd_save", 10), ("s6_mamba1_bwd_saved", 10),
+                            ("s6_pc_mamba1_fwd_save", 5), ("s6_pc_mamba1_bwd_saved", 5),
                             ("s6_pc_mamba1_bwd", 5),
                             ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5)):
             log(f"[bench] secondary {name}")
@@ -789,7 +809,7 @@ def main():
             if base.endswith(suffix):
                 base = base[: -len(suffix)]
                 break
-        if kind in ("s6", "s6_pc", "s6_save"):
+        if kind in ("s6", "s6_pc", "s6_save", "s6_pc_save"):
             out["cpu_baseline"] = cpu_baseline_s6(base)
         elif kind == "s6_bwd":
             out["cpu_baseline"] = cpu_baseline_s6_bwd(base)

@@ -283,6 +283,28 @@ int ssm_s6_scan_bwd_saved(const void *u, const float *dt, const float *dt_bias, 
                           ssm_dtype_t in_dtype, uint32_t flags,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same pair for S6 with B, C per group of channels (the inputs and
+ * outputs of ssm_s6_scan_grouped_fwd / ssm_s6_scan_grouped_bwd, d_inner a
+ * multiple of ngroups), for the same training use: the forward also writes
+ * checkpoints in the layout above, and the backward reads them instead of
+ * recomputing the states.  ngroups = 1 is the pair above.  Limits: d_state <=
+ * SSM_S6_BWD_MAX_D_STATE; the backward's workspace is
+ * ssm_s6_scan_grouped_bwd_workspace_size() (its checkpoint region unused). */
+int ssm_s6_scan_grouped_fwd_save(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                                 const void *B, const void *C, const float *D, float *y,
+                                 const float *h0, float *h_final, float *checkpoints,
+                                 int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                                 ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream);
+
+int ssm_s6_scan_grouped_bwd_saved(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                                  const void *B, const void *C, const float *D, const float *h0,
+                                  const float *dy, const float *dh_final, const float *checkpoints,
+                                  float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                                  float *dD, float *ddt_bias, float *dh0,
+                                  int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                                  ssm_dtype_t in_dtype, uint32_t flags,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------- SSD ----
  * Mamba-2 state-space dual scan with a scalar A per head [BF-SSD header and
  * ssd_chunk_forward; RS-M3 F6 K2-K5]:

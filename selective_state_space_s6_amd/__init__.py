@@ -67,6 +67,8 @@ _lib.ssm_s6_scan_grouped_bwd.restype = ctypes.c_int
 _lib.ssm_s6_scan_grouped_bwd_workspace_size.argtypes = [_I] * 5
 _lib.ssm_s6_scan_grouped_bwd_workspace_size.restype = _Z
 _lib.ssm_s6_scan_checkpoint_size.argtypes = [_I] * 4
+_lib.ssm_s6_scan_grouped_fwd_save.argtypes = [_P] * 11 + [_I] * 5 + [ctypes.c_int, ctypes.c_uint32, _P]
+_lib.ssm_s6_scan_grouped_bwd_saved.argtypes = [_P] * 19 + [_I] * 5 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
 _lib.ssm_s6_scan_checkpoint_size.restype = _Z
 _lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_chunk_scan_fwd_workspace_size.restype = _Z
@@ -316,7 +318,7 @@ def ssm_s6_scan_grouped_bwd_workspace_size(batch, L, d_inner, d_state, ngroups) 
 
 
 def ssm_s6_scan_grouped_bwd(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=None, *, flags=SSM_BBAR_ZOH,
-                            out=None, workspace=None):
+                            out=None, workspace=None, _checkpoints=None):
     """Gradients of ssm_s6_scan_grouped_fwd.  Inputs as there, plus dy (batch, L, d_inner) fp32 and
     dh_final (batch, d_inner, d_state) fp32 or None.  Returns a dict as ssm_s6_scan_bwd, with
     dB, dC (batch, L, ngroups, d_state)."""
@@ -347,13 +349,66 @@ def ssm_s6_scan_grouped_bwd(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final=Non
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the inputs' device")
-    rc = _lib.ssm_s6_scan_grouped_bwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
-                                      _ptr(D), _ptr(h0), _ptr(dy), _ptr(dh_final),
-                                      *(_ptr(g[k]) for k in _S6_GRADS), batch, L, Dm, N, G, _in_dtype(u),
-                                      flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                      _stream(dev))
+    if _checkpoints is not None:
+        _req(_checkpoints, "checkpoints", torch.float32, (batch, (L + 15) // 16, Dm, N), dev)
+        rc = _lib.ssm_s6_scan_grouped_bwd_saved(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                                _ptr(D), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(_checkpoints),
+                                                *(_ptr(g[k]) for k in _S6_GRADS), batch, L, Dm, N, G,
+                                                _in_dtype(u), flags, _ptr(workspace),
+                                                workspace.numel() * workspace.element_size(), _stream(dev))
+    else:
+        rc = _lib.ssm_s6_scan_grouped_bwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                          _ptr(D), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                                          *(_ptr(g[k]) for k in _S6_GRADS), batch, L, Dm, N, G, _in_dtype(u),
+                                          flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(dev))
     _check(rc)
     return g
+
+
+def ssm_s6_scan_grouped_fwd_save(u, dt, dt_bias, A_log, B, C, D, h0=None, *, flags=SSM_BBAR_ZOH, y=None,
+                                 h_final=None, checkpoints=None):
+    """ssm_s6_scan_grouped_fwd that also saves the state entering every 16-step tile for
+    the backward (d_state <= 16).  Returns (y, h_final, checkpoints); checkpoints is
+    (batch, ceil(L/16), d_inner, d_state) fp32."""
+    dev = u.device
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    G = B.shape[2]
+    dty = u.dtype
+    _req(u, "u", dty, (batch, L, Dm), dev)
+    _req(dt, "dt", torch.float32, (batch, L, Dm), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (Dm,), dev)
+    _req(A_log, "A_log", torch.float32, (Dm, N), dev)
+    _req(B, "B", dty, (batch, L, G, N), dev)
+    _req(C, "C", dty, (batch, L, G, N), dev)
+    _opt(D, "D", torch.float32, (Dm,), dev)
+    _opt(h0, "h0", torch.float32, (batch, Dm, N), dev)
+    if y is None:
+        y = torch.empty((batch, L, Dm), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, (batch, L, Dm), dev)
+    if h_final is None:
+        h_final = torch.empty((batch, Dm, N), dtype=torch.float32, device=dev)
+    _req(h_final, "h_final", torch.float32, (batch, Dm, N), dev)
+    ck_shape = (batch, (L + 15) // 16, Dm, N)
+    if checkpoints is None:
+        checkpoints = torch.empty(ck_shape, dtype=torch.float32, device=dev)
+    _req(checkpoints, "checkpoints", torch.float32, ck_shape, dev)
+    rc = _lib.ssm_s6_scan_grouped_fwd_save(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                           _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), _ptr(checkpoints),
+                                           batch, L, Dm, N, G, _in_dtype(u), flags, _stream(dev))
+    _check(rc)
+    return y, h_final, checkpoints
+
+
+def ssm_s6_scan_grouped_bwd_saved(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, checkpoints, *,
+                                  flags=SSM_BBAR_ZOH, out=None, workspace=None):
+    """ssm_s6_scan_grouped_bwd reading the states ssm_s6_scan_grouped_fwd_save wrote (same
+    inputs as that forward) instead of recomputing them."""
+    if checkpoints is None:
+        raise ValueError("checkpoints are required")
+    return ssm_s6_scan_grouped_bwd(u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, flags=flags, out=out,
+                                   workspace=workspace, _checkpoints=checkpoints)
 
 
 def ssm_s6_scan_checkpoint_size(batch, L, d_inner, d_state) -> int:

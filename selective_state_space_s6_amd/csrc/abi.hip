@@ -97,15 +97,18 @@ size_t ssm_s6_scan_checkpoint_size(int64_t batch, int64_t L, int64_t d_inner, in
     return (size_t)(batch * ((L + 15) / 16) * d_inner * d_state) * sizeof(float);
 }
 
-int ssm_s6_scan_fwd_save(const void *u, const float *dt, const float *dt_bias, const float *A_log,
-                         const void *B, const void *C, const float *D, float *y,
-                         const float *h0, float *h_final, float *checkpoints,
-                         int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
-                         ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream) {
-    const char *E = "ssm_s6_scan_fwd_save";
+static int s6_fwd_save_call(const char *E, int64_t ngroups, const void *u, const float *dt, const float *dt_bias,
+                            const float *A_log, const void *B, const void *C, const float *D, float *y,
+                            const float *h0, float *h_final, float *checkpoints,
+                            int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                            ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream) {
     REQUIRE_PTR(E, u); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
     REQUIRE_PTR(E, C); REQUIRE_PTR(E, y); REQUIRE_PTR(E, checkpoints);
     REQUIRE_POS(E, batch); REQUIRE_POS(E, L); REQUIRE_POS(E, d_inner); REQUIRE_POS(E, d_state);
+    REQUIRE_POS(E, ngroups);
+    if (d_inner % ngroups != 0)
+        return fail(SSM_ERR_INVALID_ARG, "%s: d_inner %lld is not a multiple of ngroups %lld", E,
+                    (long long)d_inner, (long long)ngroups);
     if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
         return fail(SSM_ERR_INVALID_ARG, "%s: in_dtype %d is not SSM_F32 or SSM_BF16", E, (int)in_dtype);
     if ((flags & ~0x3u) != 0 || (flags & 0x3u) == 0x3u)
@@ -114,7 +117,7 @@ int ssm_s6_scan_fwd_save(const void *u, const float *dt, const float *dt_bias, c
         return fail(SSM_ERR_UNSUPPORTED, "%s: d_state %lld > %d (the backward's limit)", E, (long long)d_state,
                     SSM_S6_BWD_MAX_D_STATE);
     if (too_big(batch, L, d_inner, 1) || too_big(batch, (L + 15) / 16, d_inner, d_state) ||
-        batch * ((d_inner + 255) / 16) > 0x7fffffffLL)
+        too_big(batch, L, ngroups, d_state) || batch * ((d_inner + 255) / 16) > 0x7fffffffLL)
         return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
     REQUIRE_ALIGN(E, u); REQUIRE_ALIGN(E, dt); REQUIRE_ALIGN(E, dt_bias); REQUIRE_ALIGN(E, A_log);
     REQUIRE_ALIGN(E, B); REQUIRE_ALIGN(E, C); REQUIRE_ALIGN(E, D); REQUIRE_ALIGN(E, y);
@@ -129,7 +132,25 @@ int ssm_s6_scan_fwd_save(const void *u, const float *dt, const float *dt_bias, c
     ssm::S6Args a{u, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, d_inner, d_state,
                   in_dtype == SSM_BF16, flags};
     const char *kn = "s6_save";
-    return launched(E, ssm::launch_s6_save(a, checkpoints, stream, &kn), kn);
+    return launched(E, ssm::launch_s6_grouped_save(a, ngroups, checkpoints, stream, &kn), kn);
+}
+
+int ssm_s6_scan_fwd_save(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                         const void *B, const void *C, const float *D, float *y,
+                         const float *h0, float *h_final, float *checkpoints,
+                         int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                         ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream) {
+    return s6_fwd_save_call("ssm_s6_scan_fwd_save", 1, u, dt, dt_bias, A_log, B, C, D, y, h0, h_final,
+                            checkpoints, batch, L, d_inner, d_state, in_dtype, flags, stream);
+}
+
+int ssm_s6_scan_grouped_fwd_save(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                                 const void *B, const void *C, const float *D, float *y,
+                                 const float *h0, float *h_final, float *checkpoints,
+                                 int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                                 ssm_dtype_t in_dtype, uint32_t flags, hipStream_t stream) {
+    return s6_fwd_save_call("ssm_s6_scan_grouped_fwd_save", ngroups, u, dt, dt_bias, A_log, B, C, D, y, h0,
+                            h_final, checkpoints, batch, L, d_inner, d_state, in_dtype, flags, stream);
 }
 
 int ssm_s6_scan_grouped_fwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
@@ -333,6 +354,21 @@ int ssm_s6_scan_grouped_bwd(const void *u, const float *dt, const float *dt_bias
     return s6_bwd_call("ssm_s6_scan_grouped_bwd", ngroups, u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final,
                        nullptr, du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, batch, L, d_inner, d_state, in_dtype,
                        flags, workspace, workspace_bytes, stream);
+}
+
+int ssm_s6_scan_grouped_bwd_saved(const void *u, const float *dt, const float *dt_bias, const float *A_log,
+                                  const void *B, const void *C, const float *D, const float *h0,
+                                  const float *dy, const float *dh_final, const float *checkpoints,
+                                  float *du, float *ddt, float *dB, float *dC, float *dA_log,
+                                  float *dD, float *ddt_bias, float *dh0,
+                                  int64_t batch, int64_t L, int64_t d_inner, int64_t d_state, int64_t ngroups,
+                                  ssm_dtype_t in_dtype, uint32_t flags,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *E = "ssm_s6_scan_grouped_bwd_saved";
+    REQUIRE_PTR(E, checkpoints);
+    return s6_bwd_call(E, ngroups, u, dt, dt_bias, A_log, B, C, D, h0, dy, dh_final, checkpoints,
+                       du, ddt, dB, dC, dA_log, dD, ddt_bias, dh0, batch, L, d_inner, d_state, in_dtype, flags,
+                       workspace, workspace_bytes, stream);
 }
 
 int ssm_s6_scan_bwd_saved(const void *u, const float *dt, const float *dt_bias, const float *A_log,

@@ -20,6 +20,10 @@ hipError_t launch_s6_save(const S6Args &a, float *checkpoints, hipStream_t strea
 // B, C (batch, L, ngroups, d_state): channel d reads group d * ngroups / d_inner
 // (one group goes to launch_s6)
 hipError_t launch_s6_grouped(const S6Args &a, int64_t ngroups, hipStream_t stream, const char **kernel_name);
+// launch_s6_grouped that also writes the state entering every 16-step tile to
+// checkpoints (batch, ceil(L/16), d_inner, d_state); d_state <= 16
+hipError_t launch_s6_grouped_save(const S6Args &a, int64_t ngroups, float *checkpoints, hipStream_t stream,
+                                  const char **kernel_name);
 
 // Mamba-1 layer around the scan: u = SiLU(causal conv1d(x)), y = scan(u) * SiLU(z)
 struct S6FusedArgs {

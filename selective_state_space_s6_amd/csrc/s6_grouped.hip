@@ -46,6 +46,8 @@ struct S6Gp {
     const float *h0; float *h_final;
     int64_t batch, L, Dm, N, G;
     int64_t n_cblk;                // channel groups of 16 per batch row
+    float *ck;                     // SAVE: (batch, ntiles, Dm, N), the state entering each tile
+    int64_t ntiles;
 };
 
 // one tile's loads of one lane: B, C of its states at the tile's 16 steps, and
@@ -56,7 +58,7 @@ struct GRaw {
     float dt, u;
 };
 
-template <typename TIN, int SPL, int MODE>
+template <typename TIN, int SPL, int MODE, bool SAVE = false>
 __global__ void __launch_bounds__(kGThreads)
 s6_grouped_kernel(S6Gp p) {
     const int tid = threadIdx.x;
@@ -114,6 +116,11 @@ s6_grouped_kernel(S6Gp p) {
 
     auto compute = [&](const GRaw<SPL> &R, int64_t t0, auto accTag) __attribute__((always_inline)) {
         constexpr bool ACC = decltype(accTag)::value;
+        if constexpr (SAVE) {
+#pragma unroll
+            for (int j = 0; j < SPL; ++j)
+                if (dval && nval[j]) p.ck[((b * p.ntiles + t0 / kGT) * p.Dm + d) * p.N + k + kGT * j] = h[j];
+        }
         const bool ok = dval && (t0 + k < p.L);
         const float dlk = ok ? softplus(R.dt + bias) : 0.0f;
         const float uk = ok ? R.u : 0.0f;
@@ -182,12 +189,12 @@ s6_grouped_kernel(S6Gp p) {
     }
 }
 
-template <typename TIN, int SPL>
+template <typename TIN, int SPL, bool SAVE = false>
 void launch_mode(const S6Gp &p, int mode, hipStream_t s) {
     const dim3 grid((unsigned)(p.batch * p.n_cblk)), block(kGThreads);
-    if (mode == 0) hipLaunchKernelGGL((s6_grouped_kernel<TIN, SPL, 0>), grid, block, 0, s, p);
-    else if (mode == 1) hipLaunchKernelGGL((s6_grouped_kernel<TIN, SPL, 1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((s6_grouped_kernel<TIN, SPL, 2>), grid, block, 0, s, p);
+    if (mode == 0) hipLaunchKernelGGL((s6_grouped_kernel<TIN, SPL, 0, SAVE>), grid, block, 0, s, p);
+    else if (mode == 1) hipLaunchKernelGGL((s6_grouped_kernel<TIN, SPL, 1, SAVE>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((s6_grouped_kernel<TIN, SPL, 2, SAVE>), grid, block, 0, s, p);
 }
 
 template <typename TIN>
@@ -223,6 +230,7 @@ struct S6GBp {
     float *ck;                   // (batch, ntiles, Dm, N)
     float *pA, *pD, *pT;         // (batch, Dm, N), (batch, Dm), (batch, Dm)
     int64_t batch, L, Dm, N, G, ntiles, n_cblk;
+    bool saved;                  // ck holds the forward's saved states: no pass 1
 };
 
 // phi1'(z) to z^3 (|z| < 1/16: truncation < 1e-7 relative)
@@ -324,10 +332,10 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
         }
     };
 
-    // ---- pass 1: the state entering each tile
-    float h = (ok && p.h0) ? p.h0[(b * p.Dm + d) * p.N + k] : 0.0f;
+    // ---- pass 1: the state entering each tile (unless the forward saved them)
     float *ck_b = p.ck + b * ntiles * p.Dm * p.N;         // + tile * Dm * N, + o_ck
-    {
+    if (!p.saved) {
+        float h = (ok && p.h0) ? p.h0[(b * p.Dm + d) * p.N + k] : 0.0f;
         GBRaw RA, RB;
         load(RA, 0, false);
         if (ntiles > 1) load(RB, 1, false);
@@ -353,7 +361,8 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
             }
         }
     }
-    // a lane reads back only the saved states it wrote itself
+    // a lane reads back only the states of its own (channel, state): written by
+    // itself in pass 1, or by the forward's lane of the same pair
 
     // ---- pass 2: backward over the tiles
     float g = (ok && p.dhf) ? p.dhf[(b * p.Dm + d) * p.N + k] : 0.0f;
@@ -534,7 +543,8 @@ hipError_t launch_s6_grouped_bwd(const S6BwdArgs &a, int64_t ngroups, hipStream_
     p.n_cblk = (a.d_inner + kGChan - 1) / kGChan;
     const GBLayout w = gb_layout(a.batch, a.L, a.d_inner, a.d_state, ngroups);
     char *ws = static_cast<char *>(a.workspace);
-    p.ck = reinterpret_cast<float *>(ws + w.ck);
+    p.saved = a.checkpoints != nullptr;
+    p.ck = p.saved ? const_cast<float *>(a.checkpoints) : reinterpret_cast<float *>(ws + w.ck);
     p.pA = reinterpret_cast<float *>(ws + w.pA);
     p.pD = reinterpret_cast<float *>(ws + w.pD);
     p.pT = reinterpret_cast<float *>(ws + w.pT);
@@ -570,6 +580,24 @@ hipError_t launch_s6_grouped(const S6Args &a, int64_t ngroups, hipStream_t strea
     const int mode = (int)(a.flags & 0x3u);
     if (a.bf16) launch_spl<uint16_t>(p, mode, stream);
     else launch_spl<float>(p, mode, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_s6_grouped_save(const S6Args &a, int64_t ngroups, float *checkpoints, hipStream_t stream,
+                                  const char **kernel_name) {
+    if (ngroups == 1) return launch_s6_save(a, checkpoints, stream, kernel_name);
+    *kernel_name = "s6_grouped_kernel";
+    S6Gp p{};
+    p.u = a.u; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log; p.B = a.B; p.C = a.C;
+    p.D = a.D; p.y = a.y; p.h0 = a.h0; p.h_final = a.h_final;
+    p.batch = a.batch; p.L = a.L; p.Dm = a.d_inner; p.N = a.d_state; p.G = ngroups;
+    p.n_cblk = (a.d_inner + kGChan - 1) / kGChan;
+    p.ck = checkpoints;
+    p.ntiles = (a.L + kGT - 1) / kGT;
+    const int mode = (int)(a.flags & 0x3u);
+    // d_state <= 16 (the backward's limit): one state per lane
+    if (a.bf16) launch_mode<uint16_t, 1, true>(p, mode, stream);
+    else launch_mode<float, 1, true>(p, mode, stream);
     return hipGetLastError();
 }
 

@@ -29,6 +29,8 @@ def lib():
     L.ssm_s6_scan_grouped_fwd.argtypes = [P] * 10 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P]
     L.ssm_s6_scan_fwd_save.argtypes = [P] * 11 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P]
     L.ssm_s6_scan_bwd_saved.argtypes = [P] * 19 + [I] * 4 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
+    L.ssm_s6_scan_grouped_fwd_save.argtypes = [P] * 11 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P]
+    L.ssm_s6_scan_grouped_bwd_saved.argtypes = [P] * 19 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssm_s6_scan_grouped_bwd.argtypes = [P] * 18 + [I] * 5 + [ctypes.c_int, ctypes.c_uint32, P, Z, P]
     L.ssm_s6_scan_grouped_bwd_workspace_size.argtypes = [I] * 5
     L.ssm_s6_scan_grouped_bwd_workspace_size.restype = Z
@@ -69,6 +71,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert names == {"ssm_last_error", "ssm_s6_scan_fwd_workspace_size", "ssm_s6_scan_fwd",
                      "ssm_s6_scan_grouped_fwd", "ssm_s6_scan_fwd_save", "ssm_s6_scan_bwd_saved",
                      "ssm_s6_scan_checkpoint_size", "ssm_s6_scan_grouped_bwd",
+                     "ssm_s6_scan_grouped_fwd_save", "ssm_s6_scan_grouped_bwd_saved",
                      "ssm_s6_scan_grouped_bwd_workspace_size",
                      "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd",
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
@@ -435,3 +438,29 @@ def test_trap_bwd_argument_checks(lib):
     assert need >= 2 * 2 * 4 * 64 * 128 * 4
     assert _trapb(lib, ws=None) == WORKSPACE
     assert _trapb(lib, wsb=need - 1) == WORKSPACE and "workspace" in _err(lib)
+
+
+def _gfsave(lib, dims=(2, 40, 32, 16, 32), ck=ctypes.c_void_p(0x7000000), y=ctypes.c_void_p(0x6000000)):
+    return lib.ssm_s6_scan_grouped_fwd_save(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, y, None, None, ck, *dims, 0,
+                                            0, None)
+
+
+def _gbsaved(lib, ck=ctypes.c_void_p(0xA000000), dims=(2, 40, 32, 16, 32)):
+    # a one-byte workspace: a call that passes every other check is refused for it
+    o = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(8)]
+    return lib.ssm_s6_scan_grouped_bwd_saved(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, FAKE, None, ck, *o,
+                                             *dims, 0, 0, ctypes.c_void_p(0x9000000), 1, None)
+
+
+def test_s6_grouped_saved_argument_checks(lib):
+    # every case below fails before any launch (the pointers are fake)
+    assert _gfsave(lib, dims=(2, 40, 32, 16, 5)) == INVALID and "multiple" in _err(lib)
+    assert _gfsave(lib, dims=(2, 40, 32, 17, 32)) == UNSUPPORTED and "d_state" in _err(lib)
+    assert _gfsave(lib, dims=(2, 40, 32, 16, 0)) == INVALID
+    assert _gfsave(lib, ck=None) == INVALID and "checkpoints" in _err(lib)
+    assert _gfsave(lib, ck=ctypes.c_void_p(0x6000000)) == INVALID and "alias" in _err(lib)
+    assert _gfsave(lib, ck=ctypes.c_void_p(0x7000004)) == UNSUPPORTED and "align" in _err(lib)
+    assert "ssm_s6_scan_grouped_fwd_save" in _err(lib)
+    assert _gbsaved(lib, ck=None) == INVALID and "checkpoints" in _err(lib)
+    assert _gbsaved(lib, dims=(2, 40, 32, 16, 5)) == INVALID and "multiple" in _err(lib)
+    assert _gbsaved(lib) == WORKSPACE and "ssm_s6_scan_grouped_bwd_saved" in _err(lib)

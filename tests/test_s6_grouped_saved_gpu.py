@@ -1,0 +1,69 @@
+"""GPU parity of the grouped S6 saved-state pair: ssm_s6_scan_grouped_fwd_save (the grouped
+forward that also saves the state entering each 16-step tile) and
+ssm_s6_scan_grouped_bwd_saved (the grouped backward that reads them), against the grouped
+forward and backward entry points (bit for bit: the same arithmetic), the forward's own
+prefix runs (the saved states) and the fp64 grouped oracles."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import TOL_BWD, TOL_F32, lib, report
+
+pytestmark = pytest.mark.gpu
+
+ZOH, DT, ONE = oracle.BBAR_ZOH, oracle.BBAR_DT, oracle.BBAR_ONE
+GRADS = ("du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")
+
+CASES = [  # batch, L, d_inner, N, ngroups, dtype, flags, h0, dh_final
+    (2, 100, 48, 16, 48, "f32", ZOH, True, True),       # per channel
+    (2, 70, 32, 16, 8, "f32", ZOH, True, True),         # groups of 4 channels
+    (1, 37, 20, 8, 20, "f32", DT, False, True),         # ragged tile and channel block
+    (1, 1, 16, 16, 16, "f32", ZOH, True, True),         # one step
+    (1, 130, 24, 12, 6, "bf16", ZOH, True, False),
+    (2, 64, 16, 16, 16, "f32", ONE, False, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}L{}D{}N{}G{}{}f{}h{}g{}".format(*[int(v) if isinstance(v, bool) else v for v in c]))
+def test_grouped_saved_pair(cuda_device, case):
+    batch, L, Dm, N, G, dtype, flags, h0, dhf_on = case
+    inp = synth.s6_inputs(batch, L, Dm, N, seed=(950 + L, G), dtype=dtype, h0=h0, a_log="index", ngroups=G)
+    dy, dhf = synth.s6_cotangents(batch, L, Dm, N, seed=(L, G, 1), dh_final=dhf_on)
+    t = inp.torch(cuda_device)
+    m = lib()
+    args = (t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"], t["h0"])
+    y, hf, ck = m.ssm_s6_scan_grouped_fwd_save(*args, flags=flags)
+    y0, hf0 = m.ssm_s6_scan_grouped_fwd(*args, flags=flags, return_final=True)
+    dyt = torch.from_numpy(dy).to(cuda_device)
+    dht = None if dhf is None else torch.from_numpy(dhf).to(cuda_device)
+    gs = m.ssm_s6_scan_grouped_bwd_saved(*args, dyt, dht, ck, flags=flags)
+    gr = m.ssm_s6_scan_grouped_bwd(*args, dyt, dht, flags=flags)
+    torch.cuda.synchronize()
+    # the forward's outputs are the plain grouped forward's
+    assert torch.equal(y, y0) and torch.equal(hf, hf0)
+    # saved state of tile k = the final state of the forward run over the first 16 k steps
+    ntiles = (L + 15) // 16
+    assert tuple(ck.shape) == (batch, ntiles, Dm, N)
+    h0_ref = t["h0"] if t["h0"] is not None else torch.zeros(batch, Dm, N, device=cuda_device)
+    assert torch.equal(ck[:, 0], h0_ref)
+    for k in sorted({1, ntiles // 2, ntiles - 1} - {0}):
+        if k >= ntiles:
+            continue
+        sl = {n: (v[:, :16 * k].contiguous() if n in ("u", "dt", "B", "C") else v) for n, v in t.items()}
+        _, hk = m.ssm_s6_scan_grouped_fwd(sl["u"], sl["dt"], sl["dt_bias"], sl["A_log"], sl["B"], sl["C"],
+                                          sl["D"], sl["h0"], flags=flags, return_final=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ck[:, k], hk), k
+    # the backward from saved states is the recomputing backward, and both are the oracle's
+    for k in GRADS:
+        assert torch.equal(gs[k], gr[k]), k
+    yo, _ = oracle.s6_grouped_fwd(**inp.arrays, flags=flags)
+    o = oracle.s6_grouped_bwd(**inp.arrays, dy=dy, dh_final=dhf, flags=flags)
+    errs = {k: synth.max_rel_err(gs[k].cpu().numpy(), o[k]) for k in GRADS}
+    errs["y"] = synth.max_rel_err(y.cpu().numpy(), yo)
+    report(f"s6 grouped saved {case}", **errs)
+    assert errs["y"] <= TOL_F32
+    for k in GRADS:
+        assert errs[k] <= TOL_BWD, (k, errs[k])
