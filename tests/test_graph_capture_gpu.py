@@ -119,3 +119,25 @@ def test_capture_cssd_mimo(cuda_device):
         m.ssd_cplx_mimo_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"], t["h0"],
                                        y=y, h_final=hf, workspace=ws)
     _capture_and_replay(fwd, [y, hf])
+
+
+def test_capture_grouped_saved_pair(cuda_device):
+    m = lib()
+    inp = synth.s6_inputs(2, 200, 48, 16, seed=(85,), h0=True, ngroups=48)
+    t = inp.torch(cuda_device)
+    y = torch.empty(2, 200, 48, device=cuda_device)
+    hf = torch.empty(2, 48, 16, device=cuda_device)
+    ck = torch.empty(2, 13, 48, 16, device=cuda_device)
+    dy = torch.randn(2, 200, 48, device=cuda_device)
+    shapes = dict(du=(2, 200, 48), ddt=(2, 200, 48), dB=(2, 200, 48, 16), dC=(2, 200, 48, 16), dA_log=(48, 16),
+                  dD=(48,), ddt_bias=(48,), dh0=(2, 48, 16))
+    out = {k: torch.empty(v, device=cuda_device) for k, v in shapes.items()}
+    ws = torch.empty(m.ssm_s6_scan_grouped_bwd_workspace_size(2, 200, 48, 16, 48), dtype=torch.uint8,
+                     device=cuda_device)
+
+    def pair():
+        m.ssm_s6_scan_grouped_fwd_save(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"], t["h0"],
+                                       y=y, h_final=hf, checkpoints=ck)
+        m.ssm_s6_scan_grouped_bwd_saved(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"], t["h0"],
+                                        dy, None, ck, out=out, workspace=ws)
+    _capture_and_replay(pair, [y, hf, ck, *out.values()])
