@@ -27,12 +27,37 @@ __device__ __forceinline__ float softplus(float x) {
     return fmaxf(x, 0.0f) + log1p_small(e);
 }
 
-// (e^z - 1)/z for z <= 0 and |z| < 1/16: Taylor polynomial, truncation < 2e-9.
-__device__ __forceinline__ float phi1_small(float z) {
-    float p = fmaf(z, 1.0f / 120.0f, 1.0f / 24.0f);
-    p = fmaf(z, p, 1.0f / 6.0f);
-    p = fmaf(z, p, 0.5f);
-    return fmaf(z, p, 1.0f);
+// Exact zero-order hold of one diagonal state with decay rate A < 0 over a
+// step delta: Abar = e^z and beta = (e^z - 1)/A = delta * phi1(z), z = delta*A.
+//
+// The hardware exp2 is within 0.8 ulp, but e^z - 1 taken from it carries that
+// rounding divided by |z|.  So where |z| >= 1/8, beta = (Abar - 1)/A (at most
+// ~6 ulp); below, phi1 = (e^z - 1)/z comes from its degree-3 polynomial of
+// least relative error on [-1/8, 0], written in x = z*log2(e) (fitted by
+// Lawson's iteratively reweighted least squares; error 1.8e-8, < 1 ulp in fp32
+// Horner form).  Abar is then formed on every lane as 1 + A*beta: where the
+// series is used it carries no exp rounding at all, which matters because the
+// slow states keep e^z's rounding for ~1/|z| steps (the hardware exp2 is biased
+// by about -0.1 ulp near 1), and elsewhere it equals the hardware value to a
+// few ulp of |Abar - 1|.  A, A*log2(e) and 1/A must be finite (|A| is clamped
+// where it is formed).
+constexpr float kZohSeriesX = 0.18033688f;   // 1/8 * log2(e): series below it
+constexpr float kPhi1x1 = 0.34657156467437744f;
+constexpr float kPhi1x2 = 0.08000794798135757f;
+constexpr float kPhi1x3 = 0.01322636753320694f;
+constexpr float kMaxAbsA = 1.0e38f;          // |A| clamp: A*log2(e) stays finite
+
+struct Zoh {
+    float ab;     // Abar = e^{delta A}
+    float beta;   // (Abar - 1)/A
+};
+__device__ __forceinline__ Zoh zoh_exact(float dl, float A, float A2, float iA) {
+    const float x = dl * A2;                                           // z * log2(e)
+    const float e = exp2_fast(x);
+    const float bf = fmaf(e, iA, -iA);                                 // (e^z - 1)/A
+    const float p = fmaf(x, fmaf(x, fmaf(x, kPhi1x3, kPhi1x2), kPhi1x1), 1.0f);   // phi1
+    const float beta = x > -kZohSeriesX ? dl * p : bf;
+    return {fmaf(A, beta, 1.0f), beta};
 }
 
 // SiLU(v) = v / (1 + e^-v), with the hardware reciprocal (about 1 ulp) in place of a

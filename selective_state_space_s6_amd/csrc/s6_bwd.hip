@@ -69,7 +69,7 @@ struct S6BKp {
     int64_t batch, L, Dm, N, ntiles, ncblk;
 };
 
-// phi1'(z) = sum_k k z^(k-1)/(k+1)! to z^3 (|z| < 1/16: truncation < 1e-7 relative)
+// phi1'(z) = sum_k k z^(k-1)/(k+1)! to z^3 (|z| < 1/8: truncation < 4e-6 relative)
 __device__ __forceinline__ float dphi1_series(float z) {
     float q = fmaf(z, 1.0f / 30.0f, 1.0f / 8.0f);
     q = fmaf(z, q, 1.0f / 3.0f);
@@ -103,10 +103,7 @@ struct Lds {
     float sBC[2][kT][16][16]; // [dB, dC][t][state][swizzled channel]
 };
 
-// ACC: this wave holds a ZOH state with |A| < 1/8, where (Abar - 1)/A loses
-// digits as delta*A -> 0; such waves switch to the series of phi1 below
-// |z| = 1/16.  The choice is uniform per wave and made once.
-template <typename TIN, int MODE, bool ACC>
+template <typename TIN, int MODE>
 __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
     auto &sDl = S.sDl;
     auto &sU = S.sU;
@@ -126,7 +123,7 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
     const int ntiles = (int)p.ntiles;
 
     const float al = ok ? p.A_log[d * p.N + n] : 0.0f;
-    const float A = ok ? -expf(al) : 0.0f;
+    const float A = ok ? -fminf(expf(al), kMaxAbsA) : 0.0f;
     const float A2 = A * kLog2e;
     const float iA = ok ? -expf(-al) : 0.0f;      // 1/A
 
@@ -198,19 +195,13 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
             cur_sig = __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * kLog2e));   // sigmoid(x)
         }
     };
-    auto beta_of = [&](float dl, float ab) __attribute__((always_inline)) {
-        if constexpr (MODE == 0) {
-            float beta = fmaf(ab, iA, -iA);                 // (Abar - 1)/A
-            if constexpr (ACC) {
-                const float z = dl * A;
-                beta = fabsf(z) < 0.0625f ? dl * phi1_small(z) : beta;
-            }
-            return beta;
-        } else if constexpr (MODE == 1) {
-            return dl;
-        } else {
-            return 1.0f;
-        }
+    // Abar and the input scale of one step: the forward's exact hold, so that
+    // recomputed states equal the forward's bit for bit
+    auto coef = [&](float dl) __attribute__((always_inline)) {
+        Zoh zh = zoh_exact(dl, A, A2, iA);
+        if constexpr (MODE == 1) zh.beta = dl;
+        if constexpr (MODE == 2) zh.beta = 1.0f;
+        return zh;
     };
 
     const float Bmask = n < p.N ? 1.0f : 0.0f;   // state-padding lanes carry zeros
@@ -250,9 +241,9 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
                 const float uu4[4] = {uq.x, uq.y, uq.z, uq.w};
                 static_for<0, 4>([&](auto ii) __attribute__((always_inline)) {
                     constexpr int i = decltype(ii)::value;
-                    const float ab = exp2_fast(dl4[i] * A2);
+                    const Zoh zh = coef(dl4[i]);
                     const float bu = row_bcast<4 * q + i>(Bv) * uu4[i];
-                    h = fmaf(ab, h, beta_of(dl4[i], ab) * bu);
+                    h = fmaf(zh.ab, h, zh.beta * bu);
                 });
             });
             stage(buf ^ 1, kt + 1, RSn, last);
@@ -292,9 +283,9 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
                 static_for<0, 4>([&](auto ii) __attribute__((always_inline)) {
                     constexpr int i = decltype(ii)::value;
                     constexpr int t = 4 * q + i;
-                    const float ab = exp2_fast(dl4[i] * A2);
+                    const Zoh zh = coef(dl4[i]);
                     const float bu = row_bcast<t>(Bv) * uu4[i];
-                    hh = fmaf(ab, hh, beta_of(dl4[i], ab) * bu);
+                    hh = fmaf(zh.ab, hh, zh.beta * bu);
                     hs[t] = hh;
                 });
                 __builtin_amdgcn_sched_barrier(0);
@@ -317,14 +308,15 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
                 constexpr int i = 3 - decltype(ii)::value;
                 constexpr int t = 4 * q + i;
                 const float dl = dl4[i], uu = uu4[i], dyv = dy4[i];
-                const float ab = exp2_fast(dl * A2);
+                const Zoh zh = coef(dl);
+                const float ab = zh.ab;
                 const float ht = hs[t];
                 float hp;
                 if constexpr (t > 0) hp = hs[t > 0 ? t - 1 : 0];
                 else hp = h_in;
                 const float Bt = row_bcast<t>(Bv);
                 g = fmaf(row_bcast<t>(Cv), dyv, g);          // g_t = dL/dh_t
-                const float beta = beta_of(dl, ab);
+                const float beta = zh.beta;
                 const float bu = Bt * uu;
                 const float gb = g * beta;
                 const float ga = g * ab;                     // g_t Abar_t: the cotangent passed to t - 1
@@ -337,9 +329,9 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
                     dA1 = fmaf(ga * dl, hp, dA1);
                     // A dbeta/dA = delta Abar - beta = delta z phi1'(z), z = delta A: the
                     // difference cancels to second order in z (relative error ~1e-7/z^2),
-                    // so below |z| = 1/16 it comes from the series of phi1'
+                    // so in the forward's series range it comes from the series of phi1'
                     const float z = dl * A;
-                    const float w = fabsf(z) < 0.0625f ? dl * z * dphi1_series(z) : fmaf(dl, ab, -beta);
+                    const float w = dl * A2 > -kZohSeriesX ? dl * z * dphi1_series(z) : fmaf(dl, ab, -beta);
                     dA2 = fmaf(bu * g, w, dA2);
                 } else if constexpr (MODE == 1) {
                     pd[i] = fmaf(ga, hp * A, g * bu);        // g (Abar A h_{t-1} + B u)
@@ -421,17 +413,7 @@ template <typename TIN, int MODE>
 __global__ void __launch_bounds__(kThreads, 3)
 s6_bwd_kernel(S6BKp p) {
     __shared__ __attribute__((aligned(16))) Lds S;
-    if constexpr (MODE == 0) {
-        const int tid = threadIdx.x;
-        const int64_t work = xcd_swizzle(blockIdx.x, gridDim.x);
-        const int64_t d = (work % p.ncblk) * kCW + (tid & 15);
-        const int n = tid >> 4;
-        const bool small = d < p.Dm && n < p.N && expf(p.A_log[d * p.N + n]) < 0.125f;
-        if (__builtin_amdgcn_ballot_w64(small) != 0) s6_bwd_body<TIN, MODE, true>(p, S);
-        else s6_bwd_body<TIN, MODE, false>(p, S);
-    } else {
-        s6_bwd_body<TIN, MODE, false>(p, S);
-    }
+    s6_bwd_body<TIN, MODE>(p, S);
 }
 
 // dB, dC = sum over channel blocks; dA_log = A * sum over batch; dD, ddt_bias = sum over batch

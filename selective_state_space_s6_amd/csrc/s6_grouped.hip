@@ -76,8 +76,7 @@ s6_grouped_kernel(S6Gp p) {
 
     int nidx[SPL];
     bool nval[SPL];
-    float A2[SPL], iA[SPL], h[SPL];
-    bool small = false;
+    float Av[SPL], A2[SPL], iA[SPL], h[SPL];
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
         const int n = k + kGT * j;
@@ -85,14 +84,11 @@ s6_grouped_kernel(S6Gp p) {
         nidx[j] = nval[j] ? n : (int)p.N - 1;
         const bool ok = dval && nval[j];
         const float al = ok ? p.A_log[dd * p.N + n] : 0.0f;
-        A2[j] = ok ? -expf(al) * kLog2e : 0.0f;          // A*log2(e), A = -exp(A_log)
-        iA[j] = ok ? -expf(-al) : 0.0f;                  // 1/A
+        Av[j] = ok ? -fminf(expf(al), kMaxAbsA) : 0.0f;   // A = -exp(A_log)
+        A2[j] = Av[j] * kLog2e;                            // A*log2(e)
+        iA[j] = ok ? -expf(-al) : 0.0f;                    // 1/A
         h[j] = (ok && p.h0) ? p.h0[(b * p.Dm + d) * p.N + n] : 0.0f;
-        small |= ok && (expf(al) < 0.125f);
     }
-    // ZOH with |A| small: (e^z - 1)/A loses digits as z -> 0; such waves use a
-    // series for phi1 when |z| < 1/16
-    const bool acc_wave = (MODE == 0) && (__builtin_amdgcn_ballot_w64(small) != 0);
     const float bias = (dval && p.dt_bias) ? p.dt_bias[dd] : 0.0f;
     const float Dd = (dval && p.D) ? p.D[dd] : 0.0f;
 
@@ -114,8 +110,7 @@ s6_grouped_kernel(S6Gp p) {
         R.u = In<TIN>::ld(Ub, te * p.Dm);
     };
 
-    auto compute = [&](const GRaw<SPL> &R, int64_t t0, auto accTag) __attribute__((always_inline)) {
-        constexpr bool ACC = decltype(accTag)::value;
+    auto compute = [&](const GRaw<SPL> &R, int64_t t0) __attribute__((always_inline)) {
         if constexpr (SAVE) {
 #pragma unroll
             for (int j = 0; j < SPL; ++j)
@@ -134,21 +129,9 @@ s6_grouped_kernel(S6Gp p) {
             for (int j = 0; j < SPL; ++j) {
                 const float bm = nval[j] ? R.B[t][j] : 0.0f;
                 const float cm = nval[j] ? R.C[t][j] : 0.0f;
-                const float x = dl * A2[j];
-                const float ab = exp2_fast(x);                   // Abar = exp(delta*A)
-                float beta;
-                if constexpr (MODE == 0) {
-                    beta = fmaf(ab, iA[j], -iA[j]);             // (Abar - 1)/A
-                    if constexpr (ACC) {
-                        const float z = x * kLn2;
-                        if (fabsf(z) < 0.0625f) beta = dl * phi1_small(z);
-                    }
-                } else if constexpr (MODE == 1) {
-                    beta = dl;
-                } else {
-                    beta = 1.0f;
-                }
-                h[j] = fmaf(ab, h[j], beta * (bm * uu));
+                const Zoh zh = zoh_exact(dl, Av[j], A2[j], iA[j]);   // Abar, (Abar - 1)/A
+                const float beta = MODE == 0 ? zh.beta : MODE == 1 ? dl : 1.0f;
+                h[j] = fmaf(zh.ab, h[j], beta * (bm * uu));
                 ys = fmaf(cm, h[j], ys);
             }
             part[t] = ys;
@@ -173,12 +156,10 @@ s6_grouped_kernel(S6Gp p) {
     load(RA, 0);
     if (ntiles > 1) load(RB, kGT);
     for (int64_t kt = 0; kt < ntiles; kt += 2) {
-        if (acc_wave) compute(RA, kt * kGT, std::true_type{});
-        else compute(RA, kt * kGT, std::false_type{});
+        compute(RA, kt * kGT);
         if (kt + 2 < ntiles) load(RA, (kt + 2) * kGT);
         if (kt + 1 < ntiles) {
-            if (acc_wave) compute(RB, (kt + 1) * kGT, std::true_type{});
-            else compute(RB, (kt + 1) * kGT, std::false_type{});
+            compute(RB, (kt + 1) * kGT);
             if (kt + 3 < ntiles) load(RB, (kt + 3) * kGT);
         }
     }
@@ -233,7 +214,7 @@ struct S6GBp {
     bool saved;                  // ck holds the forward's saved states: no pass 1
 };
 
-// phi1'(z) to z^3 (|z| < 1/16: truncation < 1e-7 relative)
+// phi1'(z) to z^3 (|z| < 1/8: truncation < 4e-6 relative)
 __device__ __forceinline__ float g_dphi1_small(float z) {
     float q = fmaf(z, 1.0f / 30.0f, 1.0f / 8.0f);
     q = fmaf(z, q, 1.0f / 3.0f);
@@ -260,7 +241,7 @@ struct GBRaw {
     float dt, u, dy;
 };
 
-template <typename TIN, int MODE, bool ACC>
+template <typename TIN, int MODE>
 __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
     const int tid = threadIdx.x;
     const int k = tid & (kGT - 1);                      // state k, step k of a tile
@@ -296,7 +277,7 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
     const float *DYb = p.dy + b * L * p.Dm;
 
     const float al = ok ? p.A_log[dd * p.N + nn] : 0.0f;
-    const float A = ok ? -expf(al) : 0.0f;
+    const float A = ok ? -fminf(expf(al), kMaxAbsA) : 0.0f;
     const float A2 = A * kLog2e;
     const float iA = ok ? -expf(-al) : 0.0f;
     const float bias = (dval && p.dt_bias) ? p.dt_bias[dd] : 0.0f;
@@ -317,19 +298,13 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
         R.u = In<TIN>::ld(at(Ub + t0 * p.Dm, step_i + o_chi), 0);
         R.dy = full ? *at(DYb + t0 * p.Dm, step_f + o_ch) : 0.0f;
     };
-    auto beta_of = [&](float dl, float ab) __attribute__((always_inline)) {
-        if constexpr (MODE == 0) {
-            float beta = fmaf(ab, iA, -iA);                 // (Abar - 1)/A
-            if constexpr (ACC) {
-                const float z = dl * A;
-                if (fabsf(z) < 0.0625f) beta = dl * phi1_small(z);
-            }
-            return beta;
-        } else if constexpr (MODE == 1) {
-            return dl;
-        } else {
-            return 1.0f;
-        }
+    // Abar and the input scale of one step: the forward's exact hold, so that
+    // recomputed states equal the forward's bit for bit
+    auto coef = [&](float dl) __attribute__((always_inline)) {
+        Zoh zh = zoh_exact(dl, A, A2, iA);
+        if constexpr (MODE == 1) zh.beta = dl;
+        if constexpr (MODE == 2) zh.beta = 1.0f;
+        return zh;
     };
 
     // ---- pass 1: the state entering each tile (unless the forward saved them)
@@ -347,9 +322,9 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
             g_static_for<0, kGT>([&](auto ti) __attribute__((always_inline)) {
                 constexpr int t = decltype(ti)::value;
                 const float dl = row_bcast<t>(dlk), uu = row_bcast<t>(uk);
-                const float ab = exp2_fast(dl * A2);
+                const Zoh zh = coef(dl);
                 const float bm = nval ? R.B[t] : 0.0f;
-                h = fmaf(ab, h, beta_of(dl, ab) * (bm * uu));
+                h = fmaf(zh.ab, h, zh.beta * (bm * uu));
             });
         };
         for (int64_t kt = 0; kt < ntiles; kt += 2) {
@@ -383,9 +358,9 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
             g_static_for<0, kGT>([&](auto ti) __attribute__((always_inline)) {
                 constexpr int t = decltype(ti)::value;
                 const float dl = row_bcast<t>(dlk), uu = row_bcast<t>(uk);
-                const float ab = exp2_fast(dl * A2);
+                const Zoh zh = coef(dl);
                 const float bm = nval ? R.B[t] : 0.0f;
-                hh = fmaf(ab, hh, beta_of(dl, ab) * (bm * uu));
+                hh = fmaf(zh.ab, hh, zh.beta * (bm * uu));
                 hs[t] = hh;
             });
         }
@@ -396,13 +371,15 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
         g_static_for<0, kGT>([&](auto ri) __attribute__((always_inline)) {
             constexpr int t = kGT - 1 - decltype(ri)::value;
             const float dl = row_bcast<t>(dlk), uu = row_bcast<t>(uk), dyv = row_bcast<t>(dyk);
-            const float ab = exp2_fast(dl * A2);
-            const float beta = beta_of(dl, ab);
+            const Zoh zh = coef(dl);
+            const float ab = zh.ab, beta = zh.beta;
             float bD, bA;
             if constexpr (MODE == 0) {
                 bD = ab;
+                // dbeta/dA = (delta Abar - beta)/A cancels to second order in z, so in
+                // the forward's series range it comes from the series of phi1'
                 const float z = dl * A;
-                bA = fabsf(z) < 0.0625f ? dl * dl * g_dphi1_small(z) : (dl * ab - beta) * iA;
+                bA = dl * A2 > -kZohSeriesX ? dl * dl * g_dphi1_small(z) : (dl * ab - beta) * iA;
             } else if constexpr (MODE == 1) {
                 bD = 1.0f; bA = 0.0f;
             } else {
@@ -465,15 +442,7 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
 template <typename TIN, int MODE>
 __global__ void __launch_bounds__(kGThreads)
 s6_grouped_bwd_kernel(S6GBp p) {
-    if constexpr (MODE == 0) {
-        const int64_t d = (blockIdx.x % p.n_cblk) * kGChan + (threadIdx.x >> 4);
-        const int k = threadIdx.x & (kGT - 1);
-        const bool small = d < p.Dm && k < p.N && expf(p.A_log[d * p.N + k]) < 0.125f;
-        if (__builtin_amdgcn_ballot_w64(small) != 0) s6_grouped_bwd_body<TIN, MODE, true>(p);
-        else s6_grouped_bwd_body<TIN, MODE, false>(p);
-    } else {
-        s6_grouped_bwd_body<TIN, MODE, false>(p);
-    }
+    s6_grouped_bwd_body<TIN, MODE>(p);
 }
 
 // dB, dC over each group's channels (when a group holds several); dA_log = A * sum over

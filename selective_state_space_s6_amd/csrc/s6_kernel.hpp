@@ -9,7 +9,8 @@
 // and the D skip term.  Nothing but y (and h_final) is written to memory.
 //
 // Work decomposition (the path is bound by VALU issue, not by HBM: every
-// (t, d, n) needs one exp and ~6 fp32 operations):
+// (t, d, n) needs one exp, the exact hold's series and select, and ~6 more fp32
+// operations, about 17 issue slots):
 //  * a 256-thread block owns CW = 256/G channels of one batch row and walks the
 //    whole sequence in tiles of 16 time steps;
 //  * the N states of a channel are spread over G lanes (SPL = N/G states per
@@ -159,19 +160,18 @@ s6_scan_kernel(S6Kp p) {
     const bool dok = d < p.Dm;
 
     // per-lane constants of the states this lane owns
-    float A2[SPL], iA[SPL], h[SPL];
+    float Av[SPL], A2[SPL], iA[SPL], h[SPL];
     bool nval[SPL];
-    bool small = false;
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
         const int64_t n = (int64_t)g * SPL + j;
         nval[j] = n < p.N;
         const bool ok = dok && n < p.N;
         const float al = ok ? p.A_log[d * p.N + n] : 0.0f;
-        A2[j] = ok ? -expf(al) * kLog2e : 0.0f;        // A*log2(e), A = -exp(A_log)
-        iA[j] = ok ? -expf(-al) : 0.0f;                // 1/A
+        Av[j] = ok ? -fminf(expf(al), kMaxAbsA) : 0.0f;   // A = -exp(A_log)
+        A2[j] = Av[j] * kLog2e;                            // A*log2(e)
+        iA[j] = ok ? -expf(-al) : 0.0f;                    // 1/A
         h[j] = (ok && p.h0) ? p.h0[(b * p.Dm + d) * p.N + n] : 0.0f;
-        small |= ok && (expf(al) < 0.125f);
     }
     // per-element constants of the (t, d) elements this thread stages/reduces
     float biasv[EPT], Dv[EPT];
@@ -224,10 +224,6 @@ s6_scan_kernel(S6Kp p) {
         q.B = static_cast<const TIN *>(p.B) + off;
         q.C = static_cast<const TIN *>(p.C) + off;
     }
-    // ZOH with |A| small: (e^z - 1)/A loses digits as z -> 0; such waves take a
-    // path that switches to a series for phi1 when |z| < 1/16.
-    const bool acc_wave = (MODE == 0) && (__builtin_amdgcn_ballot_w64(small) != 0);
-
     const int64_t ntiles = (p.L + kT - 1) / kT;
     // Two register sets alternate between even and odd tiles, so that loads in
     // flight are never copied (a copy would force a wait on them).  The set of
@@ -271,8 +267,7 @@ s6_scan_kernel(S6Kp p) {
         }
     };
 
-    auto compute = [&](int buf, const Raw<TIN, G, SPL, FUSE> &R, auto accTag) __attribute__((always_inline)) {
-        constexpr bool ACC = decltype(accTag)::value;
+    auto compute = [&](int buf, const Raw<TIN, G, SPL, FUSE> &R) __attribute__((always_inline)) {
         float Bm[SPL], Cm[SPL];          // this tile's B, C (state-padding lanes zeroed)
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
@@ -293,20 +288,9 @@ s6_scan_kernel(S6Kp p) {
                 float ys = 0.0f;
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) {
-                    const float x = dl * A2[j];                 // delta*A*log2(e)
-                    const float ab = exp2_fast(x);              // Abar = exp(delta*A)
-                    float beta;
-                    if constexpr (MODE == 0) {
-                        beta = fmaf(ab, iA[j], -iA[j]);         // (Abar - 1)/A
-                        if constexpr (ACC) {
-                            const float z = x * kLn2;
-                            if (fabsf(z) < 0.0625f) beta = dl * phi1_small(z);
-                        }
-                    } else if constexpr (MODE == 1) {
-                        beta = dl;
-                    } else {
-                        beta = 1.0f;
-                    }
+                    const Zoh zh = zoh_exact(dl, Av[j], A2[j], iA[j]);   // Abar, (Abar - 1)/A
+                    const float ab = zh.ab;
+                    const float beta = MODE == 0 ? zh.beta : MODE == 1 ? dl : 1.0f;
                     const float bu = row_bcast<t>(Bm[j]) * uu;   // B[t, n] * u[t, d]
                     h[j] = fmaf(ab, h[j], beta * bu);
                     if (j == 0) ys = row_bcast<t>(Cm[j]) * h[j];
@@ -356,22 +340,22 @@ s6_scan_kernel(S6Kp p) {
             }
         }
     };
-    auto body_full = [&](int64_t kt, Raw<TIN, G, SPL, FUSE> &Rk, const Raw<TIN, G, SPL, FUSE> &Rn, auto accTag)
+    auto body_full = [&](int64_t kt, Raw<TIN, G, SPL, FUSE> &Rk, const Raw<TIN, G, SPL, FUSE> &Rn)
         __attribute__((always_inline)) {
         const int buf = (int)(kt & 1);
         save(kt);
-        compute(buf, Rk, accTag);
+        compute(buf, Rk);
         reduce(buf ^ 1, (kt - 1) * kT, std::false_type{});
         shift();
         stage(buf ^ 1, (kt + 1) * kT, Rn, std::false_type{});
         load_raw<false>(Rk, q, p, (kt + 2) * kT, tid, k);
         __syncthreads();
     };
-    auto body_checked = [&](int64_t kt, Raw<TIN, G, SPL, FUSE> &Rk, const Raw<TIN, G, SPL, FUSE> &Rn, auto accTag)
+    auto body_checked = [&](int64_t kt, Raw<TIN, G, SPL, FUSE> &Rk, const Raw<TIN, G, SPL, FUSE> &Rn)
         __attribute__((always_inline)) {
         const int buf = (int)(kt & 1);
         save(kt);
-        compute(buf, Rk, accTag);
+        compute(buf, Rk);
         if (kt >= 1) reduce(buf ^ 1, (kt - 1) * kT, std::true_type{});
         shift();
         if (kt + 1 < ntiles) stage(buf ^ 1, (kt + 1) * kT, Rn, std::true_type{});
@@ -381,18 +365,18 @@ s6_scan_kernel(S6Kp p) {
     // The unchecked body of tile kt loads tile kt+2, so a pair (kt, kt+1) of
     // unchecked bodies needs tiles up to kt+3 to lie wholly inside the sequence.
     const int64_t nfull = p.L / kT;
-    auto run = [&](auto accTag) __attribute__((always_inline)) {
+    auto run = [&]() __attribute__((always_inline)) {
         int64_t kt = 0;
         if (ntiles >= 4) {
-            body_checked(0, RA, RB, accTag);
+            body_checked(0, RA, RB);
             for (kt = 1; kt + 4 <= nfull; kt += 2) {   // tiles kt (set RB) and kt+1 (set RA)
-                body_full(kt, RB, RA, accTag);
-                body_full(kt + 1, RA, RB, accTag);
+                body_full(kt, RB, RA);
+                body_full(kt + 1, RA, RB);
             }
         }
         for (; kt < ntiles; ++kt) {
-            if (kt & 1) body_checked(kt, RB, RA, accTag);
-            else body_checked(kt, RA, RB, accTag);
+            if (kt & 1) body_checked(kt, RB, RA);
+            else body_checked(kt, RA, RB);
         }
     };
 
@@ -400,8 +384,7 @@ s6_scan_kernel(S6Kp p) {
     if (ntiles > 1) load_raw<true>(RB, q, p, kT, tid, k);
     stage(0, 0, RA, std::true_type{});
     __syncthreads();
-    if (acc_wave) run(std::true_type{});
-    else run(std::false_type{});
+    run();
     reduce((int)((ntiles - 1) & 1), (ntiles - 1) * kT, std::true_type{});
 
     if (p.h_final) {

@@ -18,14 +18,6 @@ TOL_BF16 = 2e-2    # max relative error, bf16 inputs with fp32 state
 # deviate among 1e5-1e7 elements: ~2e-4.  A plain fp32 computation of the same gradients
 # (numpy, each op rounded) scores 1.3e-4 to 1e-3 at the Mamba-1 layer shape.
 TOL_BWD = 1e-3
-# The Mamba-1 layer's scan input u = SiLU(conv(x)) is biased positive (mean 0.09, rms 0.37 at
-# the layer workload), unlike the N(0, 1) u the fp32 bar was stated for.  On the layer
-# workload's sampled channels a plain fp32 recurrence (numpy, every operation correctly
-# rounded, libm exp) already scores 9.6e-5 against the fp64 oracle (8.4e-5 on the plain
-# workload): the exact ZOH scale (e^z - 1)/A carries one ulp of e^z divided by |z| ~ 0.01.
-# The kernel's hardware exp2 is within 1 ulp.  Bar for the layer's output: twice the
-# correctly rounded fp32 score.
-TOL_S6_LAYER = 2e-4
 
 
 def lib():

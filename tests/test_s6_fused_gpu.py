@@ -8,7 +8,7 @@ from scipy.special import expit
 
 import oracle
 import synth
-from helpers import TOL_BF16, TOL_F32, TOL_S6_LAYER, lib, report, sample_units
+from helpers import TOL_BF16, TOL_F32, lib, report, sample_units
 
 pytestmark = pytest.mark.gpu
 
@@ -27,12 +27,8 @@ def _gpu(inp, device, flags, **kw):
 
 
 def _ungate(y, z):
-    """y / SiLU(z), the gate formed in fp64 from the inputs.  The gate multiplies each
-    output by up to ~5 at N(0, 1) z, so the gated values' relative metric (floor 1 % of
-    their rms) would scale the scan's own error by |g| / rms(g); dividing both sides by
-    the same exact gate compares the scan at its own bar, and the gate's fp32 rounding
-    (~1e-7) stays inside it.  The gate arithmetic itself is checked against the plain
-    scan of the fused call's u."""
+    """y / SiLU(z), the gate formed in fp64 from the inputs: a printed diagnostic of the
+    scan's own error apart from the gate (the parity bar applies to the gated y)."""
     if z is None:
         return y
     z = z.astype(np.float64)
@@ -65,11 +61,11 @@ def test_fused_shapes(cuda_device, case):
     inp = synth.layer_inputs(batch, L, Dm, N, K, seed=(L, Dm), dtype=dtype, conv_state=st, gate=gate, h0=h0)
     y, hf, u, cs = _gpu(inp, cuda_device, flags)
     yo, ho, uo, cso = _oracle(inp, flags)
-    tol = TOL_S6_LAYER if dtype == "f32" else TOL_BF16
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
     z = inp.arrays["z"]
-    ey = synth.max_rel_err(_ungate(y, z), _ungate(yo, z))
+    ey = synth.max_rel_err(y, yo)
     eh, eu = synth.max_rel_err(hf, ho), synth.max_rel_err(u, uo)
-    report(f"s6 fused {case}", y=ey, h_final=eh, u=eu)
+    report(f"s6 fused {case}", y=ey, h_final=eh, u=eu, y_ungated=synth.max_rel_err(_ungate(y, z), _ungate(yo, z)))
     assert np.isfinite(y).all()
     assert ey <= tol and eh <= tol and eu <= TOL_F32
     if K > 1:
@@ -96,10 +92,9 @@ def test_fused_decode_steps_in_place(cuda_device):
         ys.append(y)
     torch.cuda.synchronize()
     yg = torch.cat(ys, dim=1).cpu().numpy()
-    z = inp.arrays["z"]
-    ey, eh = synth.max_rel_err(_ungate(yg, z), _ungate(yo, z)), synth.max_rel_err(h.cpu().numpy(), ho)
+    ey, eh = synth.max_rel_err(yg, yo), synth.max_rel_err(h.cpu().numpy(), ho)
     report("s6 decode in place", y=ey, h_final=eh)
-    assert ey <= TOL_S6_LAYER and eh <= TOL_F32
+    assert ey <= TOL_F32 and eh <= TOL_F32
     assert np.array_equal(st.cpu().numpy(), cso.astype(np.float32))
 
 
@@ -133,20 +128,20 @@ def test_fused_bitwise_deterministic(cuda_device):
 
 def test_fused_mamba1_workload_sampled(cuda_device):
     """Full Mamba-1 layer shape (8 x 2048 x 1536, N 16, K 4, fp32) against the oracle on
-    48 sampled (b, d) channels over the whole sequence."""
+    256 sampled (b, d) channels over the whole sequence."""
     w = synth.WORKLOADS["s6_layer_mamba1"]
     inp = synth.workload_inputs("s6_layer_mamba1")
     y, hf, u, cs = _gpu(inp, cuda_device, ZOH)
-    units = sample_units(np.random.default_rng(7), w["batch"], w["d_inner"], 48)
+    units = sample_units(np.random.default_rng(7), w["batch"], w["d_inner"], 256)
     yo, ho, uo, cso = _oracle(inp, ZOH, units=units)
     yg = np.stack([y[b, :, d] for b, d in units])
     hg = np.stack([hf[b, d] for b, d in units])
     ug = np.stack([u[b, :, d] for b, d in units])
     zs = np.stack([inp.arrays["z"][b, :, d] for b, d in units])
-    ey = synth.max_rel_err(_ungate(yg, zs), _ungate(yo, zs))
+    ey = synth.max_rel_err(yg, yo)
     eh, eu = synth.max_rel_err(hg, ho), synth.max_rel_err(ug, uo)
-    report("s6_layer_mamba1 sampled", y=ey, h_final=eh, u=eu)
-    assert ey <= TOL_S6_LAYER and eh <= TOL_F32 and eu <= TOL_F32
+    report("s6_layer_mamba1 sampled", y=ey, h_final=eh, u=eu, y_ungated=synth.max_rel_err(_ungate(yg, zs), _ungate(yo, zs)))
+    assert ey <= TOL_F32 and eh <= TOL_F32 and eu <= TOL_F32
     assert np.array_equal(np.stack([cs[b, d] for b, d in units]), cso.astype(np.float32))
 
 

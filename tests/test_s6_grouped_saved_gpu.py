@@ -16,20 +16,23 @@ pytestmark = pytest.mark.gpu
 ZOH, DT, ONE = oracle.BBAR_ZOH, oracle.BBAR_DT, oracle.BBAR_ONE
 GRADS = ("du", "ddt", "dB", "dC", "dA_log", "dD", "ddt_bias", "dh0")
 
-CASES = [  # batch, L, d_inner, N, ngroups, dtype, flags, h0, dh_final
-    (2, 100, 48, 16, 48, "f32", ZOH, True, True),       # per channel
-    (2, 70, 32, 16, 8, "f32", ZOH, True, True),         # groups of 4 channels
-    (1, 37, 20, 8, 20, "f32", DT, False, True),         # ragged tile and channel block
-    (1, 1, 16, 16, 16, "f32", ZOH, True, True),         # one step
-    (1, 130, 24, 12, 6, "bf16", ZOH, True, False),
-    (2, 64, 16, 16, 16, "f32", ONE, False, True),
+CASES = [  # batch, L, d_inner, N, ngroups, dtype, flags, h0, dh_final, A_log
+    (2, 100, 48, 16, 48, "f32", ZOH, True, True, "index"),       # per channel
+    (2, 70, 32, 16, 8, "f32", ZOH, True, True, "index"),         # groups of 4 channels
+    (1, 37, 20, 8, 20, "f32", DT, False, True, "index"),         # ragged tile and channel block
+    (1, 1, 16, 16, 16, "f32", ZOH, True, True, "index"),         # one step
+    (1, 130, 24, 12, 6, "bf16", ZOH, True, False, "index"),
+    (2, 64, 16, 16, 16, "f32", ONE, False, True, "index"),
+    # small |A| = e^-2.5: every |delta A| < 1/8, so every step takes the hold's series
+    (2, 90, 32, 16, 32, "f32", ZOH, True, True, -2.5),
+    (1, 120, 24, 16, 8, "f32", ZOH, True, True, "uniform"),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}L{}D{}N{}G{}{}f{}h{}g{}".format(*[int(v) if isinstance(v, bool) else v for v in c]))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}L{}D{}N{}G{}{}f{}h{}g{}A{}".format(*[int(v) if isinstance(v, bool) else v for v in c]))
 def test_grouped_saved_pair(cuda_device, case):
-    batch, L, Dm, N, G, dtype, flags, h0, dhf_on = case
-    inp = synth.s6_inputs(batch, L, Dm, N, seed=(950 + L, G), dtype=dtype, h0=h0, a_log="index", ngroups=G)
+    batch, L, Dm, N, G, dtype, flags, h0, dhf_on, a_log = case
+    inp = synth.s6_inputs(batch, L, Dm, N, seed=(950 + L, G), dtype=dtype, h0=h0, a_log=a_log, ngroups=G)
     dy, dhf = synth.s6_cotangents(batch, L, Dm, N, seed=(L, G, 1), dh_final=dhf_on)
     t = inp.torch(cuda_device)
     m = lib()
