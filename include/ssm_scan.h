@@ -105,8 +105,17 @@ const char *ssm_last_error(void);
  * dt_bias, D (d_inner) fp32; A_log (d_inner, d_state) fp32;
  * B, C (batch, L, d_state) [in_dtype]; y (batch, L, d_inner) fp32;
  * h0, h_final (batch, d_inner, d_state) fp32.
- * Limits: 1 <= d_state <= 256; any L >= 1.  No workspace is needed
- * (ssm_s6_scan_fwd_workspace_size returns 0; workspace may be NULL). */
+ * Limits: 1 <= d_state <= 256; any L >= 1.
+ *
+ * Workspace (optional; caller-owned device memory, 16-byte aligned): for long
+ * sequences over few channels (a quarter of the chip's blocks or fewer, L >=
+ * 1024, d_state <= 16), ssm_s6_scan_fwd_workspace_size returns a nonzero size,
+ * and a workspace of that size lets the call cut time into segments joined by
+ * the associative carry of the recurrence ([BF-S6 forward_scan] tile carry,
+ * with the earlier map applied first).  With workspace NULL the call walks the
+ * sequence in one pass; both give the same result up to fp32 rounding order.
+ * A non-NULL workspace smaller than the queried size is SSM_ERR_WORKSPACE.
+ * The query returns 0 where the walk is used; workspace may then be NULL. */
 size_t ssm_s6_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state);
 
 int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,

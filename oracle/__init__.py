@@ -12,6 +12,10 @@ passed as their exactly-widened float32 values); outputs are float64.
 Parity status of each function (what pins it is listed in the tests):
   s6_fwd    pinned: exact-fraction hand cases, A->0 cumulative-sum limit,
             closed-form brute force, carry composition, linearity.
+  s6_segmented_fwd  an internal cross-check of the associative carry (numpy):
+            pinned to s6_fwd for segment lengths 1, 7, 64, L and > L, and its
+            segment decay to the closed form exp(A * sum of delta); with the page's
+            printed combine it departs from s6_fwd (reading R6).
   ssd_fwd   pinned: brute-force semiseparable matrix, chunked algebra,
             reduction to S6, group replication, hand case.
   cssd_fwd  pinned: reduction to the real SSD at zero phase, L=1 closed form,
@@ -151,6 +155,80 @@ def s6_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, flags=BBAR_ZOH, units=None, 
     if full:
         return (y.reshape(batch, Dm, L).transpose(0, 2, 1).copy(), hf.reshape(batch, Dm, N))
     return y, hf
+
+
+def _s6_coeffs_np(u, dt, dt_bias, A_log, B, flags):
+    """Per-step decay and input of the S6 recurrence in fp64 numpy (the definitions of
+    selective_scan.js softplus, discretise_A, discretise_B; readings R2-R5):
+    Abar[b,t,d,n] = exp(delta A), inp[b,t,d,n] = beta B[b,t,n] u[b,t,d]."""
+    x = dt.astype(np.float64) + (0.0 if dt_bias is None else dt_bias.astype(np.float64))
+    delta = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+    A = -np.exp(A_log.astype(np.float64))
+    z = delta[..., None] * A
+    Abar = np.exp(z)
+    mode = flags & 0x3
+    if mode == BBAR_ZOH:
+        zs = np.where(z == 0.0, 1.0, z)
+        beta = delta[..., None] * np.where(z == 0.0, 1.0, np.expm1(zs) / zs)
+    elif mode == BBAR_DT:
+        beta = np.broadcast_to(delta[..., None], z.shape)
+    else:
+        beta = np.ones_like(z)
+    inp = beta * B.astype(np.float64)[:, :, None, :] * u.astype(np.float64)[..., None]
+    return Abar, inp
+
+
+def s6_segmented_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, flags=BBAR_ZOH, seg_len=64,
+                     order="earlier_first"):
+    """The S6 recurrence computed by time segments joined with the associative carry, in
+    fp64 numpy: an oracle-internal cross-check of the carry algebra the segmented kernel
+    uses (the parity reference stays s6_fwd, the plain sequential recurrence).
+
+    Each step is the affine map h -> Abar h + inp.  A segment of steps composes into one
+    map (P, c): P the product of its Abar, c its final state from a zero state.  Two maps
+    run one after the other compose as (P2 P1, P2 c1 + c2), the earlier one first
+    (order="earlier_first").  order="page" uses the combine printed in
+    builderforce-memory-engine selective_scan.js (forward_scan comment and code),
+    (P1 P2, P1 c2 + c1), which applies the earlier decay to the later input -- kept to show
+    that it is not the recurrence.  The entering state of every segment comes from an
+    inclusive Hillis-Steele scan of (0, h0), (P_0, c_0), ... (the pairs composed in a tree,
+    not a left fold), then every segment runs again from its entering state.
+    Returns y (batch, L, d_inner) and h_final (batch, d_inner, N), float64."""
+    u, dt, dt_bias, A_log, B, C, D, h0 = map(_f32, (u, dt, dt_bias, A_log, B, C, D, h0))
+    batch, L, Dm = u.shape
+    N = A_log.shape[1]
+    Abar, inp = _s6_coeffs_np(u, dt, dt_bias, A_log, B, flags)
+    starts = list(range(0, L, seg_len))
+    # segment maps: (P, c) with c the final state from zero
+    pairs = [(np.zeros((batch, Dm, N)), np.zeros((batch, Dm, N)) if h0 is None else h0.astype(np.float64))]
+    for s0 in starts[:-1]:
+        P = np.ones((batch, Dm, N))
+        c = np.zeros((batch, Dm, N))
+        for t in range(s0, min(s0 + seg_len, L)):
+            c = Abar[:, t] * c + inp[:, t]
+            P = P * Abar[:, t]
+        pairs.append((P, c))
+
+    def compose(e, l):   # e runs first, then l
+        if order == "earlier_first":
+            return (l[0] * e[0], l[0] * e[1] + l[1])
+        return (e[0] * l[0], e[0] * l[1] + e[1])
+
+    scan = list(pairs)
+    k = 1
+    while k < len(scan):
+        scan = [scan[i] if i < k else compose(scan[i - k], scan[i]) for i in range(len(scan))]
+        k *= 2
+    y = np.empty((batch, L, Dm))
+    Cd = C.astype(np.float64)
+    Dv = np.zeros(Dm) if D is None else D.astype(np.float64)
+    h = None
+    for si, s0 in enumerate(starts):
+        h = scan[si][1].copy()
+        for t in range(s0, min(s0 + seg_len, L)):
+            h = Abar[:, t] * h + inp[:, t]
+            y[:, t] = np.einsum("bdn,bn->bd", h, Cd[:, t]) + Dv * u[:, t].astype(np.float64)
+    return y, h
 
 
 def s6_grouped_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, flags=BBAR_ZOH, units=None, nthreads=None):

@@ -181,10 +181,13 @@ def ssd_cplx_chunk_scan_fwd_workspace_size(batch, L, nheads, headdim, n_complex,
 
 
 def ssm_s6_scan_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, *, flags=SSM_BBAR_ZOH,
-                    return_final=False, y=None, h_final=None):
+                    return_final=False, y=None, h_final=None, workspace="auto"):
     """S6 forward scan.  u (batch, L, d_inner) fp32|bf16; dt fp32 (same shape);
     dt_bias, D (d_inner) fp32 or None; A_log (d_inner, d_state) fp32;
     B, C (batch, L, d_state) in u's dtype; h0 (batch, d_inner, d_state) fp32 or None.
+    workspace: "auto" allocates the size the library asks for (nonzero only for
+    long sequences over few channels, which then take the segmented scan), None
+    walks the sequence in one pass, or a uint8 device tensor.
     Returns y (fp32), or (y, h_final) when return_final."""
     dev = u.device
     batch, L, Dm = u.shape
@@ -204,9 +207,13 @@ def ssm_s6_scan_fwd(u, dt, dt_bias, A_log, B, C, D, h0=None, *, flags=SSM_BBAR_Z
     if return_final and h_final is None:
         h_final = torch.empty((batch, Dm, N), dtype=torch.float32, device=dev)
     _opt(h_final, "h_final", torch.float32, (batch, Dm, N), dev)
+    if isinstance(workspace, str):
+        ws_n = ssm_s6_scan_fwd_workspace_size(batch, L, Dm, N)
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n > 0 else None
+    ws_ptr, ws_n = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     rc = _lib.ssm_s6_scan_fwd(_ptr(u), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
                               _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L, Dm, N,
-                              _in_dtype(u), flags, None, 0, _stream(dev))
+                              _in_dtype(u), flags, ws_ptr, ws_n, _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y
 

@@ -59,7 +59,10 @@ extern "C" {
 
 const char *ssm_last_error(void) { return g_err; }
 
-size_t ssm_s6_scan_fwd_workspace_size(int64_t, int64_t, int64_t, int64_t) { return 0; }
+size_t ssm_s6_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state) {
+    if (batch <= 0 || L <= 0 || d_inner <= 0 || d_state <= 0) return 0;
+    return ssm::s6_seg_plan(batch, L, d_inner, d_state).ws_bytes;
+}
 
 int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const float *A_log,
                     const void *B, const void *C, const float *D, float *y,
@@ -67,7 +70,6 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
                     int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
                     ssm_dtype_t in_dtype, uint32_t flags,
                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace; (void)workspace_bytes;
     const char *E = "ssm_s6_scan_fwd";
     REQUIRE_PTR(E, u); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
     REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
@@ -86,8 +88,14 @@ int ssm_s6_scan_fwd(const void *u, const float *dt, const float *dt_bias, const 
     if ((const void *)y == u || (const void *)y == (const void *)dt || (const void *)y == B ||
         (const void *)y == C)
         return fail(SSM_ERR_INVALID_ARG, "%s: y aliases an input", E);
+    // the workspace is optional: with one of at least the queried size, long
+    // sequences over few channels take the segmented scan; without, the walk
+    const size_t need = ssm::s6_seg_plan(batch, L, d_inner, d_state).ws_bytes;
+    if (workspace && workspace_bytes < need)
+        return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", E, workspace_bytes, need);
+    REQUIRE_ALIGN(E, workspace);
     ssm::S6Args a{u, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, d_inner, d_state,
-                  in_dtype == SSM_BF16, flags};
+                  in_dtype == SSM_BF16, flags, need > 0 ? workspace : nullptr};
     const char *kn = "s6";
     return launched(E, ssm::launch_s6(a, stream, &kn), kn);
 }

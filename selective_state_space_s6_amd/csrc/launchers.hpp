@@ -12,8 +12,15 @@ struct S6Args {
     const float *h0; float *h_final;
     int64_t batch, L, d_inner, d_state;
     bool bf16; uint32_t flags;
+    void *workspace = nullptr;   // at least s6_seg_plan(...).ws_bytes, or null: the sequential walk
 };
 hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_name);
+// Segmented S6 scan (s6_seg.hip): long sequences over few channel blocks are cut
+// into nseg time segments joined by an associative carry; nseg = 1 is the
+// sequential walk.  ws_bytes: the workspace the segmented launch needs.
+struct S6SegPlan { int64_t nseg, seg_len; size_t ws_bytes; };
+S6SegPlan s6_seg_plan(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state);
+hipError_t launch_s6_segmented(const S6Args &a, const S6SegPlan &plan, hipStream_t stream, const char **kernel_name);
 // the forward that also writes the state entering every 16-step tile, (batch,
 // ceil(L/16), d_inner, d_state) fp32, for the backward (d_state <= 16)
 hipError_t launch_s6_save(const S6Args &a, float *checkpoints, hipStream_t stream, const char **kernel_name);

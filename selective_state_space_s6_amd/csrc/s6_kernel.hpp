@@ -23,6 +23,16 @@
 //    thread per (t, d) adds the G partials, adds D*u and writes y;
 //  * global loads of the tile after next are in flight while a tile is scanned.
 //
+// Segmented form (PASS 1 and 3; the plain sequential walk is PASS 0): for long
+// sequences over few channels, time is cut into segments of seg_len steps.
+// PASS 1 runs each segment but the last from a zero state and writes its local
+// final state and its sum of delta (the segment's decay is exp(A * sum)); a
+// carry kernel combines the (decay, state) pairs with the associative rule
+// (earlier, then later: (P2 P1, P2 h1 + h2)) into every segment's entering
+// state; PASS 3 scans each segment from that state and writes y (and, in the
+// last segment, h_final).  selective_scan.js forward_scan carries a tile's
+// state the same way (its printed combine has the order reversed).
+//
 // Fused layer form (FUSE): the kernel reads x instead of u and forms
 // u_t = SiLU(sum_k conv_w[d,k] x_{t-k} + conv_b[d]) as it stages a tile (the
 // three earlier steps are cache hits, the carried conv state stands in before
@@ -30,6 +40,7 @@
 #pragma once
 #include "device_common.hpp"
 #include "launchers.hpp"
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -63,6 +74,13 @@ struct S6Kp {
     // SAVE form: the state entering every 16-step tile, (batch, ntiles, Dm, N) fp32
     // (the saved states the S6 backward reads in place of recomputing them)
     float *ck;
+    // segmented form: nseg segments of seg_len steps (the last may be shorter);
+    // PASS 1 writes h_loc (batch, nseg-1, Dm, N) and dsum (batch, nseg-1, Dm),
+    // PASS 3 reads h_in (batch, nseg, Dm, N)
+    int64_t seg_len, nseg;
+    float *h_loc;
+    double *dsum;
+    const float *h_in;
 };
 
 constexpr int kMaxConv = 4;   // longest causal convolution of the fused form
@@ -101,16 +119,16 @@ struct Ptrs {
 // (CHECK) clamps its time index into the tensors; values of steps past L,
 // channels past d_inner and states past N are masked where they are consumed
 // (channel and state indices are clamped once, in the base pointers).
-template <bool CHECK, typename TIN, int G, int SPL, bool FUSE>
+template <bool CHECK, bool WITH_C, typename TIN, int G, int SPL, bool FUSE>
 __device__ __forceinline__ void load_raw(Raw<TIN, G, SPL, FUSE> &r, const Ptrs<TIN, G, SPL> &q,
-                                         const S6Kp &p, int64_t t0, int tid, int k) {
+                                         const S6Kp &p, int64_t Lk, int64_t t0, int tid, int k) {
     constexpr int CW = kThreads / G;
     constexpr int EPT = 16 / G;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int tl = (tid + kThreads * i) / CW;
         int64_t off = t0 * p.Dm;
-        if constexpr (CHECK) off = (min(t0 + tl, p.L - 1) - tl) * p.Dm;
+        if constexpr (CHECK) off = (min(t0 + tl, Lk - 1) - tl) * p.Dm;
         r.dt[i] = q.dt[i][off];
         r.u[i] = In<TIN>::ld(q.u[i], off);
         if constexpr (FUSE) {
@@ -120,24 +138,27 @@ __device__ __forceinline__ void load_raw(Raw<TIN, G, SPL, FUSE> &r, const Ptrs<T
 #pragma unroll
             for (int kk = 1; kk < kMaxConv; ++kk) {
                 int64_t offk = t0 * p.Dm - kk * p.Dm;
-                if constexpr (CHECK) offk = (max(min(t0 + tl, p.L - 1) - kk, (int64_t)0) - tl) * p.Dm;
+                if constexpr (CHECK) offk = (max(min(t0 + tl, Lk - 1) - kk, (int64_t)0) - tl) * p.Dm;
                 r.f.xh[i][kk - 1] = In<TIN>::ld(q.u[i], offk);
             }
             r.f.z[i] = In<TIN>::ld(q.z[i], off);
         }
     }
     int64_t off = t0 * p.N;
-    if constexpr (CHECK) off = (min(t0 + k, p.L - 1) - k) * p.N;
+    if constexpr (CHECK) off = (min(t0 + k, Lk - 1) - k) * p.N;
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
         r.B[j] = In<TIN>::ld(q.B, off + q.nidx[j]);
-        r.C[j] = In<TIN>::ld(q.C, off + q.nidx[j]);
+        r.C[j] = WITH_C ? In<TIN>::ld(q.C, off + q.nidx[j]) : 0.0f;
     }
 }
 
-template <typename TIN, int G, int SPL, int MODE, bool FUSE, bool SAVE = false>
+template <typename TIN, int G, int SPL, int MODE, bool FUSE, bool SAVE = false, int PASS = 0>
 __global__ void __launch_bounds__(kThreads)
 s6_scan_kernel(S6Kp p) {
+    static_assert(PASS == 0 || PASS == 1 || PASS == 3, "PASS: 0 whole sequence, 1 segment states, 3 segment scan");
+    static_assert(PASS == 0 || (!FUSE && !SAVE), "the segmented form is the plain scan");
+    constexpr bool YOUT = PASS != 1;     // this pass forms y
     constexpr int CW = kThreads / G;     // channels per block
     constexpr int EPT = 16 / G;          // (t, d) elements per thread per tile
     __shared__ __attribute__((aligned(16))) float sD[2][CW][kTS];
@@ -154,10 +175,15 @@ s6_scan_kernel(S6Kp p) {
     const int g = row % G;
     const int cl = (row / G) * 16 + k;                 // this lane's channel in the block
     const int64_t work = xcd_swizzle(blockIdx.x, gridDim.x);
-    const int64_t b = work / p.n_cblk;
-    const int64_t d0 = (work % p.n_cblk) * CW;
+    // segmented form: work = (segment, batch row, channel block), channel block fastest
+    const int64_t seg = PASS == 0 ? 0 : work / (p.batch * p.n_cblk);
+    const int64_t rest = PASS == 0 ? work : work % (p.batch * p.n_cblk);
+    const int64_t b = rest / p.n_cblk;
+    const int64_t d0 = (rest % p.n_cblk) * CW;
     const int64_t d = d0 + cl;
     const bool dok = d < p.Dm;
+    const int64_t T0 = seg * p.seg_len;                               // first step of this block
+    const int64_t Lk = PASS == 0 ? p.L : min(p.seg_len, p.L - T0);    // steps of this block
 
     // per-lane constants of the states this lane owns
     float Av[SPL], A2[SPL], iA[SPL], h[SPL];
@@ -171,7 +197,9 @@ s6_scan_kernel(S6Kp p) {
         Av[j] = ok ? -fminf(expf(al), kMaxAbsA) : 0.0f;   // A = -exp(A_log)
         A2[j] = Av[j] * kLog2e;                            // A*log2(e)
         iA[j] = ok ? -expf(-al) : 0.0f;                    // 1/A
-        h[j] = (ok && p.h0) ? p.h0[(b * p.Dm + d) * p.N + n] : 0.0f;
+        if constexpr (PASS == 0) h[j] = (ok && p.h0) ? p.h0[(b * p.Dm + d) * p.N + n] : 0.0f;
+        if constexpr (PASS == 1) h[j] = 0.0f;
+        if constexpr (PASS == 3) h[j] = ok ? p.h_in[((b * p.nseg + seg) * p.Dm + d) * p.N + n] : 0.0f;
     }
     // per-element constants of the (t, d) elements this thread stages/reduces
     float biasv[EPT], Dv[EPT];
@@ -212,19 +240,20 @@ s6_scan_kernel(S6Kp p) {
             const int e = tid + kThreads * i;
             const int tl = e / CW, c = e % CW;
             const int64_t dd = min(d0 + c, p.Dm - 1);
-            const int64_t off = (b * p.L + tl) * p.Dm + dd;     // time step tl of tile 0
+            const int64_t off = (b * p.L + T0 + tl) * p.Dm + dd;     // time step tl of tile 0
             q.dt[i] = p.dt + off;
             q.u[i] = u + off;
             q.z[i] = (FUSE && p.z) ? static_cast<const TIN *>(p.z) + off : u + off;
-            q.y[i] = p.y + (b * p.L + tl) * p.Dm + d0 + c;
+            q.y[i] = p.y + (b * p.L + T0 + tl) * p.Dm + d0 + c;
         }
 #pragma unroll
         for (int j = 0; j < SPL; ++j) q.nidx[j] = (int)min((int64_t)g * SPL + j, p.N - 1);
-        const int64_t off = (b * p.L + k) * p.N;
+        const int64_t off = (b * p.L + T0 + k) * p.N;
         q.B = static_cast<const TIN *>(p.B) + off;
         q.C = static_cast<const TIN *>(p.C) + off;
     }
-    const int64_t ntiles = (p.L + kT - 1) / kT;
+    const int64_t ntiles = (Lk + kT - 1) / kT;
+    double dsum_acc = 0.0;   // PASS 1: this thread's sum of delta (one channel per thread)
     // Two register sets alternate between even and odd tiles, so that loads in
     // flight are never copied (a copy would force a wait on them).  The set of
     // tile k is loaded while tile k-2 is scanned; its dt/u are staged to LDS
@@ -239,8 +268,9 @@ s6_scan_kernel(S6Kp p) {
             const int e = tid + kThreads * i;
             const int tl = e / CW, c = e % CW;
             bool ok = cval[i];
-            if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < p.L);
+            if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < Lk);
             const float dl = ok ? softplus(R.dt[i] + biasv[i]) : 0.0f;
+            if constexpr (PASS == 1) dsum_acc += (double)dl;
             float uu;
             if constexpr (FUSE) {
                 float xk[kMaxConv] = {R.u[i], R.f.xh[i][0], R.f.xh[i][1], R.f.xh[i][2]};
@@ -293,17 +323,22 @@ s6_scan_kernel(S6Kp p) {
                     const float beta = MODE == 0 ? zh.beta : MODE == 1 ? dl : 1.0f;
                     const float bu = row_bcast<t>(Bm[j]) * uu;   // B[t, n] * u[t, d]
                     h[j] = fmaf(ab, h[j], beta * bu);
-                    if (j == 0) ys = row_bcast<t>(Cm[j]) * h[j];
-                    else ys = fmaf(row_bcast<t>(Cm[j]), h[j], ys);
+                    if constexpr (YOUT) {
+                        if (j == 0) ys = row_bcast<t>(Cm[j]) * h[j];
+                        else ys = fmaf(row_bcast<t>(Cm[j]), h[j], ys);
+                    }
                 }
                 yp[t] = ys;
             });
+            if constexpr (YOUT) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sY[buf][g][(4 * q + i) * CW + cl] = yp[4 * q + i];
+                for (int i = 0; i < 4; ++i) sY[buf][g][(4 * q + i) * CW + cl] = yp[4 * q + i];
+            }
         });
     };
 
     auto reduce = [&](int buf, int64_t t0, auto chkTag) __attribute__((always_inline)) {
+        if constexpr (!YOUT) return;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int e = tid + kThreads * i;
@@ -313,7 +348,7 @@ s6_scan_kernel(S6Kp p) {
             for (int gg = 0; gg < G; ++gg) s += sY[buf][gg][tl * CW + c];
             if constexpr (FUSE) s *= gate_prev[i];
             bool ok = cval[i];
-            if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < p.L);
+            if constexpr (decltype(chkTag)::value) ok = ok && (t0 + tl < Lk);
             if (ok) q.y[i][t0 * p.Dm] = s;
         }
     };
@@ -348,7 +383,7 @@ s6_scan_kernel(S6Kp p) {
         reduce(buf ^ 1, (kt - 1) * kT, std::false_type{});
         shift();
         stage(buf ^ 1, (kt + 1) * kT, Rn, std::false_type{});
-        load_raw<false>(Rk, q, p, (kt + 2) * kT, tid, k);
+        load_raw<false, YOUT>(Rk, q, p, Lk, (kt + 2) * kT, tid, k);
         __syncthreads();
     };
     auto body_checked = [&](int64_t kt, Raw<TIN, G, SPL, FUSE> &Rk, const Raw<TIN, G, SPL, FUSE> &Rn)
@@ -359,12 +394,12 @@ s6_scan_kernel(S6Kp p) {
         if (kt >= 1) reduce(buf ^ 1, (kt - 1) * kT, std::true_type{});
         shift();
         if (kt + 1 < ntiles) stage(buf ^ 1, (kt + 1) * kT, Rn, std::true_type{});
-        if (kt + 2 < ntiles) load_raw<true>(Rk, q, p, (kt + 2) * kT, tid, k);
+        if (kt + 2 < ntiles) load_raw<true, YOUT>(Rk, q, p, Lk, (kt + 2) * kT, tid, k);
         __syncthreads();
     };
     // The unchecked body of tile kt loads tile kt+2, so a pair (kt, kt+1) of
     // unchecked bodies needs tiles up to kt+3 to lie wholly inside the sequence.
-    const int64_t nfull = p.L / kT;
+    const int64_t nfull = Lk / kT;
     auto run = [&]() __attribute__((always_inline)) {
         int64_t kt = 0;
         if (ntiles >= 4) {
@@ -380,14 +415,31 @@ s6_scan_kernel(S6Kp p) {
         }
     };
 
-    load_raw<true>(RA, q, p, 0, tid, k);
-    if (ntiles > 1) load_raw<true>(RB, q, p, kT, tid, k);
+    load_raw<true, YOUT>(RA, q, p, Lk, 0, tid, k);
+    if (ntiles > 1) load_raw<true, YOUT>(RB, q, p, Lk, kT, tid, k);
     stage(0, 0, RA, std::true_type{});
     __syncthreads();
     run();
     reduce((int)((ntiles - 1) & 1), (ntiles - 1) * kT, std::true_type{});
 
-    if (p.h_final) {
+    if constexpr (PASS == 1) {
+        // the segment's local state, and its sum of delta: the G threads of a
+        // channel (tid = c + CW r) add their partial sums in a fixed order
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const int64_t n = (int64_t)g * SPL + j;
+            if (dok && n < p.N) p.h_loc[((b * (p.nseg - 1) + seg) * p.Dm + d) * p.N + n] = h[j];
+        }
+        double *sS = reinterpret_cast<double *>(&sY[0][0][0]);   // sY is unused in this pass
+        sS[tid] = dsum_acc;
+        __syncthreads();
+        if (tid < CW && d0 + tid < p.Dm) {
+            double sacc = 0.0;
+#pragma unroll
+            for (int r = 0; r < G; ++r) sacc += sS[r * CW + tid];
+            p.dsum[(b * (p.nseg - 1) + seg) * p.Dm + d0 + tid] = sacc;
+        }
+    } else if (p.h_final && (PASS == 0 || seg == p.nseg - 1)) {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
             const int64_t n = (int64_t)g * SPL + j;
@@ -396,21 +448,22 @@ s6_scan_kernel(S6Kp p) {
     }
 }
 
-template <typename TIN, int G, int SPL, int MODE, bool FUSE, bool SAVE = false>
+template <typename TIN, int G, int SPL, int MODE, bool FUSE, bool SAVE = false, int PASS = 0>
 hipError_t launch_t(const S6Kp &kp, hipStream_t s) {
     constexpr int CW = kThreads / G;
     S6Kp p = kp;
     p.n_cblk = (p.Dm + CW - 1) / CW;
-    const int64_t nblk = p.batch * p.n_cblk;
-    hipLaunchKernelGGL((s6_scan_kernel<TIN, G, SPL, MODE, FUSE, SAVE>), dim3((unsigned)nblk), dim3(kThreads), 0, s, p);
+    const int64_t nseg_run = PASS == 0 ? 1 : PASS == 1 ? p.nseg - 1 : p.nseg;   // segments in this launch
+    const int64_t nblk = p.batch * p.n_cblk * nseg_run;
+    hipLaunchKernelGGL((s6_scan_kernel<TIN, G, SPL, MODE, FUSE, SAVE, PASS>), dim3((unsigned)nblk), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <typename TIN, int G, int SPL, bool FUSE, bool SAVE = false>
+template <typename TIN, int G, int SPL, bool FUSE, bool SAVE = false, int PASS = 0>
 hipError_t launch_mode(const S6Kp &kp, int mode, hipStream_t s) {
-    if (mode == 0) return launch_t<TIN, G, SPL, 0, FUSE, SAVE>(kp, s);
-    if (mode == 1) return launch_t<TIN, G, SPL, 1, FUSE, SAVE>(kp, s);
-    return launch_t<TIN, G, SPL, 2, FUSE, SAVE>(kp, s);
+    if (mode == 0) return launch_t<TIN, G, SPL, 0, FUSE, SAVE, PASS>(kp, s);
+    if (mode == 1) return launch_t<TIN, G, SPL, 1, FUSE, SAVE, PASS>(kp, s);
+    return launch_t<TIN, G, SPL, 2, FUSE, SAVE, PASS>(kp, s);
 }
 
 // the SAVE form, for the state sizes the S6 backward takes (N <= 16)
@@ -422,6 +475,17 @@ hipError_t launch_shape_save(const S6Kp &kp, int mode, hipStream_t s) {
     if (N <= 4) return launch_mode<TIN, 4, 1, false, true>(kp, mode, s);
     if (N <= 8) return launch_mode<TIN, 8, 1, false, true>(kp, mode, s);
     return launch_mode<TIN, 16, 1, false, true>(kp, mode, s);
+}
+
+// the segmented passes, for the state sizes the segmented plan takes (N <= 16)
+template <typename TIN, int PASS>
+hipError_t launch_shape_seg(const S6Kp &kp, int mode, hipStream_t s) {
+    const int64_t N = kp.N;
+    if (N <= 1) return launch_mode<TIN, 1, 1, false, false, PASS>(kp, mode, s);
+    if (N <= 2) return launch_mode<TIN, 2, 1, false, false, PASS>(kp, mode, s);
+    if (N <= 4) return launch_mode<TIN, 4, 1, false, false, PASS>(kp, mode, s);
+    if (N <= 8) return launch_mode<TIN, 8, 1, false, false, PASS>(kp, mode, s);
+    return launch_mode<TIN, 16, 1, false, false, PASS>(kp, mode, s);
 }
 
 template <typename TIN, bool FUSE>

@@ -16,6 +16,10 @@ hipError_t launch_s6(const S6Args &a, hipStream_t stream, const char **kernel_na
                       a.h0, a.h_final, nullptr, nullptr, a.batch, a.L, a.d_inner, a.d_state, 1, a.bf16, a.flags};
         return launch_s6_step(f, false, stream, kernel_name);
     }
+    if (a.workspace) {   // few channel blocks over a long sequence: time segments joined by a carry
+        const S6SegPlan pl = s6_seg_plan(a.batch, a.L, a.d_inner, a.d_state);
+        if (pl.nseg > 1) return launch_s6_segmented(a, pl, stream, kernel_name);
+    }
     return a.bf16 ? launch_shape<uint16_t, false>(p, mode, stream) : launch_shape<float, false>(p, mode, stream);
 }
 

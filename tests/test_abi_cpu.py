@@ -87,9 +87,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def _s6(lib, u=FAKE, dt=FAKE, A_log=FAKE, B=FAKE, C=FAKE, y=FAKE, dims=(2, 8, 16, 4), dtype=0,
-        flags=0, dt_bias=None, D=None, h0=None, hf=None):
+        flags=0, dt_bias=None, D=None, h0=None, hf=None, ws=None, wsb=0):
     return lib.ssm_s6_scan_fwd(u, dt, dt_bias, A_log, B, C, D, y, h0, hf, *dims, dtype, flags,
-                               None, 0, None)
+                               ws, wsb, None)
 
 
 def _err(lib):
@@ -107,7 +107,19 @@ def test_s6_argument_checks(lib):
     assert _s6(lib, flags=0x4) == INVALID
     assert _s6(lib, B=MIS) == UNSUPPORTED and "aligned" in _err(lib)
     assert _s6(lib, y=FAKE, u=FAKE) == INVALID and "alias" in _err(lib)
+    # the Mamba-1 layer shape fills the chip: the sequential walk, no workspace
     assert lib.ssm_s6_scan_fwd_workspace_size(8, 2048, 1536, 16) == 0
+    # one batch row at long context: 8 segments of 4096 steps, 96 blocks of 16 channels;
+    # workspace = local states (7 segments) + sums of delta + entering states (8 segments)
+    need = lib.ssm_s6_scan_fwd_workspace_size(1, 32768, 1536, 16)
+    assert need == 7 * 1536 * 16 * 4 + 7 * 1536 * 8 + 8 * 1536 * 16 * 4
+    assert lib.ssm_s6_scan_fwd_workspace_size(2, 8192, 1536, 16) > 0
+    assert lib.ssm_s6_scan_fwd_workspace_size(1, 1000, 1536, 16) == 0      # too short to split
+    assert lib.ssm_s6_scan_fwd_workspace_size(1, 32768, 1536, 32) == 0     # d_state > 16: walk
+    dims = (1, 32768, 1536, 16)
+    distinct = {n: ctypes.c_void_p(0x100000 * (i + 2)) for i, n in enumerate(("u", "dt", "A_log", "B", "C", "y"))}
+    assert _s6(lib, dims=dims, ws=FAKE, wsb=need - 1, **distinct) == WORKSPACE and "workspace" in _err(lib)
+    assert _s6(lib, dims=dims, ws=MIS, wsb=need, **distinct) == UNSUPPORTED and "aligned" in _err(lib)
 
 
 def _s6b(lib, dims=(2, 40, 20, 16), dtype=0, flags=0, ws=ctypes.c_void_p(0x900000), wsb=1 << 40,
