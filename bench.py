@@ -3,12 +3,21 @@
 
 A step is one call of the scan entry point over one batch of synthetic input
 already resident in HBM (for S6: softplus, discretisation, recurrence, state
-reduction and skip term, all inside one kernel).  The headline workload is the
-S6 scan at a Mamba-1 layer shape (batch 8, L 2048, d_inner 1536, N 16, fp32);
-the SSD, complex-SSD and trapezoidal (Mamba-3) SSD workloads and the two
-backward passes are measured the same way and reported under "secondary".  Prints ONE JSON line.
+reduction and skip term, all inside one kernel; for the chunked SSD paths, the
+segment-state, state-pass and chunk-scan kernels of one call).  The headline is
+the largest single-GPU workload, the long-context SSD (batch 2, L 32768, 80
+heads x 64, N 128, 8 groups, bf16 in, fp32 state and output); every one of the
+five workloads (S6 tiny, S6 at a Mamba-1 layer shape, SSD at a Mamba-2 shape,
+long-context SSD, complex SSD) gets a full line under "configs", each with its
+roofline and the fp64 oracle timed on the host cores; the other paths (Mamba-3,
+per-channel B/C, the layer, decode steps, backward passes, the segmented long
+S6) are under "secondary".  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary] [--no-cpu]
+
+--workload NAME measures that one workload alone in the headline schema (the
+profiling runs use it); NAME copy_1gib is a plain 1 GiB device copy, the
+reference for scaling the HBM byte counters.
 """
 from __future__ import annotations
 
@@ -36,19 +45,21 @@ MFMA_PEAKS = {
 FP32_VALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, non-packed fp32
 # fp32 VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz lane-slots/s (a wave64 op takes 4 cycles)
 VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
-# one ZOH state update (b, t, d, n) of S6: x = dl*A, Abar = exp2(x), beta = fma, B*u, beta*(B u),
-# h = fma, y += C*h: 6 single-rate fp32 ops + v_exp_f32 at half rate = 8 slots, 9 flops
-S6_SLOTS_PER_UPDATE = 8
-S6_FLOPS_PER_UPDATE = 9
-S6_ALU_PEAK_TFLOPS = VALU_SLOTS_PER_S / S6_SLOTS_PER_UPDATE * S6_FLOPS_PER_UPDATE / 1e12
-# HBM bytes per launch of s6_scan_kernel on s6_mamba1, from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE (KiB per dispatch) scaled by a 1 GiB device copy (fetch x 2.0, write x 1.0);
-# valid only for the kernel sources (s6_kernel.hpp + s6_scan.hip) with this sha1
-S6_TRAFFIC = {"src_sha1": "11d0001f54f53a72d99f6f2f881663881dc0a0a7", "bytes": (100242.0 * 2.0 + 99090.8 * 1.0) * 1024}
+# one ZOH state update (b, t, d, n) of the S6 kernel: x = dl*A, exp2 (half rate: 2 slots), the
+# (Abar-1)/A form, the 3-FMA series for phi1 and delta*p, compare + select, Abar = 1 + A beta,
+# B*u, beta*(B u), h = fma, y += C*h, and the partial-sum add of the reduction over states:
+# 15 single-rate ops + the exp = 17 issue slots (the compiled loop: 16.6 VALU instructions)
+S6_SLOTS_PER_UPDATE = 17
+S6_FLOPS_PER_UPDATE = 9          # the method's flops per update (the series is the exp's cost)
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled
+# by the same counters on a 1 GiB device copy (bench.py --workload copy_1gib); each entry is
+# valid only while the sha1 of the kernels' sources matches (profiles/*_traffic.md)
+TRAFFIC = {}
 # adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
 # (products and fmas, 24 flops) plus the recomputed Abar, beta, phi1' (not counted again)
 S6_BWD_FLOPS_PER_UPDATE = 24
 N_ROTATE = 3                     # input copies rotated between steps (> Infinity Cache)
+# (--copies 1 for the counter runs, where each dispatch is read on its own)
 
 
 def log(msg):
@@ -158,12 +169,17 @@ def conv_model(d):
 
 
 def cssd_model(d):
+    """Algorithmic bytes (x, y fp32; B, C complex per group; dt; the final state) and the
+    real-equivalent flops of the complex chunked decomposition, per (b, chunk): the complex
+    C.B^T once per group as two real GEMMs with K = 2 N_c (8 Q^2 N_c), and per head Re(M) X
+    (2 Q^2 P), the complex chunk state from real x (two real GEMMs, 4 Q P N_c) and Re(C h)
+    (one real GEMM with K = 2 N_c, 4 Q P N_c)."""
     B, L, H, P, Nc, G, Q = (d["batch"], d["L"], d["nheads"], d["headdim"], d["n_complex"],
                             d["ngroups"], d["chunk_len"])
     elems = B * L * H * P
     bytes_ = elems * 4 * 2 + 2 * B * L * G * Nc * 8 + B * L * H * 4 + B * H * P * Nc * 8
     nc = -(-L // Q)
-    flops = 2 * B * nc * H * (4 * Q * Q * Nc + Q * Q * P + 2 * 4 * Q * P * Nc)
+    flops = B * nc * (G * 8 * Q * Q * Nc + H * (2 * Q * Q * P + 8 * Q * P * Nc))
     return elems, bytes_, flops
 
 
@@ -185,6 +201,16 @@ def make_runner(name, dev):
     import synth
     # name suffixes: _bwd (the backward), _bwd_saved (the backward reading the forward's saved
     # states), _fwd_save (the forward that saves them)
+    if name == "copy_1gib":       # the reference copy for the HBM byte counters
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+
+        def step(i):
+            dst.copy_(src)
+        return step, {"bytes": 2 << 30}, {"kind": "copy", "dtype": "f32"}, ["copy"]
+    walk = name.endswith("_walk")      # the S6 scan without a workspace: the sequential walk
+    if walk:
+        name = name[: -len("_walk")]
     saved = name.endswith("_bwd_saved")
     save = name.endswith("_fwd_save")
     if saved:
@@ -309,11 +335,18 @@ def make_runner(name, dev):
         t0 = copies[0]
         y = torch.empty_like(t0["u"], dtype=torch.float32)
         hf = torch.empty((dims["batch"], dims["d_inner"], dims["d_state"]), dtype=torch.float32, device=dev)
+        nws = 0 if walk else lib.ssm_s6_scan_fwd_workspace_size(dims["batch"], dims["L"], dims["d_inner"],
+                                                                dims["d_state"])
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
 
         def step(i):
             t = copies[i % N_ROTATE]
             lib.ssm_s6_scan_fwd(t["u"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
-                                None, y=y, h_final=hf)
+                                None, y=y, h_final=hf, workspace=ws)
+        if ws is not None:
+            dims = dict(dims, segmented=True)
+            return step, dims, w, ["s6_scan_kernel (segment states)", "s6_seg_carry_kernel",
+                                   "s6_scan_kernel (segment scan)"]
         return step, dims, w, ["s6_scan_kernel"]
     if kind == "trap" and bwd:
         d = dims
@@ -502,23 +535,51 @@ def graph_us_per_step(step, n=32, replays=20):
     return a.elapsed_time(b) * 1e3 / (replays * n)
 
 
-def cpu_baseline_s6(name):
-    """The fp64 oracle, untuned, on the host cores: the whole workload."""
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_s6(name, one_thread_channels=64):
+    """The fp64 oracle, untuned, on the host cores: the whole workload on every thread, and
+    a sample of channels of batch row 0 on one thread (the single-core rate)."""
     import numpy as np
     import oracle
     import synth
     inp = synth.workload_inputs(name, seed=(0,))
     d = inp.dims
     nthr = oracle.default_threads()
-    t0 = time.perf_counter()
-    if d.get("ngroups"):
-        oracle.s6_grouped_fwd(**inp.arrays, nthreads=nthr)
-    else:
-        oracle.s6_fwd(**inp.arrays, nthreads=nthr)
-    sec = time.perf_counter() - t0
     elems = d["batch"] * d["L"] * d["d_inner"]
-    return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
-            "sample": f"whole {name} workload ({elems} elements, fp64, {sec:.2f} s wall on {nthr} threads)"}
+    fn = oracle.s6_grouped_fwd if d.get("ngroups") else oracle.s6_fwd
+    reps, t0 = 0, time.perf_counter()
+    while True:            # a tiny workload is repeated to about half a second
+        fn(**inp.arrays, nthreads=nthr)
+        reps += 1
+        sec = time.perf_counter() - t0
+        if sec > 0.5 or elems * reps > 1e7:
+            break
+    out = {"value": elems * reps / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
+           "sample": f"whole {name} workload ({elems} elements x {reps} runs, fp64, {sec:.3f} s wall on "
+                     f"{nthr} threads)", "cpu_model": cpu_model()}
+    nch = min(one_thread_channels, d["d_inner"])
+    units = np.stack([np.zeros(nch, np.int64), np.arange(nch)], 1)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn(**inp.arrays, units=units, nthreads=1)
+        reps += 1
+        sec1 = time.perf_counter() - t0
+        if sec1 > 0.5:
+            break
+    e1 = nch * d["L"]
+    out["value_1thread"] = e1 * reps / sec1
+    out["sample_1thread"] = f"{nch} channels of batch row 0 ({e1} elements x {reps} runs, fp64, {sec1:.3f} s, 1 thread)"
+    return out
 
 
 def cpu_baseline_s6_layer(name):
@@ -637,21 +698,28 @@ def cpu_baseline_units(name, n_units):
                       f"({elems} elements, {sec:.2f} s wall)"}
 
 
-def s6_kernel_sha1():
-    """sha1 of the S6 forward kernel's sources (the kernel template and its instantiation)."""
+# the sources each workload's kernels are built from (for the counter-traffic table)
+TRAFFIC_SOURCES = {
+    "s6": ("device_common.hpp", "s6_kernel.hpp", "s6_scan.hip"),
+    "ssd": ("device_common.hpp", "ssd_scan.hip"),
+    "cssd": ("device_common.hpp", "cssd_scan.hip"),
+}
+
+
+def src_sha1(kind):
     import hashlib
     h = hashlib.sha1()
-    for f in ("s6_kernel.hpp", "s6_scan.hip"):
+    for f in TRAFFIC_SOURCES.get(kind, ()):
         h.update(open(os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
 
-def s6_traffic(name):
-    """Counter-measured HBM bytes per launch, or None if the kernel changed since."""
-    sha = s6_kernel_sha1()
-    if name != "s6_mamba1" or sha != S6_TRAFFIC["src_sha1"]:
+def counter_traffic(name, kind):
+    """Counter-measured HBM bytes per call, or None if the kernels changed since."""
+    ent = TRAFFIC.get(name)
+    if ent is None or kind not in TRAFFIC_SOURCES or src_sha1(kind) != ent["src_sha1"]:
         return None
-    return round(S6_TRAFFIC["bytes"])
+    return round(ent["bytes"])
 
 
 def measure(name, dev, steps, warmup):
@@ -663,7 +731,9 @@ def measure(name, dev, steps, warmup):
     dims = dict(dims, chunk_len=w.get("chunk_len"))
     if w.get("carry"):
         dims["carry"] = True
-    if kind == "s6":
+    if kind == "copy":
+        elems, bytes_, ops = dims["bytes"] // 8, dims["bytes"], 0
+    elif kind == "s6":
         elems, bytes_, ops = s6_model(dims)
     elif kind == "s6_layer":
         elems, bytes_, ops = s6_layer_model(dims)
@@ -696,15 +766,115 @@ def measure(name, dev, steps, warmup):
                 event_ms=per, elems=elems, bytes=bytes_, ops=ops, kernels=kernels, graph_us=graph_us)
 
 
+HEADLINE = "ssd_long"
+# the five workloads of the scope, in order: S6 tiny, S6 Mamba-1 layer, SSD Mamba-2 layer,
+# long-context SSD, complex SSD
+CONFIGS = ("s6_tiny", "s6_mamba1", "ssd_mamba2", "ssd_long", "cssd_mamba3")
+SECONDARY = (("s6_long", 10), ("s6_long_walk", 5), ("cssd_mimo_mamba3", 5), ("s6_pc_mamba1", 10),
+             ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
+             ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
+             ("s6_mamba1_bwd", 10), ("s6_mamba1_fwd_save", 10), ("s6_mamba1_bwd_saved", 10),
+             ("s6_pc_mamba1_fwd_save", 5), ("s6_pc_mamba1_bwd_saved", 5), ("s6_pc_mamba1_bwd", 5),
+             ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5))
+
+
+def roofline(m):
+    """The roofline object of one measured workload: the bound its path is priced on, the
+    achieved rate from the algorithmic bytes or flops of a call over the call's HIP-event
+    time (median), the counter traffic when it is current, and labelled extra fractions."""
+    kind, name = m["kind"], m["name"]
+    ev_s = m["event_ms_median"] * 1e-3
+    gbs = m["bytes"] / ev_s / 1e9
+    kern = {"kernel": " + ".join(m["kernels"]), "kernel_ms": round(m["event_ms_median"], 5)}
+    if kind == "s6":
+        # priced on HBM; the issue-slot fraction of the instruction mix is an extra field
+        updates = m["elems"] * m["dims"]["d_state"]
+        slots_frac = updates * S6_SLOTS_PER_UPDATE / ev_s / VALU_SLOTS_PER_S
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(name, "s6"),
+                "algorithmic_bytes": m["bytes"], **kern,
+                "issue_slot_frac": round(slots_frac, 4),
+                "issue_slot_basis": f"{S6_SLOTS_PER_UPDATE} fp32 VALU issue slots per state update (exact "
+                                    "hold incl.), 39.3 T lane-slots/s (256 CU x 4 SIMD x 16 lanes x 2.4 GHz)"}
+    if kind in MFMA_PEAKS and m["dims"].get("L", 2) > 1:
+        tf = m["ops"] / ev_s / 1e12
+        pk, basis = MFMA_PEAKS[kind]
+        tr_kind = "ssd" if kind in ("ssd", "trap") else "cssd" if kind in ("cssd", "cssd_mimo") else None
+        return {"bound": "mfma", "achieved": round(tf, 2), "peak": pk, "unit": "TFLOP/s",
+                "frac": round(tf / pk, 4), "traffic": counter_traffic(name, tr_kind) if tr_kind else None,
+                "algorithmic_flops": m["ops"], "peak_basis": basis, **kern,
+                "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": m["bytes"]}
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": m["bytes"], **kern}
+
+
+def cpu_baseline(name, kind):
+    if kind in ("s6", "s6_pc", "s6_save", "s6_pc_save"):
+        return cpu_baseline_s6(name)
+    if kind == "s6_bwd":
+        return cpu_baseline_s6_bwd(name)
+    if kind == "s6_layer":
+        return cpu_baseline_s6_layer(name)
+    if kind in ("ssd_bwd", "trap_bwd"):
+        return cpu_baseline_ssd_bwd(name)
+    out = cpu_baseline_units(name, 16)
+    out["cpu_model"] = cpu_model()
+    return out
+
+
+def dtype_of(m):
+    return {"s6": "f32", "cssd": "f32"}.get(m["kind"], "bf16" if m["dtype"] == "bf16" else "f32")
+
+
+def config_line(m):
+    return {"workload": m["name"], "value": round(m["elems"] / (m["ms"] * 1e-3), 1), "unit": "elements/s",
+            "ms_per_step": round(m["ms"], 5), "dtype": dtype_of(m),
+            "config": {k: v for k, v in m["dims"].items() if v is not None}, "roofline": roofline(m)}
+
+
+def secondary_line(s):
+    es = s["event_ms_median"] * 1e-3
+    ent = {"workload": s["name"], "value": round(s["elems"] / (s["ms"] * 1e-3), 1), "unit": "elements/s",
+           "ms_per_step": round(s["ms"], 4), "kernel_ms": round(s["event_ms_median"], 4),
+           "hbm_GBps": round(s["bytes"] / es / 1e9, 1), "hbm_frac": round(s["bytes"] / es / 1e9 / HBM_PEAK_GBS, 4)}
+    if s["kind"] in ("s6", "s6_layer", "s6_pc", "s6_save", "s6_pc_save"):
+        upd = s["elems"] * s["dims"]["d_state"]
+        ent["issue_slot_frac"] = round(upd * S6_SLOTS_PER_UPDATE / es / VALU_SLOTS_PER_S, 4)
+        if s["dims"].get("segmented"):
+            ent["segmented"] = True
+        if s["dims"]["L"] == 1:
+            ent["us_per_step_eager"] = round(s["event_ms_median"] * 1e3, 2)
+            ent["us_per_step_graph"] = round(s["graph_us"], 2)
+    elif s["kind"] == "s6_bwd":
+        ent["fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
+    elif s["kind"] in ("ssd_bwd", "trap_bwd"):
+        ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
+        ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
+        ent["mfma_basis"] = "executed 16x16x4 fp32 MFMAs of the walks"
+    elif s["kind"] in ("cssd", "cssd_mimo"):
+        ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
+        ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
+    elif s["kind"] in ("ssd", "trap") and s["dims"]["L"] == 1:
+        ent["us_per_step_eager"] = round(s["event_ms_median"] * 1e3, 2)
+        ent["us_per_step_graph"] = round(s["graph_us"], 2)
+    elif s["kind"] in ("ssd", "trap"):
+        ent["mfma_TFLOPs"] = round(s["ops"] / es / 1e12, 1)
+        ent["mfma_frac_bf16"] = round(s["ops"] / es / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+    return ent
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="s6_mamba1")
+    ap.add_argument("--workload", default=None, help="measure this workload alone (headline schema)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copies", type=int, default=N_ROTATE, help="input copies rotated between steps")
     args = ap.parse_args()
+    globals()["N_ROTATE"] = max(1, args.copies)
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); the scan "
               "shards over batch and heads with no communication, and no multi-GPU path exists here.",
@@ -713,112 +883,62 @@ def main():
 
     import torch
     dev = torch.device("cuda:0")
-    import synth
 
-    log(f"[bench] headline {args.workload}: warmup {args.warmup}, steps {args.steps}")
-    m = measure(args.workload, dev, args.steps, args.warmup)
-    kind = m["kind"]
-    ev_s = m["event_ms_median"] * 1e-3
-    gbs = m["bytes"] / ev_s / 1e9
-    if kind == "s6":
-        tf = m["ops"] / ev_s / 1e12
-        roof = {"bound": "alu", "achieved": round(tf, 3), "peak": round(S6_ALU_PEAK_TFLOPS, 2),
-                "unit": "TFLOP/s", "frac": round(tf / S6_ALU_PEAK_TFLOPS, 4),
-                "traffic": s6_traffic(args.workload),
-                "peak_basis": "fp32 VALU issue 39.3 T lane-slots/s; 8 slots and 9 flops per state update",
-                "kernel": "s6_scan_kernel", "kernel_ms": round(m["event_ms_median"], 5),
-                "fma_peak": FP32_VALU_PEAK_TFLOPS, "fma_frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
-                "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    elif kind in MFMA_PEAKS and m["dims"]["L"] > 1:
-        # the chunked paths are contractions on the matrix cores (executed flops of the model)
-        tf = m["ops"] / ev_s / 1e12
-        pk, basis = MFMA_PEAKS[kind]
-        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": pk, "unit": "TFLOP/s",
-                "frac": round(tf / pk, 4), "traffic": None, "peak_basis": basis,
-                "kernel": "+".join(m["kernels"]), "kernel_ms": round(m["event_ms_median"], 5),
-                "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "+".join(m["kernels"]), "kernel_ms": round(m["event_ms_median"], 5)}
-    value = m["elems"] / (m["ms"] * 1e-3)
+    single = args.workload is not None
+    head = args.workload or HEADLINE
+    log(f"[bench] headline {head}: warmup {args.warmup}, steps {args.steps}")
+    m = measure(head, dev, args.steps, args.warmup)
+    if m["kind"] == "copy":
+        gbs = m["bytes"] / (m["event_ms_median"] * 1e-3) / 1e9
+        print(json.dumps({"workload": "copy_1gib", "bytes_per_call": m["bytes"], "event_ms_median":
+                          round(m["event_ms_median"], 5), "GBps": round(gbs, 1)}), flush=True)
+        return
+    line = config_line(m)
     out = {
         "metric": "scan elements/s (batch*L*d_inner)",
-        "value": round(value, 1),
+        "value": line["value"],
         "unit": "elements/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(m["ms"], 5),
+        "ms_per_step": line["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if m["dtype"] == "f32" else "bf16-in/f32-acc",
+        "dtype": line["dtype"],
         "data": "synthetic",
-        "config": {"workload": args.workload, **{k: v for k, v in m["dims"].items() if v is not None}},
-        "roofline": roof,
+        "config": {"workload": head, **line["config"]},
+        "roofline": line["roofline"],
     }
-    if not args.no_secondary and args.workload == "s6_mamba1":
+    if not args.no_cpu:
+        log(f"[bench] cpu baseline (oracle) {head}")
+        out["cpu_baseline"] = cpu_baseline(head, m["kind"])
+    if not single:
+        cfgs = []
+        for name in CONFIGS:
+            if name == head:
+                c = dict(line)
+                if "cpu_baseline" in out:
+                    c["cpu_baseline"] = out["cpu_baseline"]
+            else:
+                log(f"[bench] config {name}")
+                cm = measure(name, dev, args.steps, args.warmup)
+                c = config_line(cm)
+                if not args.no_cpu:
+                    c["cpu_baseline"] = cpu_baseline(name, cm["kind"])
+                del cm
+                torch.cuda.empty_cache()
+            cfgs.append(c)
+        out["configs"] = cfgs
+    if not single and not args.no_secondary:
         sec = []
-        for name, steps in (("ssd_mamba2", 10), ("ssd_long", 5), ("cssd_mamba3", 5), ("cssd_mimo_mamba3", 5), ("s6_pc_mamba1", 10),
-                            ("trap_mamba3", 5), ("trap_rot_mamba3", 5), ("conv_mamba2", 10), ("s6_layer_mamba1", 10),
-                            ("s6_decode_mamba1", 50), ("ssd_decode_mamba2", 50), ("trap_decode_mamba3", 50),
-                            ("s6_mamba1_bwd", 10), ("s6_mamba1_fwd_save", 10), ("s6_mamba1_bwd_saved", 10),
-                            ("s6_pc_mamba1_fwd_save", 5), ("s6_pc_mamba1_bwd_saved", 5),
-                            ("s6_pc_mamba1_bwd", 5),
-                            ("ssd_mamba2_bwd", 5), ("trap_mamba3_bwd", 5)):
+        for name, steps in SECONDARY:
             log(f"[bench] secondary {name}")
             s = measure(name, dev, steps, 2)
-            es = s["event_ms_median"] * 1e-3
-            ent = {"workload": name, "value": round(s["elems"] / (s["ms"] * 1e-3), 1),
-                   "unit": "elements/s", "ms_per_step": round(s["ms"], 4),
-                   "hbm_GBps": round(s["bytes"] / es / 1e9, 1),
-                   "hbm_frac": round(s["bytes"] / es / 1e9 / HBM_PEAK_GBS, 4)}
-            if s["kind"] == "s6_bwd":
-                ent["fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
-                ent["kernel_ms"] = round(s["event_ms_median"], 4)
-            elif s["kind"] == "s6_layer":
-                ent["kernel_ms"] = round(s["event_ms_median"], 4)
-                ent["alu_frac"] = round(s["ops"] / es / 1e12 / S6_ALU_PEAK_TFLOPS, 4)
-                if s["dims"]["L"] == 1:
-                    ent["us_per_step_eager"] = round(s["event_ms_median"] * 1e3, 2)
-                    ent["us_per_step_graph"] = round(s["graph_us"], 2)
-            elif s["kind"] in ("ssd_bwd", "trap_bwd"):
-                ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
-                ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
-                ent["kernel_ms"] = round(s["event_ms_median"], 4)
-            elif s["kind"] in ("cssd", "cssd_mimo"):
-                ent["mfma_fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
-                ent["mfma_frac_fp32"] = round(s["ops"] / es / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
-            elif s["kind"] in ("ssd", "trap") and s["dims"]["L"] == 1:
-                ent["us_per_step_eager"] = round(s["event_ms_median"] * 1e3, 2)
-                ent["us_per_step_graph"] = round(s["graph_us"], 2)
-            elif s["kind"] in ("ssd", "trap"):
-                ent["mfma_TFLOPs"] = round(s["ops"] / es / 1e12, 1)
-                ent["mfma_frac_bf16"] = round(s["ops"] / es / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
-            else:
-                ent["fp32_TFLOPs"] = round(s["ops"] / es / 1e12, 2)
-            sec.append(ent)
+            sec.append(secondary_line(s))
             del s
             torch.cuda.empty_cache()
         out["secondary"] = sec
-    if not args.no_cpu:
-        log("[bench] cpu baseline (oracle)")
-        base = args.workload
-        for suffix in ("_bwd_saved", "_fwd_save", "_bwd"):
-            if base.endswith(suffix):
-                base = base[: -len(suffix)]
-                break
-        if kind in ("s6", "s6_pc", "s6_save", "s6_pc_save"):
-            out["cpu_baseline"] = cpu_baseline_s6(base)
-        elif kind == "s6_bwd":
-            out["cpu_baseline"] = cpu_baseline_s6_bwd(base)
-        elif kind == "s6_layer":
-            out["cpu_baseline"] = cpu_baseline_s6_layer(args.workload)
-        elif kind in ("ssd_bwd", "trap_bwd"):
-            out["cpu_baseline"] = cpu_baseline_ssd_bwd(args.workload)
-        else:
-            out["cpu_baseline"] = cpu_baseline_units(args.workload, 16)
     print(json.dumps(out), flush=True)
 
 

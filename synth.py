@@ -23,6 +23,9 @@ WORKLOADS = {
     # S6 at a Mamba-1 layer shape: 8 x 2048 x 1536, N=16, fp32
     "s6_mamba1": dict(kind="s6", batch=8, L=2048, d_inner=1536, d_state=16, dtype="f32",
                       dt_bias="uniform", D="normal"),
+    # that scan at long context for one sequence: 1 x 32768 x 1536, N=16 (the segmented scan)
+    "s6_long": dict(kind="s6", batch=1, L=32768, d_inner=1536, d_state=16, dtype="f32",
+                    dt_bias="uniform", D="normal"),
     # that scan with B, C per channel (d_inner groups of one): 16x the B/C bytes
     "s6_pc_mamba1": dict(kind="s6", batch=8, L=2048, d_inner=1536, d_state=16, dtype="f32",
                          dt_bias="uniform", D="normal", ngroups=1536),
