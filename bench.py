@@ -53,8 +53,25 @@ S6_SLOTS_PER_UPDATE = 17
 S6_FLOPS_PER_UPDATE = 9          # the method's flops per update (the series is the exp's cost)
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled
 # by the same counters on a 1 GiB device copy (bench.py --workload copy_1gib); each entry is
-# valid only while the sha1 of the kernels' sources matches (profiles/*_traffic.md)
-TRAFFIC = {}
+# valid only while the sha1 of the kernels' sources matches (profiles/*.md, "HBM traffic")
+TRAFFIC = {
+    "s6_mamba1": {
+        "src_sha1": "138bc04ec70d50e744b2cc62138b54e2f6435f4d",
+        "bytes": 308885163
+    },
+    "ssd_mamba2": {
+        "src_sha1": "d6c4b3104807a80a4751a9c565e5f72d8a4887e1",
+        "bytes": 502653439
+    },
+    "ssd_long": {
+        "src_sha1": "d6c4b3104807a80a4751a9c565e5f72d8a4887e1",
+        "bytes": 3591845848
+    },
+    "cssd_mamba3": {
+        "src_sha1": "e1f701c6580d12e54c97d7e516054ab31c714f40",
+        "bytes": 845981900
+    }
+}
 # adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
 # (products and fmas, 24 flops) plus the recomputed Abar, beta, phi1' (not counted again)
 S6_BWD_FLOPS_PER_UPDATE = 24
