@@ -351,6 +351,27 @@ int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, con
                        int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ssd_chunk_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace: the segment states go to the library's static device
+ * scratch, SSM_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held by each GPU the
+ * library runs on until the process ends; its address on a device is looked up
+ * on the first call there.  The call allocates and frees nothing.
+ * Arguments, layouts, limits and results are those of ssd_chunk_scan_fwd (the
+ * same kernels, bit for bit), plus: a shape whose segment states need more than
+ * the scratch (ssd_chunk_scan_fwd_workspace_size() > SSM_NOALLOC_SCRATCH_BYTES)
+ * returns SSM_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (concurrent streams, or
+ * threads) race on it and must be serialised by the caller.  Nothing in the
+ * scratch needs to start at zero (each call writes every slot it reads). */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *dt_bias, const float *A_log,
+                               const void *B, const void *C, const float *D, float *y,
+                               const float *h0, float *h_final,
+                               int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                               int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
+                               hipStream_t stream);
+
 /* -------------------------------------------------------- SSD backward ----
  * Gradients of a scalar loss through the SSD scan above, given dy = dL/dy and
  * optionally dh_final = dL/dh_final: the reverse-time chain rule of the

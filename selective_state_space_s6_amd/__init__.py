@@ -27,6 +27,7 @@ __all__ = [
     "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_fwd_workspace_size",
     "ssd_cplx_chunk_scan_fwd_workspace_size", "ssd_cplx_mimo_chunk_scan_fwd",
     "ssd_cplx_mimo_chunk_scan_fwd_workspace_size", "ssm_last_error", "SsmError", "LIB_PATH",
+    "ssd_chunk_scan_fwd_noalloc",
     "SSM_BBAR_ZOH", "SSM_BBAR_DT", "SSM_BBAR_ONE", "SSM_CPLX_STABLE", "SSM_CPLX_DOC",
     "SSM_CPLX_CODE", "SSM_CPLX_CONJ_C", "SSM_F32", "SSM_BF16",
 ]
@@ -74,6 +75,8 @@ _lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_chunk_scan_fwd_workspace_size.restype = _Z
 _lib.ssd_chunk_scan_fwd.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
 _lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
+_lib.ssd_chunk_scan_fwd_noalloc.argtypes = [_P] * 10 + [_I] * 7 + [ctypes.c_int, ctypes.c_uint32, _P]
+_lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
 _lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [_I] * 7
 _lib.ssd_chunk_scan_bwd_workspace_size.restype = _Z
 _lib.ssd_chunk_scan_bwd.argtypes = [_P] * 18 + [_I] * 7 + [ctypes.c_int, ctypes.c_uint32, _P, _Z, _P]
@@ -547,6 +550,36 @@ def ssd_chunk_scan_fwd(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=256
                                  _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L, H, P, N, G,
                                  chunk_len, _in_dtype(x), flags, _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ssd_chunk_scan_fwd_noalloc(x, dt, dt_bias, A_log, B, C, D, h0=None, *, chunk_len=256,
+                               flags=SSM_BBAR_DT, return_final=False, y=None, h_final=None):
+    """ssd_chunk_scan_fwd without a workspace: the segment states live in the library's
+    static device scratch (32 MiB per GPU), so the call allocates nothing when y (and
+    h_final) are given.  Calls that overlap on one GPU race on the scratch."""
+    dev = x.device
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dty = x.dtype
+    _req(x, "x", dty, (batch, L, H, P), dev)
+    _req(dt, "dt", torch.float32, (batch, L, H), dev)
+    _opt(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    _req(A_log, "A_log", torch.float32, (H,), dev)
+    _req(B, "B", dty, (batch, L, G, N), dev)
+    _req(C, "C", dty, (batch, L, G, N), dev)
+    _opt(D, "D", torch.float32, (H,), dev)
+    _opt(h0, "h0", torch.float32, (batch, H, P, N), dev)
+    if y is None:
+        y = torch.empty((batch, L, H, P), dtype=torch.float32, device=dev)
+    _req(y, "y", torch.float32, (batch, L, H, P), dev)
+    if return_final and h_final is None:
+        h_final = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    _opt(h_final, "h_final", torch.float32, (batch, H, P, N), dev)
+    rc = _lib.ssd_chunk_scan_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C),
+                                         _ptr(D), _ptr(y), _ptr(h0), _ptr(h_final), batch, L, H, P, N, G,
+                                         chunk_len, _in_dtype(x), flags, _stream(dev))
     _check(rc)
     return (y, h_final) if (return_final or h_final is not None) else y
 

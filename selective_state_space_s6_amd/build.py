@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libssmscan.so")
 SOURCES = ["abi.hip", "s6_scan.hip", "s6_seg.hip", "s6_fused.hip", "s6_decode.hip", "s6_bwd.hip", "ssd_scan.hip", "ssd_decode.hip", "ssd_bwd.hip", "cssd_scan.hip",
-           "trap_rotate.hip", "conv1d.hip", "s6_grouped.hip"]
+           "trap_rotate.hip", "conv1d.hip", "s6_grouped.hip", "scratch.hip"]
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 # Packed fp32 ops are switched off: the compiler must not emit v_pk_{add,mul,fma}_f32.
 # MFMA accumulators are kept in ordinary VGPRs, so the fp32 state that the SSD

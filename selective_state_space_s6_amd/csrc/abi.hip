@@ -413,13 +413,16 @@ size_t ssd_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nhead
     return ssm::ssd_workspace_bytes(batch, L, nheads, headdim, d_state, chunk_len);
 }
 
-int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, const float *A_log,
-                       const void *B, const void *C, const float *D, float *y,
-                       const float *h0, float *h_final,
-                       int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
-                       int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
-                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    const char *E = "ssd_chunk_scan_fwd";
+}  // extern "C"
+
+namespace {
+// ssd_chunk_scan_fwd and its no-allocation form: every check before any HIP call;
+// scratch: the workspace is the library's static device scratch
+int ssd_fwd_call(const char *E, const void *x, const float *dt, const float *dt_bias, const float *A_log,
+                 const void *B, const void *C, const float *D, float *y, const float *h0, float *h_final,
+                 int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                 int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream, bool scratch) {
     REQUIRE_PTR(E, x); REQUIRE_PTR(E, dt); REQUIRE_PTR(E, A_log); REQUIRE_PTR(E, B);
     REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
     int rc = ssd_check_shape(E, batch, L, nheads, headdim, d_state, ngroups, chunk_len);
@@ -444,13 +447,50 @@ int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, con
         (const void *)y == C)
         return fail(SSM_ERR_INVALID_ARG, "%s: y aliases an input", E);
     const size_t need = ssm::ssd_workspace_bytes(batch, L, nheads, headdim, d_state, chunk_len);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    if (scratch) {
+        if (need > ssm::kScratchBytes)
+            return fail(SSM_ERR_WORKSPACE, "%s: this shape needs %zu bytes of segment states, more than the "
+                        "%zu-byte static scratch (ssd_chunk_scan_fwd takes a caller workspace)", E, need,
+                        ssm::kScratchBytes);
+        if (need > 0) {
+            const hipError_t e = ssm::scratch_address(&workspace);
+            if (e != hipSuccess)
+                return fail(SSM_ERR_HIP, "%s: address of the static scratch: %s", E, hipGetErrorString(e));
+            workspace_bytes = ssm::kScratchBytes;
+        }
+    } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
         return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", E, need,
                     workspace ? workspace_bytes : (size_t)0);
+    }
     ssm::SsdArgs a{x, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L, nheads, headdim,
                    d_state, ngroups, chunk_len, in_dtype == SSM_BF16, flags, workspace};
     const char *kn = "ssd";
     return launched(E, ssm::launch_ssd(a, stream, &kn), kn);
+}
+}  // namespace
+
+extern "C" {
+
+int ssd_chunk_scan_fwd(const void *x, const float *dt, const float *dt_bias, const float *A_log,
+                       const void *B, const void *C, const float *D, float *y,
+                       const float *h0, float *h_final,
+                       int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                       int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return ssd_fwd_call("ssd_chunk_scan_fwd", x, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch, L,
+                        nheads, headdim, d_state, ngroups, chunk_len, in_dtype, flags, workspace,
+                        workspace_bytes, stream, false);
+}
+
+int ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *dt_bias, const float *A_log,
+                               const void *B, const void *C, const float *D, float *y,
+                               const float *h0, float *h_final,
+                               int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
+                               int64_t ngroups, int64_t chunk_len, ssm_dtype_t in_dtype, uint32_t flags,
+                               hipStream_t stream) {
+    return ssd_fwd_call("ssd_chunk_scan_fwd_noalloc", x, dt, dt_bias, A_log, B, C, D, y, h0, h_final, batch,
+                        L, nheads, headdim, d_state, ngroups, chunk_len, in_dtype, flags, nullptr, 0, stream,
+                        true);
 }
 
 size_t ssd_trap_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/ssm_scan.h"
+
 namespace ssm {
 
 struct S6Args {
@@ -77,6 +79,12 @@ struct SsdArgs {
     bool bf16; uint32_t flags;
     void *workspace;
 };
+// The static device scratch of the entry points that allocate nothing (scratch.hip):
+// kScratchBytes per GPU; scratch_address gives its address on the current device
+// (looked up on the first call on each device).
+constexpr size_t kScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
+hipError_t scratch_address(void **out);
+
 // one step (L = 1) of the SSD scan / its trapezoidal form (ssd_decode.hip)
 hipError_t launch_ssd_step(const SsdArgs &a, hipStream_t stream, const char **kernel_name);
 

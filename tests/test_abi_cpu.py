@@ -75,7 +75,7 @@ def test_every_declared_symbol_is_exported(lib):
                      "ssm_s6_scan_grouped_bwd_workspace_size",
                      "ssm_s6_fused_fwd", "ssm_causal_conv1d_fwd",
                      "ssm_s6_scan_bwd_workspace_size", "ssm_s6_scan_bwd",
-                     "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd",
+                     "ssd_chunk_scan_fwd_workspace_size", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_noalloc",
                      "ssd_chunk_scan_bwd_workspace_size", "ssd_chunk_scan_bwd",
                      "ssd_trap_chunk_scan_fwd_workspace_size", "ssd_trap_chunk_scan_fwd",
                      "ssd_trap_rotate_qk_workspace_size", "ssd_trap_rotate_qk",
@@ -476,3 +476,27 @@ def test_s6_grouped_saved_argument_checks(lib):
     assert _gbsaved(lib, ck=None) == INVALID and "checkpoints" in _err(lib)
     assert _gbsaved(lib, dims=(2, 40, 32, 16, 5)) == INVALID and "multiple" in _err(lib)
     assert _gbsaved(lib) == WORKSPACE and "ssm_s6_scan_grouped_bwd_saved" in _err(lib)
+
+
+def test_ssd_noalloc_argument_checks(lib):
+    """The no-allocation SSD entry validates like ssd_chunk_scan_fwd, and a shape whose
+    segment states exceed the static scratch is rejected before any HIP call."""
+    P = ctypes.c_void_p
+    lib.ssd_chunk_scan_fwd_noalloc.argtypes = [P] * 10 + [ctypes.c_int64] * 7 + [ctypes.c_int, ctypes.c_uint32, P]
+    lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
+    ptr = {n: ctypes.c_void_p(0x100000 * (i + 2)) for i, n in enumerate(("x", "dt", "A_log", "B", "C", "y"))}
+
+    def call(dims, dtype=1, flags=1, **kw):
+        p = dict(ptr, **kw)
+        return lib.ssd_chunk_scan_fwd_noalloc(p["x"], p["dt"], None, p["A_log"], p["B"], p["C"], None, p["y"],
+                                              None, None, *dims, dtype, flags, None)
+    # the long-context shape needs ~100 MB of segment states: more than the 32 MiB scratch
+    long_dims = (2, 32768, 80, 64, 128, 8, 256)
+    need = lib.ssd_chunk_scan_fwd_workspace_size(*long_dims)
+    assert need > 32 << 20
+    assert call(long_dims) == WORKSPACE and "scratch" in _err(lib)
+    assert call((1, 64, 2, 64, 128, 1, 256), x=None) == INVALID and "x is NULL" in _err(lib)
+    assert call((1, 64, 3, 64, 128, 2, 256)) == INVALID                       # nheads % ngroups
+    assert call((1, 64, 2, 48, 128, 1, 256)) == UNSUPPORTED and "headdim" in _err(lib)
+    assert call((1, 64, 2, 64, 128, 1, 256), dtype=0) == UNSUPPORTED
+    assert call((1, 64, 2, 64, 128, 1, 256), y=ptr["x"]) == INVALID and "alias" in _err(lib)
