@@ -813,10 +813,20 @@ def roofline(m):
                 "issue_slot_frac": round(slots_frac, 4),
                 "issue_slot_basis": f"{S6_SLOTS_PER_UPDATE} fp32 VALU issue slots per state update (exact "
                                     "hold incl.), 39.3 T lane-slots/s (256 CU x 4 SIMD x 16 lanes x 2.4 GHz)"}
+    if kind in ("ssd", "trap") and m["dims"].get("L", 2) > 1:
+        # below the bf16 ridge (~165 flop/B against ~315): priced on HBM, with the
+        # matrix-core fraction of the method's flops (the target metric) alongside
+        tf = m["ops"] / ev_s / 1e12
+        pk, basis = MFMA_PEAKS[kind]
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(name, "ssd"),
+                "algorithmic_bytes": m["bytes"], **kern,
+                "mfma_TFLOPs": round(tf, 2), "mfma_peak": pk, "mfma_frac": round(tf / pk, 4),
+                "algorithmic_flops": m["ops"], "mfma_basis": basis}
     if kind in MFMA_PEAKS and m["dims"].get("L", 2) > 1:
         tf = m["ops"] / ev_s / 1e12
         pk, basis = MFMA_PEAKS[kind]
-        tr_kind = "ssd" if kind in ("ssd", "trap") else "cssd" if kind in ("cssd", "cssd_mimo") else None
+        tr_kind = "cssd" if kind in ("cssd", "cssd_mimo") else None
         return {"bound": "mfma", "achieved": round(tf, 2), "peak": pk, "unit": "TFLOP/s",
                 "frac": round(tf / pk, 4), "traffic": counter_traffic(name, tr_kind) if tr_kind else None,
                 "algorithmic_flops": m["ops"], "peak_basis": basis, **kern,
