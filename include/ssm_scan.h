@@ -548,10 +548,12 @@ int ssd_trap_rotate_qk(const void *k_raw, const void *q_raw, const float *angles
  * multiple of 8, <= 64; chunk_len in {32, 64, 128} (checked; the kernels use
  * their own 32-step chunks, and the result does not depend on it beyond
  * rounding).  Contractions run in fp32 on the matrix cores.
- * Workspace: ssd_cplx_chunk_scan_fwd_workspace_size() bytes, 16-byte aligned,
- * owned by the caller (one complex headdim x n_complex state and one complex
- * decay per (batch, head, segment) when the sequence is cut into segments;
- * 0 when it is one segment, and workspace may then be NULL). */
+ * Workspace: ssd_cplx_chunk_scan_fwd_workspace_size() bytes (never 0),
+ * 16-byte aligned, owned by the caller: per (batch, head, 32-step chunk) a
+ * 528-byte record of the chunk's decays and input scales and the 3 KiB of
+ * its decay-masked C.B^T tiles, and, when the sequence is cut into segments,
+ * one complex headdim x n_complex state and one complex decay per (batch,
+ * head, segment).  NULL or too small: SSM_ERR_WORKSPACE, nothing launched. */
 size_t ssd_cplx_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t nheads,
                                               int64_t headdim, int64_t n_complex, int64_t ngroups,
                                               int64_t chunk_len);
@@ -582,7 +584,7 @@ int ssd_cplx_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bia
  * rejected).  Limits: rank in {1, 2, 4, 8, 16}; otherwise as for
  * ssd_cplx_chunk_scan_fwd, with L x rank in place of L.
  * Workspace: ssd_cplx_mimo_chunk_scan_fwd_workspace_size() bytes, as for
- * ssd_cplx_chunk_scan_fwd over L x rank rows (0 for one segment). */
+ * ssd_cplx_chunk_scan_fwd over L x rank rows. */
 size_t ssd_cplx_mimo_chunk_scan_fwd_workspace_size(int64_t batch, int64_t L, int64_t rank, int64_t nheads,
                                                    int64_t headdim, int64_t n_complex, int64_t ngroups,
                                                    int64_t chunk_len);

@@ -735,6 +735,8 @@ int ssd_cplx_chunk_scan_fwd(const float *x, const float *dt, const float *dt_bia
     REQUIRE_PTR(E, C); REQUIRE_PTR(E, y);
     int rc = ssd_check_shape(E, batch, L, nheads, headdim, n_complex, ngroups, chunk_len);
     if (rc != SSM_OK) return rc;
+    if (ssm::cssd_prep_blocks(batch, L, nheads, ngroups) > 0x7fffffffLL)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
     if ((flags & ~0x1Fu) != 0 || (flags & 0x3u) == 0x3u || (flags & 0xCu) == 0xCu)
         return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x not a valid combination", E, flags);
     if ((flags & 0xCu) == SSM_CPLX_CODE && (flags & 0x3u) != SSM_BBAR_ZOH)
@@ -787,6 +789,8 @@ int ssd_cplx_mimo_chunk_scan_fwd(const float *x, const float *dt, const float *d
         return fail(SSM_ERR_UNSUPPORTED, "%s: L x rank too large", E);
     int rc = ssd_check_shape(E, batch, L * rank, nheads, headdim, n_complex, ngroups, chunk_len);   // rows
     if (rc != SSM_OK) return rc;
+    if (ssm::cssd_prep_blocks(batch, L * rank, nheads, ngroups) > 0x7fffffffLL)
+        return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
     if ((flags & ~0x13u) != 0 || (flags & 0x3u) == 0x3u)
         return fail(SSM_ERR_INVALID_ARG, "%s: flags 0x%x not a valid combination (stable reading of A only)", E,
                     flags);

@@ -20,8 +20,13 @@
 // state) runs through the same kernels: a step's R rows of x, y, B, C are
 // consecutive and the kernels walk rows (see CssdKp::lgR).
 //
-// Layout of the work: as for the real SSD, the sequence of every (batch, head)
-// is cut into segments (cssd_state_kernel: segment-local states and decays;
+// Layout of the work: cssd_prep_kernel first takes, once per (batch, chunk,
+// head), everything that does not depend on the head channel: the chunk's
+// running sums of delta, input scales and decays (a record of w_s, e^{mu Lam_t}
+// and the chunk decay), and the causal tiles of M[t][s] = Re(G[t,s]
+// e^{mu(Lam_t-Lam_s)} beta_s), with G = C.B^T formed once per group of heads.
+// Then, as for the real SSD, the sequence of every (batch, head) is cut into
+// segments (cssd_state_kernel: segment-local states and decays;
 // cssd_pass_kernel: entering states; cssd_scan_kernel: outputs), and a work
 // group holds one head with one wave per 16 head channels.  The complex state
 // is stored as real pairs, k = 2n + (0 re, 1 im), and a wave keeps its
@@ -70,14 +75,27 @@ __device__ __forceinline__ cf cdiv(cf a, cf b) {
     return {(a.re * b.re + a.im * b.im) / den, (a.im * b.re - a.re * b.im) / den};
 }
 
+// per-(batch, head, chunk) record of the chunk scalars the state and output
+// passes use, written by cssd_prep_kernel
+struct CRec {
+    float2 w[kT];     // e^{mu (lam_end - lam_s)} beta_s
+    float2 et[kT];    // e^{mu lam_t}
+    float2 E;         // e^{mu lam_end}
+    double lend;      // lam_end
+};
+static_assert(sizeof(CRec) == 33 * 16, "a record is 33 16-byte pieces");
+
 struct CssdKp {
     const float *x; const float *dt; const float *dt_bias; const float *A_log;
     const float *B; const float *C; const float *D; float *y;
     const float *h0; float *h_final;
     float *ws_state;    // (batch, H, nseg, P, 2 Nc): local, then entering, segment states
     float *ws_decay;    // (batch, H, nseg, 2): complex decay over a segment
+    CRec *rec;          // (batch, H, nck) chunk records
+    f32x4 *mtile;       // (batch, H, nck, 3, 64): the causal M tiles as MFMA A fragments
     int64_t batch, L, H, P, Nc, G;
     int64_t Ls, nseg;   // segment length (a multiple of kT) and count
+    int64_t nck;        // chunks of the whole sequence
     uint32_t flags;
     // Multi-input multi-output form: R = 2^lgR inputs and outputs per head and
     // step, laid out as R consecutive rows of x, y, B, C per step.  The kernels
@@ -119,8 +137,9 @@ struct CScal {
     double lend;      // lam_end
 };
 
-// Scalars of one chunk by one wave (lane = step within each 32-lane half; the
-// upper half repeats the lower).  Steps past L have delta = beta = 0.
+// Scalars of one chunk of one head by one 32-lane half of a wave (step
+// lane & 31; the two halves may hold two heads, each with its own sc, mu,
+// bias).  Steps past L have delta = beta = 0.
 __device__ __forceinline__ void chunk_scalars(CScal &sc, const CssdKp &p, cf mu, double bias, float dtv,
                                               bool valid, int lane) {
     double dl = 0.0;
@@ -137,16 +156,17 @@ __device__ __forceinline__ void chunk_scalars(CScal &sc, const CssdKp &p, cf mu,
         if ((lane & 31) >= off) v += o;
     }
     const double lend = __shfl(v, 31, 32);
-    if (lane < kT) {
+    const int t = lane & 31;
+    {
         const float lt = (float)v, lr = (float)(lend - v);
         const cf e = cexpf_(mu.re * lt, mu.im * lt);
         const cf w = cmul(cexpf_(mu.re * lr, mu.im * lr), be);
-        sc.lam[lane] = v;
-        sc.bet[lane] = make_float2(be.re, be.im);
-        sc.et[lane] = make_float2(e.re, e.im);
-        sc.w[lane] = make_float2(w.re, w.im);
+        sc.lam[t] = v;
+        sc.bet[t] = make_float2(be.re, be.im);
+        sc.et[t] = make_float2(e.re, e.im);
+        sc.w[t] = make_float2(w.re, w.im);
     }
-    if (lane == 0) {
+    if (t == 0) {
         const float le = (float)lend;
         const cf E = cexpf_(mu.re * le, mu.im * le);
         sc.E = make_float2(E.re, E.im);
@@ -177,19 +197,18 @@ struct Stager {
     // clang vector types: arrays of HIP's float4 (a class holding a union) stayed in
     // per-lane scratch memory, which also forced a wait on each prefetch
     f32x4 rB[PBC], rC[PBC], rX[PX];
-    float rdt;
-    const float *Bb, *Cb, *Xb, *Db;
+    float2 rW[PBC], rE[PBC];     // w and e^{mu lam} of each piece's step, from the chunk record
+    const float *Bb, *Cb, *Xb;
+    const CRec *Rb;
     uint32_t oBC[PBC], oX[PX];   // per-piece offsets (floats) at chunk row 0
     int rBC[PBC], rXr[PX];       // per-piece rows
     int lBC[PBC], lX[PX];        // per-piece LDS offsets
     bool vBC[PBC];
-    int sD, lgR;
-    int64_t rowBC, rowX, H, L;
+    int64_t rowBC, rowX, L;
 
     __device__ __forceinline__ void init(const CssdKp &p, int64_t b, int64_t h, int64_t g, int tid) {
         rowBC = p.G * p.Nc * 2;
         rowX = p.H * p.P;
-        H = p.H;
         L = p.L;
         const int K = (int)(2 * p.Nc);
 #pragma unroll
@@ -210,16 +229,20 @@ struct Stager {
             oX[i] = (uint32_t)(r * rowX + c);
             lX[i] = r * XP + c;
         }
-        sD = tid & 31;
         Bb = p.B + (b * p.L * p.G + g) * p.Nc * 2;
         Cb = p.C + (b * p.L * p.G + g) * p.Nc * 2;
         Xb = p.x + (b * p.L * p.H + h) * p.P;
-        Db = p.dt + b * (p.L >> p.lgR) * p.H + h;
-        lgR = p.lgR;
+        Rb = p.rec + (b * p.H + h) * p.nck;
     }
+    // chunk t0 / kT: its rows and, per B/C piece, its step's scalars
     __device__ __forceinline__ void load(int64_t t0) {
         const float *Bu = Bb + t0 * rowBC, *Cu = Cb + t0 * rowBC, *Xu = Xb + t0 * rowX;
-        const float *Du = Db + (t0 >> lgR) * H;     // t0 is a multiple of kT, so of R
+        const CRec &rn = Rb[t0 / kT];
+#pragma unroll
+        for (int i = 0; i < PBC; ++i) {
+            rW[i] = rn.w[rBC[i]];
+            if constexpr (WITH_C) rE[i] = rn.et[rBC[i]];
+        }
         if (t0 + kT <= L) {
 #pragma unroll
             for (int i = 0; i < PBC; ++i) {
@@ -228,7 +251,6 @@ struct Stager {
             }
 #pragma unroll
             for (int i = 0; i < PX; ++i) rX[i] = *reinterpret_cast<const f32x4 *>(Xu + oX[i]);
-            rdt = Du[(uint32_t)((sD >> lgR) * H)];
         } else {
             const int last = (int)(L - 1 - t0);   // last valid step of the chunk
 #pragma unroll
@@ -242,15 +264,38 @@ struct Stager {
                 const uint32_t o = oX[i] - (uint32_t)((rXr[i] - min(rXr[i], last)) * rowX);
                 rX[i] = *reinterpret_cast<const f32x4 *>(Xu + o);
             }
-            rdt = Du[(uint32_t)((min(sD, last) >> lgR) * H)];
         }
     }
-    __device__ __forceinline__ void store(float *Bs, float *Cs, float *Xs) {
+    // The B and C tiles go to LDS as the operands every wave of the group
+    // uses, formed once here from the chunk record's scalars (a row past L
+    // has w = 0, and its output is not stored):
+    //   B -> w_s B_s[n] as real pairs (Re, Im): the D2 operand;
+    //   C -> C_t[n] e^{mu lam_t} as (Re, -Im): the D5 operand (conj(C) by csign).
+    __device__ __forceinline__ void store(float *Bs, float *Cs, float *Xs, float csign) {
 #pragma unroll
         for (int i = 0; i < PBC; ++i) {
             if (PBC * NTHR == NBC || vBC[i]) {
-                *reinterpret_cast<f32x4 *>(&Bs[lBC[i]]) = rB[i];
-                if constexpr (WITH_C) *reinterpret_cast<f32x4 *>(&Cs[lBC[i]]) = rC[i];
+                const float2 w = rW[i];
+                const f32x4 b = rB[i];
+                f32x4 wb;
+                wb[0] = fmaf(w.x, b[0], -w.y * b[1]);   // Re(w b) = w.re b.re - w.im b.im
+                wb[1] = fmaf(w.y, b[0], w.x * b[1]);    // Im(w b) = w.im b.re + w.re b.im
+                wb[2] = fmaf(w.x, b[2], -w.y * b[3]);
+                wb[3] = fmaf(w.y, b[2], w.x * b[3]);
+                *reinterpret_cast<f32x4 *>(&Bs[lBC[i]]) = wb;
+                if constexpr (WITH_C) {
+                    const float2 e = rE[i];
+                    const f32x4 cq = rC[i];
+                    const float ci0 = csign * cq[1], ci1 = csign * cq[3];
+                    // the fused forms are written out, so the operand's rounding
+                    // does not depend on the compiler's contraction choices
+                    f32x4 ch;
+                    ch[0] = fmaf(cq[0], e.x, -(ci0 * e.y));    // Re(C e)
+                    ch[1] = -fmaf(cq[0], e.y, ci0 * e.x);      // -Im(C e)
+                    ch[2] = fmaf(cq[2], e.x, -(ci1 * e.y));
+                    ch[3] = -fmaf(cq[2], e.y, ci1 * e.x);
+                    *reinterpret_cast<f32x4 *>(&Cs[lBC[i]]) = ch;
+                }
             }
         }
 #pragma unroll
@@ -275,13 +320,12 @@ __device__ __forceinline__ void decay_state(f32x4 (&S)[NTK], float2 E, int K) {
 }
 
 // D2: S[k][p] += sum_s (w B)_r[s][k] x[s][p] for one wave's 16 channels.  The A
-// operand (row k = kt*16 + lane%16, K slot s = sb*16 + 4*(lane/16) + m) is the
-// real or imaginary part of w_s B_s[n], n = k/2, formed as it is read.
+// operand (row k = kt*16 + lane%16, K slot s = sb*16 + 4*(lane/16) + m) is
+// entry k of w_s B_s as real pairs, formed when the tile was staged.
 template <int NTK, int CP, int XP>
-__device__ __forceinline__ void state_add(f32x4 (&S)[NTK], const float *Bs, const float *Xs, const CScal &sc,
-                                          int p0, int K, int lane) {
+__device__ __forceinline__ void state_add(f32x4 (&S)[NTK], const float *WB, const float *Xs, int p0, int K,
+                                          int lane) {
     const int c16 = lane & 15, q = lane >> 4;
-    const bool odd = c16 & 1;
     // the chunk's contribution is summed on its own and added once, so its
     // roundings are relative to it and not to the (larger) state
     f32x4 dS[NTK];
@@ -292,15 +336,11 @@ __device__ __forceinline__ void state_add(f32x4 (&S)[NTK], const float *Bs, cons
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int s = sb * 16 + 4 * q + m;
-            const float2 w = sc.w[s];
-            // even k: Re(w b) = w.re b.re - w.im b.im ; odd k: Im(w b) = w.im b.re + w.re b.im
-            const float al = odd ? w.y : w.x, be = odd ? w.x : -w.y;
             const float xv = Xs[s * XP + p0 + c16];
 #pragma unroll
             for (int kt = 0; kt < NTK; ++kt) {
                 if (kt * 16 >= K) break;
-                const float2 b = *reinterpret_cast<const float2 *>(&Bs[s * CP + kt * 16 + (c16 & ~1)]);
-                dS[kt] = mfma4(fmaf(al, b.x, be * b.y), xv, dS[kt]);
+                dS[kt] = mfma4(WB[s * CP + kt * 16 + c16], xv, dS[kt]);
             }
         }
     }
@@ -326,6 +366,121 @@ __device__ __forceinline__ float2 cexp_long(cf mu, double lam) {
     return make_float2(e.re, e.im);
 }
 
+// ---- chunk records and M tiles: two heads per wave (one per 32-lane half for
+// the chunk scalars), eight heads of one group per work group.  Waves 0-2
+// first form G = C.B^T over the chunk's causal tile pairs (tau = (s-tile,
+// t-tile) = (0,0), (0,1), (1,1)), which every head of the group shares; then
+// every wave takes its heads' chunk scalars and applies each head's decay and
+// input scale to G.
+template <int KC, bool EXACT>
+__global__ void __launch_bounds__(256)
+cssd_prep_kernel(CssdKp p) {
+    constexpr int NTK = KC / 16;
+    __shared__ f32x4 Gs[3][2][64];   // Re G^T and Im G^T tiles, lane-major as MFMA outputs
+    __shared__ CScal scal[8];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15, q = lane >> 4;
+    const int64_t Hg = p.H / p.G, nq = (Hg + 7) / 8;
+    int64_t r = xcd_swizzle(blockIdx.x, p.batch * p.nck * p.G * nq);   // the blocks of a group stay together
+    const int64_t hq = r % nq;
+    r /= nq;
+    const int64_t g = r % p.G;
+    r /= p.G;
+    const int64_t c = r % p.nck, b = r / p.nck;
+    const int64_t t0 = c * kT;
+    const int last = (int)min<int64_t>(kT - 1, p.L - 1 - t0);   // last valid step of the chunk
+    const int K = EXACT ? KC : (int)(2 * p.Nc);
+    const float csign = (p.flags & 0x10u) ? -1.0f : 1.0f;   // conj(C)
+
+    // G^T[s][t] (re and im) for tile pair tau = wid.  Lane holds column
+    // t = tT*16 + c16, rows s = sT*16 + q*4 + v; K slot (q, m) of block kb is
+    // k = kb*16 + 4q + m.
+    //   Re G = sum_n B_re C_re - B_im C_im,  Im G = sum_n B_re C_im + B_im C_re
+    // (C_im -> -C_im for conj(C)).  Rows past L repeat the last valid row.
+    if (wid < 3) {
+        const int sT = wid == 2 ? 1 : 0, tT = wid == 0 ? 0 : 1;
+        const int64_t rowBC = p.G * p.Nc * 2;
+        const float *Bg = p.B + ((b * p.L + t0) * p.G + g) * p.Nc * 2;
+        const float *Cg = p.C + ((b * p.L + t0) * p.G + g) * p.Nc * 2;
+        const float *Brow = Bg + min(sT * 16 + c16, last) * rowBC + 4 * q;
+        const float *Crow = Cg + min(tT * 16 + c16, last) * rowBC + 4 * q;
+        f32x4 Gr{0.0f, 0.0f, 0.0f, 0.0f}, Gi{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < NTK; ++kb) {
+            if (kb * 16 >= K) break;
+            const float4 bq = *reinterpret_cast<const float4 *>(Brow + kb * 16);
+            const float4 cq = *reinterpret_cast<const float4 *>(Crow + kb * 16);
+            const float c1 = csign * cq.y, c3 = csign * cq.w;
+            Gr = mfma4(bq.x, cq.x, Gr);
+            Gr = mfma4(-bq.y, c1, Gr);
+            Gr = mfma4(bq.z, cq.z, Gr);
+            Gr = mfma4(-bq.w, c3, Gr);
+            Gi = mfma4(bq.y, cq.x, Gi);
+            Gi = mfma4(bq.x, c1, Gi);
+            Gi = mfma4(bq.w, cq.z, Gi);
+            Gi = mfma4(bq.z, c3, Gi);
+        }
+        Gs[wid][0][lane] = Gr;
+        Gs[wid][1][lane] = Gi;
+    }
+
+    // chunk scalars: half hf of the wave takes head hq*8 + 2*wid + hf of the group
+    const int64_t hbase = hq * 8 + 2 * wid;   // within the group
+    if (hbase < Hg) {                          // uniform over the wave
+        const int hf = lane >> 5;
+        const bool hok = hbase + hf < Hg;
+        const int64_t h = g * Hg + min<int64_t>(hbase + hf, Hg - 1);
+        const double bias = p.dt_bias ? (double)p.dt_bias[h] : 0.0;
+        const int64_t step = (t0 + min(lane & 31, last)) >> p.lgR;
+        const float dtv = p.dt[(b * (p.L >> p.lgR) + step) * p.H + h];
+        chunk_scalars(scal[2 * wid + hf], p, head_mu(p, h), bias, dtv, hok && t0 + (lane & 31) < p.L, lane);
+    }
+    __syncthreads();
+
+    for (int hf = 0; hf < 2; ++hf) {
+        if (hbase + hf >= Hg) break;   // uniform over the wave
+        const int64_t h = g * Hg + hbase + hf;
+        const cf mu = head_mu(p, h);
+        const CScal &sc = scal[2 * wid + hf];
+
+        // M tiles: M^T[s][t] = Re(G[t,s] e^{mu(lam_t-lam_s)} beta_s), causal over steps
+        f32x4 *Mo = p.mtile + ((b * p.H + h) * p.nck + c) * 192 + lane;
+#pragma unroll
+        for (int tau = 0; tau < 3; ++tau) {
+            const int sT = tau == 2 ? 1 : 0, tT = tau == 0 ? 0 : 1;
+            const f32x4 Gr = Gs[tau][0][lane], Gi = Gs[tau][1][lane];
+            const int t = tT * 16 + c16;
+            const double lt = sc.lam[t];
+            f32x4 mv;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int s = sT * 16 + 4 * q + v;
+                float m = 0.0f;
+                if ((s >> p.lgR) <= (t >> p.lgR)) {
+                    const float dl = (float)(lt - sc.lam[s]);
+                    const float2 bs = sc.bet[s];
+                    const cf f = cmul(cexpf_(mu.re * dl, mu.im * dl), cf{bs.x, bs.y});
+                    m = Gr[v] * f.re - Gi[v] * f.im;
+                }
+                mv[v] = m;
+            }
+            Mo[tau * 64] = mv;
+        }
+
+        CRec *R = p.rec + (b * p.H + h) * p.nck + c;
+        if (lane < kT) {
+            R->w[lane] = sc.w[lane];
+            R->et[lane] = sc.et[lane];
+        }
+        if (lane == 0) {
+            R->E = sc.E;
+            R->lend = sc.lend;
+        }
+    }
+}
+
 // ---- segment-local final states (zero start) and the segment decay; every
 // segment but the last, all of whose chunks are whole
 template <int KC, bool EXACT, int NW>
@@ -336,7 +491,6 @@ cssd_state_kernel(CssdKp p) {
     constexpr int CP = St::CP, XP = St::XP;
     __shared__ __attribute__((aligned(16))) float Bs[2][kT * CP];
     __shared__ __attribute__((aligned(16))) float Xs[2][kT * XP];
-    __shared__ CScal scal[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -346,8 +500,6 @@ cssd_state_kernel(CssdKp p) {
     const int64_t g = wk.h * p.G / p.H;
     const int p0 = wid * 16;
     const int K = EXACT ? KC : (int)(2 * p.Nc);
-    const cf mu = head_mu(p, wk.h);
-    const double bias = p.dt_bias ? (double)p.dt_bias[wk.h] : 0.0;
 
     f32x4 S[NTK];
 #pragma unroll
@@ -356,23 +508,21 @@ cssd_state_kernel(CssdKp p) {
     St st;
     st.init(p, wk.b, wk.h, g, tid);
     const int64_t tb = wk.k * p.Ls;
+    const CRec *Rc = p.rec + (wk.b * p.H + wk.h) * p.nck + tb / kT;   // the segment's chunk records
     const int64_t nchunks = p.Ls / kT;
     st.load(tb);
-    st.store(Bs[0], nullptr, Xs[0]);
-    if (wid == 0) chunk_scalars(scal[0], p, mu, bias, st.rdt, true, lane);
+    st.store(Bs[0], nullptr, Xs[0], 1.0f);
     if (nchunks > 1) st.load(tb + kT);
     __syncthreads();
 
     double lseg = 0.0;
     for (int64_t j = 0; j < nchunks; ++j) {
         const int buf = (int)(j & 1);
-        const CScal &sc = scal[buf];
-        lseg += sc.lend;
-        decay_state<NTK>(S, sc.E, K);
-        state_add<NTK, CP, XP>(S, Bs[buf], Xs[buf], sc, p0, K, lane);
+        lseg += Rc[j].lend;
+        decay_state<NTK>(S, Rc[j].E, K);
+        state_add<NTK, CP, XP>(S, Bs[buf], Xs[buf], p0, K, lane);
         if (j + 1 < nchunks) {
-            st.store(Bs[buf ^ 1], nullptr, Xs[buf ^ 1]);
-            if (wid == 0) chunk_scalars(scal[buf ^ 1], p, mu, bias, st.rdt, true, lane);
+            st.store(Bs[buf ^ 1], nullptr, Xs[buf ^ 1], 1.0f);
             if (j + 2 < nchunks) st.load(tb + (j + 2) * kT);
         }
         __syncthreads();
@@ -386,7 +536,7 @@ cssd_state_kernel(CssdKp p) {
         *reinterpret_cast<float4 *>(dst) = make_float4(S[kt][0], S[kt][1], S[kt][2], S[kt][3]);
     }
     if (tid == 0) {
-        const float2 d = cexp_long(mu, lseg);
+        const float2 d = cexp_long(head_mu(p, wk.h), lseg);
         p.ws_decay[2 * slot] = d.x;
         p.ws_decay[2 * slot + 1] = d.y;
     }
@@ -423,10 +573,6 @@ cssd_scan_kernel(CssdKp p) {
     __shared__ __attribute__((aligned(16))) float Bs[2][kT * CP];
     __shared__ __attribute__((aligned(16))) float Cs[2][kT * CP];
     __shared__ __attribute__((aligned(16))) float Xs[2][kT * XP];
-    // the chunk's causal tiles of M[t][s] = Re(G[t,s] e^{mu(lam_t-lam_s)} beta_s) as
-    // the A fragments of M X: tile tau = (s-tile, t-tile) (0,0), (0,1), (1,1)
-    __shared__ __attribute__((aligned(16))) f32x4 Ms[3][64];
-    __shared__ CScal scal[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -435,8 +581,6 @@ cssd_scan_kernel(CssdKp p) {
     const int64_t g = wk.h * p.G / p.H;
     const int p0 = wid * 16;
     const int K = EXACT ? KC : (int)(2 * p.Nc);
-    const cf mu = head_mu(p, wk.h);
-    const double bias = p.dt_bias ? (double)p.dt_bias[wk.h] : 0.0;
     const float csign = (p.flags & 0x10u) ? -1.0f : 1.0f;   // conj(C)
     const float Dh = p.D ? p.D[wk.h] : 0.0f;
     const int64_t rowX = p.H * p.P;
@@ -461,10 +605,16 @@ cssd_scan_kernel(CssdKp p) {
     st.init(p, wk.b, wk.h, g, tid);
     const int64_t tb = wk.k * p.Ls;
     const int64_t te = min(tb + p.Ls, p.L);
+    const int64_t c0 = tb / kT;
     const int64_t nchunks = (te - tb + kT - 1) / kT;
+    const CRec *Rc = p.rec + (wk.b * p.H + wk.h) * p.nck + c0;   // the segment's chunk records
+    // the chunk's M fragments (tile tau at lane), read a chunk ahead
+    const f32x4 *Mg = p.mtile + ((wk.b * p.H + wk.h) * p.nck + c0) * 192 + lane;
+    f32x4 mnext[3];
+#pragma unroll
+    for (int tau = 0; tau < 3; ++tau) mnext[tau] = Mg[tau * 64];
     st.load(tb);
-    st.store(Bs[0], Cs[0], Xs[0]);
-    if (wid == NW - 1) chunk_scalars(scal[0], p, mu, bias, st.rdt, tb + (lane & 31) < p.L, lane);
+    st.store(Bs[0], Cs[0], Xs[0], csign);
     if (nchunks > 1) st.load(tb + kT);
     __syncthreads();
 
@@ -472,83 +622,42 @@ cssd_scan_kernel(CssdKp p) {
         const int buf = (int)(j & 1);
         const int64_t t0 = tb + j * kT;
         const float *B_ = Bs[buf], *C_ = Cs[buf], *X_ = Xs[buf];
-        const CScal &sc = scal[buf];
-
-        // D4, shared: G^T[s][t] (re and im) for the causal tile pairs, one per
-        // wave (wave tau % NW).  Lane holds column t = tT*16 + c16, rows
-        // s = sT*16 + q*4 + v.  K slot (q, m) of block kb is k = kb*16 + 4q + m.
-        //   Re G = sum_n B_re C_re - B_im C_im,  Im G = sum_n B_re C_im + B_im C_re
-        // (C_im -> -C_im for conj(C)).
+        const float2 E = Rc[j].E;
+        f32x4 mv[3];
 #pragma unroll
-        for (int tau = 0; tau < 3; ++tau) {
-            if (tau % NW != wid) continue;
-            const int sT = tau == 2 ? 1 : 0, tT = tau == 0 ? 0 : 1;
-            f32x4 Gr{0.0f, 0.0f, 0.0f, 0.0f}, Gi{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int tau = 0; tau < 3; ++tau) mv[tau] = mnext[tau];
+        if (j + 1 < nchunks) {
 #pragma unroll
-            for (int kb = 0; kb < NTK; ++kb) {
-                if (kb * 16 >= K) break;
-                const float4 bq = *reinterpret_cast<const float4 *>(&B_[(sT * 16 + c16) * CP + kb * 16 + 4 * q]);
-                const float4 cq = *reinterpret_cast<const float4 *>(&C_[(tT * 16 + c16) * CP + kb * 16 + 4 * q]);
-                const float c1 = csign * cq.y, c3 = csign * cq.w;
-                Gr = mfma4(bq.x, cq.x, Gr);
-                Gr = mfma4(-bq.y, c1, Gr);
-                Gr = mfma4(bq.z, cq.z, Gr);
-                Gr = mfma4(-bq.w, c3, Gr);
-                Gi = mfma4(bq.y, cq.x, Gi);
-                Gi = mfma4(bq.x, c1, Gi);
-                Gi = mfma4(bq.w, cq.z, Gi);
-                Gi = mfma4(bq.z, c3, Gi);
-            }
-            const int t = tT * 16 + c16;
-            const double lt = sc.lam[t];
-            f32x4 mv;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int s = sT * 16 + 4 * q + v;
-                float m = 0.0f;
-                if ((s >> p.lgR) <= (t >> p.lgR)) {      // causal over steps
-                    const float dl = (float)(lt - sc.lam[s]);
-                    const float2 bs = sc.bet[s];
-                    const cf f = cmul(cexpf_(mu.re * dl, mu.im * dl), cf{bs.x, bs.y});
-                    m = Gr[v] * f.re - Gi[v] * f.im;
-                }
-                mv[v] = m;
-            }
-            Ms[tau][lane] = mv;
+            for (int tau = 0; tau < 3; ++tau) mnext[tau] = Mg[(j + 1) * 192 + tau * 64];
         }
-
-        // D5: ys[tt] = sum_k Chat[t][k] S_r[k][p], Chat = (Re, -Im) of C_t[n] e^{mu lam_t};
-        // two partial sums (even and odd state tiles) shorten the fp32 chains
+        // D5: ys[tt] = sum_k Chat[t][k] S_r[k][p], Chat = (Re, -Im) of C_t[n] e^{mu lam_t}
+        // (the staged C tile); two partial sums (even and odd state tiles)
+        // shorten the fp32 chains
         f32x4 ys[2][2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             ys[tt][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             ys[tt][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            const float2 e = sc.et[tt * 16 + c16];
 #pragma unroll
             for (int kt = 0; kt < NTK; ++kt) {
                 if (kt * 16 >= K) break;
-                const float4 cq = *reinterpret_cast<const float4 *>(&C_[(tt * 16 + c16) * CP + kt * 16 + 4 * q]);
-                const float ci0 = csign * cq.y, ci1 = csign * cq.w;
+                const float4 ch = *reinterpret_cast<const float4 *>(&C_[(tt * 16 + c16) * CP + kt * 16 + 4 * q]);
                 f32x4 &a = ys[tt][kt & 1];
-                a = mfma4(cq.x * e.x - ci0 * e.y, S[kt][0], a);
-                a = mfma4(-(cq.x * e.y + ci0 * e.x), S[kt][1], a);
-                a = mfma4(cq.z * e.x - ci1 * e.y, S[kt][2], a);
-                a = mfma4(-(cq.z * e.y + ci1 * e.x), S[kt][3], a);
+                a = mfma4(ch.x, S[kt][0], a);
+                a = mfma4(ch.y, S[kt][1], a);
+                a = mfma4(ch.z, S[kt][2], a);
+                a = mfma4(ch.w, S[kt][3], a);
             }
         }
-
-        __syncthreads();   // the shared M fragments are complete
 
         // D4: acc[tt] = sum_{s-tile <= tt} M X
         f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
         for (int tau = 0; tau < 3; ++tau) {
             const int sT = tau == 2 ? 1 : 0, tT = tau == 0 ? 0 : 1;
-            const f32x4 mv = Ms[tau][lane];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                acc[tT] = mfma4(mv[m], X_[(sT * 16 + 4 * q + m) * XP + p0 + c16], acc[tT]);
+                acc[tT] = mfma4(mv[tau][m], X_[(sT * 16 + 4 * q + m) * XP + p0 + c16], acc[tT]);
         }
 
         // skip term and store: lane (column p0 + c16, rows t = tt*16 + q*4 + v)
@@ -577,14 +686,12 @@ cssd_scan_kernel(CssdKp p) {
         }
 
         // D2 + D3
-        decay_state<NTK>(S, sc.E, K);
-        state_add<NTK, CP, XP>(S, B_, X_, sc, p0, K, lane);
+        decay_state<NTK>(S, E, K);
+        state_add<NTK, CP, XP>(S, B_, X_, p0, K, lane);
 
         // stage chunk j+1, start loading chunk j+2
         if (j + 1 < nchunks) {
-            st.store(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1]);
-            if (wid == NW - 1)   // the wave with no decay-mask tile (or the least)
-                chunk_scalars(scal[buf ^ 1], p, mu, bias, st.rdt, t0 + kT + (lane & 31) < p.L, lane);
+            st.store(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1], csign);
             if (j + 2 < nchunks) st.load(t0 + 2 * kT);
         }
         __syncthreads();
@@ -612,8 +719,36 @@ Plan plan(int64_t batch, int64_t L, int64_t H, int64_t P) {
 }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Workspace: segment states and decays (when there are segments), then the
+// chunk records and the M tiles of every (batch, head, chunk).
+struct WsLayout {
+    Plan pl;
+    int64_t nck;
+    size_t state, decay, rec, mtile, total;
+};
+WsLayout ws_layout(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t Nc) {
+    WsLayout w{};
+    w.pl = plan(batch, L, H, P);
+    w.nck = (L + kT - 1) / kT;
+    size_t off = 0;
+    if (w.pl.nseg > 1) {
+        w.state = off;
+        off = align256(off + (size_t)(batch * H * w.pl.nseg * P * Nc * 2) * sizeof(float));
+        w.decay = off;
+        off = align256(off + (size_t)(batch * H * w.pl.nseg * 2) * sizeof(float));
+    }
+    w.rec = off;
+    off = align256(off + (size_t)(batch * H * w.nck) * sizeof(CRec));
+    w.mtile = off;
+    off += (size_t)(batch * H * w.nck) * 192 * sizeof(f32x4);
+    w.total = off;
+    return w;
+}
+
 template <int KC, bool EXACT, int NW>
 void launch_all(const CssdKp &p, hipStream_t stream) {
+    const int64_t np = p.batch * p.nck * p.G * ((p.H / p.G + 7) / 8);
+    hipLaunchKernelGGL((cssd_prep_kernel<KC, EXACT>), dim3((unsigned)np), dim3(256), 0, stream, p);
     if (p.nseg > 1) {
         const int64_t n1 = p.batch * (p.nseg - 1) * p.H;
         hipLaunchKernelGGL((cssd_state_kernel<KC, EXACT, NW>), dim3((unsigned)n1), dim3(64 * NW), 0, stream, p);
@@ -639,10 +774,11 @@ void launch_k(const CssdKp &p, hipStream_t stream) {
 
 size_t cssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t n_complex,
                             int64_t) {
-    const Plan pl = plan(batch, L, nheads, headdim);
-    if (pl.nseg <= 1) return 0;
-    return align256((size_t)(batch * nheads * pl.nseg * headdim * n_complex * 2) * sizeof(float)) +
-           (size_t)(batch * nheads * pl.nseg * 2) * sizeof(float);
+    return ws_layout(batch, L, nheads, headdim, n_complex).total;
+}
+
+int64_t cssd_prep_blocks(int64_t batch, int64_t L, int64_t nheads, int64_t ngroups) {
+    return batch * ((L + kT - 1) / kT) * ngroups * ((nheads / ngroups + 7) / 8);
 }
 
 hipError_t launch_cssd(const CssdArgs &a, hipStream_t stream, const char **kernel_name) {
@@ -654,15 +790,17 @@ hipError_t launch_cssd(const CssdArgs &a, hipStream_t stream, const char **kerne
     p.flags = a.flags;
     p.lgR = 0;
     while ((int64_t(1) << p.lgR) < a.rank) ++p.lgR;
-    const Plan pl = plan(p.batch, p.L, p.H, p.P);
-    p.nseg = pl.nseg;
-    p.Ls = pl.Ls;
+    const WsLayout w = ws_layout(p.batch, p.L, p.H, p.P, p.Nc);
+    p.nseg = w.pl.nseg;
+    p.Ls = w.pl.Ls;
+    p.nck = w.nck;
+    char *ws = static_cast<char *>(a.workspace);
     if (p.nseg > 1) {
-        p.ws_state = static_cast<float *>(a.workspace);
-        p.ws_decay = reinterpret_cast<float *>(
-            static_cast<char *>(a.workspace) +
-            align256((size_t)(p.batch * p.H * p.nseg * p.P * p.Nc * 2) * sizeof(float)));
+        p.ws_state = reinterpret_cast<float *>(ws + w.state);
+        p.ws_decay = reinterpret_cast<float *>(ws + w.decay);
     }
+    p.rec = reinterpret_cast<CRec *>(ws + w.rec);
+    p.mtile = reinterpret_cast<f32x4 *>(ws + w.mtile);
     if (p.P == 32) launch_k<2>(p, stream);
     else if (p.P == 64) launch_k<4>(p, stream);
     else launch_k<8>(p, stream);

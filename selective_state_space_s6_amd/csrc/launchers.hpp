@@ -155,6 +155,8 @@ struct CssdArgs {
 // L counts steps x rank for the multi-input multi-output form
 size_t cssd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim,
                             int64_t n_complex, int64_t chunk_len);
+// work groups of the per-chunk preparation pass (must fit a launch)
+int64_t cssd_prep_blocks(int64_t batch, int64_t L, int64_t nheads, int64_t ngroups);
 hipError_t launch_cssd(const CssdArgs &a, hipStream_t stream, const char **kernel_name);
 
 }  // namespace ssm

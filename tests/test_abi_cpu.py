@@ -219,11 +219,15 @@ def test_cssd_argument_checks(lib):
     assert _cssd(lib, flags=0xC) == INVALID
     assert _cssd(lib, flags=0x20) == INVALID
     assert _cssd(lib, dims=(2, 100, 4, 64, 72, 2, 64)) == UNSUPPORTED and "n_complex" in _err(lib)
-    # long sequences are cut into segments whose states go through the workspace
+    # the workspace holds a 528-byte chunk record and 3 KiB of M tiles per (batch, head,
+    # 32-step chunk), and, for long sequences, the segment states
+    short = lib.ssd_cplx_chunk_scan_fwd_workspace_size(2, 100, 4, 64, 32, 2, 64)
+    assert short >= 2 * 4 * 4 * (528 + 3072)
+    assert _cssd(lib, ws=None) == WORKSPACE
+    assert _cssd(lib, wsb=short - 1) == WORKSPACE
     long_dims = (4, 8192, 32, 64, 32, 1, 64)
     need = lib.ssd_cplx_chunk_scan_fwd_workspace_size(*long_dims)
-    assert need >= 4 * 32 * 2 * 64 * 32 * 2 * 4
-    assert lib.ssd_cplx_chunk_scan_fwd_workspace_size(2, 100, 4, 64, 32, 2, 64) == 0
+    assert need >= 4 * 32 * 2 * 64 * 32 * 2 * 4 + 4 * 32 * 256 * (528 + 3072)
     assert _cssd(lib, dims=long_dims, ws=None) == WORKSPACE
     assert _cssd(lib, dims=long_dims, wsb=need - 1) == WORKSPACE
 
@@ -318,7 +322,8 @@ def test_cssd_mimo_argument_checks(lib):
     dims = (4, 2048, 4, 32, 64, 32, 1, 64)
     need = lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size(*dims)
     assert need == lib.ssd_cplx_chunk_scan_fwd_workspace_size(4, 8192, 32, 64, 32, 1, 64) > 0
-    assert lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size(2, 25, 4, 4, 64, 32, 2, 64) == 0
+    assert (lib.ssd_cplx_mimo_chunk_scan_fwd_workspace_size(2, 25, 4, 4, 64, 32, 2, 64) ==
+            lib.ssd_cplx_chunk_scan_fwd_workspace_size(2, 100, 4, 64, 32, 2, 64))
     assert _mimo(lib, dims=dims, ws=None) == WORKSPACE
     assert _mimo(lib, dims=dims, wsb=need - 1) == WORKSPACE
 
