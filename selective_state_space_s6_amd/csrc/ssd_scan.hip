@@ -108,7 +108,6 @@ struct Scal {
     float gam[kT];   // input scale of the step's own output (differs from sig in the trapezoidal form)
     float w[kT];     // e^{cs_end - cs_s} sigma_s
     float end;       // e^{cs_end}
-    float csend;     // cs_end
 };
 
 // D1 for one chunk, by one wave (lanes 0..31 hold steps 0..31).
@@ -141,10 +140,7 @@ __device__ __forceinline__ void chunk_scalars(Scal &sc, float dtv, bool valid, f
         sc.gam[lane] = gm;
         sc.w[lane] = __expf(cend - v) * sg;
     }
-    if (lane == 0) {
-        sc.end = __expf(cend);
-        sc.csend = cend;
-    }
+    if (lane == 0) sc.end = __expf(cend);
 }
 
 // x tile row pitch (bf16) for P head channels: the row stride in dwords is
@@ -311,7 +307,8 @@ struct Work {
 // The segment is walked backwards, so the weight of step s is one exp of the
 // running suffix sum of a (same-signed terms, no cancellation) and the state
 // needs no rescaling between chunks; the contraction over s is a plain GEMM.
-// Chunks are loaded NS = 3 chunks ahead.
+// Chunks are loaded NS = 2 chunks ahead (two register stages keep the kernel
+// within 128 registers, four groups of four waves per compute unit).
 template <int NS, int I, typename F>
 __device__ __forceinline__ void unroll_stages(F &&f) {
     if constexpr (I < NS) {
@@ -323,7 +320,7 @@ __device__ __forceinline__ void unroll_stages(F &&f) {
 template <int NMAX, bool EXACT, int NW, bool TRAP>
 __global__ void __launch_bounds__(64 * NW)
 ssd_state_kernel(SsdKp p) {
-    constexpr int NS = 3;
+    constexpr int NS = 2;
     using St = Stager<NMAX, NW, false, NS, TRAP>;
     constexpr int NT = NMAX / 16;
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * St::BCP];
@@ -498,6 +495,20 @@ ssd_scan_kernel(SsdKp p) {
         const uint16_t *B_ = Bs[buf], *C_ = Cs[buf], *X_ = Xs[buf];
         const Scal &sc = scal[buf];
 
+        // Stage chunk j+1 (loaded during chunk j-1) into the buffers chunk j-1
+        // used, which its closing barrier freed, and start loading chunk j+2,
+        // which then has a whole chunk to arrive.  The last wave takes the next
+        // chunk's scalars while the first waves form the decay mask.
+        if (j + 1 < nchunks) {
+            const float dtn = st.rdt[0];
+            const TrapIn tin = TRAP ? st.rtp[0] : TrapIn{};
+            st.template store<0>(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1]);
+            if (j + 2 < nchunks) st.template load<0>(t0 + 2 * kT);
+            if (wid == NW - 1)
+                chunk_scalars(scal[buf ^ 1], dtn, t0 + kT + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane,
+                              TRAP ? &tin : nullptr);
+        }
+
         // D4, shared: G^T[s][t] = B[s].C[t] for the causal tile pairs (s-tile,
         // t-tile) (0,0), (0,1), (1,1), one per wave (wave tau % NW); lane holds
         // column t, rows s = q*4 .. q*4+3.  M[t][s] = G[t][s] e^{cs_t - cs_s}
@@ -614,14 +625,6 @@ ssd_scan_kernel(SsdKp p) {
         // D2+D3
         state_update<NT, BCP>(S, B_, Wh, Wl, sc.end, N, lane);
 
-        // stage chunk j+1, start loading chunk j+2
-        if (j + 1 < nchunks) {
-            st.template store<0>(Bs[buf ^ 1], Cs[buf ^ 1], Xs[buf ^ 1]);
-            if (wid == NW - 1)   // the wave with the least decay-mask work
-                chunk_scalars(scal[buf ^ 1], st.rdt[0], t0 + kT + (lane & 31) < p.L && lane < kT, bias, A,
-                              p.mode, lane, TRAP ? &st.rtp[0] : nullptr);
-            if (j + 2 < nchunks) st.template load<0>(t0 + 2 * kT);
-        }
         __syncthreads();
     }
 
