@@ -60,16 +60,16 @@ TRAFFIC = {
         "bytes": 308885163
     },
     "ssd_mamba2": {
-        "src_sha1": "d6c4b3104807a80a4751a9c565e5f72d8a4887e1",
-        "bytes": 502653439
+        "src_sha1": "33a140e3f5b78de7f34ac1211c32f4ace39a0188",
+        "bytes": 502525333
     },
     "ssd_long": {
-        "src_sha1": "d6c4b3104807a80a4751a9c565e5f72d8a4887e1",
-        "bytes": 3591845848
+        "src_sha1": "33a140e3f5b78de7f34ac1211c32f4ace39a0188",
+        "bytes": 3659754678
     },
     "cssd_mamba3": {
-        "src_sha1": "e1f701c6580d12e54c97d7e516054ab31c714f40",
-        "bytes": 845981900
+        "src_sha1": "865421db1dc9ca87b5b2912f81a362e0ac213017",
+        "bytes": 1106295030
     }
 }
 # adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
@@ -492,7 +492,7 @@ def make_runner(name, dev):
             t = copies[i % N_ROTATE]
             lib.ssd_cplx_mimo_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
                                              None, chunk_len=w["chunk_len"], y=y, h_final=hf, workspace=ws)
-        return step, dims, w, ["cssd_state_kernel", "cssd_pass_kernel", "cssd_scan_kernel"]
+        return step, dims, w, ["cssd_prep_kernel", "cssd_state_kernel", "cssd_pass_kernel", "cssd_scan_kernel"]
     ws = torch.empty(lib.ssd_cplx_chunk_scan_fwd_workspace_size(
         dims["batch"], dims["L"], dims["nheads"], dims["headdim"], dims["n_complex"],
         dims["ngroups"], w["chunk_len"]), dtype=torch.uint8, device=dev)
@@ -501,7 +501,7 @@ def make_runner(name, dev):
         t = copies[i % N_ROTATE]
         lib.ssd_cplx_chunk_scan_fwd(t["x"], t["dt"], t["dt_bias"], t["A_log"], t["B"], t["C"], t["D"],
                                     None, chunk_len=w["chunk_len"], y=y, h_final=hf, workspace=ws)
-    return step, dims, w, ["cssd_state_kernel", "cssd_pass_kernel", "cssd_scan_kernel"]
+    return step, dims, w, ["cssd_prep_kernel", "cssd_state_kernel", "cssd_pass_kernel", "cssd_scan_kernel"]
 
 
 def time_steps(step, steps, warmup):
