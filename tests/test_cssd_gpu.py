@@ -26,6 +26,10 @@ CASES = [  # batch, L, H, P, Nc, G, Q, flags, h0
     (1, 800, 2, 64, 32, 1, 64, STABLE | ZOH | CONJ, True),
     (2, 700, 3, 128, 64, 3, 128, STABLE | DT, False),
     (1, 513, 1, 32, 40, 1, 32, STABLE | ONE, True),
+    # heads per group beyond one prep block of 8: a full and a half block (12), one wave
+    # with a single valid half (5 per group, 2 groups)
+    (1, 300, 12, 32, 8, 1, 32, STABLE | ZOH, True),
+    (2, 333, 10, 32, 16, 2, 64, STABLE | ZOH | CONJ, False),
 ]
 
 
@@ -54,3 +58,37 @@ def test_cssd_workload_all_heads(cuda_device):
                 for b in range(w["batch"]) for h in range(w["nheads"])]
     report("cssd_mamba3 all heads", y=ey, h_final=eh, worst_head=max(per_head), margin=TOL_F32 / max(ey, eh))
     assert ey <= TOL_F32 and eh <= TOL_F32
+
+
+def _one_head(inp, h, G, H):
+    """The inputs of head h alone: one head in one group (the group's B and C)."""
+    import copy
+    g = h * G // H
+    a = dict(inp.arrays)
+    for k in ("x", "dt"):
+        a[k] = np.ascontiguousarray(a[k][:, :, h:h + 1])
+    for k in ("A_log", "dt_bias", "D"):
+        a[k] = np.ascontiguousarray(a[k][h:h + 1])
+    for k in ("B", "C"):
+        a[k] = np.ascontiguousarray(a[k][:, :, g:g + 1])
+    if a["h0"] is not None:
+        a["h0"] = np.ascontiguousarray(a["h0"][:, h:h + 1])
+    one = copy.copy(inp)
+    one.arrays = a
+    return one
+
+
+@pytest.mark.parametrize("case", [(1, 1100, 9, 64, 32, 1, 64, True), (2, 333, 10, 32, 16, 2, 64, False)],
+                         ids=lambda c: f"b{c[0]}L{c[1]}H{c[2]}P{c[3]}N{c[4]}G{c[5]}")
+def test_head_grouping_changes_no_value(cuda_device, case):
+    """The prep pass shares C.B^T among up to 8 heads of a group and forms two heads' scalars per
+    wave: every head's outputs and final state must be bitwise those of the head run alone
+    (9 heads: a ninth head alone in its block, with segments; 10 heads in 2 groups: a wave with
+    one valid half)."""
+    batch, L, H, P, Nc, G, Q, h0 = case
+    inp = synth.cssd_inputs(batch, L, H, P, Nc, G, seed=(310 + L,), h0=h0)
+    y, hf = gpu_cssd(inp, cuda_device, STABLE | ZOH, Q)
+    for h in range(H):
+        y1, h1 = gpu_cssd(_one_head(inp, h, G, H), cuda_device, STABLE | ZOH, Q)
+        assert np.array_equal(y1[:, :, 0], y[:, :, h]), f"head {h}: y differs from the head alone"
+        assert np.array_equal(h1[:, 0], hf[:, h]), f"head {h}: h_final differs from the head alone"

@@ -31,6 +31,7 @@ CASES = [  # batch, L, rank, H, P, Nc, G, flags, h0
     (1, 1, 16, 2, 64, 32, 1, ZOH, True),             # one step
     (1, 3, 4, 3, 32, 8, 3, ZOH, True),
     (1, 700, 2, 2, 64, 32, 2, ZOH, False),
+    (1, 45, 4, 12, 32, 16, 1, ZOH, True),           # 12 heads per group: two prep blocks
 ]
 
 
