@@ -230,6 +230,9 @@ def test_cssd_argument_checks(lib):
     assert need >= 4 * 32 * 2 * 64 * 32 * 2 * 4 + 4 * 32 * 256 * (528 + 3072)
     assert _cssd(lib, dims=long_dims, ws=None) == WORKSPACE
     assert _cssd(lib, dims=long_dims, wsb=need - 1) == WORKSPACE
+    # within the element limits, but the per-chunk prep pass would need more than 2^31 - 1
+    # work groups (2^32 chunks x 8 groups): refused before any launch
+    assert _cssd(lib, dims=(1, 1 << 37, 8, 32, 8, 8, 64)) == UNSUPPORTED and "too large" in _err(lib)
 
 
 def _s6g(lib, dims=(2, 8, 16, 16, 16), dtype=0, flags=0, y=FAKE, u=FAKE, B=FAKE):
@@ -326,6 +329,7 @@ def test_cssd_mimo_argument_checks(lib):
             lib.ssd_cplx_chunk_scan_fwd_workspace_size(2, 100, 4, 64, 32, 2, 64))
     assert _mimo(lib, dims=dims, ws=None) == WORKSPACE
     assert _mimo(lib, dims=dims, wsb=need - 1) == WORKSPACE
+    assert _mimo(lib, dims=(1, 1 << 35, 4, 8, 32, 8, 8, 64)) == UNSUPPORTED and "too large" in _err(lib)
 
 
 def _trap(lib, dims=(2, 300, 4, 64, 128, 64), dtype=1, ws=ctypes.c_void_p(0x9000000), wsb=1 << 40,
