@@ -76,6 +76,7 @@ TRAFFIC = {
 # (products and fmas, 24 flops) plus the recomputed Abar, beta, phi1' (not counted again)
 S6_BWD_FLOPS_PER_UPDATE = 24
 N_ROTATE = 3                     # input copies rotated between steps (> Infinity Cache)
+CPU_SAMPLE_WALL_S = 1.0          # wall time the SSD-type oracle samples aim at (16 host threads)
 # (--copies 1 for the counter runs, where each dispatch is read on its own)
 
 
@@ -689,7 +690,8 @@ def cpu_baseline_units(name, n_units):
         return {"value": elems / sec, "unit": "elements/s", "cores": 1, "kind": "oracle",
                 "sample": f"1 of {d['batch']} batch rows of {name} ({elems} elements, {sec:.2f} s wall)"}
     nthr = oracle.default_threads()
-    n_units = min(n_units, d["batch"] * d["nheads"])
+    total = d["batch"] * d["nheads"]
+    n_units = min(n_units, total)
     units = np.stack([np.arange(n_units) % d["batch"], np.arange(n_units) // d["batch"]], 1)
     if w["kind"] == "trap_rot":      # one batch row of the rotation (single-threaded oracle)
         a = inp.arrays
@@ -700,15 +702,25 @@ def cpu_baseline_units(name, n_units):
         elems = d["L"] * d["nheads"] * d["headdim"]
         return {"value": elems / sec, "unit": "elements/s", "cores": 1, "kind": "oracle",
                 "sample": f"1 of {d['batch']} batch rows of {name} ({elems} elements, {sec:.2f} s wall)"}
-    t0 = time.perf_counter()
-    if w["kind"] == "trap":
-        oracle.trap_fwd(**inp.arrays, units=units, nthreads=nthr)
-    elif w["kind"] == "cssd_mimo":
-        oracle.cssd_mimo_fwd(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
-    else:
-        fn = oracle.ssd_fwd if w["kind"] == "ssd" else oracle.cssd_fwd
-        fn(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
-    sec = time.perf_counter() - t0
+    def run(units):
+        t0 = time.perf_counter()
+        if w["kind"] == "trap":
+            oracle.trap_fwd(**inp.arrays, units=units, nthreads=nthr)
+        elif w["kind"] == "cssd_mimo":
+            oracle.cssd_mimo_fwd(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
+        else:
+            fn = oracle.ssd_fwd if w["kind"] == "ssd" else oracle.cssd_fwd
+            fn(**inp.arrays, ngroups=d["ngroups"], units=units, nthreads=nthr)
+        return time.perf_counter() - t0
+
+    # a first sample sizes the timed one: as many units as take about CPU_SAMPLE_WALL_S of
+    # wall time on the host threads (at most the whole workload)
+    sec = run(units)
+    n_more = min(total, int(CPU_SAMPLE_WALL_S / max(sec / n_units, 1e-9)))
+    if n_more > n_units:
+        n_units = n_more
+        units = np.stack([np.arange(n_units) % d["batch"], np.arange(n_units) // d["batch"]], 1)
+        sec = run(units)
     elems = n_units * d["L"] * d.get("rank", 1) * d["headdim"]
     return {"value": elems / sec, "unit": "elements/s", "cores": nthr, "kind": "oracle",
             "sample": f"{n_units} of {d['batch'] * d['nheads']} (b, head) units of {name} "
