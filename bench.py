@@ -907,7 +907,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="measure this workload alone (headline schema)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -949,22 +949,21 @@ def main():
         "config": {"workload": head, **line["config"]},
         "roofline": line["roofline"],
     }
-    if not args.no_cpu:
-        log(f"[bench] cpu baseline (oracle) {head}")
-        out["cpu_baseline"] = cpu_baseline(head, m["kind"])
+    # every GPU measurement first, then the host-side oracle baselines, so that no
+    # measurement follows a stretch of host work with the GPU idle
+    kinds = {head: m["kind"]}
+    del m
+    torch.cuda.empty_cache()
     if not single:
         cfgs = []
         for name in CONFIGS:
             if name == head:
                 c = dict(line)
-                if "cpu_baseline" in out:
-                    c["cpu_baseline"] = out["cpu_baseline"]
             else:
                 log(f"[bench] config {name}")
                 cm = measure(name, dev, args.steps, args.warmup)
                 c = config_line(cm)
-                if not args.no_cpu:
-                    c["cpu_baseline"] = cpu_baseline(name, cm["kind"])
+                kinds[name] = cm["kind"]
                 del cm
                 torch.cuda.empty_cache()
             cfgs.append(c)
@@ -978,6 +977,16 @@ def main():
             del s
             torch.cuda.empty_cache()
         out["secondary"] = sec
+    if not args.no_cpu:
+        log(f"[bench] cpu baseline (oracle) {head}")
+        out["cpu_baseline"] = cpu_baseline(head, kinds[head])
+        for c in out.get("configs", []):
+            name = c["workload"]
+            if name == head:
+                c["cpu_baseline"] = out["cpu_baseline"]
+            else:
+                log(f"[bench] cpu baseline (oracle) {name}")
+                c["cpu_baseline"] = cpu_baseline(name, kinds[name])
     print(json.dumps(out), flush=True)
 
 
