@@ -46,10 +46,11 @@ FP32_VALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, n
 # fp32 VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz lane-slots/s (a wave64 op takes 4 cycles)
 VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
 # one ZOH state update (b, t, d, n) of the S6 kernel: x = dl*A, exp2 (half rate: 2 slots), the
-# (Abar-1)/A form, the 3-FMA series for phi1 and delta*p, compare + select, Abar = 1 + A beta,
-# B*u, beta*(B u), h = fma, y += C*h, and the partial-sum add of the reduction over states:
-# 15 single-rate ops + the exp = 17 issue slots (the compiled loop: 16.6 VALU instructions)
-S6_SLOTS_PER_UPDATE = 17
+# (Abar-1)/A form, the 3-FMA series for phi1 and delta*p, compare + select, B*u, the state
+# update h + beta (A h + B u) (two FMAs), y += C*h, and the partial-sum add of the reduction
+# over states: 14 single-rate ops + the exp = 16 issue slots (counted: 15.8 VALU instructions
+# per update at the Mamba-1 shape)
+S6_SLOTS_PER_UPDATE = 16
 S6_FLOPS_PER_UPDATE = 9          # the method's flops per update (the series is the exp's cost)
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled
 # by the same counters on a 1 GiB device copy (bench.py --workload copy_1gib); each entry is

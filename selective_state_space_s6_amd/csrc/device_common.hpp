@@ -60,6 +60,18 @@ __device__ __forceinline__ Zoh zoh_exact(float dl, float A, float A2, float iA) 
     return {fmaf(A, beta, 1.0f), beta};
 }
 
+// One state update h <- Abar h + beta b (b = B u) under the exact hold, where
+// Abar = 1 + A beta_zoh.  With the ZOH input scale (beta = beta_zoh) it is
+// h + beta (A h + b): two fused operations in which Abar is never rounded
+// (rounded, Abar carries an absolute error of up to 2^-24 next to 1, the
+// largest per-step error of a slowly decaying state).  With the other input
+// scales (beta = delta or 1) Abar is taken as formed.
+template <int MODE>
+__device__ __forceinline__ float hold_step(float h, float ab, float A, float beta, float b) {
+    if constexpr (MODE == 0) return fmaf(beta, fmaf(A, h, b), h);
+    return fmaf(ab, h, beta * b);
+}
+
 // SiLU(v) = v / (1 + e^-v), with the hardware reciprocal (about 1 ulp) in place of a
 // division; for very negative v, e^-v overflows, its reciprocal is 0 and the result -0
 __device__ __forceinline__ float silu_f(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }

@@ -243,7 +243,7 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
                     constexpr int i = decltype(ii)::value;
                     const Zoh zh = coef(dl4[i]);
                     const float bu = row_bcast<4 * q + i>(Bv) * uu4[i];
-                    h = fmaf(zh.ab, h, zh.beta * bu);
+                    h = hold_step<MODE>(h, zh.ab, A, zh.beta, bu);
                 });
             });
             stage(buf ^ 1, kt + 1, RSn, last);
@@ -285,7 +285,7 @@ __device__ __forceinline__ void s6_bwd_body(const S6BKp &p, Lds &S) {
                     constexpr int t = 4 * q + i;
                     const Zoh zh = coef(dl4[i]);
                     const float bu = row_bcast<t>(Bv) * uu4[i];
-                    hh = fmaf(zh.ab, hh, zh.beta * bu);
+                    hh = hold_step<MODE>(hh, zh.ab, A, zh.beta, bu);
                     hs[t] = hh;
                 });
                 __builtin_amdgcn_sched_barrier(0);

@@ -131,7 +131,7 @@ s6_grouped_kernel(S6Gp p) {
                 const float cm = nval[j] ? R.C[t][j] : 0.0f;
                 const Zoh zh = zoh_exact(dl, Av[j], A2[j], iA[j]);   // Abar, (Abar - 1)/A
                 const float beta = MODE == 0 ? zh.beta : MODE == 1 ? dl : 1.0f;
-                h[j] = fmaf(zh.ab, h[j], beta * (bm * uu));
+                h[j] = hold_step<MODE>(h[j], zh.ab, Av[j], beta, bm * uu);
                 ys = fmaf(cm, h[j], ys);
             }
             part[t] = ys;
@@ -324,7 +324,7 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
                 const float dl = row_bcast<t>(dlk), uu = row_bcast<t>(uk);
                 const Zoh zh = coef(dl);
                 const float bm = nval ? R.B[t] : 0.0f;
-                h = fmaf(zh.ab, h, zh.beta * (bm * uu));
+                h = hold_step<MODE>(h, zh.ab, A, zh.beta, bm * uu);
             });
         };
         for (int64_t kt = 0; kt < ntiles; kt += 2) {
@@ -360,7 +360,7 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
                 const float dl = row_bcast<t>(dlk), uu = row_bcast<t>(uk);
                 const Zoh zh = coef(dl);
                 const float bm = nval ? R.B[t] : 0.0f;
-                hh = fmaf(zh.ab, hh, zh.beta * (bm * uu));
+                hh = hold_step<MODE>(hh, zh.ab, A, zh.beta, bm * uu);
                 hs[t] = hh;
             });
         }

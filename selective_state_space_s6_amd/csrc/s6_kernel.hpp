@@ -319,10 +319,9 @@ s6_scan_kernel(S6Kp p) {
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) {
                     const Zoh zh = zoh_exact(dl, Av[j], A2[j], iA[j]);   // Abar, (Abar - 1)/A
-                    const float ab = zh.ab;
                     const float beta = MODE == 0 ? zh.beta : MODE == 1 ? dl : 1.0f;
                     const float bu = row_bcast<t>(Bm[j]) * uu;   // B[t, n] * u[t, d]
-                    h[j] = fmaf(ab, h[j], beta * bu);
+                    h[j] = hold_step<MODE>(h[j], zh.ab, Av[j], beta, bu);
                     if constexpr (YOUT) {
                         if (j == 0) ys = row_bcast<t>(Cm[j]) * h[j];
                         else ys = fmaf(row_bcast<t>(Cm[j]), h[j], ys);
