@@ -57,20 +57,20 @@ S6_FLOPS_PER_UPDATE = 9          # the method's flops per update (the series is 
 # valid only while the sha1 of the kernels' sources matches (profiles/*.md, "HBM traffic")
 TRAFFIC = {
     "s6_mamba1": {
-        "src_sha1": "138bc04ec70d50e744b2cc62138b54e2f6435f4d",
-        "bytes": 308885163
+        "src_sha1": "a79736759aeaa1fce6cc1bbc7762eaa5f3d16967",
+        "bytes": 308664790
     },
     "ssd_mamba2": {
-        "src_sha1": "33a140e3f5b78de7f34ac1211c32f4ace39a0188",
-        "bytes": 502525333
+        "src_sha1": "dfd3486c9fa641ec6b411b76f88d752c2685cbe6",
+        "bytes": 502571839
     },
     "ssd_long": {
-        "src_sha1": "33a140e3f5b78de7f34ac1211c32f4ace39a0188",
-        "bytes": 3659754678
+        "src_sha1": "dfd3486c9fa641ec6b411b76f88d752c2685cbe6",
+        "bytes": 3659528830
     },
     "cssd_mamba3": {
-        "src_sha1": "865421db1dc9ca87b5b2912f81a362e0ac213017",
-        "bytes": 1106295030
+        "src_sha1": "d6c57f3db1e631ca1bd045b8cad57a67034d2545",
+        "bytes": 1106275978
     }
 }
 # adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
