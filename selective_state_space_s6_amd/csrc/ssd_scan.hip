@@ -154,12 +154,16 @@ constexpr int x_pitch(int P) { return P == 32 ? 48 : P == 64 ? 72 : 152; }
 // plus a 32-bit per-thread offset; a chunk that crosses L clamps its step
 // index into the tensors (rows past L never contribute: their sigma and w are
 // 0 and their outputs are not stored).
-template <int NMAX, int NW, bool WITH_C, int NS = 1, bool TRAP = false>
+template <int NMAX, int NW, bool WITH_C, int NS = 1, bool TRAP = false, bool ROWS8 = false>
 struct Stager {
     static constexpr int NTHR = 64 * NW;
     static constexpr int P = 16 * NW;
-    static constexpr int BCP = NMAX == 64 ? 72 : 2 * (NMAX / 2 + 12);  // B/C row pitch (bf16)
-    static constexpr int XP = x_pitch(P);
+    // B/C and x row pitches (bf16).  ROWS8: the tiles are read only by
+    // transposed reads in which 32 lanes take 8 consecutive rows, 8 dwords each
+    // (ds_read_b64_tr_b16 serves 32 lanes per cycle): a row stride of an odd
+    // multiple of 8 dwords puts them on distinct banks of the 64
+    static constexpr int BCP = ROWS8 ? NMAX + 16 : NMAX == 64 ? 72 : 2 * (NMAX / 2 + 12);
+    static constexpr int XP = ROWS8 ? P + 16 : x_pitch(P);
     static constexpr int LDN = NMAX / 8;                // 16-byte pieces per B/C row
     static constexpr int PER_T = kT * LDN / NTHR;       // B (and C) pieces per thread
     static constexpr int SB_STEP = NTHR / LDN;          // steps between pieces i, i+1
@@ -293,6 +297,44 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NT], const uint16_t *B_,
     }
 }
 
+// D2+D3 for one wave with the weighted inputs as B operands in registers, K
+// slot q*8+i <-> step q*4+i (i < 4) and 16+q*4+(i-4) (i >= 4); the A operand
+// B^T is read transposed in the same step order, so the 32 lanes of one read
+// cover 8 consecutive rows
+template <int NT, int BCP>
+__device__ __forceinline__ void state_update_regs(f32x4 (&S)[NT], const uint16_t *B_, u32x4 Whf, u32x4 Wlf,
+                                                  float e, int N, int lane) {
+    const int q = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (nt * 16 >= N) break;
+        S[nt] *= e;
+        const uint2 a0 = tr_read(B_, BCP, q * 4, nt * 16, lane);
+        const uint2 a1 = tr_read(B_, BCP, 16 + q * 4, nt * 16, lane);
+        const u32x4 Af{a0.x, a0.y, a1.x, a1.y};
+        S[nt] = mfma16(Af, Whf, S[nt]);
+        S[nt] = mfma16(Af, Wlf, S[nt]);
+    }
+}
+
+// The weighted inputs w_s x[s][p] of one wave's 16 channels for the steps of
+// that K order, as hi + lo B operands, from the x tile (transposed reads) and
+// the step weights
+template <int XP>
+__device__ __forceinline__ void weighted_x_regs(const uint16_t *Xs, int p0, const float *w, int lane,
+                                                u32x4 &Whf, u32x4 &Wlf) {
+    const int q = lane >> 4;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const uint2 xv = tr_read(Xs, XP, tt * 16 + q * 4, p0, lane);
+        const float4 w4 = *reinterpret_cast<const float4 *>(&w[tt * 16 + q * 4]);
+        const uint2 u0 = split_bf16(w4.x * lo_f(xv.x), w4.y * hi_f(xv.x));
+        const uint2 u1 = split_bf16(w4.z * lo_f(xv.y), w4.w * hi_f(xv.y));
+        Whf[2 * tt] = u0.x; Whf[2 * tt + 1] = u1.x;
+        Wlf[2 * tt] = u0.y; Wlf[2 * tt + 1] = u1.y;
+    }
+}
+
 // work index -> (b, segment, h); heads of one (batch, segment) are consecutive,
 // so the groups that share B and C rows land on one XCD
 struct Work {
@@ -321,12 +363,10 @@ template <int NMAX, bool EXACT, int NW, bool TRAP>
 __global__ void __launch_bounds__(64 * NW)
 ssd_state_kernel(SsdKp p) {
     constexpr int NS = 2;
-    using St = Stager<NMAX, NW, false, NS, TRAP>;
+    using St = Stager<NMAX, NW, false, NS, TRAP, true>;
     constexpr int NT = NMAX / 16;
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * St::BCP];
     __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kT * St::XP];
-    __shared__ __attribute__((aligned(16))) uint16_t Wh[NW][kT * WP];
-    __shared__ __attribute__((aligned(16))) uint16_t Wl[NW][kT * WP];
     __shared__ __attribute__((aligned(16))) float wsc[2][kT];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -386,8 +426,9 @@ ssd_state_kernel(SsdKp p) {
             const int64_t c = c0 + S_;
             if (c >= nch) return;
             const int buf = (int)(c & 1);
-            weighted_x<St::XP>(Xs[buf], p0, wsc[buf], Wh[wid], Wl[wid], lane);
-            state_update<NT, St::BCP>(S, Bs[buf], Wh[wid], Wl[wid], 1.0f, N, lane);
+            u32x4 Whf, Wlf;
+            weighted_x_regs<St::XP>(Xs[buf], p0, wsc[buf], lane, Whf, Wlf);
+            state_update_regs<NT, St::BCP>(S, Bs[buf], Whf, Wlf, 1.0f, N, lane);
             if (c + 1 < nch) {
                 constexpr int SN = (S_ + 1) % NS;
                 st.template store<SN>(Bs[buf ^ 1], nullptr, Xs[buf ^ 1]);
