@@ -61,12 +61,12 @@ TRAFFIC = {
         "bytes": 308664790
     },
     "ssd_mamba2": {
-        "src_sha1": "dfd3486c9fa641ec6b411b76f88d752c2685cbe6",
-        "bytes": 502571839
+        "src_sha1": "1f0b778c66c7bafa1ee8976d37b639fa1ddefb60",
+        "bytes": 502800612
     },
     "ssd_long": {
-        "src_sha1": "dfd3486c9fa641ec6b411b76f88d752c2685cbe6",
-        "bytes": 3659528830
+        "src_sha1": "1f0b778c66c7bafa1ee8976d37b639fa1ddefb60",
+        "bytes": 3664825240
     },
     "cssd_mamba3": {
         "src_sha1": "d6c57f3db1e631ca1bd045b8cad57a67034d2545",
