@@ -61,11 +61,11 @@ TRAFFIC = {
         "bytes": 308664790
     },
     "ssd_mamba2": {
-        "src_sha1": "1f0b778c66c7bafa1ee8976d37b639fa1ddefb60",
+        "src_sha1": "9c04e59c1aa97a758b2033036989e17cda798706",
         "bytes": 502800612
     },
     "ssd_long": {
-        "src_sha1": "1f0b778c66c7bafa1ee8976d37b639fa1ddefb60",
+        "src_sha1": "9c04e59c1aa97a758b2033036989e17cda798706",
         "bytes": 3664825240
     },
     "cssd_mamba3": {

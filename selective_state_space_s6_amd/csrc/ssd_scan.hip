@@ -143,9 +143,11 @@ __device__ __forceinline__ void chunk_scalars(Scal &sc, float dtv, bool valid, f
     if (lane == 0) sc.end = __expf(cend);
 }
 
-// x tile row pitch (bf16) for P head channels: the row stride in dwords is
-// 24, 36 or 12 (mod 64), so that the four rows of a transposed read (8 dwords
-// each) and the rows of a b128 read fall on distinct banks
+// x tile row pitch (bf16) for P head channels in the scan kernel: the row
+// stride in dwords is 24, 36 or 12 (mod 64), so the four rows that 16 lanes of
+// a transposed read take (8 dwords each) fall on distinct banks.  The 32 lanes
+// served per cycle still meet on a few banks (2-way); the state kernel, whose
+// tiles see only transposed reads, uses the conflict-free pitch P + 16.
 constexpr int x_pitch(int P) { return P == 32 ? 48 : P == 64 ? 72 : 152; }
 
 // LDS and register staging of one chunk of x, B (and C), dt for a work group
