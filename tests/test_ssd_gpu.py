@@ -37,6 +37,7 @@ CASES = [  # batch, L, H, P, N, G, Q, flags, h0
     (1, 1500, 1, 32, 64, 1, 64, ZOH, True),
     (1, 777, 3, 128, 128, 3, 128, DT, True),
     (1, 1100, 2, 64, 96, 2, 64, ONE, False),
+    (1, 1100, 2, 64, 256, 1, 256, DT, True),      # the largest state size, with segments
 ]
 
 

@@ -33,6 +33,7 @@ CASES = [  # batch, L, H, P, N, Q, h0, carried previous input
     (1, 1500, 1, 32, 64, 64, False, True),
     (1, 777, 3, 128, 128, 128, True, True),
     (1, 1100, 2, 64, 160, 64, False, False),
+    (1, 900, 2, 64, 256, 64, True, True),        # the largest state size, with segments
 ]
 
 
