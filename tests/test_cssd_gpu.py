@@ -92,3 +92,19 @@ def test_head_grouping_changes_no_value(cuda_device, case):
         y1, h1 = gpu_cssd(_one_head(inp, h, G, H), cuda_device, STABLE | ZOH, Q)
         assert np.array_equal(y1[:, :, 0], y[:, :, h]), f"head {h}: y differs from the head alone"
         assert np.array_equal(h1[:, 0], hf[:, h]), f"head {h}: h_final differs from the head alone"
+
+
+@pytest.mark.parametrize("L", [300, 1100])
+def test_cssd_extreme_dt(cuda_device, L):
+    """Steps with delta ~ 1e-11 next to steps with delta ~ 25: per-step decays down to
+    e^{-68} and rotations of tens of radians, within one segment and across segments."""
+    inp = synth.cssd_inputs(1, L, 2, 64, 32, 1, seed=(37, L), h0=True)
+    dt = inp.arrays["dt"]
+    dt[:, ::3] = -25.0
+    dt[:, 1::7] = 25.0
+    y, hf = gpu_cssd(inp, cuda_device, STABLE | ZOH, 64)
+    yo, ho = oracle.cssd_fwd(**inp.arrays, ngroups=1, flags=STABLE | ZOH)
+    ey, eh = synth.max_rel_err(y, yo), synth.max_rel_err(hf, ho)
+    report(f"cssd extreme dt L={L}", y=ey, h_final=eh)
+    assert np.isfinite(y).all() and np.isfinite(hf).all()
+    assert ey <= TOL_F32 and eh <= TOL_F32

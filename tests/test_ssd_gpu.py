@@ -124,3 +124,24 @@ def test_ssd_carry_composition(cuda_device):
     y = torch.cat([first[0], second[0]], 1).cpu().numpy()
     assert synth.max_rel_err(y, whole[0].cpu().numpy()) <= TOL_BF16
     assert synth.max_rel_err(second[1].cpu().numpy(), whole[1].cpu().numpy()) <= TOL_BF16
+
+
+@pytest.mark.parametrize("flags", [DT, ZOH])
+@pytest.mark.parametrize("L", [300, 1100])
+def test_ssd_extreme_dt(cuda_device, flags, L):
+    """Steps with delta ~ 1e-11 (no decay, no input) next to steps with delta ~ 25 (the state
+    all but erased, inputs scaled by 25): cumulative decays of hundreds inside a chunk, within
+    one segment (L = 300) and across segment boundaries (L = 1100)."""
+    inp = synth.ssd_inputs(1, L, 3, 64, 128, 1, seed=(11, L), h0=True, D="normal")
+    dt = inp.arrays["dt"]
+    dt[:, ::3] = -25.0
+    dt[:, 1::7] = 25.0
+    _check(f"ssd extreme dt L={L} flags={flags}", inp, cuda_device, flags, 256)
+
+
+@pytest.mark.parametrize("a_log", [-30.0, -3.0, 4.0])
+def test_ssd_degenerate_A(cuda_device, a_log):
+    """A -> 0 (no decay: the scan is a running sum), slow decay, and fast decay (|A| = e^4)."""
+    inp = synth.ssd_inputs(1, 900, 2, 64, 128, 1, seed=(12,), h0=True, D="normal")
+    inp.arrays["A_log"][:] = a_log
+    _check(f"ssd A_log={a_log}", inp, cuda_device, ZOH, 256)

@@ -111,3 +111,14 @@ def test_trap_mamba3_workload_sampled(cuda_device):
     report(f"{name} sampled", y=ey, h_final=eh)
     assert np.isfinite(y).all()
     assert ey <= TOL_BF16 and eh <= TOL_BF16
+
+
+@pytest.mark.parametrize("L", [300, 1100])
+def test_trap_extreme_dt(cuda_device, L):
+    """dt of 1e-11 next to dt of 25 (decays e^{-25 |a|}, inputs scaled by 25), within one
+    segment and across segment boundaries."""
+    inp = synth.trap_inputs(1, L, 2, 64, 128, seed=(35, L), h0=True, prev=True)
+    dt = inp.arrays["dt"]
+    dt[:, ::3] = 1e-11
+    dt[:, 1::7] = 25.0
+    _check(f"trap extreme dt L={L}", inp, cuda_device, 64)
