@@ -12,7 +12,12 @@
 // The decay and input-scale gradients come from per-step scalars: with
 // cs_t = sum_{k<=t} a_k,
 //   dL/dcs_t = dy_t . y_t - x_t . dx_t  (+ <dh_final, h_final> at t = L-1)
-//            = C_t . (dy_t S_t) - sigma_t x_t . (G_t B_t)   (the D terms cancel exactly), and
+//            = C_t . (dy_t S_t) - sigma_t x_t . (G_t B_t)   (the D terms cancel exactly)
+//            = C_t . (dy_t S'_t) - sigma_t x_t . (G'_t B_t) with the states less the step's own
+//              term, S'_t = S_t - sigma_t x_t B_t^T and G'_t = G_t - dy_t C_t^T: their shares,
+//              sigma_t (dy_t.x_t)(C_t.B_t) in both, cancel exactly, so they are left out of both
+//              contractions rather than cancelled in rounding (large where a step's decay all
+//              but erases the state), and
 //   da_t = sum_{t' >= t} dL/dcs_t',   dsigma_t = x_t . (G_t B_t)
 //   ddelta_t = da_t A + dsigma_t dsigma/ddelta,  dA = sum da_t delta_t + dsigma_t dsigma/dA.
 //
@@ -62,7 +67,7 @@ struct SbKp {
     float *dx, *ddt, *dB, *dC, *dA_log, *dD, *ddt_bias, *dh0;
     float *Sseg, *Gseg, *dec;          // (batch, H, nseg, P, N) x2, (batch, H, nseg)
     float *dBh, *dCh;                  // (batch, L, H, N): each head's share
-    float *dyy, *dsig, *dyx;           // (batch, L, H)
+    float *dyy, *dsig, *dyx;           // (batch, L, H): C.(dy S'), x.(G' B), dy.x
     float *hfdot;                      // (batch, H)
     double *bnd;                       // (batch, H, nseg): exact dL/da at each segment's first step
     float *pA, *pD, *pT;               // (batch, nseg, H) partial sums
@@ -72,22 +77,50 @@ struct SbKp {
     // a_t = dt_t aval_t, sigma_t = trap_t dt_t + dt_{t+1} (1 - trap_{t+1}) (the
     // shifted state's input scale), and ssdb_scal leaves dL/da_t in dyy.  The
     // walks also apply the diagonal's correction (its scale is gamma_t, not
-    // sigma_t) and walk R2 writes dgamma_t = (q_t.k_t)(dy_t.x_t) to dgam.
+    // sigma_t).
     const float *aval, *trap;
-    float *dgam;                       // (batch, L, H)
+    float *dgam;                       // (batch, L, H): (B_t.C_t)(dy_t.x_t), walk R2's diagonal
 };
 
 __device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
 // per-chunk scalars in LDS
 struct Scal {
-    float cs[kQ];     // inclusive cumulative sum of a from the chunk start
+    float cs[kQ];     // inclusive cumulative sum of a from the chunk start (summed in
+    float csl[kQ];    // double, kept as cs + csl): a mask entry's exponent is the difference
+                      // of two of them, accurate also where strong decays make the sums large
     float sig[kQ];    // input scale
     float ecs[kQ];    // e^{cs_t}
     float eme[kQ];    // e^{cs_end - cs_t}
     float cd[kQ];     // trapezoidal form: gamma_t - sigma_t (times dy_t.x_t where asked for), else 0
     float csend;
 };
+
+// fp64 DPP move: both 32-bit halves moved with the same control (zero where the
+// source lane is out of the row or the row is masked off)
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xf, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xf, true);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// inclusive prefix sum over each 32-lane half, in fp64: row_shr 1, 2, 4, 8 within
+// 16-lane rows, then row_bcast:15 into rows 1 and 3
+__device__ __forceinline__ double scan32_f64(double v) {
+    v += dpp_f64<0x111>(v);
+    v += dpp_f64<0x112>(v);
+    v += dpp_f64<0x114>(v);
+    v += dpp_f64<0x118>(v);
+    v += dpp_f64<0x142, 0xa>(v);
+    return v;
+}
+__device__ __forceinline__ double readlane31_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 31);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 31);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 
 // One wave: lanes 0..31 hold steps t0..t0+31 (steps at or past te carry a = 0, sigma = 0).
 // with_dyx: the trapezoidal coefficient is multiplied by dy_t.x_t (written by walk R2).
@@ -114,16 +147,18 @@ __device__ __forceinline__ void chunk_scalars(Scal &sc, const SbKp &p, int64_t b
             sg = p.mode == 1 ? dl : (p.mode == 0 ? (a == 0.0f ? dl : dl * (expm1f(a) / a)) : 1.0f);
         }
     }
-    const float v = scan32(a);
-    const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    const double v = scan32_f64(a);
+    const double cend = readlane31_f64(v);
     if (lane < kQ) {
-        sc.cs[lane] = v;
+        const float hi = (float)v;
+        sc.cs[lane] = hi;
+        sc.csl[lane] = (float)(v - (double)hi);
         sc.sig[lane] = sg;
         sc.cd[lane] = cd;
-        sc.ecs[lane] = __expf(v);
-        sc.eme[lane] = __expf(cend - v);
+        sc.ecs[lane] = __expf((float)v);
+        sc.eme[lane] = __expf((float)(cend - v));
     }
-    if (lane == 0) sc.csend = cend;
+    if (lane == 0) sc.csend = (float)cend;
 }
 
 // Sum over the 16 lanes of each DPP row; the total lands in lane 15 of the row.
@@ -174,8 +209,10 @@ __device__ __forceinline__ int64_t seg_off(const SbKp &p, int64_t b, int64_t h, 
 // STATE: segments 0..nseg-2 from a zero state, writing their own final states
 // and decays.  Otherwise: every segment from its entering state, writing the
 // head's dC share, the per-step scalar C_t . dC_t, and <dh_final, h_final>.
+// At P = 64, N = 128 the register allocator lands a few VGPRs above 168 (2 waves per
+// SIMD) unless asked for 3 waves, which it then meets without spilling.
 template <int P, int N, bool STATE>
-__global__ void __launch_bounds__(64 * (N / 32))
+__global__ void __launch_bounds__(64 * (N / 32)) __attribute__((amdgpu_waves_per_eu(P <= 64 && N == 128 ? 3 : 1)))
 ssdb_walk_f(SbKp p) {
     constexpr int NW = N / 32, PT = P / 16, NTH = 64 * NW;
     __shared__ __attribute__((aligned(16))) float sX[kQ][P + 4];
@@ -183,6 +220,7 @@ ssdb_walk_f(SbKp p) {
     __shared__ __attribute__((aligned(16))) float sB[kQ][N + 4];
     __shared__ __attribute__((aligned(16))) float sM[STATE ? 1 : kQ][kQ + 4];
     __shared__ float sRed[NW][kQ];
+    __shared__ float sDg[STATE ? 1 : kQ];   // the own term's coefficient, sigma_t (dy_t.x_t)
     __shared__ Scal sc;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane >> 4, c16 = lane & 15;
@@ -233,7 +271,9 @@ ssdb_walk_f(SbKp p) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int t = 16 * ti + 4 * r + v;
-                    sM[t][s] = s <= t ? acc[v] * __expf(sc.cs[t] - sc.cs[s]) * sc.sig[s] : 0.0f;
+                    const float m = s <= t ? acc[v] * __expf((sc.cs[t] - sc.cs[s]) + (sc.csl[t] - sc.csl[s])) * sc.sig[s] : 0.0f;
+                    if (s == t) sDg[t] = p.trap ? m + sc.cd[t] : m;   // with the trapezoidal diagonal's share
+                    sM[t][s] = s == t ? 0.0f : m;     // the step's own term enters dC below
                 }
             }
             __syncthreads();
@@ -268,10 +308,11 @@ ssdb_walk_f(SbKp p) {
                         const int tl = 16 * ti + 4 * r + v;
                         const int64_t t = t0 + tl;
                         if (t < T1) {
-                            // the trapezoidal diagonal's share, dq_t += (gamma_t - sigma_t)(dy_t.x_t) k_t,
-                            // is not part of C_t.dC_t (the decay does not act on the diagonal)
-                            const float dc = p.trap ? fmaf(sc.cd[tl], sB[tl][n], acc[v]) : acc[v];
-                            p.dCh[((b * p.L + t) * p.H + h) * N + n] = dc;
+                            // acc is dy_t S'_t (the state less the step's own term), whose C_t dot
+                            // product is the step's scalar; dC_t adds the own term, sigma_t
+                            // (dy_t.x_t) B_t, and in the trapezoidal form the diagonal's share
+                            // (gamma_t - sigma_t)(dy_t.x_t) k_t
+                            p.dCh[((b * p.L + t) * p.H + h) * N + n] = fmaf(sDg[tl], sB[tl][n], acc[v]);
                             part[v] += bf(p.C[((b * p.L + t) * p.G + g) * N + n]) * acc[v];
                         }
                     }
@@ -420,7 +461,7 @@ ssdb_walk_r1(SbKp p) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int t = 16 * ti + 4 * r + v;
-                    sM[t][tp] = tp >= t ? acc[v] * __expf(sc.cs[tp] - sc.cs[t]) : 0.0f;
+                    sM[t][tp] = tp >= t ? acc[v] * __expf((sc.cs[tp] - sc.cs[t]) + (sc.csl[tp] - sc.csl[t])) : 0.0f;
                 }
             }
             __syncthreads();
@@ -517,6 +558,7 @@ ssdb_walk_r2(SbKp p) {
     __shared__ __attribute__((aligned(16))) float sY[kQ][P + 4];
     __shared__ __attribute__((aligned(16))) float sM[kQ][kQ + 4];
     __shared__ float sRed[NW][2][kQ];
+    __shared__ float sDg[kQ];   // the mask's diagonal, B_t.C_t
     __shared__ Scal sc;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane >> 4, c16 = lane & 15;
@@ -564,7 +606,9 @@ ssdb_walk_r2(SbKp p) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int t = 16 * ti + 4 * r + v;
-                sM[t][tp] = tp >= t ? acc[v] * __expf(sc.cs[tp] - sc.cs[t]) : 0.0f;
+                const float m = tp >= t ? acc[v] * __expf((sc.cs[tp] - sc.cs[t]) + (sc.csl[tp] - sc.csl[t])) : 0.0f;
+                if (tp == t) sDg[t] = m;
+                sM[t][tp] = tp == t ? 0.0f : m;   // the step's own term enters dx below
             }
         }
         __syncthreads();
@@ -589,7 +633,8 @@ ssdb_walk_r2(SbKp p) {
                 acc = mfma4(a4.z, sY[16 * tj + 4 * r + 2][pc], acc);
                 acc = mfma4(a4.w, sY[16 * tj + 4 * r + 3][pc], acc);
             }
-            // u = acc: dx = sigma u + D dy and the per-step sums over p
+            // acc = u'_t = G'_t B_t (the gradient state less the step's own term):
+            // dx = sigma (u' + (B_t.C_t) dy) + D dy, and the per-step sums over p
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int tl = 16 * ti + 4 * r + v;
@@ -600,7 +645,8 @@ ssdb_walk_r2(SbKp p) {
                     xv = bf(p.x[((b * p.L + t) * p.H + h) * P + pc]);
                     // trapezoidal diagonal: dx_t += (gamma_t - sigma_t)(q_t.k_t) dy_t, with
                     // q_t.k_t the diagonal of (B C^T) o E (its decay factor there is e^0)
-                    const float sk = p.trap ? fmaf(sc.cd[tl], sM[tl][tl], Dh) : Dh;
+                    const float dg = sDg[tl];
+                    const float sk = fmaf(sc.sig[tl], dg, p.trap ? fmaf(sc.cd[tl], dg, Dh) : Dh);
                     dxv = fmaf(sc.sig[tl], acc[v], sk * dyv);
                     p.dx[((b * p.L + t) * p.H + h) * P + pc] = dxv;
                 }
@@ -633,7 +679,7 @@ ssdb_walk_r2(SbKp p) {
             const int64_t o = (b * p.L + t0 + tid) * p.H + h;
             p.dsig[o] = s0;
             p.dyx[o] = s2;
-            if (p.trap) p.dgam[o] = sM[tid][tid] * s2;
+            p.dgam[o] = sDg[tid] * s2;
         }
     }
 }
@@ -794,7 +840,7 @@ __global__ void __launch_bounds__(kScalThreads) ssdb_scal(SbKp p) {
         else { dsd = 0.0f; dsa = 0.0f; }
         carry += dcs(t, sg);                         // da_t = sum_{t' >= t} dL/dcs_t'
         const float da = (float)carry;
-        const float ds = p.dsig[o];
+        const float ds = p.dsig[o] + p.dgam[o];          // x_t.(G_t B_t), the own term included
         const float ddl = fmaf(da, A, ds * dsd);
         aA = fmaf(da, dl, fmaf(ds, dsa, aA));
         const float g = ddl * (1.0f / (1.0f + __expf(-x)));
@@ -872,11 +918,11 @@ __global__ void __launch_bounds__(256) trapb_prev_kernel(SbKp p, const float *dh
     }
 }
 
-// The chain to the inputs, one thread per (b, t, h).  The SSD backward's dsigma_t
-// (in dsig) treats the diagonal as scaled by sigma_t; the input scale's true
-// gradient is dsigma_t - dgam_t (dgam_t = (q_t.k_t)(dy_t.x_t)), and the diagonal's
-// scale gamma_t gets dgam_t.  So with da_t = dL/da_t (in dyy),
-// dgamma_t = dsig_t and dc_t = dsig_{t-1} - dgam_{t-1} (dc_0 at t = 0):
+// The chain to the inputs, one thread per (b, t, h).  The walks leave the step's own
+// term out of dsig_t = x_t.(G'_t B_t), the gradient of the shifted state's input scale
+// sigma_t = gamma_t + c_{t+1}; dgam_t = (q_t.k_t)(dy_t.x_t) is the diagonal, scaled by
+// gamma_t alone.  So with da_t = dL/da_t (in dyy),
+// dgamma_t = dsig_t + dgam_t and dc_t = dsig_{t-1} (dc_0 at t = 0):
 //   ddt = da aval + dgamma trap + dc (1 - trap),  dtrap = (dgamma - dc) dt,  daval = da dt.
 __global__ void __launch_bounds__(256) trapb_chain_kernel(SbKp p, const float *dc0, float *ddt, float *daval,
                                                          float *dtrap) {
@@ -884,8 +930,8 @@ __global__ void __launch_bounds__(256) trapb_chain_kernel(SbKp p, const float *d
     if (o >= p.batch * p.L * p.H) return;
     const int64_t h = o % p.H, t = (o / p.H) % p.L, b = o / (p.H * p.L);
     const float da = p.dyy[o];
-    const float dg = p.dsig[o];
-    const float dc = t > 0 ? p.dsig[o - p.H] - p.dgam[o - p.H] : (dc0 ? dc0[b * p.H + h] : 0.0f);
+    const float dg = p.dsig[o] + p.dgam[o];
+    const float dc = t > 0 ? p.dsig[o - p.H] : (dc0 ? dc0[b * p.H + h] : 0.0f);
     const float dtv = p.dt[o], tr = p.trap[o];
     ddt[o] = fmaf(da, p.aval[o], fmaf(dg, tr, dc * (1.0f - tr)));
     dtrap[o] = (dg - dc) * dtv;
@@ -903,7 +949,7 @@ Plan plan(int64_t batch, int64_t L, int64_t H, int64_t N) {
 }
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
-struct WsLayout { size_t Sseg, Gseg, dec, bnd, dBh, dCh, dyy, dsig, dyx, hfdot, pA, pD, pT, total; };
+struct WsLayout { size_t Sseg, Gseg, dec, bnd, dBh, dCh, dyy, dsig, dyx, dgam, hfdot, pA, pD, pT, total; };
 // shares: each head's share of dB and dC is kept for the sum over a group's
 // heads; with one head per group the walks write dB and dC themselves
 WsLayout layout(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t nseg, bool shares) {
@@ -920,6 +966,7 @@ WsLayout layout(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64
     w.dyy = o;  o += al256((size_t)(batch * L * H) * 4);
     w.dsig = o; o += al256((size_t)(batch * L * H) * 4);
     w.dyx = o;  o += al256((size_t)(batch * L * H) * 4);
+    w.dgam = o; o += al256((size_t)(batch * L * H) * 4);
     w.hfdot = o; o += al256((size_t)(batch * H) * 4);
     w.pA = o;   o += al256((size_t)(batch * nseg * H) * 4);
     w.pD = o;   o += al256((size_t)(batch * nseg * H) * 4);
@@ -964,7 +1011,7 @@ size_t ssd_trap_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, in
     const Plan pl = plan(batch, L, nheads, d_state);
     const size_t st = al256((size_t)(batch * nheads * headdim * d_state) * 4);
     return layout(batch, L, nheads, headdim, d_state, pl.nseg, false).total + 2 * st +
-           al256((size_t)(batch * nheads) * 4) + al256((size_t)(batch * L * nheads) * 4);
+           al256((size_t)(batch * nheads) * 4);
 }
 
 size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t nheads, int64_t headdim, int64_t d_state,
@@ -999,6 +1046,7 @@ SbKp make_params(const SsdBwdArgs &a) {
     p.dyy = reinterpret_cast<float *>(ws + w.dyy);
     p.dsig = reinterpret_cast<float *>(ws + w.dsig);
     p.dyx = reinterpret_cast<float *>(ws + w.dyx);
+    p.dgam = reinterpret_cast<float *>(ws + w.dgam);
     p.hfdot = reinterpret_cast<float *>(ws + w.hfdot);
     p.bnd = reinterpret_cast<double *>(ws + w.bnd);
     p.pA = reinterpret_cast<float *>(ws + w.pA);
@@ -1029,7 +1077,6 @@ hipError_t launch_ssd_trap_bwd(const SsdTrapBwdArgs &t, hipStream_t stream, cons
     float *h0p = reinterpret_cast<float *>(ws + base);
     float *dh0p = reinterpret_cast<float *>(ws + base + st);
     float *dc0 = reinterpret_cast<float *>(ws + base + 2 * st);
-    float *dgam = reinterpret_cast<float *>(ws + base + 2 * st + al256((size_t)(t.batch * t.nheads) * 4));
     const float *h0 = t.h0;
     if (t.x_prev) {
         *kernel_name = "ssd_trap_h0_kernel";
@@ -1044,7 +1091,6 @@ hipError_t launch_ssd_trap_bwd(const SsdTrapBwdArgs &t, hipStream_t stream, cons
     SbKp p = make_params(a);
     p.aval = t.a;
     p.trap = t.trap;
-    p.dgam = dgam;
     *kernel_name = "ssdb_walk_f";
     launch_walks(p, stream);
     *kernel_name = "trapb_prev_kernel";

@@ -96,3 +96,19 @@ def test_seg_long_context_sampled(cuda_device, batch, L):
     report(f"s6 segmented b{batch} L{L} sampled ({len(units)} channels)", y=ey, h_final=eh)
     assert np.isfinite(y).all()
     assert ey <= TOL_F32 and eh <= TOL_F32
+
+
+def test_seg_extreme_dt(cuda_device):
+    """delta ~ 1e-11 next to delta ~ 25 across the segments: the carried decay products
+    underflow to zero within a segment, and the states cross segment boundaries intact."""
+    assert lib().ssm_s6_scan_fwd_workspace_size(1, 4096, 64, 16) > 0
+    inp = synth.s6_inputs(1, 4096, 64, 16, seed=(75,), h0=True)
+    dt = inp.arrays["dt"]
+    dt[:, ::3] = -25.0
+    dt[:, 1::7] = 25.0
+    y, hf = _run(inp, cuda_device, ZOH)
+    yo, ho = oracle.s6_fwd(**inp.arrays, flags=ZOH)
+    ey, eh = synth.max_rel_err(y, yo), synth.max_rel_err(hf, ho)
+    report("s6 segmented extreme dt", y=ey, h_final=eh)
+    assert np.isfinite(y).all() and np.isfinite(hf).all()
+    assert ey <= TOL_F32 and eh <= TOL_F32

@@ -86,3 +86,70 @@ def test_ssd_bwd_mamba2_workload_row(cuda_device):
     report("ssd_bwd mamba2 row 0", **e)
     bad = {k: v for k, v in e.items() if not v <= TOL_BWD}
     assert not bad, bad
+
+
+EPS32 = 2.0 ** -24
+
+
+def _suffix_scale(inp, dy, dhf, flags, ou):
+    """Per (head, step): the scale of the rounding that the decay gradient da_t carries.
+
+    da_t = dL/da_t is the sum over t' >= t of the per-step scalars dL/dcs_t' (plus the
+    final state's <dh_final, h_final> at the last step), each a contraction of the states
+    with C_t' and x_t'.  Summed in fp32 pieces, da_t is accurate to some units of rounding
+    of the absolute terms of that suffix, not of da_t itself: where a step's decay all but
+    erases the state, da_t is ~0 while the suffix holds terms of size 1e2 to 1e4.  The
+    absolute terms are read off the oracle's own per-head outputs: |C_t| . |dC_t| (the
+    dy_t S_t contraction) and |x_t| . |dx_t - D dy_t| (sigma_t x_t . G_t B_t).
+    """
+    ar = inp.arrays
+    H = ar["x"].shape[2]
+    _, hf = oracle.ssd_fwd(**ar, ngroups=1, flags=flags)
+    suf = []
+    for h in range(H):
+        mag = (np.abs(ar["C"][0, :, 0]).astype(np.float64) * np.abs(ou["dC"][h])).sum(1) + \
+              (np.abs(ar["x"][0, :, h]).astype(np.float64) *
+               np.abs(ou["dx"][h] - ar["D"][h] * dy[0, :, h])).sum(1)
+        suf.append(np.cumsum(mag[::-1])[::-1] + np.abs(hf[0, h] * dhf[0, h]).sum())
+    return np.stack(suf, 1)                                  # (L, H)
+
+
+@pytest.mark.parametrize("flags", [DT, ZOH])
+def test_ssd_bwd_extreme_dt(cuda_device, flags):
+    """delta ~ 1e-11 next to delta ~ 25 (softplus' of 1e-11 and 1, decays of e^{-25 |A|}),
+    over two segments.  dx, dB, dC, dD, ddt_bias and dh0 meet the usual bar.  ddt and
+    dA_log go through da_t, whose fp32 suffix sum is accurate to a rounding unit of its
+    absolute terms (see _suffix_scale): their bar adds EPS32 times that scale, carried
+    through ddt_t = sigmoid(dt_t + bias) (da_t A + ...) and dA_log = A sum_t delta_t da_t + ...
+    (one unit of rounding per absolute suffix, against the worst case of the contraction
+    length times that; the GPU stays within a tenth of it on these inputs)."""
+    inp = synth.ssd_inputs(1, 700, 2, 64, 64, 1, seed=(13,), h0=True, D="normal")
+    ar = inp.arrays
+    dt = ar["dt"]
+    dt[:, ::3] = -25.0
+    dt[:, 1::7] = 25.0
+    dy, dhf = _cot(1, 700, 2, 64, 64, (13,))
+    g = gpu_ssd_bwd(inp, dy, dhf, cuda_device, flags)
+    o = oracle.ssd_bwd(**ar, dy=dy, dh_final=dhf, ngroups=1, flags=flags)
+    e = {k: synth.max_rel_err(g[k], o[k]) for k in GRADS}
+    report(f"ssd_bwd extreme dt flags={flags}", **e)
+    for k in GRADS:
+        assert np.isfinite(g[k]).all(), k
+    bad = {k: v for k, v in e.items() if k not in ("ddt", "dA_log") and not v <= TOL_BWD}
+    assert not bad, bad
+    ou = oracle.ssd_bwd(**ar, dy=dy, dh_final=dhf, ngroups=1, flags=flags,
+                        units=np.array([[0, 0], [0, 1]], np.int64))
+    suf = _suffix_scale(inp, dy, dhf, flags, ou)
+    A = -np.exp(ar["A_log"].astype(np.float64))
+    z = dt[0].astype(np.float64) + ar["dt_bias"]
+    delta = np.logaddexp(0.0, z)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    rms = np.sqrt(np.mean(o["ddt"] ** 2))
+    bar = TOL_BWD * (np.abs(o["ddt"][0]) + 0.01 * rms) + EPS32 * sg * np.abs(A) * suf
+    err = np.abs(g["ddt"][0].astype(np.float64) - o["ddt"][0])
+    assert (err <= bar).all(), f"ddt: worst err/bar {np.max(err / bar):.3f}"
+    bar_a = TOL_BWD * np.abs(o["dA_log"]) + EPS32 * np.abs(A) * (delta * suf).sum(0)
+    err_a = np.abs(g["dA_log"].astype(np.float64) - o["dA_log"])
+    assert (err_a <= bar_a).all(), f"dA_log: err {err_a}, bar {bar_a}"
+    report(f"ssd_bwd extreme dt flags={flags} (err/bar)", ddt=float(np.max(err / bar)),
+           dA_log=float(np.max(err_a / bar_a)))
