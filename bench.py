@@ -61,12 +61,12 @@ TRAFFIC = {
         "bytes": 308664790
     },
     "ssd_mamba2": {
-        "src_sha1": "9c04e59c1aa97a758b2033036989e17cda798706",
-        "bytes": 502800612
+        "src_sha1": "10814692ac8d7cf6080cfb97e10712ceae79f81b",
+        "bytes": 502740369
     },
     "ssd_long": {
-        "src_sha1": "9c04e59c1aa97a758b2033036989e17cda798706",
-        "bytes": 3664825240
+        "src_sha1": "10814692ac8d7cf6080cfb97e10712ceae79f81b",
+        "bytes": 3609848462
     },
     "cssd_mamba3": {
         "src_sha1": "d6c57f3db1e631ca1bd045b8cad57a67034d2545",

@@ -151,14 +151,15 @@ __device__ __forceinline__ void chunk_scalars(Scal &sc, float dtv, bool valid, f
 constexpr int x_pitch(int P) { return P == 32 ? 48 : P == 64 ? 72 : 152; }
 
 // LDS and register staging of one chunk of x, B (and C), dt for a work group
-// of NW waves holding head (b, h).  Loads are unconditional so they stay in
+// of NW waves per head holding HPW consecutive heads h.. of one group (B and C
+// staged once for them; x and dt per head, each by that head's threads).  Loads are unconditional so they stay in
 // flight across a chunk.  Addresses are a uniform base (the chunk's first row)
 // plus a 32-bit per-thread offset; a chunk that crosses L clamps its step
 // index into the tensors (rows past L never contribute: their sigma and w are
 // 0 and their outputs are not stored).
-template <int NMAX, int NW, bool WITH_C, int NS = 1, bool TRAP = false, bool ROWS8 = false>
+template <int NMAX, int NW, bool WITH_C, int NS = 1, bool TRAP = false, bool ROWS8 = false, int HPW = 1>
 struct Stager {
-    static constexpr int NTHR = 64 * NW;
+    static constexpr int NTHR = 64 * NW * HPW;
     static constexpr int P = 16 * NW;
     // B/C and x row pitches (bf16).  ROWS8: the tiles are read only by
     // transposed reads in which 32 lanes take 8 consecutive rows, 8 dwords each
@@ -171,7 +172,7 @@ struct Stager {
     static constexpr int SB_STEP = NTHR / LDN;          // steps between pieces i, i+1
     static constexpr int XPR = P / 8;                   // 16-byte pieces per x row
     static_assert(PER_T >= 1 && kT * LDN % NTHR == 0 && NTHR % LDN == 0, "B/C pieces must divide evenly");
-    static_assert(kT * XPR == NTHR, "one x piece per thread");
+    static_assert(kT * XPR == 64 * NW, "one x piece per thread of each head");
 
     // NS register stages: a chunk is loaded NS chunks before it is staged to LDS
     u32x4 rB[NS][PER_T], rC[NS][PER_T], rX[NS];
@@ -180,7 +181,7 @@ struct Stager {
     const uint16_t *Bb, *Cb, *Xb;   // step 0 of this (batch, group) / (batch, head)
     const float *Db, *Ab, *Tb;
     uint32_t colB;                  // this thread's B/C column (clamped into the state)
-    int sB, nB, sX, cX, sD;
+    int sB, nB, sX, cX, sD, xo;     // xo: this thread's head's x tile in LDS
     int64_t rowBC, rowX, H, L;
 
     __device__ __forceinline__ void init(const SsdKp &p, int64_t b, int64_t h, int64_t g, int N, int tid) {
@@ -188,18 +189,20 @@ struct Stager {
         rowX = p.H * p.P;
         H = p.H;
         L = p.L;
+        const int tx = tid % (64 * NW), xh = tid / (64 * NW);
         sB = tid / LDN;
         nB = (tid % LDN) * 8;
-        sX = tid / XPR;
-        cX = (tid % XPR) * 8;
+        sX = tx / XPR;
+        cX = (tx % XPR) * 8;
         sD = tid & 31;
+        xo = xh * kT * XP;
         colB = (uint32_t)min(nB, N - 8);
         Bb = p.B + (b * p.L * p.G + g) * p.N;
         Cb = p.C + (b * p.L * p.G + g) * p.N;
-        Xb = p.x + (b * p.L * p.H + h) * p.P;
-        Db = p.dt + b * p.L * p.H + h;
-        Ab = p.aval ? p.aval + b * p.L * p.H + h : nullptr;
-        Tb = p.trap ? p.trap + b * p.L * p.H + h : nullptr;
+        Xb = p.x + (b * p.L * p.H + h + xh) * p.P;
+        Db = p.dt + b * p.L * p.H + h + xh;
+        Ab = p.aval ? p.aval + b * p.L * p.H + h + xh : nullptr;
+        Tb = p.trap ? p.trap + b * p.L * p.H + h + xh : nullptr;
     }
     // a, trap of step t0 + i and dt, trap of step t0 + i + 1 (clamped into the
     // sequence; nvalid marks whether that next step exists)
@@ -248,7 +251,7 @@ struct Stager {
             *reinterpret_cast<u32x4 *>(&Bs[o]) = rB[S][i];
             if constexpr (WITH_C) *reinterpret_cast<u32x4 *>(&Cs[o]) = rC[S][i];
         }
-        *reinterpret_cast<u32x4 *>(&Xs[sX * XP + cX]) = rX[S];
+        *reinterpret_cast<u32x4 *>(&Xs[xo + sX * XP + cX]) = rX[S];
     }
 };
 
@@ -361,39 +364,43 @@ __device__ __forceinline__ void unroll_stages(F &&f) {
     }
 }
 
-template <int NMAX, bool EXACT, int NW, bool TRAP>
-__global__ void __launch_bounds__(64 * NW)
+// HPW heads of one group per work group (NW waves each): B is staged once for
+// them, x and the weights per head.
+template <int NMAX, bool EXACT, int NW, bool TRAP, int HPW>
+__global__ void __launch_bounds__(64 * NW * HPW)
 ssd_state_kernel(SsdKp p) {
     constexpr int NS = 2;
-    using St = Stager<NMAX, NW, false, NS, TRAP, true>;
+    using St = Stager<NMAX, NW, false, NS, TRAP, true, HPW>;
     constexpr int NT = NMAX / 16;
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kT * St::BCP];
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kT * St::XP];
-    __shared__ __attribute__((aligned(16))) float wsc[2][kT];
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][HPW * kT * St::XP];
+    __shared__ __attribute__((aligned(16))) float wsc[2][HPW][kT];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int hl = wid / NW, wh = wid % NW;                      // head in the group, wave in the head
     const int c16 = lane & 15, q = lane >> 4;
     const int64_t nseg1 = p.nseg - 1;
-    const Work wk(xcd_swizzle(blockIdx.x, p.batch * nseg1 * p.H), p.H, nseg1);
-    const int64_t g = wk.h * p.G / p.H;
-    const int p0 = wid * 16;
+    const Work wk(xcd_swizzle(blockIdx.x, p.batch * nseg1 * (p.H / HPW)), p.H / HPW, nseg1);
+    const int64_t h0 = wk.h * HPW, h = h0 + hl;
+    const int64_t g = h0 * p.G / p.H;
+    const int p0 = wh * 16;
     const int N = EXACT ? NMAX : (int)p.N;
-    const float A = p.A_log ? -expf(p.A_log[wk.h]) : 0.0f;
-    const float bias = p.dt_bias ? p.dt_bias[wk.h] : 0.0f;
+    const float A = p.A_log ? -expf(p.A_log[h]) : 0.0f;
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
 
     f32x4 S[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) S[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     St st;
-    st.init(p, wk.b, wk.h, g, N, tid);
+    st.init(p, wk.b, h0, g, N, tid);
     st.sD = kT - 1 - (tid & 31);                           // dt lanes in reverse step order
     const int64_t nch = p.Ls / kT;
     const int64_t tlast = wk.k * p.Ls + (nch - 1) * kT;   // first step of the last chunk
-    // weights of one chunk from its dt (wave 0; lane i holds step 31 - i, so
-    // the lane-order prefix sum is the step-order suffix sum); R is the sum of
-    // a over the later steps of the segment, kept by wave 0
+    // weights of one chunk from its dt (each head's wave 0; lane i holds step
+    // 31 - i, so the lane-order prefix sum is the step-order suffix sum); R is
+    // the sum of a over the later steps of the segment, kept by that wave
     float R = 0.0f;
     auto weights = [&](float *w, float dtv, const TrapIn &ti) __attribute__((always_inline)) {
         float a, sg;
@@ -417,7 +424,7 @@ ssd_state_kernel(SsdKp p) {
         if (S_ < nch) st.template load<S_>(tlast - S_ * kT);
     });
     st.template store<0>(Bs[0], nullptr, Xs[0]);
-    if (wid == 0) weights(wsc[0], st.rdt[0], st.rtp[0]);
+    if (wh == 0) weights(wsc[0][hl], st.rdt[0], st.rtp[0]);
     if (NS < nch) st.template load<0>(tlast - NS * kT);
     __syncthreads();
 
@@ -429,26 +436,26 @@ ssd_state_kernel(SsdKp p) {
             if (c >= nch) return;
             const int buf = (int)(c & 1);
             u32x4 Whf, Wlf;
-            weighted_x_regs<St::XP>(Xs[buf], p0, wsc[buf], lane, Whf, Wlf);
+            weighted_x_regs<St::XP>(Xs[buf] + hl * kT * St::XP, p0, wsc[buf][hl], lane, Whf, Wlf);
             state_update_regs<NT, St::BCP>(S, Bs[buf], Whf, Wlf, 1.0f, N, lane);
             if (c + 1 < nch) {
                 constexpr int SN = (S_ + 1) % NS;
                 st.template store<SN>(Bs[buf ^ 1], nullptr, Xs[buf ^ 1]);
-                if (wid == 0) weights(wsc[buf ^ 1], st.rdt[SN], st.rtp[SN]);
+                if (wh == 0) weights(wsc[buf ^ 1][hl], st.rdt[SN], st.rtp[TRAP ? SN : 0]);
                 if (c + 1 + NS < nch) st.template load<SN>(tlast - (c + 1 + NS) * kT);
             }
             __syncthreads();
         });
     }
 
-    const int64_t slot = (wk.b * p.H + wk.h) * p.nseg + wk.k;
+    const int64_t slot = (wk.b * p.H + h) * p.nseg + wk.k;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         if (nt * 16 >= N) break;
         float *dst = p.ws_state + (slot * p.P + p0 + c16) * p.N + nt * 16 + q * 4;
         *reinterpret_cast<float4 *>(dst) = make_float4(S[nt][0], S[nt][1], S[nt][2], S[nt][3]);
     }
-    if (tid == 0) p.ws_decay[slot] = __expf(R);
+    if (wh == 0 && lane == 0) p.ws_decay[slot] = __expf(R);
 }
 
 // ---- D3 across segments: the state entering each segment, in place of the
@@ -730,8 +737,20 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 template <int NMAX, bool EXACT, int NW, bool TRAP>
 void launch_all(const SsdKp &p, hipStream_t stream) {
     if (p.nseg > 1) {
-        const int64_t n1 = p.batch * (p.nseg - 1) * p.H;
-        hipLaunchKernelGGL((ssd_state_kernel<NMAX, EXACT, NW, TRAP>), dim3((unsigned)n1), dim3(64 * NW), 0, stream, p);
+        // two heads per work group where a group's head count is even, B's
+        // pieces divide over the doubled thread count and the pairs fill at
+        // least one round of the chip (two per CU): below that, half as many
+        // work groups of twice the size load the CUs less evenly
+        constexpr bool PAIR_OK = !TRAP && NW <= 4 && (kT * (NMAX / 8)) % (128 * NW) == 0;
+        if (PAIR_OK && (p.H / p.G) % 2 == 0 && p.batch * (p.nseg - 1) * (p.H / 2) >= 2 * kCUs) {
+            const int64_t n1 = p.batch * (p.nseg - 1) * (p.H / 2);
+            hipLaunchKernelGGL((ssd_state_kernel<NMAX, EXACT, NW, TRAP, PAIR_OK ? 2 : 1>), dim3((unsigned)n1),
+                               dim3(128 * NW), 0, stream, p);
+        } else {
+            const int64_t n1 = p.batch * (p.nseg - 1) * p.H;
+            hipLaunchKernelGGL((ssd_state_kernel<NMAX, EXACT, NW, TRAP, 1>), dim3((unsigned)n1), dim3(64 * NW), 0,
+                               stream, p);
+        }
         const int64_t nt = p.batch * p.H * p.P * p.N / 4;
         hipLaunchKernelGGL(ssd_pass_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream, p);
     }

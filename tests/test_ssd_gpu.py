@@ -38,6 +38,8 @@ CASES = [  # batch, L, H, P, N, G, Q, flags, h0
     (1, 777, 3, 128, 128, 3, 128, DT, True),
     (1, 1100, 2, 64, 96, 2, 64, ONE, False),
     (1, 1100, 2, 64, 256, 1, 256, DT, True),      # the largest state size, with segments
+    (1, 900, 4, 32, 64, 2, 64, DT, True),         # segment states of head pairs, 2 waves per head
+    (1, 700, 4, 64, 96, 2, 128, ZOH, True),       # head pairs with a state narrower than its tile
 ]
 
 
@@ -86,6 +88,27 @@ def test_ssd_workloads_sampled(cuda_device, name, per_group):
     ey, eh = synth.max_rel_err(yg, yo), synth.max_rel_err(hg, ho)
     report(f"{name} sampled ({len(units)} heads)", y=ey, h_final=eh, margin=TOL_BF16 / max(ey, eh))
     assert np.isfinite(y).all()
+    assert ey <= TOL_BF16 and eh <= TOL_BF16
+
+
+@pytest.mark.parametrize("shape", [(2, 4096, 80, 64, 128, 8, DT), (4, 4096, 64, 32, 64, 4, ZOH)],
+                         ids=["b2L4096H80P64N128G8", "b4L4096H64P32N64G4"])
+def test_ssd_head_pairs_sampled(cuda_device, shape):
+    """Shapes whose plan runs several rounds of segments, where the segment states are
+    formed for two heads of a group per work group: two heads of every group and batch
+    row (an even and an odd one, so both halves of a pair) over the whole sequence."""
+    batch, L, H, P, N, G, flags = shape
+    inp = synth.ssd_inputs(batch, L, H, P, N, G, seed=(31, L), h0=True, D="normal")
+    y, hf = gpu_ssd(inp, cuda_device, flags, 256)
+    hpg = H // G
+    rng = np.random.default_rng(3)
+    units = np.array([(b, g * hpg + int(2 * rng.integers(hpg // 2)) + o)
+                      for b in range(batch) for g in range(G) for o in (0, 1)], dtype=np.int64)
+    yo, ho = oracle.ssd_fwd(**inp.arrays, ngroups=G, flags=flags, units=units)
+    ey = synth.max_rel_err(np.stack([y[b, :, h, :] for b, h in units]), yo)
+    eh = synth.max_rel_err(np.stack([hf[b, h] for b, h in units]), ho)
+    report(f"ssd head pairs {shape} ({len(units)} heads)", y=ey, h_final=eh)
+    assert np.isfinite(y).all() and np.isfinite(hf).all()
     assert ey <= TOL_BF16 and eh <= TOL_BF16
 
 
