@@ -61,12 +61,12 @@ TRAFFIC = {
         "bytes": 308664790
     },
     "ssd_mamba2": {
-        "src_sha1": "10814692ac8d7cf6080cfb97e10712ceae79f81b",
-        "bytes": 502740369
+        "src_sha1": "a90070c832174eaea01da91dee5b407abb7b1e30",
+        "bytes": 501871827
     },
     "ssd_long": {
-        "src_sha1": "10814692ac8d7cf6080cfb97e10712ceae79f81b",
-        "bytes": 3609848462
+        "src_sha1": "a90070c832174eaea01da91dee5b407abb7b1e30",
+        "bytes": 3604600222
     },
     "cssd_mamba3": {
         "src_sha1": "d6c57f3db1e631ca1bd045b8cad57a67034d2545",

@@ -70,6 +70,15 @@ __device__ __forceinline__ uint2 split_bf16(float a, float b) {
     return make_uint2(hi, pack_bf16(a - lo_f(hi), b - hi_f(hi)));
 }
 
+// A lane's 32-bit byte offset, re-read where it is used: the empty asm keeps the
+// compiler from hoisting its zero extension out of a loop, so that base (uniform)
+// + offset stays the global instructions' SGPR-base form instead of a 64-bit add
+// per access
+__device__ __forceinline__ uint32_t lane_off(uint32_t o) {
+    asm volatile("" : "+v"(o));
+    return o;
+}
+
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
 // names a row of 4 consecutive 16-bit elements and receives element (i % 4) of
 // rows i/4, i/4 + 4, i/4 + 8, i/4 + 12.  Pointing row i at (step sb + i/4,
@@ -182,6 +191,7 @@ struct Stager {
     const float *Db, *Ab, *Tb;
     uint32_t colB;                  // this thread's B/C column (clamped into the state)
     int sB, nB, sX, cX, sD, xo;     // xo: this thread's head's x tile in LDS
+    uint32_t oB, oX;                // byte offsets of this thread's B/C and x pieces in a chunk
     int64_t rowBC, rowX, H, L;
 
     __device__ __forceinline__ void init(const SsdKp &p, int64_t b, int64_t h, int64_t g, int N, int tid) {
@@ -189,7 +199,10 @@ struct Stager {
         rowX = p.H * p.P;
         H = p.H;
         L = p.L;
-        const int tx = tid % (64 * NW), xh = tid / (64 * NW);
+        // the thread's head in the group: uniform over a wave (an SGPR), so the
+        // head's base pointers stay scalar
+        const int xh = HPW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / (64 * NW));
+        const int tx = tid - xh * 64 * NW;
         sB = tid / LDN;
         nB = (tid % LDN) * 8;
         sX = tx / XPR;
@@ -197,6 +210,8 @@ struct Stager {
         sD = tid & 31;
         xo = xh * kT * XP;
         colB = (uint32_t)min(nB, N - 8);
+        oB = ((uint32_t)sB * (uint32_t)rowBC + colB) * 2u;
+        oX = ((uint32_t)sX * (uint32_t)rowX + (uint32_t)cX) * 2u;
         Bb = p.B + (b * p.L * p.G + g) * p.N;
         Cb = p.C + (b * p.L * p.G + g) * p.N;
         Xb = p.x + (b * p.L * p.H + h + xh) * p.P;
@@ -221,14 +236,18 @@ struct Stager {
         const uint16_t *Bu = Bb + t0 * rowBC, *Cu = Cb + t0 * rowBC, *Xu = Xb + t0 * rowX;
         const float *Du = Db + t0 * H;
         if (t0 + kT <= L) {
+            // uniform row base + the lane's 32-bit byte offset (SGPR-base loads)
 #pragma unroll
             for (int i = 0; i < PER_T; ++i) {
-                const uint32_t o = (uint32_t)(sB * rowBC) + colB;
-                rB[S][i] = *reinterpret_cast<const u32x4 *>(Bu + SB_STEP * i * rowBC + o);
-                if constexpr (WITH_C) rC[S][i] = *reinterpret_cast<const u32x4 *>(Cu + SB_STEP * i * rowBC + o);
+                rB[S][i] = *reinterpret_cast<const u32x4 *>(
+                    reinterpret_cast<const char *>(Bu + SB_STEP * i * rowBC) + lane_off(oB));
+                if constexpr (WITH_C)
+                    rC[S][i] = *reinterpret_cast<const u32x4 *>(
+                        reinterpret_cast<const char *>(Cu + SB_STEP * i * rowBC) + lane_off(oB));
             }
-            rX[S] = *reinterpret_cast<const u32x4 *>(Xu + (uint32_t)(sX * rowX + cX));
-            rdt[S] = Du[(uint32_t)(sD * H)];
+            rX[S] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(Xu) + lane_off(oX));
+            rdt[S] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(Du) +
+                                                      lane_off((uint32_t)sD * (uint32_t)H * 4u));
             if constexpr (TRAP) load_trap<S>(t0, sD);
         } else {
             const int last = (int)(L - 1 - t0);   // last valid step of the chunk
@@ -660,7 +679,7 @@ ssd_scan_kernel(SsdKp p) {
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + i) * rowX) + ylane) =
+                    *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + i) * rowX) + lane_off(ylane)) =
                         yv[tt][i];
         } else {
 #pragma unroll
@@ -668,7 +687,7 @@ ssd_scan_kernel(SsdKp p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (t0 + tt * 16 + q * 4 + i < te)
-                        *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + i) * rowX) + ylane) =
+                        *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + i) * rowX) + lane_off(ylane)) =
                             yv[tt][i];
         }
 
