@@ -45,6 +45,7 @@
 #include "device_common.hpp"
 #include "launchers.hpp"
 #include <algorithm>
+#include <type_traits>
 
 namespace ssm {
 namespace {
@@ -172,33 +173,58 @@ __device__ __forceinline__ float row_total16(float v) {
 
 // stage rows t0..t0+31 of a (batch, L, R, COLS) tensor slice (row index rr) into LDS as fp32;
 // rows at or past te are zero.  COLS is a multiple of 4.
+// A lane's 32-bit byte offset, re-read where it is used: the empty asm keeps its
+// zero extension next to the access, so that uniform base + offset is the global
+// instructions' SGPR-base form rather than a 64-bit VALU add per access
+__device__ __forceinline__ uint32_t lane_off(uint32_t o) {
+    asm volatile("" : "+v"(o));
+    return o;
+}
+
+// Stage kQ steps (t0 .. t0+kQ-1, rows past te zero) of one (b, rr) slice of a
+// (batch, L, R, COLS) tensor into an fp32 LDS tile: the chunk's first row is a
+// uniform base, each lane adds a 32-bit byte offset; bf16 in 16-byte pieces
 template <int COLS, int PITCH>
 __device__ __forceinline__ void stage_bf16(float (*dst)[PITCH], const uint16_t *src, int64_t b, int64_t L,
                                            int64_t R, int64_t rr, int64_t t0, int64_t te, int tid, int nthr) {
-    constexpr int Q4 = COLS / 4;
-    for (int i = tid; i < kQ * Q4; i += nthr) {
-        const int tr = i / Q4, c4 = (i % Q4) * 4;
-        const int64_t t = t0 + tr;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t < te) {
-            const uint2 w = *reinterpret_cast<const uint2 *>(src + ((b * L + t) * R + rr) * COLS + c4);
-            v = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
-        }
-        *reinterpret_cast<float4 *>(&dst[tr][c4]) = v;
+    constexpr int Q8 = COLS / 8;
+    const char *row0 = reinterpret_cast<const char *>(src + ((b * L + t0) * R + rr) * COLS);
+    const uint32_t rs = (uint32_t)(R * COLS) * 2u;                    // row stride in bytes
+    const int nv = (int)min<int64_t>(kQ, te - t0);                     // rows in the sequence
+    for (int i = tid; i < kQ * Q8; i += nthr) {
+        const int tr = i / Q8, c8 = (i % Q8) * 8;
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if (tr < nv) w = *reinterpret_cast<const uint4 *>(row0 + lane_off((uint32_t)tr * rs + (uint32_t)c8 * 2u));
+        *reinterpret_cast<float4 *>(&dst[tr][c8]) =
+            make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+        *reinterpret_cast<float4 *>(&dst[tr][c8 + 4]) =
+            make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xffff0000u),
+                        __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xffff0000u));
     }
 }
 template <int COLS, int PITCH>
 __device__ __forceinline__ void stage_f32(float (*dst)[PITCH], const float *src, int64_t b, int64_t L,
                                           int64_t R, int64_t rr, int64_t t0, int64_t te, int tid, int nthr) {
     constexpr int Q4 = COLS / 4;
+    const char *row0 = reinterpret_cast<const char *>(src + ((b * L + t0) * R + rr) * COLS);
+    const uint32_t rs = (uint32_t)(R * COLS) * 4u;
+    const int nv = (int)min<int64_t>(kQ, te - t0);
     for (int i = tid; i < kQ * Q4; i += nthr) {
         const int tr = i / Q4, c4 = (i % Q4) * 4;
-        const int64_t t = t0 + tr;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t < te) v = *reinterpret_cast<const float4 *>(src + ((b * L + t) * R + rr) * COLS + c4);
+        if (tr < nv) v = *reinterpret_cast<const float4 *>(row0 + lane_off((uint32_t)tr * rs + (uint32_t)c4 * 4u));
         *reinterpret_cast<float4 *>(&dst[tr][c4]) = v;
     }
+}
+
+// Element (row 16 ti + 4 r + v, column) of a chunk tile in global memory: the
+// uniform chunk base plus rows (16 ti + v) whole rows (SGPRs), and the lane's
+// rows 4 r and its column as a 32-bit byte offset
+template <typename T>
+__device__ __forceinline__ T &chunk_elem(T *base0, uint32_t row_bytes, int urows, uint32_t lane_bytes) {
+    using B = std::conditional_t<std::is_const_v<T>, const char, char>;
+    return *reinterpret_cast<T *>(reinterpret_cast<B *>(base0) + (uint64_t)urows * row_bytes + lane_off(lane_bytes));
 }
 
 __device__ __forceinline__ int64_t seg_off(const SbKp &p, int64_t b, int64_t h, int64_t k) {
@@ -209,10 +235,8 @@ __device__ __forceinline__ int64_t seg_off(const SbKp &p, int64_t b, int64_t h, 
 // STATE: segments 0..nseg-2 from a zero state, writing their own final states
 // and decays.  Otherwise: every segment from its entering state, writing the
 // head's dC share, the per-step scalar C_t . dC_t, and <dh_final, h_final>.
-// At P = 64, N = 128 the register allocator lands a few VGPRs above 168 (2 waves per
-// SIMD) unless asked for 3 waves, which it then meets without spilling.
 template <int P, int N, bool STATE>
-__global__ void __launch_bounds__(64 * (N / 32)) __attribute__((amdgpu_waves_per_eu(P <= 64 && N == 128 ? 3 : 1)))
+__global__ void __launch_bounds__(64 * (N / 32))
 ssdb_walk_f(SbKp p) {
     constexpr int NW = N / 32, PT = P / 16, NTH = 64 * NW;
     __shared__ __attribute__((aligned(16))) float sX[kQ][P + 4];
@@ -303,6 +327,9 @@ ssdb_walk_f(SbKp p) {
                         acc = mfma4(a4.z, sB[16 * si + 4 * r + 2][n], acc);
                         acc = mfma4(a4.w, sB[16 * si + 4 * r + 3][n], acc);
                     }
+                    float *dC0 = p.dCh + ((b * p.L + t0) * p.H + h) * N;
+                    const uint16_t *C0 = p.C + ((b * p.L + t0) * p.G + g) * N;
+                    const uint32_t rsD = (uint32_t)(p.H * N) * 4u, rsC = (uint32_t)(p.G * N) * 2u;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int tl = 16 * ti + 4 * r + v;
@@ -312,8 +339,10 @@ ssdb_walk_f(SbKp p) {
                             // product is the step's scalar; dC_t adds the own term, sigma_t
                             // (dy_t.x_t) B_t, and in the trapezoidal form the diagonal's share
                             // (gamma_t - sigma_t)(dy_t.x_t) k_t
-                            p.dCh[((b * p.L + t) * p.H + h) * N + n] = fmaf(sDg[tl], sB[tl][n], acc[v]);
-                            part[v] += bf(p.C[((b * p.L + t) * p.G + g) * N + n]) * acc[v];
+                            chunk_elem(dC0, rsD, 16 * ti + v, (uint32_t)(4 * r) * rsD + (uint32_t)n * 4u) =
+                                fmaf(sDg[tl], sB[tl][n], acc[v]);
+                            part[v] += bf(chunk_elem(C0, rsC, 16 * ti + v, (uint32_t)(4 * r) * rsC + (uint32_t)n * 2u)) *
+                                       acc[v];
                         }
                     }
                 }
@@ -490,6 +519,8 @@ ssdb_walk_r1(SbKp p) {
                         acc = mfma4(a4.z, sC[16 * tj + 4 * r + 2][n], acc);
                         acc = mfma4(a4.w, sC[16 * tj + 4 * r + 3][n], acc);
                     }
+                    float *dB0 = p.dBh + ((b * p.L + t0) * p.H + h) * N;
+                    const uint32_t rsD = (uint32_t)(p.H * N) * 4u;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int tl = 16 * ti + 4 * r + v;
@@ -497,7 +528,8 @@ ssdb_walk_r1(SbKp p) {
                         if (t < T1) {
                             // plus the trapezoidal diagonal's dk_t += (gamma_t - sigma_t)(dy_t.x_t) q_t
                             const float db = acc[v] * sc.sig[tl];
-                            p.dBh[((b * p.L + t) * p.H + h) * N + n] = p.trap ? fmaf(sc.cd[tl], sC[tl][n], db) : db;
+                            chunk_elem(dB0, rsD, 16 * ti + v, (uint32_t)(4 * r) * rsD + (uint32_t)n * 4u) =
+                                p.trap ? fmaf(sc.cd[tl], sC[tl][n], db) : db;
                         }
                     }
                 }
@@ -635,6 +667,9 @@ ssdb_walk_r2(SbKp p) {
             }
             // acc = u'_t = G'_t B_t (the gradient state less the step's own term):
             // dx = sigma (u' + (B_t.C_t) dy) + D dy, and the per-step sums over p
+            const uint16_t *X0 = p.x + ((b * p.L + t0) * p.H + h) * P;
+            float *dX0 = p.dx + ((b * p.L + t0) * p.H + h) * P;
+            const uint32_t rsX = (uint32_t)(p.H * P) * 2u, rsDX = (uint32_t)(p.H * P) * 4u;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int tl = 16 * ti + 4 * r + v;
@@ -642,13 +677,13 @@ ssdb_walk_r2(SbKp p) {
                 const float dyv = sY[tl][pc];
                 float xv = 0.0f, dxv = 0.0f;
                 if (t < T1) {
-                    xv = bf(p.x[((b * p.L + t) * p.H + h) * P + pc]);
+                    xv = bf(chunk_elem(X0, rsX, 16 * ti + v, (uint32_t)(4 * r) * rsX + (uint32_t)pc * 2u));
                     // trapezoidal diagonal: dx_t += (gamma_t - sigma_t)(q_t.k_t) dy_t, with
                     // q_t.k_t the diagonal of (B C^T) o E (its decay factor there is e^0)
                     const float dg = sDg[tl];
                     const float sk = fmaf(sc.sig[tl], dg, p.trap ? fmaf(sc.cd[tl], dg, Dh) : Dh);
                     dxv = fmaf(sc.sig[tl], acc[v], sk * dyv);
-                    p.dx[((b * p.L + t) * p.H + h) * P + pc] = dxv;
+                    chunk_elem(dX0, rsDX, 16 * ti + v, (uint32_t)(4 * r) * rsDX + (uint32_t)pc * 4u) = dxv;
                 }
                 const float s0 = row_total16(xv * acc[v]);
                 const float s2 = row_total16(dyv * xv);
