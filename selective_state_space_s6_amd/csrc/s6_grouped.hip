@@ -32,6 +32,19 @@ constexpr int kGT = 16;            // steps per tile == lanes per DPP row
 constexpr int kGThreads = 256;     // 16 channels per work group
 constexpr int kGChan = kGThreads / kGT;
 
+// A lane's 32-bit byte offset, re-read where it is used: the empty asm keeps its
+// zero extension next to the access, so that uniform base + offset is the global
+// instructions' SGPR-base form rather than a 64-bit VALU add per access
+__device__ __forceinline__ uint32_t g_lane_off(uint32_t o) {
+    asm volatile("" : "+v"(o));
+    return o;
+}
+template <typename T>
+__device__ __forceinline__ T *g_at(T *base, uint32_t byte_off) {
+    using Ch = std::conditional_t<std::is_const_v<T>, const char, char>;
+    return reinterpret_cast<T *>(reinterpret_cast<Ch *>(base) + g_lane_off(byte_off));
+}
+
 template <int I, int N, typename F>
 __device__ __forceinline__ void g_static_for(F &&f) {
     if constexpr (I < N) {
@@ -265,11 +278,7 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
     const uint32_t o_dbc = (uint32_t)(((int64_t)c * p.N + k) * 4);                 // within a step's dB, dC rows of the group's channels
     const uint32_t o_ch = (uint32_t)(dd * 4);                                      // within a step's row of d_inner (fp32)
     const uint32_t o_chi = (uint32_t)(dd * (int64_t)sizeof(TIN));                  // the same for u
-    auto at = [](auto *base, uint32_t byte_off) __attribute__((always_inline)) {
-        using T = std::remove_pointer_t<decltype(base)>;
-        using Ch = std::conditional_t<std::is_const_v<T>, const char, char>;
-        return reinterpret_cast<decltype(base)>(reinterpret_cast<Ch *>(base) + byte_off);
-    };
+    auto at = [](auto *base, uint32_t byte_off) __attribute__((always_inline)) { return g_at(base, byte_off); };
     const TIN *Bb = static_cast<const TIN *>(p.B) + b * L * rowBC;
     const TIN *Cb = static_cast<const TIN *>(p.C) + b * L * rowBC;
     const TIN *Ub = static_cast<const TIN *>(p.u) + b * L * p.Dm;
