@@ -218,6 +218,22 @@ __device__ __forceinline__ void stage_f32(float (*dst)[PITCH], const float *src,
     }
 }
 
+// The same chunk rows of a bf16 tensor kept as bf16 in LDS (16-byte pieces)
+template <int COLS, int PITCH>
+__device__ __forceinline__ void stage_bf16_raw(uint16_t (*dst)[PITCH], const uint16_t *src, int64_t b, int64_t L,
+                                               int64_t R, int64_t rr, int64_t t0, int64_t te, int tid, int nthr) {
+    constexpr int Q8 = COLS / 8;
+    const char *row0 = reinterpret_cast<const char *>(src + ((b * L + t0) * R + rr) * COLS);
+    const uint32_t rs = (uint32_t)(R * COLS) * 2u;
+    const int nv = (int)min<int64_t>(kQ, te - t0);
+    for (int i = tid; i < kQ * Q8; i += nthr) {
+        const int tr = i / Q8, c8 = (i % Q8) * 8;
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if (tr < nv) w = *reinterpret_cast<const uint4 *>(row0 + lane_off((uint32_t)tr * rs + (uint32_t)c8 * 2u));
+        *reinterpret_cast<uint4 *>(&dst[tr][c8]) = w;
+    }
+}
+
 // Element (row 16 ti + 4 r + v, column) of a chunk tile in global memory: the
 // uniform chunk base plus rows (16 ti + v) whole rows (SGPRs), and the lane's
 // rows 4 r and its column as a 32-bit byte offset
@@ -586,7 +602,8 @@ __global__ void __launch_bounds__(64 * (P / 16))
 ssdb_walk_r2(SbKp p) {
     constexpr int NW = P / 16, NT = N / 16, NTH = 64 * NW;
     __shared__ __attribute__((aligned(16))) float sB[kQ][N + 4];
-    __shared__ __attribute__((aligned(16))) float sC[kQ][N + 4];
+    // C stays bf16 in LDS (it is exact there): the group's LDS then allows 4 groups per CU
+    __shared__ __attribute__((aligned(16))) uint16_t sC[kQ][N + 8];
     __shared__ __attribute__((aligned(16))) float sY[kQ][P + 4];
     __shared__ __attribute__((aligned(16))) float sM[kQ][kQ + 4];
     __shared__ float sRed[NW][2][kQ];
@@ -616,7 +633,7 @@ ssdb_walk_r2(SbKp p) {
     for (int64_t ci = nch - 1; ci >= 0; --ci) {
         const int64_t t0 = T0 + ci * kQ;
         stage_bf16<N, N + 4>(sB, p.B, b, p.L, p.G, g, t0, T1, tid, NTH);
-        stage_bf16<N, N + 4>(sC, p.C, b, p.L, p.G, g, t0, T1, tid, NTH);
+        stage_bf16_raw<N, N + 8>(sC, p.C, b, p.L, p.G, g, t0, T1, tid, NTH);
         stage_f32<P, P + 4>(sY, p.dy, b, p.L, p.H, h, t0, T1, tid, NTH);
         if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane);
         __syncthreads();
@@ -628,7 +645,9 @@ ssdb_walk_r2(SbKp p) {
 #pragma unroll
             for (int kt = 0; kt < NT; ++kt) {
                 const float4 a4 = *reinterpret_cast<const float4 *>(&sB[16 * ti + c16][16 * kt + 4 * r]);
-                const float4 b4 = *reinterpret_cast<const float4 *>(&sC[16 * tj + c16][16 * kt + 4 * r]);
+                const uint2 c2 = *reinterpret_cast<const uint2 *>(&sC[16 * tj + c16][16 * kt + 4 * r]);
+                const float4 b4 = make_float4(__uint_as_float(c2.x << 16), __uint_as_float(c2.x & 0xffff0000u),
+                                              __uint_as_float(c2.y << 16), __uint_as_float(c2.y & 0xffff0000u));
                 acc = mfma4(a4.x, b4.x, acc);
                 acc = mfma4(a4.y, b4.y, acc);
                 acc = mfma4(a4.z, b4.z, acc);
@@ -704,7 +723,7 @@ ssdb_walk_r2(SbKp p) {
                 const int s = 16 * st + 4 * r + v;
                 const float bb = sY[s][pc] * sc.ecs[s];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) Gt[nt] = mfma4(sC[s][16 * nt + c16], bb, Gt[nt]);
+                for (int nt = 0; nt < NT; ++nt) Gt[nt] = mfma4(bf(sC[s][16 * nt + c16]), bb, Gt[nt]);
             }
         __syncthreads();
         if (tid < kQ && t0 + tid < T1) {
