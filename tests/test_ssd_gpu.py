@@ -91,8 +91,9 @@ def test_ssd_workloads_sampled(cuda_device, name, per_group):
     assert ey <= TOL_BF16 and eh <= TOL_BF16
 
 
-@pytest.mark.parametrize("shape", [(2, 4096, 80, 64, 128, 8, DT), (4, 4096, 64, 32, 64, 4, ZOH)],
-                         ids=["b2L4096H80P64N128G8", "b4L4096H64P32N64G4"])
+@pytest.mark.parametrize("shape", [(2, 4096, 80, 64, 128, 8, DT), (4, 4096, 64, 32, 64, 4, ZOH),
+                                   (2, 4096, 80, 64, 96, 8, ZOH)],
+                         ids=["b2L4096H80P64N128G8", "b4L4096H64P32N64G4", "b2L4096H80P64N96G8"])
 def test_ssd_head_pairs_sampled(cuda_device, shape):
     """Shapes whose plan runs several rounds of segments, where the segment states are
     formed for two heads of a group per work group: two heads of every group and batch
