@@ -39,8 +39,8 @@ MFMA_PEAKS = {
     "trap": (BF16_MFMA_PEAK_TFLOPS, "dense bf16 MFMA (model flops of the chunked decomposition)"),
     "cssd": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (model flops of the complex chunked decomposition)"),
     "cssd_mimo": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (the complex model over L x rank rows)"),
-    "ssd_bwd": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (executed 16x16x4 MFMAs of the walks)"),
-    "trap_bwd": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (executed 16x16x4 MFMAs of the walks)"),
+    "ssd_bwd": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (the walks' contraction work, in 16x16x4 MFMA units)"),
+    "trap_bwd": (FP32_MFMA_PEAK_TFLOPS, "dense fp32 MFMA (the walks' contraction work, in 16x16x4 MFMA units)"),
 }
 FP32_VALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, non-packed fp32
 # fp32 VALU issue: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz lane-slots/s (a wave64 op takes 4 cycles)
@@ -129,9 +129,12 @@ def s6_bwd_model(d):
 
 def ssd_bwd_model(d):
     """Algorithmic bytes of one SSD backward call (read x, B, C, dt, dy; write dx, ddt, dB, dC)
-    and the fp32 MFMA flops its kernels execute.  Per (batch, head) and 32-step chunk each of
-    the three walks issues 3P/4 + 3N/4 + PN/16 16x16x4 MFMAs (2048 flops each; 656 at P = 64,
-    N = 128), and the two state-only walks PN/32 each over all segments but one."""
+    and the contraction work of its walks, in units of 16x16x4 fp32 MFMAs (2048 flops each):
+    per (batch, head) and 32-step chunk each of the three walks 3P/4 + 3N/4 + PN/16 (656 at
+    P = 64, N = 128), and the two state-only walks PN/32 each over all segments but one.  (The
+    gradient-state updates of walks R1 and R2 do their PN/16 share on bf16 MFMAs, the fp32
+    operand split into three bf16 terms; the work counted is the contraction's, not those
+    three passes.)"""
     B, L, H, P, N, G = d["batch"], d["L"], d["nheads"], d["headdim"], d["d_state"], d["ngroups"]
     elems = B * L * H * P
     bytes_ = (elems * 2 + 2 * B * L * G * N * 2 + B * L * H * 4 + elems * 4 + elems * 4 +

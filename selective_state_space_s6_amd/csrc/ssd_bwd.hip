@@ -61,6 +61,43 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 16x16x32 bf16 MFMA: lane (q = lane/16, i = lane%16) gives row i of A and column i of B at
+// K slots 8q..8q+7; the result tile is the 16x16x4 one's (rows 4q..4q+3 of column i)
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+// two fp32 -> two bf16 (round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+// x = hi + mid + lo in bf16, to about 2^-26 of x (each part rounds the remainder of the last)
+__device__ __forceinline__ void split3_bf16(const float (&x)[8], u32x4 &hi, u32x4 &mid, u32x4 &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = pack2_bf16(x[2 * i], x[2 * i + 1]);
+        const float r0 = x[2 * i] - __uint_as_float(h << 16), r1 = x[2 * i + 1] - __uint_as_float(h & 0xffff0000u);
+        const uint32_t m = pack2_bf16(r0, r1);
+        hi[i] = h;
+        mid[i] = m;
+        lo[i] = pack2_bf16(r0 - __uint_as_float(m << 16), r1 - __uint_as_float(m & 0xffff0000u));
+    }
+}
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives the
+// four rows sb..sb+3 of column cb + i of a row-major [row][column] bf16 tile
+__device__ __forceinline__ uint2 tr_read16(const uint16_t *tile, int pitch, int sb, int cb, int lane) {
+    const int i = lane & 15;
+    const uint16_t *a = tile + (sb + (i >> 2)) * pitch + cb + 4 * (i & 3);
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) s16x4 *)(a)));
+}
+
 struct SbKp {
     const uint16_t *x; const float *dt; const float *dt_bias; const float *A_log;
     const uint16_t *B; const uint16_t *C; const float *D; const float *h0;
@@ -444,13 +481,15 @@ ssdb_walk_f(SbKp p) {
 // gradient states (and the last segment's decay).  Otherwise: every segment
 // backward from the gradient entering from the right, writing the head's dB
 // share and, at the start of the sequence, dh0.
+// The bf16 state update's operands take the walk a few VGPRs past 128 unless 4 waves per
+// SIMD are asked for, which the compiler then meets without spilling.
 template <int P, int N, bool STATE>
-__global__ void __launch_bounds__(64 * (N / 32))
+__global__ void __launch_bounds__(64 * (N / 32)) __attribute__((amdgpu_waves_per_eu(P <= 64 && !STATE ? 4 : 1)))
 ssdb_walk_r1(SbKp p) {
     constexpr int NW = N / 32, PT = P / 16, NTH = 64 * NW;
     __shared__ __attribute__((aligned(16))) float sX[STATE ? 1 : kQ][P + 4];
     __shared__ __attribute__((aligned(16))) float sY[kQ][P + 4];
-    __shared__ __attribute__((aligned(16))) float sC[kQ][N + 4];
+    __shared__ __attribute__((aligned(16))) uint16_t sC[kQ][N + 8];   // bf16, exact
     __shared__ __attribute__((aligned(16))) float sM[STATE ? 1 : kQ][kQ + 4];
     __shared__ Scal sc;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -483,7 +522,7 @@ ssdb_walk_r1(SbKp p) {
     for (int64_t ci = nch - 1; ci >= 0; --ci) {
         const int64_t t0 = T0 + ci * kQ;
         stage_f32<P, P + 4>(sY, p.dy, b, p.L, p.H, h, t0, T1, tid, NTH);
-        stage_bf16<N, N + 4>(sC, p.C, b, p.L, p.G, g, t0, T1, tid, NTH);
+        stage_bf16_raw<N, N + 8>(sC, p.C, b, p.L, p.G, g, t0, T1, tid, NTH);
         if constexpr (!STATE) stage_bf16<P, P + 4>(sX, p.x, b, p.L, p.H, h, t0, T1, tid, NTH);
         if (w == 0) chunk_scalars(sc, p, b, h, t0, T1, bias, A, lane, !STATE);
         __syncthreads();
@@ -530,10 +569,10 @@ ssdb_walk_r1(SbKp p) {
 #pragma unroll
                     for (int tj = ti; tj < 2; ++tj) {
                         const float4 a4 = *reinterpret_cast<const float4 *>(&sM[16 * ti + c16][16 * tj + 4 * r]);
-                        acc = mfma4(a4.x, sC[16 * tj + 4 * r + 0][n], acc);
-                        acc = mfma4(a4.y, sC[16 * tj + 4 * r + 1][n], acc);
-                        acc = mfma4(a4.z, sC[16 * tj + 4 * r + 2][n], acc);
-                        acc = mfma4(a4.w, sC[16 * tj + 4 * r + 3][n], acc);
+                        acc = mfma4(a4.x, bf(sC[16 * tj + 4 * r + 0][n]), acc);
+                        acc = mfma4(a4.y, bf(sC[16 * tj + 4 * r + 1][n]), acc);
+                        acc = mfma4(a4.z, bf(sC[16 * tj + 4 * r + 2][n]), acc);
+                        acc = mfma4(a4.w, bf(sC[16 * tj + 4 * r + 3][n]), acc);
                     }
                     float *dB0 = p.dBh + ((b * p.L + t0) * p.H + h) * N;
                     const uint32_t rsD = (uint32_t)(p.H * N) * 4u;
@@ -545,31 +584,45 @@ ssdb_walk_r1(SbKp p) {
                             // plus the trapezoidal diagonal's dk_t += (gamma_t - sigma_t)(dy_t.x_t) q_t
                             const float db = acc[v] * sc.sig[tl];
                             chunk_elem(dB0, rsD, 16 * ti + v, (uint32_t)(4 * r) * rsD + (uint32_t)n * 4u) =
-                                p.trap ? fmaf(sc.cd[tl], sC[tl][n], db) : db;
+                                p.trap ? fmaf(sc.cd[tl], bf(sC[tl][n]), db) : db;
                         }
                     }
                 }
         }
-        // G <- e^{cs_end} G + (e^{cs} o dY)^T C
+        // G <- e^{cs_end} G + (e^{cs} o dY)^T C on bf16 MFMA: C read transposed from the bf16
+        // tile, e^{cs} o dY split into three bf16 terms (fp32-exact), the chunk's 32 steps in
+        // K order (4r..4r+3, 16+4r..16+4r+3) on both operands
         const float eend = __expf(csend);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) Gs[pt][nt] *= eend;
+        {
+            u32x4 Cf[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int nt = 0; nt < 2; ++nt) {
+                const uint2 a0 = tr_read16(&sC[0][0], N + 8, 4 * r, 32 * w + 16 * nt, lane);
+                const uint2 a1 = tr_read16(&sC[0][0], N + 8, 16 + 4 * r, 32 * w + 16 * nt, lane);
+                Cf[nt] = u32x4{a0.x, a0.y, a1.x, a1.y};
+            }
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int s = 16 * st + 4 * r + v;
-                const float es = sc.ecs[s];
-                const float b0 = sC[s][32 * w + c16], b1 = sC[s][32 * w + 16 + c16];
+            for (int pt = 0; pt < PT; ++pt) {
+                float av[8];
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const float a = sY[s][16 * pt + c16] * es;
-                    Gs[pt][0] = mfma4(a, b0, Gs[pt][0]);
-                    Gs[pt][1] = mfma4(a, b1, Gs[pt][1]);
+                for (int i = 0; i < 8; ++i) {
+                    const int s = (i < 4 ? 0 : 16) + 4 * r + (i & 3);
+                    av[i] = sY[s][16 * pt + c16] * sc.ecs[s];
+                }
+                u32x4 Ah, Am, Al;
+                split3_bf16(av, Ah, Am, Al);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    Gs[pt][nt] = mfma_bf16(Ah, Cf[nt], Gs[pt][nt]);
+                    Gs[pt][nt] = mfma_bf16(Am, Cf[nt], Gs[pt][nt]);
+                    Gs[pt][nt] = mfma_bf16(Al, Cf[nt], Gs[pt][nt]);
                 }
             }
+        }
         sumA += csend;
         __syncthreads();
     }
@@ -712,19 +765,31 @@ ssdb_walk_r2(SbKp p) {
                 }
             }
         }
-        // G^T <- e^{cs_end} G^T + C^T (e^{cs} o dY)
+        // G^T <- e^{cs_end} G^T + C^T (e^{cs} o dY) on bf16 MFMA: C^T read transposed from
+        // the bf16 C tile, e^{cs} o dY split into three bf16 terms (fp32-exact), the chunk's
+        // 32 steps in K order (4r..4r+3, 16+4r..16+4r+3) on both operands
         const float eend = __expf(csend);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) Gt[nt] *= eend;
+        {
+            float bb[8];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int s = 16 * st + 4 * r + v;
-                const float bb = sY[s][pc] * sc.ecs[s];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) Gt[nt] = mfma4(bf(sC[s][16 * nt + c16]), bb, Gt[nt]);
+            for (int i = 0; i < 8; ++i) {
+                const int s = (i < 4 ? 0 : 16) + 4 * r + (i & 3);
+                bb[i] = sY[s][pc] * sc.ecs[s];
             }
+            u32x4 Bh, Bm, Bl;
+            split3_bf16(bb, Bh, Bm, Bl);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const uint2 a0 = tr_read16(&sC[0][0], N + 8, 4 * r, 16 * nt, lane);
+                const uint2 a1 = tr_read16(&sC[0][0], N + 8, 16 + 4 * r, 16 * nt, lane);
+                const u32x4 Af{a0.x, a0.y, a1.x, a1.y};
+                Gt[nt] = mfma_bf16(Af, Bh, Gt[nt]);
+                Gt[nt] = mfma_bf16(Af, Bm, Gt[nt]);
+                Gt[nt] = mfma_bf16(Af, Bl, Gt[nt]);
+            }
+        }
         __syncthreads();
         if (tid < kQ && t0 + tid < T1) {
             float s0 = 0.0f, s2 = 0.0f;
