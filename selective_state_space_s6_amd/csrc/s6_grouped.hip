@@ -382,13 +382,16 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
             const float dl = row_bcast<t>(dlk), uu = row_bcast<t>(uk), dyv = row_bcast<t>(dyk);
             const Zoh zh = coef(dl);
             const float ab = zh.ab, beta = zh.beta;
+            // the derivatives of Abar and beta take the exponential itself: 1 + A beta, which
+            // the recurrence keeps, is off by ~1e-7 absolute where Abar is e^{-25} or less
+            const float ex = exp2_fast(dl * A2);
             float bD, bA;
             if constexpr (MODE == 0) {
-                bD = ab;
+                bD = ex;
                 // dbeta/dA = (delta Abar - beta)/A cancels to second order in z, so in
                 // the forward's series range it comes from the series of phi1'
                 const float z = dl * A;
-                bA = dl * A2 > -kZohSeriesX ? dl * dl * g_dphi1_small(z) : (dl * ab - beta) * iA;
+                bA = dl * A2 > -kZohSeriesX ? dl * dl * g_dphi1_small(z) : (dl * ex - beta) * iA;
             } else if constexpr (MODE == 1) {
                 bD = 1.0f; bA = 0.0f;
             } else {
@@ -405,8 +408,8 @@ __device__ __forceinline__ void s6_grouped_bwd_body(const S6GBp &p) {
                 *at(p.dCw + row, o_dbc) = dyv * hs[t];
             }
             pu[t] = gb * bm;
-            pd[t] = g * fmaf(hp * A, ab, bu * bD);
-            accA = fmaf(g, fmaf(hp * dl, ab, bu * bA), accA);
+            pd[t] = g * fmaf(hp * A, ex, bu * bD);
+            accA = fmaf(g, fmaf(hp * dl, ex, bu * bA), accA);
             g *= ab;
         });
         const float su = g_row_transpose_sum(pu, k);

@@ -121,3 +121,16 @@ def test_s6_bwd_mamba1_workload(cuda_device):
     report("s6_bwd mamba1", **e)
     bad = {k: v for k, v in e.items() if not v <= TOL_BWD}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("flags", [ZOH, DT, ONE])
+def test_s6_bwd_extreme_dt(cuda_device, flags):
+    """Raw dt of -25 (delta ~ 1e-11) next to +25 (delta ~ 25, decays of e^{-25 |A|} and
+    below).  Where a step all but erases the state, the derivatives of Abar are of that
+    step's size: they take the exponential itself, not the 1 + A beta of the recurrence,
+    whose absolute rounding (~1e-7) would otherwise dominate ddt and dA_log."""
+    inp = synth.s6_inputs(2, 300, 64, 16, seed=(37,), h0=True)
+    dt = inp.arrays["dt"]
+    dt[:, ::3] = -25.0
+    dt[:, 1::7] = 25.0
+    _check(f"s6_bwd extreme dt flags={flags}", inp, cuda_device, flags, TOL_BWD, seed=(37,))

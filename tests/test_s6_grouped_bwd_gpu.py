@@ -85,3 +85,22 @@ def test_grouped_bwd_per_channel_workload_sampled(cuda_device):
     report("s6_pc_mamba1 bwd sampled", **errs)
     for k in GRADS:
         assert errs[k] <= TOL_BWD, (k, errs[k])
+
+
+@pytest.mark.parametrize("G", [64, 16])
+@pytest.mark.parametrize("flags", [ZOH, DT])
+def test_grouped_bwd_extreme_dt(cuda_device, flags, G):
+    """Raw dt of -25 next to +25: the derivatives of Abar at steps that all but erase the
+    state are of those steps' size (the exponential itself, not 1 + A beta)."""
+    inp = synth.s6_inputs(2, 300, 64, 16, seed=(38, G), h0=True, ngroups=G)
+    dt = inp.arrays["dt"]
+    dt[:, ::3] = -25.0
+    dt[:, 1::7] = 25.0
+    dy, dhf = synth.s6_cotangents(2, 300, 64, 16, seed=(38,))
+    g = _gpu(inp, dy, dhf, cuda_device, flags)
+    o = oracle.s6_grouped_bwd(**inp.arrays, dy=dy, dh_final=dhf, flags=flags)
+    errs = {k: synth.max_rel_err(g[k], o[k]) for k in GRADS}
+    report(f"s6 grouped bwd extreme dt flags={flags} G={G}", **errs)
+    for k in GRADS:
+        assert np.isfinite(g[k]).all(), k
+        assert errs[k] <= TOL_BWD, (k, errs[k])

@@ -87,3 +87,47 @@ def test_trap_bwd_mamba3_workload_sampled(cuda_device):
     report("trap_mamba3 bwd sampled", **errs)
     for k, e in errs.items():
         assert e <= TOL_BWD, (k, e)
+
+
+EPS32 = 2.0 ** -24
+
+
+def test_trap_bwd_extreme_dt(cuda_device):
+    """dt of 1e-11 next to 25 (decays of e^{25 a}, a in [-16, -1]) over two segments.  All
+    outputs but da and ddt meet the usual bar.  da_t = dt_t s_t and ddt_t = a_t s_t + ...
+    go through s_t, the gradient of the log decay at t: a suffix sum over t' >= t of
+    per-step contractions, accurate in fp32 to a rounding unit of its absolute terms, not
+    of s_t itself (where a step erases the state s_t is ~0 while the suffix holds terms of
+    1e5 and more).  Their bar adds EPS32 times that absolute suffix, read off the oracle's
+    outputs: |q_t| . |dq_t| (the dy_t h_t contraction) and |x_t| . |dx_t - D dy_t| (the
+    injected input against the state's cotangent), plus |h_final dh_final|."""
+    inp = synth.trap_inputs(1, 700, 2, 64, 128, seed=(36,), h0=True, prev=True)
+    ar = inp.arrays
+    dt = ar["dt"]
+    dt[:, ::3] = 1e-11
+    dt[:, 1::7] = 25.0
+    dy, dh = _cot(1, 700, 2, 64, 128, (36,))
+    g = _gpu(inp, dy, dh, cuda_device)
+    o = oracle.trap_bwd(**ar, dy=dy, dh_final=dh)
+    errs = {k: synth.max_rel_err(g[k], o[k]) for k in KEYS if g.get(k) is not None}
+    report("trap bwd extreme dt", **errs)
+    for k, e in errs.items():
+        assert np.isfinite(g[k]).all(), k
+        if k not in ("da", "ddt"):
+            assert e <= TOL_BWD, (k, e)
+    _, hf = oracle.trap_fwd(**ar)
+    suf = []
+    for h in range(ar["x"].shape[2]):
+        mag = (np.abs(ar["q"][0, :, h]).astype(np.float64) * np.abs(o["dq"][0, :, h])).sum(1) + \
+              (np.abs(ar["x"][0, :, h]).astype(np.float64) *
+               np.abs(o["dx"][0, :, h] - ar["D"][h] * dy[0, :, h])).sum(1)
+        suf.append(np.cumsum(mag[::-1])[::-1] + np.abs(hf[0, h] * dh[0, h]).sum())
+    suf = np.stack(suf, 1)                                   # (L, H)
+    ratios = {}
+    for k, scale in (("da", dt[0].astype(np.float64)), ("ddt", np.abs(ar["a"][0].astype(np.float64)))):
+        rms = np.sqrt(np.mean(o[k][0] ** 2))
+        bar = TOL_BWD * (np.abs(o[k][0]) + 0.01 * rms) + EPS32 * scale * suf
+        err = np.abs(g[k][0].astype(np.float64) - o[k][0])
+        ratios[k] = float(np.max(err / bar))
+        assert (err <= bar).all(), f"{k}: worst err/bar {ratios[k]:.3f}"
+    report("trap bwd extreme dt (err/bar)", **ratios)
