@@ -335,7 +335,8 @@ int ssm_s6_scan_grouped_bwd_saved(const void *u, const float *dt, const float *d
  * y (batch, L, nheads, headdim) fp32; h0, h_final (batch, nheads, headdim, d_state) fp32.
  * in_dtype must be SSM_BF16 (the contractions run on bf16 MFMA; SSM_F32 returns
  * SSM_ERR_UNSUPPORTED).  Limits: nheads % ngroups == 0; headdim in {32, 64, 128};
- * d_state a multiple of 32, <= 256; chunk_len in {64, 128, 256}.
+ * nheads * headdim <= 2^24 (as for every SSD-family call below); d_state a
+ * multiple of 32, <= 256; chunk_len in {64, 128, 256}.
  * Workspace: ssd_chunk_scan_fwd_workspace_size() bytes, 16-byte aligned,
  * owned by the caller and reused freely between calls on one stream (one fp32
  * headdim x d_state state and one decay per (batch, head, segment)); the size

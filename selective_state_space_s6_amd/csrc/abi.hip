@@ -403,6 +403,10 @@ static int ssd_check_shape(const char *E, int64_t batch, int64_t L, int64_t nhea
                     (long long)nheads, (long long)ngroups);
     if (too_big(batch, L, nheads, headdim) || too_big(batch, L, ngroups, d_state))
         return fail(SSM_ERR_UNSUPPORTED, "%s: problem too large", E);
+    // a chunk's rows are addressed by 32-bit byte offsets from a per-chunk base
+    if (nheads * headdim > (1LL << 24))
+        return fail(SSM_ERR_UNSUPPORTED, "%s: nheads * headdim %lld exceeds 2^24", E,
+                    (long long)(nheads * headdim));
     return SSM_OK;
 }
 

@@ -50,6 +50,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kT = 32;              // steps per chunk
 constexpr int kTargetWaves = 3072;  // enough resident waves to hide latency
 constexpr int kMinSeg = 256;        // shortest segment worth a state round trip
+// word 3 of a raw buffer resource on gfx9-family chips (gfx950 included): 32-bit data
+// format, no swizzle, no index stride; with stride 0 a store at or past the record count
+// is dropped
+constexpr int kBufWord3 = 0x00020000;
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -613,6 +617,7 @@ cssd_scan_kernel(CssdKp p) {
     f32x4 mnext[3];
 #pragma unroll
     for (int tau = 0; tau < 3; ++tau) mnext[tau] = Mg[tau * 64];
+    float2 Enext = Rc[0].E;   // the chunk's state decay, also read a chunk ahead
     st.load(tb);
     st.store(Bs[0], Cs[0], Xs[0], csign);
     if (nchunks > 1) st.load(tb + kT);
@@ -622,13 +627,14 @@ cssd_scan_kernel(CssdKp p) {
         const int buf = (int)(j & 1);
         const int64_t t0 = tb + j * kT;
         const float *B_ = Bs[buf], *C_ = Cs[buf], *X_ = Xs[buf];
-        const float2 E = Rc[j].E;
+        const float2 E = Enext;
         f32x4 mv[3];
 #pragma unroll
         for (int tau = 0; tau < 3; ++tau) mv[tau] = mnext[tau];
         if (j + 1 < nchunks) {
 #pragma unroll
             for (int tau = 0; tau < 3; ++tau) mnext[tau] = Mg[(j + 1) * 192 + tau * 64];
+            Enext = Rc[j + 1].E;
         }
         // D5: ys[tt] = sum_k Chat[t][k] S_r[k][p], Chat = (Re, -Im) of C_t[n] e^{mu lam_t}
         // (the staged C tile); two partial sums (even and odd state tiles)
@@ -668,21 +674,20 @@ cssd_scan_kernel(CssdKp p) {
             for (int v = 0; v < 4; ++v)
                 yv[tt][v] = fmaf(Dh, X_[(tt * 16 + 4 * q + v) * XP + p0 + c16],
                                  (ys[tt][0][v] + ys[tt][1][v]) + acc[tt][v]);
-        if (t0 + kT <= te) {
+        // raw buffer stores whose record count ends at the chunk's last valid step: the
+        // hardware drops a ragged tail's stores, so every chunk issues the same 8 stores with
+        // no branch around them, and the compiler can count them when it waits for loads
+        // issued before them (loads and stores share one counter)
+        {
+            const int64_t nv = min((int64_t)kT, te - t0);
+            const int rec = (int)((nv - 1) * rowX * 4 + 64);   // lane columns < 16: 64 bytes of the last row
+            const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(Yg + t0 * rowX, 0, rec, kBufWord3);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + v) * rowX) + ylane) =
-                        yv[tt][v];
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (t0 + tt * 16 + q * 4 + v < te)
-                        *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + v) * rowX) + ylane) =
-                            yv[tt][v];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[tt][v]), yr,
+                                                          (int)(ylane + (uint32_t)((tt * 16 + v) * rowX) * 4u), 0, 0);
         }
 
         // D2 + D3

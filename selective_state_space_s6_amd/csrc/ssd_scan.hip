@@ -79,6 +79,11 @@ __device__ __forceinline__ uint32_t lane_off(uint32_t o) {
     return o;
 }
 
+// Word 3 of a raw buffer resource on gfx9-family chips (gfx950 included): 32-bit data
+// format, no swizzle, no index stride; with stride 0 an access whose offset is at or past
+// the record count is dropped (stores) or reads zero (loads)
+constexpr int kBufWord3 = 0x00020000;
+
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
 // names a row of 4 consecutive 16-bit elements and receives element (i % 4) of
 // rows i/4, i/4 + 4, i/4 + 8, i/4 + 12.  Pointing row i at (step sb + i/4,
@@ -556,6 +561,15 @@ ssd_scan_kernel(SsdKp p) {
         chunk_scalars(scal[0], st.rdt[0], tb + (lane & 31) < p.L && lane < kT, bias, A, p.mode, lane,
                       TRAP ? &st.rtp[0] : nullptr);
     if (nchunks > 1) st.template load<0>(tb + kT);
+    {
+        // the 8 y stores of a chunk, issued here with a record count of 0 (the hardware drops
+        // every one): the loop is entered with stores behind the prefetch loads, as from its
+        // own back edge, so the compiler's wait at the top of the loop can leave them in flight
+        const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(Yg + tb * rowX, 0, 0, kBufWord3);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            __builtin_amdgcn_raw_buffer_store_b32(0u, yr, (int)(ylane + (uint32_t)(r * rowX) * 4u), 0, 0);
+    }
     __syncthreads();
 
     for (int64_t j = 0; j < nchunks; ++j) {
@@ -674,21 +688,22 @@ ssd_scan_kernel(SsdKp p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) yv[tt][i] = fmaf(Dh, xs[i], yacc[tt][i]);
         }
-        if (t0 + kT <= te) {
+        // raw buffer stores whose record count ends at the chunk's last valid step: the
+        // hardware drops a ragged tail's stores, so every chunk issues the same 8 stores with
+        // no branch around them, and the wait for the next chunk's prefetched loads does not
+        // take in these stores (loads and stores share one counter, which the compiler can
+        // only count on a path with a fixed number of stores)
+        {
+            const int64_t nv = min((int64_t)kT, te - t0);
+            const int rec = (int)((nv - 1) * rowX * 4 + 64);   // lane columns < 16: 64 bytes of the last row
+            const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(Yg + t0 * rowX, 0, rec, kBufWord3);
+            const uint32_t yl = lane_off(ylane);      // re-read per chunk: 8 offsets not held across the loop
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + i) * rowX) + lane_off(ylane)) =
-                        yv[tt][i];
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (t0 + tt * 16 + q * 4 + i < te)
-                        *reinterpret_cast<float *>(reinterpret_cast<char *>(Yg + (t0 + tt * 16 + i) * rowX) + lane_off(ylane)) =
-                            yv[tt][i];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[tt][i]), yr,
+                                                          (int)(yl + (uint32_t)((tt * 16 + i) * rowX) * 4u), 0, 0);
         }
 
         // D2+D3

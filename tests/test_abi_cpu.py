@@ -167,6 +167,7 @@ def test_ssd_argument_checks(lib):
     assert _ssd(lib, dims=(2, 300, 4, 64, 512, 2, 256)) == UNSUPPORTED
     assert _ssd(lib, dims=(2, 300, 4, 64, 128, 2, 100)) == UNSUPPORTED and "chunk_len" in _err(lib)
     assert _ssd(lib, dims=(2, 300, 4, 64, 128, 2, 0)) == INVALID
+    assert _ssd(lib, dims=(1, 64, 1 << 18, 128, 128, 1, 256)) == UNSUPPORTED and "2^24" in _err(lib)
     assert _ssd(lib, dtype=0) == UNSUPPORTED and "bf16" in _err(lib)
     assert _ssd(lib, flags=0x8) == INVALID
     # short sequences run as one segment (no workspace); long ones keep one
