@@ -61,16 +61,16 @@ TRAFFIC = {
         "bytes": 308664790
     },
     "ssd_mamba2": {
-        "src_sha1": "a90070c832174eaea01da91dee5b407abb7b1e30",
-        "bytes": 501871827
+        "src_sha1": "5784943de805795f1dd6d85d75f4db3f1adf3b43",
+        "bytes": 502900386
     },
     "ssd_long": {
-        "src_sha1": "a90070c832174eaea01da91dee5b407abb7b1e30",
-        "bytes": 3604600222
+        "src_sha1": "5784943de805795f1dd6d85d75f4db3f1adf3b43",
+        "bytes": 3622451415
     },
     "cssd_mamba3": {
-        "src_sha1": "d6c57f3db1e631ca1bd045b8cad57a67034d2545",
-        "bytes": 1106275978
+        "src_sha1": "ae7254e078839793bbf80b24c4a75b00f4c40ee9",
+        "bytes": 1106262528
     }
 }
 # adjoint update of one (b, t, d, n) in ZOH mode: g += C dy, dh terms of du, ddt, dB, dC, dA
