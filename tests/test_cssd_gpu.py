@@ -20,6 +20,7 @@ CASES = [  # batch, L, H, P, Nc, G, Q, flags, h0
     (1, 120, 2, 32, 8, 1, 64, CODE, True),
     (1, 90, 2, 64, 32, 1, 64, STABLE | ZOH | CONJ, True),
     (1, 1, 2, 32, 8, 1, 64, STABLE | ZOH, True),
+    (3, 7, 2, 32, 8, 1, 64, STABLE | ZOH, True),  # batch rows shorter than a chunk, back to back
     (1, 64, 2, 128, 8, 1, 64, STABLE | ZOH, False),
     # long enough to be cut into segments (state kernel + pass + scan), last segment partial
     (1, 1000, 2, 64, 24, 1, 64, STABLE | ZOH, True),

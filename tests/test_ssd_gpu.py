@@ -30,6 +30,7 @@ CASES = [  # batch, L, H, P, N, G, Q, flags, h0
     (1, 130, 2, 128, 64, 2, 128, DT, True),
     (1, 100, 2, 64, 256, 1, 64, DT, True),
     (1, 1, 2, 64, 128, 1, 256, DT, True),
+    (3, 5, 2, 64, 128, 1, 64, DT, True),          # batch rows shorter than a chunk, back to back
     (1, 65, 2, 64, 128, 1, 64, ZOH, True),
     (2, 513, 4, 64, 128, 1, 256, DT, False),
     # long enough to be cut into segments (state kernel + pass + scan), last segment partial
